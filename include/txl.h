@@ -1,0 +1,196 @@
+/*
+ * libtxl — relative-positional self-attention over a cached memory, the hot path
+ * of Dai et al., "Transformer-XL: Attentive Language Models Beyond a
+ * Fixed-Length Context", for AMD Instinct MI355X (gfx950).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Ownership  Every tensor pointer is a DEVICE pointer owned by the caller.  The
+ *            library keeps no pointer after a call returns and allocates no
+ *            device memory: temporaries live in a caller-provided workspace
+ *            whose size the matching *_workspace_bytes() query returns.
+ * Streams    `stream` is a hipStream_t (NULL = the default stream).  Work is
+ *            enqueued asynchronously; returning TXL_OK means "enqueued".
+ * Errors     Every argument is validated before anything is enqueued.  On an
+ *            error nothing is launched, in/out arguments (mem_start) are left
+ *            untouched and txl_last_error() holds a message for this thread.
+ *            A failing HIP launch returns TXL_ERR_HIP.
+ * Dtypes     One storage dtype per call (TXL_F32 or TXL_BF16) for every tensor
+ *            argument; accumulation is always fp32; conversions to bf16 round
+ *            to nearest even.  The bf16 path requires d_head <= 64.
+ * Layouts    Row-major, no padding, no strides:
+ *              h        [B][L][d_model]          current segment
+ *              mem      [B][M][d_model]          memory ring: logical row p
+ *                                                (oldest first) is physical
+ *                                                slot (mem_start + p) mod M
+ *              W_q, W_kE, W_v  [H*d_head][d_model]  (out x in; q = h W_q^T)
+ *              W_kR     [H*d_head][d_pos]
+ *              u, v     [H][d_head]
+ *              R        [M+L][d_pos]             row delta = distance delta
+ *              Rk       [M+L][H][d_head]         Rk[delta] = W_kR R_delta
+ *              out      [B][L][H][d_head]        heads concatenated
+ *            Head h owns rows h*d_head .. (h+1)*d_head-1 of each W and R is
+ *            shared by all heads.
+ * Indices    Query i in [0,L), key j in [0,M+L) over [memory ; segment],
+ *            distance delta = M + i - j; key j is visible to query i iff
+ *            j <= M + i (every memory slot plus the causal part of the segment).
+ */
+#ifndef TXL_H
+#define TXL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TXL_ABI_VERSION 1
+
+typedef enum {
+  TXL_OK = 0,
+  TXL_ERR_NULL_ARG = 1,             /* a required pointer is NULL              */
+  TXL_ERR_BAD_SHAPE = 2,            /* a size is out of range or inconsistent  */
+  TXL_ERR_BAD_DTYPE = 3,            /* dtype is not TXL_F32 / TXL_BF16         */
+  TXL_ERR_WORKSPACE_TOO_SMALL = 4,  /* workspace_bytes below the query result  */
+  TXL_ERR_UNSUPPORTED = 5,          /* valid but not implemented (e.g. bf16
+                                       with d_head > 64)                       */
+  TXL_ERR_HIP = 6                   /* a HIP runtime call or launch failed     */
+} txl_status_t;
+
+typedef enum { TXL_F32 = 0, TXL_BF16 = 1 } txl_dtype_t;
+
+/* Shape of one relative-attention call (one layer, one segment). */
+typedef struct {
+  int32_t batch;     /* B >= 1                                             */
+  int32_t seg_len;   /* L >= 1                                             */
+  int32_t mem_len;   /* M >= 0 (0 = no memory: plain causal attention)     */
+  int32_t d_model;   /* width of h and mem                                 */
+  int32_t n_heads;   /* H >= 1                                             */
+  int32_t d_head;    /* per-head width                                     */
+  int32_t d_pos;     /* width of R (d_model in the paper)                  */
+  int32_t dtype;     /* txl_dtype_t                                        */
+  float scale;       /* multiplies the sum of the four score terms;
+                        <= 0 selects 1/sqrt(d_head)                        */
+} txl_attn_shape_t;
+
+/* ABI version of the loaded library (TXL_ABI_VERSION of its build). */
+int txl_abi_version(void);
+
+/* Static text for a status code. */
+const char* txl_status_str(txl_status_t status);
+
+/* Detail of the last error raised on the calling thread ("" if none). */
+const char* txl_last_error(void);
+
+/*
+ * Relative position table (Sec. 3.3: R is a sinusoid encoding matrix without
+ * learnable parameters, row delta encodes distance delta).  Writes
+ * R[n_pos][d_pos] with R[delta][2k] = sin(delta / 10000^(2k/d_pos)) and
+ * R[delta][2k+1] = cos(delta / 10000^(2k/d_pos)), evaluated in fp64 and
+ * rounded once to `dtype`.
+ * Errors: NULL R; n_pos < 1 or d_pos < 1; bad dtype; HIP failure.
+ */
+txl_status_t txl_sinusoid_pos(void* R, int32_t n_pos, int32_t d_pos, int32_t dtype,
+                              void* stream);
+
+/*
+ * Position keys for every distance (App. B: the matrix Q holds W_kR R_delta for
+ * delta = M+L-1 .. 0; here they are stored in natural order):
+ *   Rk[delta][h][c] = sum_x W_kR[h*d_head + c][x] * R[delta][x]
+ * R [n_pos][d_pos], W_kR [n_heads*d_head][d_pos], Rk [n_pos][n_heads][d_head].
+ * The result depends only on the weights and R, so a caller streaming segments
+ * may compute it once per layer and pass it to txl_rel_attn_fwd as Rk.
+ * `workspace` may be NULL when txl_rel_proj_workspace_bytes() returns 0.
+ * Errors: NULL pointers; sizes < 1; bad dtype; workspace too small; HIP.
+ */
+size_t txl_rel_proj_workspace_bytes(int32_t n_pos, int32_t d_pos, int32_t n_heads,
+                                    int32_t d_head, int32_t dtype);
+txl_status_t txl_rel_proj(const void* R, const void* W_kR, void* Rk, int32_t n_pos,
+                          int32_t d_pos, int32_t n_heads, int32_t d_head, int32_t dtype,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * One relative-attention forward over a cached memory (Sec. 3.3, the per-layer
+ * summary equations, with H heads):
+ *   h~  = [mem (logical order) ; h]
+ *   q   = h W_q^T,  k = h~ W_kE^T,  val = h~ W_v^T          (per head)
+ *   A_ij = scale * ( q_i.k_j + q_i.Rk[M+i-j] + u.k_j + v.Rk[M+i-j] )
+ *   out_i = sum_j softmax_j(A_ij masked to j <= M+i) val_j
+ * Rk: if non-NULL, the caller's position keys [M+L][H][d_head] (e.g. from
+ * txl_rel_proj) and W_kR, R are not read (may be NULL); if NULL, Rk is computed
+ * from W_kR and R (R needs >= M+L rows) inside the call.
+ * mem may be NULL iff M == 0; mem_start must lie in [0, M) (0 when M == 0).
+ * The memory is only read; advancing it is txl_mem_update's job.
+ * Errors: NULL pointers; sizes out of range; scale NaN; bad dtype; bf16 with
+ * d_head > 64 (TXL_ERR_UNSUPPORTED); workspace too small; HIP.
+ */
+size_t txl_rel_attn_workspace_bytes(const txl_attn_shape_t* shape);
+txl_status_t txl_rel_attn_fwd(const txl_attn_shape_t* shape, const void* h, const void* mem,
+                              int32_t mem_start, const void* W_q, const void* W_kE,
+                              const void* W_kR, const void* W_v, const void* u, const void* v,
+                              const void* R, const void* Rk, void* out, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/*
+ * Memory update (Sec. 3.2: the memory caches the M most recent hidden states,
+ * possibly spanning several segments).  New logical memory = last M rows of
+ * [memory ; h].  If L < M the L oldest ring slots are overwritten with h and
+ * *mem_start advances by L (mod M); if L >= M the ring receives the last M
+ * rows of h in order and *mem_start becomes 0.  M == 0 is a no-op.
+ * mem [B][M][d_model] (device), mem_start (HOST pointer, in/out, written only
+ * on success), h [B][L][d_model] (device).  Must be ordered after every read of
+ * the old memory (same stream).
+ * Errors: NULL pointers; sizes out of range; *mem_start outside [0, M); HIP.
+ */
+txl_status_t txl_mem_update(void* mem, int32_t* mem_start, const void* h, int32_t batch,
+                            int32_t mem_len, int32_t seg_len, int32_t d_model, int32_t dtype,
+                            void* stream);
+
+/*
+ * One layer of a segment step.  Required: W_q, W_kE, W_v, u, v, mem (if M > 0)
+ * and either Rk or W_kR.  The rest of the layer (Sec. 3.3 summary equations:
+ * o = LayerNorm(Linear(a) + h), then a position-wise feed-forward block) is
+ * present iff W_o is non-NULL, and then W_ff1 [d_inner][d_model] and
+ * W_ff2 [d_model][d_inner] are required:
+ *   o  = LN(a W_o^T + h),  h' = LN(o + ReLU(o W_ff1^T) W_ff2^T)
+ * with LN over d_model, eps 1e-5, no affine parameters.  Without W_o the layer
+ * output is the attention output itself and H*d_head must equal d_model when
+ * another layer follows.  W_o is [d_model][H*d_head].
+ */
+typedef struct {
+  const void* W_q;
+  const void* W_kE;
+  const void* W_kR;
+  const void* W_v;
+  const void* u;
+  const void* v;
+  const void* Rk;     /* optional cached position keys [M+L][H][d_head]     */
+  const void* W_o;    /* optional: NULL = attention-only layer              */
+  const void* W_ff1;
+  const void* W_ff2;
+  void* mem;          /* this layer's memory ring [B][M][d_model]           */
+} txl_layer_t;
+
+/*
+ * One segment through n_layers layers (Sec. 3.3 summary, for n = 1..N), with the
+ * memory update of Sec. 3.2: layer n attends over [mem_n ; h^{n-1}] and then
+ * mem_n receives h^{n-1} (its own input).  All layers share *mem_start (HOST
+ * pointer, in/out), advanced once on success.  h_in [B][L][d_model];
+ * h_out [B][L][d_out] with d_out = d_model if the last layer has W_o, else
+ * H*d_head.  R (>= M+L rows) is needed by every layer whose Rk is NULL.
+ * d_inner is the feed-forward width (ignored when no layer has W_o).
+ * Errors: as txl_rel_attn_fwd, plus n_layers < 1 and layer pointer checks.
+ */
+size_t txl_segment_workspace_bytes(const txl_attn_shape_t* shape, int32_t n_layers,
+                                   int32_t d_inner);
+txl_status_t txl_segment_step(const txl_attn_shape_t* shape, int32_t n_layers, int32_t d_inner,
+                              const txl_layer_t* layers, const void* R, const void* h_in,
+                              void* h_out, int32_t* mem_start, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TXL_H */

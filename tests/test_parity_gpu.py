@@ -1,0 +1,214 @@
+"""GPU parity: libtxl (through its C entry points) against the CPU oracle.
+
+Tolerances: max|gpu - oracle| <= 1e-4 * max|oracle| on the fp32 path and
+<= 2e-2 * max|oracle| on the bf16-in / fp32-accumulate path.  Memory rings
+after an update are compared bit for bit (they are copies of the inputs).
+Large workloads run whole on the GPU and are compared on sampled batch rows
+(rows never mix, see test_oracle.test_batch_independence).
+"""
+import numpy as np
+import pytest
+
+import synth
+from gpu_helpers import (DeviceLayers, TOL, assert_close, bf16_bits_of, from_dev, log,
+                         oracle_stream, run_attn_stream, run_segment_stream, tdtype, to_dev,
+                         txl_dtype, workspace)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def txl():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import transformer_xl_relative_attn_amd as mod
+    return mod
+
+
+def _check_ring(dl, wl, mems_oracle, start_o, start_g, b_idx, layer=0, exact=True):
+    import oracle
+    assert start_g == start_o
+    c = wl.cfg
+    if not c.mem_len:
+        return
+    if c.dtype == "bf16":
+        got_bits = bf16_bits_of(dl.mem[layer][b_idx])
+        want_bits = synth.bf16_bits(mems_oracle[layer])
+        if exact:
+            assert np.array_equal(got_bits, want_bits), "memory ring differs"
+        else:
+            got = synth.bits_to_f64(got_bits)
+            assert_close(got, mems_oracle[layer], "bf16", f"ring layer {layer}")
+    else:
+        got = from_dev(dl.mem[layer][b_idx])
+        assert np.array_equal(got, mems_oracle[layer].astype(np.float32).astype(np.float64))
+    _ = oracle
+
+
+# ------------------------------------------------------------------ R / Rk
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_sinusoid(txl, dtype):
+    import torch
+    import oracle
+    n, d = 3928, 1024
+    R = torch.empty((n, d), dtype=tdtype(dtype), device="cuda")
+    txl.txl_sinusoid_pos(R, n, d, txl_dtype(dtype))
+    torch.cuda.synchronize()
+    want = oracle.sinusoid(n, d)
+    got = from_dev(R)
+    if dtype == "f32":
+        assert np.max(np.abs(got - want)) <= 1e-7
+    else:
+        # one rounding of the fp64 value: within half a bf16 ulp (2^-9 relative)
+        assert np.all(np.abs(got - want) <= np.abs(want) * 2.0 ** -8 + 1e-30)
+
+
+@pytest.mark.parametrize("dtype,n_pos,d_pos,H,dh", [
+    ("f32", 16, 16, 1, 16), ("bf16", 300, 410, 10, 41), ("bf16", 1728, 1024, 16, 64),
+    ("bf16", 77, 128, 3, 24)])
+def test_rel_proj(txl, dtype, n_pos, d_pos, H, dh):
+    import torch
+    import oracle
+    rng = np.random.default_rng(5)
+    W = synth.round_to(rng.normal(0, 0.02, (H * dh, d_pos)), dtype)
+    Rw = oracle.sinusoid(n_pos, d_pos)
+    R = to_dev(synth.round_to(Rw, dtype), dtype)
+    Rk = torch.empty((n_pos, H, dh), dtype=tdtype(dtype), device="cuda")
+    ws = workspace(txl.txl_rel_proj_workspace_bytes(n_pos, d_pos, H, dh, txl_dtype(dtype)))
+    txl.txl_rel_proj(R, to_dev(W, dtype), Rk, n_pos, d_pos, H, dh, txl_dtype(dtype), ws)
+    torch.cuda.synchronize()
+    want = oracle.rel_proj(synth.round_to(Rw, dtype), W, H, dh)
+    assert_close(from_dev(Rk), want, dtype, f"Rk {n_pos}x{d_pos}")
+
+
+# --------------------------------------------------- single layer workloads
+def _stream_case(txl, cfg, n_seg, b_idx, start=0, use_rk=False, scale=0.0):
+    log(f"[case] {cfg.name} B={cfg.batch} L={cfg.seg_len} M={cfg.mem_len} H={cfg.n_heads} "
+        f"dh={cfg.d_head} d={cfg.d_model} {cfg.dtype} segs={n_seg} start={start} rk={use_rk}")
+    wl = synth.make_workload(cfg, n_segments=n_seg)
+    outs, dl, start_g = run_attn_stream(wl, n_seg, scale=scale, start=start, use_rk=use_rk)
+    if start and cfg.mem_len:
+        import oracle
+        # the oracle sees the same logical memory; its own ring starts at 0
+        _ = oracle
+    o_outs, o_mems, start_o = oracle_stream(wl, n_seg, b_idx, scale if scale > 0 else None)
+    for s in range(n_seg):
+        assert_close(outs[s][b_idx], o_outs[s], cfg.dtype, f"segment {s}")
+    if not start:
+        _check_ring(dl, wl, o_mems, start_o, start_g, b_idx)
+    return outs
+
+
+def test_c1_tiny_fp32_two_segments(txl):
+    cfg = synth.get_config("c1")
+    _stream_case(txl, cfg, 2, np.arange(cfg.batch))
+
+
+def test_c2_odd_head_dim(txl):
+    cfg = synth.get_config("c2")
+    _stream_case(txl, cfg, 1, np.array([0, 7, 15]))
+
+
+def test_c3_train_shaped(txl):
+    cfg = synth.get_config("c3")
+    _stream_case(txl, cfg, 4, np.array([0, 21]))
+
+
+def test_c4_eval_shaped(txl):
+    cfg = synth.get_config("c4")
+    _stream_case(txl, cfg, 8, np.array([0, 5]))
+
+
+def test_c4_with_cached_rk(txl):
+    cfg = synth.get_config("c4")
+    _stream_case(txl, cfg, 2, np.array([3]), use_rk=True)
+
+
+def test_fp32_path_c2_shape(txl):
+    cfg = synth.get_config("c2", dtype="f32", batch=2)
+    _stream_case(txl, cfg, 2, np.array([0, 1]))
+
+
+def test_literal_scale_one(txl):
+    """scale = 1 (the summary equations applied literally)."""
+    cfg = synth.get_config("c1", seed=77)
+    _stream_case(txl, cfg, 2, np.arange(cfg.batch), scale=1.0)
+
+
+# ------------------------------------------------------------------ edges
+EDGE = [
+    # (name, B, d, H, dh, L, M, dtype)
+    ("no_memory", 2, 128, 2, 64, 70, 0, "bf16"),
+    ("L_gt_M", 2, 128, 2, 64, 100, 40, "bf16"),
+    ("L_eq_1", 3, 64, 1, 64, 1, 200, "bf16"),
+    ("ragged_pack", 2, 96, 3, 24, 37, 45, "bf16"),
+    ("many_splits", 1, 64, 1, 64, 33, 3000, "bf16"),
+    ("L_257", 1, 64, 1, 32, 257, 31, "bf16"),
+    ("fp32_ragged", 2, 24, 3, 8, 13, 7, "f32"),
+    ("fp32_no_memory", 1, 16, 2, 8, 9, 0, "f32"),
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=[e[0] for e in EDGE])
+def test_edge_shapes(txl, case):
+    name, B, d, H, dh, L, M, dtype = case
+    w = 0.1 if dtype == "f32" else 0.05
+    cfg = synth.Config(name, B, d, H, dh, L, M, 1, 3, dtype, w, 4242)
+    _stream_case(txl, cfg, 3, np.arange(B))
+
+
+def test_ring_start_rotation(txl):
+    """A rotated physical ring (mem_start != 0) holding the same logical memory
+    gives the same result as the oracle on that logical memory."""
+    cfg = synth.Config("rot", 2, 128, 2, 64, 24, 100, 1, 3, "bf16", 0.05, 99)
+    _stream_case(txl, cfg, 3, np.arange(2), start=37)
+
+
+def test_deterministic(txl):
+    import torch
+    cfg = synth.get_config("c4", batch=2)
+    wl = synth.make_workload(cfg, n_segments=1)
+    a, _, _ = run_attn_stream(wl, 1)
+    b, _, _ = run_attn_stream(wl, 1)
+    assert np.array_equal(a[0], b[0])
+    _ = torch
+
+
+# ------------------------------------------------------- segment step
+def test_segment_step_single_layer_c4(txl):
+    cfg = synth.get_config("c4")
+    log(f"[case] segment_step c4 8 segments")
+    wl = synth.make_workload(cfg, n_segments=8)
+    outs, dl, start = run_segment_stream(wl, 8)
+    b_idx = np.array([0, 7])
+    o_outs, o_mems, start_o = oracle_stream(wl, 8, b_idx)
+    for s in range(8):
+        assert_close(outs[s][b_idx], o_outs[s], "bf16", f"segment {s}")
+    _check_ring(dl, wl, o_mems, start_o, start, b_idx)
+
+
+def test_segment_step_stack_small(txl):
+    """Two full layers (W_o, LayerNorm, ReLU FFN) on a small shape."""
+    cfg = synth.Config("stack2", 2, 128, 2, 64, 40, 72, 2, 3, "bf16", 0.02, 1234, d_inner=256)
+    log("[case] small stack")
+    wl = synth.make_workload(cfg)
+    outs, dl, start = run_segment_stream(wl, 3)
+    b_idx = np.arange(2)
+    o_outs, o_mems, start_o = oracle_stream(wl, 3, b_idx)
+    for s in range(3):
+        assert_close(outs[s][b_idx], o_outs[s], "bf16", f"segment {s}")
+    _check_ring(dl, wl, o_mems, start_o, start, b_idx, layer=0, exact=True)
+    _check_ring(dl, wl, o_mems, start_o, start, b_idx, layer=1, exact=False)
+
+
+def test_c5_stack_16_layers(txl):
+    cfg = synth.get_config("c5")
+    log("[case] c5 16-layer stack, 4 segments")
+    wl = synth.make_workload(cfg)
+    outs, dl, start = run_segment_stream(wl, 4)
+    b_idx = np.array([0])
+    o_outs, o_mems, start_o = oracle_stream(wl, 4, b_idx)
+    for s in range(4):
+        assert_close(outs[s][b_idx], o_outs[s], "bf16", f"segment {s}")
+    _check_ring(dl, wl, o_mems, start_o, start, b_idx, layer=0, exact=True)
+    _check_ring(dl, wl, o_mems, start_o, start, b_idx, layer=15, exact=False)

@@ -1,0 +1,173 @@
+"""Python binding of libtxl (relative-positional attention over a cached memory,
+Dai et al., Transformer-XL, Sec. 3.3) for MI355X / gfx950.
+
+Argument marshalling only: every function forwards to the C entry point of the
+same name in ``libtxl.so``.  Tensors are torch tensors that live on the GPU
+(torch is used for device memory and streams); each is passed as its data
+pointer, and the work is enqueued on torch's current HIP stream unless a
+stream is given.  There is no fallback: if the library is missing, importing
+this package raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+__all__ = [
+    "TXL_F32", "TXL_BF16", "TxlError", "AttnShape", "Layer", "lib", "lib_path",
+    "txl_abi_version", "txl_status_str", "txl_last_error", "txl_sinusoid_pos",
+    "txl_rel_proj_workspace_bytes", "txl_rel_proj", "txl_rel_attn_workspace_bytes",
+    "txl_rel_attn_fwd", "txl_mem_update", "txl_segment_workspace_bytes", "txl_segment_step",
+]
+
+TXL_F32 = 0
+TXL_BF16 = 1
+
+lib_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtxl.so")
+if not os.path.exists(lib_path):
+    raise ImportError(f"{lib_path} is missing: build it with "
+                      "`python -m transformer_xl_relative_attn_amd._build`")
+lib = ctypes.CDLL(lib_path)
+
+_vp = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_sz = ctypes.c_size_t
+
+
+class AttnShape(ctypes.Structure):
+    """txl_attn_shape_t."""
+    _fields_ = [("batch", _i32), ("seg_len", _i32), ("mem_len", _i32), ("d_model", _i32),
+                ("n_heads", _i32), ("d_head", _i32), ("d_pos", _i32), ("dtype", _i32),
+                ("scale", ctypes.c_float)]
+
+
+class Layer(ctypes.Structure):
+    """txl_layer_t (device pointers as integers; 0 = NULL)."""
+    _fields_ = [("W_q", _vp), ("W_kE", _vp), ("W_kR", _vp), ("W_v", _vp), ("u", _vp),
+                ("v", _vp), ("Rk", _vp), ("W_o", _vp), ("W_ff1", _vp), ("W_ff2", _vp),
+                ("mem", _vp)]
+
+
+def _sig(name, restype, argtypes):
+    f = getattr(lib, name)
+    f.restype = restype
+    f.argtypes = argtypes
+    return f
+
+
+_abi = _sig("txl_abi_version", ctypes.c_int, [])
+_status_str = _sig("txl_status_str", ctypes.c_char_p, [ctypes.c_int])
+_last_error = _sig("txl_last_error", ctypes.c_char_p, [])
+_sinusoid = _sig("txl_sinusoid_pos", ctypes.c_int, [_vp, _i32, _i32, _i32, _vp])
+_proj_ws = _sig("txl_rel_proj_workspace_bytes", _sz, [_i32, _i32, _i32, _i32, _i32])
+_proj = _sig("txl_rel_proj", ctypes.c_int,
+             [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _sz, _vp])
+_attn_ws = _sig("txl_rel_attn_workspace_bytes", _sz, [ctypes.POINTER(AttnShape)])
+_attn = _sig("txl_rel_attn_fwd", ctypes.c_int,
+             [ctypes.POINTER(AttnShape), _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+              _vp, _vp, _vp, _sz, _vp])
+_memup = _sig("txl_mem_update", ctypes.c_int,
+              [_vp, ctypes.POINTER(_i32), _vp, _i32, _i32, _i32, _i32, _i32, _vp])
+_seg_ws = _sig("txl_segment_workspace_bytes", _sz, [ctypes.POINTER(AttnShape), _i32, _i32])
+_seg = _sig("txl_segment_step", ctypes.c_int,
+            [ctypes.POINTER(AttnShape), _i32, _i32, ctypes.POINTER(Layer), _vp, _vp, _vp,
+             ctypes.POINTER(_i32), _vp, _sz, _vp])
+
+
+class TxlError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = _status_str(status).decode()
+        detail = _last_error().decode()
+        super().__init__(f"{where}: {msg} ({status}): {detail}")
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise TxlError(status, where)
+
+
+def _ptr(t) -> Optional[int]:
+    """Data pointer of a tensor (None -> NULL, int -> itself)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _nbytes(t) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def txl_abi_version() -> int:
+    return _abi()
+
+
+def txl_status_str(status: int) -> str:
+    return _status_str(status).decode()
+
+
+def txl_last_error() -> str:
+    return _last_error().decode()
+
+
+def txl_sinusoid_pos(R, n_pos: int, d_pos: int, dtype: int, stream=None):
+    _check(_sinusoid(_ptr(R), n_pos, d_pos, dtype, _stream(stream)), "txl_sinusoid_pos")
+
+
+def txl_rel_proj_workspace_bytes(n_pos, d_pos, n_heads, d_head, dtype) -> int:
+    return _proj_ws(n_pos, d_pos, n_heads, d_head, dtype)
+
+
+def txl_rel_proj(R, W_kR, Rk, n_pos, d_pos, n_heads, d_head, dtype, workspace=None, stream=None):
+    _check(_proj(_ptr(R), _ptr(W_kR), _ptr(Rk), n_pos, d_pos, n_heads, d_head, dtype,
+                 _ptr(workspace), _nbytes(workspace), _stream(stream)), "txl_rel_proj")
+
+
+def txl_rel_attn_workspace_bytes(shape: AttnShape) -> int:
+    return _attn_ws(ctypes.byref(shape))
+
+
+def txl_rel_attn_fwd(shape: AttnShape, h, mem, mem_start: int, W_q, W_kE, W_kR, W_v, u, v, R, Rk,
+                     out, workspace, stream=None):
+    _check(_attn(ctypes.byref(shape), _ptr(h), _ptr(mem), mem_start, _ptr(W_q), _ptr(W_kE),
+                 _ptr(W_kR), _ptr(W_v), _ptr(u), _ptr(v), _ptr(R), _ptr(Rk), _ptr(out),
+                 _ptr(workspace), _nbytes(workspace), _stream(stream)), "txl_rel_attn_fwd")
+
+
+def txl_mem_update(mem, mem_start: int, h, batch, mem_len, seg_len, d_model, dtype,
+                   stream=None) -> int:
+    """Returns the new mem_start."""
+    st = _i32(mem_start)
+    _check(_memup(_ptr(mem), ctypes.byref(st), _ptr(h), batch, mem_len, seg_len, d_model, dtype,
+                  _stream(stream)), "txl_mem_update")
+    return st.value
+
+
+def txl_segment_workspace_bytes(shape: AttnShape, n_layers: int, d_inner: int) -> int:
+    return _seg_ws(ctypes.byref(shape), n_layers, d_inner)
+
+
+def make_layer(W_q, W_kE, W_kR, W_v, u, v, mem, Rk=None, W_o=None, W_ff1=None, W_ff2=None) -> Layer:
+    return Layer(_ptr(W_q), _ptr(W_kE), _ptr(W_kR), _ptr(W_v), _ptr(u), _ptr(v), _ptr(Rk),
+                 _ptr(W_o), _ptr(W_ff1), _ptr(W_ff2), _ptr(mem))
+
+
+def txl_segment_step(shape: AttnShape, n_layers: int, d_inner: int, layers: Sequence[Layer], R,
+                     h_in, h_out, mem_start: int, workspace, stream=None) -> int:
+    """Returns the new mem_start."""
+    arr = (Layer * len(layers))(*layers)
+    st = _i32(mem_start)
+    _check(_seg(ctypes.byref(shape), n_layers, d_inner, arr, _ptr(R), _ptr(h_in), _ptr(h_out),
+                ctypes.byref(st), _ptr(workspace), _nbytes(workspace), _stream(stream)),
+           "txl_segment_step")
+    return st.value

@@ -1,0 +1,659 @@
+// libtxl C-ABI: argument validation, workspace planning and kernel dispatch.
+// Every check runs before anything is enqueued; on an error nothing is launched
+// and in/out arguments keep their values.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "txl_internal.h"
+
+namespace txl {
+namespace {
+
+thread_local std::string g_last_error;
+
+txl_status_t fail(txl_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+txl_status_t hip_status(int err, const char* where) {
+  if (err == 0) return TXL_OK;
+  return fail(TXL_ERR_HIP, "%s: %s", where, hipGetErrorString(static_cast<hipError_t>(err)));
+}
+
+#define TXL_TRY(expr)                                  \
+  do {                                                 \
+    txl_status_t _st = (expr);                         \
+    if (_st != TXL_OK) return _st;                     \
+  } while (0)
+
+#define TXL_HIP(expr, where)                           \
+  do {                                                 \
+    int _e = (expr);                                   \
+    if (_e != 0) return hip_status(_e, where);         \
+  } while (0)
+
+constexpr int64_t kMaxDim = 1 << 20;
+constexpr int kBf16Dp = 64;   // padded head width of the bf16 path
+constexpr int kBf16Dmax = 64;
+
+inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+inline int esize(int dtype) { return dtype == TXL_F32 ? 4 : 2; }
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+bool debug_sync() {
+  static const bool on = [] {
+    const char* e = getenv("TXL_DEBUG_SYNC");
+    return e && *e && *e != '0';
+  }();
+  return on;
+}
+
+txl_status_t after_launch(int err, const char* what, void* stream) {
+  if (err) return hip_status(err, what);
+  if (debug_sync()) {
+    int e = static_cast<int>(hipStreamSynchronize(static_cast<hipStream_t>(stream)));
+    if (e) return hip_status(e, what);
+  }
+  return TXL_OK;
+}
+
+// ---------------------------------------------------------------- planning
+struct Region {
+  size_t off = 0, bytes = 0;
+};
+
+struct AttnPlan {
+  int B, L, M, d, H, dh, dpos, dtype;
+  float scale;
+  int DP, Lp, Np, Pp, P;
+  int n_split, nqg;
+  bool pack_d, pack_pos;   // bf16 operands repacked to a K multiple of 64
+  int Kd, Kpos;            // reduction lengths seen by the GEMMs
+  Region q, k, v, rk, po, pml, ph, pmem, pwq, pwk, pwv, pwr, pr;
+  size_t total;
+};
+
+txl_status_t check_shape(const txl_attn_shape_t* s) {
+  if (!s) return fail(TXL_ERR_NULL_ARG, "shape is NULL");
+  if (s->dtype != TXL_F32 && s->dtype != TXL_BF16)
+    return fail(TXL_ERR_BAD_DTYPE, "dtype %d is not TXL_F32 or TXL_BF16", s->dtype);
+  if (s->batch < 1 || s->seg_len < 1 || s->mem_len < 0 || s->d_model < 1 || s->n_heads < 1 ||
+      s->d_head < 1 || s->d_pos < 1)
+    return fail(TXL_ERR_BAD_SHAPE,
+                "sizes out of range (batch=%d seg_len=%d mem_len=%d d_model=%d n_heads=%d "
+                "d_head=%d d_pos=%d)",
+                s->batch, s->seg_len, s->mem_len, s->d_model, s->n_heads, s->d_head, s->d_pos);
+  if (s->batch > kMaxDim || s->seg_len > kMaxDim || s->mem_len > kMaxDim ||
+      s->d_model > kMaxDim || s->n_heads > 4096 || s->d_head > 4096 || s->d_pos > kMaxDim)
+    return fail(TXL_ERR_BAD_SHAPE, "a size exceeds the supported range");
+  if (std::isnan(s->scale) || std::isinf(s->scale))
+    return fail(TXL_ERR_BAD_SHAPE, "scale is not finite");
+  if ((int64_t)s->mem_len + s->seg_len > INT32_MAX / 2)
+    return fail(TXL_ERR_BAD_SHAPE, "mem_len + seg_len too large");
+  if (s->dtype == TXL_BF16 && s->d_head > kBf16Dmax)
+    return fail(TXL_ERR_UNSUPPORTED, "bf16 path supports d_head <= %d (got %d)", kBf16Dmax,
+                s->d_head);
+  if (s->dtype == TXL_F32) {
+    // fp32 kernel keeps one query's scores in LDS
+    const int64_t lds = 4 * ((int64_t)s->mem_len + s->seg_len + 2 * s->d_head);
+    if (lds > 60 * 1024)
+      return fail(TXL_ERR_UNSUPPORTED, "fp32 path supports mem_len + seg_len <= ~15000");
+  }
+  return TXL_OK;
+}
+
+AttnPlan make_plan(const txl_attn_shape_t* s, bool compute_rk) {
+  AttnPlan p{};
+  p.B = s->batch;
+  p.L = s->seg_len;
+  p.M = s->mem_len;
+  p.d = s->d_model;
+  p.H = s->n_heads;
+  p.dh = s->d_head;
+  p.dpos = s->d_pos;
+  p.dtype = s->dtype;
+  p.scale = s->scale > 0 ? s->scale : 1.0f / std::sqrt((float)s->d_head);
+  p.P = p.M + p.L;
+  const bool bf = p.dtype == TXL_BF16;
+  p.DP = bf ? kBf16Dp : p.dh;
+  p.Lp = bf ? (int)round_up(p.L, 32) : p.L;
+  p.Np = bf ? (int)round_up(p.P, 32) : p.P;
+  p.Pp = p.Np;
+  p.nqg = (p.L + 127) / 128;
+  p.n_split = 1;
+  if (bf) {
+    const int64_t wgs = (int64_t)p.B * p.H * p.nqg;
+    const int nb_min = (p.M + std::min(p.L, 128) + 31) / 32;
+    int want = (int)((512 + wgs - 1) / wgs);
+    want = std::min(want, std::max(1, nb_min / 4));
+    p.n_split = std::max(1, std::min(want, 16));
+  }
+  p.pack_d = bf && (p.d % 64 != 0);
+  p.pack_pos = bf && compute_rk && (p.dpos % 64 != 0);
+  p.Kd = p.pack_d ? (int)round_up(p.d, 64) : p.d;
+  p.Kpos = p.pack_pos ? (int)round_up(p.dpos, 64) : p.dpos;
+  const size_t es = esize(p.dtype);
+  size_t off = 0;
+  auto take = [&](Region& r, size_t bytes) {
+    r.off = off;
+    r.bytes = bytes;
+    off = align256(off + bytes);
+  };
+  const size_t BH = (size_t)p.B * p.H;
+  take(p.q, BH * p.Lp * p.DP * 4);
+  take(p.k, BH * p.Np * p.DP * es);
+  take(p.v, BH * p.Np * p.DP * es);
+  take(p.rk, (size_t)p.H * p.Pp * p.DP * es);
+  if (p.n_split > 1) {
+    take(p.po, (size_t)p.n_split * BH * p.Lp * p.DP * 4);
+    take(p.pml, (size_t)p.n_split * BH * p.Lp * 2 * 4);
+  }
+  const size_t Hd = (size_t)p.H * p.dh;
+  if (p.pack_d) {
+    take(p.ph, (size_t)p.B * p.L * p.Kd * 2);
+    take(p.pmem, (size_t)p.B * p.M * p.Kd * 2);
+    take(p.pwq, Hd * p.Kd * 2);
+    take(p.pwk, Hd * p.Kd * 2);
+    take(p.pwv, Hd * p.Kd * 2);
+  }
+  if (p.pack_pos) {
+    take(p.pwr, Hd * p.Kpos * 2);
+    take(p.pr, (size_t)p.P * p.Kpos * 2);
+  }
+  p.total = off;
+  return p;
+}
+
+// Output maps ------------------------------------------------------------
+AxisMap axis(int32_t div, int64_t s1, int64_t s2) { return AxisMap{div, s1, s2}; }
+AxisMap axis_linear(int64_t s) { return AxisMap{INT32_MAX, 0, s}; }
+
+RowSrc src_plain(const void* p, int64_t ld, int32_t rows) {
+  RowSrc r{};
+  r.kind = ROW_PLAIN;
+  r.p0 = p;
+  r.ld = ld;
+  r.rows = rows;
+  return r;
+}
+RowSrc src_headpad(const void* w, int64_t ld, int32_t dh, int32_t dp) {
+  RowSrc r{};
+  r.kind = ROW_HEADPAD;
+  r.p0 = w;
+  r.ld = ld;
+  r.dh = dh;
+  r.dp = dp;
+  return r;
+}
+RowSrc src_htilde(const void* mem, const void* h, int64_t ld, int32_t np, int32_t M, int32_t L,
+                  int32_t start) {
+  RowSrc r{};
+  r.kind = ROW_HTILDE;
+  r.p0 = mem;
+  r.p1 = h;
+  r.ld = ld;
+  r.np = np;
+  r.M = M;
+  r.L = L;
+  r.start = start;
+  return r;
+}
+
+void add_problem(GemmGroup& g, int32_t M, int32_t N, int32_t K, const RowSrc& a, const RowSrc& b,
+                 const OutDst& o, int tile) {
+  GemmProblem& p = g.p[g.count++];
+  p.M = M;
+  p.N = N;
+  p.K = K;
+  p.tiles_m = (M + tile - 1) / tile;
+  p.tiles_n = (N + tile - 1) / tile;
+  p.tile_begin = g.total_tiles;
+  p.a = a;
+  p.b = b;
+  p.out = o;
+  g.total_tiles += p.tiles_m * p.tiles_n;
+}
+
+OutDst out_map(void* ptr, int dtype, int32_t mv, int32_t nv, AxisMap row, AxisMap col,
+               int flags = 0, const float* resid = nullptr) {
+  OutDst o{};
+  o.p = ptr;
+  o.dtype = dtype;
+  o.flags = flags;
+  o.m_valid = mv;
+  o.n_valid = nv;
+  o.row = row;
+  o.col = col;
+  o.resid = resid;
+  return o;
+}
+
+int launch_gemm(const GemmGroup& g, int dtype, void* stream) {
+  return dtype == TXL_BF16 ? launch_gemm_bf16(g, stream) : launch_gemm_f32(g, stream);
+}
+int gemm_tile(int dtype) { return dtype == TXL_BF16 ? 256 : 64; }
+
+// ----------------------------------------------------------- rel_attn core
+struct AttnPtrs {
+  const void *h, *mem, *W_q, *W_kE, *W_kR, *W_v, *u, *v, *R, *Rk;
+  int32_t mem_start;
+  void* out;
+};
+
+txl_status_t check_attn_ptrs(const txl_attn_shape_t* s, const AttnPtrs& a, bool need_ws,
+                             const void* ws) {
+  if (!a.h || !a.W_q || !a.W_kE || !a.W_v || !a.u || !a.v || !a.out)
+    return fail(TXL_ERR_NULL_ARG, "h, W_q, W_kE, W_v, u, v and out are required");
+  if (s->mem_len > 0 && !a.mem) return fail(TXL_ERR_NULL_ARG, "mem is NULL but mem_len > 0");
+  if (!a.Rk && (!a.W_kR || !a.R))
+    return fail(TXL_ERR_NULL_ARG, "either Rk or both W_kR and R are required");
+  if (need_ws && !ws) return fail(TXL_ERR_NULL_ARG, "workspace is NULL");
+  if (s->mem_len > 0 ? (a.mem_start < 0 || a.mem_start >= s->mem_len) : a.mem_start != 0)
+    return fail(TXL_ERR_BAD_SHAPE, "mem_start %d outside [0, mem_len=%d)", a.mem_start,
+                s->mem_len);
+  if (s->dtype == TXL_BF16) {
+    const void* ptrs[] = {a.h, a.mem, a.W_q, a.W_kE, a.W_kR, a.W_v, a.R, a.Rk, a.out};
+    for (const void* q : ptrs)
+      if (q && !aligned16(q))
+        return fail(TXL_ERR_UNSUPPORTED, "bf16 path needs 16-byte aligned tensor pointers");
+  }
+  return TXL_OK;
+}
+
+// Enqueue the projections and the fused attention of one layer.  If mem_update
+// is set the ring update (reading `h`) is enqueued between them.
+txl_status_t run_rel_attn(const AttnPlan& p, const AttnPtrs& a, char* ws, void* stream,
+                          void* mem_upd, int32_t* new_start) {
+  const bool bf = p.dtype == TXL_BF16;
+  const int dt = p.dtype;
+  const int es = esize(dt);
+  const int32_t Hd = p.H * p.dh;
+  char* q = ws + p.q.off;
+  char* k = ws + p.k.off;
+  char* v = ws + p.v.off;
+  char* rk = ws + p.rk.off;
+
+  const void* h = a.h;
+  const void* mem = a.mem;
+  const void *Wq = a.W_q, *WkE = a.W_kE, *Wv = a.W_v, *WkR = a.W_kR, *R = a.R;
+  int64_t ld_d = p.d, ld_pos = p.dpos;
+  if (p.pack_d) {
+    TXL_HIP(launch_pack_rows(ws + p.ph.off, p.Kd, h, p.d, (int64_t)p.B * p.L, p.d, dt, stream),
+            "pack h");
+    if (p.M > 0)
+      TXL_HIP(launch_pack_rows(ws + p.pmem.off, p.Kd, mem, p.d, (int64_t)p.B * p.M, p.d, dt,
+                               stream),
+              "pack mem");
+    TXL_HIP(launch_pack_rows(ws + p.pwq.off, p.Kd, Wq, p.d, Hd, p.d, dt, stream), "pack W_q");
+    TXL_HIP(launch_pack_rows(ws + p.pwk.off, p.Kd, WkE, p.d, Hd, p.d, dt, stream), "pack W_kE");
+    TXL_HIP(launch_pack_rows(ws + p.pwv.off, p.Kd, Wv, p.d, Hd, p.d, dt, stream), "pack W_v");
+    h = ws + p.ph.off;
+    mem = ws + p.pmem.off;
+    Wq = ws + p.pwq.off;
+    WkE = ws + p.pwk.off;
+    Wv = ws + p.pwv.off;
+    ld_d = p.Kd;
+  }
+  if (!a.Rk && p.pack_pos) {
+    TXL_HIP(launch_pack_rows(ws + p.pwr.off, p.Kpos, WkR, p.dpos, Hd, p.dpos, dt, stream),
+            "pack W_kR");
+    TXL_HIP(launch_pack_rows(ws + p.pr.off, p.Kpos, R, p.dpos, p.P, p.dpos, dt, stream),
+            "pack R");
+    WkR = ws + p.pwr.off;
+    R = ws + p.pr.off;
+    ld_pos = p.Kpos;
+  }
+
+  const int tile = gemm_tile(dt);
+  const int64_t DP = p.DP;
+  GemmGroup g{};
+  // q = h W_q^T -> fp32 [B][H][Lp][DP]
+  add_problem(g, p.B * p.Lp, p.H * p.DP, p.Kd,
+              src_htilde(nullptr, h, ld_d, p.Lp, 0, p.L, 0), src_headpad(Wq, ld_d, p.dh, p.DP),
+              out_map(q, TXL_F32, p.B * p.Lp, p.H * p.DP,
+                      axis(p.Lp, (int64_t)p.H * p.Lp * DP, DP), axis(p.DP, (int64_t)p.Lp * DP, 1)),
+              tile);
+  // k = h~ W_kE^T -> [B][H][Np][DP]
+  const RowSrc ht = src_htilde(mem, h, ld_d, p.Np, p.M, p.L, a.mem_start);
+  add_problem(g, p.B * p.Np, p.H * p.DP, p.Kd, ht, src_headpad(WkE, ld_d, p.dh, p.DP),
+              out_map(k, dt, p.B * p.Np, p.H * p.DP, axis(p.Np, (int64_t)p.H * p.Np * DP, DP),
+                      axis(p.DP, (int64_t)p.Np * DP, 1)),
+              tile);
+  if (bf) {
+    // val^T = W_v h~^T -> [B][H][DP][Np]
+    add_problem(g, p.H * p.DP, p.B * p.Np, p.Kd, src_headpad(Wv, ld_d, p.dh, p.DP), ht,
+                out_map(v, dt, p.H * p.DP, p.B * p.Np, axis(p.DP, DP * p.Np, p.Np),
+                        axis(p.Np, (int64_t)p.H * DP * p.Np, 1)),
+                tile);
+  } else {
+    add_problem(g, p.B * p.Np, p.H * p.DP, p.Kd, ht, src_headpad(Wv, ld_d, p.dh, p.DP),
+                out_map(v, dt, p.B * p.Np, p.H * p.DP, axis(p.Np, (int64_t)p.H * p.Np * DP, DP),
+                        axis(p.DP, (int64_t)p.Np * DP, 1)),
+                tile);
+  }
+  if (!a.Rk) {
+    // Rk = R W_kR^T -> [H][Pp][DP]
+    add_problem(g, p.Pp, p.H * p.DP, p.Kpos, src_plain(R, ld_pos, p.P),
+                src_headpad(WkR, ld_pos, p.dh, p.DP),
+                out_map(rk, dt, p.Pp, p.H * p.DP, axis_linear(DP), axis(p.DP, (int64_t)p.Pp * DP, 1)),
+                tile);
+  } else {
+    TXL_HIP(launch_repack_rk(a.Rk, rk, p.P, p.Pp, p.H, p.dh, p.DP, dt, stream), "repack Rk");
+  }
+  TXL_TRY(after_launch(launch_gemm(g, dt, stream), "projection GEMMs", stream));
+
+  if (mem_upd) {
+    TXL_TRY(after_launch(launch_mem_update(mem_upd, a.mem_start, a.h, p.B, p.M, p.L, p.d, dt,
+                                           stream),
+                         "memory update", stream));
+    *new_start = (p.M == 0) ? 0 : (p.L < p.M ? (a.mem_start + p.L) % p.M : 0);
+  }
+
+  AttnArgs aa{};
+  aa.B = p.B;
+  aa.H = p.H;
+  aa.L = p.L;
+  aa.M = p.M;
+  aa.dh = p.dh;
+  aa.Lp = p.Lp;
+  aa.Np = p.Np;
+  aa.Pp = p.Pp;
+  aa.n_split = p.n_split;
+  aa.c_scale = bf ? p.scale * 1.4426950408889634f : p.scale;
+  aa.q = reinterpret_cast<const float*>(q);
+  aa.k = k;
+  aa.vt = v;
+  aa.rk = rk;
+  aa.u = a.u;
+  aa.v = a.v;
+  aa.out = a.out;
+  aa.part_o = p.n_split > 1 ? reinterpret_cast<float*>(ws + p.po.off) : nullptr;
+  aa.part_ml = p.n_split > 1 ? reinterpret_cast<float*>(ws + p.pml.off) : nullptr;
+  aa.dtype = dt;
+  int e = bf ? launch_attn_bf16(aa, stream) : launch_attn_f32(aa, stream);
+  return after_launch(e, "attention kernel", stream);
+}
+
+// --------------------------------------------------------- segment planning
+struct SegPlan {
+  AttnPlan attn;
+  bool any_full;
+  Region a, x32a, x32b, xlo_a, xlo_b, t32, o32, olo, hid;
+  size_t total;
+};
+
+SegPlan make_seg_plan(const txl_attn_shape_t* s, int32_t d_inner, bool any_full) {
+  SegPlan sp{};
+  sp.attn = make_plan(s, true);
+  sp.any_full = any_full;
+  size_t off = align256(sp.attn.total);
+  auto take = [&](Region& r, size_t bytes) {
+    r.off = off;
+    r.bytes = bytes;
+    off = align256(off + bytes);
+  };
+  const size_t rows = (size_t)s->batch * s->seg_len;
+  const size_t es = esize(s->dtype);
+  const size_t Hd = (size_t)s->n_heads * s->d_head;
+  take(sp.a, rows * Hd * es);
+  take(sp.xlo_a, rows * std::max<size_t>(Hd, s->d_model) * es);
+  take(sp.xlo_b, rows * std::max<size_t>(Hd, s->d_model) * es);
+  if (any_full) {
+    take(sp.x32a, rows * s->d_model * 4);
+    take(sp.x32b, rows * s->d_model * 4);
+    take(sp.t32, rows * s->d_model * 4);
+    take(sp.o32, rows * s->d_model * 4);
+    take(sp.olo, rows * s->d_model * es);
+    take(sp.hid, rows * (size_t)std::max(d_inner, 1) * es);
+  }
+  sp.total = off;
+  return sp;
+}
+
+}  // namespace
+}  // namespace txl
+
+using namespace txl;
+
+extern "C" {
+
+int txl_abi_version(void) { return TXL_ABI_VERSION; }
+
+const char* txl_status_str(txl_status_t st) {
+  switch (st) {
+    case TXL_OK: return "ok";
+    case TXL_ERR_NULL_ARG: return "null argument";
+    case TXL_ERR_BAD_SHAPE: return "bad shape";
+    case TXL_ERR_BAD_DTYPE: return "bad dtype";
+    case TXL_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case TXL_ERR_UNSUPPORTED: return "unsupported";
+    case TXL_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* txl_last_error(void) { return g_last_error.c_str(); }
+
+txl_status_t txl_sinusoid_pos(void* R, int32_t n_pos, int32_t d_pos, int32_t dtype, void* stream) {
+  if (!R) return fail(TXL_ERR_NULL_ARG, "R is NULL");
+  if (dtype != TXL_F32 && dtype != TXL_BF16) return fail(TXL_ERR_BAD_DTYPE, "bad dtype %d", dtype);
+  if (n_pos < 1 || d_pos < 1 || n_pos > kMaxDim || d_pos > kMaxDim)
+    return fail(TXL_ERR_BAD_SHAPE, "n_pos=%d d_pos=%d out of range", n_pos, d_pos);
+  return after_launch(launch_sinusoid(R, n_pos, d_pos, dtype, stream), "sinusoid", stream);
+}
+
+size_t txl_rel_proj_workspace_bytes(int32_t n_pos, int32_t d_pos, int32_t n_heads, int32_t d_head,
+                                    int32_t dtype) {
+  if (dtype != TXL_BF16 || d_pos % 64 == 0 || n_pos < 1 || d_pos < 1 || n_heads < 1 || d_head < 1)
+    return 0;
+  const int64_t Kp = round_up(d_pos, 64);
+  return align256((size_t)n_pos * Kp * 2) + align256((size_t)n_heads * d_head * Kp * 2);
+}
+
+txl_status_t txl_rel_proj(const void* R, const void* W_kR, void* Rk, int32_t n_pos, int32_t d_pos,
+                          int32_t n_heads, int32_t d_head, int32_t dtype, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  if (!R || !W_kR || !Rk) return fail(TXL_ERR_NULL_ARG, "R, W_kR and Rk are required");
+  if (dtype != TXL_F32 && dtype != TXL_BF16) return fail(TXL_ERR_BAD_DTYPE, "bad dtype %d", dtype);
+  if (n_pos < 1 || d_pos < 1 || n_heads < 1 || d_head < 1 || n_pos > kMaxDim || d_pos > kMaxDim ||
+      (int64_t)n_heads * d_head > kMaxDim)
+    return fail(TXL_ERR_BAD_SHAPE, "sizes out of range");
+  const size_t need = txl_rel_proj_workspace_bytes(n_pos, d_pos, n_heads, d_head, dtype);
+  if (need && !workspace) return fail(TXL_ERR_NULL_ARG, "workspace is NULL");
+  if (workspace_bytes < need)
+    return fail(TXL_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes, need);
+  if (dtype == TXL_BF16 && (!aligned16(R) || !aligned16(W_kR) || !aligned16(Rk)))
+    return fail(TXL_ERR_UNSUPPORTED, "bf16 path needs 16-byte aligned tensor pointers");
+  const int32_t Hd = n_heads * d_head;
+  const void* Rs = R;
+  const void* Ws = W_kR;
+  int64_t ld = d_pos;
+  if (need) {
+    const int64_t Kp = round_up(d_pos, 64);
+    char* ws = static_cast<char*>(workspace);
+    char* pr = ws;
+    char* pw = ws + align256((size_t)n_pos * Kp * 2);
+    TXL_HIP(launch_pack_rows(pr, Kp, R, d_pos, n_pos, d_pos, dtype, stream), "pack R");
+    TXL_HIP(launch_pack_rows(pw, Kp, W_kR, d_pos, Hd, d_pos, dtype, stream), "pack W_kR");
+    Rs = pr;
+    Ws = pw;
+    ld = Kp;
+  }
+  GemmGroup g{};
+  add_problem(g, n_pos, Hd, (int32_t)ld, src_plain(Rs, ld, n_pos), src_plain(Ws, ld, Hd),
+              out_map(Rk, dtype, n_pos, Hd, axis_linear(Hd), axis_linear(1)), gemm_tile(dtype));
+  return after_launch(launch_gemm(g, dtype, stream), "rel_proj GEMM", stream);
+}
+
+size_t txl_rel_attn_workspace_bytes(const txl_attn_shape_t* shape) {
+  if (check_shape(shape) != TXL_OK) return 0;
+  return make_plan(shape, true).total;
+}
+
+txl_status_t txl_rel_attn_fwd(const txl_attn_shape_t* shape, const void* h, const void* mem,
+                              int32_t mem_start, const void* W_q, const void* W_kE,
+                              const void* W_kR, const void* W_v, const void* u, const void* v,
+                              const void* R, const void* Rk, void* out, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  TXL_TRY(check_shape(shape));
+  AttnPtrs a{h, mem, W_q, W_kE, W_kR, W_v, u, v, R, Rk, mem_start, out};
+  TXL_TRY(check_attn_ptrs(shape, a, true, workspace));
+  const AttnPlan p = make_plan(shape, Rk == nullptr);
+  const size_t need = make_plan(shape, true).total;
+  if (workspace_bytes < need)
+    return fail(TXL_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes, need);
+  return run_rel_attn(p, a, static_cast<char*>(workspace), stream, nullptr, nullptr);
+}
+
+txl_status_t txl_mem_update(void* mem, int32_t* mem_start, const void* h, int32_t batch,
+                            int32_t mem_len, int32_t seg_len, int32_t d_model, int32_t dtype,
+                            void* stream) {
+  if (!mem_start || !h || (mem_len > 0 && !mem))
+    return fail(TXL_ERR_NULL_ARG, "mem, mem_start and h are required");
+  if (dtype != TXL_F32 && dtype != TXL_BF16) return fail(TXL_ERR_BAD_DTYPE, "bad dtype %d", dtype);
+  if (batch < 1 || mem_len < 0 || seg_len < 1 || d_model < 1 || batch > kMaxDim ||
+      mem_len > kMaxDim || seg_len > kMaxDim || d_model > kMaxDim)
+    return fail(TXL_ERR_BAD_SHAPE, "sizes out of range");
+  const int32_t st = *mem_start;
+  if (mem_len > 0 ? (st < 0 || st >= mem_len) : st != 0)
+    return fail(TXL_ERR_BAD_SHAPE, "mem_start %d outside [0, mem_len=%d)", st, mem_len);
+  if (mem_len == 0) return TXL_OK;
+  TXL_TRY(after_launch(launch_mem_update(mem, st, h, batch, mem_len, seg_len, d_model, dtype,
+                                         stream),
+                       "memory update", stream));
+  *mem_start = seg_len < mem_len ? (st + seg_len) % mem_len : 0;
+  return TXL_OK;
+}
+
+size_t txl_segment_workspace_bytes(const txl_attn_shape_t* shape, int32_t n_layers,
+                                   int32_t d_inner) {
+  if (check_shape(shape) != TXL_OK || n_layers < 1) return 0;
+  return make_seg_plan(shape, d_inner, d_inner > 0).total;
+}
+
+txl_status_t txl_segment_step(const txl_attn_shape_t* shape, int32_t n_layers, int32_t d_inner,
+                              const txl_layer_t* layers, const void* R, const void* h_in,
+                              void* h_out, int32_t* mem_start, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  TXL_TRY(check_shape(shape));
+  if (n_layers < 1 || n_layers > 4096) return fail(TXL_ERR_BAD_SHAPE, "n_layers=%d", n_layers);
+  if (!layers || !h_in || !h_out || !mem_start || !workspace)
+    return fail(TXL_ERR_NULL_ARG, "layers, h_in, h_out, mem_start and workspace are required");
+  const int32_t start = *mem_start;
+  const int32_t d = shape->d_model, Hd = shape->n_heads * shape->d_head;
+  bool any_full = false;
+  for (int n = 0; n < n_layers; ++n) {
+    const txl_layer_t& ly = layers[n];
+    AttnPtrs a{h_in, ly.mem, ly.W_q, ly.W_kE, ly.W_kR, ly.W_v, ly.u, ly.v, R, ly.Rk, start, h_out};
+    txl_status_t st = check_attn_ptrs(shape, a, false, workspace);
+    if (st != TXL_OK) {
+      g_last_error = "layer " + std::to_string(n) + ": " + g_last_error;
+      return st;
+    }
+    if (ly.W_o) {
+      any_full = true;
+      if (!ly.W_ff1 || !ly.W_ff2)
+        return fail(TXL_ERR_NULL_ARG, "layer %d: W_ff1 and W_ff2 are required with W_o", n);
+      if (d_inner < 1 || d_inner > kMaxDim)
+        return fail(TXL_ERR_BAD_SHAPE, "d_inner=%d out of range", d_inner);
+      if (shape->dtype == TXL_BF16 &&
+          (!aligned16(ly.W_o) || !aligned16(ly.W_ff1) || !aligned16(ly.W_ff2)))
+        return fail(TXL_ERR_UNSUPPORTED, "bf16 path needs 16-byte aligned tensor pointers");
+      if (shape->dtype == TXL_BF16 && (Hd % 64 != 0 || d % 64 != 0 || d_inner % 64 != 0))
+        return fail(TXL_ERR_UNSUPPORTED,
+                    "bf16 full layers need H*d_head, d_model and d_inner multiples of 64");
+    } else if (n + 1 < n_layers && Hd != d) {
+      return fail(TXL_ERR_BAD_SHAPE,
+                  "layer %d has no W_o: H*d_head (%d) must equal d_model (%d) to feed layer %d",
+                  n, Hd, d, n + 1);
+    }
+  }
+  const SegPlan sp = make_seg_plan(shape, d_inner, any_full);
+  if (workspace_bytes < sp.total)
+    return fail(TXL_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes,
+                sp.total);
+
+  char* ws = static_cast<char*>(workspace);
+  const int dt = shape->dtype;
+  const int32_t rows = shape->batch * shape->seg_len;
+  const int tile = gemm_tile(dt);
+  const void* x_lo = h_in;        // current layer input (storage dtype)
+  float* x32 = nullptr;           // fp32 residual copy of x_lo (full layers)
+  char* lo_buf[2] = {ws + sp.xlo_a.off, ws + sp.xlo_b.off};
+  float* f32_buf[2] = {reinterpret_cast<float*>(ws + sp.x32a.off),
+                       reinterpret_cast<float*>(ws + sp.x32b.off)};
+  int pp = 0;
+  int32_t new_start = start;
+  for (int n = 0; n < n_layers; ++n) {
+    const txl_layer_t& ly = layers[n];
+    const bool last = n + 1 == n_layers;
+    const bool full = ly.W_o != nullptr;
+    if (full && !x32) {
+      x32 = f32_buf[pp];
+      TXL_HIP(launch_cast_f32(x_lo, x32, (int64_t)rows * d, dt, stream), "cast residual");
+    }
+    void* a_out = (!full && last) ? h_out : (full ? ws + sp.a.off : lo_buf[pp ^ 1]);
+    AttnPtrs a{x_lo, ly.mem, ly.W_q, ly.W_kE, ly.W_kR, ly.W_v, ly.u, ly.v, R, ly.Rk, start, a_out};
+    const AttnPlan p = make_plan(shape, ly.Rk == nullptr);
+    TXL_TRY(run_rel_attn(p, a, ws, stream, ly.mem, &new_start));
+    if (!full) {
+      x_lo = a_out;
+      x32 = nullptr;
+      pp ^= 1;
+      continue;
+    }
+    float* t32 = reinterpret_cast<float*>(ws + sp.t32.off);
+    float* o32 = reinterpret_cast<float*>(ws + sp.o32.off);
+    void* olo = ws + sp.olo.off;
+    void* hid = ws + sp.hid.off;
+    // t32 = a W_o^T + x  (fp32)
+    {
+      GemmGroup g{};
+      add_problem(g, rows, d, Hd, src_plain(ws + sp.a.off, Hd, rows), src_plain(ly.W_o, Hd, d),
+                  out_map(t32, TXL_F32, rows, d, axis_linear(d), axis_linear(1), EPI_RESID, x32),
+                  tile);
+      TXL_TRY(after_launch(launch_gemm(g, dt, stream), "W_o GEMM", stream));
+    }
+    TXL_TRY(after_launch(launch_layernorm(t32, o32, olo, rows, d, dt, 1e-5f, stream), "LN1",
+                         stream));
+    {
+      GemmGroup g{};
+      add_problem(g, rows, d_inner, d, src_plain(olo, d, rows), src_plain(ly.W_ff1, d, d_inner),
+                  out_map(hid, dt, rows, d_inner, axis_linear(d_inner), axis_linear(1), EPI_RELU),
+                  tile);
+      TXL_TRY(after_launch(launch_gemm(g, dt, stream), "FFN1 GEMM", stream));
+    }
+    {
+      GemmGroup g{};
+      add_problem(g, rows, d, d_inner, src_plain(hid, d_inner, rows),
+                  src_plain(ly.W_ff2, d_inner, d),
+                  out_map(t32, TXL_F32, rows, d, axis_linear(d), axis_linear(1), EPI_RESID, o32),
+                  tile);
+      TXL_TRY(after_launch(launch_gemm(g, dt, stream), "FFN2 GEMM", stream));
+    }
+    float* y32 = f32_buf[pp ^ 1];
+    void* ylo = last ? h_out : lo_buf[pp ^ 1];
+    TXL_TRY(after_launch(launch_layernorm(t32, y32, ylo, rows, d, dt, 1e-5f, stream), "LN2",
+                         stream));
+    x_lo = ylo;
+    x32 = y32;
+    pp ^= 1;
+  }
+  *mem_start = new_start;
+  return TXL_OK;
+}
+
+}  // extern "C"

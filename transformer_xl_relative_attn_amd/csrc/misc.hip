@@ -1,0 +1,177 @@
+// Memory-bound helpers of the segment step: the sinusoid table R, the memory
+// ring update, operand packing, LayerNorm and small casts.
+#include "dev_common.h"
+
+namespace txl {
+
+namespace {
+
+// R[delta][2k] = sin(delta / 10000^(2k/d)), R[delta][2k+1] = cos(same):
+// Transformer-XL Sec. 3.3 takes R to be Vaswani et al.'s sinusoid matrix.
+// Evaluated in fp64, rounded once to the storage dtype.
+__global__ void sinusoid_kernel(void* R, int32_t n_pos, int32_t d, int32_t dtype) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)n_pos * d) return;
+  const int32_t pos = idx / d, c = idx % d;
+  const int32_t k2 = c & ~1;
+  const double inv = pow(10000.0, -(double)k2 / (double)d);
+  const double ang = (double)pos * inv;
+  const double val = (c & 1) ? cos(ang) : sin(ang);
+  store_from_f32(R, idx, (float)val, dtype);
+}
+
+// Ring update (Transformer-XL Sec. 3.2, memory of the M most recent states):
+// slot (start + t) mod M <- h row t for t < L (case L < M), or slot p <- h row
+// L - M + p (case L >= M, start then 0).  Copies 16-byte words when aligned.
+__global__ void mem_update_kernel(char* mem, int32_t start, const char* h, int32_t B, int32_t M,
+                                  int32_t L, int64_t row_bytes, int32_t vec) {
+  const int32_t n_rows = min(L, M);
+  const int64_t words = row_bytes / vec;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)B * n_rows * words) return;
+  const int64_t w = idx % words;
+  const int64_t rt = idx / words;
+  const int32_t t = rt % n_rows;
+  const int32_t b = rt / n_rows;
+  int32_t slot, src;
+  if (L < M) {
+    slot = (start + t) % M;
+    src = t;
+  } else {
+    slot = t;
+    src = L - M + t;
+  }
+  char* dst = mem + ((int64_t)b * M + slot) * row_bytes + w * vec;
+  const char* s = h + ((int64_t)b * L + src) * row_bytes + w * vec;
+  if (vec == 16)
+    *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(s);
+  else if (vec == 4)
+    *reinterpret_cast<uint32_t*>(dst) = *reinterpret_cast<const uint32_t*>(s);
+  else
+    *reinterpret_cast<uint16_t*>(dst) = *reinterpret_cast<const uint16_t*>(s);
+}
+
+// dst[r][c] = src[r][c] for c < cols, 0 for cols <= c < ld_dst.
+__global__ void pack_rows_kernel(uint16_t* dst, int64_t ld_dst, const uint16_t* src, int64_t ld_src,
+                                 int64_t rows, int32_t cols) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= rows * ld_dst) return;
+  const int64_t r = idx / ld_dst, c = idx % ld_dst;
+  dst[idx] = c < cols ? src[r * ld_src + c] : uint16_t(0);
+}
+
+// LayerNorm over rows of length d (no affine parameters), one workgroup per
+// row, fp32 statistics; writes fp32 and, if y_lo is set, a copy in lo_dtype.
+__global__ __launch_bounds__(256) void layernorm_kernel(const float* x, float* y, void* y_lo,
+                                                        int32_t d, int32_t lo_dtype, float eps) {
+  const int64_t row = blockIdx.x;
+  const float* xr = x + row * d;
+  __shared__ float red[2][256];
+  float s = 0.0f, s2 = 0.0f;
+  for (int c = threadIdx.x; c < d; c += 256) {
+    float v = xr[c];
+    s += v;
+  }
+  red[0][threadIdx.x] = s;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (threadIdx.x < w) red[0][threadIdx.x] += red[0][threadIdx.x + w];
+    __syncthreads();
+  }
+  const float mean = red[0][0] / d;
+  for (int c = threadIdx.x; c < d; c += 256) {
+    float v = xr[c] - mean;
+    s2 += v * v;
+  }
+  red[1][threadIdx.x] = s2;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (threadIdx.x < w) red[1][threadIdx.x] += red[1][threadIdx.x + w];
+    __syncthreads();
+  }
+  const float rstd = rsqrtf(red[1][0] / d + eps);
+  for (int c = threadIdx.x; c < d; c += 256) {
+    const float v = (xr[c] - mean) * rstd;
+    y[row * d + c] = v;
+    if (y_lo) store_from_f32(y_lo, row * d + c, v, lo_dtype);
+  }
+}
+
+__global__ void cast_f32_kernel(const void* src, float* dst, int64_t n, int32_t dtype) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx < n) dst[idx] = load_as_f32(src, idx, dtype);
+}
+
+// Public Rk layout [P][H][dh] -> workspace layout [H][Pp][dp] (zero padded).
+__global__ void repack_rk_kernel(const void* src, void* dst, int32_t P, int32_t Pp, int32_t H,
+                                 int32_t dh, int32_t dp, int32_t dtype) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)H * Pp * dp) return;
+  const int32_t c = idx % dp;
+  const int64_t t = idx / dp;
+  const int32_t p = t % Pp;
+  const int32_t h = t / Pp;
+  float x = 0.0f;
+  if (p < P && c < dh) x = load_as_f32(src, ((int64_t)p * H + h) * dh + c, dtype);
+  store_from_f32(dst, idx, x, dtype);
+}
+
+inline dim3 grid1d(int64_t n) { return dim3((unsigned)((n + 255) / 256)); }
+
+}  // namespace
+
+int launch_sinusoid(void* R, int32_t n_pos, int32_t d_pos, int32_t dtype, void* stream) {
+  const int64_t n = (int64_t)n_pos * d_pos;
+  hipLaunchKernelGGL(sinusoid_kernel, grid1d(n), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     R, n_pos, d_pos, dtype);
+  return static_cast<int>(hipGetLastError());
+}
+
+int launch_mem_update(void* mem, int32_t start, const void* h, int32_t B, int32_t M, int32_t L,
+                      int32_t d, int32_t dtype, void* stream) {
+  if (M == 0) return 0;
+  const int esize = dtype == TXL_F32 ? 4 : 2;
+  const int64_t row_bytes = (int64_t)d * esize;
+  const uintptr_t align = reinterpret_cast<uintptr_t>(mem) | reinterpret_cast<uintptr_t>(h) |
+                          static_cast<uintptr_t>(row_bytes);
+  const int vec = (align % 16 == 0) ? 16 : (align % 4 == 0) ? 4 : 2;
+  const int64_t n = (int64_t)B * (L < M ? L : M) * (row_bytes / vec);
+  hipLaunchKernelGGL(mem_update_kernel, grid1d(n), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<char*>(mem), start, static_cast<const char*>(h), B, M, L,
+                     row_bytes, vec);
+  return static_cast<int>(hipGetLastError());
+}
+
+int launch_pack_rows(void* dst, int64_t ld_dst, const void* src, int64_t ld_src, int64_t rows,
+                     int32_t cols, int32_t dtype, void* stream) {
+  (void)dtype;  // bf16 only
+  const int64_t n = rows * ld_dst;
+  if (n == 0) return 0;
+  hipLaunchKernelGGL(pack_rows_kernel, grid1d(n), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<uint16_t*>(dst), ld_dst, static_cast<const uint16_t*>(src),
+                     ld_src, rows, cols);
+  return static_cast<int>(hipGetLastError());
+}
+
+int launch_layernorm(const float* x, float* y_f32, void* y_lo, int32_t rows, int32_t d,
+                     int32_t lo_dtype, float eps, void* stream) {
+  hipLaunchKernelGGL(layernorm_kernel, dim3(rows), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     x, y_f32, y_lo, d, lo_dtype, eps);
+  return static_cast<int>(hipGetLastError());
+}
+
+int launch_cast_f32(const void* src, float* dst, int64_t n, int32_t dtype, void* stream) {
+  hipLaunchKernelGGL(cast_f32_kernel, grid1d(n), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     src, dst, n, dtype);
+  return static_cast<int>(hipGetLastError());
+}
+
+int launch_repack_rk(const void* rk_pub, void* rk_ws, int32_t P, int32_t Pp, int32_t H,
+                     int32_t dh, int32_t dp, int32_t dtype, void* stream) {
+  const int64_t n = (int64_t)H * Pp * dp;
+  hipLaunchKernelGGL(repack_rk_kernel, grid1d(n), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     rk_pub, rk_ws, P, Pp, H, dh, dp, dtype);
+  return static_cast<int>(hipGetLastError());
+}
+
+}  // namespace txl

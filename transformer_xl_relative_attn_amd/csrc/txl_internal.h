@@ -1,0 +1,106 @@
+// Internal declarations shared by the libtxl translation units (not part of the ABI).
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "txl.h"
+
+namespace txl {
+
+// ---------------------------------------------------------------------------
+// Operand row maps.  A GEMM operand is a set of K-contiguous rows; the kernel
+// asks a RowSrc for the address of virtual row `v` (or NULL = a row of zeros).
+//   ROW_PLAIN   v < rows ? p0 + v*ld : zero
+//   ROW_HEADPAD v = head*dp + c;  c < dh ? p0 + (head*dh + c)*ld : zero
+//               (weight rows of one head padded from dh to dp columns)
+//   ROW_HTILDE  v = b*np + r;  r < M   -> memory ring row (start + r) mod M of batch b
+//                              r < M+L -> segment row r - M of batch b
+//                              else    -> zero
+//               (the extended context [memory ; segment] of Sec. 3.2, gathered in
+//               place: never materialised)
+// ---------------------------------------------------------------------------
+enum RowMapKind : int32_t { ROW_PLAIN = 0, ROW_HEADPAD = 1, ROW_HTILDE = 2 };
+
+struct RowSrc {
+  int32_t kind;
+  int32_t rows;    // PLAIN: valid rows
+  int32_t dh, dp;  // HEADPAD
+  int32_t np, M, L, start;  // HTILDE
+  int64_t ld;      // elements between consecutive source rows
+  const void* p0;  // PLAIN/HEADPAD base, HTILDE memory base
+  const void* p1;  // HTILDE segment base
+};
+
+// Output address of element (m, n) = rowoff(m) + coloff(n), with
+//   off(x) = (x / div) * s1 + (x % div) * s2.
+// Covers row-major stores, head-split stores [b][head][r][c] and transposed
+// head-split stores [b][head][c][r].
+struct AxisMap {
+  int32_t div;
+  int64_t s1, s2;
+};
+
+enum EpiFlags : int32_t { EPI_RELU = 1, EPI_RESID = 2 };
+
+struct OutDst {
+  void* p;
+  int32_t dtype;         // TXL_F32 / TXL_BF16
+  int32_t flags;         // EpiFlags
+  int32_t m_valid, n_valid;  // store only m < m_valid, n < n_valid
+  AxisMap row, col;
+  const float* resid;    // EPI_RESID: out += resid[rowoff + coloff] (same map)
+};
+
+struct GemmProblem {
+  // C[m][n] = sum_k A(m,k) * B(n,k),  m < M, n < N
+  int32_t M, N, K;
+  int32_t tiles_m, tiles_n;
+  int32_t tile_begin;    // first tile id of this problem in a grouped launch
+  RowSrc a, b;
+  OutDst out;
+};
+
+constexpr int kMaxGroup = 8;
+
+struct GemmGroup {
+  int32_t count;
+  int32_t total_tiles;
+  GemmProblem p[kMaxGroup];
+};
+
+// Attention kernel arguments (device workspace layouts, see api.cpp).
+struct AttnArgs {
+  int32_t B, H, L, M, dh;
+  int32_t Lp, Np, Pp;      // padded query rows, key rows, position rows
+  int32_t n_split;         // key-range splits per query group (>= 1)
+  float c_scale;           // scale * log2(e) (bf16 path) or scale (fp32 path)
+  const float* q;          // [B][H][Lp][DP] fp32
+  const void* k;           // bf16 [B][H][Np][DP]   | f32 [B][H][Np][dh]
+  const void* vt;          // bf16 [B][H][DP][Np] (transposed) | f32 [B][H][Np][dh]
+  const void* rk;          // bf16 [H][Pp][DP]      | f32 [H][Pp][dh]
+  const void* u;           // [H][dh] in the call dtype
+  const void* v;
+  void* out;               // [B][L][H][dh] in the call dtype
+  float* part_o;           // split partials [n_split][B*H*Lp][DP]
+  float* part_ml;          // [n_split][B*H*Lp][2] (running max, sum)
+  int32_t dtype;
+};
+
+// Launch wrappers (return a hipError_t as int).
+int launch_gemm_bf16(const GemmGroup& g, void* stream);
+int launch_gemm_f32(const GemmGroup& g, void* stream);
+int launch_attn_bf16(const AttnArgs& a, void* stream);
+int launch_attn_f32(const AttnArgs& a, void* stream);
+int launch_sinusoid(void* R, int32_t n_pos, int32_t d_pos, int32_t dtype, void* stream);
+int launch_mem_update(void* mem, int32_t start, const void* h, int32_t B, int32_t M, int32_t L,
+                      int32_t d, int32_t dtype, void* stream);
+int launch_pack_rows(void* dst, int64_t ld_dst, const void* src, int64_t ld_src, int64_t rows,
+                     int32_t cols, int32_t dtype, void* stream);
+int launch_layernorm(const float* x, float* y_f32, void* y_lo, int32_t rows, int32_t d,
+                     int32_t lo_dtype, float eps, void* stream);
+int launch_cast_f32(const void* src, float* dst, int64_t n, int32_t dtype, void* stream);
+int launch_repack_rk(const void* rk_pub, void* rk_ws, int32_t P, int32_t Pp, int32_t H,
+                     int32_t dh, int32_t dp, int32_t dtype, void* stream);
+
+}  // namespace txl
