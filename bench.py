@@ -1,0 +1,304 @@
+#!/usr/bin/env python3
+"""Benchmark of the relative-attention layer step on one MI355X.
+
+A step is one txl_segment_step of the eval-shaped layer (batch 8, d_model 1024,
+16 heads of 64, segment 128 against a 1,600-state memory, bf16): position keys
+Rk = R W_kR^T, projections q / k / val^T over [memory ; segment], the fused
+relative attention, and the ring memory update.  Inputs are synthetic and
+resident in HBM before timing; every step consumes the next of 8 pre-generated
+segments and advances the memory ring.
+
+Printed JSON line: metric value = algorithmic TFLOP/s of the step (projection,
+position-key and attention FLOPs over valid query/key pairs only), plus eval
+tokens/s, the roofline entry of the dominant kernel (timed live with HIP events
+on the launch stream) and the CPU oracle on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+
+
+def flops(cfg, with_rk=True):
+    """Algorithmic FLOPs of one relative-attention forward (one layer, one segment)."""
+    B, L, M, d, H, dh = cfg.batch, cfg.seg_len, cfg.mem_len, cfg.d_model, cfg.n_heads, cfg.d_head
+    Hd = H * dh
+    pairs = L * M + L * (L + 1) // 2          # visible (query, key) pairs per (b, h)
+    f_q = 2 * B * L * d * Hd
+    f_kv = 2 * 2 * B * (M + L) * d * Hd
+    f_rk = 2 * (M + L) * cfg.d_pos * Hd if with_rk else 0
+    f_core = B * H * 3 * 2 * pairs * dh       # (q+u).k, (q+v).Rk, p.val
+    extra = 0
+    if cfg.d_inner:
+        extra = 2 * B * L * Hd * d + 2 * 2 * B * L * d * cfg.d_inner
+    return dict(q=f_q, kv=f_kv, rk=f_rk, core=f_core, extra=extra,
+                total=f_q + f_kv + f_rk + f_core + extra, pairs=pairs)
+
+
+def attn_bytes(cfg):
+    """Algorithmic HBM bytes of the fused attention kernel (bf16 operands read
+    once, fp32 q, bf16 output): q + K + V + Rk + out."""
+    B, L, M, H, dh = cfg.batch, cfg.seg_len, cfg.mem_len, cfg.n_heads, cfg.d_head
+    n = M + L
+    return B * H * L * dh * 4 + 2 * B * H * n * dh * 2 + H * n * dh * 2 + B * L * H * dh * 2
+
+
+def source_sha(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "transformer_xl_relative_attn_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+KERNEL_SOURCES = {
+    "proj_gemm": ["gemm.hip", "dev_common.h", "txl_internal.h"],
+    "rel_attn": ["attn.hip", "dev_common.h", "txl_internal.h"],
+}
+
+
+def load_traffic(kernel, workload):
+    """HBM traffic per launch measured with rocprofv3 counters, if the kernel
+    source has not changed since (else None)."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(kernel)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha") != source_sha(KERNEL_SOURCES[kernel]):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(cfg, wl, budget_s):
+    """Time the fp64 oracle on the host for consecutive segments of the same
+    workload until the budget is spent (at least one segment)."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:  # noqa: BLE001
+        cores = 1
+    R = oracle.sinusoid(cfg.n_pos, cfg.d_pos)
+    mems = [m for m in wl.mem]
+    start = 0
+    t0 = time.perf_counter()
+    done = 0
+    n_pool = len(wl.segments)
+    while True:   # consecutive segments of one stream, cycling the input pool
+        _, mems, start, _ = oracle.segment_step(wl.segments[done % n_pool], wl.layers, mems,
+                                                start, wl.u, wl.v, R, cfg.n_heads, cfg.d_head)
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    f = flops(cfg)["total"] * cfg.n_layers
+    _ = np
+    return {"value": f * done / el / 1e12, "unit": "TFLOP/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"{done} consecutive segment(s) of the {cfg.name} workload, all "
+                      f"{cfg.batch} batch rows, fp64 numpy oracle, {el:.1f} s",
+            "tokens_per_s": cfg.batch * cfg.seg_len * done / el}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__,
+                                 formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="c4", help="workload (c1..c5); headline is c4")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--cached-rk", action="store_true",
+                    help="pass precomputed position keys (Rk computed once, outside the step)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the relative-attention step has no "
+              "multi-GPU path in this library (run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    import transformer_xl_relative_attn_amd as txl
+
+    cfg = synth.get_config(args.config)
+    torch.cuda.set_device(0)
+    dt_t = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    dt_x = txl.TXL_BF16 if cfg.dtype == "bf16" else txl.TXL_F32
+    n_seg_pool = 8
+
+    def dev(x):
+        if cfg.dtype == "f32":
+            return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
+        return torch.from_numpy(synth.bf16_bits(x).view(np.int16)).view(torch.bfloat16).cuda()
+
+    wl = synth.make_workload(cfg, n_segments=n_seg_pool)
+    W = []
+    for lay in wl.layers:
+        w = dict(W_q=dev(lay.W_q), W_kE=dev(lay.W_kE), W_kR=dev(lay.W_kR), W_v=dev(lay.W_v))
+        if lay.W_o is not None:
+            w.update(W_o=dev(lay.W_o), W_ff1=dev(lay.W_ff1), W_ff2=dev(lay.W_ff2))
+        W.append(w)
+    u, v = dev(wl.u), dev(wl.v)
+    mems = [dev(m) for m in wl.mem]
+    segs = [dev(s) for s in wl.segments]
+    R = torch.empty((cfg.n_pos, cfg.d_pos), dtype=dt_t, device="cuda")
+    txl.txl_sinusoid_pos(R, cfg.n_pos, cfg.d_pos, dt_x)
+    Rks = None
+    if args.cached_rk:
+        Rks = []
+        for w in W:
+            rk = torch.empty((cfg.n_pos, cfg.n_heads, cfg.d_head), dtype=dt_t, device="cuda")
+            pws = torch.empty(max(1, txl.txl_rel_proj_workspace_bytes(
+                cfg.n_pos, cfg.d_pos, cfg.n_heads, cfg.d_head, dt_x)), dtype=torch.uint8,
+                device="cuda")
+            txl.txl_rel_proj(R, w["W_kR"], rk, cfg.n_pos, cfg.d_pos, cfg.n_heads, cfg.d_head,
+                             dt_x, pws)
+            Rks.append(rk)
+    layers = [txl.make_layer(w["W_q"], w["W_kE"], w["W_kR"], w["W_v"], u, v,
+                             mems[n] if cfg.mem_len else None,
+                             Rk=None if Rks is None else Rks[n], W_o=w.get("W_o"),
+                             W_ff1=w.get("W_ff1"), W_ff2=w.get("W_ff2"))
+              for n, w in enumerate(W)]
+    shape = txl.AttnShape(cfg.batch, cfg.seg_len, cfg.mem_len, cfg.d_model, cfg.n_heads,
+                          cfg.d_head, cfg.d_pos, dt_x, 0.0)
+    ws = torch.empty(txl.txl_segment_workspace_bytes(shape, cfg.n_layers, cfg.d_inner),
+                     dtype=torch.uint8, device="cuda")
+    d_out = cfg.d_model if cfg.d_inner else cfg.n_heads * cfg.d_head
+    h_out = torch.empty((cfg.batch, cfg.seg_len, d_out), dtype=dt_t, device="cuda")
+    stream = torch.cuda.current_stream()
+    state = {"start": 0, "i": 0}
+
+    def step():
+        state["start"] = txl.txl_segment_step(shape, cfg.n_layers, cfg.d_inner, layers, R,
+                                              segs[state["i"] % n_seg_pool], h_out,
+                                              state["start"], ws, stream)
+        state["i"] += 1
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # ---- headline timing (no instrumentation)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = ev0.elapsed_time(ev1)
+    ms_per_step = max(gpu_ms, wall * 1e3) / args.steps
+
+    # ---- per-kernel timing with HIP events on the launch stream
+    txl.txl_timing_reset()
+    txl.txl_timing_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    per = txl.txl_timing_read()
+    txl.txl_timing_enable(False)
+    kernels = {k: {"launches": c, "avg_us": (ms / c * 1e3) if c else 0.0,
+                   "share": 0.0} for k, (c, ms) in per.items() if c}
+    tot = sum(ms for (c, ms) in per.values() if c)
+    for k, (c, ms) in per.items():
+        if c:
+            kernels[k]["share"] = ms / tot
+
+    f = flops(cfg, with_rk=not args.cached_rk)
+    f_step = f["total"] * cfg.n_layers
+    value = f_step / (ms_per_step * 1e-3) / 1e12
+    tokens = cfg.batch * cfg.seg_len / (ms_per_step * 1e-3)
+
+    dominant = max(kernels, key=lambda k: kernels[k]["share"])
+    roof = None
+    wl_name = cfg.name
+    if dominant == "proj_gemm":
+        fl = f["q"] + f["kv"] + f["rk"]
+        ach = fl / (kernels[dominant]["avg_us"] * 1e-6) / 1e12
+        roof = {"kernel": "proj_gemm", "bound": "mfma", "achieved": round(ach, 1),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                "traffic": load_traffic("proj_gemm", wl_name),
+                "algorithmic_per_launch": fl}
+    elif dominant == "rel_attn":
+        by = attn_bytes(cfg)
+        ach = by / (kernels[dominant]["avg_us"] * 1e-6) / 1e9
+        roof = {"kernel": "rel_attn", "bound": "hbm", "achieved": round(ach, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
+                "traffic": load_traffic("rel_attn", wl_name), "algorithmic_per_launch": by}
+    else:
+        roof = {"kernel": dominant, "bound": "hbm", "achieved": None, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": None, "traffic": None}
+    attn_info = None
+    if "rel_attn" in kernels:
+        us = kernels["rel_attn"]["avg_us"]
+        attn_info = {"avg_us": round(us, 2),
+                     "core_tflops": round(f["core"] / (us * 1e-6) / 1e12, 1),
+                     "algorithmic_gbs": round(attn_bytes(cfg) / (us * 1e-6) / 1e9, 1)}
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(cfg, wl, args.cpu_budget)
+
+    out = {
+        "metric": "rel-attn fwd TFLOP/s (% bf16 MFMA peak) + eval tokens/s at L=128,M=1600",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: relative-attention layer step over a cached memory",
+                   "batch": cfg.batch, "seg_len": cfg.seg_len, "mem_len": cfg.mem_len,
+                   "d_model": cfg.d_model, "n_heads": cfg.n_heads, "d_head": cfg.d_head,
+                   "n_layers": cfg.n_layers, "d_inner": cfg.d_inner,
+                   "rk": "cached" if args.cached_rk else "computed in step",
+                   "parallelism": "single GPU"},
+        "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "tokens_per_s": round(tokens, 1),
+        "gflop_per_step": round(f_step / 1e9, 3),
+        "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv)
+                        for kk, vv in d.items()} for k, d in kernels.items()},
+        "attention_kernel": attn_info,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

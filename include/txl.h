@@ -189,6 +189,19 @@ txl_status_t txl_segment_step(const txl_attn_shape_t* shape, int32_t n_layers, i
                               void* h_out, int32_t* mem_start, void* workspace,
                               size_t workspace_bytes, void* stream);
 
+/*
+ * Kernel timing (diagnostics, off by default).  While enabled, every kernel the
+ * library launches is bracketed by two HIP events recorded on its launch
+ * stream.  txl_timing_read() waits for the recorded events, accumulates their
+ * elapsed times per kernel kind, and fills up to `capacity` entries of names
+ * (static strings), counts (launches) and total_ms; it returns the number of
+ * kinds.  txl_timing_reset() drops everything accumulated.  Enabling adds two
+ * event records per launch; keep it off for headline timings.
+ */
+txl_status_t txl_timing_enable(int32_t on);
+void txl_timing_reset(void);
+int32_t txl_timing_read(int32_t capacity, const char** names, int64_t* counts, double* total_ms);
+
 #ifdef __cplusplus
 }
 #endif

@@ -19,6 +19,7 @@ __all__ = [
     "txl_abi_version", "txl_status_str", "txl_last_error", "txl_sinusoid_pos",
     "txl_rel_proj_workspace_bytes", "txl_rel_proj", "txl_rel_attn_workspace_bytes",
     "txl_rel_attn_fwd", "txl_mem_update", "txl_segment_workspace_bytes", "txl_segment_step",
+    "txl_timing_enable", "txl_timing_reset", "txl_timing_read",
 ]
 
 TXL_F32 = 0
@@ -27,7 +28,7 @@ TXL_BF16 = 1
 lib_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtxl.so")
 if not os.path.exists(lib_path):
     raise ImportError(f"{lib_path} is missing: build it with "
-                      "`python -m transformer_xl_relative_attn_amd._build`")
+                      "`python transformer_xl_relative_attn_amd/_build.py`")
 lib = ctypes.CDLL(lib_path)
 
 _vp = ctypes.c_void_p
@@ -73,6 +74,13 @@ _seg_ws = _sig("txl_segment_workspace_bytes", _sz, [ctypes.POINTER(AttnShape), _
 _seg = _sig("txl_segment_step", ctypes.c_int,
             [ctypes.POINTER(AttnShape), _i32, _i32, ctypes.POINTER(Layer), _vp, _vp, _vp,
              ctypes.POINTER(_i32), _vp, _sz, _vp])
+
+
+_t_enable = _sig("txl_timing_enable", ctypes.c_int, [_i32])
+_t_reset = _sig("txl_timing_reset", None, [])
+_t_read = _sig("txl_timing_read", _i32, [_i32, ctypes.POINTER(ctypes.c_char_p),
+                                          ctypes.POINTER(ctypes.c_int64),
+                                          ctypes.POINTER(ctypes.c_double)])
 
 
 class TxlError(RuntimeError):
@@ -171,3 +179,21 @@ def txl_segment_step(shape: AttnShape, n_layers: int, d_inner: int, layers: Sequ
                 ctypes.byref(st), _ptr(workspace), _nbytes(workspace), _stream(stream)),
            "txl_segment_step")
     return st.value
+
+
+def txl_timing_enable(on: bool):
+    _check(_t_enable(1 if on else 0), "txl_timing_enable")
+
+
+def txl_timing_reset():
+    _t_reset()
+
+
+def txl_timing_read() -> dict:
+    """{kernel kind: (launches, total_ms)} accumulated since the last reset."""
+    cap = 32
+    names = (ctypes.c_char_p * cap)()
+    counts = (ctypes.c_int64 * cap)()
+    ms = (ctypes.c_double * cap)()
+    n = _t_read(cap, names, counts, ms)
+    return {names[i].decode(): (counts[i], ms[i]) for i in range(min(n, cap))}

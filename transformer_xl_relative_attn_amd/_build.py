@@ -1,6 +1,6 @@
 """Build libtxl.so (HIP, gfx950) in-tree with hipcc.
 
-Usage: python -m transformer_xl_relative_attn_amd._build
+Usage: python transformer_xl_relative_attn_amd/_build.py   (or __graft_entry__.build())
 """
 from __future__ import annotations
 

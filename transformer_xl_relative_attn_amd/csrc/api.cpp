@@ -8,7 +8,9 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
+#include <vector>
 
 #include "txl_internal.h"
 
@@ -68,6 +70,65 @@ txl_status_t after_launch(int err, const char* what, void* stream) {
     if (e) return hip_status(e, what);
   }
   return TXL_OK;
+}
+
+// ------------------------------------------------------------ kernel timing
+// Optional diagnostics: when enabled, every kernel launch is bracketed by two
+// HIP events recorded on the launch stream; txl_timing_read() waits for them.
+enum Kind : int {
+  K_PROJ_GEMM, K_ATTN, K_ATTN_COMBINE, K_MEM_UPDATE, K_REL_PROJ, K_WO_GEMM, K_FFN1_GEMM,
+  K_FFN2_GEMM, K_LAYERNORM, K_PACK, K_SINUSOID, K_CAST, K_REPACK_RK, K_NKINDS
+};
+const char* const kKindNames[K_NKINDS] = {
+    "proj_gemm", "rel_attn", "attn_combine", "mem_update", "rel_proj_gemm", "wo_gemm",
+    "ffn1_gemm", "ffn2_gemm", "layernorm", "pack_rows", "sinusoid", "cast_f32", "repack_rk"};
+
+struct TimingState {
+  std::mutex mu;
+  bool on = false;
+  std::vector<hipEvent_t> pool;
+  struct Rec { int kind; hipEvent_t a, b; };
+  std::vector<Rec> pending;
+  double ms[K_NKINDS] = {};
+  int64_t count[K_NKINDS] = {};
+};
+TimingState& timing() {
+  static TimingState t;
+  return t;
+}
+
+hipEvent_t take_event(TimingState& t) {
+  if (!t.pool.empty()) {
+    hipEvent_t e = t.pool.back();
+    t.pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Run a launch function, bracketed by timing events when timing is on.
+template <class F>
+int timed(int kind, void* stream, F&& launch) {
+  TimingState& t = timing();
+  hipEvent_t a = nullptr, b = nullptr;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  {
+    std::lock_guard<std::mutex> lk(t.mu);
+    if (t.on) {
+      a = take_event(t);
+      b = take_event(t);
+    }
+  }
+  if (a && b) (void)hipEventRecord(a, st);
+  int err = launch();
+  if (a && b) {
+    (void)hipEventRecord(b, st);
+    std::lock_guard<std::mutex> lk(t.mu);
+    t.pending.push_back({kind, a, b});
+  }
+  return err;
 }
 
 // ---------------------------------------------------------------- planning
@@ -178,8 +239,8 @@ AttnPlan make_plan(const txl_attn_shape_t* s, bool compute_rk) {
 }
 
 // Output maps ------------------------------------------------------------
-AxisMap axis(int32_t div, int64_t s1, int64_t s2) { return AxisMap{div, s1, s2}; }
-AxisMap axis_linear(int64_t s) { return AxisMap{INT32_MAX, 0, s}; }
+AxisMap axis(int32_t div, int64_t s1, int64_t s2) { return make_axis(div, s1, s2); }
+AxisMap axis_linear(int64_t s) { return make_axis(kLinearDiv, 0, s); }
 
 RowSrc src_plain(const void* p, int64_t ld, int32_t rows) {
   RowSrc r{};
@@ -238,6 +299,13 @@ OutDst out_map(void* ptr, int dtype, int32_t mv, int32_t nv, AxisMap row, AxisMa
   o.row = row;
   o.col = col;
   o.resid = resid;
+  // vectorised epilogue: 4 consecutive columns (n % 4 == 0) map to 4
+  // consecutive, aligned elements for every row
+  const bool col_ok = col.s2 == 1 && col.s1 % 4 == 0 && (col.div == kLinearDiv || col.div % 4 == 0);
+  const bool row_ok = row.s1 % 4 == 0 && row.s2 % 4 == 0;
+  const bool ptr_ok = (reinterpret_cast<uintptr_t>(ptr) % 16) == 0 &&
+                      (!resid || (reinterpret_cast<uintptr_t>(resid) % 16) == 0);
+  o.vec_ok = col_ok && row_ok && ptr_ok && nv % 4 == 0;
   return o;
 }
 
@@ -291,15 +359,15 @@ txl_status_t run_rel_attn(const AttnPlan& p, const AttnPtrs& a, char* ws, void* 
   const void *Wq = a.W_q, *WkE = a.W_kE, *Wv = a.W_v, *WkR = a.W_kR, *R = a.R;
   int64_t ld_d = p.d, ld_pos = p.dpos;
   if (p.pack_d) {
-    TXL_HIP(launch_pack_rows(ws + p.ph.off, p.Kd, h, p.d, (int64_t)p.B * p.L, p.d, dt, stream),
+    TXL_HIP(timed(K_PACK, stream, [&] { return launch_pack_rows(ws + p.ph.off, p.Kd, h, p.d, (int64_t)p.B * p.L, p.d, dt, stream); }),
             "pack h");
     if (p.M > 0)
-      TXL_HIP(launch_pack_rows(ws + p.pmem.off, p.Kd, mem, p.d, (int64_t)p.B * p.M, p.d, dt,
-                               stream),
+      TXL_HIP(timed(K_PACK, stream, [&] { return launch_pack_rows(ws + p.pmem.off, p.Kd, mem, p.d, (int64_t)p.B * p.M, p.d, dt,
+                               stream); }),
               "pack mem");
-    TXL_HIP(launch_pack_rows(ws + p.pwq.off, p.Kd, Wq, p.d, Hd, p.d, dt, stream), "pack W_q");
-    TXL_HIP(launch_pack_rows(ws + p.pwk.off, p.Kd, WkE, p.d, Hd, p.d, dt, stream), "pack W_kE");
-    TXL_HIP(launch_pack_rows(ws + p.pwv.off, p.Kd, Wv, p.d, Hd, p.d, dt, stream), "pack W_v");
+    TXL_HIP(timed(K_PACK, stream, [&] { return launch_pack_rows(ws + p.pwq.off, p.Kd, Wq, p.d, Hd, p.d, dt, stream); }), "pack W_q");
+    TXL_HIP(timed(K_PACK, stream, [&] { return launch_pack_rows(ws + p.pwk.off, p.Kd, WkE, p.d, Hd, p.d, dt, stream); }), "pack W_kE");
+    TXL_HIP(timed(K_PACK, stream, [&] { return launch_pack_rows(ws + p.pwv.off, p.Kd, Wv, p.d, Hd, p.d, dt, stream); }), "pack W_v");
     h = ws + p.ph.off;
     mem = ws + p.pmem.off;
     Wq = ws + p.pwq.off;
@@ -308,9 +376,9 @@ txl_status_t run_rel_attn(const AttnPlan& p, const AttnPtrs& a, char* ws, void* 
     ld_d = p.Kd;
   }
   if (!a.Rk && p.pack_pos) {
-    TXL_HIP(launch_pack_rows(ws + p.pwr.off, p.Kpos, WkR, p.dpos, Hd, p.dpos, dt, stream),
+    TXL_HIP(timed(K_PACK, stream, [&] { return launch_pack_rows(ws + p.pwr.off, p.Kpos, WkR, p.dpos, Hd, p.dpos, dt, stream); }),
             "pack W_kR");
-    TXL_HIP(launch_pack_rows(ws + p.pr.off, p.Kpos, R, p.dpos, p.P, p.dpos, dt, stream),
+    TXL_HIP(timed(K_PACK, stream, [&] { return launch_pack_rows(ws + p.pr.off, p.Kpos, R, p.dpos, p.P, p.dpos, dt, stream); }),
             "pack R");
     WkR = ws + p.pwr.off;
     R = ws + p.pr.off;
@@ -351,13 +419,14 @@ txl_status_t run_rel_attn(const AttnPlan& p, const AttnPtrs& a, char* ws, void* 
                 out_map(rk, dt, p.Pp, p.H * p.DP, axis_linear(DP), axis(p.DP, (int64_t)p.Pp * DP, 1)),
                 tile);
   } else {
-    TXL_HIP(launch_repack_rk(a.Rk, rk, p.P, p.Pp, p.H, p.dh, p.DP, dt, stream), "repack Rk");
+    TXL_HIP(timed(K_REPACK_RK, stream, [&] { return launch_repack_rk(a.Rk, rk, p.P, p.Pp, p.H, p.dh, p.DP, dt, stream); }), "repack Rk");
   }
-  TXL_TRY(after_launch(launch_gemm(g, dt, stream), "projection GEMMs", stream));
+  TXL_TRY(after_launch(timed(K_PROJ_GEMM, stream, [&] { return launch_gemm(g, dt, stream); }),
+                       "projection GEMMs", stream));
 
   if (mem_upd) {
-    TXL_TRY(after_launch(launch_mem_update(mem_upd, a.mem_start, a.h, p.B, p.M, p.L, p.d, dt,
-                                           stream),
+    TXL_TRY(after_launch(timed(K_MEM_UPDATE, stream, [&] { return launch_mem_update(mem_upd, a.mem_start, a.h, p.B, p.M, p.L, p.d, dt,
+                                           stream); }),
                          "memory update", stream));
     *new_start = (p.M == 0) ? 0 : (p.L < p.M ? (a.mem_start + p.L) % p.M : 0);
   }
@@ -383,8 +452,16 @@ txl_status_t run_rel_attn(const AttnPlan& p, const AttnPtrs& a, char* ws, void* 
   aa.part_o = p.n_split > 1 ? reinterpret_cast<float*>(ws + p.po.off) : nullptr;
   aa.part_ml = p.n_split > 1 ? reinterpret_cast<float*>(ws + p.pml.off) : nullptr;
   aa.dtype = dt;
-  int e = bf ? launch_attn_bf16(aa, stream) : launch_attn_f32(aa, stream);
-  return after_launch(e, "attention kernel", stream);
+  TXL_TRY(after_launch(timed(K_ATTN, stream,
+                             [&] {
+                               return bf ? launch_attn_bf16(aa, stream)
+                                         : launch_attn_f32(aa, stream);
+                             }),
+                       "attention kernel", stream));
+  if (bf && p.n_split > 1)
+    TXL_TRY(after_launch(timed(K_ATTN_COMBINE, stream, [&] { return launch_attn_combine(aa, stream); }),
+                         "attention combine", stream));
+  return TXL_OK;
 }
 
 // --------------------------------------------------------- segment planning
@@ -452,7 +529,7 @@ txl_status_t txl_sinusoid_pos(void* R, int32_t n_pos, int32_t d_pos, int32_t dty
   if (dtype != TXL_F32 && dtype != TXL_BF16) return fail(TXL_ERR_BAD_DTYPE, "bad dtype %d", dtype);
   if (n_pos < 1 || d_pos < 1 || n_pos > kMaxDim || d_pos > kMaxDim)
     return fail(TXL_ERR_BAD_SHAPE, "n_pos=%d d_pos=%d out of range", n_pos, d_pos);
-  return after_launch(launch_sinusoid(R, n_pos, d_pos, dtype, stream), "sinusoid", stream);
+  return after_launch(timed(K_SINUSOID, stream, [&] { return launch_sinusoid(R, n_pos, d_pos, dtype, stream); }), "sinusoid", stream);
 }
 
 size_t txl_rel_proj_workspace_bytes(int32_t n_pos, int32_t d_pos, int32_t n_heads, int32_t d_head,
@@ -486,8 +563,8 @@ txl_status_t txl_rel_proj(const void* R, const void* W_kR, void* Rk, int32_t n_p
     char* ws = static_cast<char*>(workspace);
     char* pr = ws;
     char* pw = ws + align256((size_t)n_pos * Kp * 2);
-    TXL_HIP(launch_pack_rows(pr, Kp, R, d_pos, n_pos, d_pos, dtype, stream), "pack R");
-    TXL_HIP(launch_pack_rows(pw, Kp, W_kR, d_pos, Hd, d_pos, dtype, stream), "pack W_kR");
+    TXL_HIP(timed(K_PACK, stream, [&] { return launch_pack_rows(pr, Kp, R, d_pos, n_pos, d_pos, dtype, stream); }), "pack R");
+    TXL_HIP(timed(K_PACK, stream, [&] { return launch_pack_rows(pw, Kp, W_kR, d_pos, Hd, d_pos, dtype, stream); }), "pack W_kR");
     Rs = pr;
     Ws = pw;
     ld = Kp;
@@ -495,7 +572,8 @@ txl_status_t txl_rel_proj(const void* R, const void* W_kR, void* Rk, int32_t n_p
   GemmGroup g{};
   add_problem(g, n_pos, Hd, (int32_t)ld, src_plain(Rs, ld, n_pos), src_plain(Ws, ld, Hd),
               out_map(Rk, dtype, n_pos, Hd, axis_linear(Hd), axis_linear(1)), gemm_tile(dtype));
-  return after_launch(launch_gemm(g, dtype, stream), "rel_proj GEMM", stream);
+  return after_launch(timed(K_REL_PROJ, stream, [&] { return launch_gemm(g, dtype, stream); }),
+                      "rel_proj GEMM", stream);
 }
 
 size_t txl_rel_attn_workspace_bytes(const txl_attn_shape_t* shape) {
@@ -531,8 +609,8 @@ txl_status_t txl_mem_update(void* mem, int32_t* mem_start, const void* h, int32_
   if (mem_len > 0 ? (st < 0 || st >= mem_len) : st != 0)
     return fail(TXL_ERR_BAD_SHAPE, "mem_start %d outside [0, mem_len=%d)", st, mem_len);
   if (mem_len == 0) return TXL_OK;
-  TXL_TRY(after_launch(launch_mem_update(mem, st, h, batch, mem_len, seg_len, d_model, dtype,
-                                         stream),
+  TXL_TRY(after_launch(timed(K_MEM_UPDATE, stream, [&] { return launch_mem_update(mem, st, h, batch, mem_len, seg_len, d_model, dtype,
+                                         stream); }),
                        "memory update", stream));
   *mem_start = seg_len < mem_len ? (st + seg_len) % mem_len : 0;
   return TXL_OK;
@@ -603,7 +681,7 @@ txl_status_t txl_segment_step(const txl_attn_shape_t* shape, int32_t n_layers, i
     const bool full = ly.W_o != nullptr;
     if (full && !x32) {
       x32 = f32_buf[pp];
-      TXL_HIP(launch_cast_f32(x_lo, x32, (int64_t)rows * d, dt, stream), "cast residual");
+      TXL_HIP(timed(K_CAST, stream, [&] { return launch_cast_f32(x_lo, x32, (int64_t)rows * d, dt, stream); }), "cast residual");
     }
     void* a_out = (!full && last) ? h_out : (full ? ws + sp.a.off : lo_buf[pp ^ 1]);
     AttnPtrs a{x_lo, ly.mem, ly.W_q, ly.W_kE, ly.W_kR, ly.W_v, ly.u, ly.v, R, ly.Rk, start, a_out};
@@ -625,16 +703,18 @@ txl_status_t txl_segment_step(const txl_attn_shape_t* shape, int32_t n_layers, i
       add_problem(g, rows, d, Hd, src_plain(ws + sp.a.off, Hd, rows), src_plain(ly.W_o, Hd, d),
                   out_map(t32, TXL_F32, rows, d, axis_linear(d), axis_linear(1), EPI_RESID, x32),
                   tile);
-      TXL_TRY(after_launch(launch_gemm(g, dt, stream), "W_o GEMM", stream));
+      TXL_TRY(after_launch(timed(K_WO_GEMM, stream, [&] { return launch_gemm(g, dt, stream); }), "W_o GEMM",
+                           stream));
     }
-    TXL_TRY(after_launch(launch_layernorm(t32, o32, olo, rows, d, dt, 1e-5f, stream), "LN1",
+    TXL_TRY(after_launch(timed(K_LAYERNORM, stream, [&] { return launch_layernorm(t32, o32, olo, rows, d, dt, 1e-5f, stream); }), "LN1",
                          stream));
     {
       GemmGroup g{};
       add_problem(g, rows, d_inner, d, src_plain(olo, d, rows), src_plain(ly.W_ff1, d, d_inner),
                   out_map(hid, dt, rows, d_inner, axis_linear(d_inner), axis_linear(1), EPI_RELU),
                   tile);
-      TXL_TRY(after_launch(launch_gemm(g, dt, stream), "FFN1 GEMM", stream));
+      TXL_TRY(after_launch(timed(K_FFN1_GEMM, stream, [&] { return launch_gemm(g, dt, stream); }), "FFN1 GEMM",
+                           stream));
     }
     {
       GemmGroup g{};
@@ -642,11 +722,12 @@ txl_status_t txl_segment_step(const txl_attn_shape_t* shape, int32_t n_layers, i
                   src_plain(ly.W_ff2, d_inner, d),
                   out_map(t32, TXL_F32, rows, d, axis_linear(d), axis_linear(1), EPI_RESID, o32),
                   tile);
-      TXL_TRY(after_launch(launch_gemm(g, dt, stream), "FFN2 GEMM", stream));
+      TXL_TRY(after_launch(timed(K_FFN2_GEMM, stream, [&] { return launch_gemm(g, dt, stream); }), "FFN2 GEMM",
+                           stream));
     }
     float* y32 = f32_buf[pp ^ 1];
     void* ylo = last ? h_out : lo_buf[pp ^ 1];
-    TXL_TRY(after_launch(launch_layernorm(t32, y32, ylo, rows, d, dt, 1e-5f, stream), "LN2",
+    TXL_TRY(after_launch(timed(K_LAYERNORM, stream, [&] { return launch_layernorm(t32, y32, ylo, rows, d, dt, 1e-5f, stream); }), "LN2",
                          stream));
     x_lo = ylo;
     x32 = y32;
@@ -654,6 +735,50 @@ txl_status_t txl_segment_step(const txl_attn_shape_t* shape, int32_t n_layers, i
   }
   *mem_start = new_start;
   return TXL_OK;
+}
+
+txl_status_t txl_timing_enable(int32_t on) {
+  TimingState& t = timing();
+  std::lock_guard<std::mutex> lk(t.mu);
+  t.on = on != 0;
+  return TXL_OK;
+}
+
+void txl_timing_reset(void) {
+  TimingState& t = timing();
+  std::lock_guard<std::mutex> lk(t.mu);
+  for (auto& r : t.pending) {
+    (void)hipEventSynchronize(r.b);
+    t.pool.push_back(r.a);
+    t.pool.push_back(r.b);
+  }
+  t.pending.clear();
+  for (int k = 0; k < K_NKINDS; ++k) {
+    t.ms[k] = 0.0;
+    t.count[k] = 0;
+  }
+}
+
+int32_t txl_timing_read(int32_t capacity, const char** names, int64_t* counts, double* total_ms) {
+  TimingState& t = timing();
+  std::lock_guard<std::mutex> lk(t.mu);
+  for (auto& r : t.pending) {
+    float ms = 0.0f;
+    if (hipEventSynchronize(r.b) == hipSuccess && hipEventElapsedTime(&ms, r.a, r.b) == hipSuccess) {
+      t.ms[r.kind] += ms;
+      t.count[r.kind] += 1;
+    }
+    t.pool.push_back(r.a);
+    t.pool.push_back(r.b);
+  }
+  t.pending.clear();
+  const int n = capacity < K_NKINDS ? capacity : K_NKINDS;
+  for (int k = 0; k < n; ++k) {
+    if (names) names[k] = kKindNames[k];
+    if (counts) counts[k] = t.count[k];
+    if (total_ms) total_ms[k] = t.ms[k];
+  }
+  return K_NKINDS;
 }
 
 }  // extern "C"

@@ -384,12 +384,15 @@ int launch_attn_bf16(const AttnArgs& a, void* stream) {
   const int32_t nqg = (a.L + QG - 1) / QG;
   const int32_t total = a.B * a.H * nqg * a.n_split;
   const int32_t padded = (total + 7) & ~7;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  hipLaunchKernelGGL(attn_bf16_kernel, dim3(padded), dim3(256), 0, st, a, padded, nqg);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.n_split == 1) return static_cast<int>(e);
+  hipLaunchKernelGGL(attn_bf16_kernel, dim3(padded), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), a, padded, nqg);
+  return static_cast<int>(hipGetLastError());
+}
+
+int launch_attn_combine(const AttnArgs& a, void* stream) {
   const int64_t n = (int64_t)a.B * a.H * a.L * a.dh;
-  hipLaunchKernelGGL(attn_combine_kernel, dim3((n + 255) / 256), dim3(256), 0, st, a, DP);
+  hipLaunchKernelGGL(attn_combine_kernel, dim3((n + 255) / 256), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), a, DP);
   return static_cast<int>(hipGetLastError());
 }
 

@@ -70,8 +70,7 @@ __device__ __forceinline__ const char* row_address(const RowSrc& s, int32_t v, i
 }
 
 __device__ __forceinline__ int64_t axis_off(const AxisMap& a, int32_t x) {
-  int32_t q = x / a.div;
-  return (int64_t)q * a.s1 + (int64_t)(x - q * a.div) * a.s2;
+  return axis_offset(a, x);
 }
 
 // Epilogue store of one accumulator element.

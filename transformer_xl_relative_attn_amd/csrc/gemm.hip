@@ -5,12 +5,13 @@
 //   that h~ = [memory ring ; segment] is gathered on the fly.
 //
 // gemm_bf16: bf16 operands, fp32 accumulation on the gfx950 matrix cores
-//   (v_mfma_f32_32x32x16_bf16).  256x256x64 block tile, 4 waves in a 2x2
-//   grid, each wave owns a 128x128 sub-tile (4x4 MFMA tiles, 256 accumulator
-//   registers).  Operand tiles are double-buffered in LDS; each 16-byte chunk
-//   of a 128-byte LDS row is XOR-swizzled by (row & 7) so the MFMA operand
-//   reads (8 consecutive rows, same chunk) hit distinct banks.  Requirements
-//   (checked by the host): K % 64 == 0, every row 16-byte aligned.
+//   (v_mfma_f32_32x32x16_bf16).  256x256 block tile, 4 waves in a 2x2 grid,
+//   each wave owns a 128x128 sub-tile (4x4 MFMA tiles, 256 accumulator
+//   registers).  Operands stream through a 4-deep LDS ring of 32-wide K steps
+//   filled by direct global->LDS loads (no register staging), issued up to
+//   four K steps ahead of their use; MFMA operand reads for the next k-step
+//   are interleaved with the current MFMAs.  Requirements (checked by the host):
+//   K % 64 == 0, every row 16-byte aligned.
 //
 // gemm_f32: fp32 operands and arithmetic on the vector ALUs (64x64 tile),
 //   used by the fp32 path.
@@ -20,9 +21,15 @@ namespace txl {
 
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 64, NT = 256;
-constexpr int CHUNKS = BK / 8;           // 16-byte chunks per tile row (8)
-constexpr int LOADS = BM * CHUNKS / NT;  // chunks per thread per operand (8)
+constexpr int BM = 256, BN = 256, BK = 32, NT = 256;
+constexpr int NSTAGE = 4;                // LDS ring depth: loads run NSTAGE-1 K-steps ahead
+constexpr int CH = BK / 8;               // 16-byte chunks per tile row (4)
+constexpr int TILE_U = BM * CH;          // 16-byte units per operand tile (1024)
+constexpr int STAGE_U = 2 * TILE_U;      // A tile then B tile
+constexpr int LOADS = TILE_U / NT;       // LDS-DMA loads per thread per operand (4)
+
+// 128 bytes of zeros: the source of every "zero row" chunk (padding rows).
+__device__ __align__(16) uint32_t g_zero_chunk[32];
 
 __device__ __forceinline__ const GemmProblem* find_problem(const GemmGroup& g, int32_t tile,
                                                            int32_t* local) {
@@ -34,6 +41,71 @@ __device__ __forceinline__ const GemmProblem* find_problem(const GemmGroup& g, i
   return &g.p[idx];
 }
 
+// Wait until at most n LDS-DMA loads of this wave are still in flight.  The
+// loads are not fenced by the compiler (a __syncthreads would wait for all of
+// them), so the waits are explicit.
+__device__ __forceinline__ void wait_vm(int n) {
+  if (n >= 24)
+    asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
+  else if (n >= 16)
+    asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  else if (n >= 8)
+    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// Workgroup barrier after this wave's LDS reads have completed (no wait on
+// outstanding global loads).
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Vectorised epilogue: four consecutive output columns per store.  FLAGS < 0
+// means "read the residual / ReLU flags at run time".
+template <int DTYPE, int FLAGS>
+__device__ __forceinline__ void epilogue_vec(const OutDst& o, const floatx16 (&acc)[4][4],
+                                             int32_t mb, int32_t nb) {
+  const int flags = FLAGS < 0 ? o.flags : FLAGS;
+  int64_t roff[4];
+  bool mok[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    mok[i] = mb + 32 * i < o.m_valid;
+    roff[i] = axis_off(o.row, mb + 32 * i);
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int32_t n = nb + 32 * j + 8 * g;
+      if (n >= o.n_valid) continue;
+      const int64_t coff = axis_off(o.col, n);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (!mok[i]) continue;
+        const int64_t off = roff[i] + coff;
+        floatx4 v = floatx4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                            acc[i][j][4 * g + 3]};
+        if (flags & EPI_RESID) v += *reinterpret_cast<const floatx4*>(o.resid + off);
+        if (flags & EPI_RELU) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) v[c] = fmaxf(v[c], 0.0f);
+        }
+        if (DTYPE == TXL_F32) {
+          *reinterpret_cast<floatx4*>(static_cast<float*>(o.p) + off) = v;
+        } else {
+          typedef float floatx2_t __attribute__((ext_vector_type(2)));
+          typedef bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+          const bf16x2_t lo = __builtin_convertvector(floatx2_t{v[0], v[1]}, bf16x2_t);
+          const bf16x2_t hi = __builtin_convertvector(floatx2_t{v[2], v[3]}, bf16x2_t);
+          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(o.p) + off) =
+              u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+        }
+      }
+    }
+}
+
 __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(GemmGroup g, int32_t padded) {
   const int32_t tile = xcd_swizzle(blockIdx.x, padded);
   if (tile >= g.total_tiles) return;
@@ -42,43 +114,44 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(GemmGroup g, int32_t p
   // consecutive tiles share the A rows (tm), sweeping n fastest
   const int32_t tm = local / P.tiles_n, tn = local - tm * P.tiles_n;
   const int32_t m0 = tm * BM, n0 = tn * BN;
+  const int32_t K = P.K;
 
-  __shared__ u32x4 smA[2][BM * CHUNKS];
-  __shared__ u32x4 smB[2][BN * CHUNKS];
+  // LDS ring: stage s holds A rows [0,256) then B rows [0,256), each row 4
+  // chunks of 16 bytes; chunk c of row r is stored at slot c ^ ((r >> 1) & 3)
+  // so that 8 consecutive rows read at one chunk hit distinct banks.
+  __shared__ u32x4 smem[NSTAGE * STAGE_U];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
-  // Rows this thread stages: row = tid/8 + 32*i, chunk = tid%8.
-  const int chunk = tid & 7;
+  // LDS-DMA mapping: load i of this wave fills units [(4i + wave)*64, +64) of a
+  // tile, i.e. row (4i + wave)*16 + lane/4, slot lane%4, which holds global
+  // chunk (lane%4) ^ ((row >> 1) & 3) = (lane%4) ^ ((lane >> 3) & 3).
+  const int gchunk = (lane & 3) ^ ((lane >> 3) & 3);
   const char* pa[LOADS];
   const char* pb[LOADS];
+  int64_t ka[LOADS], kb[LOADS];   // K-advance masks (all ones, or 0 for zero rows)
+  const char* zero = reinterpret_cast<const char*>(g_zero_chunk) + gchunk * 16;
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
-    int r = (tid >> 3) + 32 * i;
-    pa[i] = (m0 + r < P.M) ? row_address(P.a, m0 + r, 2) : nullptr;
-    pb[i] = (n0 + r < P.N) ? row_address(P.b, n0 + r, 2) : nullptr;
-    if (pa[i]) pa[i] += chunk * 16;
-    if (pb[i]) pb[i] += chunk * 16;
+    const int r = (4 * i + wave) * 16 + (lane >> 2);
+    const char* a = (m0 + r < P.M) ? row_address(P.a, m0 + r, 2) : nullptr;
+    const char* b = (n0 + r < P.N) ? row_address(P.b, n0 + r, 2) : nullptr;
+    pa[i] = a ? a + gchunk * 16 : zero;
+    pb[i] = b ? b + gchunk * 16 : zero;
+    ka[i] = a ? -1 : 0;
+    kb[i] = b ? -1 : 0;
   }
 
-  u32x4 ra[LOADS], rb[LOADS];
-  auto gload = [&](int kt) {
+  auto issue = [&](int kt) {   // LDS-DMA of K-step kt into ring slot kt % NSTAGE
     const int64_t koff = (int64_t)kt * BK * 2;
+    u32x4* st = smem + (kt % NSTAGE) * STAGE_U;
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
-      ra[i] = pa[i] ? *reinterpret_cast<const u32x4*>(pa[i] + koff) : u32x4{0, 0, 0, 0};
-      rb[i] = pb[i] ? *reinterpret_cast<const u32x4*>(pb[i] + koff) : u32x4{0, 0, 0, 0};
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      int r = (tid >> 3) + 32 * i;
-      int pos = r * CHUNKS + (chunk ^ (r & 7));
-      smA[buf][pos] = ra[i];
-      smB[buf][pos] = rb[i];
+      u32x4* dA = st + (4 * i + wave) * 64;
+      __builtin_amdgcn_global_load_lds(pa[i] + (koff & ka[i]), dA, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(pb[i] + (koff & kb[i]), dA + TILE_U, 16, 0, 0);
     }
   };
 
@@ -88,52 +161,114 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(GemmGroup g, int32_t p
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = floatx16{0};
 
-  const int nk = P.K / BK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
+  const int nk = K / BK;
+#pragma unroll
+  for (int s = 0; s < NSTAGE; ++s)
+    if (s < nk) issue(s);
 
   const int lrow = lane & 31, lhalf = lane >> 5;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
+  const int sw = (lrow >> 1) & 3;  // same for every fragment row of a lane
+  int fa[4], fb[4];                // fragment row base (16-byte units) within a stage
 #pragma unroll
-    for (int s = 0; s < BK / 16; ++s) {
-      bf16x8 af[4], bfr[4];
-      const int c = 2 * s + lhalf;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        int ra_ = wm * 128 + i * 32 + lrow;
-        int rb_ = wn * 128 + i * 32 + lrow;
-        af[i] = __builtin_bit_cast(bf16x8, smA[buf][ra_ * CHUNKS + (c ^ (ra_ & 7))]);
-        bfr[i] = __builtin_bit_cast(bf16x8, smB[buf][rb_ * CHUNKS + (c ^ (rb_ & 7))]);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < nk) {
-      lstore(buf ^ 1);
-      __syncthreads();
-    }
+  for (int i = 0; i < 4; ++i) {
+    fa[i] = (wm * 128 + i * 32 + lrow) * CH;
+    fb[i] = TILE_U + (wn * 128 + i * 32 + lrow) * CH;
   }
-
-  // Epilogue: acc[i][j] element e -> row m = 8*(e/4) + 4*lhalf + e%4, col n = lrow.
-  const OutDst& o = P.out;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int32_t n = n0 + wn * 128 + j * 32 + lrow;
-    if (n >= o.n_valid) continue;
-    const int64_t coff = axis_off(o.col, n);
+  // fragments of k-step s (0 or 1) of a staged 32-wide K step
+  auto read_frags = [&](const u32x4* st, int s, bf16x8* af, bf16x8* bfr) {
+    const int c = (2 * s + lhalf) ^ sw;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+      af[i] = __builtin_bit_cast(bf16x8, st[fa[i] + c]);
+      bfr[i] = __builtin_bit_cast(bf16x8, st[fb[i] + c]);
+    }
+  };
+  auto mfma16 = [&](const bf16x8* af, const bf16x8* bfr) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int32_t m = m0 + wm * 128 + i * 32 + 8 * (e >> 2) + 4 * lhalf + (e & 3);
-        if (m < o.m_valid) epi_store(o, axis_off(o.row, m) + coff, acc[i][j][e]);
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+  };
+
+  // Pipeline per K step kt (ring slot kt % NSTAGE):
+  //   A: MFMAs of k-step 0 (fragments F0 already in registers), reading the
+  //      k-step 1 fragments F1 in between;
+  //   wait for step kt+1 to land, barrier (slot kt % NSTAGE is then free);
+  //   B: refill that slot with step kt+NSTAGE, MFMAs of F1, reading step kt+1's
+  //      k-step 0 fragments into F0 in between.
+  // Reads are interleaved one per two MFMAs so the LDS queue never backs up.
+  bf16x8 f0a[4], f0b[4], f1a[4], f1b[4];
+  wait_vm((min(NSTAGE, nk) - 1) * 2 * LOADS);
+  barrier_lds();
+  read_frags(smem, 0, f0a, f0b);
+  for (int kt = 0; kt < nk; ++kt) {
+    const u32x4* st = smem + (kt % NSTAGE) * STAGE_U;
+    read_frags(st, 1, f1a, f1b);
+    mfma16(f0a, f0b);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // 2 MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 LDS read
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (kt + 1 < nk) {
+      const int after = min(NSTAGE - 2, nk - 2 - kt);
+      wait_vm(after * 2 * LOADS);
+      barrier_lds();
+      if (kt + NSTAGE < nk) issue(kt + NSTAGE);
+      read_frags(smem + ((kt + 1) % NSTAGE) * STAGE_U, 0, f0a, f0b);
+    }
+    mfma16(f1a, f1b);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);   // 2 MFMA
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);   // 1 global->LDS load
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);   // 1 LDS read
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // ---- epilogue, straight from the accumulators.  The MFMA operands are
+  // swapped (B fragment first), so block (i, j) holds C^T: element 4g + r of a
+  // lane is C[m][n] with m = mb + 32i and n = nb + 32j + 8g + r, i.e. four
+  // consecutive output columns of one row per (i, j, g).
+  const OutDst& o = P.out;
+  const int32_t mb = m0 + wm * 128 + lrow;
+  const int32_t nb = n0 + wn * 128 + 4 * lhalf;
+  if (o.vec_ok) {
+    if (o.flags == 0 && o.dtype == TXL_BF16)
+      epilogue_vec<TXL_BF16, 0>(o, acc, mb, nb);
+    else if (o.flags == 0)
+      epilogue_vec<TXL_F32, 0>(o, acc, mb, nb);
+    else if (o.dtype == TXL_BF16)
+      epilogue_vec<TXL_BF16, -1>(o, acc, mb, nb);
+    else
+      epilogue_vec<TXL_F32, -1>(o, acc, mb, nb);
+    return;
+  }
+  // Rare layouts (unaligned or odd leading dimension): one element at a time
+  // through an LDS transpose, so that the accumulators are only indexed
+  // statically.
+  barrier_lds();
+  float* stage = reinterpret_cast<float*>(smem) + wave * (32 * 33);
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      // only i is dynamic here; acc[i] is selected with a switch to keep it static
+      floatx16 a = i == 0 ? acc[0][j] : i == 1 ? acc[1][j] : i == 2 ? acc[2][j] : acc[3][j];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) stage[lrow * 33 + 8 * (e >> 2) + 4 * lhalf + (e & 3)] = a[e];
+      wave_lds_fence();
+      // stage[m_local][n_local] for m = mb - lrow + m_local, n = nb - 4*lhalf + 32j + n_local
+      for (int t = lane; t < 32 * 32; t += 64) {
+        const int ml = t >> 5, nl = t & 31;
+        const int32_t m = m0 + wm * 128 + 32 * i + ml;
+        const int32_t n = n0 + wn * 128 + 32 * j + nl;
+        if (m < o.m_valid && n < o.n_valid)
+          epi_store(o, axis_off(o.row, m) + axis_off(o.col, n), stage[ml * 33 + nl]);
       }
+      wave_lds_fence();
     }
   }
 }

@@ -32,14 +32,46 @@ struct RowSrc {
   const void* p1;  // HTILDE segment base
 };
 
+#if defined(__HIPCC__)
+#define TXL_HD __host__ __device__
+#else
+#define TXL_HD
+#endif
+
 // Output address of element (m, n) = rowoff(m) + coloff(n), with
 //   off(x) = (x / div) * s1 + (x % div) * s2.
 // Covers row-major stores, head-split stores [b][head][r][c] and transposed
-// head-split stores [b][head][c][r].
+// head-split stores [b][head][c][r].  The quotient uses a precomputed
+// multiply-shift (exact for 0 <= x < 2^31); div == kLinearDiv means q = 0.
 struct AxisMap {
   int32_t div;
+  uint32_t mul;
+  int32_t shift;
   int64_t s1, s2;
 };
+
+constexpr int32_t kLinearDiv = 0x7fffffff;
+
+// Multiplier and shift with floor(x / d) == (x * mul) >> shift for all
+// 0 <= x < 2^31 (round-up reciprocal with l = ceil(log2 d) extra bits).
+inline AxisMap make_axis(int32_t div, int64_t s1, int64_t s2) {
+  AxisMap a{div, 0u, 0, s1, s2};
+  if (div == kLinearDiv) return a;
+  int l = 0;
+  while ((1ull << l) < (uint64_t)div) ++l;
+  a.mul = (uint32_t)(((1ull << (31 + l)) / (uint64_t)div) + 1);
+  a.shift = 31 + l;
+  return a;
+}
+
+TXL_HD inline int32_t axis_quot(const AxisMap& a, int32_t x) {
+  return (int32_t)(((uint64_t)(uint32_t)x * a.mul) >> a.shift);
+}
+
+TXL_HD inline int64_t axis_offset(const AxisMap& a, int32_t x) {
+  const int32_t q = axis_quot(a, x);
+  return (int64_t)q * a.s1 + (int64_t)(x - q * a.div) * a.s2;
+}
 
 enum EpiFlags : int32_t { EPI_RELU = 1, EPI_RESID = 2 };
 
@@ -47,6 +79,8 @@ struct OutDst {
   void* p;
   int32_t dtype;         // TXL_F32 / TXL_BF16
   int32_t flags;         // EpiFlags
+  int32_t vec_ok;        // groups of 4 columns (n % 4 == 0) are contiguous and
+                         // 16-byte (f32) / 8-byte (bf16) aligned
   int32_t m_valid, n_valid;  // store only m < m_valid, n < n_valid
   AxisMap row, col;
   const float* resid;    // EPI_RESID: out += resid[rowoff + coloff] (same map)
@@ -91,6 +125,7 @@ struct AttnArgs {
 int launch_gemm_bf16(const GemmGroup& g, void* stream);
 int launch_gemm_f32(const GemmGroup& g, void* stream);
 int launch_attn_bf16(const AttnArgs& a, void* stream);
+int launch_attn_combine(const AttnArgs& a, void* stream);
 int launch_attn_f32(const AttnArgs& a, void* stream);
 int launch_sinusoid(void* R, int32_t n_pos, int32_t d_pos, int32_t dtype, void* stream);
 int launch_mem_update(void* mem, int32_t start, const void* h, int32_t B, int32_t M, int32_t L,
