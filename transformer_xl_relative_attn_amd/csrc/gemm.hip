@@ -55,10 +55,14 @@ __device__ __forceinline__ void wait_vm(int n) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-// Workgroup barrier after this wave's LDS reads have completed (no wait on
-// outstanding global loads).
+// Workgroup barrier after this wave's LDS reads have completed, without
+// waiting on outstanding global loads.  The LDS wait is the compiler's own
+// s_waitcnt, so its wait-count bookkeeping knows the reads are done.
 __device__ __forceinline__ void barrier_lds() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt / expcnt untouched
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
 }
 
 // Vectorised epilogue: four consecutive output columns per store.  FLAGS < 0
@@ -117,8 +121,10 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(GemmGroup g, int32_t p
   const int32_t K = P.K;
 
   // LDS ring: stage s holds A rows [0,256) then B rows [0,256), each row 4
-  // chunks of 16 bytes; chunk c of row r is stored at slot c ^ ((r >> 1) & 3)
-  // so that 8 consecutive rows read at one chunk hit distinct banks.
+  // chunks of 16 bytes; chunk c of row r is stored at slot c ^ ((r >> 2) & 3).
+  // gfx950 serves a 16-byte read for 16 lanes at a time from 64 four-byte
+  // banks, so rows r, r+4, r+8, r+12 (same bank group at a 64-byte pitch) must
+  // use different slots: 16 consecutive rows then read one chunk conflict-free.
   __shared__ u32x4 smem[NSTAGE * STAGE_U];
 
   const int tid = threadIdx.x;
@@ -127,11 +133,11 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(GemmGroup g, int32_t p
 
   // LDS-DMA mapping: load i of this wave fills units [(4i + wave)*64, +64) of a
   // tile, i.e. row (4i + wave)*16 + lane/4, slot lane%4, which holds global
-  // chunk (lane%4) ^ ((row >> 1) & 3) = (lane%4) ^ ((lane >> 3) & 3).
-  const int gchunk = (lane & 3) ^ ((lane >> 3) & 3);
+  // chunk (lane%4) ^ ((row >> 2) & 3) = (lane%4) ^ ((lane >> 4) & 3).
+  const int gchunk = (lane & 3) ^ ((lane >> 4) & 3);
   const char* pa[LOADS];
   const char* pb[LOADS];
-  int64_t ka[LOADS], kb[LOADS];   // K-advance masks (all ones, or 0 for zero rows)
+  int64_t sa[LOADS], sb[LOADS];   // per-K-step advance: BK*2 bytes, or 0 for zero rows
   const char* zero = reinterpret_cast<const char*>(g_zero_chunk) + gchunk * 16;
 #pragma unroll
   for (int i = 0; i < LOADS; ++i) {
@@ -140,18 +146,23 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(GemmGroup g, int32_t p
     const char* b = (n0 + r < P.N) ? row_address(P.b, n0 + r, 2) : nullptr;
     pa[i] = a ? a + gchunk * 16 : zero;
     pb[i] = b ? b + gchunk * 16 : zero;
-    ka[i] = a ? -1 : 0;
-    kb[i] = b ? -1 : 0;
+    sa[i] = a ? BK * 2 : 0;
+    sb[i] = b ? BK * 2 : 0;
   }
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
 
-  auto issue = [&](int kt) {   // LDS-DMA of K-step kt into ring slot kt % NSTAGE
-    const int64_t koff = (int64_t)kt * BK * 2;
-    u32x4* st = smem + (kt % NSTAGE) * STAGE_U;
+  // LDS-DMA of the next K step into ring slot `slot`; the running pointers
+  // advance by one K step.  With `real` false (past the end of K) the zero
+  // chunk is loaded instead into a slot that is never read again, which keeps
+  // the instruction stream identical in every iteration.
+  auto issue = [&](int slot, bool real) {
+    u32x4* st = smem + slot * STAGE_U + wave_s * 64;
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
-      u32x4* dA = st + (4 * i + wave) * 64;
-      __builtin_amdgcn_global_load_lds(pa[i] + (koff & ka[i]), dA, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(pb[i] + (koff & kb[i]), dA + TILE_U, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(real ? pa[i] : zero, st + 4 * i * 64, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(real ? pb[i] : zero, st + 4 * i * 64 + TILE_U, 16, 0, 0);
+      pa[i] += sa[i];
+      pb[i] += sb[i];
     }
   };
 
@@ -163,11 +174,10 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(GemmGroup g, int32_t p
 
   const int nk = K / BK;
 #pragma unroll
-  for (int s = 0; s < NSTAGE; ++s)
-    if (s < nk) issue(s);
+  for (int s = 0; s < NSTAGE; ++s) issue(s, s < nk);
 
   const int lrow = lane & 31, lhalf = lane >> 5;
-  const int sw = (lrow >> 1) & 3;  // same for every fragment row of a lane
+  const int sw = (lrow >> 2) & 3;  // same for every fragment row of a lane
   int fa[4], fb[4];                // fragment row base (16-byte units) within a stage
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -199,7 +209,9 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(GemmGroup g, int32_t p
   //      k-step 0 fragments into F0 in between.
   // Reads are interleaved one per two MFMAs so the LDS queue never backs up.
   bf16x8 f0a[4], f0b[4], f1a[4], f1b[4];
-  wait_vm((min(NSTAGE, nk) - 1) * 2 * LOADS);
+  // every iteration issues exactly one stage, so the counts below are fixed:
+  // stage kt+1 has landed once 2 stages (16 loads) issued after it remain
+  wait_vm((NSTAGE - 1) * 2 * LOADS);
   barrier_lds();
   read_frags(smem, 0, f0a, f0b);
   for (int kt = 0; kt < nk; ++kt) {
@@ -212,13 +224,11 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(GemmGroup g, int32_t p
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 LDS read
     }
     __builtin_amdgcn_sched_barrier(0);
-    if (kt + 1 < nk) {
-      const int after = min(NSTAGE - 2, nk - 2 - kt);
-      wait_vm(after * 2 * LOADS);
-      barrier_lds();
-      if (kt + NSTAGE < nk) issue(kt + NSTAGE);
-      read_frags(smem + ((kt + 1) % NSTAGE) * STAGE_U, 0, f0a, f0b);
-    }
+    // (in the last iteration this refills nothing and reads a stale slot)
+    wait_vm((NSTAGE - 2) * 2 * LOADS);
+    barrier_lds();
+    issue(kt % NSTAGE, kt + NSTAGE < nk);
+    read_frags(smem + ((kt + 1) % NSTAGE) * STAGE_U, 0, f0a, f0b);
     mfma16(f1a, f1b);
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
@@ -228,6 +238,9 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(GemmGroup g, int32_t p
     }
     __builtin_amdgcn_sched_barrier(0);
   }
+  // the tail iterations' zero-chunk loads must land before the LDS is reused
+  // or the workgroup exits
+  wait_vm(0);
 
   // ---- epilogue, straight from the accumulators.  The MFMA operands are
   // swapped (B fragment first), so block (i, j) holds C^T: element 4g + r of a
