@@ -212,3 +212,28 @@ def test_c5_stack_16_layers(txl):
         assert_close(outs[s][b_idx], o_outs[s], "bf16", f"segment {s}")
     _check_ring(dl, wl, o_mems, start_o, start, b_idx, layer=0, exact=True)
     _check_ring(dl, wl, o_mems, start_o, start, b_idx, layer=15, exact=False)
+
+
+def test_segment_step_in_place(txl):
+    """h_out may be the same buffer as h_in: the memory must still receive the
+    layer input, not the attention output."""
+    import torch
+    cfg = synth.Config("inplace", 2, 128, 2, 64, 40, 72, 1, 3, "bf16", 0.05, 4321)
+    log("[case] in-place segment step")
+    wl = synth.make_workload(cfg)
+    dl = DeviceLayers(wl)
+    shp = dl.shape()
+    ws = workspace(txl.txl_segment_workspace_bytes(shp, 1, 0))
+    layers = dl.layer_structs()
+    start = 0
+    outs = []
+    for s in range(3):
+        h = to_dev(wl.segments[s], "bf16")
+        start = txl.txl_segment_step(shp, 1, 0, layers, dl.R, h, h, start, ws)
+        torch.cuda.synchronize()
+        outs.append(from_dev(h))
+    b_idx = np.arange(2)
+    o_outs, o_mems, start_o = oracle_stream(wl, 3, b_idx)
+    for s in range(3):
+        assert_close(outs[s], o_outs[s], "bf16", f"segment {s}")
+    _check_ring(dl, wl, o_mems, start_o, start, b_idx)

@@ -424,10 +424,20 @@ txl_status_t run_rel_attn(const AttnPlan& p, const AttnPtrs& a, char* ws, void* 
   TXL_TRY(after_launch(timed(K_PROJ_GEMM, stream, [&] { return launch_gemm(g, dt, stream); }),
                        "projection GEMMs", stream));
 
+  // The ring update is folded into the bf16 attention kernel when rows are
+  // 16-byte multiples; otherwise it is a kernel of its own.
+  // (not when the output overlaps h: other workgroups may still be copying it)
+  const char* h_lo = static_cast<const char*>(a.h);
+  const char* h_hi = h_lo + (size_t)p.B * p.L * p.d * esize(dt);
+  const char* o_lo = static_cast<const char*>(a.out);
+  const char* o_hi = o_lo + (size_t)p.B * p.L * p.H * p.dh * esize(dt);
+  const bool overlap = o_lo < h_hi && h_lo < o_hi;
+  const bool fuse_upd = mem_upd && bf && p.M > 0 && (p.d * 2) % 16 == 0 && !overlap;
   if (mem_upd) {
-    TXL_TRY(after_launch(timed(K_MEM_UPDATE, stream, [&] { return launch_mem_update(mem_upd, a.mem_start, a.h, p.B, p.M, p.L, p.d, dt,
-                                           stream); }),
-                         "memory update", stream));
+    if (!fuse_upd)
+      TXL_TRY(after_launch(timed(K_MEM_UPDATE, stream, [&] { return launch_mem_update(mem_upd, a.mem_start, a.h, p.B, p.M, p.L, p.d, dt,
+                                             stream); }),
+                           "memory update", stream));
     *new_start = (p.M == 0) ? 0 : (p.L < p.M ? (a.mem_start + p.L) % p.M : 0);
   }
 
@@ -452,6 +462,13 @@ txl_status_t run_rel_attn(const AttnPlan& p, const AttnPtrs& a, char* ws, void* 
   aa.part_o = p.n_split > 1 ? reinterpret_cast<float*>(ws + p.po.off) : nullptr;
   aa.part_ml = p.n_split > 1 ? reinterpret_cast<float*>(ws + p.pml.off) : nullptr;
   aa.dtype = dt;
+  if (fuse_upd) {
+    aa.upd_src = a.h;
+    aa.upd_mem = mem_upd;
+    aa.upd_start = a.mem_start;
+    aa.upd_rows = p.L < p.M ? p.L : p.M;
+    aa.upd_row_bytes = (int64_t)p.d * 2;
+  }
   TXL_TRY(after_launch(timed(K_ATTN, stream,
                              [&] {
                                return bf ? launch_attn_bf16(aa, stream)

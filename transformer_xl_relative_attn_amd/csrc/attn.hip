@@ -51,6 +51,7 @@ struct AttnSmem {
   uint16_t vt[DP * VST];              // V^T tile [d][key]
   u32x4 rk[RK_SLOTS][KB * 8];         // Rk chunk ring, swizzled like K
   float bd[NWAVE][32 * BDS];          // per-wave shifted (b)+(d) window
+  float uv[2 * DP];                   // u then v of this head, zero padded
 };
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * 8 + (chunk ^ (row & 7)); }
@@ -75,6 +76,24 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a, int32_t p
 
   __shared__ AttnSmem sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  // Optional fused memory-ring update (segment step): this workgroup copies
+  // segment rows wid, wid + total, ... into their ring slots.  The projections
+  // that read the old memory ran before this kernel.
+  if (a.upd_mem) {
+    const int64_t chunks = a.upd_row_bytes / 16;
+    const int32_t nrow = a.B * a.upd_rows;
+    for (int32_t r = wid; r < nrow; r += total) {
+      const int32_t bb = r / a.upd_rows, t = r - bb * a.upd_rows;
+      const int32_t src = a.L < a.M ? t : a.L - a.M + t;
+      const int32_t slot = a.L < a.M ? (a.upd_start + t) % a.M : t;
+      const u32x4* sp = reinterpret_cast<const u32x4*>(
+          static_cast<const char*>(a.upd_src) + ((int64_t)bb * a.L + src) * a.upd_row_bytes);
+      u32x4* dp = reinterpret_cast<u32x4*>(static_cast<char*>(a.upd_mem) +
+                                           ((int64_t)bb * a.M + slot) * a.upd_row_bytes);
+      for (int64_t c = tid; c < chunks; c += 256) dp[c] = sp[c];
+    }
+  }
   const int ii = lane & 31, hf = lane >> 5;
 
   const int32_t i_base = qg * QG;
@@ -120,23 +139,28 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a, int32_t p
     sm.rk[slot][swz(kr, kc)] = x;
   };
 
-  // ---- per-wave query operands: (q+u)*c and (q+v)*c as bf16, d = 16s + 8hf + e
+  // ---- per-wave query operands: (q+u)*c and (q+v)*c as bf16, d = 16s + 8hf + e.
+  // u and v of this head are staged once in LDS, zero-padded to 64 columns.
+  if (tid < 2 * DP) {
+    const int d = tid & (DP - 1);
+    const uint16_t* src = static_cast<const uint16_t*>(tid < DP ? a.u : a.v) + (int64_t)head * a.dh;
+    sm.uv[tid] = d < a.dh ? bf16_to_f32(src[d]) : 0.0f;
+  }
+  __syncthreads();
   bf16x8 qu[4], qv[4];
   {
-    const float* qrow = a.q + ((int64_t)bh * a.Lp + (wave_on ? i0 + ii : 0)) * DP;
-    const uint16_t* ub = static_cast<const uint16_t*>(a.u) + (int64_t)head * a.dh;
-    const uint16_t* vb = static_cast<const uint16_t*>(a.v) + (int64_t)head * a.dh;
+    const floatx4* qrow =
+        reinterpret_cast<const floatx4*>(a.q + ((int64_t)bh * a.Lp + (wave_on ? i0 + ii : 0)) * DP);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
+      const int d0 = 16 * s + 8 * hf;
+      const floatx4 q0 = qrow[d0 / 4], q1 = qrow[d0 / 4 + 1];
       float xu[8], xv[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int d = 16 * s + 8 * hf + e;
-        const float qd = qrow[d];
-        const float ud = d < a.dh ? bf16_to_f32(ub[d]) : 0.0f;
-        const float vd_ = d < a.dh ? bf16_to_f32(vb[d]) : 0.0f;
-        xu[e] = (qd + ud) * a.c_scale;
-        xv[e] = (qd + vd_) * a.c_scale;
+        const float qd = e < 4 ? q0[e] : q1[e - 4];
+        xu[e] = (qd + sm.uv[d0 + e]) * a.c_scale;
+        xv[e] = (qd + sm.uv[DP + d0 + e]) * a.c_scale;
       }
       qu[s] = pack8(xu);
       qv[s] = pack8(xv);
@@ -217,7 +241,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a, int32_t p
       mb = fmaxf(mb, __shfl_xor(mb, 32));
       const bool need = mb > m_ref + 8.0f;
       if (__ballot(need)) {
-        const float alpha = need ? exp2f(m_ref - mb) : 1.0f;
+        const float alpha = need ? __builtin_amdgcn_exp2f(m_ref - mb) : 1.0f;
         if (need) m_ref = mb;
         l_sum *= alpha;
 #pragma unroll
@@ -230,7 +254,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a, int32_t p
       float p[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        p[e] = exp2f(s[e] - m_use);
+        p[e] = __builtin_amdgcn_exp2f(s[e] - m_use);
         l_sum += p[e];
       }
       // P^T (keys x queries) times V^T: k-slot order (16t2 + 4hf + r, 16t2 + 8 + 4hf + r)
@@ -259,57 +283,77 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a, int32_t p
   if (!wave_on) return;
   l_sum += __shfl_xor(l_sum, 32);
   const int32_t i = i0 + ii;
+  // lane holds d = 32e + 8g + 4hf + r (r = 0..3): four consecutive columns per (e, g)
   if (a.n_split == 1) {
     if (i >= L) return;
     const float inv = 1.0f / l_sum;
     uint16_t* out = static_cast<uint16_t*>(a.out) + (((int64_t)b * L + i) * a.H + head) * a.dh;
+    const bool vec = (a.dh == DP);
 #pragma unroll
     for (int e = 0; e < 2; ++e)
 #pragma unroll
-      for (int r16 = 0; r16 < 16; ++r16) {
-        const int d = 32 * e + 8 * (r16 >> 2) + 4 * hf + (r16 & 3);
-        if (d < a.dh) out[d] = f32_to_bf16_bits(o[e][r16] * inv);
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * e + 8 * g + 4 * hf;
+        if (vec) {
+          typedef float floatx2_t __attribute__((ext_vector_type(2)));
+          typedef bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+          const bf16x2_t lo = __builtin_convertvector(
+              floatx2_t{o[e][4 * g] * inv, o[e][4 * g + 1] * inv}, bf16x2_t);
+          const bf16x2_t hi = __builtin_convertvector(
+              floatx2_t{o[e][4 * g + 2] * inv, o[e][4 * g + 3] * inv}, bf16x2_t);
+          *reinterpret_cast<u32x2*>(out + d0) =
+              u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (d0 + r < a.dh) out[d0 + r] = f32_to_bf16_bits(o[e][4 * g + r] * inv);
+        }
       }
   } else {
     const int64_t row = (int64_t)split * a.B * a.H * a.Lp + (int64_t)bh * a.Lp + i;
-    float* po = a.part_o + row * DP;
+    floatx4* po = reinterpret_cast<floatx4*>(a.part_o + row * DP);
 #pragma unroll
     for (int e = 0; e < 2; ++e)
 #pragma unroll
-      for (int r16 = 0; r16 < 16; ++r16) {
-        const int d = 32 * e + 8 * (r16 >> 2) + 4 * hf + (r16 & 3);
-        po[d] = o[e][r16];
-      }
-    if (hf == 0) {
-      a.part_ml[row * 2 + 0] = m_ref;
-      a.part_ml[row * 2 + 1] = l_sum;
-    }
+      for (int g = 0; g < 4; ++g)
+        po[(32 * e + 8 * g + 4 * hf) / 4] =
+            floatx4{o[e][4 * g], o[e][4 * g + 1], o[e][4 * g + 2], o[e][4 * g + 3]};
+    if (hf == 0) a.part_ml[row * 2 + 0] = m_ref;
+    if (hf == 0) a.part_ml[row * 2 + 1] = l_sum;
   }
 }
 
 // Merge split partials in split order: out = sum_s 2^(m_s-m*) O_s / sum_s 2^(m_s-m*) l_s.
-// Partials of the fp32 path use width dh (row stride dp_stride).
-__global__ void attn_combine_kernel(AttnArgs a, int32_t dp_stride) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+// 16 threads per output row, 4 columns each.
+__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
+  const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);   // (b, h, i), i < L
+  const int c4 = threadIdx.x & 15;
   const int64_t rows = (int64_t)a.B * a.H * a.L;
-  if (idx >= rows * a.dh) return;
-  const int32_t d = idx % a.dh;
-  const int64_t r = idx / a.dh;                // (b, h, i) with i < L
-  const int32_t i = r % a.L;
-  const int64_t bh = r / a.L;
+  if (row >= rows) return;
+  const int32_t i = row % a.L;
+  const int64_t bh = row / a.L;
   const int32_t b = bh / a.H, head = bh % a.H;
   const int64_t prow = bh * a.Lp + i;
   const int64_t stride = (int64_t)a.B * a.H * a.Lp;
   float mx = kNegInf;
   for (int s = 0; s < a.n_split; ++s) mx = fmaxf(mx, a.part_ml[(s * stride + prow) * 2]);
-  float num = 0.0f, den = 0.0f;
+  floatx4 num = floatx4{0.f, 0.f, 0.f, 0.f};
+  float den = 0.0f;
   for (int s = 0; s < a.n_split; ++s) {
-    const float ms = a.part_ml[(s * stride + prow) * 2];
-    const float w = (ms == kNegInf) ? 0.0f : exp2f(ms - mx);
-    num += w * a.part_o[(s * stride + prow) * dp_stride + d];
-    den += w * a.part_ml[(s * stride + prow) * 2 + 1];
+    const int64_t pr = s * stride + prow;
+    const float ms = a.part_ml[pr * 2];
+    const float w = (ms == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(ms - mx);
+    num += w * reinterpret_cast<const floatx4*>(a.part_o + pr * DP)[c4];
+    den += w * a.part_ml[pr * 2 + 1];
   }
-  store_from_f32(a.out, (((int64_t)b * a.L + i) * a.H + head) * a.dh + d, num / den, a.dtype);
+  const float inv = 1.0f / den;
+  uint16_t* out = static_cast<uint16_t*>(a.out) + ((int64_t)b * a.L + i) * a.H * a.dh +
+                  (int64_t)head * a.dh;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int d = 4 * c4 + r;
+    if (d < a.dh) out[d] = f32_to_bf16_bits(num[r] * inv);
+  }
 }
 
 // ------------------------------------------------------------ fp32 kernel
@@ -390,9 +434,9 @@ int launch_attn_bf16(const AttnArgs& a, void* stream) {
 }
 
 int launch_attn_combine(const AttnArgs& a, void* stream) {
-  const int64_t n = (int64_t)a.B * a.H * a.L * a.dh;
-  hipLaunchKernelGGL(attn_combine_kernel, dim3((n + 255) / 256), dim3(256), 0,
-                     static_cast<hipStream_t>(stream), a, DP);
+  const int64_t rows = (int64_t)a.B * a.H * a.L;
+  hipLaunchKernelGGL(attn_combine_kernel, dim3((rows + 15) / 16), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), a);
   return static_cast<int>(hipGetLastError());
 }
 

@@ -119,6 +119,12 @@ struct AttnArgs {
   float* part_o;           // split partials [n_split][B*H*Lp][DP]
   float* part_ml;          // [n_split][B*H*Lp][2] (running max, sum)
   int32_t dtype;
+  // optional fused ring update (bf16 kernel): copy min(L, M) rows of upd_src
+  // [B][L][*] into upd_mem [B][M][*] (row_bytes % 16 == 0); NULL = none
+  const void* upd_src;
+  void* upd_mem;
+  int32_t upd_start, upd_rows;
+  int64_t upd_row_bytes;
 };
 
 // Launch wrappers (return a hipError_t as int).
