@@ -31,14 +31,13 @@ constexpr int LOADS = TILE_U / NT;       // LDS-DMA loads per thread per operand
 // 128 bytes of zeros: the source of every "zero row" chunk (padding rows).
 __device__ __align__(16) uint32_t g_zero_chunk[32];
 
-__device__ __forceinline__ const GemmProblem* find_problem(const GemmGroup& g, int32_t tile,
-                                                           int32_t* local) {
+__device__ __forceinline__ int find_problem(const GemmGroup& g, int32_t tile, int32_t* local) {
   int idx = 0;
 #pragma unroll
   for (int i = 1; i < kMaxGroup; ++i)
     if (i < g.count && tile >= g.p[i].tile_begin) idx = i;
   *local = tile - g.p[idx].tile_begin;
-  return &g.p[idx];
+  return idx;
 }
 
 // Wait until at most n LDS-DMA loads of this wave are still in flight.  The
@@ -110,142 +109,14 @@ __device__ __forceinline__ void epilogue_vec(const OutDst& o, const floatx16 (&a
     }
 }
 
-__global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(GemmGroup g, int32_t padded) {
-  const int32_t tile = xcd_swizzle(blockIdx.x, padded);
-  if (tile >= g.total_tiles) return;
-  int32_t local;
-  const GemmProblem& P = *find_problem(g, tile, &local);
-  // consecutive tiles share the A rows (tm), sweeping n fastest
-  const int32_t tm = local / P.tiles_n, tn = local - tm * P.tiles_n;
-  const int32_t m0 = tm * BM, n0 = tn * BN;
-  const int32_t K = P.K;
-
-  // LDS ring: stage s holds A rows [0,256) then B rows [0,256), each row 4
-  // chunks of 16 bytes; chunk c of row r is stored at slot c ^ ((r >> 2) & 3).
-  // gfx950 serves a 16-byte read for 16 lanes at a time from 64 four-byte
-  // banks, so rows r, r+4, r+8, r+12 (same bank group at a 64-byte pitch) must
-  // use different slots: 16 consecutive rows then read one chunk conflict-free.
-  __shared__ u32x4 smem[NSTAGE * STAGE_U];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-
-  // LDS-DMA mapping: load i of this wave fills units [(4i + wave)*64, +64) of a
-  // tile, i.e. row (4i + wave)*16 + lane/4, slot lane%4, which holds global
-  // chunk (lane%4) ^ ((row >> 2) & 3) = (lane%4) ^ ((lane >> 4) & 3).
-  const int gchunk = (lane & 3) ^ ((lane >> 4) & 3);
-  const char* pa[LOADS];
-  const char* pb[LOADS];
-  int64_t sa[LOADS], sb[LOADS];   // per-K-step advance: BK*2 bytes, or 0 for zero rows
-  const char* zero = reinterpret_cast<const char*>(g_zero_chunk) + gchunk * 16;
-#pragma unroll
-  for (int i = 0; i < LOADS; ++i) {
-    const int r = (4 * i + wave) * 16 + (lane >> 2);
-    const char* a = (m0 + r < P.M) ? row_address(P.a, m0 + r, 2) : nullptr;
-    const char* b = (n0 + r < P.N) ? row_address(P.b, n0 + r, 2) : nullptr;
-    pa[i] = a ? a + gchunk * 16 : zero;
-    pb[i] = b ? b + gchunk * 16 : zero;
-    sa[i] = a ? BK * 2 : 0;
-    sb[i] = b ? BK * 2 : 0;
-  }
-  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
-
-  // LDS-DMA of the next K step into ring slot `slot`; the running pointers
-  // advance by one K step.  With `real` false (past the end of K) the zero
-  // chunk is loaded instead into a slot that is never read again, which keeps
-  // the instruction stream identical in every iteration.
-  auto issue = [&](int slot, bool real) {
-    u32x4* st = smem + slot * STAGE_U + wave_s * 64;
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      __builtin_amdgcn_global_load_lds(real ? pa[i] : zero, st + 4 * i * 64, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(real ? pb[i] : zero, st + 4 * i * 64 + TILE_U, 16, 0, 0);
-      pa[i] += sa[i];
-      pb[i] += sb[i];
-    }
-  };
-
-  floatx16 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = floatx16{0};
-
-  const int nk = K / BK;
-#pragma unroll
-  for (int s = 0; s < NSTAGE; ++s) issue(s, s < nk);
-
-  const int lrow = lane & 31, lhalf = lane >> 5;
-  const int sw = (lrow >> 2) & 3;  // same for every fragment row of a lane
-  int fa[4], fb[4];                // fragment row base (16-byte units) within a stage
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    fa[i] = (wm * 128 + i * 32 + lrow) * CH;
-    fb[i] = TILE_U + (wn * 128 + i * 32 + lrow) * CH;
-  }
-  // fragments of k-step s (0 or 1) of a staged 32-wide K step
-  auto read_frags = [&](const u32x4* st, int s, bf16x8* af, bf16x8* bfr) {
-    const int c = (2 * s + lhalf) ^ sw;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      af[i] = __builtin_bit_cast(bf16x8, st[fa[i] + c]);
-      bfr[i] = __builtin_bit_cast(bf16x8, st[fb[i] + c]);
-    }
-  };
-  auto mfma16 = [&](const bf16x8* af, const bf16x8* bfr) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
-  };
-
-  // Pipeline per K step kt (ring slot kt % NSTAGE):
-  //   A: MFMAs of k-step 0 (fragments F0 already in registers), reading the
-  //      k-step 1 fragments F1 in between;
-  //   wait for step kt+1 to land, barrier (slot kt % NSTAGE is then free);
-  //   B: refill that slot with step kt+NSTAGE, MFMAs of F1, reading step kt+1's
-  //      k-step 0 fragments into F0 in between.
-  // Reads are interleaved one per two MFMAs so the LDS queue never backs up.
-  bf16x8 f0a[4], f0b[4], f1a[4], f1b[4];
-  // every iteration issues exactly one stage, so the counts below are fixed:
-  // stage kt+1 has landed once 2 stages (16 loads) issued after it remain
-  wait_vm((NSTAGE - 1) * 2 * LOADS);
-  barrier_lds();
-  read_frags(smem, 0, f0a, f0b);
-  for (int kt = 0; kt < nk; ++kt) {
-    const u32x4* st = smem + (kt % NSTAGE) * STAGE_U;
-    read_frags(st, 1, f1a, f1b);
-    mfma16(f0a, f0b);
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // 2 MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 LDS read
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    // (in the last iteration this refills nothing and reads a stale slot)
-    wait_vm((NSTAGE - 2) * 2 * LOADS);
-    barrier_lds();
-    issue(kt % NSTAGE, kt + NSTAGE < nk);
-    read_frags(smem + ((kt + 1) % NSTAGE) * STAGE_U, 0, f0a, f0b);
-    mfma16(f1a, f1b);
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);   // 2 MFMA
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);   // 1 global->LDS load
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);   // 1 LDS read
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  // the tail iterations' zero-chunk loads must land before the LDS is reused
-  // or the workgroup exits
-  wait_vm(0);
-
-  // ---- epilogue, straight from the accumulators.  The MFMA operands are
-  // swapped (B fragment first), so block (i, j) holds C^T: element 4g + r of a
-  // lane is C[m][n] with m = mb + 32i and n = nb + 32j + 8g + r, i.e. four
-  // consecutive output columns of one row per (i, j, g).
+// Epilogue of one tile, straight from the accumulators.  The MFMA operands are
+// swapped (B fragment first), so block (i, j) holds C^T: element 4g + r of a
+// lane is C[m][n] with m = mb + 32i and n = nb + 32j + 8g + r, i.e. four
+// consecutive output columns of one row per (i, j, g).
+__device__ __forceinline__ void epilogue(const GemmProblem& P, const floatx16 (&acc)[4][4],
+                                         int32_t m0, int32_t n0, int wm, int wn, int lane,
+                                         u32x4* smem) {
+  const int lrow = lane & 31, lhalf = lane >> 5, wave = wm * 2 + wn;
   const OutDst& o = P.out;
   const int32_t mb = m0 + wm * 128 + lrow;
   const int32_t nb = n0 + wn * 128 + 4 * lhalf;
@@ -262,8 +133,9 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(GemmGroup g, int32_t p
   }
   // Rare layouts (unaligned or odd leading dimension): one element at a time
   // through an LDS transpose, so that the accumulators are only indexed
-  // statically.
-  barrier_lds();
+  // statically.  The ring is idle (all reads done) but the last K steps'
+  // zero-chunk loads may still be landing in it.
+  wait_vm(0);
   float* stage = reinterpret_cast<float*>(smem) + wave * (32 * 33);
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -286,6 +158,171 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(GemmGroup g, int32_t p
   }
 }
 
+__global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(GemmGroup g, int32_t padded,
+                                                          int32_t grid) {
+  // LDS ring: stage s holds A rows [0,256) then B rows [0,256), each row 4
+  // chunks of 16 bytes; chunk c of row r is stored at slot c ^ ((r >> 2) & 3).
+  // gfx950 serves a 16-byte read for 16 lanes at a time from 64 four-byte
+  // banks, so rows r, r+4, r+8, r+12 (same bank group at a 64-byte pitch) must
+  // use different slots: 16 consecutive rows then read one chunk conflict-free.
+  __shared__ u32x4 smem[NSTAGE * STAGE_U];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+
+  // LDS-DMA mapping: load i of this wave fills units [(4i + wave)*64, +64) of a
+  // tile, i.e. row (4i + wave)*16 + lane/4, slot lane%4, which holds global
+  // chunk (lane%4) ^ ((row >> 2) & 3) = (lane%4) ^ ((lane >> 4) & 3).
+  const int gchunk = (lane & 3) ^ ((lane >> 4) & 3);
+  const char* zero = reinterpret_cast<const char*>(g_zero_chunk) + gchunk * 16;
+
+  // Persistent: this workgroup walks tiles seq = blockIdx.x, +grid, ...; the
+  // XCD swizzle keeps tiles that share A rows on one XCD.
+  int32_t seq = blockIdx.x;
+  auto next_tile = [&](int32_t s) {   // first valid tile at or after sequence s
+    while (s < padded && xcd_swizzle(s, padded) >= g.total_tiles) s += grid;
+    return s;
+  };
+  seq = next_tile(seq);
+  if (seq >= padded) return;
+
+  // per-tile state (the problem is addressed by index: a pointer into the
+  // kernel-argument block would force a private copy of it)
+  int pidx = 0;
+  int32_t m0 = 0, n0 = 0, nk = 0;
+  const char* pa[LOADS];
+  const char* pb[LOADS];
+  int64_t sa[LOADS], sb[LOADS];   // per-K-step advance: BK*2 bytes, or 0 for zero rows
+  auto setup = [&](int32_t tile) {
+    int32_t local;
+    pidx = find_problem(g, tile, &local);
+    const GemmProblem& P = g.p[pidx];
+    // consecutive tiles share the A rows (tm), sweeping n fastest
+    const int32_t tm = local / P.tiles_n, tn = local - tm * P.tiles_n;
+    m0 = tm * BM;
+    n0 = tn * BN;
+    nk = P.K / BK;
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int r = (4 * i + wave) * 16 + (lane >> 2);
+      const char* a = (m0 + r < P.M) ? row_address(P.a, m0 + r, 2) : nullptr;
+      const char* b = (n0 + r < P.N) ? row_address(P.b, n0 + r, 2) : nullptr;
+      pa[i] = a ? a + gchunk * 16 : zero;
+      pb[i] = b ? b + gchunk * 16 : zero;
+      sa[i] = a ? BK * 2 : 0;
+      sb[i] = b ? BK * 2 : 0;
+    }
+  };
+
+  // LDS-DMA of the next K step into ring slot `slot`; the running pointers
+  // advance by one K step.  With `real` false (past the end of K) the zero
+  // chunk is loaded instead into a slot that is never read again, which keeps
+  // the instruction stream identical in every iteration.
+  auto issue = [&](int slot, bool real) {
+    u32x4* st = smem + slot * STAGE_U + wave_s * 64;
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      __builtin_amdgcn_global_load_lds(real ? pa[i] : zero, st + 4 * i * 64, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(real ? pb[i] : zero, st + 4 * i * 64 + TILE_U, 16, 0, 0);
+      pa[i] += sa[i];
+      pb[i] += sb[i];
+    }
+  };
+
+  const int lrow = lane & 31, lhalf = lane >> 5;
+  const int sw = (lrow >> 2) & 3;  // same for every fragment row of a lane
+  int fa[4], fb[4];                // fragment row base (16-byte units) within a stage
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    fa[i] = (wm * 128 + i * 32 + lrow) * CH;
+    fb[i] = TILE_U + (wn * 128 + i * 32 + lrow) * CH;
+  }
+  // fragments of k-step s (0 or 1) of a staged 32-wide K step
+  auto read_frags = [&](const u32x4* st, int s, bf16x8* af, bf16x8* bfr) {
+    const int c = (2 * s + lhalf) ^ sw;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      af[i] = __builtin_bit_cast(bf16x8, st[fa[i] + c]);
+      bfr[i] = __builtin_bit_cast(bf16x8, st[fb[i] + c]);
+    }
+  };
+  floatx16 acc[4][4];
+  auto mfma16 = [&](const bf16x8* af, const bf16x8* bfr) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+  };
+
+  setup(xcd_swizzle(seq, padded));
+#pragma unroll
+  for (int s = 0; s < NSTAGE; ++s) issue(s, s < nk);
+
+  while (true) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = floatx16{0};
+
+    // Pipeline per K step kt (ring slot kt % NSTAGE):
+    //   A: MFMAs of k-step 0 (fragments F0 already in registers), reading the
+    //      k-step 1 fragments F1 in between;
+    //   wait for step kt+1 to land, barrier (slot kt % NSTAGE is then free);
+    //   B: refill that slot with step kt+NSTAGE, MFMAs of F1, reading step kt+1's
+    //      k-step 0 fragments into F0 in between.
+    // Reads are interleaved one per two MFMAs so the LDS queue never backs up.
+    // Every iteration issues exactly one stage and loads return in order, so
+    // the counts are fixed: stage 0 has landed once at most 3 stages (24
+    // loads) issued after it remain, stage kt+1 once at most 2 stages remain
+    // (outstanding epilogue stores of the previous tile only make these waits
+    // stricter).
+    bf16x8 f0a[4], f0b[4], f1a[4], f1b[4];
+    wait_vm((NSTAGE - 1) * 2 * LOADS);
+    barrier_lds();
+    read_frags(smem, 0, f0a, f0b);
+    for (int kt = 0; kt < nk; ++kt) {
+      const u32x4* st = smem + (kt % NSTAGE) * STAGE_U;
+      read_frags(st, 1, f1a, f1b);
+      mfma16(f0a, f0b);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // 2 MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 LDS read
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // (in the last iteration this refills nothing and reads a stale slot)
+      wait_vm((NSTAGE - 2) * 2 * LOADS);
+      barrier_lds();
+      issue(kt % NSTAGE, kt + NSTAGE < nk);
+      read_frags(smem + ((kt + 1) % NSTAGE) * STAGE_U, 0, f0a, f0b);
+      mfma16(f1a, f1b);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);   // 2 MFMA
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);   // 1 global->LDS load
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);   // 1 LDS read
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // every wave is done reading the ring before it is refilled for the next tile
+    barrier_lds();
+
+    epilogue(g.p[pidx], acc, m0, n0, wm, wn, lane, smem);
+
+    seq = next_tile(seq + grid);
+    if (seq >= padded) break;
+    barrier_lds();   // the epilogue may have used the ring for staging
+    setup(xcd_swizzle(seq, padded));
+#pragma unroll
+    for (int s = 0; s < NSTAGE; ++s) issue(s, s < nk);
+  }
+  // no LDS-DMA may still be writing when the workgroup exits
+  wait_vm(0);
+}
+
 // ------------------------------------------------------------------ fp32 GEMM
 constexpr int FT = 64, FK = 16;
 
@@ -293,7 +330,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmGroup g, int32_t padd
   const int32_t tile = xcd_swizzle(blockIdx.x, padded);
   if (tile >= g.total_tiles) return;
   int32_t local;
-  const GemmProblem& P = *find_problem(g, tile, &local);
+  const GemmProblem& P = g.p[find_problem(g, tile, &local)];
   const int32_t tm = local / P.tiles_n, tn = local - tm * P.tiles_n;
   const int32_t m0 = tm * FT, n0 = tn * FT;
 
@@ -347,11 +384,28 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmGroup g, int32_t padd
 
 }  // namespace
 
+// Compute units of the current device (cached per device id).
+int32_t device_cu_count() {
+  static int32_t cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cached[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 int launch_gemm_bf16(const GemmGroup& g, void* stream) {
   if (g.total_tiles <= 0) return 0;
-  int32_t padded = (g.total_tiles + 7) & ~7;
-  hipLaunchKernelGGL(gemm_bf16_kernel, dim3(padded), dim3(NT), 0,
-                     static_cast<hipStream_t>(stream), g, padded);
+  const int32_t padded = (g.total_tiles + 7) & ~7;
+  // one persistent workgroup per compute unit (multiple of 8, the XCD count)
+  int32_t grid = (device_cu_count() + 7) & ~7;
+  if (grid > padded) grid = padded;
+  hipLaunchKernelGGL(gemm_bf16_kernel, dim3(grid), dim3(NT), 0,
+                     static_cast<hipStream_t>(stream), g, padded, grid);
   return static_cast<int>(hipGetLastError());
 }
 
