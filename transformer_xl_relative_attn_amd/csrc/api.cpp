@@ -306,6 +306,11 @@ OutDst out_map(void* ptr, int dtype, int32_t mv, int32_t nv, AxisMap row, AxisMa
   const bool ptr_ok = (reinterpret_cast<uintptr_t>(ptr) % 16) == 0 &&
                       (!resid || (reinterpret_cast<uintptr_t>(resid) % 16) == 0);
   o.vec_ok = col_ok && row_ok && ptr_ok && nv % 4 == 0;
+  // staged bf16 epilogue: 8 consecutive columns per 16-byte store, and rows
+  // advanced 4 at a time with at most one wrap of the row axis per step
+  const bool col8 = col.s2 == 1 && col.s1 % 8 == 0 && (col.div == kLinearDiv || col.div % 8 == 0);
+  const bool row8 = row.s1 % 8 == 0 && row.s2 % 8 == 0 && row.div >= 4;
+  o.vec8_ok = dtype == TXL_BF16 && col8 && row8 && ptr_ok && nv % 8 == 0;
   return o;
 }
 

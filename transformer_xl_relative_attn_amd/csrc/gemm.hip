@@ -109,6 +109,74 @@ __device__ __forceinline__ void epilogue_vec(const OutDst& o, const floatx16 (&a
     }
 }
 
+// bf16 output without residual / activation: the wave's 128x128 sub-tile
+// (rows mw.., columns nw..) passes through the wave's own 32 KB of the idle
+// LDS ring, so that the global stores write whole lines (16 lanes cover 256
+// contiguous bytes of one row) instead of 16-byte pieces of 32 rows, which
+// the L2 would receive as 32 partial-line writes per instruction.  Staging
+// layout: row r (0..127) is 16 chunks of 16 bytes, chunk c at slot c ^ (r & 15);
+// both the 8-byte writes (32 rows x 2 halves) and the 16-byte reads (16 lanes
+// per row) are then spread over all 64 banks.
+__device__ __forceinline__ void epilogue_staged(const OutDst& o, const floatx16 (&acc)[4][4],
+                                                int32_t mw, int32_t nw, int lane,
+                                                u32x4* region) {
+  typedef float floatx2_t __attribute__((ext_vector_type(2)));
+  typedef bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  char* base = reinterpret_cast<char*>(region);
+  const int lrow = lane & 31, lhalf = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 32 * i + lrow;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int c = 4 * j + q;   // columns 32j + 8q + 4*lhalf .. +3
+        const bf16x2_t lo =
+            __builtin_convertvector(floatx2_t{acc[i][j][4 * q], acc[i][j][4 * q + 1]}, bf16x2_t);
+        const bf16x2_t hi =
+            __builtin_convertvector(floatx2_t{acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]}, bf16x2_t);
+        *reinterpret_cast<u32x2*>(base + r * 256 + ((c ^ (r & 15)) << 4) + 8 * lhalf) =
+            u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+      }
+  }
+  wave_lds_fence();
+
+  // lane -> chunk c = lane % 16 (columns nw + 8c .. +7) of rows 4t + lane/16
+  const int c = lane & 15, rsub = lane >> 4;
+  const int32_t n = nw + 8 * c;
+  const bool nok = n < o.n_valid;
+  const int64_t coff = axis_off(o.col, n);
+  // row offsets advance incrementally: +4 rows per step, at most one wrap of
+  // the row axis (div >= 4)
+  int32_t m = mw + rsub;
+  const int32_t q0 = axis_quot(o.row, m);
+  int32_t rem = m - q0 * o.row.div;
+  int64_t off = (int64_t)q0 * o.row.s1 + (int64_t)rem * o.row.s2 + coff;
+  const int64_t step = 4 * o.row.s2, wrap = o.row.s1 - (int64_t)o.row.div * o.row.s2;
+  uint16_t* out = static_cast<uint16_t*>(o.p);
+#pragma unroll 1
+  for (int t0 = 0; t0 < 32; t0 += 8) {
+    u32x4 v[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int r = 4 * (t0 + t) + rsub;
+      v[t] = *reinterpret_cast<const u32x4*>(base + r * 256 + ((c ^ (r & 15)) << 4));
+    }
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      if (nok && m < o.m_valid) *reinterpret_cast<u32x4*>(out + off) = v[t];
+      m += 4;
+      rem += 4;
+      off += step;
+      if (rem >= o.row.div) {
+        rem -= o.row.div;
+        off += wrap;
+      }
+    }
+  }
+}
+
 // Epilogue of one tile, straight from the accumulators.  The MFMA operands are
 // swapped (B fragment first), so block (i, j) holds C^T: element 4g + r of a
 // lane is C[m][n] with m = mb + 32i and n = nb + 32j + 8g + r, i.e. four
@@ -120,6 +188,10 @@ __device__ __forceinline__ void epilogue(const GemmProblem& P, const floatx16 (&
   const OutDst& o = P.out;
   const int32_t mb = m0 + wm * 128 + lrow;
   const int32_t nb = n0 + wn * 128 + 4 * lhalf;
+  if (o.vec8_ok && o.flags == 0) {
+    epilogue_staged(o, acc, m0 + wm * 128, n0 + wn * 128, lane, smem + wave * (STAGE_U));
+    return;
+  }
   if (o.vec_ok) {
     if (o.flags == 0 && o.dtype == TXL_BF16)
       epilogue_vec<TXL_BF16, 0>(o, acc, mb, nb);
@@ -133,9 +205,7 @@ __device__ __forceinline__ void epilogue(const GemmProblem& P, const floatx16 (&
   }
   // Rare layouts (unaligned or odd leading dimension): one element at a time
   // through an LDS transpose, so that the accumulators are only indexed
-  // statically.  The ring is idle (all reads done) but the last K steps'
-  // zero-chunk loads may still be landing in it.
-  wait_vm(0);
+  // statically (the ring is idle).
   float* stage = reinterpret_cast<float*>(smem) + wave * (32 * 33);
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -307,7 +377,9 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(GemmGroup g, int32_t p
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    // every wave is done reading the ring before it is refilled for the next tile
+    // Every wave is done reading the ring, and the (zero-chunk) loads of the
+    // last K steps have landed, before the epilogue stages through it.
+    wait_vm(0);
     barrier_lds();
 
     epilogue(g.p[pidx], acc, m0, n0, wm, wn, lane, smem);

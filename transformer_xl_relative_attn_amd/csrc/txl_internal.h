@@ -81,6 +81,8 @@ struct OutDst {
   int32_t flags;         // EpiFlags
   int32_t vec_ok;        // groups of 4 columns (n % 4 == 0) are contiguous and
                          // 16-byte (f32) / 8-byte (bf16) aligned
+  int32_t vec8_ok;       // bf16: groups of 8 columns are contiguous and 16-byte
+                         // aligned, and the row map has div >= 4
   int32_t m_valid, n_valid;  // store only m < m_valid, n < n_valid
   AxisMap row, col;
   const float* resid;    // EPI_RESID: out += resid[rowoff + coloff] (same map)
