@@ -7,11 +7,12 @@
 // gemm_bf16: bf16 operands, fp32 accumulation on the gfx950 matrix cores
 //   (v_mfma_f32_32x32x16_bf16).  256x256 block tile, 4 waves in a 2x2 grid,
 //   each wave owns a 128x128 sub-tile (4x4 MFMA tiles, 256 accumulator
-//   registers).  Operands stream through a 4-deep LDS ring of 32-wide K steps
-//   filled by direct global->LDS loads (no register staging), issued up to
-//   four K steps ahead of their use; MFMA operand reads for the next k-step
-//   are interleaved with the current MFMAs.  Requirements (checked by the host):
-//   K % 64 == 0, every row 16-byte aligned.
+//   registers).  Operands stream through an NSTAGE-deep LDS ring of 32-wide
+//   K steps filled by direct global->LDS loads (no register staging), issued
+//   NSTAGE-1 K steps ahead of their use; MFMA operand reads and refill loads
+//   are spread evenly between the MFMAs.  Persistent: one workgroup per CU
+//   walks the tiles.  Requirements (checked by the host): K % 64 == 0, every
+//   row 16-byte aligned.
 //
 // gemm_f32: fp32 operands and arithmetic on the vector ALUs (64x64 tile),
 //   used by the fp32 path.
@@ -22,7 +23,10 @@ namespace txl {
 namespace {
 
 constexpr int BM = 256, BN = 256, BK = 32, NT = 256;
-constexpr int NSTAGE = 4;                // LDS ring depth: loads run NSTAGE-1 K-steps ahead
+#ifndef TXL_GEMM_NSTAGE
+#define TXL_GEMM_NSTAGE 3
+#endif
+constexpr int NSTAGE = TXL_GEMM_NSTAGE;  // LDS ring depth: loads run NSTAGE-1 K-steps ahead
 constexpr int CH = BK / 8;               // 16-byte chunks per tile row (4)
 constexpr int TILE_U = BM * CH;          // 16-byte units per operand tile (1024)
 constexpr int STAGE_U = 2 * TILE_U;      // A tile then B tile
@@ -44,7 +48,9 @@ __device__ __forceinline__ int find_problem(const GemmGroup& g, int32_t tile, in
 // loads are not fenced by the compiler (a __syncthreads would wait for all of
 // them), so the waits are explicit.
 __device__ __forceinline__ void wait_vm(int n) {
-  if (n >= 24)
+  if (n >= 32)
+    asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
+  else if (n >= 24)
     asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
   else if (n >= 16)
     asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
@@ -286,20 +292,22 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(GemmGroup g, int32_t p
     }
   };
 
-  // LDS-DMA of the next K step into ring slot `slot`; the running pointers
-  // advance by one K step.  With `real` false (past the end of K) the zero
-  // chunk is loaded instead into a slot that is never read again, which keeps
-  // the instruction stream identical in every iteration.
-  auto issue = [&](int slot, bool real) {
-    u32x4* st = smem + slot * STAGE_U + wave_s * 64;
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      __builtin_amdgcn_global_load_lds(real ? pa[i] : zero, st + 4 * i * 64, 16, 0, 0);
+  // LDS-DMA q (0..7: operand q & 1, row group q >> 1) of the next K step
+  // into a ring stage; the running pointer advances by one K step.  With
+  // `real` false (past the end of K) the zero chunk is loaded instead, into a
+  // slot that is never read again: the loop body stays the same in every
+  // iteration and the wait counts stay fixed.
+  auto issue_one = [&](u32x4* st, int q, bool real) {
+    const int i = q >> 1;
+    if (q & 1) {
       __builtin_amdgcn_global_load_lds(real ? pb[i] : zero, st + 4 * i * 64 + TILE_U, 16, 0, 0);
-      pa[i] += sa[i];
       pb[i] += sb[i];
+    } else {
+      __builtin_amdgcn_global_load_lds(real ? pa[i] : zero, st + 4 * i * 64, 16, 0, 0);
+      pa[i] += sa[i];
     }
   };
+  auto stage_ptr = [&](int slot) { return smem + slot * STAGE_U; };
 
   const int lrow = lane & 31, lhalf = lane >> 5;
   const int sw = (lrow >> 2) & 3;  // same for every fragment row of a lane
@@ -309,27 +317,74 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(GemmGroup g, int32_t p
     fa[i] = (wm * 128 + i * 32 + lrow) * CH;
     fb[i] = TILE_U + (wn * 128 + i * 32 + lrow) * CH;
   }
-  // fragments of k-step s (0 or 1) of a staged 32-wide K step
-  auto read_frags = [&](const u32x4* st, int s, bf16x8* af, bf16x8* bfr) {
+  // fragment f (0..3: A rows 32f.., 4..7: B rows 32(f-4)..) of k-step s (0 or
+  // 1) of a staged 32-wide K step
+  auto read_one = [&](const u32x4* st, int s, int f, bf16x8* af, bf16x8* bfr) {
     const int c = (2 * s + lhalf) ^ sw;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      af[i] = __builtin_bit_cast(bf16x8, st[fa[i] + c]);
-      bfr[i] = __builtin_bit_cast(bf16x8, st[fb[i] + c]);
-    }
+    if (f < 4)
+      af[f] = __builtin_bit_cast(bf16x8, st[fa[f] + c]);
+    else
+      bfr[f - 4] = __builtin_bit_cast(bf16x8, st[fb[f - 4] + c]);
   };
   floatx16 acc[4][4];
-  auto mfma16 = [&](const bf16x8* af, const bf16x8* bfr) {
+  auto mfma_one = [&](int x, const bf16x8* af, const bf16x8* bfr) {
+    const int i = x >> 2, j = x & 3;
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+  };
+
+  // One K step (ring slot `slot`, 32 wide = two MFMA k-steps), in two halves
+  // whose instruction order is fixed with scheduling fences:
+  //   A: 16 MFMAs on k-step 0 (fragments F0, already in registers); the
+  //      k-step 1 fragments F1 are read during the first 8;
+  //   wait until K step kt+1 has landed (`vm` loads may stay in flight),
+  //   barrier: every wave is done with this slot;
+  //   B: 16 MFMAs on F1, each pair followed by one refill load of this slot
+  //      (K step kt+NSTAGE; zero chunk if that is past the end), the first
+  //      four pairs also by two reads of K step kt+1's F0.
+  // Spreading the loads and reads evenly keeps the single wave per SIMD
+  // issuing MFMAs back to back.  (In the last step the F0 read is of a stale
+  // slot and unused.)
+  bf16x8 f0a[4], f0b[4], f1a[4], f1b[4];
+  auto kstep = [&](int slot, int nslot, bool refill) {
+    const u32x4* st = stage_ptr(slot);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int x = 0; x < 16; ++x) {
+      mfma_one(x, f0a, f0b);
+      if (x < 8) read_one(st, 1, x, f1a, f1b);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    wait_vm((NSTAGE - 2) * 2 * LOADS);
+    barrier_lds();
+    u32x4* rs = smem + slot * STAGE_U + wave_s * 64;
+    const u32x4* nst = stage_ptr(nslot);
+    // F0 reads in the order the next MFMAs consume them, all in the first
+    // half so that they have landed when the next step starts
+    constexpr int order[8] = {0, 4, 5, 6, 7, 1, 2, 3};
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+    for (int q = 0; q < 8; ++q) {
+      mfma_one(2 * q, f1a, f1b);
+      mfma_one(2 * q + 1, f1a, f1b);
+      issue_one(rs, q, refill);
+      if (q < 4) {
+        read_one(nst, 0, order[2 * q], f0a, f0b);
+        read_one(nst, 0, order[2 * q + 1], f0a, f0b);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Stage the first NSTAGE K steps of the current tile (zero chunks past K).
+  auto prologue = [&]() {
+#pragma unroll
+    for (int s = 0; s < NSTAGE; ++s) {
+      u32x4* rs = smem + s * STAGE_U + wave_s * 64;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) issue_one(rs, q, s < nk);
+    }
   };
 
   setup(xcd_swizzle(seq, padded));
-#pragma unroll
-  for (int s = 0; s < NSTAGE; ++s) issue(s, s < nk);
+  prologue();
 
   while (true) {
 #pragma unroll
@@ -337,49 +392,28 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(GemmGroup g, int32_t p
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc[i][j] = floatx16{0};
 
-    // Pipeline per K step kt (ring slot kt % NSTAGE):
-    //   A: MFMAs of k-step 0 (fragments F0 already in registers), reading the
-    //      k-step 1 fragments F1 in between;
-    //   wait for step kt+1 to land, barrier (slot kt % NSTAGE is then free);
-    //   B: refill that slot with step kt+NSTAGE, MFMAs of F1, reading step kt+1's
-    //      k-step 0 fragments into F0 in between.
-    // Reads are interleaved one per two MFMAs so the LDS queue never backs up.
-    // Every iteration issues exactly one stage and loads return in order, so
-    // the counts are fixed: stage 0 has landed once at most 3 stages (24
-    // loads) issued after it remain, stage kt+1 once at most 2 stages remain
-    // (outstanding epilogue stores of the previous tile only make these waits
-    // stricter).
-    bf16x8 f0a[4], f0b[4], f1a[4], f1b[4];
+    // Loads return in order and every step issues exactly one stage, so the
+    // wait counts are fixed: K step 0 has landed once at most NSTAGE-1 stages
+    // issued after it remain, step kt+1 once NSTAGE-2 remain.  Outstanding
+    // epilogue stores of the previous tile only make these waits stricter.
     wait_vm((NSTAGE - 1) * 2 * LOADS);
     barrier_lds();
-    read_frags(smem, 0, f0a, f0b);
-    for (int kt = 0; kt < nk; ++kt) {
-      const u32x4* st = smem + (kt % NSTAGE) * STAGE_U;
-      read_frags(st, 1, f1a, f1b);
-      mfma16(f0a, f0b);
+    {
+      const u32x4* st = stage_ptr(0);
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // 2 MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 LDS read
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      // (in the last iteration this refills nothing and reads a stale slot)
-      wait_vm((NSTAGE - 2) * 2 * LOADS);
-      barrier_lds();
-      issue(kt % NSTAGE, kt + NSTAGE < nk);
-      read_frags(smem + ((kt + 1) % NSTAGE) * STAGE_U, 0, f0a, f0b);
-      mfma16(f1a, f1b);
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 1);   // 2 MFMA
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);   // 1 global->LDS load
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);   // 1 LDS read
-      }
-      __builtin_amdgcn_sched_barrier(0);
+      for (int f = 0; f < 8; ++f) read_one(st, 0, f, f0a, f0b);
     }
-    // Every wave is done reading the ring, and the (zero-chunk) loads of the
-    // last K steps have landed, before the epilogue stages through it.
+    int slot = 0;
+#pragma unroll 1
+    for (int kt = 0; kt < nk; ++kt) {
+      const int nslot = slot + 1 == NSTAGE ? 0 : slot + 1;
+      kstep(slot, nslot, kt + NSTAGE < nk);
+      slot = nslot;
+    }
+    // The last K steps' zero-chunk loads must land before the epilogue
+    // reuses the ring.
     wait_vm(0);
+    // Every wave is done reading the ring before the epilogue stages through it.
     barrier_lds();
 
     epilogue(g.p[pidx], acc, m0, n0, wm, wn, lane, smem);
@@ -388,8 +422,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(GemmGroup g, int32_t p
     if (seq >= padded) break;
     barrier_lds();   // the epilogue may have used the ring for staging
     setup(xcd_swizzle(seq, padded));
-#pragma unroll
-    for (int s = 0; s < NSTAGE; ++s) issue(s, s < nk);
+    prologue();
   }
   // no LDS-DMA may still be writing when the workgroup exits
   wait_vm(0);
