@@ -41,26 +41,52 @@ constexpr int DP = 64;        // padded head width of the bf16 path
 constexpr int KB = 32;        // keys per block
 constexpr int NWAVE = 4;      // waves per workgroup, 32 queries each
 constexpr int QG = 32 * NWAVE;
-constexpr int RK_SLOTS = 5;   // Rk chunks resident in LDS
-constexpr int VST = 36;       // bf16 per V^T tile row (32 keys + pad)
-constexpr int BDS = 100;      // floats per row of the per-wave shift window
+constexpr int NST = 4;        // K / V^T ring stages: blocks tb .. tb+NST-1 resident or in flight
+constexpr int RKS = NST + 3;  // Rk chunk slots: chunks tb-3 .. tb in use, NST-1 ahead
+constexpr int WP = 36;        // floats per row of a wave's (b)+(d) window
+constexpr int KT_U = KB * 8;  // 16-byte units of a K tile (32 keys x 128 bytes)
+constexpr int VT_U = DP * 4;  // of a V^T tile (64 rows x 64 bytes)
+constexpr int RK_U = KB * 8;  // of an Rk chunk (32 rows x 128 bytes)
 constexpr float kNegInf = -__builtin_inff();
 
 struct AttnSmem {
-  u32x4 k[KB * 8];                    // K tile, 16-byte chunks XOR-swizzled
-  uint16_t vt[DP * VST];              // V^T tile [d][key]
-  u32x4 rk[RK_SLOTS][KB * 8];         // Rk chunk ring, swizzled like K
-  float bd[NWAVE][32 * BDS];          // per-wave shifted (b)+(d) window
-  float uv[2 * DP];                   // u then v of this head, zero padded
+  u32x4 kv[NST][KT_U + VT_U];   // per stage: K tile, then V^T tile
+  u32x4 rk[RKS][RK_U];          // Rk chunk ring
+  float bd[NWAVE][32 * WP];     // per-wave skewed (b)+(d) window
+  float uv[2 * DP];             // u then v of this head, zero padded
 };
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * 8 + (chunk ^ (row & 7)); }
+// 16-byte slot of chunk c (0..7) in row r of a K tile or Rk chunk.  gfx950
+// serves 16-byte LDS reads 16 lanes at a time; the fragment reads cover rows
+// 0..15 (128-byte pitch, two rows per 64-bank line) at one chunk, and
+// c ^ ((r >> 1) & 7) puts those 16 rows on 16 distinct bank groups.
+__device__ __forceinline__ int ksw(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }
+// V^T tile: row d (64 bytes) holds 4 chunks of 8 keys, chunk c at slot
+// c ^ ((d >> 2) & 3).
+__device__ __forceinline__ int vsw(int d, int c) { return KT_U + d * 4 + (c ^ ((d >> 2) & 3)); }
 
 __device__ __forceinline__ bf16x8 pack8(const float* x) {
   bf16x8 r;
 #pragma unroll
   for (int e = 0; e < 8; ++e) r[e] = static_cast<bf16>(x[e]);
   return r;
+}
+
+// Wait until at most 3*n LDS-DMA loads of this wave are in flight (n uniform).
+__device__ __forceinline__ void wait_stages(int n) {
+  if (n >= 2)
+    asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+  else if (n >= 1)
+    asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+__device__ __forceinline__ void barrier_lds() {
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
 }
 
 __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a, int32_t padded, int32_t nqg) {
@@ -76,6 +102,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a, int32_t p
 
   __shared__ AttnSmem sm;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
 
   // Optional fused memory-ring update (segment step): this workgroup copies
   // segment rows wid, wid + total, ... into their ring slots.  The projections
@@ -107,40 +134,8 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a, int32_t p
   // blocks past this are fully masked for every query of the wave
   const int32_t t_wave_end = wave_on ? (M + min(i0 + 31, L - 1) + 1 + KB - 1) / KB : 0;
 
-  const uint16_t* kg = static_cast<const uint16_t*>(a.k) + (int64_t)bh * a.Np * DP;
-  const uint16_t* vg = static_cast<const uint16_t*>(a.vt) + (int64_t)bh * DP * a.Np;
-  const uint16_t* rg = static_cast<const uint16_t*>(a.rk) + (int64_t)head * a.Pp * DP;
-
-  // ---- cooperative staging: one 16-byte chunk of K, V^T and Rk per thread
-  const int kr = tid >> 3, kc = tid & 7;     // K / Rk: row, chunk
-  const int vd = tid >> 2, vc = tid & 3;     // V^T: row d, 8-key chunk
-  auto rk_row = [&](int32_t chunk_id) {      // first row of a chunk, clamped later
-    return M + i_base - KB * chunk_id - (KB - 1);
-  };
-  auto load_k = [&](int32_t tb) {
-    return *reinterpret_cast<const u32x4*>(kg + (int64_t)(tb * KB + kr) * DP + kc * 8);
-  };
-  auto load_v = [&](int32_t tb) {
-    return *reinterpret_cast<const u32x4*>(vg + (int64_t)vd * a.Np + tb * KB + vc * 8);
-  };
-  auto load_r = [&](int32_t chunk_id) {
-    int32_t d = rk_row(chunk_id) + kr;
-    d = max(0, min(d, a.Pp - 1));
-    return *reinterpret_cast<const u32x4*>(rg + (int64_t)d * DP + kc * 8);
-  };
-  auto put_k = [&](u32x4 x) { sm.k[swz(kr, kc)] = x; };
-  auto put_v = [&](u32x4 x) {
-    u32x2* dst = reinterpret_cast<u32x2*>(&sm.vt[vd * VST + vc * 8]);
-    dst[0] = u32x2{x[0], x[1]};
-    dst[1] = u32x2{x[2], x[3]};
-  };
-  auto put_r = [&](int32_t chunk_id, u32x4 x) {
-    int slot = ((chunk_id % RK_SLOTS) + RK_SLOTS) % RK_SLOTS;
-    sm.rk[slot][swz(kr, kc)] = x;
-  };
-
-  // ---- per-wave query operands: (q+u)*c and (q+v)*c as bf16, d = 16s + 8hf + e.
-  // u and v of this head are staged once in LDS, zero-padded to 64 columns.
+  // ---- u, v of this head (zero padded) and the per-wave query operands
+  // (q+u)*c, (q+v)*c as bf16, d = 16s + 8hf + e
   if (tid < 2 * DP) {
     const int d = tid & (DP - 1);
     const uint16_t* src = static_cast<const uint16_t*>(tid < DP ? a.u : a.v) + (int64_t)head * a.dh;
@@ -167,62 +162,111 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a, int32_t p
     }
   }
 
-  float* bdw = sm.bd[wave];
-  // BDw^T chunk for `chunk_id` (rows w = delta - first row) -> window slot X.
-  auto bd_chunk = [&](int32_t chunk_id, int X, bool mirror) {
-    const int slot = ((chunk_id % RK_SLOTS) + RK_SLOTS) % RK_SLOTS;
-    floatx16 acc = floatx16{0};
+  // ---- LDS-DMA of one block's operands.  Block tb brings K tile tb, V^T tile
+  // tb and Rk chunk tb (rows M + i_base - 32 tb - 31 + r, r = 0..31, clamped;
+  // clamped rows only meet masked pairs).  The 12 wave-instructions of a
+  // block (4 each for K, V^T, Rk; 64 lanes x 16 bytes) are dealt 3 per wave;
+  // each lane fetches the global chunk that lands in the swizzled slot.
+  const uint16_t* kg = static_cast<const uint16_t*>(a.k) + (int64_t)bh * a.Np * DP;
+  const uint16_t* vg = static_cast<const uint16_t*>(a.vt) + (int64_t)bh * DP * a.Np;
+  const uint16_t* rg = static_cast<const uint16_t*>(a.rk) + (int64_t)head * a.Pp * DP;
+  const int32_t rk_top = M + i_base - (KB - 1);   // first row of chunk 0
+  auto rk_slot = [&](int32_t c) { return ((c % RKS) + RKS) % RKS; };
+  auto issue_rk = [&](int32_t c, int n) {          // instruction n (0..3) of Rk chunk c
+    const int r = n * 8 + (lane >> 3);
+    const int32_t row = max(0, min(rk_top - KB * c + r, a.Pp - 1));
+    const uint16_t* src = rg + (int64_t)row * DP + ((lane & 7) ^ ((r >> 1) & 7)) * 8;
+    __builtin_amdgcn_global_load_lds(src, &sm.rk[rk_slot(c)][n * 64], 16, 0, 0);
+  };
+  auto issue_block = [&](int32_t tb) {
+    u32x4* kv = sm.kv[tb % NST];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      bf16x8 ar = __builtin_bit_cast(bf16x8, sm.rk[slot][swz(ii, 2 * s + hf)]);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ar, qv[s], acc, 0, 0, 0);
-    }
-    // lane holds rows w = 8g + 4hf + r of column ii
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      floatx4 v4 = floatx4{acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
-      *reinterpret_cast<floatx4*>(&bdw[ii * BDS + X + 8 * g + 4 * hf]) = v4;
-      if (mirror) *reinterpret_cast<floatx4*>(&bdw[ii * BDS + X + 64 + 8 * g + 4 * hf]) = v4;
+    for (int j = 0; j < 3; ++j) {
+      const int n = 3 * wave_s + j;
+      if (n < 4) {
+        const int r = n * 8 + (lane >> 3);
+        const uint16_t* src = kg + (int64_t)(tb * KB + r) * DP + ((lane & 7) ^ ((r >> 1) & 7)) * 8;
+        __builtin_amdgcn_global_load_lds(src, kv + n * 64, 16, 0, 0);
+      } else if (n < 8) {
+        const int d = (n - 4) * 16 + (lane >> 2);
+        const uint16_t* src = vg + (int64_t)d * a.Np + tb * KB + ((lane & 3) ^ ((d >> 2) & 3)) * 8;
+        __builtin_amdgcn_global_load_lds(src, kv + KT_U + (n - 4) * 64, 16, 0, 0);
+      } else {
+        issue_rk(tb, n - 8);
+      }
     }
   };
 
-  // ---- prologue: Rk chunks t_lo-4 .. t_lo, K/V tile t_lo
-  if (t_lo < t_hi) {
+  // ---- (b)+(d) through the per-wave window.  At block tb the wave's queries
+  // i0 + ii meet keys tb*32 + jj at distance delta = D + ii - jj, D = M + i0 -
+  // 32 tb, i.e. at row y = 31 + ii - jj of the 64-row window
+  // [Rk chunk tb-wave ; Rk chunk tb-wave-1] (rows D-31 .. D+32).  The window
+  // is kept skewed per query: row ii holds W[ii][k] = window row ii + k,
+  // k = 0..31, so the 16 values a lane needs (k = 31 - jj) are four aligned
+  // float4 reads.  W[ii][(w - ii) & 31] takes chunk tb-wave's row w when
+  // w >= ii and chunk tb-wave-1's row w otherwise; both chunks are computed
+  // on the matrix cores (BDw[w][i] = (q_i+v).Rk[row w]) and each exactly once
+  // (the previous one is kept in registers).
+  float* win = sm.bd[wave] + ii * WP;
+  int wpos[16];
 #pragma unroll
-    for (int c = 0; c < RK_SLOTS; ++c) put_r(t_lo - 4 + c, load_r(t_lo - 4 + c));
-    put_k(load_k(t_lo));
-    put_v(load_v(t_lo));
+  for (int e = 0; e < 16; ++e) wpos[e] = ((8 * (e >> 2) + 4 * hf + (e & 3)) - ii) & 31;
+  auto bd_chunk = [&](int32_t c) {
+    const u32x4* rs = sm.rk[rk_slot(c)];
+    floatx16 acc = floatx16{0};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const bf16x8 ar = __builtin_bit_cast(bf16x8, rs[ksw(ii, 2 * s + hf)]);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ar, qv[s], acc, 0, 0, 0);
+    }
+    return acc;   // lane: rows w = 8g + 4hf + r (element 4g + r) of column ii
+  };
+
+  // ---- prologue: Rk chunks t_lo-4 .. t_lo-1 (one per wave), then blocks
+  // t_lo .. t_lo+NST-2
+  const int32_t nblk = t_hi - t_lo;
+  if (nblk > 0) {
+#pragma unroll
+    for (int n = 0; n < 4; ++n) issue_rk(t_lo - 4 + wave_s, n);
+    for (int32_t t = 0; t < NST - 1 && t < nblk; ++t) issue_block(t_lo + t);
   }
-  __syncthreads();
-  if (wave_on && t_lo < t_wave_end && t_lo < t_hi) bd_chunk(t_lo - wave - 1, 32, false);
+  // the four prologue chunks are the oldest loads of every wave
+  wait_stages(min(NST - 1, nblk));
+  barrier_lds();
+  floatx16 prev = floatx16{0};
+  if (wave_on && t_lo < t_wave_end && nblk > 0) prev = bd_chunk(t_lo - wave - 1);
 
   floatx16 o[2] = {floatx16{0}, floatx16{0}};
   float m_ref = kNegInf, l_sum = 0.0f;
 
   for (int32_t tb = t_lo; tb < t_hi; ++tb) {
-    const bool more = tb + 1 < t_hi;
-    u32x4 nk, nv, nr;
-    if (more) {
-      nk = load_k(tb + 1);
-      nv = load_v(tb + 1);
-      nr = load_r(tb + 1);
-    }
+    // block tb has landed once the loads of later blocks are all that remain
+    wait_stages(min(NST - 2, t_hi - 1 - tb));
+    barrier_lds();   // ... for every wave; block tb-1 is done everywhere
+    if (tb + NST - 1 < t_hi) issue_block(tb + NST - 1);
+
     if (wave_on && tb < t_wave_end) {
-      const int tl = tb - t_lo;
-      const int X = (tl & 1) ? 32 : 0;
-      bd_chunk(tb - wave, X, (tl & 1) == 0);
+      const u32x4* kv = sm.kv[tb % NST];
+      const floatx16 cur = bd_chunk(tb - wave);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int w = 8 * (e >> 2) + 4 * hf + (e & 3);
+        win[wpos[e]] = w >= ii ? cur[e] : prev[e];
+      }
+      prev = cur;
       wave_lds_fence();
-      // shifted (b)+(d): key jj = 8g + 4hf + r reads position X + 31 + ii - jj
+      // shifted (b)+(d) initialises the score accumulator: key jj = 8g + 4hf + r
       floatx16 s;
-      const float* rbase = &bdw[ii * BDS + X + 4 + ii - 4 * hf];
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
+      for (int g = 0; g < 4; ++g) {
+        const floatx4 x = *reinterpret_cast<const floatx4*>(win + 28 - 8 * g - 4 * hf);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) s[4 * g + r] = rbase[8 * (3 - g) + (3 - r)];
+        for (int r = 0; r < 4; ++r) s[4 * g + r] = x[3 - r];
+      }
       // (q+u).K on top
 #pragma unroll
       for (int st = 0; st < 4; ++st) {
-        bf16x8 ak = __builtin_bit_cast(bf16x8, sm.k[swz(ii, 2 * st + hf)]);
+        const bf16x8 ak = __builtin_bit_cast(bf16x8, kv[ksw(ii, 2 * st + hf)]);
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qu[st], s, 0, 0, 0);
       }
       // causal/memory mask: key j = tb*32 + jj visible iff j <= M + i0 + ii
@@ -264,20 +308,13 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a, int32_t p
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
           const int d = 32 * e + ii;
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(&sm.vt[d * VST + 16 * t2 + 4 * hf]);
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(&sm.vt[d * VST + 16 * t2 + 8 + 4 * hf]);
+          const u32x2 lo = reinterpret_cast<const u32x2*>(&kv[vsw(d, 2 * t2)])[hf];
+          const u32x2 hi = reinterpret_cast<const u32x2*>(&kv[vsw(d, 2 * t2 + 1)])[hf];
           const bf16x8 av = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
           o[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb, o[e], 0, 0, 0);
         }
       }
     }
-    __syncthreads();
-    if (more) {
-      put_k(nk);
-      put_v(nv);
-      put_r(tb + 1, nr);
-    }
-    __syncthreads();
   }
 
   if (!wave_on) return;

@@ -24,13 +24,15 @@ namespace {
 
 constexpr int BM = 256, BN = 256, BK = 32, NT = 256;
 #ifndef TXL_GEMM_NSTAGE
-#define TXL_GEMM_NSTAGE 3
+#define TXL_GEMM_NSTAGE 4
 #endif
 constexpr int NSTAGE = TXL_GEMM_NSTAGE;  // LDS ring depth: loads run NSTAGE-1 K-steps ahead
 constexpr int CH = BK / 8;               // 16-byte chunks per tile row (4)
 constexpr int TILE_U = BM * CH;          // 16-byte units per operand tile (1024)
 constexpr int STAGE_U = 2 * TILE_U;      // A tile then B tile
 constexpr int LOADS = TILE_U / NT;       // LDS-DMA loads per thread per operand (4)
+// the bf16 epilogue stages each wave's 128x128 sub-tile (32 KB) in the ring
+static_assert(NSTAGE * STAGE_U * 16 >= 4 * 128 * 128 * 2, "LDS ring too small for the epilogue");
 
 // 128 bytes of zeros: the source of every "zero row" chunk (padding rows).
 __device__ __align__(16) uint32_t g_zero_chunk[32];
