@@ -140,6 +140,7 @@ struct AttnPlan {
   int B, L, M, d, H, dh, dpos, dtype;
   float scale;
   int DP, Lp, Np, Pp, P;
+  int rk_pad;              // padding rows before / after each head's Rk rows
   int n_split, nqg;
   bool pack_d, pack_pos;   // bf16 operands repacked to a K multiple of 64
   int Kd, Kpos;            // reduction lengths seen by the GEMMs
@@ -193,6 +194,7 @@ AttnPlan make_plan(const txl_attn_shape_t* s, bool compute_rk) {
   p.Lp = bf ? (int)round_up(p.L, 32) : p.L;
   p.Np = bf ? (int)round_up(p.P, 32) : p.P;
   p.Pp = p.Np;
+  p.rk_pad = bf ? kRkPad : 0;
   p.nqg = (p.L + 127) / 128;
   p.n_split = 1;
   if (bf) {
@@ -217,7 +219,7 @@ AttnPlan make_plan(const txl_attn_shape_t* s, bool compute_rk) {
   take(p.q, BH * p.Lp * p.DP * 4);
   take(p.k, BH * p.Np * p.DP * es);
   take(p.v, BH * p.Np * p.DP * es);
-  take(p.rk, (size_t)p.H * p.Pp * p.DP * es);
+  take(p.rk, (size_t)p.H * (p.Pp + 2 * p.rk_pad) * p.DP * es);
   if (p.n_split > 1) {
     take(p.po, (size_t)p.n_split * BH * p.Lp * p.DP * 4);
     take(p.pml, (size_t)p.n_split * BH * p.Lp * 2 * 4);
@@ -406,10 +408,12 @@ txl_status_t run_rel_attn(const AttnPlan& p, const AttnPtrs& a, char* ws, void* 
                       axis(p.DP, (int64_t)p.Np * DP, 1)),
               tile);
   if (bf) {
-    // val^T = W_v h~^T -> [B][H][DP][Np]
+    // val^T = W_v h~^T in 32-key tiles -> [B][Np/32][H][DP][32]: row (head, d)
+    // at (head*DP + d)*32, token b*Np + key at (token/32)*(H*DP*32) + key%32
+    // (Np is a multiple of 32)
     add_problem(g, p.H * p.DP, p.B * p.Np, p.Kd, src_headpad(Wv, ld_d, p.dh, p.DP), ht,
-                out_map(v, dt, p.H * p.DP, p.B * p.Np, axis(p.DP, DP * p.Np, p.Np),
-                        axis(p.Np, (int64_t)p.H * DP * p.Np, 1)),
+                out_map(v, dt, p.H * p.DP, p.B * p.Np, axis_linear(32),
+                        axis(32, (int64_t)p.H * DP * 32, 1)),
                 tile);
   } else {
     add_problem(g, p.B * p.Np, p.H * p.DP, p.Kd, ht, src_headpad(Wv, ld_d, p.dh, p.DP),
@@ -417,14 +421,16 @@ txl_status_t run_rel_attn(const AttnPlan& p, const AttnPtrs& a, char* ws, void* 
                         axis(p.DP, (int64_t)p.Np * DP, 1)),
                 tile);
   }
+  const int64_t rk_rows = p.Pp + 2 * p.rk_pad;   // per head, padding included
   if (!a.Rk) {
-    // Rk = R W_kR^T -> [H][Pp][DP]
+    // Rk = R W_kR^T -> [H][pad + Pp + pad][DP] (rows of the padding not written)
     add_problem(g, p.Pp, p.H * p.DP, p.Kpos, src_plain(R, ld_pos, p.P),
                 src_headpad(WkR, ld_pos, p.dh, p.DP),
-                out_map(rk, dt, p.Pp, p.H * p.DP, axis_linear(DP), axis(p.DP, (int64_t)p.Pp * DP, 1)),
+                out_map(rk + (size_t)p.rk_pad * DP * es, dt, p.Pp, p.H * p.DP, axis_linear(DP),
+                        axis(p.DP, rk_rows * DP, 1)),
                 tile);
   } else {
-    TXL_HIP(timed(K_REPACK_RK, stream, [&] { return launch_repack_rk(a.Rk, rk, p.P, p.Pp, p.H, p.dh, p.DP, dt, stream); }), "repack Rk");
+    TXL_HIP(timed(K_REPACK_RK, stream, [&] { return launch_repack_rk(a.Rk, rk, p.P, p.Pp, p.rk_pad, p.H, p.dh, p.DP, dt, stream); }), "repack Rk");
   }
   TXL_TRY(after_launch(timed(K_PROJ_GEMM, stream, [&] { return launch_gemm(g, dt, stream); }),
                        "projection GEMMs", stream));

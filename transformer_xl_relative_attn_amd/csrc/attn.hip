@@ -9,26 +9,30 @@
 // bf16 kernel (d_head <= 64, padded to 64).  A workgroup owns 128 queries (4
 // waves x 32) of one (b, h) and a contiguous range of 32-key blocks.  Scores are
 // kept transposed, S^T[j][i], so each lane owns one query column and the
-// softmax row statistics stay in-lane.
-//   * K (32 keys x 64) and V^T (64 x 32 keys) tiles and 32-row chunks of Rk are
-//     staged in LDS once per block and shared by the 4 waves.
+// softmax row statistics stay in-lane (plus the partner lane ii+32).
+//   * Block tb's K tile, V^T tile (both 4 KB contiguous in the workspace) and
+//     Rk chunk tb (32 rows) stream into LDS by direct global->LDS loads, up
+//     to NST-1 blocks ahead; one barrier per block.  Rk chunks stay resident
+//     for four blocks (wave w uses chunk tb-w).
 //   * Term (b)+(d): per block a wave multiplies its 32 queries (q+v) by a
 //     32-row chunk of Rk on the matrix cores: BDw[w][i] = (q_i+v).Rk[D-31+w],
 //     D = M + i0 - j0.  The pair (i, j) needs row delta = D + i - j, i.e.
-//     position 31 + i - j of the 63-row window [chunk_t ; chunk_{t-1}] — the
-//     previous block's chunk is the upper half of this block's window, so every
-//     chunk is computed once.  The window lives in a per-wave LDS ring (row i =
-//     one query); reading position 31+i-j per lane performs App. B's per-row
-//     left shift by index arithmetic.  No L x (M+L) matrix is ever written.
-//   * The shifted (b)+(d) values initialise the accumulator of the
-//     (q+u).K MFMA, so the sum of the four terms costs no vector instruction.
+//     position 31 + i - j of the 63-row window [chunk_t ; chunk_{t-1}]; the
+//     previous chunk stays in registers, so every chunk is computed once.  A
+//     per-wave LDS window, skewed by query, turns App. B's per-row left shift
+//     into aligned reads.  No L x (M+L) matrix is ever written.
+//   * (q+u).K (terms (a), (c)) runs as a second, independent MFMA chain and the
+//     shifted (b)+(d) is added to it.
 //   * Online softmax in base 2 (c = scale*log2 e is folded into q+u and q+v),
 //     with a lazy rescale: the reference maximum only moves when a block's
 //     maximum exceeds it by more than 8, which keeps every p <= 2^8.
-//   * P (bf16) times V^T on the matrix cores; the key order inside an MFMA is
-//     permuted identically in both operands to match the accumulator layout.
+//   * P (bf16) times V^T on the matrix cores: bf16 pairs of P are exchanged
+//     with the partner lane so that both operands list the keys in order; the
+//     same P times a ones operand accumulates the softmax denominators.
 //   * With several key-range splits each workgroup writes (max, sum, O) and a
-//     combine kernel merges them in a fixed order (deterministic).
+//     combine kernel merges them in split order (deterministic).  (Merging in
+//     the last-arriving workgroup would need device-scope fences, i.e. L2
+//     write-back and invalidation, which cost far more than a second launch.)
 //
 // fp32 kernel: one workgroup per (b, h, i), plain loops; used by the fp32 path.
 #include "dev_common.h"
@@ -41,7 +45,10 @@ constexpr int DP = 64;        // padded head width of the bf16 path
 constexpr int KB = 32;        // keys per block
 constexpr int NWAVE = 4;      // waves per workgroup, 32 queries each
 constexpr int QG = 32 * NWAVE;
-constexpr int NST = 4;        // K / V^T ring stages: blocks tb .. tb+NST-1 resident or in flight
+#ifndef TXL_ATTN_NST
+#define TXL_ATTN_NST 4
+#endif
+constexpr int NST = TXL_ATTN_NST;  // K / V^T ring stages: blocks tb .. tb+NST-1 resident or in flight
 constexpr int RKS = NST + 3;  // Rk chunk slots: chunks tb-3 .. tb in use, NST-1 ahead
 constexpr int WP = 36;        // floats per row of a wave's (b)+(d) window
 constexpr int KT_U = KB * 8;  // 16-byte units of a K tile (32 keys x 128 bytes)
@@ -62,7 +69,8 @@ struct AttnSmem {
 // c ^ ((r >> 1) & 7) puts those 16 rows on 16 distinct bank groups.
 __device__ __forceinline__ int ksw(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }
 // V^T tile: row d (64 bytes) holds 4 chunks of 8 keys, chunk c at slot
-// c ^ ((d >> 2) & 3).
+// c ^ ((d >> 2) & 3); a 16-byte read of one chunk by rows 0..15 then covers all
+// 64 banks.
 __device__ __forceinline__ int vsw(int d, int c) { return KT_U + d * 4 + (c ^ ((d >> 2) & 3)); }
 
 __device__ __forceinline__ bf16x8 pack8(const float* x) {
@@ -74,7 +82,9 @@ __device__ __forceinline__ bf16x8 pack8(const float* x) {
 
 // Wait until at most 3*n LDS-DMA loads of this wave are in flight (n uniform).
 __device__ __forceinline__ void wait_stages(int n) {
-  if (n >= 2)
+  if (n >= 3)
+    asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+  else if (n >= 2)
     asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
   else if (n >= 1)
     asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
@@ -163,37 +173,48 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a, int32_t p
   }
 
   // ---- LDS-DMA of one block's operands.  Block tb brings K tile tb, V^T tile
-  // tb and Rk chunk tb (rows M + i_base - 32 tb - 31 + r, r = 0..31, clamped;
-  // clamped rows only meet masked pairs).  The 12 wave-instructions of a
-  // block (4 each for K, V^T, Rk; 64 lanes x 16 bytes) are dealt 3 per wave;
-  // each lane fetches the global chunk that lands in the swizzled slot.
-  const uint16_t* kg = static_cast<const uint16_t*>(a.k) + (int64_t)bh * a.Np * DP;
-  const uint16_t* vg = static_cast<const uint16_t*>(a.vt) + (int64_t)bh * DP * a.Np;
-  const uint16_t* rg = static_cast<const uint16_t*>(a.rk) + (int64_t)head * a.Pp * DP;
-  const int32_t rk_top = M + i_base - (KB - 1);   // first row of chunk 0
+  // tb and Rk chunk tb (rows M + i_base - 32 tb - 31 + r, r = 0..31; the
+  // padding of the table covers rows outside [0, Pp)).  Each is 4 KB
+  // contiguous, i.e. four wave-instructions of 64 lanes x 16 bytes; the 12
+  // instructions of a block are dealt 3 per wave.  A lane fetches the global
+  // chunk that lands in the swizzled slot, at a fixed byte offset from a
+  // workgroup-uniform base.
+  const int32_t nkb = a.Np / KB;
+  const char* kbase = static_cast<const char*>(a.k) + (int64_t)bh * a.Np * DP * 2;
+  const char* vbase = static_cast<const char*>(a.vt) + ((int64_t)b * nkb * a.H + head) * DP * KB * 2;
+  const int64_t vstep = (int64_t)a.H * DP * KB * 2;
+  const char* rbase = static_cast<const char*>(a.rk) +
+                      ((int64_t)head * (a.Pp + 2 * kRkPad) + kRkPad + M + i_base - (KB - 1)) * DP * 2;
   auto rk_slot = [&](int32_t c) { return ((c % RKS) + RKS) % RKS; };
-  auto issue_rk = [&](int32_t c, int n) {          // instruction n (0..3) of Rk chunk c
+  auto row_off = [&](int n) {      // instruction n (0..3) of a K tile or Rk chunk
     const int r = n * 8 + (lane >> 3);
-    const int32_t row = max(0, min(rk_top - KB * c + r, a.Pp - 1));
-    const uint16_t* src = rg + (int64_t)row * DP + ((lane & 7) ^ ((r >> 1) & 7)) * 8;
-    __builtin_amdgcn_global_load_lds(src, &sm.rk[rk_slot(c)][n * 64], 16, 0, 0);
+    return (uint32_t)(r * 128 + (((lane & 7) ^ ((r >> 1) & 7)) << 4));
   };
+  uint32_t loff[3];
+#pragma unroll
+  for (int j = 0; j < 3; ++j) {
+    const int n = 3 * wave + j;
+    if (n < 4 || n >= 8) {
+      loff[j] = row_off(n & 3);
+    } else {
+      const int d = (n - 4) * 16 + (lane >> 2);
+      loff[j] = (uint32_t)(d * 64 + (((lane & 3) ^ ((d >> 2) & 3)) << 4));
+    }
+  }
   auto issue_block = [&](int32_t tb) {
     u32x4* kv = sm.kv[tb % NST];
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
       const int n = 3 * wave_s + j;
-      if (n < 4) {
-        const int r = n * 8 + (lane >> 3);
-        const uint16_t* src = kg + (int64_t)(tb * KB + r) * DP + ((lane & 7) ^ ((r >> 1) & 7)) * 8;
-        __builtin_amdgcn_global_load_lds(src, kv + n * 64, 16, 0, 0);
-      } else if (n < 8) {
-        const int d = (n - 4) * 16 + (lane >> 2);
-        const uint16_t* src = vg + (int64_t)d * a.Np + tb * KB + ((lane & 3) ^ ((d >> 2) & 3)) * 8;
-        __builtin_amdgcn_global_load_lds(src, kv + KT_U + (n - 4) * 64, 16, 0, 0);
-      } else {
-        issue_rk(tb, n - 8);
-      }
+      if (n < 4)
+        __builtin_amdgcn_global_load_lds(kbase + (int64_t)tb * (KB * DP * 2) + loff[j],
+                                         kv + n * 64, 16, 0, 0);
+      else if (n < 8)
+        __builtin_amdgcn_global_load_lds(vbase + tb * vstep + loff[j], kv + KT_U + (n - 4) * 64,
+                                         16, 0, 0);
+      else
+        __builtin_amdgcn_global_load_lds(rbase - (int64_t)tb * (KB * DP * 2) + loff[j],
+                                         &sm.rk[rk_slot(tb)][(n - 8) * 64], 16, 0, 0);
     }
   };
 
@@ -206,19 +227,19 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a, int32_t p
   // float4 reads.  W[ii][(w - ii) & 31] takes chunk tb-wave's row w when
   // w >= ii and chunk tb-wave-1's row w otherwise; both chunks are computed
   // on the matrix cores (BDw[w][i] = (q_i+v).Rk[row w]) and each exactly once
-  // (the previous one is kept in registers).
+  // (the previous one stays in registers; the loop is unrolled twice so the
+  // two register sets trade roles instead of being copied).
   float* win = sm.bd[wave] + ii * WP;
-  int wpos[16];
+  float* wptr[16];
 #pragma unroll
-  for (int e = 0; e < 16; ++e) wpos[e] = ((8 * (e >> 2) + 4 * hf + (e & 3)) - ii) & 31;
-  auto bd_chunk = [&](int32_t c) {
-    const u32x4* rs = sm.rk[rk_slot(c)];
+  for (int e = 0; e < 16; ++e) wptr[e] = win + (((8 * (e >> 2) + 4 * hf + (e & 3)) - ii) & 31);
+  auto bd_chunk = [&](const u32x4* rs) {
+    bf16x8 ar[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) ar[s] = __builtin_bit_cast(bf16x8, rs[ksw(ii, 2 * s + hf)]);
     floatx16 acc = floatx16{0};
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const bf16x8 ar = __builtin_bit_cast(bf16x8, rs[ksw(ii, 2 * s + hf)]);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ar, qv[s], acc, 0, 0, 0);
-    }
+    for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ar[s], qv[s], acc, 0, 0, 0);
     return acc;   // lane: rows w = 8g + 4hf + r (element 4g + r) of column ii
   };
 
@@ -226,48 +247,74 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a, int32_t p
   // t_lo .. t_lo+NST-2
   const int32_t nblk = t_hi - t_lo;
   if (nblk > 0) {
+    const int32_t c = t_lo - 4 + wave_s;
 #pragma unroll
-    for (int n = 0; n < 4; ++n) issue_rk(t_lo - 4 + wave_s, n);
+    for (int n = 0; n < 4; ++n)
+      __builtin_amdgcn_global_load_lds(rbase - (int64_t)c * (KB * DP * 2) + row_off(n),
+                                       &sm.rk[rk_slot(c)][n * 64], 16, 0, 0);
     for (int32_t t = 0; t < NST - 1 && t < nblk; ++t) issue_block(t_lo + t);
   }
   // the four prologue chunks are the oldest loads of every wave
   wait_stages(min(NST - 1, nblk));
   barrier_lds();
-  floatx16 prev = floatx16{0};
-  if (wave_on && t_lo < t_wave_end && nblk > 0) prev = bd_chunk(t_lo - wave - 1);
+  floatx16 bd_a = floatx16{0}, bd_b = floatx16{0};
+  if (wave_on && t_lo < t_wave_end && nblk > 0) bd_b = bd_chunk(sm.rk[rk_slot(t_lo - wave - 1)]);
+  // bf16 ones: A operand of the MFMA that sums P over keys
+  bf16x8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = static_cast<bf16>(1.0f);
+  floatx16 lacc = floatx16{0};   // every row: sum_j p_ij of column ii
 
   floatx16 o[2] = {floatx16{0}, floatx16{0}};
-  float m_ref = kNegInf, l_sum = 0.0f;
+  float m_ref = kNegInf;
 
-  for (int32_t tb = t_lo; tb < t_hi; ++tb) {
+  // one key block: `cur` receives Rk chunk tb-wave, `prev` holds chunk tb-wave-1
+  auto block = [&](int32_t tb, floatx16& cur, const floatx16& prev) {
     // block tb has landed once the loads of later blocks are all that remain
     wait_stages(min(NST - 2, t_hi - 1 - tb));
     barrier_lds();   // ... for every wave; block tb-1 is done everywhere
-    if (tb + NST - 1 < t_hi) issue_block(tb + NST - 1);
+    const bool refill = tb + NST - 1 < t_hi;
 
     if (wave_on && tb < t_wave_end) {
       const u32x4* kv = sm.kv[tb % NST];
-      const floatx16 cur = bd_chunk(tb - wave);
+      const u32x4* rs = sm.rk[rk_slot(tb - wave)];
+      // operand fragments of this block, read up front in the order the MFMAs
+      // use them: K (keys x d) and Rk chunk tb-wave (rows x d), then V^T
+      // (d x keys, rows d = 32e + ii, keys 16 t2 + 8 hf .. +7 in order)
+      bf16x8 kf[4], rf[4];
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        kf[st] = __builtin_bit_cast(bf16x8, kv[ksw(ii, 2 * st + hf)]);
+        rf[st] = __builtin_bit_cast(bf16x8, rs[ksw(ii, 2 * st + hf)]);
+      }
+      bf16x8 vf[2][2];
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+        for (int e = 0; e < 2; ++e) vf[t2][e] = __builtin_bit_cast(bf16x8, kv[vsw(32 * e + ii, 2 * t2 + hf)]);
+      // (q+u).K (terms a, c) and BDw = (q+v).Rk (terms b, d): two independent
+      // MFMA chains
+      floatx16 s = floatx16{0};
+      cur = floatx16{0};
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st], qu[st], s, 0, 0, 0);
+        cur = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rf[st], qv[st], cur, 0, 0, 0);
+      }
+      // the refill of block tb-1's ring slot is issued while they run
+      if (refill) issue_block(tb + NST - 1);
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int w = 8 * (e >> 2) + 4 * hf + (e & 3);
-        win[wpos[e]] = w >= ii ? cur[e] : prev[e];
+        *wptr[e] = w >= ii ? cur[e] : prev[e];
       }
-      prev = cur;
       wave_lds_fence();
-      // shifted (b)+(d) initialises the score accumulator: key jj = 8g + 4hf + r
-      floatx16 s;
+      // add the shifted (b)+(d): key jj = 8g + 4hf + r
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const floatx4 x = *reinterpret_cast<const floatx4*>(win + 28 - 8 * g - 4 * hf);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) s[4 * g + r] = x[3 - r];
-      }
-      // (q+u).K on top
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        const bf16x8 ak = __builtin_bit_cast(bf16x8, kv[ksw(ii, 2 * st + hf)]);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qu[st], s, 0, 0, 0);
+        for (int r = 0; r < 4; ++r) s[4 * g + r] += x[3 - r];
       }
       // causal/memory mask: key j = tb*32 + jj visible iff j <= M + i0 + ii
       const int32_t j0 = tb * KB;
@@ -282,48 +329,58 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a, int32_t p
       float mb = s[0];
 #pragma unroll
       for (int e = 1; e < 16; ++e) mb = fmaxf(mb, s[e]);
-      mb = fmaxf(mb, __shfl_xor(mb, 32));
+      {  // with the partner lane (ii, 1-hf): both halves of the column
+        const auto mm = __builtin_amdgcn_permlane32_swap(__float_as_uint(mb), __float_as_uint(mb), false, false);
+        mb = fmaxf(__uint_as_float(mm[0]), __uint_as_float(mm[1]));
+      }
       const bool need = mb > m_ref + 8.0f;
       if (__ballot(need)) {
         const float alpha = need ? __builtin_amdgcn_exp2f(m_ref - mb) : 1.0f;
         if (need) m_ref = mb;
-        l_sum *= alpha;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           o[0][e] *= alpha;
           o[1][e] *= alpha;
+          lacc[e] *= alpha;
         }
       }
       const float m_use = (m_ref == kNegInf) ? 0.0f : m_ref;
       float p[16];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        p[e] = __builtin_amdgcn_exp2f(s[e] - m_use);
-        l_sum += p[e];
-      }
-      // P^T (keys x queries) times V^T: k-slot order (16t2 + 4hf + r, 16t2 + 8 + 4hf + r)
+      for (int e = 0; e < 16; ++e) p[e] = __builtin_amdgcn_exp2f(s[e] - m_use);
+      // P^T (keys x queries) times V^T.  The lane holds p for keys
+      // 16t2 + 4hf + {0..3} and 16t2 + 8 + 4hf + {0..3}; swapping bf16 pairs
+      // with the partner lane (ii, 1-hf) gives it keys 16t2 + 8hf .. +7 in
+      // order, the k-slots of the V^T fragment.  The same operand times ones
+      // accumulates the row sums.
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2) {
-        const bf16x8 pb = pack8(&p[8 * t2]);
+        const u32x4 pw = __builtin_bit_cast(u32x4, pack8(&p[8 * t2]));
+        const auto s02 = __builtin_amdgcn_permlane32_swap(pw[0], pw[2], false, false);
+        const auto s13 = __builtin_amdgcn_permlane32_swap(pw[1], pw[3], false, false);
+        const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{s02[0], s13[0], s02[1], s13[1]});
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int d = 32 * e + ii;
-          const u32x2 lo = reinterpret_cast<const u32x2*>(&kv[vsw(d, 2 * t2)])[hf];
-          const u32x2 hi = reinterpret_cast<const u32x2*>(&kv[vsw(d, 2 * t2 + 1)])[hf];
-          const bf16x8 av = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-          o[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb, o[e], 0, 0, 0);
-        }
+        for (int e = 0; e < 2; ++e) o[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[t2][e], pb, o[e], 0, 0, 0);
+        lacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pb, lacc, 0, 0, 0);
       }
+    } else if (refill) {
+      issue_block(tb + NST - 1);
     }
+  };
+  for (int32_t tb = t_lo; tb < t_hi; tb += 2) {
+    block(tb, bd_a, bd_b);
+    if (tb + 1 < t_hi) block(tb + 1, bd_b, bd_a);
   }
 
-  if (!wave_on) return;
-  l_sum += __shfl_xor(l_sum, 32);
+
+  const float l_sum = lacc[0];
   const int32_t i = i0 + ii;
-  // lane holds d = 32e + 8g + 4hf + r (r = 0..3): four consecutive columns per (e, g)
-  if (a.n_split == 1) {
+  typedef float floatx2_t __attribute__((ext_vector_type(2)));
+  typedef bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  // out[b, i, head, :] = num / den; lane holds d = 32e + 8g + 4hf + r (r = 0..3)
+  auto write_out = [&](const floatx16 (&num)[2], float den) {
     if (i >= L) return;
-    const float inv = 1.0f / l_sum;
+    const float inv = 1.0f / den;
     uint16_t* out = static_cast<uint16_t*>(a.out) + (((int64_t)b * L + i) * a.H + head) * a.dh;
     const bool vec = (a.dh == DP);
 #pragma unroll
@@ -332,31 +389,37 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a, int32_t p
       for (int g = 0; g < 4; ++g) {
         const int d0 = 32 * e + 8 * g + 4 * hf;
         if (vec) {
-          typedef float floatx2_t __attribute__((ext_vector_type(2)));
-          typedef bf16 bf16x2_t __attribute__((ext_vector_type(2)));
           const bf16x2_t lo = __builtin_convertvector(
-              floatx2_t{o[e][4 * g] * inv, o[e][4 * g + 1] * inv}, bf16x2_t);
+              floatx2_t{num[e][4 * g] * inv, num[e][4 * g + 1] * inv}, bf16x2_t);
           const bf16x2_t hi = __builtin_convertvector(
-              floatx2_t{o[e][4 * g + 2] * inv, o[e][4 * g + 3] * inv}, bf16x2_t);
+              floatx2_t{num[e][4 * g + 2] * inv, num[e][4 * g + 3] * inv}, bf16x2_t);
           *reinterpret_cast<u32x2*>(out + d0) =
               u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
         } else {
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            if (d0 + r < a.dh) out[d0 + r] = f32_to_bf16_bits(o[e][4 * g + r] * inv);
+            if (d0 + r < a.dh) out[d0 + r] = f32_to_bf16_bits(num[e][4 * g + r] * inv);
         }
       }
-  } else {
-    const int64_t row = (int64_t)split * a.B * a.H * a.Lp + (int64_t)bh * a.Lp + i;
-    floatx4* po = reinterpret_cast<floatx4*>(a.part_o + row * DP);
+  };
+  if (a.n_split == 1) {
+    if (wave_on) write_out(o, l_sum);
+    return;
+  }
+
+  // key-range splits: (max, sum, O) of this range, merged by attn_combine_kernel
+  if (!wave_on) return;
+  const int64_t row = (int64_t)split * a.B * a.H * a.Lp + (int64_t)bh * a.Lp + i;
+  floatx4* po = reinterpret_cast<floatx4*>(a.part_o + row * DP);
 #pragma unroll
-    for (int e = 0; e < 2; ++e)
+  for (int e = 0; e < 2; ++e)
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
-        po[(32 * e + 8 * g + 4 * hf) / 4] =
-            floatx4{o[e][4 * g], o[e][4 * g + 1], o[e][4 * g + 2], o[e][4 * g + 3]};
-    if (hf == 0) a.part_ml[row * 2 + 0] = m_ref;
-    if (hf == 0) a.part_ml[row * 2 + 1] = l_sum;
+    for (int g = 0; g < 4; ++g)
+      po[(32 * e + 8 * g + 4 * hf) / 4] =
+          floatx4{o[e][4 * g], o[e][4 * g + 1], o[e][4 * g + 2], o[e][4 * g + 3]};
+  if (hf == 0) {
+    a.part_ml[row * 2 + 0] = m_ref;
+    a.part_ml[row * 2 + 1] = l_sum;
   }
 }
 

@@ -103,8 +103,10 @@ __global__ void cast_f32_kernel(const void* src, float* dst, int64_t n, int32_t 
 }
 
 // Public Rk layout [P][H][dh] -> workspace layout [H][Pp][dp] (zero padded).
-__global__ void repack_rk_kernel(const void* src, void* dst, int32_t P, int32_t Pp, int32_t H,
-                                 int32_t dh, int32_t dp, int32_t dtype) {
+// Caller's Rk [P][H][dh] -> workspace [H][pad + Pp + pad][dp] (rows p >= P and
+// columns c >= dh zero; the padding rows are left as they are).
+__global__ void repack_rk_kernel(const void* src, void* dst, int32_t P, int32_t Pp, int32_t pad,
+                                 int32_t H, int32_t dh, int32_t dp, int32_t dtype) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (int64_t)H * Pp * dp) return;
   const int32_t c = idx % dp;
@@ -113,7 +115,7 @@ __global__ void repack_rk_kernel(const void* src, void* dst, int32_t P, int32_t 
   const int32_t h = t / Pp;
   float x = 0.0f;
   if (p < P && c < dh) x = load_as_f32(src, ((int64_t)p * H + h) * dh + c, dtype);
-  store_from_f32(dst, idx, x, dtype);
+  store_from_f32(dst, ((int64_t)h * (Pp + 2 * pad) + pad + p) * dp + c, x, dtype);
 }
 
 inline dim3 grid1d(int64_t n) { return dim3((unsigned)((n + 255) / 256)); }
@@ -166,11 +168,11 @@ int launch_cast_f32(const void* src, float* dst, int64_t n, int32_t dtype, void*
   return static_cast<int>(hipGetLastError());
 }
 
-int launch_repack_rk(const void* rk_pub, void* rk_ws, int32_t P, int32_t Pp, int32_t H,
+int launch_repack_rk(const void* rk_pub, void* rk_ws, int32_t P, int32_t Pp, int32_t pad, int32_t H,
                      int32_t dh, int32_t dp, int32_t dtype, void* stream) {
   const int64_t n = (int64_t)H * Pp * dp;
   hipLaunchKernelGGL(repack_rk_kernel, grid1d(n), dim3(256), 0, static_cast<hipStream_t>(stream),
-                     rk_pub, rk_ws, P, Pp, H, dh, dp, dtype);
+                     rk_pub, rk_ws, P, Pp, pad, H, dh, dp, dtype);
   return static_cast<int>(hipGetLastError());
 }
 

@@ -106,6 +106,12 @@ struct GemmGroup {
 };
 
 // Attention kernel arguments (device workspace layouts, see api.cpp).
+// bf16 path: the position-key table in the workspace carries kRkPad rows of
+// padding before and after each head's Pp rows, so that the attention kernel
+// can fetch 32-row chunks without clamping (padding rows only ever meet
+// masked query/key pairs, so their contents do not matter).
+constexpr int32_t kRkPad = 192;
+
 struct AttnArgs {
   int32_t B, H, L, M, dh;
   int32_t Lp, Np, Pp;      // padded query rows, key rows, position rows
@@ -113,8 +119,8 @@ struct AttnArgs {
   float c_scale;           // scale * log2(e) (bf16 path) or scale (fp32 path)
   const float* q;          // [B][H][Lp][DP] fp32
   const void* k;           // bf16 [B][H][Np][DP]   | f32 [B][H][Np][dh]
-  const void* vt;          // bf16 [B][H][DP][Np] (transposed) | f32 [B][H][Np][dh]
-  const void* rk;          // bf16 [H][Pp][DP]      | f32 [H][Pp][dh]
+  const void* vt;          // bf16 [B][Np/32][H][DP][32] (transposed 32-key tiles) | f32 [B][H][Np][dh]
+  const void* rk;          // bf16 [H][kRkPad + Pp + kRkPad][DP] | f32 [H][Pp][dh]
   const void* u;           // [H][dh] in the call dtype
   const void* v;
   void* out;               // [B][L][H][dh] in the call dtype
@@ -143,7 +149,7 @@ int launch_pack_rows(void* dst, int64_t ld_dst, const void* src, int64_t ld_src,
 int launch_layernorm(const float* x, float* y_f32, void* y_lo, int32_t rows, int32_t d,
                      int32_t lo_dtype, float eps, void* stream);
 int launch_cast_f32(const void* src, float* dst, int64_t n, int32_t dtype, void* stream);
-int launch_repack_rk(const void* rk_pub, void* rk_ws, int32_t P, int32_t Pp, int32_t H,
+int launch_repack_rk(const void* rk_pub, void* rk_ws, int32_t P, int32_t Pp, int32_t pad, int32_t H,
                      int32_t dh, int32_t dp, int32_t dtype, void* stream);
 
 }  // namespace txl
