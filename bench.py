@@ -121,7 +121,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="c4", help="workload (c1..c5); headline is c4")
+    ap.add_argument("--config", default="eval_l128_m1600", help="workload name (see synth.CONFIGS); the headline is eval_l128_m1600")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--cached-rk", action="store_true",

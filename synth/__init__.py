@@ -57,19 +57,19 @@ class Config:
 
 CONFIGS = {
     # Tiny fp32 single layer, two segments with the memory carried over.
-    "c1": Config("c1", batch=1, d_model=16, n_heads=1, d_head=16, seg_len=8, mem_len=8,
+    "tiny_f32": Config("tiny_f32", batch=1, d_model=16, n_heads=1, d_head=16, seg_len=8, mem_len=8,
                  n_layers=1, n_segments=2, dtype="f32", w_std=0.1, seed=1001),
     # Odd head dimension (41): exercises zero padding of the head axis.
-    "c2": Config("c2", batch=16, d_model=410, n_heads=10, d_head=41, seg_len=150, mem_len=150,
+    "odd_head41": Config("odd_head41", batch=16, d_model=410, n_heads=10, d_head=41, seg_len=150, mem_len=150,
                  n_layers=1, n_segments=1, dtype="bf16", w_std=0.02, seed=1002),
     # Train-shaped: memory length equals segment length, 4 streamed segments.
-    "c3": Config("c3", batch=22, d_model=512, n_heads=8, d_head=64, seg_len=512, mem_len=512,
+    "train_l512_m512": Config("train_l512_m512", batch=22, d_model=512, n_heads=8, d_head=64, seg_len=512, mem_len=512,
                  n_layers=1, n_segments=4, dtype="bf16", w_std=0.02, seed=1003),
     # Eval-shaped: segment 128 against a 1,600-state memory, 8 streamed segments.
-    "c4": Config("c4", batch=8, d_model=1024, n_heads=16, d_head=64, seg_len=128, mem_len=1600,
+    "eval_l128_m1600": Config("eval_l128_m1600", batch=8, d_model=1024, n_heads=16, d_head=64, seg_len=128, mem_len=1600,
                  n_layers=1, n_segments=8, dtype="bf16", w_std=0.02, seed=1004),
     # 16-layer stack with W_o + LayerNorm + ReLU FFN, 3,800-state memory, 4 segments.
-    "c5": Config("c5", batch=4, d_model=1024, n_heads=16, d_head=64, seg_len=128, mem_len=3800,
+    "stack16_l128_m3800": Config("stack16_l128_m3800", batch=4, d_model=1024, n_heads=16, d_head=64, seg_len=128, mem_len=3800,
                  n_layers=16, n_segments=4, dtype="bf16", w_std=0.02, seed=1005, d_inner=4096),
 }
 

@@ -82,11 +82,11 @@ def test_workspace_sizes(txl):
     assert 0 < a < b
     assert txl.txl_rel_attn_workspace_bytes(_shape(txl, seg_len=-3)) == 0
     # eval-shaped layer: K, V^T, Rk in bf16 plus fp32 q and split partials
-    c4 = _shape(txl, batch=8, seg_len=128, mem_len=1600, d_model=1024, n_heads=16, d_head=64,
+    eval_shape = _shape(txl, batch=8, seg_len=128, mem_len=1600, d_model=1024, n_heads=16, d_head=64,
                 d_pos=1024)
     kv = 2 * 8 * 16 * 1728 * 64 * 2
-    assert txl.txl_rel_attn_workspace_bytes(c4) >= kv
-    assert txl.txl_segment_workspace_bytes(c4, 1, 0) > txl.txl_rel_attn_workspace_bytes(c4)
+    assert txl.txl_rel_attn_workspace_bytes(eval_shape) >= kv
+    assert txl.txl_segment_workspace_bytes(eval_shape, 1, 0) > txl.txl_rel_attn_workspace_bytes(eval_shape)
     assert txl.txl_rel_proj_workspace_bytes(300, 410, 10, 41, txl.TXL_BF16) > 0
     assert txl.txl_rel_proj_workspace_bytes(300, 512, 10, 41, txl.TXL_BF16) == 0
     assert txl.txl_rel_proj_workspace_bytes(300, 410, 10, 41, txl.TXL_F32) == 0

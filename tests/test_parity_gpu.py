@@ -99,39 +99,39 @@ def _stream_case(txl, cfg, n_seg, b_idx, start=0, use_rk=False, scale=0.0):
     return outs
 
 
-def test_c1_tiny_fp32_two_segments(txl):
-    cfg = synth.get_config("c1")
+def test_tiny_fp32_two_segments(txl):
+    cfg = synth.get_config("tiny_f32")
     _stream_case(txl, cfg, 2, np.arange(cfg.batch))
 
 
-def test_c2_odd_head_dim(txl):
-    cfg = synth.get_config("c2")
+def test_odd_head_dim(txl):
+    cfg = synth.get_config("odd_head41")
     _stream_case(txl, cfg, 1, np.array([0, 7, 15]))
 
 
-def test_c3_train_shaped(txl):
-    cfg = synth.get_config("c3")
+def test_train_shaped(txl):
+    cfg = synth.get_config("train_l512_m512")
     _stream_case(txl, cfg, 4, np.array([0, 21]))
 
 
-def test_c4_eval_shaped(txl):
-    cfg = synth.get_config("c4")
+def test_eval_shaped(txl):
+    cfg = synth.get_config("eval_l128_m1600")
     _stream_case(txl, cfg, 8, np.array([0, 5]))
 
 
-def test_c4_with_cached_rk(txl):
-    cfg = synth.get_config("c4")
+def test_eval_with_cached_rk(txl):
+    cfg = synth.get_config("eval_l128_m1600")
     _stream_case(txl, cfg, 2, np.array([3]), use_rk=True)
 
 
-def test_fp32_path_c2_shape(txl):
-    cfg = synth.get_config("c2", dtype="f32", batch=2)
+def test_fp32_path_odd_head_shape(txl):
+    cfg = synth.get_config("odd_head41", dtype="f32", batch=2)
     _stream_case(txl, cfg, 2, np.array([0, 1]))
 
 
 def test_literal_scale_one(txl):
     """scale = 1 (the summary equations applied literally)."""
-    cfg = synth.get_config("c1", seed=77)
+    cfg = synth.get_config("tiny_f32", seed=77)
     _stream_case(txl, cfg, 2, np.arange(cfg.batch), scale=1.0)
 
 
@@ -166,7 +166,7 @@ def test_ring_start_rotation(txl):
 
 def test_deterministic(txl):
     import torch
-    cfg = synth.get_config("c4", batch=2)
+    cfg = synth.get_config("eval_l128_m1600", batch=2)
     wl = synth.make_workload(cfg, n_segments=1)
     a, _, _ = run_attn_stream(wl, 1)
     b, _, _ = run_attn_stream(wl, 1)
@@ -175,9 +175,9 @@ def test_deterministic(txl):
 
 
 # ------------------------------------------------------- segment step
-def test_segment_step_single_layer_c4(txl):
-    cfg = synth.get_config("c4")
-    log(f"[case] segment_step c4 8 segments")
+def test_segment_step_single_layer_eval(txl):
+    cfg = synth.get_config("eval_l128_m1600")
+    log("[case] segment_step eval layer, 8 segments")
     wl = synth.make_workload(cfg, n_segments=8)
     outs, dl, start = run_segment_stream(wl, 8)
     b_idx = np.array([0, 7])
@@ -201,9 +201,9 @@ def test_segment_step_stack_small(txl):
     _check_ring(dl, wl, o_mems, start_o, start, b_idx, layer=1, exact=False)
 
 
-def test_c5_stack_16_layers(txl):
-    cfg = synth.get_config("c5")
-    log("[case] c5 16-layer stack, 4 segments")
+def test_stack_16_layers(txl):
+    cfg = synth.get_config("stack16_l128_m3800")
+    log("[case] 16-layer stack, 4 segments")
     wl = synth.make_workload(cfg)
     outs, dl, start = run_segment_stream(wl, 4)
     b_idx = np.array([0])
