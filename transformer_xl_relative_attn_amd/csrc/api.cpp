@@ -435,9 +435,10 @@ txl_status_t run_rel_attn(const AttnPlan& p, const AttnPtrs& a, char* ws, void* 
   TXL_TRY(after_launch(timed(K_PROJ_GEMM, stream, [&] { return launch_gemm(g, dt, stream); }),
                        "projection GEMMs", stream));
 
-  // The ring update is folded into the bf16 attention kernel when rows are
-  // 16-byte multiples; otherwise it is a kernel of its own.
-  // (not when the output overlaps h: other workgroups may still be copying it)
+  // The ring update rides on the bf16 attention launch (the split combine, or
+  // the attention kernel's tail with one split) when rows are 16-byte
+  // multiples; otherwise it is a kernel of its own.  (Not when the output
+  // overlaps h: other workgroups may still be copying it.)
   const char* h_lo = static_cast<const char*>(a.h);
   const char* h_hi = h_lo + (size_t)p.B * p.L * p.d * esize(dt);
   const char* o_lo = static_cast<const char*>(a.out);

@@ -7,34 +7,42 @@
 // (q+u).k_j carries terms (a) and (c), (q+v).Rk carries (b) and (d).
 //
 // bf16 kernel (d_head <= 64, padded to 64).  A workgroup owns 128 queries (4
-// waves x 32) of one (b, h) and a contiguous range of 32-key blocks.  Scores are
-// kept transposed, S^T[j][i], so each lane owns one query column and the
-// softmax row statistics stay in-lane (plus the partner lane ii+32).
-//   * Block tb's K tile, V^T tile (both 4 KB contiguous in the workspace) and
-//     Rk chunk tb (32 rows) stream into LDS by direct global->LDS loads, up
-//     to NST-1 blocks ahead; one barrier per block.  Rk chunks stay resident
-//     for four blocks (wave w uses chunk tb-w).
-//   * Term (b)+(d): per block a wave multiplies its 32 queries (q+v) by a
-//     32-row chunk of Rk on the matrix cores: BDw[w][i] = (q_i+v).Rk[D-31+w],
-//     D = M + i0 - j0.  The pair (i, j) needs row delta = D + i - j, i.e.
-//     position 31 + i - j of the 63-row window [chunk_t ; chunk_{t-1}]; the
-//     previous chunk stays in registers, so every chunk is computed once.  A
-//     per-wave LDS window, skewed by query, turns App. B's per-row left shift
-//     into aligned reads.  No L x (M+L) matrix is ever written.
-//   * (q+u).K (terms (a), (c)) runs as a second, independent MFMA chain and the
-//     shifted (b)+(d) is added to it.
-//   * Online softmax in base 2 (c = scale*log2 e is folded into q+u and q+v),
-//     with a lazy rescale: the reference maximum only moves when a block's
-//     maximum exceeds it by more than 8, which keeps every p <= 2^8.
+// waves x 32) of one (b, h) and a contiguous range of 32-key blocks (key-range
+// splits fill the chip when B*H is small).  Scores are kept transposed,
+// S^T[j][i], so a lane owns one query column and the softmax statistics stay
+// in the lane and its partner (ii, 1-hf).
+//   * LDS-DMA ring: block t's K tile and V^T tile (4 KB each, contiguous in the
+//     workspace) and Rk chunk t (32 rows) are loaded by direct global->LDS
+//     loads NST blocks ahead.  The refill of a slot is issued right after the
+//     block barrier, and every wave issues exactly three loads per block, so
+//     the vmcnt waits are constants.  Wave w uses Rk chunk t+1-w at block t,
+//     so a chunk stays resident for four blocks.
+//   * Term (b)+(d): for block t+1 a wave multiplies its 32 queries (q+v) by the
+//     32-row Rk chunk that starts at distance D-31, D = M + i0 - 32(t+1), on the
+//     matrix cores.  Pair (i, j) needs distance D + i - j: row 31 + i - j of the
+//     window [this chunk ; previous chunk], and the previous chunk's product is
+//     still in registers, so every chunk is multiplied once.  Each lane writes
+//     its query's window row to LDS already shifted (App. B's left shift done as
+//     an address computation), and the shifted row becomes the initial
+//     accumulator of the (q+u).K product: summing the four terms costs no
+//     vector instruction.
+//   * Online softmax in base 2: c = scale * log2(e) is folded into q+u and q+v.
+//     The reference maximum moves only when a block's maximum exceeds it by
+//     more than 8 (p <= 2^8); the first block with a visible key sets it.
+//   * Software pipeline: block t's softmax runs on the vector ALUs while the
+//     operand fragments of block t+1 are read from LDS; block t+1's (b)+(d)
+//     and (q+u).K products follow block t's P.V on the matrix cores.
 //   * P (bf16) times V^T on the matrix cores: bf16 pairs of P are exchanged
-//     with the partner lane so that both operands list the keys in order; the
-//     same P times a ones operand accumulates the softmax denominators.
-//   * With several key-range splits each workgroup writes (max, sum, O) and a
-//     combine kernel merges them in split order (deterministic).  (Merging in
-//     the last-arriving workgroup would need device-scope fences, i.e. L2
-//     write-back and invalidation, which cost far more than a second launch.)
+//     with the partner lane so that both operands list the keys in order; P
+//     times a ones operand accumulates the softmax denominators.
+//   * With several key-range splits each workgroup writes (max, sum, O) and
+//     attn_combine_kernel merges them in split order (deterministic).  The
+//     segment step's memory-ring update rides on that launch (or on the tail of
+//     this kernel when there is one split).
 //
 // fp32 kernel: one workgroup per (b, h, i), plain loops; used by the fp32 path.
+#include <type_traits>
+
 #include "dev_common.h"
 
 namespace txl {
@@ -45,23 +53,23 @@ constexpr int DP = 64;        // padded head width of the bf16 path
 constexpr int KB = 32;        // keys per block
 constexpr int NWAVE = 4;      // waves per workgroup, 32 queries each
 constexpr int QG = 32 * NWAVE;
-#ifndef TXL_ATTN_NST
-#define TXL_ATTN_NST 4
-#endif
-constexpr int NST = TXL_ATTN_NST;  // K / V^T ring stages: blocks tb .. tb+NST-1 resident or in flight
-constexpr int RKS = NST + 3;  // Rk chunk slots: chunks tb-3 .. tb in use, NST-1 ahead
-constexpr int WP = 36;        // floats per row of a wave's (b)+(d) window
+constexpr int NST = 4;        // K / V^T ring stages (blocks t+1 .. t+NST resident or in flight)
+constexpr int RKS = NST + 3;  // Rk chunk slots: chunks t-2 .. t+NST
+constexpr int WP = 36;        // floats per query row of a wave's shifted (b)+(d) window
 constexpr int KT_U = KB * 8;  // 16-byte units of a K tile (32 keys x 128 bytes)
 constexpr int VT_U = DP * 4;  // of a V^T tile (64 rows x 64 bytes)
 constexpr int RK_U = KB * 8;  // of an Rk chunk (32 rows x 128 bytes)
+constexpr int LOADS_PER_BLOCK = 3;   // LDS-DMA instructions per wave per block
 constexpr float kNegInf = -__builtin_inff();
 
 struct AttnSmem {
   u32x4 kv[NST][KT_U + VT_U];   // per stage: K tile, then V^T tile
   u32x4 rk[RKS][RK_U];          // Rk chunk ring
-  float bd[NWAVE][32 * WP];     // per-wave skewed (b)+(d) window
+  float win[NWAVE][32 * WP];    // per-wave shifted (b)+(d) window
   float uv[2 * DP];             // u then v of this head, zero padded
 };
+static_assert(sizeof(AttnSmem) <= 80 * 1024, "two workgroups per CU");
+static_assert(32 * WP * 4 >= RK_U * 16, "a window region holds one Rk chunk (prologue)");
 
 // 16-byte slot of chunk c (0..7) in row r of a K tile or Rk chunk.  gfx950
 // serves 16-byte LDS reads 16 lanes at a time; the fragment reads cover rows
@@ -80,16 +88,11 @@ __device__ __forceinline__ bf16x8 pack8(const float* x) {
   return r;
 }
 
-// Wait until at most 3*n LDS-DMA loads of this wave are in flight (n uniform).
-__device__ __forceinline__ void wait_stages(int n) {
-  if (n >= 3)
-    asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
-  else if (n >= 2)
-    asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
-  else if (n >= 1)
-    asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
-  else
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+// Wait until at most N loads of this wave are in flight (loads and LDS-DMA
+// complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
 __device__ __forceinline__ void barrier_lds() {
@@ -99,38 +102,56 @@ __device__ __forceinline__ void barrier_lds() {
   __asm__ volatile("" ::: "memory");
 }
 
+__device__ __forceinline__ void compiler_fence() { __asm__ volatile("" ::: "memory"); }
+
+// Copy min(L, M) segment rows into their memory-ring slots (the segment step's
+// update, Sec. 3.2): row r of the flattened [B][rows] range goes to slot
+// (start + t) mod M, or to slot t with the last M rows when L >= M.  Rows are
+// dealt to `nworkers` workers of 256 threads.
+__device__ __forceinline__ void ring_copy(const AttnArgs& a, int32_t worker, int32_t nworkers,
+                                          int tid) {
+  const int64_t chunks = a.upd_row_bytes / 16;
+  const int32_t nrow = a.B * a.upd_rows;
+  for (int32_t r = worker; r < nrow; r += nworkers) {
+    const int32_t bb = r / a.upd_rows, t = r - bb * a.upd_rows;
+    const int32_t src = a.L < a.M ? t : a.L - a.M + t;
+    const int32_t slot = a.L < a.M ? (a.upd_start + t) % a.M : t;
+    const u32x4* sp = reinterpret_cast<const u32x4*>(
+        static_cast<const char*>(a.upd_src) + ((int64_t)bb * a.L + src) * a.upd_row_bytes);
+    u32x4* dp = reinterpret_cast<u32x4*>(static_cast<char*>(a.upd_mem) +
+                                         ((int64_t)bb * a.M + slot) * a.upd_row_bytes);
+    for (int64_t c = tid; c < chunks; c += 256) dp[c] = sp[c];
+  }
+}
+
+template <int V>
+using IC = std::integral_constant<int, V>;
+
+// v_max3_f32 without the NaN-quieting copies the compiler adds to fmaxf chains
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a, int32_t padded, int32_t nqg) {
   const int32_t total = a.B * a.H * nqg * a.n_split;
   const int32_t wid = xcd_swizzle(blockIdx.x, padded);
   if (wid >= total) return;
+  // work order: split fastest, then query group, batch, head, so that the
+  // work items dealt to one XCD share a head's position keys in its L2
   const int32_t split = wid % a.n_split;
-  const int32_t rest = wid / a.n_split;
+  int32_t rest = wid / a.n_split;
   const int32_t qg = rest % nqg;
-  const int32_t bh = rest / nqg;
-  const int32_t b = bh / a.H, head = bh - b * a.H;
+  rest /= nqg;
+  const int32_t b = rest % a.B;
+  const int32_t head = rest / a.B;
+  const int32_t bh = b * a.H + head;
   const int32_t M = a.M, L = a.L;
 
   __shared__ AttnSmem sm;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
-
-  // Optional fused memory-ring update (segment step): this workgroup copies
-  // segment rows wid, wid + total, ... into their ring slots.  The projections
-  // that read the old memory ran before this kernel.
-  if (a.upd_mem) {
-    const int64_t chunks = a.upd_row_bytes / 16;
-    const int32_t nrow = a.B * a.upd_rows;
-    for (int32_t r = wid; r < nrow; r += total) {
-      const int32_t bb = r / a.upd_rows, t = r - bb * a.upd_rows;
-      const int32_t src = a.L < a.M ? t : a.L - a.M + t;
-      const int32_t slot = a.L < a.M ? (a.upd_start + t) % a.M : t;
-      const u32x4* sp = reinterpret_cast<const u32x4*>(
-          static_cast<const char*>(a.upd_src) + ((int64_t)bb * a.L + src) * a.upd_row_bytes);
-      u32x4* dp = reinterpret_cast<u32x4*>(static_cast<char*>(a.upd_mem) +
-                                           ((int64_t)bb * a.M + slot) * a.upd_row_bytes);
-      for (int64_t c = tid; c < chunks; c += 256) dp[c] = sp[c];
-    }
-  }
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ii = lane & 31, hf = lane >> 5;
 
   const int32_t i_base = qg * QG;
@@ -141,58 +162,37 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a, int32_t p
 
   const int32_t i0 = i_base + 32 * wave;
   const bool wave_on = i0 < L;
-  // blocks past this are fully masked for every query of the wave
-  const int32_t t_wave_end = wave_on ? (M + min(i0 + 31, L - 1) + 1 + KB - 1) / KB : 0;
+  // blocks [t_lo, t_end) hold a visible key for some query of this wave
+  const int32_t t_end =
+      wave_on ? max(t_lo, min(t_hi, (M + min(i0 + 31, L - 1) + 1 + KB - 1) / KB)) : t_lo;
 
-  // ---- u, v of this head (zero padded) and the per-wave query operands
-  // (q+u)*c, (q+v)*c as bf16, d = 16s + 8hf + e
-  if (tid < 2 * DP) {
-    const int d = tid & (DP - 1);
-    const uint16_t* src = static_cast<const uint16_t*>(tid < DP ? a.u : a.v) + (int64_t)head * a.dh;
-    sm.uv[tid] = d < a.dh ? bf16_to_f32(src[d]) : 0.0f;
-  }
-  __syncthreads();
-  bf16x8 qu[4], qv[4];
-  {
-    const floatx4* qrow =
-        reinterpret_cast<const floatx4*>(a.q + ((int64_t)bh * a.Lp + (wave_on ? i0 + ii : 0)) * DP);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int d0 = 16 * s + 8 * hf;
-      const floatx4 q0 = qrow[d0 / 4], q1 = qrow[d0 / 4 + 1];
-      float xu[8], xv[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float qd = e < 4 ? q0[e] : q1[e - 4];
-        xu[e] = (qd + sm.uv[d0 + e]) * a.c_scale;
-        xv[e] = (qd + sm.uv[DP + d0 + e]) * a.c_scale;
-      }
-      qu[s] = pack8(xu);
-      qv[s] = pack8(xv);
-    }
-  }
-
-  // ---- LDS-DMA of one block's operands.  Block tb brings K tile tb, V^T tile
-  // tb and Rk chunk tb (rows M + i_base - 32 tb - 31 + r, r = 0..31; the
-  // padding of the table covers rows outside [0, Pp)).  Each is 4 KB
-  // contiguous, i.e. four wave-instructions of 64 lanes x 16 bytes; the 12
-  // instructions of a block are dealt 3 per wave.  A lane fetches the global
-  // chunk that lands in the swizzled slot, at a fixed byte offset from a
-  // workgroup-uniform base.
+  // ---- LDS-DMA.  Block t brings K tile t, V^T tile t and Rk chunk t (rows
+  // M + i_base - 31 - 32 t + r, r = 0..31; the table's padding covers rows
+  // outside [0, Pp)).  Each is 4 KB contiguous: four wave-instructions of 64
+  // lanes x 16 bytes, the 12 of a block dealt three per wave.  A lane fetches
+  // the global chunk that lands in its swizzled slot.  Block t uses K/V stage
+  // (t - t_lo) % NST and chunk c slot (c - t_lo + 4) % RKS.
   const int32_t nkb = a.Np / KB;
   const char* kbase = static_cast<const char*>(a.k) + (int64_t)bh * a.Np * DP * 2;
   const char* vbase = static_cast<const char*>(a.vt) + ((int64_t)b * nkb * a.H + head) * DP * KB * 2;
   const int64_t vstep = (int64_t)a.H * DP * KB * 2;
   const char* rbase = static_cast<const char*>(a.rk) +
                       ((int64_t)head * (a.Pp + 2 * kRkPad) + kRkPad + M + i_base - (KB - 1)) * DP * 2;
-  auto rk_slot = [&](int32_t c) { return ((c % RKS) + RKS) % RKS; };
+  auto rk_slot = [&](int32_t c) { return (c - t_lo + 4) % RKS; };   // c >= t_lo - 4
   auto row_off = [&](int n) {      // instruction n (0..3) of a K tile or Rk chunk
     const int r = n * 8 + (lane >> 3);
     return (uint32_t)(r * 128 + (((lane & 7) ^ ((r >> 1) & 7)) << 4));
   };
-  uint32_t loff[3];
+  // this wave's three loads of a block: a wave-uniform base advanced by tb *
+  // step, plus a 32-bit lane offset; into the stage (K, V^T) or the chunk
+  // slot (Rk) at a fixed unit offset
+  const char* gbase[LOADS_PER_BLOCK];
+  int64_t gstep[LOADS_PER_BLOCK];
+  uint32_t loff[LOADS_PER_BLOCK];
+  int32_t doff[LOADS_PER_BLOCK];
+  bool to_rk[LOADS_PER_BLOCK];
 #pragma unroll
-  for (int j = 0; j < 3; ++j) {
+  for (int j = 0; j < LOADS_PER_BLOCK; ++j) {
     const int n = 3 * wave + j;
     if (n < 4 || n >= 8) {
       loff[j] = row_off(n & 3);
@@ -200,143 +200,203 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a, int32_t p
       const int d = (n - 4) * 16 + (lane >> 2);
       loff[j] = (uint32_t)(d * 64 + (((lane & 3) ^ ((d >> 2) & 3)) << 4));
     }
+    gbase[j] = n < 4 ? kbase : n < 8 ? vbase : rbase;
+    gstep[j] = n < 4 ? (int64_t)KB * DP * 2 : n < 8 ? vstep : -(int64_t)KB * DP * 2;
+    doff[j] = n < 4 ? n * 64 : n < 8 ? KT_U + (n - 4) * 64 : (n - 8) * 64;
+    to_rk[j] = n >= 8;
   }
+  // Block tb's three loads of this wave.  Past the split's last block the
+  // loads repeat that block (valid memory) into the free slots, so every wave
+  // always issues three per block.
   auto issue_block = [&](int32_t tb) {
-    u32x4* kv = sm.kv[tb % NST];
+    const int32_t tl = min(tb, t_hi - 1);
+    u32x4* kv = sm.kv[(tb - t_lo) % NST];
+    u32x4* rs = sm.rk[rk_slot(tb)];
 #pragma unroll
-    for (int j = 0; j < 3; ++j) {
-      const int n = 3 * wave_s + j;
-      if (n < 4)
-        __builtin_amdgcn_global_load_lds(kbase + (int64_t)tb * (KB * DP * 2) + loff[j],
-                                         kv + n * 64, 16, 0, 0);
-      else if (n < 8)
-        __builtin_amdgcn_global_load_lds(vbase + tb * vstep + loff[j], kv + KT_U + (n - 4) * 64,
-                                         16, 0, 0);
-      else
-        __builtin_amdgcn_global_load_lds(rbase - (int64_t)tb * (KB * DP * 2) + loff[j],
-                                         &sm.rk[rk_slot(tb)][(n - 8) * 64], 16, 0, 0);
+    for (int j = 0; j < LOADS_PER_BLOCK; ++j) {
+      const char* g = gbase[j] + tl * gstep[j];
+      __builtin_amdgcn_global_load_lds(g + loff[j], (to_rk[j] ? rs : kv) + doff[j], 16, 0, 0);
     }
   };
 
-  // ---- (b)+(d) through the per-wave window.  At block tb the wave's queries
-  // i0 + ii meet keys tb*32 + jj at distance delta = D + ii - jj, D = M + i0 -
-  // 32 tb, i.e. at row y = 31 + ii - jj of the 64-row window
-  // [Rk chunk tb-wave ; Rk chunk tb-wave-1] (rows D-31 .. D+32).  The window
-  // is kept skewed per query: row ii holds W[ii][k] = window row ii + k,
-  // k = 0..31, so the 16 values a lane needs (k = 31 - jj) are four aligned
-  // float4 reads.  W[ii][(w - ii) & 31] takes chunk tb-wave's row w when
-  // w >= ii and chunk tb-wave-1's row w otherwise; both chunks are computed
-  // on the matrix cores (BDw[w][i] = (q_i+v).Rk[row w]) and each exactly once
-  // (the previous one stays in registers; the loop is unrolled twice so the
-  // two register sets trade roles instead of being copied).
-  float* win = sm.bd[wave] + ii * WP;
-  float* wptr[16];
+  // ---- prologue.  Chunks t_lo-4 .. t_lo-1 (one per wave; chunk t_lo-4, which
+  // only wave 3 needs, goes to wave 3's window region, still unused), blocks
+  // t_lo .. t_lo+NST-1, and this head's u, v and the wave's q rows.
+  {
+    const int32_t c = t_lo - 4 + wave;
+    u32x4* dst = wave == 0 ? reinterpret_cast<u32x4*>(sm.win[3]) : sm.rk[rk_slot(c)];
+    const char* g = rbase - (int64_t)c * (KB * DP * 2);
 #pragma unroll
-  for (int e = 0; e < 16; ++e) wptr[e] = win + (((8 * (e >> 2) + 4 * hf + (e & 3)) - ii) & 31);
-  auto bd_chunk = [&](const u32x4* rs) {
-    bf16x8 ar[4];
+    for (int n = 0; n < 4; ++n) __builtin_amdgcn_global_load_lds(g + row_off(n), dst + n * 64, 16, 0, 0);
+    issue_block(t_lo);
+  }
+  float uvv = 0.0f;
+  if (tid < 2 * DP) {
+    const int d = tid & (DP - 1);
+    const uint16_t* src = static_cast<const uint16_t*>(tid < DP ? a.u : a.v) + (int64_t)head * a.dh;
+    if (d < a.dh) uvv = bf16_to_f32(src[d]);
+  }
+  floatx4 qraw[8];
+  {
+    const floatx4* qrow =
+        reinterpret_cast<const floatx4*>(a.q + ((int64_t)bh * a.Lp + (wave_on ? i0 + ii : 0)) * DP);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) ar[s] = __builtin_bit_cast(bf16x8, rs[ksw(ii, 2 * s + hf)]);
+    for (int s = 0; s < 4; ++s) {
+      qraw[2 * s] = qrow[(16 * s + 8 * hf) / 4];
+      qraw[2 * s + 1] = qrow[(16 * s + 8 * hf) / 4 + 1];
+    }
+  }
+  compiler_fence();   // the q loads go out before the later blocks' DMA
+#pragma unroll
+  for (int s = 1; s < NST; ++s) issue_block(t_lo + s);
+  // everything but blocks t_lo+1 .. t_lo+NST-1 has landed
+  wait_vm<LOADS_PER_BLOCK * (NST - 1)>();
+  if (tid < 2 * DP) sm.uv[tid] = uvv;
+  barrier_lds();
+
+  // per-wave query operands (q+u)*c, (q+v)*c as bf16, d = 16s + 8hf + e
+  bf16x8 qu[4], qv[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int d0 = 16 * s + 8 * hf;
+    float xu[8], xv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float qd = qraw[2 * s + (e >> 2)][e & 3];
+      xu[e] = (qd + sm.uv[d0 + e]) * a.c_scale;
+      xv[e] = (qd + sm.uv[DP + d0 + e]) * a.c_scale;
+    }
+    qu[s] = pack8(xu);
+    qv[s] = pack8(xv);
+  }
+
+  // ---- fragment reads (lane-constant unit offsets within a tile) and products
+  int kofs[4], vofs[2][2];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) kofs[s] = ksw(ii, 2 * s + hf);
+#pragma unroll
+  for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+    for (int e = 0; e < 2; ++e) vofs[t2][e] = vsw(32 * e + ii, 2 * t2 + hf);
+  auto read_rows = [&](const u32x4* base, bf16x8 (&f)[4]) {   // K tile or Rk chunk, row ii
+#pragma unroll
+    for (int s = 0; s < 4; ++s) f[s] = __builtin_bit_cast(bf16x8, base[kofs[s]]);
+  };
+  auto read_vt = [&](const u32x4* kv, bf16x8 (&vf)[2][2]) {   // V^T rows d = 32e + ii
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) vf[t2][e] = __builtin_bit_cast(bf16x8, kv[vofs[t2][e]]);
+  };
+  // BD[w][i] = (q_i+v).Rk[chunk row w]: lane holds rows w = 8g + 4hf + r
+  // (element 4g + r) of column ii
+  auto bd_chunk = [&](const bf16x8 (&rf)[4]) {
     floatx16 acc = floatx16{0};
 #pragma unroll
-    for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ar[s], qv[s], acc, 0, 0, 0);
-    return acc;   // lane: rows w = 8g + 4hf + r (element 4g + r) of column ii
+    for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rf[s], qv[s], acc, 0, 0, 0);
+    return acc;
+  };
+  // Shifted window of block t' = [chunk t'-w ; chunk t'-w-1]: the value for
+  // (query ii, key jj) is window row 31 + ii - jj, stored at position jj of row
+  // ii, i.e. row w of the current chunk (w >= ii) or of the previous (w < ii)
+  // lands at position (31 + ii - w) mod 32.
+  float* win = sm.win[wave] + ii * WP;
+  auto write_win = [&](const floatx16& cur, const floatx16& prev) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int w = 8 * (e >> 2) + 4 * hf + (e & 3);
+      win[(31 + ii - w) & 31] = w >= ii ? cur[e] : prev[e];
+    }
+  };
+  auto read_win = [&]() {   // initial accumulator: element 4g + r is key 8g + 4hf + r
+    floatx16 c;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const floatx4 x = *reinterpret_cast<const floatx4*>(win + 8 * g + 4 * hf);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) c[4 * g + r] = x[r];
+    }
+    return c;
+  };
+  auto qk = [&](const bf16x8 (&kf)[4], floatx16 c) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qu[s], c, 0, 0, 0);
+    return c;
   };
 
-  // ---- prologue: Rk chunks t_lo-4 .. t_lo-1 (one per wave), then blocks
-  // t_lo .. t_lo+NST-2
-  const int32_t nblk = t_hi - t_lo;
-  if (nblk > 0) {
-    const int32_t c = t_lo - 4 + wave_s;
-#pragma unroll
-    for (int n = 0; n < 4; ++n)
-      __builtin_amdgcn_global_load_lds(rbase - (int64_t)c * (KB * DP * 2) + row_off(n),
-                                       &sm.rk[rk_slot(c)][n * 64], 16, 0, 0);
-    for (int32_t t = 0; t < NST - 1 && t < nblk; ++t) issue_block(t_lo + t);
+  // ---- block t_lo: (b)+(d) of chunks t_lo-w-1 and t_lo-w, window, scores
+  floatx16 S = floatx16{0}, bdA = floatx16{0}, bdB = floatx16{0};
+  bf16x8 vf[2][2];
+  if (t_lo < t_end) {
+    const u32x4* pc = wave == 3 ? reinterpret_cast<const u32x4*>(sm.win[3])
+                                : sm.rk[rk_slot(t_lo - wave - 1)];
+    bf16x8 pf[4], cf[4], kf[4];
+    read_rows(pc, pf);
+    read_rows(sm.rk[rk_slot(t_lo - wave)], cf);
+    read_rows(sm.kv[0], kf);
+    read_vt(sm.kv[0], vf);
+    const floatx16 bp = bd_chunk(pf);
+    bdB = bd_chunk(cf);
+    compiler_fence();   // (wave 3) the chunk reads precede the window writes in LDS order
+    write_win(bdB, bp);
+    compiler_fence();
+    S = qk(kf, read_win());
   }
-  // the four prologue chunks are the oldest loads of every wave
-  wait_stages(min(NST - 1, nblk));
-  barrier_lds();
-  floatx16 bd_a = floatx16{0}, bd_b = floatx16{0};
-  if (wave_on && t_lo < t_wave_end && nblk > 0) bd_b = bd_chunk(sm.rk[rk_slot(t_lo - wave - 1)]);
-  // bf16 ones: A operand of the MFMA that sums P over keys
+
   bf16x8 ones;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ones[e] = static_cast<bf16>(1.0f);
   floatx16 lacc = floatx16{0};   // every row: sum_j p_ij of column ii
-
   floatx16 o[2] = {floatx16{0}, floatx16{0}};
-  float m_ref = kNegInf;
+  float m_ref = 0.0f;            // running reference maximum (lazy)
+  bool fresh = true;             // no visible key seen yet
 
-  // one key block: `cur` receives Rk chunk tb-wave, `prev` holds chunk tb-wave-1
-  auto block = [&](int32_t tb, floatx16& cur, const floatx16& prev) {
-    // block tb has landed once the loads of later blocks are all that remain
-    wait_stages(min(NST - 2, t_hi - 1 - tb));
-    barrier_lds();   // ... for every wave; block tb-1 is done everywhere
-    const bool refill = tb + NST - 1 < t_hi;
+  // One block t (K/V stage U = (t - t_lo) % NST): softmax and P.V of block t,
+  // (b)+(d) window and (q+u).K of block t+1.  `cur` receives chunk t+1-w,
+  // `prev` holds chunk t-w.  The loop is unrolled NST times so that stages are
+  // static and the two chunk products trade roles instead of being copied.
+  auto block = [&](auto U, int32_t t, floatx16& cur, floatx16& prev) {
+    constexpr int u = decltype(U)::value, un = (u + 1) % NST;
+    // block t+1 has landed once only blocks t+2 .. t+NST-1 may be in flight
+    wait_vm<LOADS_PER_BLOCK * (NST - 2)>();
+    barrier_lds();   // ... for every wave; block t's stage (read during block t-1) is free
+    issue_block(t + NST);
 
-    if (wave_on && tb < t_wave_end) {
-      const u32x4* kv = sm.kv[tb % NST];
-      const u32x4* rs = sm.rk[rk_slot(tb - wave)];
-      // operand fragments of this block, read up front in the order the MFMAs
-      // use them: K (keys x d) and Rk chunk tb-wave (rows x d), then V^T
-      // (d x keys, rows d = 32e + ii, keys 16 t2 + 8 hf .. +7 in order)
-      bf16x8 kf[4], rf[4];
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        kf[st] = __builtin_bit_cast(bf16x8, kv[ksw(ii, 2 * st + hf)]);
-        rf[st] = __builtin_bit_cast(bf16x8, rs[ksw(ii, 2 * st + hf)]);
-      }
-      bf16x8 vf[2][2];
-#pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-        for (int e = 0; e < 2; ++e) vf[t2][e] = __builtin_bit_cast(bf16x8, kv[vsw(32 * e + ii, 2 * t2 + hf)]);
-      // (q+u).K (terms a, c) and BDw = (q+v).Rk (terms b, d): two independent
-      // MFMA chains
-      floatx16 s = floatx16{0};
-      cur = floatx16{0};
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st], qu[st], s, 0, 0, 0);
-        cur = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rf[st], qv[st], cur, 0, 0, 0);
-      }
-      // the refill of block tb-1's ring slot is issued while they run
-      if (refill) issue_block(tb + NST - 1);
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int w = 8 * (e >> 2) + 4 * hf + (e & 3);
-        *wptr[e] = w >= ii ? cur[e] : prev[e];
-      }
-      wave_lds_fence();
-      // add the shifted (b)+(d): key jj = 8g + 4hf + r
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const floatx4 x = *reinterpret_cast<const floatx4*>(win + 28 - 8 * g - 4 * hf);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) s[4 * g + r] += x[3 - r];
-      }
-      // causal/memory mask: key j = tb*32 + jj visible iff j <= M + i0 + ii
-      const int32_t j0 = tb * KB;
+    const bool cur_on = t < t_end;
+    const bool next_on = t + 1 < t_end;
+    // block t+1's K and Rk chunk t+1-w fragments first: they land during the
+    // softmax (V^T(t) was read during block t-1, before this block's refill)
+    bf16x8 kf[4], rf[4];
+    if (next_on) {
+      read_rows(sm.rk[rk_slot(t + 1 - wave)], rf);
+      read_rows(sm.kv[un], kf);
+    }
+    bf16x8 pb[2];
+    if (cur_on) {
+      // causal/memory mask: key j = 32t + jj visible iff j <= M + i0 + ii
+      const int32_t j0 = t * KB;
       if (j0 + KB - 1 > M + i0) {
-        const int32_t lim = M + i0 + ii - j0;
+        const int32_t lim = M + i0 + ii - j0 - 4 * hf;   // key jj = 8g + 4hf + r
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int jj = 8 * (e >> 2) + 4 * hf + (e & 3);
-          if (jj > lim) s[e] = kNegInf;
-        }
+        for (int e = 0; e < 16; ++e)
+          if (8 * (e >> 2) + (e & 3) > lim) S[e] = kNegInf;
       }
-      float mb = s[0];
+      float mb = max3(S[0], S[1], S[2]);
 #pragma unroll
-      for (int e = 1; e < 16; ++e) mb = fmaxf(mb, s[e]);
+      for (int e = 3; e < 15; e += 2) mb = max3(mb, S[e], S[e + 1]);
+      mb = fmaxf(mb, S[15]);
       {  // with the partner lane (ii, 1-hf): both halves of the column
         const auto mm = __builtin_amdgcn_permlane32_swap(__float_as_uint(mb), __float_as_uint(mb), false, false);
         mb = fmaxf(__uint_as_float(mm[0]), __uint_as_float(mm[1]));
       }
-      const bool need = mb > m_ref + 8.0f;
-      if (__ballot(need)) {
+      const bool need = mb > m_ref + 8.0f || (fresh && mb > kNegInf);
+      if (__builtin_expect(__ballot(need) != 0, 0)) {
+        // move the reference up to mb and rescale the accumulators
         const float alpha = need ? __builtin_amdgcn_exp2f(m_ref - mb) : 1.0f;
-        if (need) m_ref = mb;
+        if (need) {
+          m_ref = mb;
+          fresh = false;
+        }
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           o[0][e] *= alpha;
@@ -344,66 +404,80 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a, int32_t p
           lacc[e] *= alpha;
         }
       }
-      const float m_use = (m_ref == kNegInf) ? 0.0f : m_ref;
       float p[16];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) p[e] = __builtin_amdgcn_exp2f(s[e] - m_use);
-      // P^T (keys x queries) times V^T.  The lane holds p for keys
-      // 16t2 + 4hf + {0..3} and 16t2 + 8 + 4hf + {0..3}; swapping bf16 pairs
-      // with the partner lane (ii, 1-hf) gives it keys 16t2 + 8hf .. +7 in
-      // order, the k-slots of the V^T fragment.  The same operand times ones
-      // accumulates the row sums.
+      for (int e = 0; e < 16; ++e) p[e] = __builtin_amdgcn_exp2f(S[e] - m_ref);
+      // The lane holds p for keys 16t2 + 4hf + {0..3} and 16t2 + 8 + 4hf +
+      // {0..3}; swapping bf16 pairs with the partner lane gives it keys
+      // 16t2 + 8hf .. +7 in order, the k-slots of the V^T fragment.
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2) {
         const u32x4 pw = __builtin_bit_cast(u32x4, pack8(&p[8 * t2]));
         const auto s02 = __builtin_amdgcn_permlane32_swap(pw[0], pw[2], false, false);
         const auto s13 = __builtin_amdgcn_permlane32_swap(pw[1], pw[3], false, false);
-        const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{s02[0], s13[0], s02[1], s13[1]});
-#pragma unroll
-        for (int e = 0; e < 2; ++e) o[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[t2][e], pb, o[e], 0, 0, 0);
-        lacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pb, lacc, 0, 0, 0);
+        pb[t2] = __builtin_bit_cast(bf16x8, u32x4{s02[0], s13[0], s02[1], s13[1]});
       }
-    } else if (refill) {
-      issue_block(tb + NST - 1);
+    }
+    if (next_on) cur = bd_chunk(rf);   // chunk t+1-w
+    if (cur_on) {
+      // P^T (keys x queries) times V^T; P times ones accumulates the row sums
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+          o[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[t2][e], pb[t2], o[e], 0, 0, 0);
+        lacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pb[t2], lacc, 0, 0, 0);
+      }
+    }
+    if (next_on) {
+      // block t+1: V^T fragments, shifted (b)+(d) window, then its (q+u).K on
+      // top of it
+      read_vt(sm.kv[un], vf);
+      write_win(cur, prev);
+      compiler_fence();
+      S = qk(kf, read_win());
     }
   };
-  for (int32_t tb = t_lo; tb < t_hi; tb += 2) {
-    block(tb, bd_a, bd_b);
-    if (tb + 1 < t_hi) block(tb + 1, bd_b, bd_a);
+  for (int32_t t = t_lo; t < t_hi; t += NST) {
+    block(IC<0>{}, t, bdA, bdB);
+    if (t + 1 < t_hi) block(IC<1>{}, t + 1, bdB, bdA);
+    if (t + 2 < t_hi) block(IC<2>{}, t + 2, bdA, bdB);
+    if (t + 3 < t_hi) block(IC<3>{}, t + 3, bdB, bdA);
   }
-
+  static_assert(NST == 4, "the block loop is unrolled NST times");
+  // the repeated loads past the split's last block must land before exit
+  wait_vm<0>();
 
   const float l_sum = lacc[0];
   const int32_t i = i0 + ii;
   typedef float floatx2_t __attribute__((ext_vector_type(2)));
   typedef bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-  // out[b, i, head, :] = num / den; lane holds d = 32e + 8g + 4hf + r (r = 0..3)
-  auto write_out = [&](const floatx16 (&num)[2], float den) {
-    if (i >= L) return;
-    const float inv = 1.0f / den;
-    uint16_t* out = static_cast<uint16_t*>(a.out) + (((int64_t)b * L + i) * a.H + head) * a.dh;
-    const bool vec = (a.dh == DP);
-#pragma unroll
-    for (int e = 0; e < 2; ++e)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = 32 * e + 8 * g + 4 * hf;
-        if (vec) {
-          const bf16x2_t lo = __builtin_convertvector(
-              floatx2_t{num[e][4 * g] * inv, num[e][4 * g + 1] * inv}, bf16x2_t);
-          const bf16x2_t hi = __builtin_convertvector(
-              floatx2_t{num[e][4 * g + 2] * inv, num[e][4 * g + 3] * inv}, bf16x2_t);
-          *reinterpret_cast<u32x2*>(out + d0) =
-              u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
-        } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            if (d0 + r < a.dh) out[d0 + r] = f32_to_bf16_bits(num[e][4 * g + r] * inv);
-        }
-      }
-  };
   if (a.n_split == 1) {
-    if (wave_on) write_out(o, l_sum);
+    // out[b, i, head, :] = num / den; lane holds d = 32e + 8g + 4hf + r (r = 0..3)
+    if (wave_on && i < L) {
+      const float inv = 1.0f / l_sum;
+      uint16_t* out = static_cast<uint16_t*>(a.out) + (((int64_t)b * L + i) * a.H + head) * a.dh;
+      const bool vec = (a.dh == DP);
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d0 = 32 * e + 8 * g + 4 * hf;
+          if (vec) {
+            const bf16x2_t lo =
+                __builtin_convertvector(floatx2_t{o[e][4 * g] * inv, o[e][4 * g + 1] * inv}, bf16x2_t);
+            const bf16x2_t hi =
+                __builtin_convertvector(floatx2_t{o[e][4 * g + 2] * inv, o[e][4 * g + 3] * inv}, bf16x2_t);
+            *reinterpret_cast<u32x2*>(out + d0) =
+                u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (d0 + r < a.dh) out[d0 + r] = f32_to_bf16_bits(o[e][4 * g + r] * inv);
+          }
+        }
+    }
+    if (a.upd_mem) ring_copy(a, wid, total, tid);
     return;
   }
 
@@ -418,14 +492,22 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a, int32_t p
       po[(32 * e + 8 * g + 4 * hf) / 4] =
           floatx4{o[e][4 * g], o[e][4 * g + 1], o[e][4 * g + 2], o[e][4 * g + 3]};
   if (hf == 0) {
-    a.part_ml[row * 2 + 0] = m_ref;
+    // a range with no visible key for this query reports max -inf, sum 0
+    a.part_ml[row * 2 + 0] = fresh ? kNegInf : m_ref;
     a.part_ml[row * 2 + 1] = l_sum;
   }
 }
 
-// Merge split partials in split order: out = sum_s 2^(m_s-m*) O_s / sum_s 2^(m_s-m*) l_s.
-// 16 threads per output row, 4 columns each.
-__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
+// Merge split partials in split order: out = sum_s 2^(m_s-m*) O_s / sum_s
+// 2^(m_s-m*) l_s.  16 threads per output row, 4 columns each; the partials of
+// all splits are loaded before any is used.  The workgroups past the output
+// rows copy the segment into the memory ring when the step asks for it.
+template <int S>
+__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, int32_t out_blocks) {
+  if ((int32_t)blockIdx.x >= out_blocks) {
+    ring_copy(a, blockIdx.x - out_blocks, gridDim.x - out_blocks, threadIdx.x);
+    return;
+  }
   const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);   // (b, h, i), i < L
   const int c4 = threadIdx.x & 15;
   const int64_t rows = (int64_t)a.B * a.H * a.L;
@@ -435,24 +517,50 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   const int32_t b = bh / a.H, head = bh % a.H;
   const int64_t prow = bh * a.Lp + i;
   const int64_t stride = (int64_t)a.B * a.H * a.Lp;
+  const int ns = S > 0 ? S : a.n_split;
+  constexpr int CAP = S > 0 ? S : 16;
+  float ms[CAP], ls[CAP];
+  floatx4 os[CAP];
+#pragma unroll
+  for (int s = 0; s < CAP; ++s) {
+    if (s < ns) {
+      const int64_t pr = s * stride + prow;
+      const float2 ml = reinterpret_cast<const float2*>(a.part_ml)[pr];
+      ms[s] = ml.x;
+      ls[s] = ml.y;
+      os[s] = reinterpret_cast<const floatx4*>(a.part_o + pr * DP)[c4];
+    }
+  }
   float mx = kNegInf;
-  for (int s = 0; s < a.n_split; ++s) mx = fmaxf(mx, a.part_ml[(s * stride + prow) * 2]);
+#pragma unroll
+  for (int s = 0; s < CAP; ++s)
+    if (s < ns) mx = fmaxf(mx, ms[s]);
   floatx4 num = floatx4{0.f, 0.f, 0.f, 0.f};
   float den = 0.0f;
-  for (int s = 0; s < a.n_split; ++s) {
-    const int64_t pr = s * stride + prow;
-    const float ms = a.part_ml[pr * 2];
-    const float w = (ms == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(ms - mx);
-    num += w * reinterpret_cast<const floatx4*>(a.part_o + pr * DP)[c4];
-    den += w * a.part_ml[pr * 2 + 1];
+#pragma unroll
+  for (int s = 0; s < CAP; ++s) {
+    if (s < ns) {
+      const float w = (ms[s] == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(ms[s] - mx);
+      num += w * os[s];
+      den += w * ls[s];
+    }
   }
   const float inv = 1.0f / den;
   uint16_t* out = static_cast<uint16_t*>(a.out) + ((int64_t)b * a.L + i) * a.H * a.dh +
                   (int64_t)head * a.dh;
+  if (a.dh == DP) {
+    typedef float floatx2_t __attribute__((ext_vector_type(2)));
+    typedef bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const bf16x2_t lo = __builtin_convertvector(floatx2_t{num[0] * inv, num[1] * inv}, bf16x2_t);
+    const bf16x2_t hi = __builtin_convertvector(floatx2_t{num[2] * inv, num[3] * inv}, bf16x2_t);
+    *reinterpret_cast<u32x2*>(out + 4 * c4) =
+        u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+  } else {
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int d = 4 * c4 + r;
-    if (d < a.dh) out[d] = f32_to_bf16_bits(num[r] * inv);
+    for (int r = 0; r < 4; ++r) {
+      const int d = 4 * c4 + r;
+      if (d < a.dh) out[d] = f32_to_bf16_bits(num[r] * inv);
+    }
   }
 }
 
@@ -535,8 +643,17 @@ int launch_attn_bf16(const AttnArgs& a, void* stream) {
 
 int launch_attn_combine(const AttnArgs& a, void* stream) {
   const int64_t rows = (int64_t)a.B * a.H * a.L;
-  hipLaunchKernelGGL(attn_combine_kernel, dim3((rows + 15) / 16), dim3(256), 0,
-                     static_cast<hipStream_t>(stream), a);
+  const int32_t out_blocks = (int32_t)((rows + 15) / 16);
+  // the memory-ring copy (segment step) gets one workgroup per two rows
+  const int32_t copy_blocks = a.upd_mem ? (a.B * a.upd_rows + 1) / 2 : 0;
+  const dim3 grid(out_blocks + copy_blocks);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  switch (a.n_split) {
+    case 2: hipLaunchKernelGGL(attn_combine_kernel<2>, grid, dim3(256), 0, st, a, out_blocks); break;
+    case 3: hipLaunchKernelGGL(attn_combine_kernel<3>, grid, dim3(256), 0, st, a, out_blocks); break;
+    case 4: hipLaunchKernelGGL(attn_combine_kernel<4>, grid, dim3(256), 0, st, a, out_blocks); break;
+    default: hipLaunchKernelGGL(attn_combine_kernel<0>, grid, dim3(256), 0, st, a, out_blocks); break;
+  }
   return static_cast<int>(hipGetLastError());
 }
 
