@@ -11,7 +11,9 @@
 //   K steps filled by direct global->LDS loads (no register staging), issued
 //   NSTAGE-1 K steps ahead of their use; MFMA operand reads and refill loads
 //   are spread evenly between the MFMAs.  Persistent: one workgroup per CU
-//   walks the tiles.  Requirements (checked by the host): K % 64 == 0, every
+//   walks the tiles; the next tile's first K steps are issued before the
+//   current tile's epilogue, which stages its bf16 output through a separate
+//   32 KB LDS region.  Requirements (checked by the host): K % 64 == 0, every
 //   row 16-byte aligned.
 //
 // gemm_f32: fp32 operands and arithmetic on the vector ALUs (64x64 tile),
@@ -24,15 +26,13 @@ namespace {
 
 constexpr int BM = 256, BN = 256, BK = 32, NT = 256;
 #ifndef TXL_GEMM_NSTAGE
-#define TXL_GEMM_NSTAGE 4
+#define TXL_GEMM_NSTAGE 3
 #endif
 constexpr int NSTAGE = TXL_GEMM_NSTAGE;  // LDS ring depth: loads run NSTAGE-1 K-steps ahead
 constexpr int CH = BK / 8;               // 16-byte chunks per tile row (4)
 constexpr int TILE_U = BM * CH;          // 16-byte units per operand tile (1024)
 constexpr int STAGE_U = 2 * TILE_U;      // A tile then B tile
 constexpr int LOADS = TILE_U / NT;       // LDS-DMA loads per thread per operand (4)
-// the bf16 epilogue stages each wave's 128x128 sub-tile (32 KB) in the ring
-static_assert(NSTAGE * STAGE_U * 16 >= 4 * 128 * 128 * 2, "LDS ring too small for the epilogue");
 
 // 128 bytes of zeros: the source of every "zero row" chunk (padding rows).
 __device__ __align__(16) uint32_t g_zero_chunk[32];
@@ -118,13 +118,17 @@ __device__ __forceinline__ void epilogue_vec(const OutDst& o, const floatx16 (&a
 }
 
 // bf16 output without residual / activation: the wave's 128x128 sub-tile
-// (rows mw.., columns nw..) passes through the wave's own 32 KB of the idle
-// LDS ring, so that the global stores write whole lines (16 lanes cover 256
-// contiguous bytes of one row) instead of 16-byte pieces of 32 rows, which
-// the L2 would receive as 32 partial-line writes per instruction.  Staging
-// layout: row r (0..127) is 16 chunks of 16 bytes, chunk c at slot c ^ (r & 15);
-// both the 8-byte writes (32 rows x 2 halves) and the 16-byte reads (16 lanes
-// per row) are then spread over all 64 banks.
+// (rows mw.., columns nw..) passes through the wave's own 8 KB LDS region in
+// four rounds of 32 rows, so that the global stores write whole lines (16
+// lanes cover 256 contiguous bytes of one row) instead of 16-byte pieces of
+// 32 rows, which the L2 would receive as 32 partial-line writes per
+// instruction.  The region is separate from the operand ring, so the next
+// tile's first K steps can already be landing.  Staging layout: row r (0..31)
+// is 16 chunks of 16 bytes, chunk c at slot c ^ (r & 15); both the 8-byte
+// writes (32 rows x 2 halves) and the 16-byte reads (16 lanes per row) are
+// then spread over all 64 banks.
+constexpr int EPI_U = 32 * 16;   // 16-byte units of a wave's staging region (8 KB)
+
 __device__ __forceinline__ void epilogue_staged(const OutDst& o, const floatx16 (&acc)[4][4],
                                                 int32_t mw, int32_t nw, int lane,
                                                 u32x4* region) {
@@ -132,24 +136,6 @@ __device__ __forceinline__ void epilogue_staged(const OutDst& o, const floatx16 
   typedef bf16 bf16x2_t __attribute__((ext_vector_type(2)));
   char* base = reinterpret_cast<char*>(region);
   const int lrow = lane & 31, lhalf = lane >> 5;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 32 * i + lrow;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int c = 4 * j + q;   // columns 32j + 8q + 4*lhalf .. +3
-        const bf16x2_t lo =
-            __builtin_convertvector(floatx2_t{acc[i][j][4 * q], acc[i][j][4 * q + 1]}, bf16x2_t);
-        const bf16x2_t hi =
-            __builtin_convertvector(floatx2_t{acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]}, bf16x2_t);
-        *reinterpret_cast<u32x2*>(base + r * 256 + ((c ^ (r & 15)) << 4) + 8 * lhalf) =
-            u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
-      }
-  }
-  wave_lds_fence();
-
   // lane -> chunk c = lane % 16 (columns nw + 8c .. +7) of rows 4t + lane/16
   const int c = lane & 15, rsub = lane >> 4;
   const int32_t n = nw + 8 * c;
@@ -163,14 +149,28 @@ __device__ __forceinline__ void epilogue_staged(const OutDst& o, const floatx16 
   int64_t off = (int64_t)q0 * o.row.s1 + (int64_t)rem * o.row.s2 + coff;
   const int64_t step = 4 * o.row.s2, wrap = o.row.s1 - (int64_t)o.row.div * o.row.s2;
   uint16_t* out = static_cast<uint16_t*>(o.p);
-#pragma unroll 1
-  for (int t0 = 0; t0 < 32; t0 += 8) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int cc = 4 * j + q;   // columns 32j + 8q + 4*lhalf .. +3
+        const bf16x2_t lo =
+            __builtin_convertvector(floatx2_t{acc[i][j][4 * q], acc[i][j][4 * q + 1]}, bf16x2_t);
+        const bf16x2_t hi =
+            __builtin_convertvector(floatx2_t{acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]}, bf16x2_t);
+        *reinterpret_cast<u32x2*>(base + lrow * 256 + ((cc ^ (lrow & 15)) << 4) + 8 * lhalf) =
+            u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+      }
+    wave_lds_fence();
     u32x4 v[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      const int r = 4 * (t0 + t) + rsub;
+      const int r = 4 * t + rsub;
       v[t] = *reinterpret_cast<const u32x4*>(base + r * 256 + ((c ^ (r & 15)) << 4));
     }
+    wave_lds_fence();   // the next round rewrites the region
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       if (nok && m < o.m_valid) *reinterpret_cast<u32x4*>(out + off) = v[t];
@@ -197,7 +197,7 @@ __device__ __forceinline__ void epilogue(const GemmProblem& P, const floatx16 (&
   const int32_t mb = m0 + wm * 128 + lrow;
   const int32_t nb = n0 + wn * 128 + 4 * lhalf;
   if (o.vec8_ok && o.flags == 0) {
-    epilogue_staged(o, acc, m0 + wm * 128, n0 + wn * 128, lane, smem + wave * (STAGE_U));
+    epilogue_staged(o, acc, m0 + wm * 128, n0 + wn * 128, lane, smem + wave * EPI_U);
     return;
   }
   if (o.vec_ok) {
@@ -212,9 +212,9 @@ __device__ __forceinline__ void epilogue(const GemmProblem& P, const floatx16 (&
     return;
   }
   // Rare layouts (unaligned or odd leading dimension): one element at a time
-  // through an LDS transpose, so that the accumulators are only indexed
-  // statically (the ring is idle).
-  float* stage = reinterpret_cast<float*>(smem) + wave * (32 * 33);
+  // through an LDS transpose in the wave's staging region, so that the
+  // accumulators are only indexed statically.
+  float* stage = reinterpret_cast<float*>(smem + wave * EPI_U);
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -243,7 +243,11 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(GemmGroup g, int32_t p
   // gfx950 serves a 16-byte read for 16 lanes at a time from 64 four-byte
   // banks, so rows r, r+4, r+8, r+12 (same bank group at a 64-byte pitch) must
   // use different slots: 16 consecutive rows then read one chunk conflict-free.
-  __shared__ u32x4 smem[NSTAGE * STAGE_U];
+  // the per-wave epilogue staging follows the ring in the same LDS object
+  // (a second object defeats the compiler's LDS-DMA alias tracking, which
+  // then waits for every load before each LDS read)
+  __shared__ u32x4 smem[NSTAGE * STAGE_U + 4 * EPI_U];
+  u32x4* const stage_out = smem + NSTAGE * STAGE_U;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -397,7 +401,8 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(GemmGroup g, int32_t p
     // Loads return in order and every step issues exactly one stage, so the
     // wait counts are fixed: K step 0 has landed once at most NSTAGE-1 stages
     // issued after it remain, step kt+1 once NSTAGE-2 remain.  Outstanding
-    // epilogue stores of the previous tile only make these waits stricter.
+    // epilogue stores of the previous tile only make these waits stricter (a
+    // pending load keeps every later load pending too).
     wait_vm((NSTAGE - 1) * 2 * LOADS);
     barrier_lds();
     {
@@ -412,19 +417,21 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(GemmGroup g, int32_t p
       kstep(slot, nslot, kt + NSTAGE < nk);
       slot = nslot;
     }
-    // The last K steps' zero-chunk loads must land before the epilogue
-    // reuses the ring.
-    wait_vm(0);
-    // Every wave is done reading the ring before the epilogue stages through it.
+    // Every wave is done reading the ring: the next tile's first K steps are
+    // issued now and land while this tile's epilogue runs (this tile's
+    // trailing zero-chunk loads into the same slots were issued earlier by
+    // the same lanes and land first).
     barrier_lds();
-
-    epilogue(g.p[pidx], acc, m0, n0, wm, wn, lane, smem);
-
+    const int cpidx = pidx;
+    const int32_t cm0 = m0, cn0 = n0;
     seq = next_tile(seq + grid);
-    if (seq >= padded) break;
-    barrier_lds();   // the epilogue may have used the ring for staging
-    setup(xcd_swizzle(seq, padded));
-    prologue();
+    const bool more = seq < padded;
+    if (more) {
+      setup(xcd_swizzle(seq, padded));
+      prologue();
+    }
+    epilogue(g.p[cpidx], acc, cm0, cn0, wm, wn, lane, stage_out);
+    if (!more) break;
   }
   // no LDS-DMA may still be writing when the workgroup exits
   wait_vm(0);
