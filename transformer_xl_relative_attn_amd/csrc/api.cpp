@@ -221,7 +221,7 @@ AttnPlan make_plan(const txl_attn_shape_t* s, bool compute_rk) {
   take(p.v, BH * p.Np * p.DP * es);
   take(p.rk, (size_t)p.H * (p.Pp + 2 * p.rk_pad) * p.DP * es);
   if (p.n_split > 1) {
-    take(p.po, (size_t)p.n_split * BH * p.Lp * p.DP * 4);
+    take(p.po, (size_t)p.n_split * BH * p.Lp * p.DP * 2);
     take(p.pml, (size_t)p.n_split * BH * p.Lp * 2 * 4);
   }
   const size_t Hd = (size_t)p.H * p.dh;
@@ -471,7 +471,7 @@ txl_status_t run_rel_attn(const AttnPlan& p, const AttnPtrs& a, char* ws, void* 
   aa.u = a.u;
   aa.v = a.v;
   aa.out = a.out;
-  aa.part_o = p.n_split > 1 ? reinterpret_cast<float*>(ws + p.po.off) : nullptr;
+  aa.part_o = p.n_split > 1 ? ws + p.po.off : nullptr;
   aa.part_ml = p.n_split > 1 ? reinterpret_cast<float*>(ws + p.pml.off) : nullptr;
   aa.dtype = dt;
   if (fuse_upd) {

@@ -481,16 +481,23 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a, int32_t p
     return;
   }
 
-  // key-range splits: (max, sum, O) of this range, merged by attn_combine_kernel
+  // key-range splits: (max, sum) of this range and its normalised output O/sum
+  // in bf16, merged by attn_combine_kernel
   if (!wave_on) return;
   const int64_t row = (int64_t)split * a.B * a.H * a.Lp + (int64_t)bh * a.Lp + i;
-  floatx4* po = reinterpret_cast<floatx4*>(a.part_o + row * DP);
+  uint16_t* po = static_cast<uint16_t*>(a.part_o) + row * DP;
+  const float inv = l_sum > 0.0f ? 1.0f / l_sum : 0.0f;
 #pragma unroll
   for (int e = 0; e < 2; ++e)
 #pragma unroll
-    for (int g = 0; g < 4; ++g)
-      po[(32 * e + 8 * g + 4 * hf) / 4] =
-          floatx4{o[e][4 * g], o[e][4 * g + 1], o[e][4 * g + 2], o[e][4 * g + 3]};
+    for (int g = 0; g < 4; ++g) {
+      const bf16x2_t lo =
+          __builtin_convertvector(floatx2_t{o[e][4 * g] * inv, o[e][4 * g + 1] * inv}, bf16x2_t);
+      const bf16x2_t hi =
+          __builtin_convertvector(floatx2_t{o[e][4 * g + 2] * inv, o[e][4 * g + 3] * inv}, bf16x2_t);
+      *reinterpret_cast<u32x2*>(po + 32 * e + 8 * g + 4 * hf) =
+          u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+    }
   if (hf == 0) {
     // a range with no visible key for this query reports max -inf, sum 0
     a.part_ml[row * 2 + 0] = fresh ? kNegInf : m_ref;
@@ -498,9 +505,9 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a, int32_t p
   }
 }
 
-// Merge split partials in split order: out = sum_s 2^(m_s-m*) O_s / sum_s
-// 2^(m_s-m*) l_s.  16 threads per output row, 4 columns each; the partials of
-// all splits are loaded before any is used.  The workgroups past the output
+// Merge split partials in split order: with w_s = 2^(m_s-m*) l_s,
+// out = sum_s w_s (O_s / l_s) / sum_s w_s.  16 threads per output row, 4
+// columns each; the partials of all splits are loaded before any is used.  The workgroups past the output
 // rows copy the segment into the memory ring when the step asks for it.
 template <int S>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, int32_t out_blocks) {
@@ -520,7 +527,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, int32_t o
   const int ns = S > 0 ? S : a.n_split;
   constexpr int CAP = S > 0 ? S : 16;
   float ms[CAP], ls[CAP];
-  floatx4 os[CAP];
+  u32x2 os[CAP];   // four bf16 of O/sum
 #pragma unroll
   for (int s = 0; s < CAP; ++s) {
     if (s < ns) {
@@ -528,7 +535,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, int32_t o
       const float2 ml = reinterpret_cast<const float2*>(a.part_ml)[pr];
       ms[s] = ml.x;
       ls[s] = ml.y;
-      os[s] = reinterpret_cast<const floatx4*>(a.part_o + pr * DP)[c4];
+      os[s] = reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(a.part_o) + pr * DP)[c4];
     }
   }
   float mx = kNegInf;
@@ -540,9 +547,11 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, int32_t o
 #pragma unroll
   for (int s = 0; s < CAP; ++s) {
     if (s < ns) {
-      const float w = (ms[s] == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(ms[s] - mx);
-      num += w * os[s];
-      den += w * ls[s];
+      const float w = (ms[s] == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(ms[s] - mx) * ls[s];
+      const floatx4 x = floatx4{__uint_as_float(os[s][0] << 16), __uint_as_float(os[s][0] & 0xffff0000u),
+                                __uint_as_float(os[s][1] << 16), __uint_as_float(os[s][1] & 0xffff0000u)};
+      num += w * x;
+      den += w;
     }
   }
   const float inv = 1.0f / den;

@@ -124,7 +124,7 @@ struct AttnArgs {
   const void* u;           // [H][dh] in the call dtype
   const void* v;
   void* out;               // [B][L][H][dh] in the call dtype
-  float* part_o;           // split partials [n_split][B*H*Lp][DP]
+  void* part_o;            // split partials: bf16 O/sum [n_split][B*H*Lp][DP]
   float* part_ml;          // [n_split][B*H*Lp][2] (running max, sum)
   int32_t dtype;
   // optional fused ring update (bf16 kernel): copy min(L, M) rows of upd_src
