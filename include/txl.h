@@ -133,6 +133,52 @@ txl_status_t txl_rel_attn_fwd(const txl_attn_shape_t* shape, const void* h, cons
                               size_t workspace_bytes, void* stream);
 
 /*
+ * Carried projected-K/V memory for evaluation (bf16 only, seg_len % 32 == 0).
+ * Sec. 3.2 extends each segment with the cached hidden states,
+ * h~ = [SG(m) ; h], and Sec. 3.3 projects k = h~ W_kE^T, val = h~ W_v^T row by
+ * row.  With W_kE and W_v fixed (evaluation), the key and value of a memory
+ * row are exactly those computed when that row was in the segment, so a ring
+ * of projected keys and values can stand in for the hidden-state memory and a
+ * step then projects only its L new rows.  The attention itself is unchanged:
+ * same keys, values, position keys, mask and result as txl_rel_attn_fwd over
+ * the hidden-state memory the ring was built from.
+ *
+ * Ring (one per layer, caller-owned device memory, txl_kv_ring_bytes()):
+ * C = txl_kv_ring_slots() = round_up(M, 32) + L slots holding K
+ * [B][H][C][64] followed by V^T in 32-slot tiles [B][C/32][H][64][32], bf16,
+ * head width zero-padded to 64.  At ring start s, the G = round_up(M,32) - M
+ * slots s .. s+G-1 (mod C) are unused, the next M hold the memory oldest
+ * first, and the last L receive the segment's keys and values.  The layout is
+ * internal to the library; only these functions read or write it.
+ *
+ * txl_kv_ring_init projects a hidden-state memory mem [B][M][d_model]
+ * (logical row p at slot (mem_start + p) mod M, as in txl_rel_attn_fwd) into
+ * the ring and sets *ring_start (HOST pointer) to 0.  mem may be NULL iff
+ * M == 0.
+ * txl_rel_attn_fwd_kv computes txl_rel_attn_fwd's output for the segment h
+ * with the memory held by the ring, writes the segment's keys and values into
+ * the ring (so it is also the memory update) and advances *ring_start (HOST
+ * pointer, in/out, a multiple of 32 in [0, C)) by L mod C on success.
+ * Ring calls of one layer must be stream-ordered.  Both take a workspace of
+ * txl_kv_ring_workspace_bytes(); ring_bytes is the size of `ring`.
+ * Errors: fp32 or seg_len % 32 != 0 (TXL_ERR_UNSUPPORTED); NULL pointers;
+ * ring too small or *ring_start invalid (TXL_ERR_BAD_SHAPE); the errors of
+ * txl_rel_attn_fwd.  The query functions return 0 for unsupported shapes.
+ */
+int32_t txl_kv_ring_slots(const txl_attn_shape_t* shape);
+size_t txl_kv_ring_bytes(const txl_attn_shape_t* shape);
+size_t txl_kv_ring_workspace_bytes(const txl_attn_shape_t* shape);
+txl_status_t txl_kv_ring_init(const txl_attn_shape_t* shape, const void* mem, int32_t mem_start,
+                              const void* W_kE, const void* W_v, void* ring, size_t ring_bytes,
+                              int32_t* ring_start, void* workspace, size_t workspace_bytes,
+                              void* stream);
+txl_status_t txl_rel_attn_fwd_kv(const txl_attn_shape_t* shape, const void* h, const void* W_q,
+                                 const void* W_kE, const void* W_kR, const void* W_v,
+                                 const void* u, const void* v, const void* R, const void* Rk,
+                                 void* ring, size_t ring_bytes, int32_t* ring_start, void* out,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Memory update (Sec. 3.2: the memory caches the M most recent hidden states,
  * possibly spanning several segments).  New logical memory = last M rows of
  * [memory ; h].  If L < M the L oldest ring slots are overwritten with h and

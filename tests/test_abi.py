@@ -145,3 +145,59 @@ def test_rel_proj_and_sinusoid_validation(txl):
     assert g(None, 4, 4, txl.TXL_F32, None) == 1
     assert g(16, 0, 4, txl.TXL_F32, None) == 2
     assert g(16, 4, 4, 5, None) == 3
+
+
+def test_kv_ring_queries_and_validation(txl):
+    # eval-shaped layer: C = round_up(1600, 32) + 128 slots, K and V^T in bf16
+    s = _shape(txl, batch=8, seg_len=128, mem_len=1600, d_model=1024, n_heads=16, d_head=64,
+               d_pos=1024)
+    assert txl.txl_kv_ring_slots(s) == 1728
+    assert txl.txl_kv_ring_bytes(s) == 2 * 8 * 16 * 1728 * 64 * 2
+    assert txl.txl_kv_ring_workspace_bytes(s) > 0
+    # memory not a multiple of 32: ghost slots round it up
+    assert txl.txl_kv_ring_slots(_shape(txl, seg_len=64, mem_len=150)) == 160 + 64
+    # unsupported: fp32, segment not a multiple of 32
+    assert txl.txl_kv_ring_slots(_shape(txl, dtype=txl.TXL_F32, seg_len=32)) == 0
+    assert txl.txl_kv_ring_bytes(_shape(txl, seg_len=33)) == 0
+
+    s = _shape(txl, seg_len=32, mem_len=40)
+    rb = txl.txl_kv_ring_bytes(s)
+    wsb = txl.txl_kv_ring_workspace_bytes(s)
+    st = ctypes.c_int32(64)
+    f = txl.lib.txl_rel_attn_fwd_kv
+
+    def fwd(shape, ring_bytes=rb, ws_bytes=wsb, **kw):
+        p = dict(h=16, W_q=48, W_kE=64, W_kR=80, W_v=96, u=112, v=128, R=144, Rk=None,
+                 ring=192, out=160, ws=176)
+        p.update(kw)
+        return f(ctypes.byref(shape), p["h"], p["W_q"], p["W_kE"], p["W_kR"], p["W_v"], p["u"],
+                 p["v"], p["R"], p["Rk"], p["ring"], ring_bytes, ctypes.byref(st), p["out"],
+                 p["ws"], ws_bytes, None)
+
+    assert fwd(_shape(txl, seg_len=32, mem_len=40, dtype=txl.TXL_F32)) == 5
+    assert fwd(_shape(txl, seg_len=40, mem_len=40)) == 5
+    assert fwd(s, h=None) == 1
+    assert fwd(s, ring=None) == 1
+    assert fwd(s, W_kR=None, R=None) == 1
+    assert fwd(s, ring_bytes=rb - 1) == 2
+    assert fwd(s, ws_bytes=wsb - 1) == 4
+    assert fwd(s, ring=200) == 5                          # unaligned ring
+    st.value = 16                                          # not a multiple of 32
+    assert fwd(s) == 2 and st.value == 16
+    st.value = txl.txl_kv_ring_slots(s)                    # outside [0, C)
+    assert fwd(s) == 2 and st.value == txl.txl_kv_ring_slots(s)
+
+    g = txl.lib.txl_kv_ring_init
+    st.value = 96
+
+    def init(shape, mem=32, mem_start=0, ring=192, ring_bytes=rb, ws=176, ws_bytes=wsb):
+        return g(ctypes.byref(shape), mem, mem_start, 64, 96, ring, ring_bytes, ctypes.byref(st),
+                 ws, ws_bytes, None)
+
+    assert init(s, mem=None) == 1
+    assert init(s, mem_start=40) == 2
+    assert init(s, ring_bytes=rb - 1) == 2
+    assert init(s, ws_bytes=wsb - 1) == 4
+    assert init(s, ws=None) == 1
+    assert init(_shape(txl, seg_len=32, mem_len=40, dtype=txl.TXL_F32)) == 5
+    assert st.value == 96

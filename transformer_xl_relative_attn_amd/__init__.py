@@ -19,6 +19,8 @@ __all__ = [
     "txl_abi_version", "txl_status_str", "txl_last_error", "txl_sinusoid_pos",
     "txl_rel_proj_workspace_bytes", "txl_rel_proj", "txl_rel_attn_workspace_bytes",
     "txl_rel_attn_fwd", "txl_mem_update", "txl_segment_workspace_bytes", "txl_segment_step",
+    "txl_kv_ring_slots", "txl_kv_ring_bytes", "txl_kv_ring_workspace_bytes", "txl_kv_ring_init",
+    "txl_rel_attn_fwd_kv",
     "txl_timing_enable", "txl_timing_reset", "txl_timing_read",
 ]
 
@@ -75,6 +77,15 @@ _seg = _sig("txl_segment_step", ctypes.c_int,
             [ctypes.POINTER(AttnShape), _i32, _i32, ctypes.POINTER(Layer), _vp, _vp, _vp,
              ctypes.POINTER(_i32), _vp, _sz, _vp])
 
+_ring_slots = _sig("txl_kv_ring_slots", _i32, [ctypes.POINTER(AttnShape)])
+_ring_bytes = _sig("txl_kv_ring_bytes", _sz, [ctypes.POINTER(AttnShape)])
+_ring_ws = _sig("txl_kv_ring_workspace_bytes", _sz, [ctypes.POINTER(AttnShape)])
+_ring_init = _sig("txl_kv_ring_init", ctypes.c_int,
+                  [ctypes.POINTER(AttnShape), _vp, _i32, _vp, _vp, _vp, _sz,
+                   ctypes.POINTER(_i32), _vp, _sz, _vp])
+_attn_kv = _sig("txl_rel_attn_fwd_kv", ctypes.c_int,
+                [ctypes.POINTER(AttnShape), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                 _vp, _sz, ctypes.POINTER(_i32), _vp, _vp, _sz, _vp])
 
 _t_enable = _sig("txl_timing_enable", ctypes.c_int, [_i32])
 _t_reset = _sig("txl_timing_reset", None, [])
@@ -178,6 +189,39 @@ def txl_segment_step(shape: AttnShape, n_layers: int, d_inner: int, layers: Sequ
     _check(_seg(ctypes.byref(shape), n_layers, d_inner, arr, _ptr(R), _ptr(h_in), _ptr(h_out),
                 ctypes.byref(st), _ptr(workspace), _nbytes(workspace), _stream(stream)),
            "txl_segment_step")
+    return st.value
+
+
+def txl_kv_ring_slots(shape: AttnShape) -> int:
+    return _ring_slots(ctypes.byref(shape))
+
+
+def txl_kv_ring_bytes(shape: AttnShape) -> int:
+    return _ring_bytes(ctypes.byref(shape))
+
+
+def txl_kv_ring_workspace_bytes(shape: AttnShape) -> int:
+    return _ring_ws(ctypes.byref(shape))
+
+
+def txl_kv_ring_init(shape: AttnShape, mem, mem_start: int, W_kE, W_v, ring, workspace,
+                     stream=None) -> int:
+    """Returns the ring start (0)."""
+    st = _i32(0)
+    _check(_ring_init(ctypes.byref(shape), _ptr(mem), mem_start, _ptr(W_kE), _ptr(W_v),
+                      _ptr(ring), _nbytes(ring), ctypes.byref(st), _ptr(workspace),
+                      _nbytes(workspace), _stream(stream)), "txl_kv_ring_init")
+    return st.value
+
+
+def txl_rel_attn_fwd_kv(shape: AttnShape, h, W_q, W_kE, W_kR, W_v, u, v, R, Rk, ring,
+                        ring_start: int, out, workspace, stream=None) -> int:
+    """Returns the new ring start."""
+    st = _i32(ring_start)
+    _check(_attn_kv(ctypes.byref(shape), _ptr(h), _ptr(W_q), _ptr(W_kE), _ptr(W_kR), _ptr(W_v),
+                    _ptr(u), _ptr(v), _ptr(R), _ptr(Rk), _ptr(ring), _nbytes(ring),
+                    ctypes.byref(st), _ptr(out), _ptr(workspace), _nbytes(workspace),
+                    _stream(stream)), "txl_rel_attn_fwd_kv")
     return st.value
 
 

@@ -3,6 +3,7 @@
 // and in/out arguments keep their values.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <climits>
 #include <cmath>
 #include <cstdarg>
@@ -136,10 +137,18 @@ struct Region {
   size_t off = 0, bytes = 0;
 };
 
+// What a plan is for: the plain layer (K, V^T of [memory ; segment] in the
+// workspace), a step over a carried K/V ring (only the segment's K, V^T are
+// projected, into the ring), or the ring's initial projection of a memory.
+enum PlanKind { PLAN_STD = 0, PLAN_RING = 1, PLAN_RING_INIT = 2 };
+
 struct AttnPlan {
+  int kind;
   int B, L, M, d, H, dh, dpos, dtype;
   float scale;
   int DP, Lp, Np, Pp, P;
+  int Mk, G;               // keys before the segment as the kernel sees them
+                           // (ring: M rounded up to 32, G = Mk - M ghost keys)
   int rk_pad;              // padding rows before / after each head's Rk rows
   int n_split, nqg;
   bool pack_d, pack_pos;   // bf16 operands repacked to a K multiple of 64
@@ -177,8 +186,19 @@ txl_status_t check_shape(const txl_attn_shape_t* s) {
   return TXL_OK;
 }
 
-AttnPlan make_plan(const txl_attn_shape_t* s, bool compute_rk) {
+// The K/V ring path: bf16, and segments of whole 32-key tiles.
+txl_status_t check_ring_shape(const txl_attn_shape_t* s) {
+  TXL_TRY(check_shape(s));
+  if (s->dtype != TXL_BF16) return fail(TXL_ERR_UNSUPPORTED, "the K/V ring is bf16 only");
+  if (s->seg_len % 32 != 0)
+    return fail(TXL_ERR_UNSUPPORTED, "the K/V ring needs seg_len %% 32 == 0 (got %d)",
+                s->seg_len);
+  return TXL_OK;
+}
+
+AttnPlan make_plan(const txl_attn_shape_t* s, bool compute_rk, int kind = PLAN_STD) {
   AttnPlan p{};
+  p.kind = kind;
   p.B = s->batch;
   p.L = s->seg_len;
   p.M = s->mem_len;
@@ -194,12 +214,20 @@ AttnPlan make_plan(const txl_attn_shape_t* s, bool compute_rk) {
   p.Lp = bf ? (int)round_up(p.L, 32) : p.L;
   p.Np = bf ? (int)round_up(p.P, 32) : p.P;
   p.Pp = p.Np;
+  p.Mk = p.M;
+  p.G = 0;
+  if (kind != PLAN_STD) {
+    // ring of Mk + L slots: ghost keys, memory, segment; 32-key tiles
+    p.Mk = (int)round_up(p.M, 32);
+    p.G = p.Mk - p.M;
+    p.Np = p.Mk + p.L;
+  }
   p.rk_pad = bf ? kRkPad : 0;
   p.nqg = (p.L + 127) / 128;
   p.n_split = 1;
   if (bf) {
     const int64_t wgs = (int64_t)p.B * p.H * p.nqg;
-    const int nb_min = (p.M + std::min(p.L, 128) + 31) / 32;
+    const int nb_min = (p.Mk + std::min(p.L, 128) + 31) / 32;
     int want = (int)((512 + wgs - 1) / wgs);
     want = std::min(want, std::max(1, nb_min / 4));
     p.n_split = std::max(1, std::min(want, 16));
@@ -216,23 +244,25 @@ AttnPlan make_plan(const txl_attn_shape_t* s, bool compute_rk) {
     off = align256(off + bytes);
   };
   const size_t BH = (size_t)p.B * p.H;
-  take(p.q, BH * p.Lp * p.DP * 4);
-  take(p.k, BH * p.Np * p.DP * es);
-  take(p.v, BH * p.Np * p.DP * es);
-  take(p.rk, (size_t)p.H * (p.Pp + 2 * p.rk_pad) * p.DP * es);
-  if (p.n_split > 1) {
+  if (kind != PLAN_RING_INIT) take(p.q, BH * p.Lp * p.DP * 4);
+  if (kind == PLAN_STD) {
+    take(p.k, BH * p.Np * p.DP * es);
+    take(p.v, BH * p.Np * p.DP * es);
+  }
+  if (kind != PLAN_RING_INIT) take(p.rk, (size_t)p.H * (p.Pp + 2 * p.rk_pad) * p.DP * es);
+  if (kind != PLAN_RING_INIT && p.n_split > 1) {
     take(p.po, (size_t)p.n_split * BH * p.Lp * p.DP * 2);
     take(p.pml, (size_t)p.n_split * BH * p.Lp * 2 * 4);
   }
   const size_t Hd = (size_t)p.H * p.dh;
   if (p.pack_d) {
-    take(p.ph, (size_t)p.B * p.L * p.Kd * 2);
-    take(p.pmem, (size_t)p.B * p.M * p.Kd * 2);
-    take(p.pwq, Hd * p.Kd * 2);
+    if (kind != PLAN_RING_INIT) take(p.ph, (size_t)p.B * p.L * p.Kd * 2);
+    if (kind != PLAN_RING) take(p.pmem, (size_t)p.B * p.M * p.Kd * 2);
+    if (kind != PLAN_RING_INIT) take(p.pwq, Hd * p.Kd * 2);
     take(p.pwk, Hd * p.Kd * 2);
     take(p.pwv, Hd * p.Kd * 2);
   }
-  if (p.pack_pos) {
+  if (p.pack_pos && kind != PLAN_RING_INIT) {
     take(p.pwr, Hd * p.Kpos * 2);
     take(p.pr, (size_t)p.P * p.Kpos * 2);
   }
@@ -262,8 +292,9 @@ RowSrc src_headpad(const void* w, int64_t ld, int32_t dh, int32_t dp) {
   return r;
 }
 RowSrc src_htilde(const void* mem, const void* h, int64_t ld, int32_t np, int32_t M, int32_t L,
-                  int32_t start) {
+                  int32_t start, int32_t lead = 0) {
   RowSrc r{};
+  r.lead = lead;
   r.kind = ROW_HTILDE;
   r.p0 = mem;
   r.p1 = h;
@@ -290,8 +321,10 @@ void add_problem(GemmGroup& g, int32_t M, int32_t N, int32_t K, const RowSrc& a,
   g.total_tiles += p.tiles_m * p.tiles_n;
 }
 
+const AxisMap kNoAxis = make_axis(kLinearDiv, 0, 0);
+
 OutDst out_map(void* ptr, int dtype, int32_t mv, int32_t nv, AxisMap row, AxisMap col,
-               int flags = 0, const float* resid = nullptr) {
+               int flags = 0, const float* resid = nullptr, AxisMap col2 = kNoAxis) {
   OutDst o{};
   o.p = ptr;
   o.dtype = dtype;
@@ -300,17 +333,24 @@ OutDst out_map(void* ptr, int dtype, int32_t mv, int32_t nv, AxisMap row, AxisMa
   o.n_valid = nv;
   o.row = row;
   o.col = col;
+  o.col2 = col2;
   o.resid = resid;
   // vectorised epilogue: 4 consecutive columns (n % 4 == 0) map to 4
   // consecutive, aligned elements for every row
-  const bool col_ok = col.s2 == 1 && col.s1 % 4 == 0 && (col.div == kLinearDiv || col.div % 4 == 0);
+  // (the second column term must be constant over those groups)
+  const auto col2_ok = [&](int g) {
+    return col2.s2 == 0 && col2.s1 % g == 0 && (col2.div == kLinearDiv || col2.div % g == 0);
+  };
+  const bool col_ok = col.s2 == 1 && col.s1 % 4 == 0 &&
+                      (col.div == kLinearDiv || col.div % 4 == 0) && col2_ok(4);
   const bool row_ok = row.s1 % 4 == 0 && row.s2 % 4 == 0;
   const bool ptr_ok = (reinterpret_cast<uintptr_t>(ptr) % 16) == 0 &&
                       (!resid || (reinterpret_cast<uintptr_t>(resid) % 16) == 0);
   o.vec_ok = col_ok && row_ok && ptr_ok && nv % 4 == 0;
   // staged bf16 epilogue: 8 consecutive columns per 16-byte store, and rows
   // advanced 4 at a time with at most one wrap of the row axis per step
-  const bool col8 = col.s2 == 1 && col.s1 % 8 == 0 && (col.div == kLinearDiv || col.div % 8 == 0);
+  const bool col8 = col.s2 == 1 && col.s1 % 8 == 0 &&
+                    (col.div == kLinearDiv || col.div % 8 == 0) && col2_ok(8);
   const bool row8 = row.s1 % 8 == 0 && row.s2 % 8 == 0 && row.div >= 4;
   o.vec8_ok = dtype == TXL_BF16 && col8 && row8 && ptr_ok && nv % 8 == 0;
   return o;
@@ -329,14 +369,16 @@ struct AttnPtrs {
 };
 
 txl_status_t check_attn_ptrs(const txl_attn_shape_t* s, const AttnPtrs& a, bool need_ws,
-                             const void* ws) {
+                             const void* ws, bool need_mem = true) {
   if (!a.h || !a.W_q || !a.W_kE || !a.W_v || !a.u || !a.v || !a.out)
     return fail(TXL_ERR_NULL_ARG, "h, W_q, W_kE, W_v, u, v and out are required");
-  if (s->mem_len > 0 && !a.mem) return fail(TXL_ERR_NULL_ARG, "mem is NULL but mem_len > 0");
+  if (need_mem && s->mem_len > 0 && !a.mem)
+    return fail(TXL_ERR_NULL_ARG, "mem is NULL but mem_len > 0");
   if (!a.Rk && (!a.W_kR || !a.R))
     return fail(TXL_ERR_NULL_ARG, "either Rk or both W_kR and R are required");
   if (need_ws && !ws) return fail(TXL_ERR_NULL_ARG, "workspace is NULL");
-  if (s->mem_len > 0 ? (a.mem_start < 0 || a.mem_start >= s->mem_len) : a.mem_start != 0)
+  if (need_mem &&
+      (s->mem_len > 0 ? (a.mem_start < 0 || a.mem_start >= s->mem_len) : a.mem_start != 0))
     return fail(TXL_ERR_BAD_SHAPE, "mem_start %d outside [0, mem_len=%d)", a.mem_start,
                 s->mem_len);
   if (s->dtype == TXL_BF16) {
@@ -348,93 +390,87 @@ txl_status_t check_attn_ptrs(const txl_attn_shape_t* s, const AttnPtrs& a, bool 
   return TXL_OK;
 }
 
-// Enqueue the projections and the fused attention of one layer.  If mem_update
-// is set the ring update (reading `h`) is enqueued between them.
-txl_status_t run_rel_attn(const AttnPlan& p, const AttnPtrs& a, char* ws, void* stream,
-                          void* mem_upd, int32_t* new_start) {
-  const bool bf = p.dtype == TXL_BF16;
+// Operands as the GEMMs read them: the caller's tensors, or bf16 copies whose
+// rows are padded to a multiple of 64 elements.
+struct Operands {
+  const void *h, *mem, *Wq, *WkE, *Wv, *WkR, *R;
+  int64_t ld_d, ld_pos;
+};
+
+txl_status_t pack_operands(const AttnPlan& p, const AttnPtrs& a, char* ws, void* stream,
+                           Operands& o) {
   const int dt = p.dtype;
-  const int es = esize(dt);
   const int32_t Hd = p.H * p.dh;
-  char* q = ws + p.q.off;
-  char* k = ws + p.k.off;
-  char* v = ws + p.v.off;
-  char* rk = ws + p.rk.off;
-
-  const void* h = a.h;
-  const void* mem = a.mem;
-  const void *Wq = a.W_q, *WkE = a.W_kE, *Wv = a.W_v, *WkR = a.W_kR, *R = a.R;
-  int64_t ld_d = p.d, ld_pos = p.dpos;
+  o = Operands{a.h, a.mem, a.W_q, a.W_kE, a.W_v, a.W_kR, a.R, p.d, p.dpos};
+  const bool seg = p.kind != PLAN_RING_INIT;    // the segment h and W_q are read
+  const bool mem = p.kind != PLAN_RING && p.M > 0;
   if (p.pack_d) {
-    TXL_HIP(timed(K_PACK, stream, [&] { return launch_pack_rows(ws + p.ph.off, p.Kd, h, p.d, (int64_t)p.B * p.L, p.d, dt, stream); }),
-            "pack h");
-    if (p.M > 0)
-      TXL_HIP(timed(K_PACK, stream, [&] { return launch_pack_rows(ws + p.pmem.off, p.Kd, mem, p.d, (int64_t)p.B * p.M, p.d, dt,
-                               stream); }),
-              "pack mem");
-    TXL_HIP(timed(K_PACK, stream, [&] { return launch_pack_rows(ws + p.pwq.off, p.Kd, Wq, p.d, Hd, p.d, dt, stream); }), "pack W_q");
-    TXL_HIP(timed(K_PACK, stream, [&] { return launch_pack_rows(ws + p.pwk.off, p.Kd, WkE, p.d, Hd, p.d, dt, stream); }), "pack W_kE");
-    TXL_HIP(timed(K_PACK, stream, [&] { return launch_pack_rows(ws + p.pwv.off, p.Kd, Wv, p.d, Hd, p.d, dt, stream); }), "pack W_v");
-    h = ws + p.ph.off;
-    mem = ws + p.pmem.off;
-    Wq = ws + p.pwq.off;
-    WkE = ws + p.pwk.off;
-    Wv = ws + p.pwv.off;
-    ld_d = p.Kd;
+    auto pack = [&](const Region& r, const void* src, int64_t rows, const char* what,
+                    const void*& dst) -> txl_status_t {
+      TXL_HIP(timed(K_PACK, stream, [&] {
+                return launch_pack_rows(ws + r.off, p.Kd, src, p.d, rows, p.d, dt, stream);
+              }),
+              what);
+      dst = ws + r.off;
+      return TXL_OK;
+    };
+    if (seg) TXL_TRY(pack(p.ph, a.h, (int64_t)p.B * p.L, "pack h", o.h));
+    if (mem) TXL_TRY(pack(p.pmem, a.mem, (int64_t)p.B * p.M, "pack mem", o.mem));
+    if (seg) TXL_TRY(pack(p.pwq, a.W_q, Hd, "pack W_q", o.Wq));
+    TXL_TRY(pack(p.pwk, a.W_kE, Hd, "pack W_kE", o.WkE));
+    TXL_TRY(pack(p.pwv, a.W_v, Hd, "pack W_v", o.Wv));
+    o.ld_d = p.Kd;
   }
-  if (!a.Rk && p.pack_pos) {
-    TXL_HIP(timed(K_PACK, stream, [&] { return launch_pack_rows(ws + p.pwr.off, p.Kpos, WkR, p.dpos, Hd, p.dpos, dt, stream); }),
+  if (seg && !a.Rk && p.pack_pos) {
+    TXL_HIP(timed(K_PACK, stream, [&] { return launch_pack_rows(ws + p.pwr.off, p.Kpos, a.W_kR, p.dpos, Hd, p.dpos, dt, stream); }),
             "pack W_kR");
-    TXL_HIP(timed(K_PACK, stream, [&] { return launch_pack_rows(ws + p.pr.off, p.Kpos, R, p.dpos, p.P, p.dpos, dt, stream); }),
+    TXL_HIP(timed(K_PACK, stream, [&] { return launch_pack_rows(ws + p.pr.off, p.Kpos, a.R, p.dpos, p.P, p.dpos, dt, stream); }),
             "pack R");
-    WkR = ws + p.pwr.off;
-    R = ws + p.pr.off;
-    ld_pos = p.Kpos;
+    o.WkR = ws + p.pwr.off;
+    o.R = ws + p.pr.off;
+    o.ld_pos = p.Kpos;
   }
+  return TXL_OK;
+}
 
-  const int tile = gemm_tile(dt);
+// q = h W_q^T -> fp32 [B][H][Lp][DP]
+void add_q_problem(GemmGroup& g, const AttnPlan& p, const Operands& o, char* ws) {
   const int64_t DP = p.DP;
-  GemmGroup g{};
-  // q = h W_q^T -> fp32 [B][H][Lp][DP]
   add_problem(g, p.B * p.Lp, p.H * p.DP, p.Kd,
-              src_htilde(nullptr, h, ld_d, p.Lp, 0, p.L, 0), src_headpad(Wq, ld_d, p.dh, p.DP),
-              out_map(q, TXL_F32, p.B * p.Lp, p.H * p.DP,
+              src_htilde(nullptr, o.h, o.ld_d, p.Lp, 0, p.L, 0), src_headpad(o.Wq, o.ld_d, p.dh, p.DP),
+              out_map(ws + p.q.off, TXL_F32, p.B * p.Lp, p.H * p.DP,
                       axis(p.Lp, (int64_t)p.H * p.Lp * DP, DP), axis(p.DP, (int64_t)p.Lp * DP, 1)),
-              tile);
-  // k = h~ W_kE^T -> [B][H][Np][DP]
-  const RowSrc ht = src_htilde(mem, h, ld_d, p.Np, p.M, p.L, a.mem_start);
-  add_problem(g, p.B * p.Np, p.H * p.DP, p.Kd, ht, src_headpad(WkE, ld_d, p.dh, p.DP),
-              out_map(k, dt, p.B * p.Np, p.H * p.DP, axis(p.Np, (int64_t)p.H * p.Np * DP, DP),
-                      axis(p.DP, (int64_t)p.Np * DP, 1)),
-              tile);
-  if (bf) {
-    // val^T = W_v h~^T in 32-key tiles -> [B][Np/32][H][DP][32]: row (head, d)
-    // at (head*DP + d)*32, token b*Np + key at (token/32)*(H*DP*32) + key%32
-    // (Np is a multiple of 32)
-    add_problem(g, p.H * p.DP, p.B * p.Np, p.Kd, src_headpad(Wv, ld_d, p.dh, p.DP), ht,
-                out_map(v, dt, p.H * p.DP, p.B * p.Np, axis_linear(32),
-                        axis(32, (int64_t)p.H * DP * 32, 1)),
-                tile);
-  } else {
-    add_problem(g, p.B * p.Np, p.H * p.DP, p.Kd, ht, src_headpad(Wv, ld_d, p.dh, p.DP),
-                out_map(v, dt, p.B * p.Np, p.H * p.DP, axis(p.Np, (int64_t)p.H * p.Np * DP, DP),
-                        axis(p.DP, (int64_t)p.Np * DP, 1)),
-                tile);
-  }
+              gemm_tile(p.dtype));
+}
+
+// Position keys: computed into the workspace table [H][pad + Pp + pad][DP] as
+// one more problem of the group (rows of the padding not written), or the
+// caller's Rk repacked into it.
+txl_status_t add_rk(GemmGroup& g, const AttnPlan& p, const AttnPtrs& a, const Operands& o,
+                    char* ws, void* stream) {
+  const int dt = p.dtype;
+  const int64_t DP = p.DP;
+  char* rk = ws + p.rk.off;
   const int64_t rk_rows = p.Pp + 2 * p.rk_pad;   // per head, padding included
   if (!a.Rk) {
-    // Rk = R W_kR^T -> [H][pad + Pp + pad][DP] (rows of the padding not written)
-    add_problem(g, p.Pp, p.H * p.DP, p.Kpos, src_plain(R, ld_pos, p.P),
-                src_headpad(WkR, ld_pos, p.dh, p.DP),
-                out_map(rk + (size_t)p.rk_pad * DP * es, dt, p.Pp, p.H * p.DP, axis_linear(DP),
-                        axis(p.DP, rk_rows * DP, 1)),
-                tile);
-  } else {
-    TXL_HIP(timed(K_REPACK_RK, stream, [&] { return launch_repack_rk(a.Rk, rk, p.P, p.Pp, p.rk_pad, p.H, p.dh, p.DP, dt, stream); }), "repack Rk");
+    add_problem(g, p.Pp, p.H * p.DP, p.Kpos, src_plain(o.R, o.ld_pos, p.P),
+                src_headpad(o.WkR, o.ld_pos, p.dh, p.DP),
+                out_map(rk + (size_t)p.rk_pad * DP * esize(dt), dt, p.Pp, p.H * p.DP,
+                        axis_linear(DP), axis(p.DP, rk_rows * DP, 1)),
+                gemm_tile(dt));
+    return TXL_OK;
   }
-  TXL_TRY(after_launch(timed(K_PROJ_GEMM, stream, [&] { return launch_gemm(g, dt, stream); }),
-                       "projection GEMMs", stream));
+  TXL_HIP(timed(K_REPACK_RK, stream, [&] { return launch_repack_rk(a.Rk, rk, p.P, p.Pp, p.rk_pad, p.H, p.dh, p.DP, dt, stream); }), "repack Rk");
+  return TXL_OK;
+}
 
+// Enqueue the fused attention (and the split combine) over K, V^T already in
+// place.  `mem_upd` (optional) is the hidden-state ring to update with h.
+txl_status_t run_attention(const AttnPlan& p, const AttnPtrs& a, char* ws, void* stream,
+                           const void* k, const void* vt, int32_t kv_tile0, void* mem_upd,
+                           int32_t* new_start) {
+  const bool bf = p.dtype == TXL_BF16;
+  const int dt = p.dtype;
   // The ring update rides on the bf16 attention launch (the split combine, or
   // the attention kernel's tail with one split) when rows are 16-byte
   // multiples; otherwise it is a kernel of its own.  (Not when the output
@@ -457,17 +493,19 @@ txl_status_t run_rel_attn(const AttnPlan& p, const AttnPtrs& a, char* ws, void* 
   aa.B = p.B;
   aa.H = p.H;
   aa.L = p.L;
-  aa.M = p.M;
+  aa.M = p.Mk;
   aa.dh = p.dh;
   aa.Lp = p.Lp;
   aa.Np = p.Np;
   aa.Pp = p.Pp;
   aa.n_split = p.n_split;
+  aa.k_lo = p.G;
+  aa.kv_tile0 = kv_tile0;
   aa.c_scale = bf ? p.scale * 1.4426950408889634f : p.scale;
-  aa.q = reinterpret_cast<const float*>(q);
+  aa.q = reinterpret_cast<const float*>(ws + p.q.off);
   aa.k = k;
-  aa.vt = v;
-  aa.rk = rk;
+  aa.vt = vt;
+  aa.rk = ws + p.rk.off;
   aa.u = a.u;
   aa.v = a.v;
   aa.out = a.out;
@@ -491,6 +529,97 @@ txl_status_t run_rel_attn(const AttnPlan& p, const AttnPtrs& a, char* ws, void* 
     TXL_TRY(after_launch(timed(K_ATTN_COMBINE, stream, [&] { return launch_attn_combine(aa, stream); }),
                          "attention combine", stream));
   return TXL_OK;
+}
+
+// Enqueue the projections and the fused attention of one layer.  If mem_update
+// is set the ring update (reading `h`) is enqueued between them.
+txl_status_t run_rel_attn(const AttnPlan& p, const AttnPtrs& a, char* ws, void* stream,
+                          void* mem_upd, int32_t* new_start) {
+  const bool bf = p.dtype == TXL_BF16;
+  const int dt = p.dtype;
+  char* k = ws + p.k.off;
+  char* v = ws + p.v.off;
+  Operands o;
+  TXL_TRY(pack_operands(p, a, ws, stream, o));
+
+  const int tile = gemm_tile(dt);
+  const int64_t DP = p.DP;
+  GemmGroup g{};
+  add_q_problem(g, p, o, ws);
+  // k = h~ W_kE^T -> [B][H][Np][DP]
+  const RowSrc ht = src_htilde(o.mem, o.h, o.ld_d, p.Np, p.M, p.L, a.mem_start);
+  add_problem(g, p.B * p.Np, p.H * p.DP, p.Kd, ht, src_headpad(o.WkE, o.ld_d, p.dh, p.DP),
+              out_map(k, dt, p.B * p.Np, p.H * p.DP, axis(p.Np, (int64_t)p.H * p.Np * DP, DP),
+                      axis(p.DP, (int64_t)p.Np * DP, 1)),
+              tile);
+  if (bf) {
+    // val^T = W_v h~^T in 32-key tiles -> [B][Np/32][H][DP][32]: row (head, d)
+    // at (head*DP + d)*32, token b*Np + key at (token/32)*(H*DP*32) + key%32
+    // (Np is a multiple of 32)
+    add_problem(g, p.H * p.DP, p.B * p.Np, p.Kd, src_headpad(o.Wv, o.ld_d, p.dh, p.DP), ht,
+                out_map(v, dt, p.H * p.DP, p.B * p.Np, axis_linear(32),
+                        axis(32, (int64_t)p.H * DP * 32, 1)),
+                tile);
+  } else {
+    add_problem(g, p.B * p.Np, p.H * p.DP, p.Kd, ht, src_headpad(o.Wv, o.ld_d, p.dh, p.DP),
+                out_map(v, dt, p.B * p.Np, p.H * p.DP, axis(p.Np, (int64_t)p.H * p.Np * DP, DP),
+                        axis(p.DP, (int64_t)p.Np * DP, 1)),
+                tile);
+  }
+  TXL_TRY(add_rk(g, p, a, o, ws, stream));
+  TXL_TRY(after_launch(timed(K_PROJ_GEMM, stream, [&] { return launch_gemm(g, dt, stream); }),
+                       "projection GEMMs", stream));
+  return run_attention(p, a, ws, stream, k, v, 0, mem_upd, new_start);
+}
+
+// ------------------------------------------------------------- K/V ring
+// A layer's carried keys and values: C = Mk + L slots of K [B][H][C][DP]
+// followed by V^T in 32-slot tiles [B][C/32][H][DP][32] (bf16).  At a step
+// whose ring start is s (a multiple of 32), key j' of the kernel's sequence
+// [G ghost keys ; M memory rows ; L segment rows] sits at slot (s + j') mod C:
+// the ghost keys are masked, and the segment's rows are projected straight
+// into slots (s + Mk + p) mod C, i.e. over the oldest rows, which the next
+// step no longer sees.  The next step starts at (s + L) mod C.
+size_t ring_k_bytes(const AttnPlan& p) { return (size_t)p.B * p.H * p.Np * p.DP * 2; }
+size_t ring_bytes(const AttnPlan& p) { return 2 * ring_k_bytes(p); }
+
+// Append the K and V^T problems that project rows [p0, p0 + n) of every
+// batch's segment (or of the extended context, for the initial projection)
+// to ring slots slot0 + r (n, slot0 multiples of 32, no wrap inside).
+void add_ring_kv(GemmGroup& g, const AttnPlan& p, const RowSrc& src, int32_t n, int32_t slot0,
+                 const Operands& o, void* ring) {
+  const RingMaps m = ring_maps(p.H, p.DP, p.Np, n, slot0);
+  uint16_t* kr = static_cast<uint16_t*>(ring);
+  uint16_t* vr = kr + ring_k_bytes(p) / 2;
+  const int tile = gemm_tile(p.dtype);
+  add_problem(g, p.B * n, p.H * p.DP, p.Kd, src, src_headpad(o.WkE, o.ld_d, p.dh, p.DP),
+              out_map(kr + m.k_base, TXL_BF16, p.B * n, p.H * p.DP, m.k_row, m.k_col), tile);
+  add_problem(g, p.H * p.DP, p.B * n, p.Kd, src_headpad(o.Wv, o.ld_d, p.dh, p.DP), src,
+              out_map(vr + m.v_base, TXL_BF16, p.H * p.DP, p.B * n, m.v_row, m.v_col, 0, nullptr,
+                      m.v_col2),
+              tile);
+}
+
+txl_status_t run_rel_attn_ring(const AttnPlan& p, const AttnPtrs& a, void* ring, int32_t start,
+                               char* ws, void* stream) {
+  Operands o;
+  TXL_TRY(pack_operands(p, a, ws, stream, o));
+  GemmGroup g{};
+  add_q_problem(g, p, o, ws);
+  // the segment's rows go to slots base .. base + L - 1 (mod C): at most two
+  // contiguous pieces
+  const int32_t base = (start + p.Mk) % p.Np;
+  const int32_t n1 = ring_first_piece(start, p.Mk, p.L, p.Np);
+  add_ring_kv(g, p, src_htilde(nullptr, o.h, o.ld_d, n1, 0, p.L, 0), n1, base, o, ring);
+  if (n1 < p.L) {
+    const char* h2 = static_cast<const char*>(o.h) + (size_t)n1 * o.ld_d * 2;
+    add_ring_kv(g, p, src_htilde(nullptr, h2, o.ld_d, p.L - n1, 0, p.L, 0), p.L - n1, 0, o, ring);
+  }
+  TXL_TRY(add_rk(g, p, a, o, ws, stream));
+  TXL_TRY(after_launch(timed(K_PROJ_GEMM, stream, [&] { return launch_gemm(g, p.dtype, stream); }),
+                       "projection GEMMs", stream));
+  const char* kr = static_cast<const char*>(ring);
+  return run_attention(p, a, ws, stream, kr, kr + ring_k_bytes(p), start / 32, nullptr, nullptr);
 }
 
 // --------------------------------------------------------- segment planning
@@ -623,6 +752,85 @@ txl_status_t txl_rel_attn_fwd(const txl_attn_shape_t* shape, const void* h, cons
   if (workspace_bytes < need)
     return fail(TXL_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes, need);
   return run_rel_attn(p, a, static_cast<char*>(workspace), stream, nullptr, nullptr);
+}
+
+int32_t txl_kv_ring_slots(const txl_attn_shape_t* shape) {
+  if (check_ring_shape(shape) != TXL_OK) return 0;
+  return make_plan(shape, true, PLAN_RING).Np;
+}
+
+size_t txl_kv_ring_bytes(const txl_attn_shape_t* shape) {
+  if (check_ring_shape(shape) != TXL_OK) return 0;
+  return ring_bytes(make_plan(shape, true, PLAN_RING));
+}
+
+size_t txl_kv_ring_workspace_bytes(const txl_attn_shape_t* shape) {
+  if (check_ring_shape(shape) != TXL_OK) return 0;
+  return std::max(make_plan(shape, true, PLAN_RING).total,
+                  make_plan(shape, true, PLAN_RING_INIT).total);
+}
+
+txl_status_t txl_kv_ring_init(const txl_attn_shape_t* shape, const void* mem, int32_t mem_start,
+                              const void* W_kE, const void* W_v, void* ring, size_t ring_nbytes,
+                              int32_t* ring_start, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  TXL_TRY(check_ring_shape(shape));
+  if (!W_kE || !W_v || !ring || !ring_start || !workspace)
+    return fail(TXL_ERR_NULL_ARG, "W_kE, W_v, ring, ring_start and workspace are required");
+  if (shape->mem_len > 0 && !mem) return fail(TXL_ERR_NULL_ARG, "mem is NULL but mem_len > 0");
+  if (shape->mem_len > 0 ? (mem_start < 0 || mem_start >= shape->mem_len) : mem_start != 0)
+    return fail(TXL_ERR_BAD_SHAPE, "mem_start %d outside [0, mem_len=%d)", mem_start,
+                shape->mem_len);
+  for (const void* q : {mem, W_kE, W_v, (const void*)ring})
+    if (q && !aligned16(q))
+      return fail(TXL_ERR_UNSUPPORTED, "bf16 path needs 16-byte aligned tensor pointers");
+  const AttnPlan p = make_plan(shape, true, PLAN_RING_INIT);
+  if (ring_nbytes < ring_bytes(p))
+    return fail(TXL_ERR_BAD_SHAPE, "ring %zu < %zu bytes", ring_nbytes, ring_bytes(p));
+  const size_t need = txl_kv_ring_workspace_bytes(shape);
+  if (workspace_bytes < need)
+    return fail(TXL_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes, need);
+  if (p.M > 0) {
+    AttnPtrs a{nullptr, mem, nullptr, W_kE, nullptr, W_v, nullptr, nullptr, nullptr, nullptr,
+               mem_start, nullptr};
+    char* ws = static_cast<char*>(workspace);
+    Operands o;
+    TXL_TRY(pack_operands(p, a, ws, stream, o));
+    // slots 0 .. Mk-1: G zero rows, then the memory in logical order
+    GemmGroup g{};
+    add_ring_kv(g, p, src_htilde(o.mem, nullptr, o.ld_d, p.Mk, p.M, 0, mem_start, p.G), p.Mk, 0,
+                o, ring);
+    TXL_TRY(after_launch(timed(K_PROJ_GEMM, stream, [&] { return launch_gemm(g, p.dtype, stream); }),
+                         "ring projection GEMMs", stream));
+  }
+  *ring_start = 0;
+  return TXL_OK;
+}
+
+txl_status_t txl_rel_attn_fwd_kv(const txl_attn_shape_t* shape, const void* h, const void* W_q,
+                                 const void* W_kE, const void* W_kR, const void* W_v,
+                                 const void* u, const void* v, const void* R, const void* Rk,
+                                 void* ring, size_t ring_nbytes, int32_t* ring_start, void* out,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  TXL_TRY(check_ring_shape(shape));
+  AttnPtrs a{h, nullptr, W_q, W_kE, W_kR, W_v, u, v, R, Rk, 0, out};
+  TXL_TRY(check_attn_ptrs(shape, a, true, workspace, false));
+  if (!ring || !ring_start) return fail(TXL_ERR_NULL_ARG, "ring and ring_start are required");
+  if (!aligned16(ring))
+    return fail(TXL_ERR_UNSUPPORTED, "bf16 path needs 16-byte aligned tensor pointers");
+  const AttnPlan p = make_plan(shape, Rk == nullptr, PLAN_RING);
+  if (ring_nbytes < ring_bytes(p))
+    return fail(TXL_ERR_BAD_SHAPE, "ring %zu < %zu bytes", ring_nbytes, ring_bytes(p));
+  const int32_t start = *ring_start;
+  if (start < 0 || start >= p.Np || start % 32 != 0)
+    return fail(TXL_ERR_BAD_SHAPE, "ring_start %d is not a multiple of 32 in [0, %d)", start,
+                p.Np);
+  const size_t need = txl_kv_ring_workspace_bytes(shape);
+  if (workspace_bytes < need)
+    return fail(TXL_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes, need);
+  TXL_TRY(run_rel_attn_ring(p, a, ring, start, static_cast<char*>(workspace), stream));
+  *ring_start = (start + p.L) % p.Np;
+  return TXL_OK;
 }
 
 txl_status_t txl_mem_update(void* mem, int32_t* mem_start, const void* h, int32_t batch,

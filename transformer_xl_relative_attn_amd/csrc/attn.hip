@@ -208,13 +208,17 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a, int32_t p
   // Block tb's three loads of this wave.  Past the split's last block the
   // loads repeat that block (valid memory) into the free slots, so every wave
   // always issues three per block.
+  // K/V tiles are addressed through the ring rotation (block t at tile
+  // (t + kv_tile0) mod nkb; kv_tile0 = 0 outside the ring).
   auto issue_block = [&](int32_t tb) {
     const int32_t tl = min(tb, t_hi - 1);
+    int32_t tk = tl + a.kv_tile0;
+    tk -= tk >= nkb ? nkb : 0;
     u32x4* kv = sm.kv[(tb - t_lo) % NST];
     u32x4* rs = sm.rk[rk_slot(tb)];
 #pragma unroll
     for (int j = 0; j < LOADS_PER_BLOCK; ++j) {
-      const char* g = gbase[j] + tl * gstep[j];
+      const char* g = gbase[j] + (to_rk[j] ? tl : tk) * gstep[j];
       __builtin_amdgcn_global_load_lds(g + loff[j], (to_rk[j] ? rs : kv) + doff[j], 16, 0, 0);
     }
   };
@@ -373,13 +377,16 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a, int32_t p
     }
     bf16x8 pb[2];
     if (cur_on) {
-      // causal/memory mask: key j = 32t + jj visible iff j <= M + i0 + ii
+      // causal/memory mask: key j = 32t + jj visible iff k_lo <= j <= M + i0 + ii
       const int32_t j0 = t * KB;
-      if (j0 + KB - 1 > M + i0) {
+      if (j0 + KB - 1 > M + i0 || j0 < a.k_lo) {
         const int32_t lim = M + i0 + ii - j0 - 4 * hf;   // key jj = 8g + 4hf + r
+        const int32_t lo = a.k_lo - j0 - 4 * hf;
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-          if (8 * (e >> 2) + (e & 3) > lim) S[e] = kNegInf;
+        for (int e = 0; e < 16; ++e) {
+          const int kk = 8 * (e >> 2) + (e & 3);
+          if (kk > lim || kk < lo) S[e] = kNegInf;
+        }
       }
       float mb = max3(S[0], S[1], S[2]);
 #pragma unroll

@@ -55,8 +55,9 @@ __device__ __forceinline__ const char* row_address(const RowSrc& s, int32_t v, i
       break;
     }
     default: {  // ROW_HTILDE
-      int32_t b = v / s.np, r = v - b * s.np;
-      if (r < s.M) {
+      int32_t b = v / s.np, r = v - b * s.np - s.lead;
+      if (r < 0) {
+      } else if (r < s.M) {
         int32_t slot = r + s.start;
         if (slot >= s.M) slot -= s.M;
         p = static_cast<const char*>(s.p0) + ((int64_t)b * s.M + slot) * s.ld * esize;
@@ -71,6 +72,10 @@ __device__ __forceinline__ const char* row_address(const RowSrc& s, int32_t v, i
 
 __device__ __forceinline__ int64_t axis_off(const AxisMap& a, int32_t x) {
   return axis_offset(a, x);
+}
+
+__device__ __forceinline__ int64_t col_off(const OutDst& o, int32_t n) {
+  return axis_offset(o.col, n) + axis_offset(o.col2, n);
 }
 
 // Epilogue store of one accumulator element.

@@ -91,7 +91,7 @@ __device__ __forceinline__ void epilogue_vec(const OutDst& o, const floatx16 (&a
     for (int g = 0; g < 4; ++g) {
       const int32_t n = nb + 32 * j + 8 * g;
       if (n >= o.n_valid) continue;
-      const int64_t coff = axis_off(o.col, n);
+      const int64_t coff = col_off(o, n);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         if (!mok[i]) continue;
@@ -140,7 +140,7 @@ __device__ __forceinline__ void epilogue_staged(const OutDst& o, const floatx16 
   const int c = lane & 15, rsub = lane >> 4;
   const int32_t n = nw + 8 * c;
   const bool nok = n < o.n_valid;
-  const int64_t coff = axis_off(o.col, n);
+  const int64_t coff = col_off(o, n);
   // row offsets advance incrementally: +4 rows per step, at most one wrap of
   // the row axis (div >= 4)
   int32_t m = mw + rsub;
@@ -229,7 +229,7 @@ __device__ __forceinline__ void epilogue(const GemmProblem& P, const floatx16 (&
         const int32_t m = m0 + wm * 128 + 32 * i + ml;
         const int32_t n = n0 + wn * 128 + 32 * j + nl;
         if (m < o.m_valid && n < o.n_valid)
-          epi_store(o, axis_off(o.row, m) + axis_off(o.col, n), stage[ml * 33 + nl]);
+          epi_store(o, axis_off(o.row, m) + col_off(o, n), stage[ml * 33 + nl]);
       }
       wave_lds_fence();
     }
@@ -491,7 +491,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmGroup g, int32_t padd
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int32_t n = n0 + tx + 16 * j;
-      if (n < o.n_valid) epi_store(o, roff + axis_off(o.col, n), acc[i][j]);
+      if (n < o.n_valid) epi_store(o, roff + col_off(o, n), acc[i][j]);
     }
   }
 }

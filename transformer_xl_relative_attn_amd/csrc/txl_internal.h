@@ -14,9 +14,10 @@ namespace txl {
 //   ROW_PLAIN   v < rows ? p0 + v*ld : zero
 //   ROW_HEADPAD v = head*dp + c;  c < dh ? p0 + (head*dh + c)*ld : zero
 //               (weight rows of one head padded from dh to dp columns)
-//   ROW_HTILDE  v = b*np + r;  r < M   -> memory ring row (start + r) mod M of batch b
-//                              r < M+L -> segment row r - M of batch b
-//                              else    -> zero
+//   ROW_HTILDE  v = b*np + lead + r;  r < 0   -> zero
+//                                     r < M   -> memory ring row (start + r) mod M of batch b
+//                                     r < M+L -> segment row r - M of batch b
+//                                     else    -> zero
 //               (the extended context [memory ; segment] of Sec. 3.2, gathered in
 //               place: never materialised)
 // ---------------------------------------------------------------------------
@@ -27,6 +28,7 @@ struct RowSrc {
   int32_t rows;    // PLAIN: valid rows
   int32_t dh, dp;  // HEADPAD
   int32_t np, M, L, start;  // HTILDE
+  int32_t lead;             // HTILDE: zero rows before the memory rows
   int64_t ld;      // elements between consecutive source rows
   const void* p0;  // PLAIN/HEADPAD base, HTILDE memory base
   const void* p1;  // HTILDE segment base
@@ -38,10 +40,12 @@ struct RowSrc {
 #define TXL_HD
 #endif
 
-// Output address of element (m, n) = rowoff(m) + coloff(n), with
+// Output address of element (m, n) = rowoff(m) + coloff(n) + col2off(n), with
 //   off(x) = (x / div) * s1 + (x % div) * s2.
 // Covers row-major stores, head-split stores [b][head][r][c] and transposed
-// head-split stores [b][head][c][r].  The quotient uses a precomputed
+// head-split stores [b][head][c][r]; the second column term adds a per-batch
+// jump (K/V ring tiles, whose batch stride is not a multiple of the tokens
+// written).  The quotient uses a precomputed
 // multiply-shift (exact for 0 <= x < 2^31); div == kLinearDiv means q = 0.
 struct AxisMap {
   int32_t div;
@@ -73,6 +77,40 @@ TXL_HD inline int64_t axis_offset(const AxisMap& a, int32_t x) {
   return (int64_t)q * a.s1 + (int64_t)(x - q * a.div) * a.s2;
 }
 
+// K/V ring placement.  A ring of C slots (C a multiple of 32) holds K as
+// [B][H][C][DP] and, right after it, V^T in 32-slot tiles [B][C/32][H][DP][32].
+// The GEMM problems that project n tokens per batch (token index b*n + r) to
+// slots slot0 + r (n, slot0 multiples of 32, slot0 + n <= C) store through
+// these maps; offsets are in elements, relative to the start of K (k_*) and of
+// V^T (v_*).  K rows are tokens and columns head*DP + d; V^T rows are
+// head*DP + d and columns tokens.
+struct RingMaps {
+  int64_t k_base, v_base;
+  AxisMap k_row, k_col, v_row, v_col, v_col2;
+};
+
+inline RingMaps ring_maps(int32_t H, int32_t DP, int32_t C, int32_t n, int32_t slot0) {
+  const int64_t T = (int64_t)H * DP * 32;   // one 32-slot V^T tile of all heads
+  RingMaps m;
+  m.k_base = (int64_t)slot0 * DP;
+  m.k_row = make_axis(n, (int64_t)H * C * DP, DP);
+  m.k_col = make_axis(DP, (int64_t)C * DP, 1);
+  // token b*n + r -> tile b*C/32 + (slot0 + r)/32, lane (slot0 + r) % 32:
+  // (token/32)*T + token%32 plus a jump of (C - n)/32 tiles per batch
+  m.v_base = (int64_t)(slot0 / 32) * T;
+  m.v_row = make_axis(kLinearDiv, 0, 32);
+  m.v_col = make_axis(32, T, 1);
+  m.v_col2 = make_axis(n, (int64_t)(C / 32 - n / 32) * T, 0);
+  return m;
+}
+
+// The segment's L rows go to slots (base + p) mod C, base = (start + Mk) mod C:
+// n1 rows from `base`, then (if they wrap) L - n1 rows from slot 0.
+inline int32_t ring_first_piece(int32_t start, int32_t Mk, int32_t L, int32_t C) {
+  const int32_t base = (start + Mk) % C;
+  return L < C - base ? L : C - base;
+}
+
 enum EpiFlags : int32_t { EPI_RELU = 1, EPI_RESID = 2 };
 
 struct OutDst {
@@ -84,7 +122,7 @@ struct OutDst {
   int32_t vec8_ok;       // bf16: groups of 8 columns are contiguous and 16-byte
                          // aligned, and the row map has div >= 4
   int32_t m_valid, n_valid;  // store only m < m_valid, n < n_valid
-  AxisMap row, col;
+  AxisMap row, col, col2;
   const float* resid;    // EPI_RESID: out += resid[rowoff + coloff] (same map)
 };
 
@@ -116,10 +154,13 @@ struct AttnArgs {
   int32_t B, H, L, M, dh;
   int32_t Lp, Np, Pp;      // padded query rows, key rows, position rows
   int32_t n_split;         // key-range splits per query group (>= 1)
+  int32_t k_lo;            // keys j < k_lo are masked (ghost keys of the K/V ring)
+  int32_t kv_tile0;        // key block t is stored at 32-key tile (t + kv_tile0) mod (Np / 32)
   float c_scale;           // scale * log2(e) (bf16 path) or scale (fp32 path)
   const float* q;          // [B][H][Lp][DP] fp32
   const void* k;           // bf16 [B][H][Np][DP]   | f32 [B][H][Np][dh]
   const void* vt;          // bf16 [B][Np/32][H][DP][32] (transposed 32-key tiles) | f32 [B][H][Np][dh]
+                           // (K/V ring: Np = ring slots, block t at tile (t + kv_tile0) mod (Np/32))
   const void* rk;          // bf16 [H][kRkPad + Pp + kRkPad][DP] | f32 [H][Pp][dh]
   const void* u;           // [H][dh] in the call dtype
   const void* v;
