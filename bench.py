@@ -11,7 +11,10 @@ segments and advances the memory ring.
 Printed JSON line: metric value = algorithmic TFLOP/s of the step (projection,
 position-key and attention FLOPs over valid query/key pairs only), plus eval
 tokens/s, the roofline entry of the dominant kernel (timed live with HIP events
-on the launch stream) and the CPU oracle on a bounded sample.
+on the launch stream) and the CPU oracle on a bounded sample.  A second leg
+("kv_ring") streams the same segments through txl_segment_step_kv, which
+carries projected keys and values instead of hidden states (exact with fixed
+weights), and reports its tokens/s beside the headline step.
 """
 from __future__ import annotations
 
@@ -44,6 +47,15 @@ def flops(cfg, with_rk=True):
         extra = 2 * B * L * Hd * d + 2 * 2 * B * L * d * cfg.d_inner
     return dict(q=f_q, kv=f_kv, rk=f_rk, core=f_core, extra=extra,
                 total=f_q + f_kv + f_rk + f_core + extra, pairs=pairs)
+
+
+def flops_kv_ring(cfg, with_rk=True):
+    """Executed FLOPs of one step over a carried K/V ring: keys and values are
+    projected for the segment's L rows only."""
+    f = flops(cfg, with_rk)
+    B, L, d, Hd = cfg.batch, cfg.seg_len, cfg.d_model, cfg.n_heads * cfg.d_head
+    kv = 2 * 2 * B * L * d * Hd
+    return f["total"] - f["kv"] + kv
 
 
 def attn_bytes(cfg):
@@ -126,6 +138,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--cached-rk", action="store_true",
                     help="pass precomputed position keys (Rk computed once, outside the step)")
+    ap.add_argument("--no-ring", action="store_true",
+                    help="skip the carried K/V ring leg")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -265,6 +279,45 @@ def main():
                      "core_tflops": round(f["core"] / (us * 1e-6) / 1e12, 1),
                      "algorithmic_gbs": round(attn_bytes(cfg) / (us * 1e-6) / 1e9, 1)}
 
+    # ---- the same stream of segments over carried K/V rings (evaluation with
+    # fixed weights: memory keys and values are not recomputed)
+    ring_info = None
+    if cfg.dtype == "bf16" and cfg.seg_len % 32 == 0 and not args.no_ring:
+        ws_r = torch.empty(txl.txl_segment_kv_workspace_bytes(shape, cfg.n_layers, cfg.d_inner),
+                           dtype=torch.uint8, device="cuda")
+        rings = []
+        for n, w in enumerate(W):
+            ring = torch.empty(txl.txl_kv_ring_bytes(shape), dtype=torch.uint8, device="cuda")
+            txl.txl_kv_ring_init(shape, mems[n] if cfg.mem_len else None, state["start"],
+                                 w["W_kE"], w["W_v"], ring, ws_r, stream)
+            rings.append(ring)
+        rstate = {"start": 0, "i": 0}
+
+        def ring_step():
+            rstate["start"] = txl.txl_segment_step_kv(shape, cfg.n_layers, cfg.d_inner, layers,
+                                                      rings, R, segs[rstate["i"] % n_seg_pool],
+                                                      h_out, rstate["start"], ws_r, stream)
+            rstate["i"] += 1
+
+        for _ in range(args.warmup):
+            ring_step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev0.record(stream)
+        for _ in range(args.steps):
+            ring_step()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        wall_r = time.perf_counter() - t0
+        ms_r = max(ev0.elapsed_time(ev1), wall_r * 1e3) / args.steps
+        fr = flops_kv_ring(cfg, with_rk=not args.cached_rk) * cfg.n_layers
+        ring_info = {"ms_per_step": round(ms_r, 4),
+                     "tokens_per_s": round(cfg.batch * cfg.seg_len / (ms_r * 1e-3), 1),
+                     "speedup_vs_hidden_state_memory": round(ms_per_step / ms_r, 3),
+                     "executed_gflop_per_step": round(fr / 1e9, 3),
+                     "executed_tflops": round(fr / (ms_r * 1e-3) / 1e12, 1)}
+        del rings, ws_r
+
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(cfg, wl, args.cpu_budget)
@@ -294,6 +347,7 @@ def main():
         "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv)
                         for kk, vv in d.items()} for k, d in kernels.items()},
         "attention_kernel": attn_info,
+        "kv_ring": ring_info,
         "roofline": roof,
         "cpu_baseline": cpu,
     }

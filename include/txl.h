@@ -236,6 +236,25 @@ txl_status_t txl_segment_step(const txl_attn_shape_t* shape, int32_t n_layers, i
                               size_t workspace_bytes, void* stream);
 
 /*
+ * txl_segment_step over per-layer K/V rings (evaluation; see txl_kv_ring_init):
+ * rings[n] (ring_bytes each, txl_kv_ring_bytes()) carries layer n's projected
+ * keys and values and replaces layers[n].mem, which is not read.  Every ring
+ * must have been initialised (txl_kv_ring_init, from that layer's memory) and
+ * all share *ring_start (HOST pointer, in/out), advanced by L mod C once on
+ * success.  Same result as txl_segment_step on the hidden-state memories the
+ * rings were built from.  Workspace: txl_segment_kv_workspace_bytes() (also
+ * enough for txl_kv_ring_init).
+ * Errors: as txl_segment_step and txl_rel_attn_fwd_kv.
+ */
+size_t txl_segment_kv_workspace_bytes(const txl_attn_shape_t* shape, int32_t n_layers,
+                                      int32_t d_inner);
+txl_status_t txl_segment_step_kv(const txl_attn_shape_t* shape, int32_t n_layers,
+                                 int32_t d_inner, const txl_layer_t* layers,
+                                 void* const* rings, size_t ring_bytes, const void* R,
+                                 const void* h_in, void* h_out, int32_t* ring_start,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Kernel timing (diagnostics, off by default).  While enabled, every kernel the
  * library launches is bracketed by two HIP events recorded on its launch
  * stream.  txl_timing_read() waits for the recorded events, accumulates their

@@ -120,3 +120,69 @@ def test_ring_edges(txl, case):
     name, B, d, H, dh, L, M = case
     cfg = synth.Config(name, B, d, H, dh, L, M, 1, 3, "bf16", 0.05, 4242)
     _ring_case(txl, cfg, 3, np.arange(B))
+
+
+def run_segment_ring_stream(wl, n_seg):
+    """Stream n_seg segments through txl_segment_step_kv (rings initialised from
+    each layer's memory).  Returns the outputs per segment (float64)."""
+    import torch
+    import transformer_xl_relative_attn_amd as txl
+    c = wl.cfg
+    dl = DeviceLayers(wl)
+    shp = dl.shape()
+    ws = workspace(txl.txl_segment_kv_workspace_bytes(shp, c.n_layers, c.d_inner))
+    rings = []
+    for n, w in enumerate(dl.W):
+        ring = torch.empty(txl.txl_kv_ring_bytes(shp), dtype=torch.uint8, device="cuda")
+        assert txl.txl_kv_ring_init(shp, dl.mem[n] if c.mem_len else None, 0, w["W_kE"],
+                                    w["W_v"], ring, ws) == 0
+        rings.append(ring)
+    layers = dl.layer_structs()
+    d_out = c.d_model if c.d_inner else c.n_heads * c.d_head
+    start, outs = 0, []
+    for s in range(n_seg):
+        h = to_dev(wl.segments[s], c.dtype)
+        out = torch.empty((c.batch, c.seg_len, d_out), dtype=tdtype(c.dtype), device="cuda")
+        start = txl.txl_segment_step_kv(shp, c.n_layers, c.d_inner, layers, rings, dl.R, h, out,
+                                        start, ws)
+        torch.cuda.synchronize()
+        outs.append(from_dev(out))
+    return outs
+
+
+def test_segment_ring_small_stack(txl):
+    """Two full layers (W_o, LayerNorm, ReLU FFN), memory 72 (24 ghost slots)."""
+    cfg = synth.Config("ring_stack2", 2, 128, 2, 64, 32, 72, 2, 3, "bf16", 0.02, 1234,
+                       d_inner=256)
+    log("[case] kv-ring small stack")
+    wl = synth.make_workload(cfg)
+    outs = run_segment_ring_stream(wl, 3)
+    b_idx = np.arange(2)
+    o_outs, _, _ = oracle_stream(wl, 3, b_idx)
+    for s in range(3):
+        assert_close(outs[s][b_idx], o_outs[s], "bf16", f"segment {s}")
+
+
+def test_segment_ring_matches_hidden_state_step(txl):
+    """Memory a multiple of 32: the ring step equals txl_segment_step bit for bit."""
+    from gpu_helpers import run_segment_stream
+    cfg = synth.Config("ring_stack_eq", 2, 128, 2, 64, 64, 96, 2, 3, "bf16", 0.02, 555,
+                       d_inner=256)
+    log("[case] kv-ring stack vs hidden-state stack")
+    wl = synth.make_workload(cfg)
+    ring_outs = run_segment_ring_stream(wl, 3)
+    plain, _, _ = run_segment_stream(wl, 3)
+    for s in range(3):
+        assert np.array_equal(ring_outs[s], plain[s]), f"segment {s}"
+
+
+def test_segment_ring_stack_16_layers(txl):
+    """16-layer stack with the 3,800-state memory (8 ghost slots per ring)."""
+    cfg = synth.get_config("stack16_l128_m3800")
+    log("[case] kv-ring 16-layer stack, 4 segments")
+    wl = synth.make_workload(cfg)
+    outs = run_segment_ring_stream(wl, 4)
+    b_idx = np.array([0])
+    o_outs, _, _ = oracle_stream(wl, 4, b_idx)
+    for s in range(4):
+        assert_close(outs[s][b_idx], o_outs[s], "bf16", f"segment {s}")

@@ -20,7 +20,7 @@ __all__ = [
     "txl_rel_proj_workspace_bytes", "txl_rel_proj", "txl_rel_attn_workspace_bytes",
     "txl_rel_attn_fwd", "txl_mem_update", "txl_segment_workspace_bytes", "txl_segment_step",
     "txl_kv_ring_slots", "txl_kv_ring_bytes", "txl_kv_ring_workspace_bytes", "txl_kv_ring_init",
-    "txl_rel_attn_fwd_kv",
+    "txl_rel_attn_fwd_kv", "txl_segment_kv_workspace_bytes", "txl_segment_step_kv",
     "txl_timing_enable", "txl_timing_reset", "txl_timing_read",
 ]
 
@@ -86,6 +86,10 @@ _ring_init = _sig("txl_kv_ring_init", ctypes.c_int,
 _attn_kv = _sig("txl_rel_attn_fwd_kv", ctypes.c_int,
                 [ctypes.POINTER(AttnShape), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                  _vp, _sz, ctypes.POINTER(_i32), _vp, _vp, _sz, _vp])
+_seg_kv_ws = _sig("txl_segment_kv_workspace_bytes", _sz, [ctypes.POINTER(AttnShape), _i32, _i32])
+_seg_kv = _sig("txl_segment_step_kv", ctypes.c_int,
+               [ctypes.POINTER(AttnShape), _i32, _i32, ctypes.POINTER(Layer),
+                ctypes.POINTER(_vp), _sz, _vp, _vp, _vp, ctypes.POINTER(_i32), _vp, _sz, _vp])
 
 _t_enable = _sig("txl_timing_enable", ctypes.c_int, [_i32])
 _t_reset = _sig("txl_timing_reset", None, [])
@@ -222,6 +226,22 @@ def txl_rel_attn_fwd_kv(shape: AttnShape, h, W_q, W_kE, W_kR, W_v, u, v, R, Rk, 
                     _ptr(u), _ptr(v), _ptr(R), _ptr(Rk), _ptr(ring), _nbytes(ring),
                     ctypes.byref(st), _ptr(out), _ptr(workspace), _nbytes(workspace),
                     _stream(stream)), "txl_rel_attn_fwd_kv")
+    return st.value
+
+
+def txl_segment_kv_workspace_bytes(shape: AttnShape, n_layers: int, d_inner: int) -> int:
+    return _seg_kv_ws(ctypes.byref(shape), n_layers, d_inner)
+
+
+def txl_segment_step_kv(shape: AttnShape, n_layers: int, d_inner: int, layers: Sequence[Layer],
+                        rings, R, h_in, h_out, ring_start: int, workspace, stream=None) -> int:
+    """rings: one equally sized byte tensor per layer.  Returns the new ring start."""
+    arr = (Layer * len(layers))(*layers)
+    ptrs = (_vp * len(rings))(*[_ptr(r) for r in rings])
+    st = _i32(ring_start)
+    _check(_seg_kv(ctypes.byref(shape), n_layers, d_inner, arr, ptrs, _nbytes(rings[0]), _ptr(R),
+                   _ptr(h_in), _ptr(h_out), ctypes.byref(st), _ptr(workspace),
+                   _nbytes(workspace), _stream(stream)), "txl_segment_step_kv")
     return st.value
 
 

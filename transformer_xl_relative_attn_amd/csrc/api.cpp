@@ -630,9 +630,10 @@ struct SegPlan {
   size_t total;
 };
 
-SegPlan make_seg_plan(const txl_attn_shape_t* s, int32_t d_inner, bool any_full) {
+SegPlan make_seg_plan(const txl_attn_shape_t* s, int32_t d_inner, bool any_full,
+                      int kind = PLAN_STD) {
   SegPlan sp{};
-  sp.attn = make_plan(s, true);
+  sp.attn = make_plan(s, true, kind);
   sp.any_full = any_full;
   size_t off = align256(sp.attn.total);
   auto take = [&](Region& r, size_t bytes) {
@@ -656,6 +657,144 @@ SegPlan make_seg_plan(const txl_attn_shape_t* s, int32_t d_inner, bool any_full)
   }
   sp.total = off;
   return sp;
+}
+
+// Segment step over n_layers layers; with `rings` (one K/V ring per layer)
+// the layers attend through their rings and ly.mem is not used.
+txl_status_t segment_step(const txl_attn_shape_t* shape, int32_t n_layers, int32_t d_inner,
+                          const txl_layer_t* layers, void* const* rings, size_t ring_nbytes,
+                          const void* R, const void* h_in, void* h_out, int32_t* mem_start,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  const bool kv = rings != nullptr;
+  const int kind = kv ? PLAN_RING : PLAN_STD;
+  TXL_TRY(check_shape(shape));
+  if (n_layers < 1 || n_layers > 4096) return fail(TXL_ERR_BAD_SHAPE, "n_layers=%d", n_layers);
+  if (!layers || !h_in || !h_out || !mem_start || !workspace)
+    return fail(TXL_ERR_NULL_ARG, "layers, h_in, h_out, mem_start and workspace are required");
+  const int32_t start = *mem_start;
+  const int32_t d = shape->d_model, Hd = shape->n_heads * shape->d_head;
+  bool any_full = false;
+  for (int n = 0; n < n_layers; ++n) {
+    const txl_layer_t& ly = layers[n];
+    AttnPtrs a{h_in, kv ? nullptr : ly.mem, ly.W_q, ly.W_kE, ly.W_kR, ly.W_v, ly.u, ly.v, R,
+               ly.Rk, kv ? 0 : start, h_out};
+    txl_status_t st = check_attn_ptrs(shape, a, false, workspace, !kv);
+    if (st == TXL_OK && kv) {
+      const AttnPlan rp = make_plan(shape, true, PLAN_RING);
+      if (!rings[n])
+        st = fail(TXL_ERR_NULL_ARG, "ring is NULL");
+      else if (!aligned16(rings[n]))
+        st = fail(TXL_ERR_UNSUPPORTED, "bf16 path needs 16-byte aligned tensor pointers");
+      else if (ring_nbytes < ring_bytes(rp))
+        st = fail(TXL_ERR_BAD_SHAPE, "ring %zu < %zu bytes", ring_nbytes, ring_bytes(rp));
+      else if (start < 0 || start >= rp.Np || start % 32 != 0)
+        st = fail(TXL_ERR_BAD_SHAPE, "ring_start %d is not a multiple of 32 in [0, %d)", start,
+                  rp.Np);
+    }
+    if (st != TXL_OK) {
+      g_last_error = "layer " + std::to_string(n) + ": " + g_last_error;
+      return st;
+    }
+    if (ly.W_o) {
+      any_full = true;
+      if (!ly.W_ff1 || !ly.W_ff2)
+        return fail(TXL_ERR_NULL_ARG, "layer %d: W_ff1 and W_ff2 are required with W_o", n);
+      if (d_inner < 1 || d_inner > kMaxDim)
+        return fail(TXL_ERR_BAD_SHAPE, "d_inner=%d out of range", d_inner);
+      if (shape->dtype == TXL_BF16 &&
+          (!aligned16(ly.W_o) || !aligned16(ly.W_ff1) || !aligned16(ly.W_ff2)))
+        return fail(TXL_ERR_UNSUPPORTED, "bf16 path needs 16-byte aligned tensor pointers");
+      if (shape->dtype == TXL_BF16 && (Hd % 64 != 0 || d % 64 != 0 || d_inner % 64 != 0))
+        return fail(TXL_ERR_UNSUPPORTED,
+                    "bf16 full layers need H*d_head, d_model and d_inner multiples of 64");
+    } else if (n + 1 < n_layers && Hd != d) {
+      return fail(TXL_ERR_BAD_SHAPE,
+                  "layer %d has no W_o: H*d_head (%d) must equal d_model (%d) to feed layer %d",
+                  n, Hd, d, n + 1);
+    }
+  }
+  const SegPlan sp = make_seg_plan(shape, d_inner, any_full, kind);
+  if (workspace_bytes < sp.total)
+    return fail(TXL_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes,
+                sp.total);
+
+  char* ws = static_cast<char*>(workspace);
+  const int dt = shape->dtype;
+  const int32_t rows = shape->batch * shape->seg_len;
+  const int tile = gemm_tile(dt);
+  const void* x_lo = h_in;        // current layer input (storage dtype)
+  float* x32 = nullptr;           // fp32 residual copy of x_lo (full layers)
+  char* lo_buf[2] = {ws + sp.xlo_a.off, ws + sp.xlo_b.off};
+  float* f32_buf[2] = {reinterpret_cast<float*>(ws + sp.x32a.off),
+                       reinterpret_cast<float*>(ws + sp.x32b.off)};
+  int pp = 0;
+  int32_t new_start = start;
+  for (int n = 0; n < n_layers; ++n) {
+    const txl_layer_t& ly = layers[n];
+    const bool last = n + 1 == n_layers;
+    const bool full = ly.W_o != nullptr;
+    if (full && !x32) {
+      x32 = f32_buf[pp];
+      TXL_HIP(timed(K_CAST, stream, [&] { return launch_cast_f32(x_lo, x32, (int64_t)rows * d, dt, stream); }), "cast residual");
+    }
+    void* a_out = (!full && last) ? h_out : (full ? ws + sp.a.off : lo_buf[pp ^ 1]);
+    AttnPtrs a{x_lo, ly.mem, ly.W_q, ly.W_kE, ly.W_kR, ly.W_v, ly.u, ly.v, R, ly.Rk, start, a_out};
+    const AttnPlan p = make_plan(shape, ly.Rk == nullptr, kind);
+    if (kv) {
+      a.mem = nullptr;
+      TXL_TRY(run_rel_attn_ring(p, a, rings[n], start, ws, stream));
+      new_start = (start + p.L) % p.Np;
+    } else {
+      TXL_TRY(run_rel_attn(p, a, ws, stream, ly.mem, &new_start));
+    }
+    if (!full) {
+      x_lo = a_out;
+      x32 = nullptr;
+      pp ^= 1;
+      continue;
+    }
+    float* t32 = reinterpret_cast<float*>(ws + sp.t32.off);
+    float* o32 = reinterpret_cast<float*>(ws + sp.o32.off);
+    void* olo = ws + sp.olo.off;
+    void* hid = ws + sp.hid.off;
+    // t32 = a W_o^T + x  (fp32)
+    {
+      GemmGroup g{};
+      add_problem(g, rows, d, Hd, src_plain(ws + sp.a.off, Hd, rows), src_plain(ly.W_o, Hd, d),
+                  out_map(t32, TXL_F32, rows, d, axis_linear(d), axis_linear(1), EPI_RESID, x32),
+                  tile);
+      TXL_TRY(after_launch(timed(K_WO_GEMM, stream, [&] { return launch_gemm(g, dt, stream); }), "W_o GEMM",
+                           stream));
+    }
+    TXL_TRY(after_launch(timed(K_LAYERNORM, stream, [&] { return launch_layernorm(t32, o32, olo, rows, d, dt, 1e-5f, stream); }), "LN1",
+                         stream));
+    {
+      GemmGroup g{};
+      add_problem(g, rows, d_inner, d, src_plain(olo, d, rows), src_plain(ly.W_ff1, d, d_inner),
+                  out_map(hid, dt, rows, d_inner, axis_linear(d_inner), axis_linear(1), EPI_RELU),
+                  tile);
+      TXL_TRY(after_launch(timed(K_FFN1_GEMM, stream, [&] { return launch_gemm(g, dt, stream); }), "FFN1 GEMM",
+                           stream));
+    }
+    {
+      GemmGroup g{};
+      add_problem(g, rows, d, d_inner, src_plain(hid, d_inner, rows),
+                  src_plain(ly.W_ff2, d_inner, d),
+                  out_map(t32, TXL_F32, rows, d, axis_linear(d), axis_linear(1), EPI_RESID, o32),
+                  tile);
+      TXL_TRY(after_launch(timed(K_FFN2_GEMM, stream, [&] { return launch_gemm(g, dt, stream); }), "FFN2 GEMM",
+                           stream));
+    }
+    float* y32 = f32_buf[pp ^ 1];
+    void* ylo = last ? h_out : lo_buf[pp ^ 1];
+    TXL_TRY(after_launch(timed(K_LAYERNORM, stream, [&] { return launch_layernorm(t32, y32, ylo, rows, d, dt, 1e-5f, stream); }), "LN2",
+                         stream));
+    x_lo = ylo;
+    x32 = y32;
+    pp ^= 1;
+  }
+  *mem_start = new_start;
+  return TXL_OK;
 }
 
 }  // namespace
@@ -863,115 +1002,26 @@ txl_status_t txl_segment_step(const txl_attn_shape_t* shape, int32_t n_layers, i
                               const txl_layer_t* layers, const void* R, const void* h_in,
                               void* h_out, int32_t* mem_start, void* workspace,
                               size_t workspace_bytes, void* stream) {
-  TXL_TRY(check_shape(shape));
-  if (n_layers < 1 || n_layers > 4096) return fail(TXL_ERR_BAD_SHAPE, "n_layers=%d", n_layers);
-  if (!layers || !h_in || !h_out || !mem_start || !workspace)
-    return fail(TXL_ERR_NULL_ARG, "layers, h_in, h_out, mem_start and workspace are required");
-  const int32_t start = *mem_start;
-  const int32_t d = shape->d_model, Hd = shape->n_heads * shape->d_head;
-  bool any_full = false;
-  for (int n = 0; n < n_layers; ++n) {
-    const txl_layer_t& ly = layers[n];
-    AttnPtrs a{h_in, ly.mem, ly.W_q, ly.W_kE, ly.W_kR, ly.W_v, ly.u, ly.v, R, ly.Rk, start, h_out};
-    txl_status_t st = check_attn_ptrs(shape, a, false, workspace);
-    if (st != TXL_OK) {
-      g_last_error = "layer " + std::to_string(n) + ": " + g_last_error;
-      return st;
-    }
-    if (ly.W_o) {
-      any_full = true;
-      if (!ly.W_ff1 || !ly.W_ff2)
-        return fail(TXL_ERR_NULL_ARG, "layer %d: W_ff1 and W_ff2 are required with W_o", n);
-      if (d_inner < 1 || d_inner > kMaxDim)
-        return fail(TXL_ERR_BAD_SHAPE, "d_inner=%d out of range", d_inner);
-      if (shape->dtype == TXL_BF16 &&
-          (!aligned16(ly.W_o) || !aligned16(ly.W_ff1) || !aligned16(ly.W_ff2)))
-        return fail(TXL_ERR_UNSUPPORTED, "bf16 path needs 16-byte aligned tensor pointers");
-      if (shape->dtype == TXL_BF16 && (Hd % 64 != 0 || d % 64 != 0 || d_inner % 64 != 0))
-        return fail(TXL_ERR_UNSUPPORTED,
-                    "bf16 full layers need H*d_head, d_model and d_inner multiples of 64");
-    } else if (n + 1 < n_layers && Hd != d) {
-      return fail(TXL_ERR_BAD_SHAPE,
-                  "layer %d has no W_o: H*d_head (%d) must equal d_model (%d) to feed layer %d",
-                  n, Hd, d, n + 1);
-    }
-  }
-  const SegPlan sp = make_seg_plan(shape, d_inner, any_full);
-  if (workspace_bytes < sp.total)
-    return fail(TXL_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes,
-                sp.total);
+  return segment_step(shape, n_layers, d_inner, layers, nullptr, 0, R, h_in, h_out, mem_start,
+                      workspace, workspace_bytes, stream);
+}
 
-  char* ws = static_cast<char*>(workspace);
-  const int dt = shape->dtype;
-  const int32_t rows = shape->batch * shape->seg_len;
-  const int tile = gemm_tile(dt);
-  const void* x_lo = h_in;        // current layer input (storage dtype)
-  float* x32 = nullptr;           // fp32 residual copy of x_lo (full layers)
-  char* lo_buf[2] = {ws + sp.xlo_a.off, ws + sp.xlo_b.off};
-  float* f32_buf[2] = {reinterpret_cast<float*>(ws + sp.x32a.off),
-                       reinterpret_cast<float*>(ws + sp.x32b.off)};
-  int pp = 0;
-  int32_t new_start = start;
-  for (int n = 0; n < n_layers; ++n) {
-    const txl_layer_t& ly = layers[n];
-    const bool last = n + 1 == n_layers;
-    const bool full = ly.W_o != nullptr;
-    if (full && !x32) {
-      x32 = f32_buf[pp];
-      TXL_HIP(timed(K_CAST, stream, [&] { return launch_cast_f32(x_lo, x32, (int64_t)rows * d, dt, stream); }), "cast residual");
-    }
-    void* a_out = (!full && last) ? h_out : (full ? ws + sp.a.off : lo_buf[pp ^ 1]);
-    AttnPtrs a{x_lo, ly.mem, ly.W_q, ly.W_kE, ly.W_kR, ly.W_v, ly.u, ly.v, R, ly.Rk, start, a_out};
-    const AttnPlan p = make_plan(shape, ly.Rk == nullptr);
-    TXL_TRY(run_rel_attn(p, a, ws, stream, ly.mem, &new_start));
-    if (!full) {
-      x_lo = a_out;
-      x32 = nullptr;
-      pp ^= 1;
-      continue;
-    }
-    float* t32 = reinterpret_cast<float*>(ws + sp.t32.off);
-    float* o32 = reinterpret_cast<float*>(ws + sp.o32.off);
-    void* olo = ws + sp.olo.off;
-    void* hid = ws + sp.hid.off;
-    // t32 = a W_o^T + x  (fp32)
-    {
-      GemmGroup g{};
-      add_problem(g, rows, d, Hd, src_plain(ws + sp.a.off, Hd, rows), src_plain(ly.W_o, Hd, d),
-                  out_map(t32, TXL_F32, rows, d, axis_linear(d), axis_linear(1), EPI_RESID, x32),
-                  tile);
-      TXL_TRY(after_launch(timed(K_WO_GEMM, stream, [&] { return launch_gemm(g, dt, stream); }), "W_o GEMM",
-                           stream));
-    }
-    TXL_TRY(after_launch(timed(K_LAYERNORM, stream, [&] { return launch_layernorm(t32, o32, olo, rows, d, dt, 1e-5f, stream); }), "LN1",
-                         stream));
-    {
-      GemmGroup g{};
-      add_problem(g, rows, d_inner, d, src_plain(olo, d, rows), src_plain(ly.W_ff1, d, d_inner),
-                  out_map(hid, dt, rows, d_inner, axis_linear(d_inner), axis_linear(1), EPI_RELU),
-                  tile);
-      TXL_TRY(after_launch(timed(K_FFN1_GEMM, stream, [&] { return launch_gemm(g, dt, stream); }), "FFN1 GEMM",
-                           stream));
-    }
-    {
-      GemmGroup g{};
-      add_problem(g, rows, d, d_inner, src_plain(hid, d_inner, rows),
-                  src_plain(ly.W_ff2, d_inner, d),
-                  out_map(t32, TXL_F32, rows, d, axis_linear(d), axis_linear(1), EPI_RESID, o32),
-                  tile);
-      TXL_TRY(after_launch(timed(K_FFN2_GEMM, stream, [&] { return launch_gemm(g, dt, stream); }), "FFN2 GEMM",
-                           stream));
-    }
-    float* y32 = f32_buf[pp ^ 1];
-    void* ylo = last ? h_out : lo_buf[pp ^ 1];
-    TXL_TRY(after_launch(timed(K_LAYERNORM, stream, [&] { return launch_layernorm(t32, y32, ylo, rows, d, dt, 1e-5f, stream); }), "LN2",
-                         stream));
-    x_lo = ylo;
-    x32 = y32;
-    pp ^= 1;
-  }
-  *mem_start = new_start;
-  return TXL_OK;
+size_t txl_segment_kv_workspace_bytes(const txl_attn_shape_t* shape, int32_t n_layers,
+                                      int32_t d_inner) {
+  if (check_ring_shape(shape) != TXL_OK || n_layers < 1) return 0;
+  return std::max(make_seg_plan(shape, d_inner, d_inner > 0, PLAN_RING).total,
+                  make_plan(shape, true, PLAN_RING_INIT).total);
+}
+
+txl_status_t txl_segment_step_kv(const txl_attn_shape_t* shape, int32_t n_layers,
+                                 int32_t d_inner, const txl_layer_t* layers,
+                                 void* const* rings, size_t ring_bytes, const void* R,
+                                 const void* h_in, void* h_out, int32_t* ring_start,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  TXL_TRY(check_ring_shape(shape));
+  if (!rings) return fail(TXL_ERR_NULL_ARG, "rings is NULL");
+  return segment_step(shape, n_layers, d_inner, layers, rings, ring_bytes, R, h_in, h_out,
+                      ring_start, workspace, workspace_bytes, stream);
 }
 
 txl_status_t txl_timing_enable(int32_t on) {
