@@ -127,6 +127,143 @@ def cpu_baseline(cfg, wl, budget_s):
             "tokens_per_s": cfg.batch * cfg.seg_len * done / el}
 
 
+TABLE9_PAPER = {3800: 1874, 2800: 1409, 1800: 773, 800: 363}
+
+
+def table9(args):
+    """Evaluation speed of Sec. 4.5 / Table 9 at this library's scale: per-token
+    time of the vanilla sliding-window evaluation (Sec. 3.1: every step runs a
+    whole window of the attention length from scratch, no memory, and predicts
+    only its last position) against the Transformer-XL segment step (128 new
+    tokens per step against a memory of the attention length), both on the
+    16-layer stack (d_model 1024, 16 heads of 64, FFN 4096, batch 4, bf16).
+    The vanilla window runs through the same layers with M = 0 (the pages'
+    vanilla model uses absolute positions; the work per window is the same
+    shape).  Prints one JSON line."""
+    import numpy as np
+    import torch
+
+    import synth
+    import transformer_xl_relative_attn_amd as txl
+
+    cfg = synth.get_config("stack16_l128_m3800")
+    torch.cuda.set_device(0)
+    wl = synth.make_workload(cfg, n_segments=2)
+
+    def dev(x):
+        return torch.from_numpy(synth.bf16_bits(x).view(np.int16)).view(torch.bfloat16).cuda()
+
+    W = [dict(W_q=dev(l.W_q), W_kE=dev(l.W_kE), W_kR=dev(l.W_kR), W_v=dev(l.W_v),
+              W_o=dev(l.W_o), W_ff1=dev(l.W_ff1), W_ff2=dev(l.W_ff2)) for l in wl.layers]
+    u, v = dev(wl.u), dev(wl.v)
+    mems_full = [dev(m) for m in wl.mem]
+    segs = [dev(x) for x in wl.segments]
+    del wl
+    n_pos = cfg.mem_len + cfg.seg_len
+    R = torch.empty((n_pos, cfg.d_pos), dtype=torch.bfloat16, device="cuda")
+    txl.txl_sinusoid_pos(R, n_pos, cfg.d_pos, txl.TXL_BF16)
+    stream = torch.cuda.current_stream()
+    B, L, d = cfg.batch, cfg.seg_len, cfg.d_model
+
+    def timed(fn, warm, reps):
+        for _ in range(warm):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return max(e0.elapsed_time(e1), (time.perf_counter() - t0) * 1e3) / reps
+
+    def layer_list(mems):
+        return [txl.make_layer(w["W_q"], w["W_kE"], w["W_kR"], w["W_v"], u, v,
+                               None if mems is None else mems[n], W_o=w["W_o"],
+                               W_ff1=w["W_ff1"], W_ff2=w["W_ff2"]) for n, w in enumerate(W)]
+
+    rows = []
+    for A in (800, 1800, 2800, 3800):
+        # Transformer-XL: segment of 128 against a memory of A states per layer
+        mems = [m[:, -A:, :].contiguous() for m in mems_full]
+        shp = txl.AttnShape(B, L, A, d, cfg.n_heads, cfg.d_head, cfg.d_pos, txl.TXL_BF16, 0.0)
+        ws = torch.empty(txl.txl_segment_workspace_bytes(shp, cfg.n_layers, cfg.d_inner),
+                         dtype=torch.uint8, device="cuda")
+        out = torch.empty((B, L, d), dtype=torch.bfloat16, device="cuda")
+        layers = layer_list(mems)
+        st = {"start": 0, "i": 0}
+
+        def xl_step():
+            st["start"] = txl.txl_segment_step(shp, cfg.n_layers, cfg.d_inner, layers, R,
+                                               segs[st["i"] % 2], out, st["start"], ws, stream)
+            st["i"] += 1
+
+        ms_xl = timed(xl_step, 2, args.table9_steps)
+        # ... and over carried K/V rings
+        wsr = torch.empty(txl.txl_segment_kv_workspace_bytes(shp, cfg.n_layers, cfg.d_inner),
+                          dtype=torch.uint8, device="cuda")
+        rings = []
+        for n, w in enumerate(W):
+            ring = torch.empty(txl.txl_kv_ring_bytes(shp), dtype=torch.uint8, device="cuda")
+            txl.txl_kv_ring_init(shp, mems[n], st["start"], w["W_kE"], w["W_v"], ring, wsr,
+                                 stream)
+            rings.append(ring)
+        rs = {"start": 0, "i": 0}
+
+        def ring_step():
+            rs["start"] = txl.txl_segment_step_kv(shp, cfg.n_layers, cfg.d_inner, layers, rings,
+                                                  R, segs[rs["i"] % 2], out, rs["start"], wsr,
+                                                  stream)
+            rs["i"] += 1
+
+        ms_ring = timed(ring_step, 2, args.table9_steps)
+        del rings, wsr, ws, mems, layers
+        # vanilla: the whole window of A positions from scratch, no memory
+        vshp = txl.AttnShape(B, A, 0, d, cfg.n_heads, cfg.d_head, cfg.d_pos, txl.TXL_BF16, 0.0)
+        vws = torch.empty(txl.txl_segment_workspace_bytes(vshp, cfg.n_layers, cfg.d_inner),
+                          dtype=torch.uint8, device="cuda")
+        win = mems_full[0][:, -A:, :].contiguous()
+        vout = torch.empty((B, A, d), dtype=torch.bfloat16, device="cuda")
+        vlayers = layer_list(None)
+
+        def vanilla_step():
+            txl.txl_segment_step(vshp, cfg.n_layers, cfg.d_inner, vlayers, R, win, vout, 0, vws,
+                                 stream)
+
+        ms_van = timed(vanilla_step, 1, max(1, args.table9_steps // 2))
+        del vws, win, vout
+        xl_tok = ms_xl * 1e3 / (B * L)
+        ring_tok = ms_ring * 1e3 / (B * L)
+        van_tok = ms_van * 1e3 / B        # one prediction per window and batch row
+        rows.append({"attn_len": A, "xl_us_per_token": round(xl_tok, 3),
+                     "xl_kv_ring_us_per_token": round(ring_tok, 3),
+                     "vanilla_us_per_token": round(van_tok, 3),
+                     "slowdown_vs_xl": round(van_tok / xl_tok, 1),
+                     "slowdown_vs_xl_kv_ring": round(van_tok / ring_tok, 1),
+                     "paper_slowdown": TABLE9_PAPER[A]})
+        print(json.dumps(rows[-1]), file=sys.stderr, flush=True)
+    out = {
+        "metric": "eval slowdown of the vanilla sliding window vs the XL segment step "
+                  "(per-token time, attention length 3800)",
+        "value": rows[-1]["slowdown_vs_xl"],
+        "unit": "x",
+        "n_gpus": 1,
+        "steps": args.table9_steps,
+        "higher_is_better": True,
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "table9: 16-layer stack, d_model 1024, 16x64 heads, FFN 4096, "
+                               "batch 4, segment 128, attention lengths 800-3800"},
+        "table9": rows,
+        "paper_context": "Table 9 ratios are per-token evaluation time on one GPU; the "
+                         "pages name neither the GPU, the model size nor the precision",
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__,
                                  formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -142,12 +279,20 @@ def main():
                     help="skip the carried K/V ring leg")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--table9", action="store_true",
+                    help="instead of the headline, measure the vanilla-vs-XL evaluation "
+                         "slowdown at attention lengths 800..3800 (one JSON line)")
+    ap.add_argument("--table9-steps", type=int, default=6)
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the relative-attention step has no "
               "multi-GPU path in this library (run with --gpus 1).", file=sys.stderr)
         sys.exit(2)
+
+    if args.table9:
+        table9(args)
+        return
 
     import numpy as np
     import torch

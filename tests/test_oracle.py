@@ -134,6 +134,41 @@ def test_reduces_to_causal_attention(M):
     assert np.max(np.abs(got - ref)) <= 1e-12
 
 
+@pytest.mark.parametrize("M", [0, 4, 7])
+def test_shaw_variant_two_terms(M):
+    """The Shaw et al. (2018) form compared in Sec. 3.3 keeps only terms (a) and
+    (b), with a learned table R_hat in place of W_kR R.  Taking u = v = 0 and the
+    caller's Rk = R_hat must give: torch's scaled-dot-product attention in
+    float64 with an additive bias scale * q_i . R_hat[M+i-j], the bias formed
+    pair by pair in Python loops."""
+    B, d, H, dh, L = 2, 10, 2, 5, 6
+    wl, lay, R = _case(seed=19, B=B, d=d, H=H, dh=dh, L=L, M=M)
+    h, mem = wl.segments[0], wl.mem[0]
+    rng = np.random.default_rng(3)
+    R_hat = rng.normal(0.0, 0.5, (M + L, H, dh))
+    z = np.zeros_like
+    scale = 0.41
+    got = oracle.rel_attn_fwd(h, mem, lay.W_q, lay.W_kE, None, lay.W_v, z(wl.u), z(wl.v), None,
+                              H, dh, scale, Rk=R_hat)
+    ht = np.concatenate([mem, h], axis=1)
+    qn = (h @ lay.W_q.T).reshape(B, L, H, dh)
+    bias = np.full((B, H, L, M + L), -np.inf)
+    for b in range(B):
+        for hh in range(H):
+            for i in range(L):
+                for j in range(M + i + 1):
+                    bias[b, hh, i, j] = scale * sum(qn[b, i, hh, c] * R_hat[M + i - j, hh, c]
+                                                    for c in range(dh))
+    q = torch.tensor(qn).transpose(1, 2)
+    k = torch.tensor(ht @ lay.W_kE.T).reshape(B, M + L, H, dh).transpose(1, 2)
+    val = torch.tensor(ht @ lay.W_v.T).reshape(B, M + L, H, dh).transpose(1, 2)
+    ref = torch.nn.functional.scaled_dot_product_attention(q, k, val,
+                                                           attn_mask=torch.tensor(bias),
+                                                           scale=scale)
+    ref = ref.transpose(1, 2).reshape(B, L, H * dh).numpy()
+    assert np.max(np.abs(got - ref)) <= 1e-12
+
+
 # --------------------------------------------------------- term invariants
 def test_term_structure():
     """(c) does not depend on the query position and (d) depends only on i - j

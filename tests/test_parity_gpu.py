@@ -237,3 +237,59 @@ def test_segment_step_in_place(txl):
     for s in range(3):
         assert_close(outs[s], o_outs[s], "bf16", f"segment {s}")
     _check_ring(dl, wl, o_mems, start_o, start, b_idx)
+
+
+# ------------------------------------------------- Shaw et al. variant
+@pytest.mark.parametrize("path", ["hidden_state", "kv_ring"])
+def test_shaw_variant(txl, path):
+    """Terms (a) + (b) only with a learned table R_hat (the Shaw et al. form
+    compared in Sec. 3.3): u = v = 0 and the caller's Rk = R_hat; W_kR and R are
+    not passed.  Eval-shaped layer, 3 segments, through the hidden-state memory
+    and through the K/V ring."""
+    import torch
+    import oracle
+    cfg = synth.get_config("eval_l128_m1600", batch=2)
+    log(f"[case] Shaw variant via {path}")
+    wl = synth.make_workload(cfg, n_segments=3)
+    rng = np.random.default_rng(2018)
+    n_pos = cfg.mem_len + cfg.seg_len
+    R_hat = synth.round_to(rng.normal(0.0, 1.0, (n_pos, cfg.n_heads, cfg.d_head)), "bf16")
+    zeros = np.zeros((cfg.n_heads, cfg.d_head))
+    dl = DeviceLayers(wl)
+    zu = to_dev(zeros, "bf16")
+    Rk = to_dev(R_hat, "bf16")
+    shp = dl.shape()
+    w = dl.W[0]
+    outs = []
+    if path == "hidden_state":
+        ws = workspace(txl.txl_rel_attn_workspace_bytes(shp))
+        start = 0
+        for s in range(3):
+            h = to_dev(wl.segments[s], "bf16")
+            out = torch.empty((cfg.batch, cfg.seg_len, cfg.n_heads * cfg.d_head),
+                              dtype=torch.bfloat16, device="cuda")
+            txl.txl_rel_attn_fwd(shp, h, dl.mem[0], start, w["W_q"], w["W_kE"], None, w["W_v"],
+                                 zu, zu, None, Rk, out, ws)
+            start = txl.txl_mem_update(dl.mem[0], start, h, cfg.batch, cfg.mem_len, cfg.seg_len,
+                                       cfg.d_model, txl.TXL_BF16)
+            torch.cuda.synchronize()
+            outs.append(from_dev(out))
+    else:
+        ws = workspace(txl.txl_kv_ring_workspace_bytes(shp))
+        ring = torch.empty(txl.txl_kv_ring_bytes(shp), dtype=torch.uint8, device="cuda")
+        start = txl.txl_kv_ring_init(shp, dl.mem[0], 0, w["W_kE"], w["W_v"], ring, ws)
+        for s in range(3):
+            h = to_dev(wl.segments[s], "bf16")
+            out = torch.empty((cfg.batch, cfg.seg_len, cfg.n_heads * cfg.d_head),
+                              dtype=torch.bfloat16, device="cuda")
+            start = txl.txl_rel_attn_fwd_kv(shp, h, w["W_q"], w["W_kE"], None, w["W_v"], zu, zu,
+                                            None, Rk, ring, start, out, ws)
+            torch.cuda.synchronize()
+            outs.append(from_dev(out))
+    mems = [m for m in wl.mem]
+    start_o = 0
+    for s in range(3):
+        want, mems, start_o, _ = oracle.segment_step(wl.segments[s], wl.layers, mems, start_o,
+                                                     zeros, zeros, None, cfg.n_heads,
+                                                     cfg.d_head, Rks=[R_hat])
+        assert_close(outs[s], want, "bf16", f"segment {s}")
