@@ -348,10 +348,10 @@ OutDst out_map(void* ptr, int dtype, int32_t mv, int32_t nv, AxisMap row, AxisMa
                       (!resid || (reinterpret_cast<uintptr_t>(resid) % 16) == 0);
   o.vec_ok = col_ok && row_ok && ptr_ok && nv % 4 == 0;
   // staged bf16 epilogue: 8 consecutive columns per 16-byte store, and rows
-  // advanced 4 at a time with at most one wrap of the row axis per step
+  // advanced up to 8 at a time with at most one wrap of the row axis per step
   const bool col8 = col.s2 == 1 && col.s1 % 8 == 0 &&
                     (col.div == kLinearDiv || col.div % 8 == 0) && col2_ok(8);
-  const bool row8 = row.s1 % 8 == 0 && row.s2 % 8 == 0 && row.div >= 4;
+  const bool row8 = row.s1 % 8 == 0 && row.s2 % 8 == 0 && row.div >= 8;
   o.vec8_ok = dtype == TXL_BF16 && col8 && row8 && ptr_ok && nv % 8 == 0;
   return o;
 }
@@ -623,10 +623,23 @@ txl_status_t run_rel_attn_ring(const AttnPlan& p, const AttnPtrs& a, void* ring,
 }
 
 // --------------------------------------------------------- segment planning
+// Split-K factor (a power of two <= kMaxGroup) for a rows x N product of
+// reduction length K whose fp32 result feeds a LayerNorm: grow it while the
+// 128x128 tiles of all splits still fit the compute units once and every split
+// keeps at least 256 of K (K / S a multiple of 64).
+int split_k(int32_t rows, int32_t N, int32_t K) {
+  const int64_t t = (int64_t)((rows + 127) / 128) * ((N + 127) / 128);
+  const int64_t cus = device_cu_count();
+  int S = 1;
+  while (2 * S <= kMaxGroup && t * 2 * S <= cus && K % (64 * 2 * S) == 0 && K / (2 * S) >= 256)
+    S *= 2;
+  return S;
+}
+
 struct SegPlan {
   AttnPlan attn;
   bool any_full;
-  Region a, x32a, x32b, xlo_a, xlo_b, t32, o32, olo, hid;
+  Region a, x32a, x32b, xlo_a, xlo_b, parts, o32, olo, hid;
   size_t total;
 };
 
@@ -650,7 +663,7 @@ SegPlan make_seg_plan(const txl_attn_shape_t* s, int32_t d_inner, bool any_full,
   if (any_full) {
     take(sp.x32a, rows * s->d_model * 4);
     take(sp.x32b, rows * s->d_model * 4);
-    take(sp.t32, rows * s->d_model * 4);
+    take(sp.parts, kMaxGroup * rows * s->d_model * 4);
     take(sp.o32, rows * s->d_model * 4);
     take(sp.olo, rows * s->d_model * es);
     take(sp.hid, rows * (size_t)std::max(d_inner, 1) * es);
@@ -753,20 +766,32 @@ txl_status_t segment_step(const txl_attn_shape_t* shape, int32_t n_layers, int32
       pp ^= 1;
       continue;
     }
-    float* t32 = reinterpret_cast<float*>(ws + sp.t32.off);
+    float* parts = reinterpret_cast<float*>(ws + sp.parts.off);
+    const int64_t pstride = (int64_t)rows * d;
     float* o32 = reinterpret_cast<float*>(ws + sp.o32.off);
     void* olo = ws + sp.olo.off;
     void* hid = ws + sp.hid.off;
-    // t32 = a W_o^T + x  (fp32)
-    {
+    // parts[s] = A[:, Ks*s ..) W[:, Ks*s ..)^T (fp32), K split S ways; the
+    // LayerNorm that follows adds the residual and the S partial products
+    auto split_gemm = [&](const void* A, const void* Wt, int32_t K, int kind,
+                          const char* what, int* S_out) -> txl_status_t {
+      const int S = dt == TXL_BF16 ? split_k(rows, d, K) : 1;
+      const int32_t Ks = K / S;
       GemmGroup g{};
-      add_problem(g, rows, d, Hd, src_plain(ws + sp.a.off, Hd, rows), src_plain(ly.W_o, Hd, d),
-                  out_map(t32, TXL_F32, rows, d, axis_linear(d), axis_linear(1), EPI_RESID, x32),
-                  tile);
-      TXL_TRY(after_launch(timed(K_WO_GEMM, stream, [&] { return launch_gemm(g, dt, stream); }), "W_o GEMM",
-                           stream));
-    }
-    TXL_TRY(after_launch(timed(K_LAYERNORM, stream, [&] { return launch_layernorm(t32, o32, olo, rows, d, dt, 1e-5f, stream); }), "LN1",
+      for (int sk = 0; sk < S; ++sk)
+        add_problem(g, rows, d, Ks,
+                    src_plain(static_cast<const char*>(A) + (size_t)sk * Ks * esize(dt), K, rows),
+                    src_plain(static_cast<const char*>(Wt) + (size_t)sk * Ks * esize(dt), K, d),
+                    out_map(parts + sk * pstride, TXL_F32, rows, d, axis_linear(d), axis_linear(1)),
+                    tile);
+      *S_out = S;
+      return after_launch(timed(kind, stream, [&] { return launch_gemm(g, dt, stream); }), what,
+                          stream);
+    };
+    // o = LN(a W_o^T + x)
+    int S = 1;
+    TXL_TRY(split_gemm(ws + sp.a.off, ly.W_o, Hd, K_WO_GEMM, "W_o GEMM", &S));
+    TXL_TRY(after_launch(timed(K_LAYERNORM, stream, [&] { return launch_layernorm(x32, parts, S, pstride, o32, olo, rows, d, dt, 1e-5f, stream); }), "LN1",
                          stream));
     {
       GemmGroup g{};
@@ -776,18 +801,11 @@ txl_status_t segment_step(const txl_attn_shape_t* shape, int32_t n_layers, int32
       TXL_TRY(after_launch(timed(K_FFN1_GEMM, stream, [&] { return launch_gemm(g, dt, stream); }), "FFN1 GEMM",
                            stream));
     }
-    {
-      GemmGroup g{};
-      add_problem(g, rows, d, d_inner, src_plain(hid, d_inner, rows),
-                  src_plain(ly.W_ff2, d_inner, d),
-                  out_map(t32, TXL_F32, rows, d, axis_linear(d), axis_linear(1), EPI_RESID, o32),
-                  tile);
-      TXL_TRY(after_launch(timed(K_FFN2_GEMM, stream, [&] { return launch_gemm(g, dt, stream); }), "FFN2 GEMM",
-                           stream));
-    }
+    // h' = LN(o + ReLU(o W_ff1^T) W_ff2^T)
+    TXL_TRY(split_gemm(hid, ly.W_ff2, d_inner, K_FFN2_GEMM, "FFN2 GEMM", &S));
     float* y32 = f32_buf[pp ^ 1];
     void* ylo = last ? h_out : lo_buf[pp ^ 1];
-    TXL_TRY(after_launch(timed(K_LAYERNORM, stream, [&] { return launch_layernorm(t32, y32, ylo, rows, d, dt, 1e-5f, stream); }), "LN2",
+    TXL_TRY(after_launch(timed(K_LAYERNORM, stream, [&] { return launch_layernorm(o32, parts, S, pstride, y32, ylo, rows, d, dt, 1e-5f, stream); }), "LN2",
                          stream));
     x_lo = ylo;
     x32 = y32;

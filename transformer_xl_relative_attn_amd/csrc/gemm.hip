@@ -24,15 +24,28 @@ namespace txl {
 
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 32, NT = 256;
+constexpr int BK = 32, NT = 256;
 #ifndef TXL_GEMM_NSTAGE
 #define TXL_GEMM_NSTAGE 3
 #endif
-constexpr int NSTAGE = TXL_GEMM_NSTAGE;  // LDS ring depth: loads run NSTAGE-1 K-steps ahead
 constexpr int CH = BK / 8;               // 16-byte chunks per tile row (4)
-constexpr int TILE_U = BM * CH;          // 16-byte units per operand tile (1024)
-constexpr int STAGE_U = 2 * TILE_U;      // A tile then B tile
-constexpr int LOADS = TILE_U / NT;       // LDS-DMA loads per thread per operand (4)
+
+// Block-tile variants: WT x WT MFMA tiles of 32x32 per wave, 2x2 waves.
+//   WT = 4: 256x256 block, one workgroup per CU (large problems);
+//   WT = 2: 128x128 block, two workgroups per CU (problems with fewer
+//           256-tiles than compute units).
+template <int WT>
+struct Tile {
+  static constexpr int BM = 64 * WT;            // block tile rows = columns
+  static constexpr int WTILE = 32 * WT;         // wave tile
+  static constexpr int TILE_U = BM * CH;        // 16-byte units per operand tile
+  static constexpr int STAGE_U = 2 * TILE_U;    // A tile then B tile
+  static constexpr int LOADS = TILE_U / NT;     // LDS-DMA loads per thread per operand
+  static constexpr int NSTAGE = WT == 4 ? TXL_GEMM_NSTAGE : 4;   // LDS ring depth
+  static constexpr int CPR = 4 * WT;            // 16-byte chunks per staged output row
+  static constexpr int EPI_U = 32 * CPR;        // 16-byte units of a wave's staging region
+  static constexpr int WAVES_PER_SIMD = WT == 4 ? 1 : 2;
+};
 
 // 128 bytes of zeros: the source of every "zero row" chunk (padding rows).
 __device__ __align__(16) uint32_t g_zero_chunk[32];
@@ -46,20 +59,13 @@ __device__ __forceinline__ int find_problem(const GemmGroup& g, int32_t tile, in
   return idx;
 }
 
-// Wait until at most n LDS-DMA loads of this wave are still in flight.  The
+// Wait until at most N LDS-DMA loads of this wave are still in flight.  The
 // loads are not fenced by the compiler (a __syncthreads would wait for all of
 // them), so the waits are explicit.
-__device__ __forceinline__ void wait_vm(int n) {
-  if (n >= 32)
-    asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
-  else if (n >= 24)
-    asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
-  else if (n >= 16)
-    asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-  else if (n >= 8)
-    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-  else
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
 // Workgroup barrier after this wave's LDS reads have completed, without
@@ -74,26 +80,26 @@ __device__ __forceinline__ void barrier_lds() {
 
 // Vectorised epilogue: four consecutive output columns per store.  FLAGS < 0
 // means "read the residual / ReLU flags at run time".
-template <int DTYPE, int FLAGS>
-__device__ __forceinline__ void epilogue_vec(const OutDst& o, const floatx16 (&acc)[4][4],
+template <int WT, int DTYPE, int FLAGS>
+__device__ __forceinline__ void epilogue_vec(const OutDst& o, const floatx16 (&acc)[WT][WT],
                                              int32_t mb, int32_t nb) {
   const int flags = FLAGS < 0 ? o.flags : FLAGS;
-  int64_t roff[4];
-  bool mok[4];
+  int64_t roff[WT];
+  bool mok[WT];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < WT; ++i) {
     mok[i] = mb + 32 * i < o.m_valid;
     roff[i] = axis_off(o.row, mb + 32 * i);
   }
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+  for (int j = 0; j < WT; ++j)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int32_t n = nb + 32 * j + 8 * g;
       if (n >= o.n_valid) continue;
       const int64_t coff = col_off(o, n);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < WT; ++i) {
         if (!mok[i]) continue;
         const int64_t off = roff[i] + coff;
         floatx4 v = floatx4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
@@ -117,42 +123,44 @@ __device__ __forceinline__ void epilogue_vec(const OutDst& o, const floatx16 (&a
     }
 }
 
-// bf16 output without residual / activation: the wave's 128x128 sub-tile
-// (rows mw.., columns nw..) passes through the wave's own 8 KB LDS region in
-// four rounds of 32 rows, so that the global stores write whole lines (16
-// lanes cover 256 contiguous bytes of one row) instead of 16-byte pieces of
-// 32 rows, which the L2 would receive as 32 partial-line writes per
-// instruction.  The region is separate from the operand ring, so the next
-// tile's first K steps can already be landing.  Staging layout: row r (0..31)
-// is 16 chunks of 16 bytes, chunk c at slot c ^ (r & 15); both the 8-byte
-// writes (32 rows x 2 halves) and the 16-byte reads (16 lanes per row) are
-// then spread over all 64 banks.
-constexpr int EPI_U = 32 * 16;   // 16-byte units of a wave's staging region (8 KB)
-
-__device__ __forceinline__ void epilogue_staged(const OutDst& o, const floatx16 (&acc)[4][4],
+// bf16 output without residual / activation: the wave's WTILE x WTILE
+// sub-tile (rows mw.., columns nw..) passes through the wave's own LDS region
+// in rounds of 32 rows, so that the global stores write whole lines (CPR
+// lanes cover one output row of the sub-tile contiguously) instead of
+// 16-byte pieces of 32 rows, which the L2 would receive as 32 partial-line
+// writes per instruction.  The region is separate from the operand ring, so
+// the next tile's first K steps can already be landing.  Staging layout: row
+// r (0..31) is CPR chunks of 16 bytes, chunk c at slot c ^ (r % CPR); both the
+// 8-byte writes (32 rows x 2 halves) and the 16-byte reads (CPR lanes per row)
+// are then spread over all 64 banks.
+template <int WT>
+__device__ __forceinline__ void epilogue_staged(const OutDst& o, const floatx16 (&acc)[WT][WT],
                                                 int32_t mw, int32_t nw, int lane,
                                                 u32x4* region) {
   typedef float floatx2_t __attribute__((ext_vector_type(2)));
   typedef bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  constexpr int CPR = Tile<WT>::CPR;     // chunks (lanes) per row
+  constexpr int RG = 64 / CPR;           // rows per store instruction
+  constexpr int NR = 32 / RG;            // store instructions per round
   char* base = reinterpret_cast<char*>(region);
   const int lrow = lane & 31, lhalf = lane >> 5;
-  // lane -> chunk c = lane % 16 (columns nw + 8c .. +7) of rows 4t + lane/16
-  const int c = lane & 15, rsub = lane >> 4;
+  // lane -> chunk c (columns nw + 8c .. +7) of rows RG*t + rsub
+  const int c = lane % CPR, rsub = lane / CPR;
   const int32_t n = nw + 8 * c;
   const bool nok = n < o.n_valid;
   const int64_t coff = col_off(o, n);
-  // row offsets advance incrementally: +4 rows per step, at most one wrap of
-  // the row axis (div >= 4)
+  // row offsets advance incrementally: +RG rows per step, at most one wrap of
+  // the row axis (div >= 8)
   int32_t m = mw + rsub;
   const int32_t q0 = axis_quot(o.row, m);
   int32_t rem = m - q0 * o.row.div;
   int64_t off = (int64_t)q0 * o.row.s1 + (int64_t)rem * o.row.s2 + coff;
-  const int64_t step = 4 * o.row.s2, wrap = o.row.s1 - (int64_t)o.row.div * o.row.s2;
+  const int64_t step = RG * o.row.s2, wrap = o.row.s1 - (int64_t)o.row.div * o.row.s2;
   uint16_t* out = static_cast<uint16_t*>(o.p);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < WT; ++i) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < WT; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int cc = 4 * j + q;   // columns 32j + 8q + 4*lhalf .. +3
@@ -160,22 +168,23 @@ __device__ __forceinline__ void epilogue_staged(const OutDst& o, const floatx16 
             __builtin_convertvector(floatx2_t{acc[i][j][4 * q], acc[i][j][4 * q + 1]}, bf16x2_t);
         const bf16x2_t hi =
             __builtin_convertvector(floatx2_t{acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]}, bf16x2_t);
-        *reinterpret_cast<u32x2*>(base + lrow * 256 + ((cc ^ (lrow & 15)) << 4) + 8 * lhalf) =
+        *reinterpret_cast<u32x2*>(base + lrow * (CPR * 16) + ((cc ^ (lrow % CPR)) << 4) +
+                                  8 * lhalf) =
             u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
       }
     wave_lds_fence();
-    u32x4 v[8];
+    u32x4 v[NR];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const int r = 4 * t + rsub;
-      v[t] = *reinterpret_cast<const u32x4*>(base + r * 256 + ((c ^ (r & 15)) << 4));
+    for (int t = 0; t < NR; ++t) {
+      const int r = RG * t + rsub;
+      v[t] = *reinterpret_cast<const u32x4*>(base + r * (CPR * 16) + ((c ^ (r % CPR)) << 4));
     }
     wave_lds_fence();   // the next round rewrites the region
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
+    for (int t = 0; t < NR; ++t) {
       if (nok && m < o.m_valid) *reinterpret_cast<u32x4*>(out + off) = v[t];
-      m += 4;
-      rem += 4;
+      m += RG;
+      rem += RG;
       off += step;
       if (rem >= o.row.div) {
         rem -= o.row.div;
@@ -189,56 +198,64 @@ __device__ __forceinline__ void epilogue_staged(const OutDst& o, const floatx16 
 // swapped (B fragment first), so block (i, j) holds C^T: element 4g + r of a
 // lane is C[m][n] with m = mb + 32i and n = nb + 32j + 8g + r, i.e. four
 // consecutive output columns of one row per (i, j, g).
-__device__ __forceinline__ void epilogue(const GemmProblem& P, const floatx16 (&acc)[4][4],
+template <int WT>
+__device__ __forceinline__ void epilogue(const GemmProblem& P, const floatx16 (&acc)[WT][WT],
                                          int32_t m0, int32_t n0, int wm, int wn, int lane,
                                          u32x4* smem) {
+  constexpr int WTILE = Tile<WT>::WTILE, EPI_U = Tile<WT>::EPI_U;
   const int lrow = lane & 31, lhalf = lane >> 5, wave = wm * 2 + wn;
   const OutDst& o = P.out;
-  const int32_t mb = m0 + wm * 128 + lrow;
-  const int32_t nb = n0 + wn * 128 + 4 * lhalf;
+  const int32_t mb = m0 + wm * WTILE + lrow;
+  const int32_t nb = n0 + wn * WTILE + 4 * lhalf;
   if (o.vec8_ok && o.flags == 0) {
-    epilogue_staged(o, acc, m0 + wm * 128, n0 + wn * 128, lane, smem + wave * EPI_U);
+    epilogue_staged<WT>(o, acc, m0 + wm * WTILE, n0 + wn * WTILE, lane, smem + wave * EPI_U);
     return;
   }
   if (o.vec_ok) {
     if (o.flags == 0 && o.dtype == TXL_BF16)
-      epilogue_vec<TXL_BF16, 0>(o, acc, mb, nb);
+      epilogue_vec<WT, TXL_BF16, 0>(o, acc, mb, nb);
     else if (o.flags == 0)
-      epilogue_vec<TXL_F32, 0>(o, acc, mb, nb);
+      epilogue_vec<WT, TXL_F32, 0>(o, acc, mb, nb);
     else if (o.dtype == TXL_BF16)
-      epilogue_vec<TXL_BF16, -1>(o, acc, mb, nb);
+      epilogue_vec<WT, TXL_BF16, -1>(o, acc, mb, nb);
     else
-      epilogue_vec<TXL_F32, -1>(o, acc, mb, nb);
+      epilogue_vec<WT, TXL_F32, -1>(o, acc, mb, nb);
     return;
   }
   // Rare layouts (unaligned or odd leading dimension): one element at a time
-  // through an LDS transpose in the wave's staging region, so that the
-  // accumulators are only indexed statically.
+  // through an LDS transpose in the wave's staging region (a 32 x 32 float
+  // block, row ml rotated by ml to spread the column accesses over the banks),
+  // so that the accumulators are only indexed statically.
+  static_assert(32 * 32 * 4 <= EPI_U * 16, "transpose block fits the staging region");
   float* stage = reinterpret_cast<float*>(smem + wave * EPI_U);
-  for (int i = 0; i < 4; ++i) {
+  auto at = [](int ml, int nl) { return ml * 32 + ((nl + ml) & 31); };
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      // only i is dynamic here; acc[i] is selected with a switch to keep it static
-      floatx16 a = i == 0 ? acc[0][j] : i == 1 ? acc[1][j] : i == 2 ? acc[2][j] : acc[3][j];
+  for (int i = 0; i < WT; ++i) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) stage[lrow * 33 + 8 * (e >> 2) + 4 * lhalf + (e & 3)] = a[e];
+    for (int j = 0; j < WT; ++j) {
+      const floatx16 a = acc[i][j];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) stage[at(lrow, 8 * (e >> 2) + 4 * lhalf + (e & 3))] = a[e];
       wave_lds_fence();
       // stage[m_local][n_local] for m = mb - lrow + m_local, n = nb - 4*lhalf + 32j + n_local
       for (int t = lane; t < 32 * 32; t += 64) {
         const int ml = t >> 5, nl = t & 31;
-        const int32_t m = m0 + wm * 128 + 32 * i + ml;
-        const int32_t n = n0 + wn * 128 + 32 * j + nl;
+        const int32_t m = m0 + wm * WTILE + 32 * i + ml;
+        const int32_t n = n0 + wn * WTILE + 32 * j + nl;
         if (m < o.m_valid && n < o.n_valid)
-          epi_store(o, axis_off(o.row, m) + col_off(o, n), stage[ml * 33 + nl]);
+          epi_store(o, axis_off(o.row, m) + col_off(o, n), stage[at(ml, nl)]);
       }
       wave_lds_fence();
     }
   }
 }
 
-__global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(GemmGroup g, int32_t padded,
-                                                          int32_t grid) {
-  // LDS ring: stage s holds A rows [0,256) then B rows [0,256), each row 4
+template <int WT>
+__device__ __forceinline__ void gemm_bf16_body(const GemmGroup& g, int32_t padded, int32_t grid) {
+  using T = Tile<WT>;
+  constexpr int BM = T::BM, BN = T::BM, WTILE = T::WTILE, TILE_U = T::TILE_U,
+                STAGE_U = T::STAGE_U, LOADS = T::LOADS, NSTAGE = T::NSTAGE, EPI_U = T::EPI_U;
+  // LDS ring: stage s holds A rows [0,BM) then B rows [0,BN), each row 4
   // chunks of 16 bytes; chunk c of row r is stored at slot c ^ ((r >> 2) & 3).
   // gfx950 serves a 16-byte read for 16 lanes at a time from 64 four-byte
   // banks, so rows r, r+4, r+8, r+12 (same bank group at a 64-byte pitch) must
@@ -298,7 +315,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(GemmGroup g, int32_t p
     }
   };
 
-  // LDS-DMA q (0..7: operand q & 1, row group q >> 1) of the next K step
+  // LDS-DMA q (0..2*LOADS-1: operand q & 1, row group q >> 1) of the next K step
   // into a ring stage; the running pointer advances by one K step.  With
   // `real` false (past the end of K) the zero chunk is loaded instead, into a
   // slot that is never read again: the loop body stays the same in every
@@ -317,63 +334,68 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(GemmGroup g, int32_t p
 
   const int lrow = lane & 31, lhalf = lane >> 5;
   const int sw = (lrow >> 2) & 3;  // same for every fragment row of a lane
-  int fa[4], fb[4];                // fragment row base (16-byte units) within a stage
+  int fa[WT], fb[WT];              // fragment row base (16-byte units) within a stage
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    fa[i] = (wm * 128 + i * 32 + lrow) * CH;
-    fb[i] = TILE_U + (wn * 128 + i * 32 + lrow) * CH;
+  for (int i = 0; i < WT; ++i) {
+    fa[i] = (wm * WTILE + i * 32 + lrow) * CH;
+    fb[i] = TILE_U + (wn * WTILE + i * 32 + lrow) * CH;
   }
-  // fragment f (0..3: A rows 32f.., 4..7: B rows 32(f-4)..) of k-step s (0 or
-  // 1) of a staged 32-wide K step
+  // fragment f (0..WT-1: A rows 32f.., WT..2WT-1: B rows 32(f-WT)..) of k-step
+  // s (0 or 1) of a staged 32-wide K step
   auto read_one = [&](const u32x4* st, int s, int f, bf16x8* af, bf16x8* bfr) {
     const int c = (2 * s + lhalf) ^ sw;
-    if (f < 4)
+    if (f < WT)
       af[f] = __builtin_bit_cast(bf16x8, st[fa[f] + c]);
     else
-      bfr[f - 4] = __builtin_bit_cast(bf16x8, st[fb[f - 4] + c]);
+      bfr[f - WT] = __builtin_bit_cast(bf16x8, st[fb[f - WT] + c]);
   };
-  floatx16 acc[4][4];
+  floatx16 acc[WT][WT];
   auto mfma_one = [&](int x, const bf16x8* af, const bf16x8* bfr) {
-    const int i = x >> 2, j = x & 3;
+    const int i = x / WT, j = x % WT;
     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
   };
 
   // One K step (ring slot `slot`, 32 wide = two MFMA k-steps), in two halves
   // whose instruction order is fixed with scheduling fences:
-  //   A: 16 MFMAs on k-step 0 (fragments F0, already in registers); the
-  //      k-step 1 fragments F1 are read during the first 8;
+  //   A: WT*WT MFMAs on k-step 0 (fragments F0, already in registers); the
+  //      k-step 1 fragments F1 are read during the first 2*WT;
   //   wait until K step kt+1 has landed (`vm` loads may stay in flight),
   //   barrier: every wave is done with this slot;
-  //   B: 16 MFMAs on F1, each pair followed by one refill load of this slot
-  //      (K step kt+NSTAGE; zero chunk if that is past the end), the first
-  //      four pairs also by two reads of K step kt+1's F0.
+  //   B: WT*WT MFMAs on F1, interleaved with the 2*LOADS refill loads of this
+  //      slot (K step kt+NSTAGE; zero chunk if that is past the end) and, in
+  //      the first half of them, the reads of K step kt+1's F0.
   // Spreading the loads and reads evenly keeps the single wave per SIMD
   // issuing MFMAs back to back.  (In the last step the F0 read is of a stale
   // slot and unused.)
-  bf16x8 f0a[4], f0b[4], f1a[4], f1b[4];
+  bf16x8 f0a[WT], f0b[WT], f1a[WT], f1b[WT];
+  constexpr int NQ = 2 * LOADS;           // refill loads per wave and K step
+  constexpr int MPQ = WT * WT / NQ;       // MFMAs per refill load
+  static_assert(MPQ * NQ == WT * WT, "MFMAs split evenly between the loads");
   auto kstep = [&](int slot, int nslot, bool refill) {
     const u32x4* st = stage_ptr(slot);
 #pragma unroll
-    for (int x = 0; x < 16; ++x) {
+    for (int x = 0; x < WT * WT; ++x) {
       mfma_one(x, f0a, f0b);
-      if (x < 8) read_one(st, 1, x, f1a, f1b);
+      if (x < 2 * WT) read_one(st, 1, x, f1a, f1b);
       __builtin_amdgcn_sched_barrier(0);
     }
-    wait_vm((NSTAGE - 2) * 2 * LOADS);
+    wait_vm<(NSTAGE - 2) * 2 * LOADS>();
     barrier_lds();
     u32x4* rs = smem + slot * STAGE_U + wave_s * 64;
     const u32x4* nst = stage_ptr(nslot);
-    // F0 reads in the order the next MFMAs consume them, all in the first
-    // half so that they have landed when the next step starts
-    constexpr int order[8] = {0, 4, 5, 6, 7, 1, 2, 3};
+    // F0 reads in the order the next MFMAs consume them (A0, B0..B(WT-1),
+    // A1..A(WT-1)), all in the first half so that they have landed when the
+    // next step starts
+    constexpr int RPQ = (2 * WT + NQ / 2 - 1) / (NQ / 2);   // reads per load
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      mfma_one(2 * q, f1a, f1b);
-      mfma_one(2 * q + 1, f1a, f1b);
+    for (int q = 0; q < NQ; ++q) {
+#pragma unroll
+      for (int x = 0; x < MPQ; ++x) mfma_one(MPQ * q + x, f1a, f1b);
       issue_one(rs, q, refill);
-      if (q < 4) {
-        read_one(nst, 0, order[2 * q], f0a, f0b);
-        read_one(nst, 0, order[2 * q + 1], f0a, f0b);
+#pragma unroll
+      for (int r = 0; r < RPQ; ++r) {
+        const int k = RPQ * q + r;   // k-th fragment in consumption order
+        if (k < 2 * WT) read_one(nst, 0, k == 0 ? 0 : k <= WT ? WT + k - 1 : k - WT, f0a, f0b);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -385,7 +407,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(GemmGroup g, int32_t p
     for (int s = 0; s < NSTAGE; ++s) {
       u32x4* rs = smem + s * STAGE_U + wave_s * 64;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) issue_one(rs, q, s < nk);
+      for (int q = 0; q < 2 * LOADS; ++q) issue_one(rs, q, s < nk);
     }
   };
 
@@ -394,21 +416,21 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(GemmGroup g, int32_t p
 
   while (true) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < WT; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = floatx16{0};
+      for (int j = 0; j < WT; ++j) acc[i][j] = floatx16{0};
 
     // Loads return in order and every step issues exactly one stage, so the
     // wait counts are fixed: K step 0 has landed once at most NSTAGE-1 stages
     // issued after it remain, step kt+1 once NSTAGE-2 remain.  Outstanding
     // epilogue stores of the previous tile only make these waits stricter (a
     // pending load keeps every later load pending too).
-    wait_vm((NSTAGE - 1) * 2 * LOADS);
+    wait_vm<(NSTAGE - 1) * 2 * LOADS>();
     barrier_lds();
     {
       const u32x4* st = stage_ptr(0);
 #pragma unroll
-      for (int f = 0; f < 8; ++f) read_one(st, 0, f, f0a, f0b);
+      for (int f = 0; f < 2 * WT; ++f) read_one(st, 0, f, f0a, f0b);
     }
     int slot = 0;
 #pragma unroll 1
@@ -430,11 +452,23 @@ __global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(GemmGroup g, int32_t p
       setup(xcd_swizzle(seq, padded));
       prologue();
     }
-    epilogue(g.p[cpidx], acc, cm0, cn0, wm, wn, lane, stage_out);
+    epilogue<WT>(g.p[cpidx], acc, cm0, cn0, wm, wn, lane, stage_out);
     if (!more) break;
   }
   // no LDS-DMA may still be writing when the workgroup exits
-  wait_vm(0);
+  wait_vm<0>();
+}
+
+// 256x256 blocks, one workgroup per CU
+__global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(GemmGroup g, int32_t padded,
+                                                          int32_t grid) {
+  gemm_bf16_body<4>(g, padded, grid);
+}
+
+// 128x128 blocks, two workgroups per CU
+__global__ __launch_bounds__(NT, 2) void gemm_bf16_t128_kernel(GemmGroup g, int32_t padded,
+                                                               int32_t grid) {
+  gemm_bf16_body<2>(g, padded, grid);
 }
 
 // ------------------------------------------------------------------ fp32 GEMM
@@ -512,15 +546,36 @@ int32_t device_cu_count() {
   return cached[dev];
 }
 
+int launch_tiles(const GemmGroup& g, bool small, void* stream) {
+  const int32_t padded = (g.total_tiles + 7) & ~7;
+  // persistent workgroups, one (256x256) or two (128x128) per compute unit,
+  // a multiple of 8 (the XCD count)
+  int32_t grid = (device_cu_count() * (small ? 2 : 1) + 7) & ~7;
+  if (grid > padded) grid = padded;
+  if (small)
+    hipLaunchKernelGGL(gemm_bf16_t128_kernel, dim3(grid), dim3(NT), 0,
+                       static_cast<hipStream_t>(stream), g, padded, grid);
+  else
+    hipLaunchKernelGGL(gemm_bf16_kernel, dim3(grid), dim3(NT), 0,
+                       static_cast<hipStream_t>(stream), g, padded, grid);
+  return static_cast<int>(hipGetLastError());
+}
+
+// The group arrives tiled for 256x256 blocks.  A group with fewer such tiles
+// than compute units is re-tiled for 128x128 blocks (two workgroups per CU).
 int launch_gemm_bf16(const GemmGroup& g, void* stream) {
   if (g.total_tiles <= 0) return 0;
-  const int32_t padded = (g.total_tiles + 7) & ~7;
-  // one persistent workgroup per compute unit (multiple of 8, the XCD count)
-  int32_t grid = (device_cu_count() + 7) & ~7;
-  if (grid > padded) grid = padded;
-  hipLaunchKernelGGL(gemm_bf16_kernel, dim3(grid), dim3(NT), 0,
-                     static_cast<hipStream_t>(stream), g, padded, grid);
-  return static_cast<int>(hipGetLastError());
+  if (2 * g.total_tiles > device_cu_count()) return launch_tiles(g, false, stream);
+  GemmGroup s = g;
+  s.total_tiles = 0;
+  for (int i = 0; i < s.count; ++i) {
+    GemmProblem& p = s.p[i];
+    p.tiles_m = (p.M + 127) / 128;
+    p.tiles_n = (p.N + 127) / 128;
+    p.tile_begin = s.total_tiles;
+    s.total_tiles += p.tiles_m * p.tiles_n;
+  }
+  return launch_tiles(s, true, stream);
 }
 
 int launch_gemm_f32(const GemmGroup& g, void* stream) {

@@ -60,40 +60,81 @@ __global__ void pack_rows_kernel(uint16_t* dst, int64_t ld_dst, const uint16_t* 
   dst[idx] = c < cols ? src[r * ld_src + c] : uint16_t(0);
 }
 
-// LayerNorm over rows of length d (no affine parameters), one workgroup per
-// row, fp32 statistics; writes fp32 and, if y_lo is set, a copy in lo_dtype.
-__global__ __launch_bounds__(256) void layernorm_kernel(const float* x, float* y, void* y_lo,
-                                                        int32_t d, int32_t lo_dtype, float eps) {
+// Sum over the 256 threads of a workgroup (fixed order: deterministic).
+__device__ __forceinline__ float block_sum256(float v, float* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  __syncthreads();   // red may still be read from the previous sum
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+// LayerNorm (no affine parameters, fp32 statistics) of x = resid + sum of
+// n_parts split-K partial products (each [rows][d], part_stride floats apart),
+// one workgroup per row.  Writes fp32 y and, if y_lo is set, a copy in
+// lo_dtype.  VPT > 0 keeps the row in registers (d <= 256 * VPT); VPT == 0
+// uses y as the staging buffer (y must not overlap the inputs).
+template <int VPT>
+__global__ __launch_bounds__(256) void layernorm_kernel(const float* resid, const float* parts,
+                                                        int32_t n_parts, int64_t part_stride,
+                                                        float* y, void* y_lo, int32_t d,
+                                                        int32_t lo_dtype, float eps) {
+  __shared__ float red[4];
   const int64_t row = blockIdx.x;
-  const float* xr = x + row * d;
-  __shared__ float red[2][256];
-  float s = 0.0f, s2 = 0.0f;
-  for (int c = threadIdx.x; c < d; c += 256) {
-    float v = xr[c];
-    s += v;
-  }
-  red[0][threadIdx.x] = s;
-  __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if (threadIdx.x < w) red[0][threadIdx.x] += red[0][threadIdx.x + w];
-    __syncthreads();
-  }
-  const float mean = red[0][0] / d;
-  for (int c = threadIdx.x; c < d; c += 256) {
-    float v = xr[c] - mean;
-    s2 += v * v;
-  }
-  red[1][threadIdx.x] = s2;
-  __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if (threadIdx.x < w) red[1][threadIdx.x] += red[1][threadIdx.x + w];
-    __syncthreads();
-  }
-  const float rstd = rsqrtf(red[1][0] / d + eps);
-  for (int c = threadIdx.x; c < d; c += 256) {
-    const float v = (xr[c] - mean) * rstd;
-    y[row * d + c] = v;
-    if (y_lo) store_from_f32(y_lo, row * d + c, v, lo_dtype);
+  const int tid = threadIdx.x;
+  auto load_x = [&](int c) {
+    float v = resid[row * d + c];
+    for (int s = 0; s < n_parts; ++s) v += parts[s * part_stride + row * d + c];
+    return v;
+  };
+  if constexpr (VPT > 0) {
+    float x[VPT];
+    float s = 0.0f;
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      const int c = tid + 256 * k;
+      x[k] = c < d ? load_x(c) : 0.0f;
+      s += x[k];
+    }
+    const float mean = block_sum256(s, red) / d;
+    float s2 = 0.0f;
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      const int c = tid + 256 * k;
+      const float dv = c < d ? x[k] - mean : 0.0f;
+      s2 += dv * dv;
+    }
+    const float rstd = rsqrtf(block_sum256(s2, red) / d + eps);
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      const int c = tid + 256 * k;
+      if (c < d) {
+        const float v = (x[k] - mean) * rstd;
+        y[row * d + c] = v;
+        if (y_lo) store_from_f32(y_lo, row * d + c, v, lo_dtype);
+      }
+    }
+  } else {
+    float* yr = y + row * d;
+    float s = 0.0f;
+    for (int c = tid; c < d; c += 256) {
+      const float v = load_x(c);
+      yr[c] = v;
+      s += v;
+    }
+    const float mean = block_sum256(s, red) / d;
+    float s2 = 0.0f;
+    for (int c = tid; c < d; c += 256) {
+      const float dv = yr[c] - mean;
+      s2 += dv * dv;
+    }
+    const float rstd = rsqrtf(block_sum256(s2, red) / d + eps);
+    for (int c = tid; c < d; c += 256) {
+      const float v = (yr[c] - mean) * rstd;
+      yr[c] = v;
+      if (y_lo) store_from_f32(y_lo, row * d + c, v, lo_dtype);
+    }
   }
 }
 
@@ -155,10 +196,19 @@ int launch_pack_rows(void* dst, int64_t ld_dst, const void* src, int64_t ld_src,
   return static_cast<int>(hipGetLastError());
 }
 
-int launch_layernorm(const float* x, float* y_f32, void* y_lo, int32_t rows, int32_t d,
-                     int32_t lo_dtype, float eps, void* stream) {
-  hipLaunchKernelGGL(layernorm_kernel, dim3(rows), dim3(256), 0, static_cast<hipStream_t>(stream),
-                     x, y_f32, y_lo, d, lo_dtype, eps);
+int launch_layernorm(const float* resid, const float* parts, int32_t n_parts, int64_t part_stride,
+                     float* y_f32, void* y_lo, int32_t rows, int32_t d, int32_t lo_dtype, float eps,
+                     void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (d <= 1024)
+    hipLaunchKernelGGL(layernorm_kernel<4>, dim3(rows), dim3(256), 0, st, resid, parts, n_parts,
+                       part_stride, y_f32, y_lo, d, lo_dtype, eps);
+  else if (d <= 4096)
+    hipLaunchKernelGGL(layernorm_kernel<16>, dim3(rows), dim3(256), 0, st, resid, parts, n_parts,
+                       part_stride, y_f32, y_lo, d, lo_dtype, eps);
+  else
+    hipLaunchKernelGGL(layernorm_kernel<0>, dim3(rows), dim3(256), 0, st, resid, parts, n_parts,
+                       part_stride, y_f32, y_lo, d, lo_dtype, eps);
   return static_cast<int>(hipGetLastError());
 }
 

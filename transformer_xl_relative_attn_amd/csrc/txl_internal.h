@@ -176,6 +176,9 @@ struct AttnArgs {
   int64_t upd_row_bytes;
 };
 
+// Compute units of the current device (cached per device id).
+int32_t device_cu_count();
+
 // Launch wrappers (return a hipError_t as int).
 int launch_gemm_bf16(const GemmGroup& g, void* stream);
 int launch_gemm_f32(const GemmGroup& g, void* stream);
@@ -187,8 +190,9 @@ int launch_mem_update(void* mem, int32_t start, const void* h, int32_t B, int32_
                       int32_t d, int32_t dtype, void* stream);
 int launch_pack_rows(void* dst, int64_t ld_dst, const void* src, int64_t ld_src, int64_t rows,
                      int32_t cols, int32_t dtype, void* stream);
-int launch_layernorm(const float* x, float* y_f32, void* y_lo, int32_t rows, int32_t d,
-                     int32_t lo_dtype, float eps, void* stream);
+int launch_layernorm(const float* resid, const float* parts, int32_t n_parts, int64_t part_stride,
+                     float* y_f32, void* y_lo, int32_t rows, int32_t d, int32_t lo_dtype, float eps,
+                     void* stream);
 int launch_cast_f32(const void* src, float* dst, int64_t n, int32_t dtype, void* stream);
 int launch_repack_rk(const void* rk_pub, void* rk_ws, int32_t P, int32_t Pp, int32_t pad, int32_t H,
                      int32_t dh, int32_t dp, int32_t dtype, void* stream);
