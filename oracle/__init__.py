@@ -5,3 +5,4 @@ benchmark's CPU-baseline leg, never by the library or its Python binding.
 """
 from .oracle import *  # noqa: F401,F403
 from . import brute  # noqa: F401
+from . import backward  # noqa: F401
