@@ -133,6 +133,39 @@ txl_status_t txl_rel_attn_fwd(const txl_attn_shape_t* shape, const void* h, cons
                               size_t workspace_bytes, void* stream);
 
 /*
+ * Backward of txl_rel_attn_fwd (bf16 inputs; fp32 gradients).  Gradients flow
+ * within the segment only: Sec. 3.2 puts a stop-gradient on the cached
+ * memory, so nothing is returned for `mem`, while the keys and values computed
+ * from it are ordinary tensors and receive gradients.  With s_ij = scale *
+ * A_ij (Sec. 3.3 summary equations), P = Masked-Softmax(s), out = P val and
+ * G = d_out:
+ *   d_val_j  = sum_i P_ij G_i
+ *   dS_ij    = P_ij (G_i . val_j - G_i . out_i)
+ *   d_q_i    = scale sum_j dS_ij (k_j + Rk[M+i-j])        terms (a), (b)
+ *   d_k_j    = scale sum_i dS_ij (q_i + u)                terms (a), (c)
+ *   d_u      = scale sum_{b,i,j} dS_ij k_j                term (c)
+ *   d_v      = scale sum_{b,i,j} dS_ij Rk[M+i-j]          term (d)
+ *   d_Rk[delta] = scale sum over pairs with M+i-j = delta of dS_ij (q_i + v)
+ *   d_W_kR   = sum_delta d_Rk[delta] (x) R_delta          (optional)
+ * Inputs as txl_rel_attn_fwd (the forward is recomputed inside), plus d_out
+ * [B][L][H][d_head] bf16.  Outputs (device, fp32, overwritten):
+ *   d_q [B][L][H][d_head]; d_k, d_val [B][M+L][H][d_head] (memory rows first);
+ *   d_u, d_v [H][d_head]; d_Rk [M+L][H][d_head]; d_W_kR [H*d_head][d_pos] or
+ *   NULL (only allowed when Rk is NULL, i.e. computed from W_kR and R).
+ * Workspace: txl_rel_attn_bwd_workspace_bytes() (0 for unsupported shapes).
+ * Errors: fp32 (TXL_ERR_UNSUPPORTED); the errors of txl_rel_attn_fwd; NULL
+ * gradient pointers; d_W_kR with a caller Rk (TXL_ERR_BAD_SHAPE).
+ */
+size_t txl_rel_attn_bwd_workspace_bytes(const txl_attn_shape_t* shape);
+txl_status_t txl_rel_attn_bwd(const txl_attn_shape_t* shape, const void* h, const void* mem,
+                              int32_t mem_start, const void* W_q, const void* W_kE,
+                              const void* W_kR, const void* W_v, const void* u, const void* v,
+                              const void* R, const void* Rk, const void* d_out, float* d_q,
+                              float* d_k, float* d_val, float* d_u, float* d_v, float* d_Rk,
+                              float* d_W_kR, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/*
  * Carried projected-K/V memory for evaluation (bf16 only, seg_len % 32 == 0).
  * Sec. 3.2 extends each segment with the cached hidden states,
  * h~ = [SG(m) ; h], and Sec. 3.3 projects k = h~ W_kE^T, val = h~ W_v^T row by

@@ -201,3 +201,31 @@ def test_kv_ring_queries_and_validation(txl):
     assert init(s, ws=None) == 1
     assert init(_shape(txl, seg_len=32, mem_len=40, dtype=txl.TXL_F32)) == 5
     assert st.value == 96
+
+
+def test_rel_attn_bwd_validation(txl):
+    s = _shape(txl)
+    wsb = txl.txl_rel_attn_bwd_workspace_bytes(s)
+    assert wsb > txl.txl_rel_attn_workspace_bytes(s)
+    assert txl.txl_rel_attn_bwd_workspace_bytes(_shape(txl, dtype=txl.TXL_F32)) == 0
+    f = txl.lib.txl_rel_attn_bwd
+
+    def bwd(shape, ws_bytes=wsb, **kw):
+        p = dict(h=16, mem=32, mem_start=0, W_q=48, W_kE=64, W_kR=80, W_v=96, u=112, v=128,
+                 R=144, Rk=None, d_out=160, d_q=176, d_k=192, d_val=208, d_u=224, d_v=240,
+                 d_Rk=256, d_W_kR=None, ws=272)
+        p.update(kw)
+        return f(ctypes.byref(shape), p["h"], p["mem"], p["mem_start"], p["W_q"], p["W_kE"],
+                 p["W_kR"], p["W_v"], p["u"], p["v"], p["R"], p["Rk"], p["d_out"], p["d_q"],
+                 p["d_k"], p["d_val"], p["d_u"], p["d_v"], p["d_Rk"], p["d_W_kR"], p["ws"],
+                 ws_bytes, None)
+
+    assert bwd(_shape(txl, dtype=txl.TXL_F32)) == 5
+    assert bwd(s, d_out=None) == 1
+    assert bwd(s, d_q=None) == 1
+    assert bwd(s, d_Rk=None) == 1
+    assert bwd(s, mem=None) == 1
+    assert bwd(s, mem_start=16) == 2
+    assert bwd(s, Rk=288, d_W_kR=304) == 2          # no W_kR gradient with a caller Rk
+    assert bwd(s, ws_bytes=wsb - 1) == 4
+    assert bwd(s, ws=None) == 1

@@ -21,6 +21,7 @@ __all__ = [
     "txl_rel_attn_fwd", "txl_mem_update", "txl_segment_workspace_bytes", "txl_segment_step",
     "txl_kv_ring_slots", "txl_kv_ring_bytes", "txl_kv_ring_workspace_bytes", "txl_kv_ring_init",
     "txl_rel_attn_fwd_kv", "txl_segment_kv_workspace_bytes", "txl_segment_step_kv",
+    "txl_rel_attn_bwd_workspace_bytes", "txl_rel_attn_bwd",
     "txl_timing_enable", "txl_timing_reset", "txl_timing_read",
 ]
 
@@ -90,6 +91,11 @@ _seg_kv_ws = _sig("txl_segment_kv_workspace_bytes", _sz, [ctypes.POINTER(AttnSha
 _seg_kv = _sig("txl_segment_step_kv", ctypes.c_int,
                [ctypes.POINTER(AttnShape), _i32, _i32, ctypes.POINTER(Layer),
                 ctypes.POINTER(_vp), _sz, _vp, _vp, _vp, ctypes.POINTER(_i32), _vp, _sz, _vp])
+
+_bwd_ws = _sig("txl_rel_attn_bwd_workspace_bytes", _sz, [ctypes.POINTER(AttnShape)])
+_bwd = _sig("txl_rel_attn_bwd", ctypes.c_int,
+            [ctypes.POINTER(AttnShape), _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+             _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp])
 
 _t_enable = _sig("txl_timing_enable", ctypes.c_int, [_i32])
 _t_reset = _sig("txl_timing_reset", None, [])
@@ -243,6 +249,19 @@ def txl_segment_step_kv(shape: AttnShape, n_layers: int, d_inner: int, layers: S
                    _ptr(h_in), _ptr(h_out), ctypes.byref(st), _ptr(workspace),
                    _nbytes(workspace), _stream(stream)), "txl_segment_step_kv")
     return st.value
+
+
+def txl_rel_attn_bwd_workspace_bytes(shape: AttnShape) -> int:
+    return _bwd_ws(ctypes.byref(shape))
+
+
+def txl_rel_attn_bwd(shape: AttnShape, h, mem, mem_start: int, W_q, W_kE, W_kR, W_v, u, v, R, Rk,
+                     d_out, d_q, d_k, d_val, d_u, d_v, d_Rk, d_W_kR, workspace, stream=None):
+    _check(_bwd(ctypes.byref(shape), _ptr(h), _ptr(mem), mem_start, _ptr(W_q), _ptr(W_kE),
+                _ptr(W_kR), _ptr(W_v), _ptr(u), _ptr(v), _ptr(R), _ptr(Rk), _ptr(d_out),
+                _ptr(d_q), _ptr(d_k), _ptr(d_val), _ptr(d_u), _ptr(d_v), _ptr(d_Rk),
+                _ptr(d_W_kR), _ptr(workspace), _nbytes(workspace), _stream(stream)),
+           "txl_rel_attn_bwd")
 
 
 def txl_timing_enable(on: bool):

@@ -78,11 +78,13 @@ txl_status_t after_launch(int err, const char* what, void* stream) {
 // HIP events recorded on the launch stream; txl_timing_read() waits for them.
 enum Kind : int {
   K_PROJ_GEMM, K_ATTN, K_ATTN_COMBINE, K_MEM_UPDATE, K_REL_PROJ, K_WO_GEMM, K_FFN1_GEMM,
-  K_FFN2_GEMM, K_LAYERNORM, K_PACK, K_SINUSOID, K_CAST, K_REPACK_RK, K_NKINDS
+  K_FFN2_GEMM, K_LAYERNORM, K_PACK, K_SINUSOID, K_CAST, K_REPACK_RK, K_BWD_Q, K_BWD_BMM,
+  K_BWD_AUX, K_NKINDS
 };
 const char* const kKindNames[K_NKINDS] = {
     "proj_gemm", "rel_attn", "attn_combine", "mem_update", "rel_proj_gemm", "wo_gemm",
-    "ffn1_gemm", "ffn2_gemm", "layernorm", "pack_rows", "sinusoid", "cast_f32", "repack_rk"};
+    "ffn1_gemm", "ffn2_gemm", "layernorm", "pack_rows", "sinusoid", "cast_f32", "repack_rk",
+    "attn_bwd_q", "bwd_bmm64", "bwd_aux"};
 
 struct TimingState {
   std::mutex mu;
@@ -468,7 +470,7 @@ txl_status_t add_rk(GemmGroup& g, const AttnPlan& p, const AttnPtrs& a, const Op
 // place.  `mem_upd` (optional) is the hidden-state ring to update with h.
 txl_status_t run_attention(const AttnPlan& p, const AttnPtrs& a, char* ws, void* stream,
                            const void* k, const void* vt, int32_t kv_tile0, void* mem_upd,
-                           int32_t* new_start) {
+                           int32_t* new_start, float* lse = nullptr) {
   const bool bf = p.dtype == TXL_BF16;
   const int dt = p.dtype;
   // The ring update rides on the bf16 attention launch (the split combine, or
@@ -512,6 +514,7 @@ txl_status_t run_attention(const AttnPlan& p, const AttnPtrs& a, char* ws, void*
   aa.part_o = p.n_split > 1 ? ws + p.po.off : nullptr;
   aa.part_ml = p.n_split > 1 ? reinterpret_cast<float*>(ws + p.pml.off) : nullptr;
   aa.dtype = dt;
+  aa.lse = lse;
   if (fuse_upd) {
     aa.upd_src = a.h;
     aa.upd_mem = mem_upd;
@@ -620,6 +623,197 @@ txl_status_t run_rel_attn_ring(const AttnPlan& p, const AttnPtrs& a, void* ring,
                        "projection GEMMs", stream));
   const char* kr = static_cast<const char*>(ring);
   return run_attention(p, a, ws, stream, kr, kr + ring_k_bytes(p), start / 32, nullptr, nullptr);
+}
+
+// ------------------------------------------------------------- backward
+// Workspace of the backward: the forward plan's regions (projections, split
+// partials, packing), then the extra operand layouts and the intermediate
+// P^T, dS^T, dS'^T of the key-side products.
+struct BwdPlan {
+  AttnPlan p;
+  Region kt, vn, o, lse, dop, dot, qut, qvt, dsum, pt, dst, dspt, duv, rkt, rt, drkt;
+  int32_t rkt_ld, rkt_pad, dsp_rows;
+  size_t total;
+};
+
+BwdPlan make_bwd_plan(const txl_attn_shape_t* s, bool compute_rk, bool want_wkr) {
+  BwdPlan bp{};
+  bp.p = make_plan(s, compute_rk);
+  const AttnPlan& p = bp.p;
+  size_t off = align256(p.total);
+  auto take = [&](Region& r, size_t bytes) {
+    r.off = off;
+    r.bytes = bytes;
+    off = align256(off + bytes);
+  };
+  const size_t BH = (size_t)p.B * p.H;
+  take(bp.kt, BH * p.Np * p.DP * 2);
+  take(bp.vn, BH * p.Np * p.DP * 2);
+  take(bp.o, (size_t)p.B * p.L * p.H * p.dh * 2);
+  take(bp.lse, BH * p.Lp * 4);
+  take(bp.dop, BH * p.Lp * p.DP * 2);
+  take(bp.dot, BH * p.Lp * p.DP * 2);
+  take(bp.qut, BH * p.Lp * p.DP * 2);
+  take(bp.qvt, BH * p.Lp * p.DP * 2);
+  take(bp.dsum, BH * p.Lp * 4);
+  take(bp.pt, BH * p.Np * p.Lp * 2);
+  take(bp.dst, BH * p.Np * p.Lp * 2);
+  bp.dsp_rows = p.Pp + 32;
+  take(bp.dspt, (size_t)p.H * bp.dsp_rows * p.B * p.Lp * 2);
+  take(bp.duv, 2 * BH * (p.Lp / 32) * p.DP * 4);
+  // Rk^T columns: distance delta at rkt_pad + delta; rkt_pad = 31 - M (mod 8)
+  // keeps every window the kernel reads 16-byte aligned
+  bp.rkt_pad = 64 + (((31 - p.M) % 8) + 8) % 8;
+  bp.rkt_ld = (int32_t)round_up(bp.rkt_pad + p.Pp + 64, 8);
+  take(bp.rkt, (size_t)p.H * p.DP * bp.rkt_ld * 2);
+  if (want_wkr) {
+    take(bp.rt, (size_t)p.dpos * p.P * 4);
+    take(bp.drkt, (size_t)p.H * p.dh * p.P * 4);
+  }
+  bp.total = off;
+  return bp;
+}
+
+struct BwdOut {
+  const void* d_out;
+  float *d_q, *d_k, *d_val, *d_u, *d_v, *d_Rk, *d_W_kR;
+};
+
+txl_status_t run_rel_attn_bwd(const BwdPlan& bp, const AttnPtrs& a, const BwdOut& g, char* ws,
+                              void* stream) {
+  const AttnPlan& p = bp.p;
+  const int dt = p.dtype;
+  const int64_t DP = p.DP;
+  char* k = ws + p.k.off;
+  char* v = ws + p.v.off;
+  Operands o;
+  TXL_TRY(pack_operands(p, a, ws, stream, o));
+  // projections: the forward's q, K, V^T, Rk, plus K^T tiles and V rows
+  const int tile = gemm_tile(dt);
+  GemmGroup gg{};
+  add_q_problem(gg, p, o, ws);
+  const RowSrc ht = src_htilde(o.mem, o.h, o.ld_d, p.Np, p.M, p.L, a.mem_start);
+  add_problem(gg, p.B * p.Np, p.H * p.DP, p.Kd, ht, src_headpad(o.WkE, o.ld_d, p.dh, p.DP),
+              out_map(k, dt, p.B * p.Np, p.H * p.DP, axis(p.Np, (int64_t)p.H * p.Np * DP, DP),
+                      axis(p.DP, (int64_t)p.Np * DP, 1)),
+              tile);
+  add_problem(gg, p.H * p.DP, p.B * p.Np, p.Kd, src_headpad(o.Wv, o.ld_d, p.dh, p.DP), ht,
+              out_map(v, dt, p.H * p.DP, p.B * p.Np, axis_linear(32),
+                      axis(32, (int64_t)p.H * DP * 32, 1)),
+              tile);
+  add_problem(gg, p.H * p.DP, p.B * p.Np, p.Kd, src_headpad(o.WkE, o.ld_d, p.dh, p.DP), ht,
+              out_map(ws + bp.kt.off, dt, p.H * p.DP, p.B * p.Np, axis_linear(32),
+                      axis(32, (int64_t)p.H * DP * 32, 1)),
+              tile);
+  add_problem(gg, p.B * p.Np, p.H * p.DP, p.Kd, ht, src_headpad(o.Wv, o.ld_d, p.dh, p.DP),
+              out_map(ws + bp.vn.off, dt, p.B * p.Np, p.H * p.DP,
+                      axis(p.Np, (int64_t)p.H * p.Np * DP, DP), axis(p.DP, (int64_t)p.Np * DP, 1)),
+              tile);
+  TXL_TRY(add_rk(gg, p, a, o, ws, stream));
+  TXL_TRY(after_launch(timed(K_PROJ_GEMM, stream, [&] { return launch_gemm(gg, dt, stream); }),
+                       "backward projection GEMMs", stream));
+  // forward recompute: out (bf16, workspace) and the rows' log-sum-exp
+  AttnPtrs fa = a;
+  fa.out = ws + bp.o.off;
+  float* lse = reinterpret_cast<float*>(ws + bp.lse.off);
+  TXL_TRY(run_attention(p, fa, ws, stream, k, v, 0, nullptr, nullptr, lse));
+
+  BwdPrepArgs pa{};
+  pa.B = p.B; pa.H = p.H; pa.L = p.L; pa.dh = p.dh; pa.Lp = p.Lp;
+  pa.dout = g.d_out;
+  pa.out = fa.out;
+  pa.q = reinterpret_cast<const float*>(ws + p.q.off);
+  pa.u = a.u;
+  pa.v = a.v;
+  pa.dop = ws + bp.dop.off;
+  pa.dot = ws + bp.dot.off;
+  pa.qut = ws + bp.qut.off;
+  pa.qvt = ws + bp.qvt.off;
+  pa.dsum = reinterpret_cast<float*>(ws + bp.dsum.off);
+  TXL_TRY(after_launch(timed(K_BWD_AUX, stream, [&] { return launch_bwd_prep(pa, stream); }),
+                       "backward prep", stream));
+  TXL_TRY(after_launch(timed(K_BWD_AUX, stream, [&] {
+                         return launch_rk_transpose(ws + p.rk.off, ws + bp.rkt.off, p.H, p.Pp,
+                                                    p.rk_pad, bp.rkt_ld, bp.rkt_pad, stream);
+                       }),
+                       "Rk transpose", stream));
+
+  BwdArgs ba{};
+  ba.B = p.B; ba.H = p.H; ba.L = p.L; ba.M = p.M; ba.dh = p.dh;
+  ba.Lp = p.Lp; ba.Np = p.Np; ba.Pp = p.Pp;
+  ba.c_scale = p.scale * 1.4426950408889634f;
+  ba.scale = p.scale;
+  ba.q = pa.q;
+  ba.k = k;
+  ba.kt = ws + bp.kt.off;
+  ba.vn = ws + bp.vn.off;
+  ba.rk = ws + p.rk.off;
+  ba.rkt = ws + bp.rkt.off;
+  ba.rkt_ld = bp.rkt_ld;
+  ba.rkt_pad = bp.rkt_pad;
+  ba.u = a.u;
+  ba.v = a.v;
+  ba.dop = pa.dop;
+  ba.lse = lse;
+  ba.dsum = pa.dsum;
+  ba.pt = ws + bp.pt.off;
+  ba.dst = ws + bp.dst.off;
+  ba.dspt = ws + bp.dspt.off;
+  ba.dsp_rows = bp.dsp_rows;
+  ba.dq = g.d_q;
+  ba.duv_part = reinterpret_cast<float*>(ws + bp.duv.off);
+  TXL_TRY(after_launch(timed(K_BWD_Q, stream, [&] { return launch_attn_bwd_q(ba, stream); }),
+                       "backward query kernel", stream));
+
+  // key side: dk = scale dS^T (q+u), dval = P^T G (per batch row and head),
+  // dRk = scale dS'^T (q+v) (per head, summed over batch rows)
+  const int64_t HD = (int64_t)p.H * p.dh;
+  auto bmm = [&](const void* A, int64_t lda, AxisMap ab, const void* Bm, int64_t ldb, AxisMap bb,
+                 int32_t batch, int32_t K, float alpha, float* C, AxisMap cb, float* C2,
+                 AxisMap c2b, int64_t c2m, int64_t c2n, const char* what) -> txl_status_t {
+    BmmArgs m{};
+    m.A = A; m.Bm = Bm; m.lda = lda; m.ldb = ldb; m.a_batch = ab; m.b_batch = bb;
+    m.M = p.P; m.K = K; m.batch = batch; m.n_valid = p.dh; m.m_valid = p.P;
+    m.kdiv = p.Lp; m.moff = p.M; m.klim = p.L; m.alpha = alpha;
+    m.C = C; m.ldc = HD; m.c_batch = cb;
+    m.C2 = C2; m.c2_m = c2m; m.c2_n = c2n; m.c2_batch = c2b;
+    return after_launch(timed(K_BWD_BMM, stream, [&] { return launch_bmm64(m, stream); }), what,
+                        stream);
+  };
+  const int32_t BHn = p.B * p.H;
+  const AxisMap per_bh_c = make_axis(p.H, (int64_t)p.P * HD, p.dh);   // [B][P][H][dh]
+  TXL_TRY(bmm(ws + bp.dst.off, p.Lp, axis_linear((int64_t)p.Np * p.Lp), ws + bp.qut.off, p.Lp,
+              axis_linear(DP * p.Lp), BHn, p.Lp, p.scale, g.d_k, per_bh_c, nullptr, kNoAxis, 0, 0,
+              "dk product"));
+  TXL_TRY(bmm(ws + bp.pt.off, p.Lp, axis_linear((int64_t)p.Np * p.Lp), ws + bp.dot.off, p.Lp,
+              axis_linear(DP * p.Lp), BHn, p.Lp, 1.0f, g.d_val, per_bh_c, nullptr, kNoAxis, 0, 0,
+              "dval product"));
+  const int64_t BL = (int64_t)p.B * p.Lp;
+  float* drkt = g.d_W_kR ? reinterpret_cast<float*>(ws + bp.drkt.off) : nullptr;
+  TXL_TRY(bmm(ws + bp.dspt.off, BL, axis_linear((int64_t)bp.dsp_rows * BL), ws + bp.qvt.off, BL,
+              axis_linear(DP * BL), p.H, (int32_t)BL, p.scale, g.d_Rk, axis_linear(p.dh), drkt,
+              axis_linear((int64_t)p.dh * p.P), 1, p.P, "dRk product"));
+  TXL_TRY(after_launch(timed(K_BWD_AUX, stream, [&] {
+                         return launch_duv_reduce(ba.duv_part, p.B, p.H, p.Lp / 32, p.dh, g.d_u,
+                                                  g.d_v, stream);
+                       }),
+                       "du, dv reduction", stream));
+  if (g.d_W_kR) {
+    // dW_kR = sum_delta dRk[delta] (x) R_delta: rows h*dh + c, K = distances
+    float* rt = reinterpret_cast<float*>(ws + bp.rt.off);
+    TXL_TRY(after_launch(timed(K_BWD_AUX, stream, [&] {
+                           return launch_transpose_f32(a.R, p.P, p.dpos, dt, rt, stream);
+                         }),
+                         "R transpose", stream));
+    GemmGroup gw{};
+    add_problem(gw, (int32_t)HD, p.dpos, p.P, src_plain(drkt, p.P, (int32_t)HD),
+                src_plain(rt, p.P, p.dpos),
+                out_map(g.d_W_kR, TXL_F32, (int32_t)HD, p.dpos, axis_linear(p.dpos), axis_linear(1)),
+                gemm_tile(TXL_F32));
+    TXL_TRY(after_launch(timed(K_BWD_AUX, stream, [&] { return launch_gemm_f32(gw, stream); }),
+                         "dW_kR GEMM", stream));
+  }
+  return TXL_OK;
 }
 
 // --------------------------------------------------------- segment planning
@@ -909,6 +1103,34 @@ txl_status_t txl_rel_attn_fwd(const txl_attn_shape_t* shape, const void* h, cons
   if (workspace_bytes < need)
     return fail(TXL_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes, need);
   return run_rel_attn(p, a, static_cast<char*>(workspace), stream, nullptr, nullptr);
+}
+
+size_t txl_rel_attn_bwd_workspace_bytes(const txl_attn_shape_t* shape) {
+  if (check_shape(shape) != TXL_OK || shape->dtype != TXL_BF16) return 0;
+  return make_bwd_plan(shape, true, true).total;
+}
+
+txl_status_t txl_rel_attn_bwd(const txl_attn_shape_t* shape, const void* h, const void* mem,
+                              int32_t mem_start, const void* W_q, const void* W_kE,
+                              const void* W_kR, const void* W_v, const void* u, const void* v,
+                              const void* R, const void* Rk, const void* d_out, float* d_q,
+                              float* d_k, float* d_val, float* d_u, float* d_v, float* d_Rk,
+                              float* d_W_kR, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  TXL_TRY(check_shape(shape));
+  if (shape->dtype != TXL_BF16) return fail(TXL_ERR_UNSUPPORTED, "the backward is bf16 only");
+  AttnPtrs a{h, mem, W_q, W_kE, W_kR, W_v, u, v, R, Rk, mem_start, const_cast<void*>(d_out)};
+  TXL_TRY(check_attn_ptrs(shape, a, true, workspace));
+  if (!d_q || !d_k || !d_val || !d_u || !d_v || !d_Rk)
+    return fail(TXL_ERR_NULL_ARG, "d_q, d_k, d_val, d_u, d_v and d_Rk are required");
+  if (d_W_kR && Rk)
+    return fail(TXL_ERR_BAD_SHAPE, "d_W_kR needs Rk computed from W_kR and R (Rk must be NULL)");
+  const BwdPlan bp = make_bwd_plan(shape, Rk == nullptr, d_W_kR != nullptr);
+  const size_t need = txl_rel_attn_bwd_workspace_bytes(shape);
+  if (workspace_bytes < need)
+    return fail(TXL_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes, need);
+  const BwdOut g{d_out, d_q, d_k, d_val, d_u, d_v, d_Rk, d_W_kR};
+  return run_rel_attn_bwd(bp, a, g, static_cast<char*>(workspace), stream);
 }
 
 int32_t txl_kv_ring_slots(const txl_attn_shape_t* shape) {

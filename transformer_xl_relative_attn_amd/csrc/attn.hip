@@ -463,6 +463,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a, int32_t p
     // out[b, i, head, :] = num / den; lane holds d = 32e + 8g + 4hf + r (r = 0..3)
     if (wave_on && i < L) {
       const float inv = 1.0f / l_sum;
+      if (a.lse && hf == 0) a.lse[(int64_t)bh * a.Lp + i] = m_ref + log2f(l_sum);
       uint16_t* out = static_cast<uint16_t*>(a.out) + (((int64_t)b * L + i) * a.H + head) * a.dh;
       const bool vec = (a.dh == DP);
 #pragma unroll
@@ -562,6 +563,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, int32_t o
     }
   }
   const float inv = 1.0f / den;
+  if (a.lse && c4 == 0) a.lse[prow] = mx + log2f(den);
   uint16_t* out = static_cast<uint16_t*>(a.out) + ((int64_t)b * a.L + i) * a.H * a.dh +
                   (int64_t)head * a.dh;
   if (a.dh == DP) {

@@ -1,0 +1,487 @@
+// Backward of the relative-position attention core (Dai et al., Transformer-XL,
+// Sec. 3.3 score A^rel with its four terms; Sec. 3.2: the memory enters with a
+// stop-gradient, so gradients stop at the cached states, while the keys and
+// values computed from them are ordinary tensors of the segment).
+//
+// With s_ij = scale * A_ij, P = softmax_j(s) over visible keys j <= M + i,
+// out = P val, and G = dLoss/dout:
+//   dP_ij  = G_i . val_j,  D_i = G_i . out_i,  dS_ij = P_ij (dP_ij - D_i)
+//   dq_i   = scale * sum_j dS_ij (k_j + Rk[M+i-j])        terms (a), (b)
+//   dk_j   = scale * sum_i dS_ij (q_i + u)                terms (a), (c)
+//   dval_j = sum_i P_ij G_i
+//   du     = scale * sum_ij dS_ij k_j,  dv = scale * sum_ij dS_ij Rk[M+i-j]
+//   dRk[delta] = scale * sum over pairs with M+i-j = delta of dS_ij (q_i + v)
+//
+// attn_bwd_q_kernel (one wave per 32 queries of one (b, h); no barriers): for
+//   every visible 32-key block it recomputes the scores exactly as the forward
+//   kernel does (the (b)+(d) window written shifted to LDS and read back as the
+//   accumulator of (q+u).K), P from the forward's log-sum-exp, dP^T = val
+//   G^T on the matrix cores, and dS.  It accumulates dq's k-part (K^T tile
+//   times dS^T) and its Rk-part (Rk^T window times dS written shifted, row
+//   31 + i - j of the window holds pair (i, j), the App. B shift in reverse),
+//   and writes P^T, dS^T and the shifted dS'^T (row delta) for the key-side
+//   products, which need sums over queries.
+// bmm64_kernel: batched A B^T with 64 output columns (dk, dval, dRk), the
+//   masked entries of A selected away by index.
+#include "dev_common.h"
+
+namespace txl {
+
+namespace {
+
+constexpr int DP = 64;
+constexpr int KB = 32;
+constexpr int WP = 36;     // floats per query row of the score window
+constexpr int DSW = 72;    // bf16 per query row of the dS' window (64 + pad)
+constexpr float kNegInf = -__builtin_inff();
+
+struct BwdSmem {
+  float win[4][32 * WP];            // per wave: shifted (b)+(d) window of the scores
+  uint16_t dsw[4][32 * DSW];        // per wave: query row i, position 31 + i - j -> dS_ij
+  uint16_t half[4][2][32 * 32];     // per wave: two 32-row halves of dS'^T [row][query]
+};
+
+__device__ __forceinline__ bf16x8 load8(const void* base, int64_t elem) {
+  return *reinterpret_cast<const bf16x8*>(static_cast<const uint16_t*>(base) + elem);
+}
+
+__device__ __forceinline__ bf16x8 pack8(const float* x) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = static_cast<bf16>(x[e]);
+  return r;
+}
+
+__device__ __forceinline__ uint16_t bf16_bits(float x) {
+  return __builtin_bit_cast(uint16_t, static_cast<bf16>(x));
+}
+
+__global__ __launch_bounds__(256, 1) void attn_bwd_q_kernel(BwdArgs a) {
+  const int32_t nqg = (a.L + 127) / 128;
+  const int32_t wid = blockIdx.x;
+  if (wid >= a.B * a.H * nqg) return;
+  const int32_t qg = wid % nqg;
+  const int32_t rest = wid / nqg;
+  const int32_t b = rest % a.B, head = rest / a.B;
+  const int32_t bh = b * a.H + head;
+
+  __shared__ BwdSmem sm;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ii = lane & 31, hf = lane >> 5;
+  const int32_t i0 = qg * 128 + 32 * wave;
+  if (i0 >= a.L) return;   // no workgroup barrier below: idle waves leave
+  const int32_t M = a.M, L = a.L, Np = a.Np, Lp = a.Lp;
+  const int32_t i = i0 + ii;
+  const bool qok = i < L;
+  const int32_t t_end = (M + min(i0 + 31, L - 1) + 1 + KB - 1) / KB;
+  const int32_t nkb = Np / KB;
+
+  const float lse = qok ? a.lse[(int64_t)bh * Lp + i] : 0.0f;
+  const float dsum = qok ? a.dsum[(int64_t)bh * Lp + i] : 0.0f;
+
+  // query operands (q+u)c, (q+v)c, d = 16s + 8hf + e, and G_i for dP^T
+  bf16x8 qu[4], qv[4], go[4];
+  {
+    const float* qrow = a.q + ((int64_t)bh * Lp + i) * DP;
+    const uint16_t* up = static_cast<const uint16_t*>(a.u) + (int64_t)head * a.dh;
+    const uint16_t* vp = static_cast<const uint16_t*>(a.v) + (int64_t)head * a.dh;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      float xu[8], xv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int d = 16 * s + 8 * hf + e;
+        const float qd = qrow[d];
+        const float uu = d < a.dh ? bf16_to_f32(up[d]) : 0.0f;
+        const float vv = d < a.dh ? bf16_to_f32(vp[d]) : 0.0f;
+        xu[e] = (qd + uu) * a.c_scale;
+        xv[e] = (qd + vv) * a.c_scale;
+      }
+      qu[s] = pack8(xu);
+      qv[s] = pack8(xv);
+      go[s] = load8(a.dop, ((int64_t)bh * Lp + i) * DP + 16 * s + 8 * hf);
+    }
+  }
+
+  const int64_t rk_head = (int64_t)head * (a.Pp + 2 * kRkPad) + kRkPad;
+  auto rk_rows = [&](int32_t base, bf16x8 (&f)[4]) {   // Rk rows base + ii
+#pragma unroll
+    for (int s = 0; s < 4; ++s) f[s] = load8(a.rk, (rk_head + base + ii) * DP + 16 * s + 8 * hf);
+  };
+  auto bd_chunk = [&](const bf16x8 (&rf)[4]) {
+    floatx16 acc = floatx16{0};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rf[s], qv[s], acc, 0, 0, 0);
+    return acc;
+  };
+  // score window: value for (query ii, key jj) is window row 31 + ii - jj of
+  // [lower chunk ; upper chunk], stored at position jj of row ii
+  float* win = sm.win[wave] + ii * WP;
+  auto write_win = [&](const floatx16& lower, const floatx16& upper) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int w = 8 * (e >> 2) + 4 * hf + (e & 3);
+      win[(31 + ii - w) & 31] = w >= ii ? lower[e] : upper[e];
+    }
+  };
+  auto read_win = [&]() {
+    floatx16 c;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const floatx4 x = *reinterpret_cast<const floatx4*>(win + 8 * g + 4 * hf);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) c[4 * g + r] = x[r];
+    }
+    return c;
+  };
+
+  uint16_t* drow = sm.dsw[wave] + ii * DSW;
+  uint16_t* halves = sm.half[wave][0];
+  // the first block's upper half starts empty
+  {
+    u32x4* h1 = reinterpret_cast<u32x4*>(sm.half[wave][1]);
+    h1[lane] = u32x4{0u, 0u, 0u, 0u};
+    h1[lane + 64] = u32x4{0u, 0u, 0u, 0u};
+  }
+  const int64_t dsp_col = (int64_t)b * Lp + i0;
+  const int64_t dsp_ld = (int64_t)a.B * Lp;
+  auto flush_half = [&](const uint16_t* hsrc, int32_t row0) {   // rows row0 + rr of dS'^T
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int c = lane + 64 * q, rr = c >> 2, part = c & 3;
+      const u32x4 val = *reinterpret_cast<const u32x4*>(hsrc + rr * 32 + 8 * part);
+      const int32_t row = row0 + rr;
+      if (row >= 0 && row < a.dsp_rows)
+        *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.dspt) +
+                                  ((int64_t)head * a.dsp_rows + row) * dsp_ld + dsp_col +
+                                  8 * part) = val;
+    }
+  };
+
+  floatx16 dqk[2] = {floatx16{0}, floatx16{0}}, dqr[2] = {floatx16{0}, floatx16{0}};
+  // upper chunk of block 0: rows base_0 + 32 .. +63, base_t = M + i0 - 32t - 31
+  floatx16 upper;
+  {
+    bf16x8 rf[4];
+    rk_rows(M + i0 - 31 + 32, rf);
+    upper = bd_chunk(rf);
+  }
+  uint16_t* ptp = static_cast<uint16_t*>(a.pt) + (int64_t)bh * Np * Lp + i;
+  uint16_t* dstp = static_cast<uint16_t*>(a.dst) + (int64_t)bh * Np * Lp + i;
+  const int64_t rkt_row0 = (int64_t)head * DP * a.rkt_ld + a.rkt_pad;
+
+  for (int32_t t = 0; t < t_end; ++t) {
+    const int32_t j0 = t * KB;
+    const int32_t base = M + i0 - 32 * t - 31;
+    bf16x8 kf[4], rf[4], vf[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      kf[s] = load8(a.k, ((int64_t)bh * Np + j0 + ii) * DP + 16 * s + 8 * hf);
+      vf[s] = load8(a.vn, ((int64_t)bh * Np + j0 + ii) * DP + 16 * s + 8 * hf);
+    }
+    rk_rows(base, rf);
+    // K^T tile fragments (rows d = 32e + ii, keys 16t2 + 8hf ..) and the Rk^T
+    // window (rows d, window positions 16s + 8hf ..)
+    bf16x8 ktf[2][2], rtf[2][4];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2)
+        ktf[t2][e] = load8(a.kt, ((((int64_t)b * nkb + t) * a.H + head) * DP + 32 * e + ii) * KB +
+                                     16 * t2 + 8 * hf);
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        rtf[e][s] = load8(a.rkt, rkt_row0 + (int64_t)(32 * e + ii) * a.rkt_ld + base + 16 * s + 8 * hf);
+    }
+    const floatx16 lower = bd_chunk(rf);
+    write_win(lower, upper);
+    wave_lds_fence();
+    floatx16 S = read_win();
+#pragma unroll
+    for (int s = 0; s < 4; ++s) S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qu[s], S, 0, 0, 0);
+    floatx16 dpt = floatx16{0};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) dpt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[s], go[s], dpt, 0, 0, 0);
+    // P and dS; key jj = 8g + 4hf + r (element 4g + r) visible iff j0 + jj <= M + i
+    const int32_t lim = M + i - j0 - 4 * hf;
+    float ds[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int kk = 8 * (e >> 2) + (e & 3);
+      const float p = (qok && kk <= lim) ? __builtin_amdgcn_exp2f(S[e] - lse) : 0.0f;
+      ds[e] = p * (dpt[e] - dsum);
+      const int jj = kk + 4 * hf;
+      ptp[(int64_t)(j0 + jj) * Lp] = bf16_bits(p);
+      dstp[(int64_t)(j0 + jj) * Lp] = bf16_bits(ds[e]);
+    }
+    // dq, k-part: K^T tile times dS^T (bf16 pairs exchanged with the partner
+    // lane so that the operand lists keys 16t2 + 8hf .. +7 in order)
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) {
+      const u32x4 pw = __builtin_bit_cast(u32x4, pack8(&ds[8 * t2]));
+      const auto s02 = __builtin_amdgcn_permlane32_swap(pw[0], pw[2], false, false);
+      const auto s13 = __builtin_amdgcn_permlane32_swap(pw[1], pw[3], false, false);
+      const bf16x8 dsb = __builtin_bit_cast(bf16x8, u32x4{s02[0], s13[0], s02[1], s13[1]});
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+        dqk[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ktf[t2][e], dsb, dqk[e], 0, 0, 0);
+    }
+    // dS shifted by distance: window position r = 31 + ii - jj, rows base + r
+    uint16_t* lo = halves + (t & 1) * (32 * 32);
+    uint16_t* up = halves + ((t + 1) & 1) * (32 * 32);
+    {
+      u32x4* z = reinterpret_cast<u32x4*>(drow + 32 * hf);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) z[c] = u32x4{0u, 0u, 0u, 0u};
+      u32x4* zl = reinterpret_cast<u32x4*>(lo);
+      zl[lane] = u32x4{0u, 0u, 0u, 0u};
+      zl[lane + 64] = u32x4{0u, 0u, 0u, 0u};
+    }
+    wave_lds_fence();
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int jj = 8 * (e >> 2) + 4 * hf + (e & 3);
+      const int r = 31 + ii - jj;
+      const uint16_t x = bf16_bits(ds[e]);
+      drow[r] = x;
+      if (r >= 32)
+        up[(r - 32) * 32 + ii] = x;
+      else
+        lo[r * 32 + ii] = x;
+    }
+    wave_lds_fence();
+    bf16x8 dw[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) dw[s] = *reinterpret_cast<const bf16x8*>(drow + 16 * s + 8 * hf);
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        dqr[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rtf[e][s], dw[s], dqr[e], 0, 0, 0);
+    // rows base + 32 .. +63 are complete (keys of blocks t-1 and t)
+    flush_half(up, base + 32);
+    wave_lds_fence();
+    upper = lower;
+  }
+  flush_half(halves + ((t_end - 1) & 1) * (32 * 32), M + i0 - 32 * (t_end - 1) - 31);
+
+  // dq = scale (k-part + Rk-part); lane holds d = 32e + 8g + 4hf + r of query i
+  if (qok) {
+    float* dqrow = a.dq + (((int64_t)b * L + i) * a.H + head) * a.dh;
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int d = 32 * e + 8 * g + 4 * hf + r;
+          if (d < a.dh) dqrow[d] = a.scale * (dqk[e][4 * g + r] + dqr[e][4 * g + r]);
+        }
+  }
+  // per-32-query sums of both parts (-> du, dv); padded queries hold zeros
+  const int32_t nch = Lp / 32;
+#pragma unroll
+  for (int which = 0; which < 2; ++which) {
+    float* dst = a.duv_part + ((((int64_t)which * a.B + b) * a.H + head) * nch + i0 / 32) * DP;
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int x = 0; x < 16; ++x) {
+        float val = which == 0 ? dqk[e][x] : dqr[e][x];
+#pragma unroll
+        for (int o = 1; o < 32; o <<= 1) val += __shfl_xor(val, o);
+        if (ii == 0) dst[32 * e + 8 * (x >> 2) + 4 * hf + (x & 3)] = a.scale * val;
+      }
+  }
+}
+
+// ------------------------------------------------------------------ bmm64
+// One wave per 32 rows of A, both 32-column halves of the output.  Operand
+// fragments come straight from global memory (rows are K-contiguous), one
+// 16-wide k-step ahead of the matrix-core products.
+__global__ __launch_bounds__(256) void bmm64_kernel(BmmArgs a) {
+  const int32_t bi = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int ii = lane & 31, hf = lane >> 5;
+  const int32_t m0 = blockIdx.x * 128 + 32 * wave;
+  if (m0 >= a.M) return;
+  const uint16_t* A = static_cast<const uint16_t*>(a.A) + axis_offset(a.a_batch, bi);
+  const uint16_t* Bm = static_cast<const uint16_t*>(a.Bm) + axis_offset(a.b_batch, bi);
+  const int32_t m = m0 + ii;
+  const bool mok = m < a.M;
+  const uint16_t* arow = A + (int64_t)(mok ? m : m0) * a.lda;
+  const uint16_t* brow[2];
+  bool nok[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int n = 32 * e + ii;
+    nok[e] = n < a.n_valid;
+    brow[e] = Bm + (int64_t)(nok[e] ? n : 0) * a.ldb;
+  }
+  floatx16 acc[2] = {floatx16{0}, floatx16{0}};
+  // A(m, k) counts iff klim > k % kdiv >= m - moff: this wave's rows need
+  // kk >= m0 - moff, and none past klim
+  const int32_t kk_first = max(0, m0 - a.moff) & ~15;
+  const int32_t kk_end = min(a.kdiv, a.klim);
+  const int32_t nseg = a.K / a.kdiv;
+  const int32_t lo_row = m - a.moff;   // first valid kk of this lane's row
+  for (int32_t seg = 0; seg < nseg; ++seg) {
+    const int64_t kbase = (int64_t)seg * a.kdiv;
+    for (int32_t kk = kk_first; kk < kk_end; kk += 16) {
+      const int32_t k8 = kk + 8 * hf;
+      bf16x8 af = bf16x8{};
+      if (mok) af = *reinterpret_cast<const bf16x8*>(arow + kbase + k8);
+      const int lo = lo_row - k8, hi = kk_end - k8;
+      if (!mok || lo > 0 || hi < 8) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (!mok || e < lo || e >= hi) af[e] = static_cast<bf16>(0.0f);
+      }
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        bf16x8 bfr = bf16x8{};
+        if (nok[e]) bfr = *reinterpret_cast<const bf16x8*>(brow[e] + kbase + k8);
+        acc[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bfr, acc[e], 0, 0, 0);
+      }
+    }
+  }
+  // lane holds column n = 32e + ii, rows m0 + 8g + 4hf + r (element 4g + r)
+  float* C = a.C + axis_offset(a.c_batch, bi);
+  float* C2 = a.C2 ? a.C2 + axis_offset(a.c2_batch, bi) : nullptr;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int n = 32 * e + ii;
+    if (!nok[e]) continue;
+#pragma unroll
+    for (int x = 0; x < 16; ++x) {
+      const int32_t row = m0 + 8 * (x >> 2) + 4 * hf + (x & 3);
+      if (row >= a.m_valid) continue;
+      const float val = a.alpha * acc[e][x];
+      C[(int64_t)row * a.ldc + n] = val;
+      if (C2) C2[(int64_t)row * a.c2_m + (int64_t)n * a.c2_n] = val;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ helpers
+// One thread per (b, h, i < Lp): D_i = G_i . out_i, G repacked [bh][i][64] and
+// transposed [bh][64][i], (q+u)^T [bh][64][i], (q+v)^T [h][64][b*Lp + i].
+__global__ void bwd_prep_kernel(BwdPrepArgs a) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)a.B * a.H * a.Lp) return;
+  const int32_t i = idx % a.Lp;
+  const int32_t bh = idx / a.Lp;
+  const int32_t b = bh / a.H, head = bh % a.H;
+  const bool ok = i < a.L;
+  const uint16_t* g = static_cast<const uint16_t*>(a.dout) + (((int64_t)b * a.L + i) * a.H + head) * a.dh;
+  const uint16_t* o = static_cast<const uint16_t*>(a.out) + (((int64_t)b * a.L + i) * a.H + head) * a.dh;
+  const float* q = a.q + ((int64_t)bh * a.Lp + i) * DP;
+  const uint16_t* up = static_cast<const uint16_t*>(a.u) + (int64_t)head * a.dh;
+  const uint16_t* vp = static_cast<const uint16_t*>(a.v) + (int64_t)head * a.dh;
+  uint16_t* dop = static_cast<uint16_t*>(a.dop) + ((int64_t)bh * a.Lp + i) * DP;
+  uint16_t* dot = static_cast<uint16_t*>(a.dot) + (int64_t)bh * DP * a.Lp + i;
+  uint16_t* qut = static_cast<uint16_t*>(a.qut) + (int64_t)bh * DP * a.Lp + i;
+  const int64_t qv_ld = (int64_t)a.B * a.Lp;
+  uint16_t* qvt = static_cast<uint16_t*>(a.qvt) + (int64_t)head * DP * qv_ld + (int64_t)b * a.Lp + i;
+  float dsum = 0.0f;
+  for (int d = 0; d < DP; ++d) {
+    const bool dok = ok && d < a.dh;
+    const float gd = dok ? bf16_to_f32(g[d]) : 0.0f;
+    const float od = dok ? bf16_to_f32(o[d]) : 0.0f;
+    dsum += gd * od;
+    const uint16_t gb = bf16_bits(gd);
+    dop[d] = gb;
+    dot[(int64_t)d * a.Lp] = gb;
+    const float qd = ok ? q[d] : 0.0f;
+    qut[(int64_t)d * a.Lp] = dok ? bf16_bits(qd + bf16_to_f32(up[d])) : uint16_t(0);
+    qvt[(int64_t)d * qv_ld] = dok ? bf16_bits(qd + bf16_to_f32(vp[d])) : uint16_t(0);
+  }
+  a.dsum[idx] = dsum;
+}
+
+// Rk^T [h][d][c] = Rk[h][pad_ws + c - pad_t][d] for 0 <= c - pad_t < Pp, else 0.
+__global__ void rk_transpose_kernel(const uint16_t* rk, uint16_t* rkt, int32_t H, int32_t Pp,
+                                    int32_t pad_ws, int32_t ld, int32_t pad_t) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)H * DP * ld) return;
+  const int32_t c = idx % ld;
+  const int64_t hd = idx / ld;
+  const int32_t d = hd % DP, h = hd / DP;
+  const int32_t delta = c - pad_t;
+  rkt[idx] = (delta >= 0 && delta < Pp)
+                 ? rk[(((int64_t)h * (Pp + 2 * pad_ws)) + pad_ws + delta) * DP + d]
+                 : uint16_t(0);
+}
+
+// dst[c][r] = src[r][c] as fp32.
+__global__ void transpose_f32_kernel(const void* src, int32_t rows, int32_t cols, int32_t dtype,
+                                     float* dst) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)rows * cols) return;
+  const int32_t r = idx % rows;
+  const int32_t c = idx / rows;
+  dst[idx] = load_as_f32(src, (int64_t)r * cols + c, dtype);
+}
+
+// du[h][d], dv[h][d] = sums over batch rows and 32-query chunks, in order.
+__global__ void duv_reduce_kernel(const float* part, int32_t B, int32_t H, int32_t nchunk,
+                                  int32_t dh, float* du, float* dv) {
+  const int32_t idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= 2 * H * dh) return;
+  const int32_t which = idx / (H * dh);
+  const int32_t hd = idx % (H * dh);
+  const int32_t h = hd / dh, d = hd % dh;
+  float s = 0.0f;
+  for (int32_t b = 0; b < B; ++b)
+    for (int32_t c = 0; c < nchunk; ++c)
+      s += part[((((int64_t)which * B + b) * H + h) * nchunk + c) * DP + d];
+  (which == 0 ? du : dv)[hd] = s;
+}
+
+dim3 grid_for(int64_t n) { return dim3((unsigned)((n + 255) / 256)); }
+
+}  // namespace
+
+int launch_attn_bwd_q(const BwdArgs& a, void* stream) {
+  const int32_t nqg = (a.L + 127) / 128;
+  hipLaunchKernelGGL(attn_bwd_q_kernel, dim3(a.B * a.H * nqg), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), a);
+  return static_cast<int>(hipGetLastError());
+}
+
+int launch_bmm64(const BmmArgs& a, void* stream) {
+  hipLaunchKernelGGL(bmm64_kernel, dim3((a.M + 127) / 128, a.batch), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), a);
+  return static_cast<int>(hipGetLastError());
+}
+
+int launch_bwd_prep(const BwdPrepArgs& a, void* stream) {
+  hipLaunchKernelGGL(bwd_prep_kernel, grid_for((int64_t)a.B * a.H * a.Lp), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), a);
+  return static_cast<int>(hipGetLastError());
+}
+
+int launch_rk_transpose(const void* rk_ws, void* rkt, int32_t H, int32_t Pp, int32_t pad_ws,
+                        int32_t ld, int32_t pad_t, void* stream) {
+  hipLaunchKernelGGL(rk_transpose_kernel, grid_for((int64_t)H * DP * ld), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const uint16_t*>(rk_ws),
+                     static_cast<uint16_t*>(rkt), H, Pp, pad_ws, ld, pad_t);
+  return static_cast<int>(hipGetLastError());
+}
+
+int launch_transpose_f32(const void* src, int32_t rows, int32_t cols, int32_t dtype, float* dst,
+                         void* stream) {
+  hipLaunchKernelGGL(transpose_f32_kernel, grid_for((int64_t)rows * cols), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), src, rows, cols, dtype, dst);
+  return static_cast<int>(hipGetLastError());
+}
+
+int launch_duv_reduce(const float* part, int32_t B, int32_t H, int32_t nchunk, int32_t dh,
+                      float* du, float* dv, void* stream) {
+  hipLaunchKernelGGL(duv_reduce_kernel, grid_for(2 * H * dh), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), part, B, H, nchunk, dh, du, dv);
+  return static_cast<int>(hipGetLastError());
+}
+
+}  // namespace txl

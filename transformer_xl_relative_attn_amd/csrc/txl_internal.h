@@ -167,6 +167,8 @@ struct AttnArgs {
   void* out;               // [B][L][H][dh] in the call dtype
   void* part_o;            // split partials: bf16 O/sum [n_split][B*H*Lp][DP]
   float* part_ml;          // [n_split][B*H*Lp][2] (running max, sum)
+  float* lse;              // optional [B*H*Lp]: log2 of each row's softmax denominator,
+                           // in the base-2 units of the bf16 kernel (rows i < L)
   int32_t dtype;
   // optional fused ring update (bf16 kernel): copy min(L, M) rows of upd_src
   // [B][L][*] into upd_mem [B][M][*] (row_bytes % 16 == 0); NULL = none
@@ -178,6 +180,70 @@ struct AttnArgs {
 
 // Compute units of the current device (cached per device id).
 int32_t device_cu_count();
+
+// Backward of the bf16 attention core (attn_bwd.hip).  Gradients are taken
+// with respect to the score s = scale * A (dS), then scaled by `scale`.
+struct BwdArgs {
+  int32_t B, H, L, M, dh, Lp, Np, Pp;
+  float c_scale;           // scale * log2(e), the forward kernel's score units
+  float scale;
+  const float* q;          // fp32 [B][H][Lp][DP]
+  const void* k;           // bf16 K [B][H][Np][DP]
+  const void* kt;          // bf16 K^T in 32-key tiles [B][Np/32][H][DP][32]
+  const void* vn;          // bf16 val [B][H][Np][DP]
+  const void* rk;          // bf16 [H][kRkPad + Pp + kRkPad][DP]
+  const void* rkt;         // bf16 Rk^T [H][DP][rkt_ld], distance delta at column rkt_pad + delta
+  int32_t rkt_ld, rkt_pad;
+  const void* u;           // bf16 [H][dh]
+  const void* v;
+  const void* dop;         // bf16 dLoss/dout [B][H][Lp][DP] (zero padded)
+  const float* lse;        // [B*H*Lp] log2 softmax denominators (base-2 score units)
+  const float* dsum;       // [B*H*Lp] D_i = dout_i . out_i
+  void* pt;                // bf16 P^T  [B][H][Np][Lp]
+  void* dst;               // bf16 dS^T [B][H][Np][Lp]
+  void* dspt;              // bf16 dS'^T [H][dsp_rows][B*Lp]: row delta, column b*Lp + i holds
+  int32_t dsp_rows;        //   dS[i][M+i-delta] (rows and columns outside the band unwritten)
+  float* dq;               // fp32 [B][L][H][dh]
+  float* duv_part;         // fp32 [2][B][H][Lp/32][DP]: per 32 queries, the sums of the
+                           //   k-part and the Rk-part of dq (-> du, dv)
+};
+
+// Batched "A times B^T" with 64 output columns, fp32 result:
+//   C[bi][m][n] = alpha * sum_k A[bi][m][k] B[bi][n][k],  n < n_valid <= 64,
+// A and B bf16 with rows K-contiguous.  A(m, k) counts only where
+// klim > k % kdiv >= m - moff (the other entries are never read as data:
+// they may hold anything).  Batch bi starts at a_batch(bi), b_batch(bi),
+// c_batch(bi) elements; C2 (optional) receives the same values at
+// c2_batch(bi) + m*c2_m + n*c2_n.
+struct BmmArgs {
+  const void* A;
+  const void* Bm;
+  int64_t lda, ldb;
+  AxisMap a_batch, b_batch;
+  int32_t M, K, batch, n_valid, m_valid;
+  int32_t kdiv, moff, klim;
+  float alpha;
+  float* C;
+  int64_t ldc;
+  AxisMap c_batch;
+  float* C2;
+  int64_t c2_m, c2_n;
+  AxisMap c2_batch;
+};
+
+struct BwdPrepArgs {
+  int32_t B, H, L, dh, Lp;
+  const void* dout;        // bf16 [B][L][H][dh]
+  const void* out;         // bf16 [B][L][H][dh] (forward output)
+  const float* q;          // fp32 [B][H][Lp][DP]
+  const void* u;
+  const void* v;
+  void* dop;               // bf16 [B][H][Lp][DP]
+  void* dot;               // bf16 [B][H][DP][Lp]   dout^T
+  void* qut;               // bf16 [B][H][DP][Lp]   (q+u)^T
+  void* qvt;               // bf16 [H][DP][B*Lp]    (q+v)^T
+  float* dsum;             // [B*H*Lp]
+};
 
 // Launch wrappers (return a hipError_t as int).
 int launch_gemm_bf16(const GemmGroup& g, void* stream);
@@ -194,6 +260,15 @@ int launch_layernorm(const float* resid, const float* parts, int32_t n_parts, in
                      float* y_f32, void* y_lo, int32_t rows, int32_t d, int32_t lo_dtype, float eps,
                      void* stream);
 int launch_cast_f32(const void* src, float* dst, int64_t n, int32_t dtype, void* stream);
+int launch_attn_bwd_q(const BwdArgs& a, void* stream);
+int launch_bmm64(const BmmArgs& a, void* stream);
+int launch_bwd_prep(const BwdPrepArgs& a, void* stream);
+int launch_rk_transpose(const void* rk_ws, void* rkt, int32_t H, int32_t Pp, int32_t pad_ws,
+                        int32_t ld, int32_t pad_t, void* stream);
+int launch_transpose_f32(const void* src, int32_t rows, int32_t cols, int32_t dtype, float* dst,
+                         void* stream);
+int launch_duv_reduce(const float* part, int32_t B, int32_t H, int32_t nchunk, int32_t dh,
+                      float* du, float* dv, void* stream);
 int launch_repack_rk(const void* rk_pub, void* rk_ws, int32_t P, int32_t Pp, int32_t pad, int32_t H,
                      int32_t dh, int32_t dp, int32_t dtype, void* stream);
 
