@@ -264,6 +264,114 @@ def table9(args):
     print(json.dumps(out), flush=True)
 
 
+def bwd_flops(cfg):
+    """Algorithmic FLOPs of the attention backward over the visible pairs: the
+    score recompute ((q+u).k and (q+v).Rk), dP = G val^T, dq's two products,
+    dk, dval and dRk (8 products of 2 * pairs * d_head per (b, h)), plus
+    dW_kR."""
+    f = flops(cfg)
+    core = cfg.batch * cfg.n_heads * 8 * 2 * f["pairs"] * cfg.d_head
+    wkr = 2 * (cfg.mem_len + cfg.seg_len) * cfg.n_heads * cfg.d_head * cfg.d_pos
+    return core, wkr
+
+
+def bwd_bench(args):
+    """Backward of the train-shaped layer (txl_rel_attn_bwd, batch 22, segment
+    512, memory 512, 8 heads of 64, d_model 512, bf16 in, fp32 gradients):
+    one step = the whole call (projections and forward recomputed inside).
+    Prints one JSON line."""
+    import numpy as np
+    import torch
+
+    import synth
+    import transformer_xl_relative_attn_amd as txl
+
+    cfg = synth.get_config(args.bwd_config)
+    torch.cuda.set_device(0)
+    wl = synth.make_workload(cfg, n_segments=1)
+
+    def dev(x):
+        return torch.from_numpy(synth.bf16_bits(x).view(np.int16)).view(torch.bfloat16).cuda()
+
+    lay = wl.layers[0]
+    W = dict(W_q=dev(lay.W_q), W_kE=dev(lay.W_kE), W_kR=dev(lay.W_kR), W_v=dev(lay.W_v))
+    u, v = dev(wl.u), dev(wl.v)
+    mem = dev(wl.mem[0])
+    h = dev(wl.segments[0])
+    B, L, M, H, dh = cfg.batch, cfg.seg_len, cfg.mem_len, cfg.n_heads, cfg.d_head
+    P = M + L
+    G = dev(np.random.default_rng(cfg.seed + 1).normal(0.0, 1.0, (B, L, H * dh)))
+    R = torch.empty((cfg.n_pos, cfg.d_pos), dtype=torch.bfloat16, device="cuda")
+    txl.txl_sinusoid_pos(R, cfg.n_pos, cfg.d_pos, txl.TXL_BF16)
+    shape = txl.AttnShape(B, L, M, cfg.d_model, H, dh, cfg.d_pos, txl.TXL_BF16, 0.0)
+    f32 = dict(dtype=torch.float32, device="cuda")
+    outs = dict(d_q=torch.empty((B, L, H, dh), **f32), d_k=torch.empty((B, P, H, dh), **f32),
+                d_val=torch.empty((B, P, H, dh), **f32), d_u=torch.empty((H, dh), **f32),
+                d_v=torch.empty((H, dh), **f32), d_Rk=torch.empty((P, H, dh), **f32),
+                d_W_kR=torch.empty((H * dh, cfg.d_pos), **f32))
+    ws = torch.empty(txl.txl_rel_attn_bwd_workspace_bytes(shape), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        txl.txl_rel_attn_bwd(shape, h, mem, 0, W["W_q"], W["W_kE"], W["W_kR"], W["W_v"], u, v, R,
+                             None, G, outs["d_q"], outs["d_k"], outs["d_val"], outs["d_u"],
+                             outs["d_v"], outs["d_Rk"], outs["d_W_kR"], ws, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = max(e0.elapsed_time(e1), (time.perf_counter() - t0) * 1e3) / args.steps
+    txl.txl_timing_reset()
+    txl.txl_timing_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    per = txl.txl_timing_read()
+    txl.txl_timing_enable(False)
+    kernels = {k: {"launches": c, "avg_us": round(t / c * 1e3, 2), "ms_per_step": round(t / args.steps, 4)}
+               for k, (c, t) in per.items() if c}
+    core, wkr = bwd_flops(cfg)
+    value = (core + wkr) / (ms * 1e-3) / 1e12
+    q_us = kernels.get("attn_bwd_q", {}).get("avg_us")
+    # the query-side kernel runs 5 of the 8 products of 2 * pairs * d_head
+    q_flops = cfg.batch * H * 5 * 2 * flops(cfg)["pairs"] * dh
+    roof = None
+    if q_us:
+        ach = q_flops / (q_us * 1e-6) / 1e12
+        roof = {"kernel": "attn_bwd_q", "bound": "mfma", "achieved": round(ach, 1),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                "traffic": None, "algorithmic_per_launch": q_flops}
+    out = {
+        "metric": "rel-attn bwd TFLOP/s (train-shaped layer, algorithmic backward FLOPs)",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: backward of one relative-attention layer",
+                   "batch": B, "seg_len": L, "mem_len": M, "d_model": cfg.d_model,
+                   "n_heads": H, "d_head": dh},
+        "gflop_per_step": round((core + wkr) / 1e9, 3),
+        "tokens_per_s": round(B * L / (ms * 1e-3), 1),
+        "kernels": kernels,
+        "roofline": roof,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__,
                                  formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -283,6 +391,10 @@ def main():
                     help="instead of the headline, measure the vanilla-vs-XL evaluation "
                          "slowdown at attention lengths 800..3800 (one JSON line)")
     ap.add_argument("--table9-steps", type=int, default=6)
+    ap.add_argument("--bwd", action="store_true",
+                    help="instead of the headline, time the backward of the train-shaped layer "
+                         "(one JSON line)")
+    ap.add_argument("--bwd-config", default="train_l512_m512")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -292,6 +404,9 @@ def main():
 
     if args.table9:
         table9(args)
+        return
+    if args.bwd:
+        bwd_bench(args)
         return
 
     import numpy as np

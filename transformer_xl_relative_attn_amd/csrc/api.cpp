@@ -631,7 +631,7 @@ txl_status_t run_rel_attn_ring(const AttnPlan& p, const AttnPtrs& a, void* ring,
 // P^T, dS^T, dS'^T of the key-side products.
 struct BwdPlan {
   AttnPlan p;
-  Region kt, vn, o, lse, dop, dot, qut, qvt, dsum, pt, dst, dspt, duv, rkt, rt, drkt;
+  Region kt, vn, o, lse, dop, dot, qut, qvt, dsum, pt, dst, dspt, duv, rkt, rt, drkt, drkp;
   int32_t rkt_ld, rkt_pad, dsp_rows;
   size_t total;
 };
@@ -661,14 +661,17 @@ BwdPlan make_bwd_plan(const txl_attn_shape_t* s, bool compute_rk, bool want_wkr)
   bp.dsp_rows = p.Pp + 32;
   take(bp.dspt, (size_t)p.H * bp.dsp_rows * p.B * p.Lp * 2);
   take(bp.duv, 2 * BH * (p.Lp / 32) * p.DP * 4);
+  take(bp.drkp, (size_t)p.B * p.P * p.H * p.dh * 4);
   // Rk^T columns: distance delta at rkt_pad + delta; rkt_pad = 31 - M (mod 8)
   // keeps every window the kernel reads 16-byte aligned
   bp.rkt_pad = 64 + (((31 - p.M) % 8) + 8) % 8;
   bp.rkt_ld = (int32_t)round_up(bp.rkt_pad + p.Pp + 64, 8);
   take(bp.rkt, (size_t)p.H * p.DP * bp.rkt_ld * 2);
   if (want_wkr) {
-    take(bp.rt, (size_t)p.dpos * p.P * 4);
-    take(bp.drkt, (size_t)p.H * p.dh * p.P * 4);
+    // bf16 transposes for dW_kR, distances padded to a multiple of 64
+    const size_t Pk = round_up(p.P, 64);
+    take(bp.rt, (size_t)p.dpos * Pk * 2);
+    take(bp.drkt, (size_t)p.H * p.dh * Pk * 2);
   }
   bp.total = off;
   return bp;
@@ -788,29 +791,43 @@ txl_status_t run_rel_attn_bwd(const BwdPlan& bp, const AttnPtrs& a, const BwdOut
   TXL_TRY(bmm(ws + bp.pt.off, p.Lp, axis_linear((int64_t)p.Np * p.Lp), ws + bp.dot.off, p.Lp,
               axis_linear(DP * p.Lp), BHn, p.Lp, 1.0f, g.d_val, per_bh_c, nullptr, kNoAxis, 0, 0,
               "dval product"));
+  // dRk per (head, batch row) into partials [B][P][H][dh], then summed over
+  // the batch rows in order (one product per head would leave the chip idle)
   const int64_t BL = (int64_t)p.B * p.Lp;
-  float* drkt = g.d_W_kR ? reinterpret_cast<float*>(ws + bp.drkt.off) : nullptr;
-  TXL_TRY(bmm(ws + bp.dspt.off, BL, axis_linear((int64_t)bp.dsp_rows * BL), ws + bp.qvt.off, BL,
-              axis_linear(DP * BL), p.H, (int32_t)BL, p.scale, g.d_Rk, axis_linear(p.dh), drkt,
-              axis_linear((int64_t)p.dh * p.P), 1, p.P, "dRk product"));
+  float* drk_part = reinterpret_cast<float*>(ws + bp.drkp.off);
+  TXL_TRY(bmm(ws + bp.dspt.off, BL, make_axis(p.B, (int64_t)bp.dsp_rows * BL, p.Lp),
+              ws + bp.qvt.off, BL, make_axis(p.B, DP * BL, p.Lp), BHn, p.Lp, p.scale, drk_part,
+              make_axis(p.B, p.dh, (int64_t)p.P * HD), nullptr, kNoAxis, 0, 0, "dRk product"));
+  TXL_TRY(after_launch(timed(K_BWD_AUX, stream, [&] {
+                         return launch_sum_rows(drk_part, p.B, (int64_t)p.P * HD, g.d_Rk, stream);
+                       }),
+                       "dRk batch sum", stream));
   TXL_TRY(after_launch(timed(K_BWD_AUX, stream, [&] {
                          return launch_duv_reduce(ba.duv_part, p.B, p.H, p.Lp / 32, p.dh, g.d_u,
                                                   g.d_v, stream);
                        }),
                        "du, dv reduction", stream));
   if (g.d_W_kR) {
-    // dW_kR = sum_delta dRk[delta] (x) R_delta: rows h*dh + c, K = distances
-    float* rt = reinterpret_cast<float*>(ws + bp.rt.off);
+    // dW_kR = sum_delta dRk[delta] (x) R_delta on the matrix cores: rows
+    // h*dh + c, K = distances (bf16 transposes padded with zero distances)
+    const int32_t Pk = (int32_t)round_up(p.P, 64);
+    char* rt = ws + bp.rt.off;
+    char* drkt = ws + bp.drkt.off;
     TXL_TRY(after_launch(timed(K_BWD_AUX, stream, [&] {
-                           return launch_transpose_f32(a.R, p.P, p.dpos, dt, rt, stream);
+                           return launch_transpose_bf16(a.R, p.P, p.dpos, dt, Pk, rt, stream);
                          }),
                          "R transpose", stream));
+    TXL_TRY(after_launch(timed(K_BWD_AUX, stream, [&] {
+                           return launch_transpose_bf16(g.d_Rk, p.P, (int32_t)HD, TXL_F32, Pk, drkt,
+                                                        stream);
+                         }),
+                         "dRk transpose", stream));
     GemmGroup gw{};
-    add_problem(gw, (int32_t)HD, p.dpos, p.P, src_plain(drkt, p.P, (int32_t)HD),
-                src_plain(rt, p.P, p.dpos),
+    add_problem(gw, (int32_t)HD, p.dpos, Pk, src_plain(drkt, Pk, (int32_t)HD),
+                src_plain(rt, Pk, p.dpos),
                 out_map(g.d_W_kR, TXL_F32, (int32_t)HD, p.dpos, axis_linear(p.dpos), axis_linear(1)),
-                gemm_tile(TXL_F32));
-    TXL_TRY(after_launch(timed(K_BWD_AUX, stream, [&] { return launch_gemm_f32(gw, stream); }),
+                gemm_tile(TXL_BF16));
+    TXL_TRY(after_launch(timed(K_BWD_AUX, stream, [&] { return launch_gemm_bf16(gw, stream); }),
                          "dW_kR GEMM", stream));
   }
   return TXL_OK;

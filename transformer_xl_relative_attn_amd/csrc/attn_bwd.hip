@@ -171,18 +171,29 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_q_kernel(BwdArgs a) {
   uint16_t* dstp = static_cast<uint16_t*>(a.dst) + (int64_t)bh * Np * Lp + i;
   const int64_t rkt_row0 = (int64_t)head * DP * a.rkt_ld + a.rkt_pad;
 
-  for (int32_t t = 0; t < t_end; ++t) {
+  // operands of the scores and dP^T of a block (loaded one block ahead)
+  struct Frags {
+    bf16x8 kf[4], vf[4], rf[4];
+  };
+  auto load_frags = [&](int32_t t, Frags& f) {
     const int32_t j0 = t * KB;
-    const int32_t base = M + i0 - 32 * t - 31;
-    bf16x8 kf[4], rf[4], vf[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      kf[s] = load8(a.k, ((int64_t)bh * Np + j0 + ii) * DP + 16 * s + 8 * hf);
-      vf[s] = load8(a.vn, ((int64_t)bh * Np + j0 + ii) * DP + 16 * s + 8 * hf);
+      f.kf[s] = load8(a.k, ((int64_t)bh * Np + j0 + ii) * DP + 16 * s + 8 * hf);
+      f.vf[s] = load8(a.vn, ((int64_t)bh * Np + j0 + ii) * DP + 16 * s + 8 * hf);
     }
-    rk_rows(base, rf);
+    rk_rows(M + i0 - 32 * t - 31, f.rf);
+  };
+
+  Frags cf;
+  auto block = [&](int32_t t) {
+    const int32_t j0 = t * KB;
+    const int32_t base = M + i0 - 32 * t - 31;
+    const bf16x8 (&kf)[4] = cf.kf;   // overwritten by the next block's load once used
+    const bf16x8 (&vf)[4] = cf.vf;
+    const bf16x8 (&rf)[4] = cf.rf;
     // K^T tile fragments (rows d = 32e + ii, keys 16t2 + 8hf ..) and the Rk^T
-    // window (rows d, window positions 16s + 8hf ..)
+    // window (rows d, window positions 16s + 8hf ..), used later in the block
     bf16x8 ktf[2][2], rtf[2][4];
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
@@ -203,6 +214,9 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_q_kernel(BwdArgs a) {
     floatx16 dpt = floatx16{0};
 #pragma unroll
     for (int s = 0; s < 4; ++s) dpt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[s], go[s], dpt, 0, 0, 0);
+    // this block's K, val and Rk fragments are consumed: the next block's load
+    // now, in flight during the rest of this block
+    if (t + 1 < t_end) load_frags(t + 1, cf);
     // P and dS; key jj = 8g + 4hf + r (element 4g + r) visible iff j0 + jj <= M + i
     const int32_t lim = M + i - j0 - 4 * hf;
     float ds[16];
@@ -263,7 +277,9 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_q_kernel(BwdArgs a) {
     flush_half(up, base + 32);
     wave_lds_fence();
     upper = lower;
-  }
+  };
+  load_frags(0, cf);
+  for (int32_t t = 0; t < t_end; ++t) block(t);
   flush_half(halves + ((t_end - 1) & 1) * (32 * 32), M + i0 - 32 * (t_end - 1) - 31);
 
   // dq = scale (k-part + Rk-part); lane holds d = 32e + 8g + 4hf + r of query i
@@ -321,30 +337,54 @@ __global__ __launch_bounds__(256) void bmm64_kernel(BmmArgs a) {
   }
   floatx16 acc[2] = {floatx16{0}, floatx16{0}};
   // A(m, k) counts iff klim > k % kdiv >= m - moff: this wave's rows need
-  // kk >= m0 - moff, and none past klim
+  // kk >= m0 - moff, and none past klim.  Steps of 16 k are numbered across
+  // the segments; fragments are loaded a group of G steps ahead.
   const int32_t kk_first = max(0, m0 - a.moff) & ~15;
   const int32_t kk_end = min(a.kdiv, a.klim);
-  const int32_t nseg = a.K / a.kdiv;
+  const int32_t per_seg = kk_end > kk_first ? (kk_end - kk_first + 15) / 16 : 0;
+  const int32_t nsteps = per_seg * (a.K / a.kdiv);
   const int32_t lo_row = m - a.moff;   // first valid kk of this lane's row
-  for (int32_t seg = 0; seg < nseg; ++seg) {
-    const int64_t kbase = (int64_t)seg * a.kdiv;
-    for (int32_t kk = kk_first; kk < kk_end; kk += 16) {
-      const int32_t k8 = kk + 8 * hf;
-      bf16x8 af = bf16x8{};
-      if (mok) af = *reinterpret_cast<const bf16x8*>(arow + kbase + k8);
-      const int lo = lo_row - k8, hi = kk_end - k8;
-      if (!mok || lo > 0 || hi < 8) {
+  constexpr int G = 4;
+  struct Frag {
+    bf16x8 a, b0, b1;
+    int32_t k8;   // kk + 8hf of the step
+  };
+  auto load = [&](int32_t st, Frag& f) {
+    const int32_t seg = st / per_seg;
+    const int32_t kk = kk_first + 16 * (st - seg * per_seg);
+    f.k8 = kk + 8 * hf;
+    const int64_t k = (int64_t)seg * a.kdiv + f.k8;
+    f.a = mok ? *reinterpret_cast<const bf16x8*>(arow + k) : bf16x8{};
+    f.b0 = nok[0] ? *reinterpret_cast<const bf16x8*>(brow[0] + k) : bf16x8{};
+    f.b1 = nok[1] ? *reinterpret_cast<const bf16x8*>(brow[1] + k) : bf16x8{};
+  };
+  auto use = [&](Frag& f) {
+    const int lo = lo_row - f.k8, hi = kk_end - f.k8;
+    if (!mok || lo > 0 || hi < 8) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (!mok || e < lo || e >= hi) af[e] = static_cast<bf16>(0.0f);
-      }
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        bf16x8 bfr = bf16x8{};
-        if (nok[e]) bfr = *reinterpret_cast<const bf16x8*>(brow[e] + kbase + k8);
-        acc[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bfr, acc[e], 0, 0, 0);
-      }
+      for (int e = 0; e < 8; ++e)
+        if (!mok || e < lo || e >= hi) f.a[e] = static_cast<bf16>(0.0f);
     }
+    acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a, f.b0, acc[0], 0, 0, 0);
+    acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a, f.b1, acc[1], 0, 0, 0);
+  };
+  Frag fa[G], fb[G];
+  auto load_group = [&](int32_t g0, Frag (&f)[G]) {
+#pragma unroll
+    for (int x = 0; x < G; ++x)
+      if (g0 + x < nsteps) load(g0 + x, f[x]);
+  };
+  auto use_group = [&](int32_t g0, Frag (&f)[G]) {
+#pragma unroll
+    for (int x = 0; x < G; ++x)
+      if (g0 + x < nsteps) use(f[x]);
+  };
+  load_group(0, fa);
+  for (int32_t g0 = 0; g0 < nsteps; g0 += 2 * G) {
+    load_group(g0 + G, fb);
+    use_group(g0, fa);
+    load_group(g0 + 2 * G, fa);
+    use_group(g0 + G, fb);
   }
   // lane holds column n = 32e + ii, rows m0 + 8g + 4hf + r (element 4g + r)
   float* C = a.C + axis_offset(a.c_batch, bi);
@@ -365,39 +405,118 @@ __global__ __launch_bounds__(256) void bmm64_kernel(BmmArgs a) {
 }
 
 // ------------------------------------------------------------------ helpers
-// One thread per (b, h, i < Lp): D_i = G_i . out_i, G repacked [bh][i][64] and
-// transposed [bh][64][i], (q+u)^T [bh][64][i], (q+v)^T [h][64][b*Lp + i].
-__global__ void bwd_prep_kernel(BwdPrepArgs a) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (int64_t)a.B * a.H * a.Lp) return;
-  const int32_t i = idx % a.Lp;
-  const int32_t bh = idx / a.Lp;
+// One workgroup per (b, h) and 64 queries: D_i = G_i . out_i, G repacked
+// [bh][i][64] and, through an LDS tile, transposed [bh][64][i]; (q+u)^T
+// [bh][64][i] and (q+v)^T [h][64][b*Lp + i].  Rows i >= L and columns d >= dh
+// are zeros.
+__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdPrepArgs a) {
+  __shared__ __align__(16) uint16_t tg[64][72];   // [i][d], 144-byte rows
+  __shared__ __align__(16) uint16_t tu[64][72];
+  __shared__ __align__(16) uint16_t tv[64][72];
+  __shared__ float red[64][4];
+  const int32_t nch = a.Lp / 64 + (a.Lp % 64 ? 1 : 0);
+  const int32_t bh = blockIdx.x / nch, i_base = (blockIdx.x % nch) * 64;
   const int32_t b = bh / a.H, head = bh % a.H;
-  const bool ok = i < a.L;
-  const uint16_t* g = static_cast<const uint16_t*>(a.dout) + (((int64_t)b * a.L + i) * a.H + head) * a.dh;
-  const uint16_t* o = static_cast<const uint16_t*>(a.out) + (((int64_t)b * a.L + i) * a.H + head) * a.dh;
-  const float* q = a.q + ((int64_t)bh * a.Lp + i) * DP;
-  const uint16_t* up = static_cast<const uint16_t*>(a.u) + (int64_t)head * a.dh;
-  const uint16_t* vp = static_cast<const uint16_t*>(a.v) + (int64_t)head * a.dh;
-  uint16_t* dop = static_cast<uint16_t*>(a.dop) + ((int64_t)bh * a.Lp + i) * DP;
-  uint16_t* dot = static_cast<uint16_t*>(a.dot) + (int64_t)bh * DP * a.Lp + i;
-  uint16_t* qut = static_cast<uint16_t*>(a.qut) + (int64_t)bh * DP * a.Lp + i;
-  const int64_t qv_ld = (int64_t)a.B * a.Lp;
-  uint16_t* qvt = static_cast<uint16_t*>(a.qvt) + (int64_t)head * DP * qv_ld + (int64_t)b * a.Lp + i;
-  float dsum = 0.0f;
-  for (int d = 0; d < DP; ++d) {
-    const bool dok = ok && d < a.dh;
-    const float gd = dok ? bf16_to_f32(g[d]) : 0.0f;
-    const float od = dok ? bf16_to_f32(o[d]) : 0.0f;
-    dsum += gd * od;
-    const uint16_t gb = bf16_bits(gd);
-    dop[d] = gb;
-    dot[(int64_t)d * a.Lp] = gb;
-    const float qd = ok ? q[d] : 0.0f;
-    qut[(int64_t)d * a.Lp] = dok ? bf16_bits(qd + bf16_to_f32(up[d])) : uint16_t(0);
-    qvt[(int64_t)d * qv_ld] = dok ? bf16_bits(qd + bf16_to_f32(vp[d])) : uint16_t(0);
+  const int tid = threadIdx.x;
+  {
+    // thread -> row r = tid / 4, columns 16 * (tid % 4) .. +15
+    const int r = tid >> 2, c0 = 16 * (tid & 3);
+    const int32_t i = i_base + r;
+    const bool ok = i < a.L;
+    const int64_t src = (((int64_t)b * a.L + (ok ? i : 0)) * a.H + head) * a.dh;
+    const uint16_t* g = static_cast<const uint16_t*>(a.dout) + src;
+    const uint16_t* o = static_cast<const uint16_t*>(a.out) + src;
+    const float* q = a.q + ((int64_t)bh * a.Lp + (i < a.Lp ? i : 0)) * DP;
+    const uint16_t* up = static_cast<const uint16_t*>(a.u) + (int64_t)head * a.dh;
+    const uint16_t* vp = static_cast<const uint16_t*>(a.v) + (int64_t)head * a.dh;
+    float dsum = 0.0f;
+    if (ok && a.dh == DP) {
+      // whole rows: 16-byte loads
+      uint16_t gv[16], ov[16], uv[16], vv[16];
+      float qv[16];
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const u32x4 gx = *reinterpret_cast<const u32x4*>(g + c0 + 8 * h2);
+        const u32x4 ox = *reinterpret_cast<const u32x4*>(o + c0 + 8 * h2);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          gv[8 * h2 + 2 * w] = gx[w] & 0xffff;
+          gv[8 * h2 + 2 * w + 1] = gx[w] >> 16;
+          ov[8 * h2 + 2 * w] = ox[w] & 0xffff;
+          ov[8 * h2 + 2 * w + 1] = ox[w] >> 16;
+        }
+      }
+      // u, v carry no alignment guarantee: element loads (cached, tiny)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        uv[e] = up[c0 + e];
+        vv[e] = vp[c0 + e];
+      }
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        const floatx4 x = *reinterpret_cast<const floatx4*>(q + c0 + 4 * f);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) qv[4 * f + w] = x[w];
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int d = c0 + e;
+        const float gd = bf16_to_f32(gv[e]);
+        dsum += gd * bf16_to_f32(ov[e]);
+        tg[r][d] = gv[e];
+        tu[r][d] = bf16_bits(qv[e] + bf16_to_f32(uv[e]));
+        tv[r][d] = bf16_bits(qv[e] + bf16_to_f32(vv[e]));
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int d = c0 + e;
+        const bool dok = ok && d < a.dh;
+        const float gd = dok ? bf16_to_f32(g[d]) : 0.0f;
+        const float od = dok ? bf16_to_f32(o[d]) : 0.0f;
+        dsum += gd * od;
+        tg[r][d] = bf16_bits(gd);
+        const float qd = dok ? q[d] : 0.0f;
+        tu[r][d] = dok ? bf16_bits(qd + bf16_to_f32(up[d])) : uint16_t(0);
+        tv[r][d] = dok ? bf16_bits(qd + bf16_to_f32(vp[d])) : uint16_t(0);
+      }
+    }
+    red[r][tid & 3] = dsum;
+    if (i < a.Lp) {
+      uint16_t* dop = static_cast<uint16_t*>(a.dop) + ((int64_t)bh * a.Lp + i) * DP + c0;
+      *reinterpret_cast<u32x4*>(dop) = *reinterpret_cast<const u32x4*>(&tg[r][c0]);
+      *reinterpret_cast<u32x4*>(dop + 8) = *reinterpret_cast<const u32x4*>(&tg[r][c0 + 8]);
+    }
   }
-  a.dsum[idx] = dsum;
+  __syncthreads();
+  if (tid < 64 && i_base + tid < a.Lp)
+    a.dsum[(int64_t)bh * a.Lp + i_base + tid] =
+        (red[tid][0] + red[tid][1]) + (red[tid][2] + red[tid][3]);
+  // transposed: thread -> column d = tid / 4, queries 16 * (tid % 4) .. +15
+  {
+    const int d = tid >> 2, r0 = 16 * (tid & 3);
+    const int32_t i = i_base + r0;
+    if (i < a.Lp) {
+      u32x4 xg[2], xu[2], xv[2];   // 16 bf16 each, packed in pairs
+#pragma unroll
+      for (int e = 0; e < 16; e += 2) {
+        xg[e >> 3][(e & 7) >> 1] = (uint32_t)tg[r0 + e][d] | ((uint32_t)tg[r0 + e + 1][d] << 16);
+        xu[e >> 3][(e & 7) >> 1] = (uint32_t)tu[r0 + e][d] | ((uint32_t)tu[r0 + e + 1][d] << 16);
+        xv[e >> 3][(e & 7) >> 1] = (uint32_t)tv[r0 + e][d] | ((uint32_t)tv[r0 + e + 1][d] << 16);
+      }
+      const int64_t qv_ld = (int64_t)a.B * a.Lp;
+      uint16_t* dot = static_cast<uint16_t*>(a.dot) + ((int64_t)bh * DP + d) * a.Lp + i;
+      uint16_t* qut = static_cast<uint16_t*>(a.qut) + ((int64_t)bh * DP + d) * a.Lp + i;
+      uint16_t* qvt = static_cast<uint16_t*>(a.qvt) + ((int64_t)head * DP + d) * qv_ld +
+                      (int64_t)b * a.Lp + i;
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        *reinterpret_cast<u32x4*>(dot + 8 * h2) = xg[h2];
+        *reinterpret_cast<u32x4*>(qut + 8 * h2) = xu[h2];
+        *reinterpret_cast<u32x4*>(qvt + 8 * h2) = xv[h2];
+      }
+    }
+  }
 }
 
 // Rk^T [h][d][c] = Rk[h][pad_ws + c - pad_t][d] for 0 <= c - pad_t < Pp, else 0.
@@ -414,29 +533,51 @@ __global__ void rk_transpose_kernel(const uint16_t* rk, uint16_t* rkt, int32_t H
                  : uint16_t(0);
 }
 
-// dst[c][r] = src[r][c] as fp32.
-__global__ void transpose_f32_kernel(const void* src, int32_t rows, int32_t cols, int32_t dtype,
-                                     float* dst) {
+// dst[c][r] = bf16(src[r][c]) for r < rows, zero for rows <= r < ld (src in
+// `dtype`, [rows][cols]; dst [cols][ld]).
+__global__ void transpose_bf16_kernel(const void* src, int32_t rows, int32_t cols, int32_t dtype,
+                                      int32_t ld, uint16_t* dst) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (int64_t)rows * cols) return;
-  const int32_t r = idx % rows;
-  const int32_t c = idx / rows;
-  dst[idx] = load_as_f32(src, (int64_t)r * cols + c, dtype);
+  if (idx >= (int64_t)cols * ld) return;
+  const int32_t r = idx % ld;
+  const int32_t c = idx / ld;
+  dst[idx] = r < rows ? bf16_bits(load_as_f32(src, (int64_t)r * cols + c, dtype)) : uint16_t(0);
 }
 
-// du[h][d], dv[h][d] = sums over batch rows and 32-query chunks, in order.
-__global__ void duv_reduce_kernel(const float* part, int32_t B, int32_t H, int32_t nchunk,
-                                  int32_t dh, float* du, float* dv) {
-  const int32_t idx = blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= 2 * H * dh) return;
-  const int32_t which = idx / (H * dh);
-  const int32_t hd = idx % (H * dh);
-  const int32_t h = hd / dh, d = hd % dh;
+// du[h][d], dv[h][d] = sums over batch rows and 32-query chunks.  One
+// workgroup per (which, h, 8 columns): 32 strided partial sums per column,
+// then a fixed-order tree.
+__global__ __launch_bounds__(256) void duv_reduce_kernel(const float* part, int32_t B, int32_t H,
+                                                         int32_t nchunk, int32_t dh, float* du,
+                                                         float* dv) {
+  __shared__ float red[32][8];
+  const int32_t nblk = (dh + 7) / 8;
+  const int32_t which = blockIdx.x / (H * nblk);
+  const int32_t rest = blockIdx.x % (H * nblk);
+  const int32_t h = rest / nblk, d0 = 8 * (rest % nblk);
+  const int tid = threadIdx.x, dd = tid & 7, grp = tid >> 3;
+  const int32_t n = B * nchunk;
   float s = 0.0f;
-  for (int32_t b = 0; b < B; ++b)
-    for (int32_t c = 0; c < nchunk; ++c)
-      s += part[((((int64_t)which * B + b) * H + h) * nchunk + c) * DP + d];
-  (which == 0 ? du : dv)[hd] = s;
+  for (int32_t p = grp; p < n; p += 32) {
+    const int32_t bb = p / nchunk, c = p % nchunk;
+    s += part[((((int64_t)which * B + bb) * H + h) * nchunk + c) * DP + d0 + dd];
+  }
+  red[grp][dd] = s;
+  __syncthreads();
+  for (int w = 16; w > 0; w >>= 1) {
+    if (grp < w) red[grp][dd] += red[grp + w][dd];
+    __syncthreads();
+  }
+  if (tid < 8 && d0 + tid < dh) (which == 0 ? du : dv)[(int64_t)h * dh + d0 + tid] = red[0][tid];
+}
+
+// dst[x] = sum_r src[r][x] over n_rows rows of length row_len, in row order.
+__global__ void sum_rows_kernel(const float* src, int32_t n_rows, int64_t row_len, float* dst) {
+  const int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (x >= row_len) return;
+  float s = 0.0f;
+  for (int32_t r = 0; r < n_rows; ++r) s += src[(int64_t)r * row_len + x];
+  dst[x] = s;
 }
 
 dim3 grid_for(int64_t n) { return dim3((unsigned)((n + 255) / 256)); }
@@ -457,7 +598,8 @@ int launch_bmm64(const BmmArgs& a, void* stream) {
 }
 
 int launch_bwd_prep(const BwdPrepArgs& a, void* stream) {
-  hipLaunchKernelGGL(bwd_prep_kernel, grid_for((int64_t)a.B * a.H * a.Lp), dim3(256), 0,
+  const int32_t nch = (a.Lp + 63) / 64;
+  hipLaunchKernelGGL(bwd_prep_kernel, dim3(a.B * a.H * nch), dim3(256), 0,
                      static_cast<hipStream_t>(stream), a);
   return static_cast<int>(hipGetLastError());
 }
@@ -470,16 +612,23 @@ int launch_rk_transpose(const void* rk_ws, void* rkt, int32_t H, int32_t Pp, int
   return static_cast<int>(hipGetLastError());
 }
 
-int launch_transpose_f32(const void* src, int32_t rows, int32_t cols, int32_t dtype, float* dst,
-                         void* stream) {
-  hipLaunchKernelGGL(transpose_f32_kernel, grid_for((int64_t)rows * cols), dim3(256), 0,
-                     static_cast<hipStream_t>(stream), src, rows, cols, dtype, dst);
+int launch_transpose_bf16(const void* src, int32_t rows, int32_t cols, int32_t dtype, int32_t ld,
+                          void* dst, void* stream) {
+  hipLaunchKernelGGL(transpose_bf16_kernel, grid_for((int64_t)cols * ld), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), src, rows, cols, dtype, ld,
+                     static_cast<uint16_t*>(dst));
+  return static_cast<int>(hipGetLastError());
+}
+
+int launch_sum_rows(const float* src, int32_t n_rows, int64_t row_len, float* dst, void* stream) {
+  hipLaunchKernelGGL(sum_rows_kernel, grid_for(row_len), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), src, n_rows, row_len, dst);
   return static_cast<int>(hipGetLastError());
 }
 
 int launch_duv_reduce(const float* part, int32_t B, int32_t H, int32_t nchunk, int32_t dh,
                       float* du, float* dv, void* stream) {
-  hipLaunchKernelGGL(duv_reduce_kernel, grid_for(2 * H * dh), dim3(256), 0,
+  hipLaunchKernelGGL(duv_reduce_kernel, dim3(2 * H * ((dh + 7) / 8)), dim3(256), 0,
                      static_cast<hipStream_t>(stream), part, B, H, nchunk, dh, du, dv);
   return static_cast<int>(hipGetLastError());
 }

@@ -265,8 +265,9 @@ int launch_bmm64(const BmmArgs& a, void* stream);
 int launch_bwd_prep(const BwdPrepArgs& a, void* stream);
 int launch_rk_transpose(const void* rk_ws, void* rkt, int32_t H, int32_t Pp, int32_t pad_ws,
                         int32_t ld, int32_t pad_t, void* stream);
-int launch_transpose_f32(const void* src, int32_t rows, int32_t cols, int32_t dtype, float* dst,
-                         void* stream);
+int launch_transpose_bf16(const void* src, int32_t rows, int32_t cols, int32_t dtype, int32_t ld,
+                          void* dst, void* stream);
+int launch_sum_rows(const float* src, int32_t n_rows, int64_t row_len, float* dst, void* stream);
 int launch_duv_reduce(const float* part, int32_t B, int32_t H, int32_t nchunk, int32_t dh,
                       float* du, float* dv, void* stream);
 int launch_repack_rk(const void* rk_pub, void* rk_ws, int32_t P, int32_t Pp, int32_t pad, int32_t H,
