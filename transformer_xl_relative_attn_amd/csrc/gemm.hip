@@ -5,9 +5,10 @@
 //   that h~ = [memory ring ; segment] is gathered on the fly.
 //
 // gemm_bf16: bf16 operands, fp32 accumulation on the gfx950 matrix cores
-//   (v_mfma_f32_32x32x16_bf16).  256x256 block tile, 4 waves in a 2x2 grid,
-//   each wave owns a 128x128 sub-tile (4x4 MFMA tiles, 256 accumulator
-//   registers).  Operands stream through an NSTAGE-deep LDS ring of 32-wide
+//   (v_mfma_f32_32x32x16_bf16).  256x256 block tile, 8 waves in a 2x4 grid
+//   (two per SIMD), each wave owns a 128x64 sub-tile (4x2 MFMA tiles, 128
+//   accumulator registers); groups with few tiles use 128x128 blocks of 4
+//   waves, two workgroups per CU.  Operands stream through an NSTAGE-deep LDS ring of 32-wide
 //   K steps filled by direct global->LDS loads (no register staging), issued
 //   NSTAGE-1 K steps ahead of their use; MFMA operand reads and refill loads
 //   are spread evenly between the MFMAs.  Persistent: one workgroup per CU
@@ -24,28 +25,39 @@ namespace txl {
 
 namespace {
 
-constexpr int BK = 32, NT = 256;
+constexpr int BK = 32;
 #ifndef TXL_GEMM_NSTAGE
 #define TXL_GEMM_NSTAGE 3
 #endif
 constexpr int CH = BK / 8;               // 16-byte chunks per tile row (4)
 
-// Block-tile variants: WT x WT MFMA tiles of 32x32 per wave, 2x2 waves.
-//   WT = 4: 256x256 block, one workgroup per CU (large problems);
-//   WT = 2: 128x128 block, two workgroups per CU (problems with fewer
-//           256-tiles than compute units).
-template <int WT>
-struct Tile {
-  static constexpr int BM = 64 * WT;            // block tile rows = columns
-  static constexpr int WTILE = 32 * WT;         // wave tile
-  static constexpr int TILE_U = BM * CH;        // 16-byte units per operand tile
-  static constexpr int STAGE_U = 2 * TILE_U;    // A tile then B tile
-  static constexpr int LOADS = TILE_U / NT;     // LDS-DMA loads per thread per operand
-  static constexpr int NSTAGE = WT == 4 ? TXL_GEMM_NSTAGE : 4;   // LDS ring depth
-  static constexpr int CPR = 4 * WT;            // 16-byte chunks per staged output row
-  static constexpr int EPI_U = 32 * CPR;        // 16-byte units of a wave's staging region
-  static constexpr int WAVES_PER_SIMD = WT == 4 ? 1 : 2;
+// Block-tile variants: WM x WN MFMA tiles of 32x32 per wave, GM x GN waves,
+// square blocks (BM == BN), NSTAGE-deep LDS ring, OCC workgroups per CU.
+template <int WM_, int WN_, int GM_, int GN_, int NSTAGE_, int OCC_>
+struct Var {
+  static constexpr int WM = WM_, WN = WN_, GM = GM_, GN = GN_;
+  static constexpr int NW = GM * GN;              // waves per workgroup
+  static constexpr int NTH = 64 * NW;             // threads
+  static constexpr int WTM = 32 * WM, WTN = 32 * WN;   // wave tile
+  static constexpr int BM = WTM * GM, BN = WTN * GN;   // block tile
+  static_assert(BM == BN, "square block tiles");
+  static constexpr int TILE_U = BM * CH;          // 16-byte units per operand tile
+  static constexpr int STAGE_U = 2 * TILE_U;      // A tile then B tile
+  static constexpr int LOADS = TILE_U / NTH;      // LDS-DMA loads per thread per operand
+  static constexpr int NSTAGE = NSTAGE_;          // LDS ring depth
+  static constexpr int CPR = 4 * WN;              // 16-byte chunks per staged output row
+  static constexpr int EPI_U = 32 * CPR;          // 16-byte units of a wave's staging region
+  static constexpr int OCC = OCC_;
 };
+//   V256W8: 256x256, 8 waves of 128x64 (two per SIMD: while one waits on the
+//           barrier or its LDS reads the other keeps the matrix core busy),
+//           one workgroup per CU (large problems).  Measured against 4 waves of
+//           128x128 on the same LDS ring: 70 vs 75 us on the eval-shaped
+//           projections, 118 vs 121 us at 4096^3.
+//   V128:   128x128, 4 waves of 64x64, two workgroups per CU (problems with
+//           few 256-tiles)
+using V256W8 = Var<4, 2, 2, 4, TXL_GEMM_NSTAGE, 1>;
+using V128 = Var<2, 2, 2, 2, 4, 2>;
 
 // 128 bytes of zeros: the source of every "zero row" chunk (padding rows).
 __device__ __align__(16) uint32_t g_zero_chunk[32];
@@ -80,26 +92,27 @@ __device__ __forceinline__ void barrier_lds() {
 
 // Vectorised epilogue: four consecutive output columns per store.  FLAGS < 0
 // means "read the residual / ReLU flags at run time".
-template <int WT, int DTYPE, int FLAGS>
-__device__ __forceinline__ void epilogue_vec(const OutDst& o, const floatx16 (&acc)[WT][WT],
+template <class V, int DTYPE, int FLAGS>
+__device__ __forceinline__ void epilogue_vec(const OutDst& o, const floatx16 (&acc)[V::WM][V::WN],
                                              int32_t mb, int32_t nb) {
+  constexpr int WM = V::WM, WN = V::WN;
   const int flags = FLAGS < 0 ? o.flags : FLAGS;
-  int64_t roff[WT];
-  bool mok[WT];
+  int64_t roff[WM];
+  bool mok[WM];
 #pragma unroll
-  for (int i = 0; i < WT; ++i) {
+  for (int i = 0; i < WM; ++i) {
     mok[i] = mb + 32 * i < o.m_valid;
     roff[i] = axis_off(o.row, mb + 32 * i);
   }
 #pragma unroll
-  for (int j = 0; j < WT; ++j)
+  for (int j = 0; j < WN; ++j)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int32_t n = nb + 32 * j + 8 * g;
       if (n >= o.n_valid) continue;
       const int64_t coff = col_off(o, n);
 #pragma unroll
-      for (int i = 0; i < WT; ++i) {
+      for (int i = 0; i < WM; ++i) {
         if (!mok[i]) continue;
         const int64_t off = roff[i] + coff;
         floatx4 v = floatx4{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
@@ -123,7 +136,7 @@ __device__ __forceinline__ void epilogue_vec(const OutDst& o, const floatx16 (&a
     }
 }
 
-// bf16 output without residual / activation: the wave's WTILE x WTILE
+// bf16 output without residual / activation: the wave's WTM x WTN
 // sub-tile (rows mw.., columns nw..) passes through the wave's own LDS region
 // in rounds of 32 rows, so that the global stores write whole lines (CPR
 // lanes cover one output row of the sub-tile contiguously) instead of
@@ -133,13 +146,14 @@ __device__ __forceinline__ void epilogue_vec(const OutDst& o, const floatx16 (&a
 // r (0..31) is CPR chunks of 16 bytes, chunk c at slot c ^ (r % CPR); both the
 // 8-byte writes (32 rows x 2 halves) and the 16-byte reads (CPR lanes per row)
 // are then spread over all 64 banks.
-template <int WT>
-__device__ __forceinline__ void epilogue_staged(const OutDst& o, const floatx16 (&acc)[WT][WT],
-                                                int32_t mw, int32_t nw, int lane,
-                                                u32x4* region) {
+template <class V>
+__device__ __forceinline__ void epilogue_staged(const OutDst& o,
+                                                const floatx16 (&acc)[V::WM][V::WN], int32_t mw,
+                                                int32_t nw, int lane, u32x4* region) {
+  constexpr int WM = V::WM, WN = V::WN;
   typedef float floatx2_t __attribute__((ext_vector_type(2)));
   typedef bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-  constexpr int CPR = Tile<WT>::CPR;     // chunks (lanes) per row
+  constexpr int CPR = V::CPR;            // chunks (lanes) per row
   constexpr int RG = 64 / CPR;           // rows per store instruction
   constexpr int NR = 32 / RG;            // store instructions per round
   char* base = reinterpret_cast<char*>(region);
@@ -158,9 +172,9 @@ __device__ __forceinline__ void epilogue_staged(const OutDst& o, const floatx16 
   const int64_t step = RG * o.row.s2, wrap = o.row.s1 - (int64_t)o.row.div * o.row.s2;
   uint16_t* out = static_cast<uint16_t*>(o.p);
 #pragma unroll
-  for (int i = 0; i < WT; ++i) {
+  for (int i = 0; i < WM; ++i) {
 #pragma unroll
-    for (int j = 0; j < WT; ++j)
+    for (int j = 0; j < WN; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int cc = 4 * j + q;   // columns 32j + 8q + 4*lhalf .. +3
@@ -198,28 +212,28 @@ __device__ __forceinline__ void epilogue_staged(const OutDst& o, const floatx16 
 // swapped (B fragment first), so block (i, j) holds C^T: element 4g + r of a
 // lane is C[m][n] with m = mb + 32i and n = nb + 32j + 8g + r, i.e. four
 // consecutive output columns of one row per (i, j, g).
-template <int WT>
-__device__ __forceinline__ void epilogue(const GemmProblem& P, const floatx16 (&acc)[WT][WT],
+template <class V>
+__device__ __forceinline__ void epilogue(const GemmProblem& P, const floatx16 (&acc)[V::WM][V::WN],
                                          int32_t m0, int32_t n0, int wm, int wn, int lane,
                                          u32x4* smem) {
-  constexpr int WTILE = Tile<WT>::WTILE, EPI_U = Tile<WT>::EPI_U;
-  const int lrow = lane & 31, lhalf = lane >> 5, wave = wm * 2 + wn;
+  constexpr int WM = V::WM, WN = V::WN, WTM = V::WTM, WTN = V::WTN, EPI_U = V::EPI_U;
+  const int lrow = lane & 31, lhalf = lane >> 5, wave = wm * V::GN + wn;
   const OutDst& o = P.out;
-  const int32_t mb = m0 + wm * WTILE + lrow;
-  const int32_t nb = n0 + wn * WTILE + 4 * lhalf;
+  const int32_t mb = m0 + wm * WTM + lrow;
+  const int32_t nb = n0 + wn * WTN + 4 * lhalf;
   if (o.vec8_ok && o.flags == 0) {
-    epilogue_staged<WT>(o, acc, m0 + wm * WTILE, n0 + wn * WTILE, lane, smem + wave * EPI_U);
+    epilogue_staged<V>(o, acc, m0 + wm * WTM, n0 + wn * WTN, lane, smem + wave * EPI_U);
     return;
   }
   if (o.vec_ok) {
     if (o.flags == 0 && o.dtype == TXL_BF16)
-      epilogue_vec<WT, TXL_BF16, 0>(o, acc, mb, nb);
+      epilogue_vec<V, TXL_BF16, 0>(o, acc, mb, nb);
     else if (o.flags == 0)
-      epilogue_vec<WT, TXL_F32, 0>(o, acc, mb, nb);
+      epilogue_vec<V, TXL_F32, 0>(o, acc, mb, nb);
     else if (o.dtype == TXL_BF16)
-      epilogue_vec<WT, TXL_BF16, -1>(o, acc, mb, nb);
+      epilogue_vec<V, TXL_BF16, -1>(o, acc, mb, nb);
     else
-      epilogue_vec<WT, TXL_F32, -1>(o, acc, mb, nb);
+      epilogue_vec<V, TXL_F32, -1>(o, acc, mb, nb);
     return;
   }
   // Rare layouts (unaligned or odd leading dimension): one element at a time
@@ -230,9 +244,9 @@ __device__ __forceinline__ void epilogue(const GemmProblem& P, const floatx16 (&
   float* stage = reinterpret_cast<float*>(smem + wave * EPI_U);
   auto at = [](int ml, int nl) { return ml * 32 + ((nl + ml) & 31); };
 #pragma unroll
-  for (int i = 0; i < WT; ++i) {
+  for (int i = 0; i < WM; ++i) {
 #pragma unroll
-    for (int j = 0; j < WT; ++j) {
+    for (int j = 0; j < WN; ++j) {
       const floatx16 a = acc[i][j];
 #pragma unroll
       for (int e = 0; e < 16; ++e) stage[at(lrow, 8 * (e >> 2) + 4 * lhalf + (e & 3))] = a[e];
@@ -240,8 +254,8 @@ __device__ __forceinline__ void epilogue(const GemmProblem& P, const floatx16 (&
       // stage[m_local][n_local] for m = mb - lrow + m_local, n = nb - 4*lhalf + 32j + n_local
       for (int t = lane; t < 32 * 32; t += 64) {
         const int ml = t >> 5, nl = t & 31;
-        const int32_t m = m0 + wm * WTILE + 32 * i + ml;
-        const int32_t n = n0 + wn * WTILE + 32 * j + nl;
+        const int32_t m = m0 + wm * WTM + 32 * i + ml;
+        const int32_t n = n0 + wn * WTN + 32 * j + nl;
         if (m < o.m_valid && n < o.n_valid)
           epi_store(o, axis_off(o.row, m) + col_off(o, n), stage[at(ml, nl)]);
       }
@@ -250,11 +264,11 @@ __device__ __forceinline__ void epilogue(const GemmProblem& P, const floatx16 (&
   }
 }
 
-template <int WT>
+template <class V>
 __device__ __forceinline__ void gemm_bf16_body(const GemmGroup& g, int32_t padded, int32_t grid) {
-  using T = Tile<WT>;
-  constexpr int BM = T::BM, BN = T::BM, WTILE = T::WTILE, TILE_U = T::TILE_U,
-                STAGE_U = T::STAGE_U, LOADS = T::LOADS, NSTAGE = T::NSTAGE, EPI_U = T::EPI_U;
+  constexpr int WM = V::WM, WN = V::WN, NW = V::NW, BM = V::BM, BN = V::BN, WTM = V::WTM,
+                WTN = V::WTN, TILE_U = V::TILE_U, STAGE_U = V::STAGE_U, LOADS = V::LOADS,
+                NSTAGE = V::NSTAGE, EPI_U = V::EPI_U;
   // LDS ring: stage s holds A rows [0,BM) then B rows [0,BN), each row 4
   // chunks of 16 bytes; chunk c of row r is stored at slot c ^ ((r >> 2) & 3).
   // gfx950 serves a 16-byte read for 16 lanes at a time from 64 four-byte
@@ -263,17 +277,17 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmGroup& g, int32_t padde
   // the per-wave epilogue staging follows the ring in the same LDS object
   // (a second object defeats the compiler's LDS-DMA alias tracking, which
   // then waits for every load before each LDS read)
-  __shared__ u32x4 smem[NSTAGE * STAGE_U + 4 * EPI_U];
+  __shared__ u32x4 smem[NSTAGE * STAGE_U + NW * EPI_U];
   u32x4* const stage_out = smem + NSTAGE * STAGE_U;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / V::GN, wn = wave % V::GN;
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
 
-  // LDS-DMA mapping: load i of this wave fills units [(4i + wave)*64, +64) of a
-  // tile, i.e. row (4i + wave)*16 + lane/4, slot lane%4, which holds global
-  // chunk (lane%4) ^ ((row >> 2) & 3) = (lane%4) ^ ((lane >> 4) & 3).
+  // LDS-DMA mapping: load i of this wave fills units [(NW*i + wave)*64, +64)
+  // of a tile, i.e. row (NW*i + wave)*16 + lane/4, slot lane%4, which holds
+  // global chunk (lane%4) ^ ((row >> 2) & 3) = (lane%4) ^ ((lane >> 4) & 3).
   const int gchunk = (lane & 3) ^ ((lane >> 4) & 3);
   const char* zero = reinterpret_cast<const char*>(g_zero_chunk) + gchunk * 16;
 
@@ -305,7 +319,7 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmGroup& g, int32_t padde
     nk = P.K / BK;
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
-      const int r = (4 * i + wave) * 16 + (lane >> 2);
+      const int r = (NW * i + wave) * 16 + (lane >> 2);
       const char* a = (m0 + r < P.M) ? row_address(P.a, m0 + r, 2) : nullptr;
       const char* b = (n0 + r < P.N) ? row_address(P.b, n0 + r, 2) : nullptr;
       pa[i] = a ? a + gchunk * 16 : zero;
@@ -323,10 +337,10 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmGroup& g, int32_t padde
   auto issue_one = [&](u32x4* st, int q, bool real) {
     const int i = q >> 1;
     if (q & 1) {
-      __builtin_amdgcn_global_load_lds(real ? pb[i] : zero, st + 4 * i * 64 + TILE_U, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(real ? pb[i] : zero, st + NW * i * 64 + TILE_U, 16, 0, 0);
       pb[i] += sb[i];
     } else {
-      __builtin_amdgcn_global_load_lds(real ? pa[i] : zero, st + 4 * i * 64, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(real ? pa[i] : zero, st + NW * i * 64, 16, 0, 0);
       pa[i] += sa[i];
     }
   };
@@ -334,59 +348,59 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmGroup& g, int32_t padde
 
   const int lrow = lane & 31, lhalf = lane >> 5;
   const int sw = (lrow >> 2) & 3;  // same for every fragment row of a lane
-  int fa[WT], fb[WT];              // fragment row base (16-byte units) within a stage
+  int fa[WM], fb[WN];              // fragment row base (16-byte units) within a stage
 #pragma unroll
-  for (int i = 0; i < WT; ++i) {
-    fa[i] = (wm * WTILE + i * 32 + lrow) * CH;
-    fb[i] = TILE_U + (wn * WTILE + i * 32 + lrow) * CH;
-  }
-  // fragment f (0..WT-1: A rows 32f.., WT..2WT-1: B rows 32(f-WT)..) of k-step
-  // s (0 or 1) of a staged 32-wide K step
+  for (int i = 0; i < WM; ++i) fa[i] = (wm * WTM + i * 32 + lrow) * CH;
+#pragma unroll
+  for (int j = 0; j < WN; ++j) fb[j] = TILE_U + (wn * WTN + j * 32 + lrow) * CH;
+  // fragment f (0..WM-1: A rows 32f.., WM..WM+WN-1: B rows 32(f-WM)..) of
+  // k-step s (0 or 1) of a staged 32-wide K step
   auto read_one = [&](const u32x4* st, int s, int f, bf16x8* af, bf16x8* bfr) {
     const int c = (2 * s + lhalf) ^ sw;
-    if (f < WT)
+    if (f < WM)
       af[f] = __builtin_bit_cast(bf16x8, st[fa[f] + c]);
     else
-      bfr[f - WT] = __builtin_bit_cast(bf16x8, st[fb[f - WT] + c]);
+      bfr[f - WM] = __builtin_bit_cast(bf16x8, st[fb[f - WM] + c]);
   };
-  floatx16 acc[WT][WT];
+  floatx16 acc[WM][WN];
   auto mfma_one = [&](int x, const bf16x8* af, const bf16x8* bfr) {
-    const int i = x / WT, j = x % WT;
+    const int i = x / WN, j = x % WN;
     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
   };
 
   // One K step (ring slot `slot`, 32 wide = two MFMA k-steps), in two halves
   // whose instruction order is fixed with scheduling fences:
-  //   A: WT*WT MFMAs on k-step 0 (fragments F0, already in registers); the
-  //      k-step 1 fragments F1 are read during the first 2*WT;
+  //   A: WM*WN MFMAs on k-step 0 (fragments F0, already in registers); the
+  //      k-step 1 fragments F1 are read during the first WM+WN;
   //   wait until K step kt+1 has landed (`vm` loads may stay in flight),
   //   barrier: every wave is done with this slot;
-  //   B: WT*WT MFMAs on F1, interleaved with the 2*LOADS refill loads of this
+  //   B: WM*WN MFMAs on F1, interleaved with the 2*LOADS refill loads of this
   //      slot (K step kt+NSTAGE; zero chunk if that is past the end) and, in
   //      the first half of them, the reads of K step kt+1's F0.
   // Spreading the loads and reads evenly keeps the single wave per SIMD
   // issuing MFMAs back to back.  (In the last step the F0 read is of a stale
   // slot and unused.)
-  bf16x8 f0a[WT], f0b[WT], f1a[WT], f1b[WT];
+  bf16x8 f0a[WM], f0b[WN], f1a[WM], f1b[WN];
+  constexpr int NF = WM + WN;             // fragments per k-step
   constexpr int NQ = 2 * LOADS;           // refill loads per wave and K step
-  constexpr int MPQ = WT * WT / NQ;       // MFMAs per refill load
-  static_assert(MPQ * NQ == WT * WT, "MFMAs split evenly between the loads");
+  constexpr int MPQ = WM * WN / NQ;       // MFMAs per refill load
+  static_assert(MPQ * NQ == WM * WN, "MFMAs split evenly between the loads");
   auto kstep = [&](int slot, int nslot, bool refill) {
     const u32x4* st = stage_ptr(slot);
 #pragma unroll
-    for (int x = 0; x < WT * WT; ++x) {
+    for (int x = 0; x < WM * WN; ++x) {
       mfma_one(x, f0a, f0b);
-      if (x < 2 * WT) read_one(st, 1, x, f1a, f1b);
+      if (x < NF) read_one(st, 1, x, f1a, f1b);
       __builtin_amdgcn_sched_barrier(0);
     }
     wait_vm<(NSTAGE - 2) * 2 * LOADS>();
     barrier_lds();
     u32x4* rs = smem + slot * STAGE_U + wave_s * 64;
     const u32x4* nst = stage_ptr(nslot);
-    // F0 reads in the order the next MFMAs consume them (A0, B0..B(WT-1),
-    // A1..A(WT-1)), all in the first half so that they have landed when the
+    // F0 reads in the order the next MFMAs consume them (A0, B0..B(WN-1),
+    // A1..A(WM-1)), all in the first half so that they have landed when the
     // next step starts
-    constexpr int RPQ = (2 * WT + NQ / 2 - 1) / (NQ / 2);   // reads per load
+    constexpr int RPQ = (NF + NQ / 2 - 1) / (NQ / 2);   // reads per load
 #pragma unroll
     for (int q = 0; q < NQ; ++q) {
 #pragma unroll
@@ -395,7 +409,7 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmGroup& g, int32_t padde
 #pragma unroll
       for (int r = 0; r < RPQ; ++r) {
         const int k = RPQ * q + r;   // k-th fragment in consumption order
-        if (k < 2 * WT) read_one(nst, 0, k == 0 ? 0 : k <= WT ? WT + k - 1 : k - WT, f0a, f0b);
+        if (k < NF) read_one(nst, 0, k == 0 ? 0 : k <= WN ? WM + k - 1 : k - WN, f0a, f0b);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -416,9 +430,9 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmGroup& g, int32_t padde
 
   while (true) {
 #pragma unroll
-    for (int i = 0; i < WT; ++i)
+    for (int i = 0; i < WM; ++i)
 #pragma unroll
-      for (int j = 0; j < WT; ++j) acc[i][j] = floatx16{0};
+      for (int j = 0; j < WN; ++j) acc[i][j] = floatx16{0};
 
     // Loads return in order and every step issues exactly one stage, so the
     // wait counts are fixed: K step 0 has landed once at most NSTAGE-1 stages
@@ -430,7 +444,7 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmGroup& g, int32_t padde
     {
       const u32x4* st = stage_ptr(0);
 #pragma unroll
-      for (int f = 0; f < 2 * WT; ++f) read_one(st, 0, f, f0a, f0b);
+      for (int f = 0; f < NF; ++f) read_one(st, 0, f, f0a, f0b);
     }
     int slot = 0;
 #pragma unroll 1
@@ -452,23 +466,24 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmGroup& g, int32_t padde
       setup(xcd_swizzle(seq, padded));
       prologue();
     }
-    epilogue<WT>(g.p[cpidx], acc, cm0, cn0, wm, wn, lane, stage_out);
+    epilogue<V>(g.p[cpidx], acc, cm0, cn0, wm, wn, lane, stage_out);
     if (!more) break;
   }
   // no LDS-DMA may still be writing when the workgroup exits
   wait_vm<0>();
 }
 
-// 256x256 blocks, one workgroup per CU
-__global__ __launch_bounds__(NT, 1) void gemm_bf16_kernel(GemmGroup g, int32_t padded,
-                                                          int32_t grid) {
-  gemm_bf16_body<4>(g, padded, grid);
+// 256x256 blocks of 8 waves (two per SIMD), one workgroup per CU
+__global__ __launch_bounds__(V256W8::NTH, 1) void gemm_bf16_kernel(GemmGroup g, int32_t padded,
+                                                                   int32_t grid) {
+  gemm_bf16_body<V256W8>(g, padded, grid);
 }
 
 // 128x128 blocks, two workgroups per CU
-__global__ __launch_bounds__(NT, 2) void gemm_bf16_t128_kernel(GemmGroup g, int32_t padded,
-                                                               int32_t grid) {
-  gemm_bf16_body<2>(g, padded, grid);
+__global__ __launch_bounds__(V128::NTH, 2) void gemm_bf16_t128_kernel(GemmGroup g,
+                                                                      int32_t padded,
+                                                                      int32_t grid) {
+  gemm_bf16_body<V128>(g, padded, grid);
 }
 
 // ------------------------------------------------------------------ fp32 GEMM
@@ -552,17 +567,17 @@ int launch_tiles(const GemmGroup& g, bool small, void* stream) {
   // a multiple of 8 (the XCD count)
   int32_t grid = (device_cu_count() * (small ? 2 : 1) + 7) & ~7;
   if (grid > padded) grid = padded;
+  hipStream_t st = static_cast<hipStream_t>(stream);
   if (small)
-    hipLaunchKernelGGL(gemm_bf16_t128_kernel, dim3(grid), dim3(NT), 0,
-                       static_cast<hipStream_t>(stream), g, padded, grid);
+    hipLaunchKernelGGL(gemm_bf16_t128_kernel, dim3(grid), dim3(V128::NTH), 0, st, g, padded, grid);
   else
-    hipLaunchKernelGGL(gemm_bf16_kernel, dim3(grid), dim3(NT), 0,
-                       static_cast<hipStream_t>(stream), g, padded, grid);
+    hipLaunchKernelGGL(gemm_bf16_kernel, dim3(grid), dim3(V256W8::NTH), 0, st, g, padded, grid);
   return static_cast<int>(hipGetLastError());
 }
 
-// The group arrives tiled for 256x256 blocks.  A group with fewer such tiles
-// than compute units is re-tiled for 128x128 blocks (two workgroups per CU).
+// The group arrives tiled for 256x256 blocks.  A group with no more such
+// tiles than half the compute units is re-tiled for 128x128 blocks (two
+// workgroups per CU).
 int launch_gemm_bf16(const GemmGroup& g, void* stream) {
   if (g.total_tiles <= 0) return 0;
   if (2 * g.total_tiles > device_cu_count()) return launch_tiles(g, false, stream);
