@@ -167,67 +167,95 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_q_kernel(BwdArgs a) {
     rk_rows(M + i0 - 31 + 32, rf);
     upper = bd_chunk(rf);
   }
-  uint16_t* ptp = static_cast<uint16_t*>(a.pt) + (int64_t)bh * Np * Lp + i;
-  uint16_t* dstp = static_cast<uint16_t*>(a.dst) + (int64_t)bh * Np * Lp + i;
+  // P^T, dS^T rows are written as bf16 pairs of queries (2i', 2i'+1): the even
+  // lane of a pair stores one key, the odd lane the next
+  uint32_t* ptp = reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.pt) +
+                                              (int64_t)bh * Np * Lp + (i & ~1));
+  uint32_t* dstp = reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.dst) +
+                                               (int64_t)bh * Np * Lp + (i & ~1));
+  const bool odd = ii & 1;
   const int64_t rkt_row0 = (int64_t)head * DP * a.rkt_ld + a.rkt_pad;
 
-  // operands of the scores and dP^T of a block (loaded one block ahead)
-  struct Frags {
-    bf16x8 kf[4], vf[4], rf[4];
-  };
-  auto load_frags = [&](int32_t t, Frags& f) {
+  // operand fragments of a block, each group reloaded for the next block as
+  // soon as this block has consumed it: K, val and Rk rows (scores, dP^T),
+  // K^T tile (rows d = 32e + ii, keys 16t2 + 8hf ..) and the Rk^T window
+  // (rows d, window positions 16s + 8hf ..)
+  bf16x8 kf[4], vf[4], rf[4], ktf[2][2], rtf[2][4];
+  auto load_rows = [&](int32_t t) {
     const int32_t j0 = t * KB;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      f.kf[s] = load8(a.k, ((int64_t)bh * Np + j0 + ii) * DP + 16 * s + 8 * hf);
-      f.vf[s] = load8(a.vn, ((int64_t)bh * Np + j0 + ii) * DP + 16 * s + 8 * hf);
+      kf[s] = load8(a.k, ((int64_t)bh * Np + j0 + ii) * DP + 16 * s + 8 * hf);
+      vf[s] = load8(a.vn, ((int64_t)bh * Np + j0 + ii) * DP + 16 * s + 8 * hf);
     }
-    rk_rows(M + i0 - 32 * t - 31, f.rf);
+    rk_rows(M + i0 - 32 * t - 31, rf);
   };
-
-  Frags cf;
-  auto block = [&](int32_t t) {
-    const int32_t j0 = t * KB;
-    const int32_t base = M + i0 - 32 * t - 31;
-    const bf16x8 (&kf)[4] = cf.kf;   // overwritten by the next block's load once used
-    const bf16x8 (&vf)[4] = cf.vf;
-    const bf16x8 (&rf)[4] = cf.rf;
-    // K^T tile fragments (rows d = 32e + ii, keys 16t2 + 8hf ..) and the Rk^T
-    // window (rows d, window positions 16s + 8hf ..), used later in the block
-    bf16x8 ktf[2][2], rtf[2][4];
+  auto load_kt = [&](int32_t t) {
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
+    for (int e = 0; e < 2; ++e)
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2)
         ktf[t2][e] = load8(a.kt, ((((int64_t)b * nkb + t) * a.H + head) * DP + 32 * e + ii) * KB +
                                      16 * t2 + 8 * hf);
+  };
+  auto load_rt = [&](int32_t t) {
+    const int32_t base = M + i0 - 32 * t - 31;
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
 #pragma unroll
       for (int s = 0; s < 4; ++s)
         rtf[e][s] = load8(a.rkt, rkt_row0 + (int64_t)(32 * e + ii) * a.rkt_ld + base + 16 * s + 8 * hf);
-    }
+  };
+
+  // scores and dP^T of block t from the row fragments (which are then free
+  // for the next block's load); `upper` holds the chunk product of rows
+  // base_t + 32 .. +63 and receives that of base_t .. +31
+  floatx16 S, dpt;
+  auto scores = [&](int32_t t, floatx16& So, floatx16& dpo) {
     const floatx16 lower = bd_chunk(rf);
+    dpo = floatx16{0};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) dpo = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[s], go[s], dpo, 0, 0, 0);
     write_win(lower, upper);
     wave_lds_fence();
-    floatx16 S = read_win();
+    So = read_win();
 #pragma unroll
-    for (int s = 0; s < 4; ++s) S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qu[s], S, 0, 0, 0);
-    floatx16 dpt = floatx16{0};
-#pragma unroll
-    for (int s = 0; s < 4; ++s) dpt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[s], go[s], dpt, 0, 0, 0);
-    // this block's K, val and Rk fragments are consumed: the next block's load
-    // now, in flight during the rest of this block
-    if (t + 1 < t_end) load_frags(t + 1, cf);
+    for (int s = 0; s < 4; ++s) So = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qu[s], So, 0, 0, 0);
+    upper = lower;
+    if (t + 1 < t_end) load_rows(t + 1);
+  };
+
+  // Block t with its scores and dP^T already in S, dpt.  The next block's
+  // products are issued once this block's dS exists, so that they run on the
+  // matrix cores while this block's shifted-dS phase runs on LDS and VALU.
+  auto block = [&](int32_t t) {
+    const int32_t j0 = t * KB;
+    const int32_t base = M + i0 - 32 * t - 31;
+    const bool more = t + 1 < t_end;
     // P and dS; key jj = 8g + 4hf + r (element 4g + r) visible iff j0 + jj <= M + i
     const int32_t lim = M + i - j0 - 4 * hf;
     float ds[16];
+    uint32_t pb[16], db[16];
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int kk = 8 * (e >> 2) + (e & 3);
       const float p = (qok && kk <= lim) ? __builtin_amdgcn_exp2f(S[e] - lse) : 0.0f;
       ds[e] = p * (dpt[e] - dsum);
-      const int jj = kk + 4 * hf;
-      ptp[(int64_t)(j0 + jj) * Lp] = bf16_bits(p);
-      dstp[(int64_t)(j0 + jj) * Lp] = bf16_bits(ds[e]);
+      pb[e] = bf16_bits(p);
+      db[e] = bf16_bits(ds[e]);
+    }
+    // keys (e, e+1) of the query pair: the partner lane's two values arrive
+    // in one 32-bit exchange; the even lane stores key e, the odd key e+1
+#pragma unroll
+    for (int e = 0; e < 16; e += 2) {
+      const uint32_t pmine = pb[e] | (pb[e + 1] << 16), dmine = db[e] | (db[e + 1] << 16);
+      const uint32_t pnb = __builtin_amdgcn_update_dpp(0u, pmine, 0xB1, 0xF, 0xF, false);
+      const uint32_t dnb = __builtin_amdgcn_update_dpp(0u, dmine, 0xB1, 0xF, 0xF, false);
+      const int jj = 8 * (e >> 2) + (e & 3) + 4 * hf + (odd ? 1 : 0);
+      const uint32_t pw = odd ? (pnb >> 16) | (pmine & 0xffff0000u) : (pmine & 0xffffu) | (pnb << 16);
+      const uint32_t dw2 = odd ? (dnb >> 16) | (dmine & 0xffff0000u) : (dmine & 0xffffu) | (dnb << 16);
+      ptp[((int64_t)(j0 + jj) * Lp) >> 1] = pw;
+      dstp[((int64_t)(j0 + jj) * Lp) >> 1] = dw2;
     }
     // dq, k-part: K^T tile times dS^T (bf16 pairs exchanged with the partner
     // lane so that the operand lists keys 16t2 + 8hf .. +7 in order)
@@ -241,6 +269,9 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_q_kernel(BwdArgs a) {
       for (int e = 0; e < 2; ++e)
         dqk[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ktf[t2][e], dsb, dqk[e], 0, 0, 0);
     }
+    if (more) load_kt(t + 1);
+    floatx16 Sn, dptn;
+    if (more) scores(t + 1, Sn, dptn);
     // dS shifted by distance: window position r = 31 + ii - jj, rows base + r
     uint16_t* lo = halves + (t & 1) * (32 * 32);
     uint16_t* up = halves + ((t + 1) & 1) * (32 * 32);
@@ -273,12 +304,19 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_q_kernel(BwdArgs a) {
 #pragma unroll
       for (int s = 0; s < 4; ++s)
         dqr[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rtf[e][s], dw[s], dqr[e], 0, 0, 0);
+    if (more) load_rt(t + 1);
     // rows base + 32 .. +63 are complete (keys of blocks t-1 and t)
     flush_half(up, base + 32);
     wave_lds_fence();
-    upper = lower;
+    if (more) {
+      S = Sn;
+      dpt = dptn;
+    }
   };
-  load_frags(0, cf);
+  load_rows(0);
+  load_kt(0);
+  load_rt(0);
+  scores(0, S, dpt);
   for (int32_t t = 0; t < t_end; ++t) block(t);
   flush_half(halves + ((t_end - 1) & 1) * (32 * 32), M + i0 - 32 * (t_end - 1) - 31);
 
