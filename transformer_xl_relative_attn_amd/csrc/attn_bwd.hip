@@ -93,8 +93,12 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_q_kernel(BwdArgs a) {
       for (int e = 0; e < 8; ++e) {
         const int d = 16 * s + 8 * hf + e;
         const float qd = qrow[d];
-        const float uu = d < a.dh ? bf16_to_f32(up[d]) : 0.0f;
-        const float vv = d < a.dh ? bf16_to_f32(vp[d]) : 0.0f;
+        // clamped in-bounds element, selected after the load, so the loads
+        // issue together instead of one branch-and-wait each
+        const int dc = min(d, a.dh - 1);
+        const float ur = bf16_to_f32(up[dc]), vr = bf16_to_f32(vp[dc]);
+        const float uu = d < a.dh ? ur : 0.0f;
+        const float vv = d < a.dh ? vr : 0.0f;
         xu[e] = (qd + uu) * a.c_scale;
         xv[e] = (qd + vv) * a.c_scale;
       }
@@ -351,20 +355,31 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_q_kernel(BwdArgs a) {
 }
 
 // ------------------------------------------------------------------ bmm64
-// One wave per 32 rows of A, both 32-column halves of the output.  Operand
-// fragments come straight from global memory (rows are K-contiguous), one
-// 16-wide k-step ahead of the matrix-core products.
+// One wave per 64 rows of A (two 32-row tiles) and both 32-column halves of
+// the output: four matrix-core products per 16-wide k-step on fragments that
+// come straight from global memory (rows are K-contiguous), loaded a group of
+// G k-steps ahead.
+constexpr int BMM_RM = 2;            // 32-row tiles per wave
+constexpr int BMM_ROWS = 4 * 32 * BMM_RM;   // rows per workgroup
+
 __global__ __launch_bounds__(256) void bmm64_kernel(BmmArgs a) {
   const int32_t bi = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int ii = lane & 31, hf = lane >> 5;
-  const int32_t m0 = blockIdx.x * 128 + 32 * wave;
+  const int32_t m0 = blockIdx.x * BMM_ROWS + 32 * BMM_RM * wave;
   if (m0 >= a.M) return;
   const uint16_t* A = static_cast<const uint16_t*>(a.A) + axis_offset(a.a_batch, bi);
   const uint16_t* Bm = static_cast<const uint16_t*>(a.Bm) + axis_offset(a.b_batch, bi);
-  const int32_t m = m0 + ii;
-  const bool mok = m < a.M;
-  const uint16_t* arow = A + (int64_t)(mok ? m : m0) * a.lda;
+  const uint16_t* arow[BMM_RM];
+  bool mok[BMM_RM];
+  int32_t lo_row[BMM_RM];   // first valid kk of the lane's row in each tile
+#pragma unroll
+  for (int r = 0; r < BMM_RM; ++r) {
+    const int32_t m = m0 + 32 * r + ii;
+    mok[r] = m < a.M;
+    arow[r] = A + (int64_t)(mok[r] ? m : m0) * a.lda;
+    lo_row[r] = m - a.moff;
+  }
   const uint16_t* brow[2];
   bool nok[2];
 #pragma unroll
@@ -373,18 +388,19 @@ __global__ __launch_bounds__(256) void bmm64_kernel(BmmArgs a) {
     nok[e] = n < a.n_valid;
     brow[e] = Bm + (int64_t)(nok[e] ? n : 0) * a.ldb;
   }
-  floatx16 acc[2] = {floatx16{0}, floatx16{0}};
+  floatx16 acc[BMM_RM][2];
+#pragma unroll
+  for (int r = 0; r < BMM_RM; ++r) acc[r][0] = acc[r][1] = floatx16{0};
   // A(m, k) counts iff klim > k % kdiv >= m - moff: this wave's rows need
   // kk >= m0 - moff, and none past klim.  Steps of 16 k are numbered across
-  // the segments; fragments are loaded a group of G steps ahead.
+  // the segments.
   const int32_t kk_first = max(0, m0 - a.moff) & ~15;
   const int32_t kk_end = min(a.kdiv, a.klim);
   const int32_t per_seg = kk_end > kk_first ? (kk_end - kk_first + 15) / 16 : 0;
   const int32_t nsteps = per_seg * (a.K / a.kdiv);
-  const int32_t lo_row = m - a.moff;   // first valid kk of this lane's row
   constexpr int G = 4;
   struct Frag {
-    bf16x8 a, b0, b1;
+    bf16x8 a[BMM_RM], b[2];
     int32_t k8;   // kk + 8hf of the step
   };
   auto load = [&](int32_t st, Frag& f) {
@@ -392,54 +408,62 @@ __global__ __launch_bounds__(256) void bmm64_kernel(BmmArgs a) {
     const int32_t kk = kk_first + 16 * (st - seg * per_seg);
     f.k8 = kk + 8 * hf;
     const int64_t k = (int64_t)seg * a.kdiv + f.k8;
-    f.a = mok ? *reinterpret_cast<const bf16x8*>(arow + k) : bf16x8{};
-    f.b0 = nok[0] ? *reinterpret_cast<const bf16x8*>(brow[0] + k) : bf16x8{};
-    f.b1 = nok[1] ? *reinterpret_cast<const bf16x8*>(brow[1] + k) : bf16x8{};
+#pragma unroll
+    for (int r = 0; r < BMM_RM; ++r) f.a[r] = *reinterpret_cast<const bf16x8*>(arow[r] + k);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) f.b[e] = *reinterpret_cast<const bf16x8*>(brow[e] + k);
   };
   auto use = [&](Frag& f) {
-    const int lo = lo_row - f.k8, hi = kk_end - f.k8;
-    if (!mok || lo > 0 || hi < 8) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (!mok || e < lo || e >= hi) f.a[e] = static_cast<bf16>(0.0f);
+    for (int r = 0; r < BMM_RM; ++r) {
+      const int lo = lo_row[r] - f.k8, hi = kk_end - f.k8;
+      if (!mok[r] || lo > 0 || hi < 8) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (!mok[r] || e < lo || e >= hi) f.a[r][e] = static_cast<bf16>(0.0f);
+      }
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+        acc[r][e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[r], f.b[e], acc[r][e], 0, 0, 0);
     }
-    acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a, f.b0, acc[0], 0, 0, 0);
-    acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a, f.b1, acc[1], 0, 0, 0);
   };
   Frag fa[G], fb[G];
+  // Loads are unconditional (steps past the end re-read the last one) so
+  // that the waits before each group count only the loads issued after it.
   auto load_group = [&](int32_t g0, Frag (&f)[G]) {
 #pragma unroll
-    for (int x = 0; x < G; ++x)
-      if (g0 + x < nsteps) load(g0 + x, f[x]);
+    for (int x = 0; x < G; ++x) load(min(g0 + x, nsteps - 1), f[x]);
   };
   auto use_group = [&](int32_t g0, Frag (&f)[G]) {
 #pragma unroll
     for (int x = 0; x < G; ++x)
       if (g0 + x < nsteps) use(f[x]);
   };
-  load_group(0, fa);
+  if (nsteps > 0) load_group(0, fa);
   for (int32_t g0 = 0; g0 < nsteps; g0 += 2 * G) {
     load_group(g0 + G, fb);
     use_group(g0, fa);
     load_group(g0 + 2 * G, fa);
     use_group(g0 + G, fb);
   }
-  // lane holds column n = 32e + ii, rows m0 + 8g + 4hf + r (element 4g + r)
+  // lane holds column n = 32e + ii, rows m0 + 32r + 8g + 4hf + q (element 4g + q)
   float* C = a.C + axis_offset(a.c_batch, bi);
   float* C2 = a.C2 ? a.C2 + axis_offset(a.c2_batch, bi) : nullptr;
 #pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    const int n = 32 * e + ii;
-    if (!nok[e]) continue;
+  for (int r = 0; r < BMM_RM; ++r)
 #pragma unroll
-    for (int x = 0; x < 16; ++x) {
-      const int32_t row = m0 + 8 * (x >> 2) + 4 * hf + (x & 3);
-      if (row >= a.m_valid) continue;
-      const float val = a.alpha * acc[e][x];
-      C[(int64_t)row * a.ldc + n] = val;
-      if (C2) C2[(int64_t)row * a.c2_m + (int64_t)n * a.c2_n] = val;
+    for (int e = 0; e < 2; ++e) {
+      const int n = 32 * e + ii;
+      if (!nok[e]) continue;
+#pragma unroll
+      for (int x = 0; x < 16; ++x) {
+        const int32_t row = m0 + 32 * r + 8 * (x >> 2) + 4 * hf + (x & 3);
+        if (row >= a.m_valid) continue;
+        const float val = a.alpha * acc[r][e][x];
+        C[(int64_t)row * a.ldc + n] = val;
+        if (C2) C2[(int64_t)row * a.c2_m + (int64_t)n * a.c2_n] = val;
+      }
     }
-  }
 }
 
 // ------------------------------------------------------------------ helpers
@@ -630,7 +654,7 @@ int launch_attn_bwd_q(const BwdArgs& a, void* stream) {
 }
 
 int launch_bmm64(const BmmArgs& a, void* stream) {
-  hipLaunchKernelGGL(bmm64_kernel, dim3((a.M + 127) / 128, a.batch), dim3(256), 0,
+  hipLaunchKernelGGL(bmm64_kernel, dim3((a.M + BMM_ROWS - 1) / BMM_ROWS, a.batch), dim3(256), 0,
                      static_cast<hipStream_t>(stream), a);
   return static_cast<int>(hipGetLastError());
 }
