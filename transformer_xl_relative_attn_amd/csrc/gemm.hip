@@ -19,6 +19,8 @@
 //
 // gemm_f32: fp32 operands and arithmetic on the vector ALUs (64x64 tile),
 //   used by the fp32 path.
+#include <type_traits>
+
 #include "dev_common.h"
 
 namespace txl {
@@ -26,6 +28,9 @@ namespace txl {
 namespace {
 
 constexpr int BK = 32;
+
+template <int X>
+using IC = std::integral_constant<int, X>;
 #ifndef TXL_GEMM_NSTAGE
 #define TXL_GEMM_NSTAGE 3
 #endif
@@ -385,7 +390,8 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmGroup& g, int32_t padde
   constexpr int NQ = 2 * LOADS;           // refill loads per wave and K step
   constexpr int MPQ = WM * WN / NQ;       // MFMAs per refill load
   static_assert(MPQ * NQ == WM * WN, "MFMAs split evenly between the loads");
-  auto kstep = [&](int slot, int nslot, bool refill) {
+  auto kstep = [&](auto X, int slot, int nslot, bool refill) {
+    constexpr int EXTRA = decltype(X)::value;   // stores queued behind K step kt+1
     const u32x4* st = stage_ptr(slot);
 #pragma unroll
     for (int x = 0; x < WM * WN; ++x) {
@@ -393,7 +399,7 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmGroup& g, int32_t padde
       if (x < NF) read_one(st, 1, x, f1a, f1b);
       __builtin_amdgcn_sched_barrier(0);
     }
-    wait_vm<(NSTAGE - 2) * 2 * LOADS>();
+    wait_vm<(NSTAGE - 2) * 2 * LOADS + EXTRA>();
     barrier_lds();
     u32x4* rs = smem + slot * STAGE_U + wave_s * 64;
     const u32x4* nst = stage_ptr(nslot);
@@ -428,6 +434,13 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmGroup& g, int32_t padde
   setup(xcd_swizzle(seq, padded));
   prologue();
 
+  // A staged epilogue of a sub-tile that lies wholly inside the output issues
+  // exactly EPI_STORES global stores, after the next tile's first NSTAGE
+  // stages.  Vector memory operations of a wave complete in issue order, so
+  // the waits for those stages may leave the stores in flight: the next
+  // tile's first K steps overlap the previous tile's write-back.
+  constexpr int EPI_STORES = WM * (32 / (64 / V::CPR));
+  bool pend = false;
   while (true) {
 #pragma unroll
     for (int i = 0; i < WM; ++i)
@@ -436,21 +449,30 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmGroup& g, int32_t padde
 
     // Loads return in order and every step issues exactly one stage, so the
     // wait counts are fixed: K step 0 has landed once at most NSTAGE-1 stages
-    // issued after it remain, step kt+1 once NSTAGE-2 remain.  Outstanding
-    // epilogue stores of the previous tile only make these waits stricter (a
-    // pending load keeps every later load pending too).
-    wait_vm<(NSTAGE - 1) * 2 * LOADS>();
+    // issued after it remain, step kt+1 once NSTAGE-2 remain (plus, while it
+    // is one of the first NSTAGE stages, the previous tile's stores).
+    // Epilogue stores other than the counted ones only make the waits stricter.
+    const bool peel = pend && nk >= NSTAGE - 1;
+    if (peel)
+      wait_vm<(NSTAGE - 1) * 2 * LOADS + EPI_STORES>();
+    else
+      wait_vm<(NSTAGE - 1) * 2 * LOADS>();
     barrier_lds();
     {
       const u32x4* st = stage_ptr(0);
 #pragma unroll
       for (int f = 0; f < NF; ++f) read_one(st, 0, f, f0a, f0b);
     }
-    int slot = 0;
+    int slot = 0, kt = 0;
+    if (peel) {
+#pragma unroll
+      for (int p = 0; p < NSTAGE - 1; ++p) kstep(IC<EPI_STORES>{}, p, p + 1, p + NSTAGE < nk);
+      slot = kt = NSTAGE - 1;
+    }
 #pragma unroll 1
-    for (int kt = 0; kt < nk; ++kt) {
+    for (; kt < nk; ++kt) {
       const int nslot = slot + 1 == NSTAGE ? 0 : slot + 1;
-      kstep(slot, nslot, kt + NSTAGE < nk);
+      kstep(IC<0>{}, slot, nslot, kt + NSTAGE < nk);
       slot = nslot;
     }
     // Every wave is done reading the ring: the next tile's first K steps are
@@ -465,6 +487,12 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmGroup& g, int32_t padde
     if (more) {
       setup(xcd_swizzle(seq, padded));
       prologue();
+    }
+    {
+      const OutDst& o = g.p[cpidx].out;
+      const int wms = wave_s / V::GN, wns = wave_s % V::GN;   // wave-uniform
+      pend = more && o.vec8_ok && o.flags == 0 && cm0 + wms * WTM + WTM <= o.m_valid &&
+             cn0 + wns * WTN + WTN <= o.n_valid;
     }
     epilogue<V>(g.p[cpidx], acc, cm0, cn0, wm, wn, lane, stage_out);
     if (!more) break;
