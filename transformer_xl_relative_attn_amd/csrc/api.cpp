@@ -777,7 +777,7 @@ txl_status_t run_rel_attn_bwd(const BwdPlan& bp, const AttnPtrs& a, const BwdOut
     BmmArgs m{};
     m.A = A; m.Bm = Bm; m.lda = lda; m.ldb = ldb; m.a_batch = ab; m.b_batch = bb;
     m.M = p.P; m.K = K; m.batch = batch; m.n_valid = p.dh; m.m_valid = p.P;
-    m.kdiv = p.Lp; m.moff = p.M; m.klim = p.L; m.alpha = alpha;
+    m.moff = p.M; m.klim = p.L; m.alpha = alpha;
     m.C = C; m.ldc = HD; m.c_batch = cb;
     m.C2 = C2; m.c2_m = c2m; m.c2_n = c2n; m.c2_batch = c2b;
     return after_launch(timed(K_BWD_BMM, stream, [&] { return launch_bmm64(m, stream); }), what,

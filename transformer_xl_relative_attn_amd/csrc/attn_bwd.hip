@@ -356,96 +356,131 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_q_kernel(BwdArgs a) {
 
 // ------------------------------------------------------------------ bmm64
 // One wave per 64 rows of A (two 32-row tiles) and both 32-column halves of
-// the output: four matrix-core products per 16-wide k-step on fragments that
-// come straight from global memory (rows are K-contiguous), loaded a group of
-// G k-steps ahead.
-constexpr int BMM_RM = 2;            // 32-row tiles per wave
+// the output: four matrix-core products per 16-wide k-step.  A fragments come
+// straight from global memory (rows are K-contiguous; each lane streams its
+// row), loaded a group of G k-steps ahead.  B (64 rows, shared by the whole
+// workgroup) is staged in LDS once per 512-wide K chunk by direct
+// global->LDS loads and read from there: fetched per wave from global memory
+// it cost as much as A.  A(m, k) counts iff m - moff <= k < min(K, klim): a
+// step whose 32 x 16 fragment lies inside that band (decided per wave, so on
+// the scalar unit) runs unmasked; only the band's edge pays for masking.
+constexpr int BMM_RM = 2;                   // 32-row tiles per wave
 constexpr int BMM_ROWS = 4 * 32 * BMM_RM;   // rows per workgroup
+constexpr int BMM_KC = 512;                 // K chunk staged in LDS
 
-__global__ __launch_bounds__(256) void bmm64_kernel(BmmArgs a) {
+// zero the elements e of a row fragment outside [lo, hi), all if !ok
+__device__ __forceinline__ bf16x8 band_mask(bf16x8 f, int32_t lo, int32_t hi, bool ok) {
+  const int32_t l = min(max(lo, 0), 8), h = min(max(hi, 0), 8);
+  const uint32_t bits = ok && h > l ? ((1u << h) - 1u) & ~((1u << l) - 1u) : 0u;
+  u32x4 w = __builtin_bit_cast(u32x4, f);
+#pragma unroll
+  for (int p = 0; p < 4; ++p)
+    w[p] &= ((bits >> (2 * p)) & 1u ? 0x0000ffffu : 0u) | ((bits >> (2 * p + 1)) & 1u ? 0xffff0000u : 0u);
+  return __builtin_bit_cast(bf16x8, w);
+}
+
+__global__ __launch_bounds__(256, 2) void bmm64_kernel(BmmArgs a) {
+  // B chunk: row n (1 KB) holds 16-byte chunk c at slot c ^ (n & 15), so the
+  // 16 rows a fragment read serves at once sit on distinct bank groups
+  __shared__ u32x4 bsm[64 * (BMM_KC / 8)];
   const int32_t bi = blockIdx.y;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ii = lane & 31, hf = lane >> 5;
-  const int32_t m0 = blockIdx.x * BMM_ROWS + 32 * BMM_RM * wave;
-  if (m0 >= a.M) return;
+  const int32_t mwg = blockIdx.x * BMM_ROWS;
+  const int32_t m0 = mwg + 32 * BMM_RM * wave;
+  const bool wave_on = m0 < a.M;   // idle waves still take part in the staging
   const uint16_t* A = static_cast<const uint16_t*>(a.A) + axis_offset(a.a_batch, bi);
   const uint16_t* Bm = static_cast<const uint16_t*>(a.Bm) + axis_offset(a.b_batch, bi);
+  // rows past M read row m0 (valid memory, masked); B rows past n_valid read
+  // row 0: a B row only reaches its own, unstored, output column
   const uint16_t* arow[BMM_RM];
   bool mok[BMM_RM];
-  int32_t lo_row[BMM_RM];   // first valid kk of the lane's row in each tile
+  int32_t lo_row[BMM_RM];   // first k of the lane's row in each tile
 #pragma unroll
   for (int r = 0; r < BMM_RM; ++r) {
     const int32_t m = m0 + 32 * r + ii;
     mok[r] = m < a.M;
-    arow[r] = A + (int64_t)(mok[r] ? m : m0) * a.lda;
+    arow[r] = A + (int64_t)(mok[r] ? m : (wave_on ? m0 : 0)) * a.lda;
     lo_row[r] = m - a.moff;
-  }
-  const uint16_t* brow[2];
-  bool nok[2];
-#pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    const int n = 32 * e + ii;
-    nok[e] = n < a.n_valid;
-    brow[e] = Bm + (int64_t)(nok[e] ? n : 0) * a.ldb;
   }
   floatx16 acc[BMM_RM][2];
 #pragma unroll
   for (int r = 0; r < BMM_RM; ++r) acc[r][0] = acc[r][1] = floatx16{0};
-  // A(m, k) counts iff klim > k % kdiv >= m - moff: this wave's rows need
-  // kk >= m0 - moff, and none past klim.  Steps of 16 k are numbered across
-  // the segments.
-  const int32_t kk_first = max(0, m0 - a.moff) & ~15;
-  const int32_t kk_end = min(a.kdiv, a.klim);
-  const int32_t per_seg = kk_end > kk_first ? (kk_end - kk_first + 15) / 16 : 0;
-  const int32_t nsteps = per_seg * (a.K / a.kdiv);
+  // rows need k >= m - moff and none at or past kend
+  const int32_t kend = min(a.K, a.klim);
+  const int32_t kfirst_wg = max(0, mwg - a.moff) & ~(BMM_KC - 1);
+  const int32_t kfirst = max(0, m0 - a.moff) & ~15;
+  int bofs[2];   // this lane's B row base (16-byte units) and swizzle
+#pragma unroll
+  for (int e = 0; e < 2; ++e) bofs[e] = (32 * e + ii) * (BMM_KC / 8);
+  const int bsw = ii & 15;
   constexpr int G = 4;
   struct Frag {
-    bf16x8 a[BMM_RM], b[2];
-    int32_t k8;   // kk + 8hf of the step
+    bf16x8 a[BMM_RM];
+    int32_t kk;   // first k of the step (wave-uniform)
   };
-  auto load = [&](int32_t st, Frag& f) {
-    const int32_t seg = st / per_seg;
-    const int32_t kk = kk_first + 16 * (st - seg * per_seg);
-    f.k8 = kk + 8 * hf;
-    const int64_t k = (int64_t)seg * a.kdiv + f.k8;
-#pragma unroll
-    for (int r = 0; r < BMM_RM; ++r) f.a[r] = *reinterpret_cast<const bf16x8*>(arow[r] + k);
-#pragma unroll
-    for (int e = 0; e < 2; ++e) f.b[e] = *reinterpret_cast<const bf16x8*>(brow[e] + k);
-  };
-  auto use = [&](Frag& f) {
-#pragma unroll
-    for (int r = 0; r < BMM_RM; ++r) {
-      const int lo = lo_row[r] - f.k8, hi = kk_end - f.k8;
-      if (!mok[r] || lo > 0 || hi < 8) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (!mok[r] || e < lo || e >= hi) f.a[r][e] = static_cast<bf16>(0.0f);
-      }
-#pragma unroll
-      for (int e = 0; e < 2; ++e)
-        acc[r][e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[r], f.b[e], acc[r][e], 0, 0, 0);
+  for (int32_t kc = kfirst_wg; kc < kend; kc += BMM_KC) {
+    const int32_t kc_end = min(kend, kc + BMM_KC);
+    // stage B[:, kc .. kc + 512): wave w fills rows 16w .. 16w+15, one 1 KB
+    // row per instruction (columns past K are never read as data)
+    __syncthreads();   // every wave is done with the previous chunk
+#pragma unroll 4
+    for (int t = 0; t < 16; ++t) {
+      const int n = 16 * wave + t;
+      const int nr = n < a.n_valid ? n : 0;
+      const int c = lane ^ (n & 15);   // chunk that lands in slot `lane`
+      const int32_t k = min(kc + 8 * c, a.K - 8);
+      __builtin_amdgcn_global_load_lds(Bm + (int64_t)nr * a.ldb + k, bsm + n * (BMM_KC / 8), 16, 0, 0);
     }
-  };
-  Frag fa[G], fb[G];
-  // Loads are unconditional (steps past the end re-read the last one) so
-  // that the waits before each group count only the loads issued after it.
-  auto load_group = [&](int32_t g0, Frag (&f)[G]) {
+    __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): this wave's rows have landed
+    __syncthreads();
+    const int32_t k_lo = max(kfirst, kc);
+    const int32_t nsteps = wave_on && kc_end > k_lo ? (kc_end - k_lo + 15) / 16 : 0;
+    auto load = [&](int32_t st, Frag& f) {
+      f.kk = k_lo + 16 * st;
+      const int32_t k = f.kk + 8 * hf;
 #pragma unroll
-    for (int x = 0; x < G; ++x) load(min(g0 + x, nsteps - 1), f[x]);
-  };
-  auto use_group = [&](int32_t g0, Frag (&f)[G]) {
+      for (int r = 0; r < BMM_RM; ++r) f.a[r] = *reinterpret_cast<const bf16x8*>(arow[r] + k);
+    };
+    auto use = [&](Frag& f) {
+      const int c = (f.kk - kc) / 8 + hf;
+      bf16x8 b[2];
 #pragma unroll
-    for (int x = 0; x < G; ++x)
-      if (g0 + x < nsteps) use(f[x]);
-  };
-  if (nsteps > 0) load_group(0, fa);
-  for (int32_t g0 = 0; g0 < nsteps; g0 += 2 * G) {
-    load_group(g0 + G, fb);
-    use_group(g0, fa);
-    load_group(g0 + 2 * G, fa);
-    use_group(g0 + G, fb);
+      for (int e = 0; e < 2; ++e) b[e] = __builtin_bit_cast(bf16x8, bsm[bofs[e] + (c ^ bsw)]);
+#pragma unroll
+      for (int r = 0; r < BMM_RM; ++r) {
+        const int32_t mlast = m0 + 32 * r + 31;
+        const bool inside = mlast < a.M && mlast - a.moff <= f.kk && f.kk + 16 <= kend;
+        if (!inside) {
+          const int32_t k8 = f.kk + 8 * hf;
+          f.a[r] = band_mask(f.a[r], lo_row[r] - k8, kend - k8, mok[r]);
+        }
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+          acc[r][e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[r], b[e], acc[r][e], 0, 0, 0);
+      }
+    };
+    Frag fa[G], fb[G];
+    // Loads are unconditional (steps past the end re-read the last one) so
+    // that the waits before each group count only the loads issued after it.
+    auto load_group = [&](int32_t g0, Frag (&f)[G]) {
+#pragma unroll
+      for (int x = 0; x < G; ++x) load(min(g0 + x, nsteps - 1), f[x]);
+    };
+    auto use_group = [&](int32_t g0, Frag (&f)[G]) {
+#pragma unroll
+      for (int x = 0; x < G; ++x)
+        if (g0 + x < nsteps) use(f[x]);
+    };
+    if (nsteps > 0) load_group(0, fa);
+    for (int32_t g0 = 0; g0 < nsteps; g0 += 2 * G) {
+      load_group(g0 + G, fb);
+      use_group(g0, fa);
+      load_group(g0 + 2 * G, fa);
+      use_group(g0 + G, fb);
+    }
   }
+  if (!wave_on) return;
   // lane holds column n = 32e + ii, rows m0 + 32r + 8g + 4hf + q (element 4g + q)
   float* C = a.C + axis_offset(a.c_batch, bi);
   float* C2 = a.C2 ? a.C2 + axis_offset(a.c2_batch, bi) : nullptr;
@@ -454,7 +489,7 @@ __global__ __launch_bounds__(256) void bmm64_kernel(BmmArgs a) {
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int n = 32 * e + ii;
-      if (!nok[e]) continue;
+      if (n >= a.n_valid) continue;
 #pragma unroll
       for (int x = 0; x < 16; ++x) {
         const int32_t row = m0 + 32 * r + 8 * (x >> 2) + 4 * hf + (x & 3);
@@ -654,6 +689,7 @@ int launch_attn_bwd_q(const BwdArgs& a, void* stream) {
 }
 
 int launch_bmm64(const BmmArgs& a, void* stream) {
+  if (a.K % 16 != 0) return static_cast<int>(hipErrorInvalidValue);
   hipLaunchKernelGGL(bmm64_kernel, dim3((a.M + BMM_ROWS - 1) / BMM_ROWS, a.batch), dim3(256), 0,
                      static_cast<hipStream_t>(stream), a);
   return static_cast<int>(hipGetLastError());

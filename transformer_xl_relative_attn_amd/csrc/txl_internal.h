@@ -210,9 +210,9 @@ struct BwdArgs {
 
 // Batched "A times B^T" with 64 output columns, fp32 result:
 //   C[bi][m][n] = alpha * sum_k A[bi][m][k] B[bi][n][k],  n < n_valid <= 64,
-// A and B bf16 with rows K-contiguous.  A(m, k) counts only where
-// klim > k % kdiv >= m - moff (the other entries are never read as data:
-// they may hold anything).  Batch bi starts at a_batch(bi), b_batch(bi),
+// A and B bf16 with rows K-contiguous (K a multiple of 16).  A(m, k) counts
+// only where min(K, klim) > k >= m - moff (the other entries are never read
+// as data: they may hold anything).  Batch bi starts at a_batch(bi), b_batch(bi),
 // c_batch(bi) elements; C2 (optional) receives the same values at
 // c2_batch(bi) + m*c2_m + n*c2_n.
 struct BmmArgs {
@@ -221,7 +221,7 @@ struct BmmArgs {
   int64_t lda, ldb;
   AxisMap a_batch, b_batch;
   int32_t M, K, batch, n_valid, m_valid;
-  int32_t kdiv, moff, klim;
+  int32_t moff, klim;
   float alpha;
   float* C;
   int64_t ldc;
