@@ -120,3 +120,12 @@ def test_bwd_train_shaped_full_batch_sampled(txl):
     """The full train-shaped batch (22 rows): per-row gradients on sampled rows."""
     cfg = synth.get_config("train_l512_m512")
     _run(txl, cfg, np.array([0, 21]), with_wkr=False)
+
+
+def test_bwd_long_segment(txl):
+    """Segment 640 > 512: the key-side products stage their shared operand in
+    two K chunks, and workgroups whose band starts in the second chunk skip the
+    first."""
+    cfg = synth.Config("bwd_long_seg", 1, 128, 2, 64, 640, 96, 1, 1, "bf16", 0.05, 91)
+    got, want = _run(txl, cfg, np.arange(1))
+    _check_summed(got, want, True)
