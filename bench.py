@@ -395,7 +395,14 @@ def main():
                     help="instead of the headline, time the backward of the train-shaped layer "
                          "(one JSON line)")
     ap.add_argument("--bwd-config", default="train_l512_m512")
+    ap.add_argument("--shaw", action="store_true",
+                    help="instead of the headline, time the same layer step as the two-term "
+                         "variant of Shaw et al.: u = v = 0 and a learned position table R^ "
+                         "passed as the position keys (no W_kR product; one JSON line)")
     args = ap.parse_args()
+    if args.shaw:
+        args.cached_rk = True
+        args.no_ring = True
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the relative-attention step has no "
@@ -434,12 +441,19 @@ def main():
             w.update(W_o=dev(lay.W_o), W_ff1=dev(lay.W_ff1), W_ff2=dev(lay.W_ff2))
         W.append(w)
     u, v = dev(wl.u), dev(wl.v)
+    if args.shaw:
+        u.zero_()
+        v.zero_()
     mems = [dev(m) for m in wl.mem]
     segs = [dev(s) for s in wl.segments]
     R = torch.empty((cfg.n_pos, cfg.d_pos), dtype=dt_t, device="cuda")
     txl.txl_sinusoid_pos(R, cfg.n_pos, cfg.d_pos, dt_x)
     Rks = None
-    if args.cached_rk:
+    if args.shaw:
+        # the learned table R^ (one row per distance, already per head): synthetic
+        rng = np.random.default_rng(cfg.seed + 77)
+        Rks = [dev(rng.normal(0.0, 0.5, (cfg.n_pos, cfg.n_heads, cfg.d_head))) for _ in W]
+    elif args.cached_rk:
         Rks = []
         for w in W:
             rk = torch.empty((cfg.n_pos, cfg.n_heads, cfg.d_head), dtype=dt_t, device="cuda")
@@ -581,6 +595,24 @@ def main():
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(cfg, wl, args.cpu_budget)
+
+    if args.shaw:
+        out = {"metric": "Shaw-variant layer step TFLOP/s (executed: q, K, V projections + "
+                         "two-term attention core)",
+               "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+               "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+               "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+               "dtype": cfg.dtype, "data": "synthetic",
+               "config": {"workload": f"{cfg.name}: Shaw et al. two-term layer step (u = v = 0, "
+                                      "learned R^ as position keys)",
+                          "batch": cfg.batch, "seg_len": cfg.seg_len, "mem_len": cfg.mem_len,
+                          "d_model": cfg.d_model, "n_heads": cfg.n_heads, "d_head": cfg.d_head},
+               "tokens_per_s": round(tokens, 1), "gflop_per_step": round(f_step / 1e9, 3),
+               "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv)
+                               for kk, vv in d.items()} for k, d in kernels.items()},
+               "attention_kernel": attn_info}
+        print(json.dumps(out), flush=True)
+        return
 
     out = {
         "metric": "rel-attn fwd TFLOP/s (% bf16 MFMA peak) + eval tokens/s at L=128,M=1600",

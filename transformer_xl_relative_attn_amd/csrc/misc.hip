@@ -159,6 +159,20 @@ __global__ void repack_rk_kernel(const void* src, void* dst, int32_t P, int32_t 
   store_from_f32(dst, ((int64_t)h * (Pp + 2 * pad) + pad + p) * dp + c, x, dtype);
 }
 
+// bf16 with dh == dp: one 16-byte chunk (8 columns) per thread, 32-bit index
+// arithmetic (the element-wise kernel's 64-bit divisions dominated its time)
+__global__ void repack_rk_vec_kernel(const uint16_t* src, uint16_t* dst, int32_t P, int32_t Pp,
+                                     int32_t pad, int32_t H, int32_t dp) {
+  const int32_t cpr = dp / 8;
+  const int32_t idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= H * Pp * cpr) return;
+  const int32_t c = idx % cpr, t = idx / cpr;
+  const int32_t p = t % Pp, h = t / Pp;
+  u32x4 x = u32x4{0u, 0u, 0u, 0u};
+  if (p < P) x = *reinterpret_cast<const u32x4*>(src + ((int64_t)p * H + h) * dp + 8 * c);
+  *reinterpret_cast<u32x4*>(dst + ((int64_t)h * (Pp + 2 * pad) + pad + p) * dp + 8 * c) = x;
+}
+
 inline dim3 grid1d(int64_t n) { return dim3((unsigned)((n + 255) / 256)); }
 
 }  // namespace
@@ -221,8 +235,15 @@ int launch_cast_f32(const void* src, float* dst, int64_t n, int32_t dtype, void*
 int launch_repack_rk(const void* rk_pub, void* rk_ws, int32_t P, int32_t Pp, int32_t pad, int32_t H,
                      int32_t dh, int32_t dp, int32_t dtype, void* stream) {
   const int64_t n = (int64_t)H * Pp * dp;
-  hipLaunchKernelGGL(repack_rk_kernel, grid1d(n), dim3(256), 0, static_cast<hipStream_t>(stream),
-                     rk_pub, rk_ws, P, Pp, pad, H, dh, dp, dtype);
+  const bool vec = dtype == TXL_BF16 && dh == dp && dp % 8 == 0 && n / 8 < INT32_MAX &&
+                   (reinterpret_cast<uintptr_t>(rk_pub) | reinterpret_cast<uintptr_t>(rk_ws)) % 16 == 0;
+  if (vec)
+    hipLaunchKernelGGL(repack_rk_vec_kernel, grid1d(n / 8), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), static_cast<const uint16_t*>(rk_pub),
+                       static_cast<uint16_t*>(rk_ws), P, Pp, pad, H, dp);
+  else
+    hipLaunchKernelGGL(repack_rk_kernel, grid1d(n), dim3(256), 0, static_cast<hipStream_t>(stream),
+                       rk_pub, rk_ws, P, Pp, pad, H, dh, dp, dtype);
   return static_cast<int>(hipGetLastError());
 }
 
