@@ -338,6 +338,33 @@ def bwd_bench(args):
     txl.txl_timing_enable(False)
     kernels = {k: {"launches": c, "avg_us": round(t / c * 1e3, 2), "ms_per_step": round(t / args.steps, 4)}
                for k, (c, t) in per.items() if c}
+    # the training pair: forward with its state kept, then the backward from it
+    out_fwd = torch.empty((B, L, H, dh), dtype=torch.bfloat16, device="cuda")
+
+    def fwd_train():
+        txl.txl_rel_attn_fwd_train(shape, h, mem, 0, W["W_q"], W["W_kE"], W["W_kR"], W["W_v"], u,
+                                   v, R, None, out_fwd, ws, stream)
+
+    def bwd_saved():
+        txl.txl_rel_attn_bwd_saved(shape, u, v, R, False, out_fwd, G, outs["d_q"], outs["d_k"],
+                                   outs["d_val"], outs["d_u"], outs["d_v"], outs["d_Rk"],
+                                   outs["d_W_kR"], ws, stream)
+
+    def timed_ms(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(args.steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return max(e0.elapsed_time(e1), (time.perf_counter() - t1) * 1e3) / args.steps
+
+    fwd_train()
+    ms_saved = timed_ms(bwd_saved)
+    ms_pair = timed_ms(lambda: (fwd_train(), bwd_saved()))
     core, wkr = bwd_flops(cfg)
     value = (core + wkr) / (ms * 1e-3) / 1e12
     q_us = kernels.get("attn_bwd_q", {}).get("avg_us")
@@ -368,6 +395,10 @@ def bwd_bench(args):
         "tokens_per_s": round(B * L / (ms * 1e-3), 1),
         "kernels": kernels,
         "roofline": roof,
+        "from_saved_forward": {
+            "bwd_saved_ms": round(ms_saved, 4),
+            "bwd_saved_tflops": round((core + wkr) / (ms_saved * 1e-3) / 1e12, 2),
+            "fwd_train_plus_bwd_saved_ms": round(ms_pair, 4)},
     }
     print(json.dumps(out), flush=True)
 

@@ -166,6 +166,33 @@ txl_status_t txl_rel_attn_bwd(const txl_attn_shape_t* shape, const void* h, cons
                               void* stream);
 
 /*
+ * The same backward split at the forward, for training loops that run the
+ * forward anyway: no recompute.
+ * txl_rel_attn_fwd_train: txl_rel_attn_fwd's arguments and output (bf16
+ * only), with a workspace of txl_rel_attn_bwd_workspace_bytes() in which it
+ * leaves what the backward reads (projected q, K, V, Rk in the kernels'
+ * layouts and each row's log-sum-exp).
+ * txl_rel_attn_bwd_saved: the gradients of txl_rel_attn_bwd from that state.
+ * `workspace` must be the one the forward used, unchanged since; `out` the
+ * forward's output, unchanged; u, v the forward's; rk_given nonzero iff the
+ * forward was passed a caller Rk; R (the forward's sinusoid table) is read
+ * only for d_W_kR.  Outputs and their conditions as txl_rel_attn_bwd.
+ * Errors: fp32 (TXL_ERR_UNSUPPORTED); NULL u, v, out, d_out, workspace or
+ * gradient pointers; d_W_kR with rk_given or without R (TXL_ERR_BAD_SHAPE);
+ * misaligned out, d_out, R (TXL_ERR_UNSUPPORTED); workspace too small.
+ */
+txl_status_t txl_rel_attn_fwd_train(const txl_attn_shape_t* shape, const void* h, const void* mem,
+                                    int32_t mem_start, const void* W_q, const void* W_kE,
+                                    const void* W_kR, const void* W_v, const void* u,
+                                    const void* v, const void* R, const void* Rk, void* out,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+txl_status_t txl_rel_attn_bwd_saved(const txl_attn_shape_t* shape, const void* u, const void* v,
+                                    const void* R, int32_t rk_given, const void* out,
+                                    const void* d_out, float* d_q, float* d_k, float* d_val,
+                                    float* d_u, float* d_v, float* d_Rk, float* d_W_kR,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Carried projected-K/V memory for evaluation (bf16 only, seg_len % 32 == 0).
  * Sec. 3.2 extends each segment with the cached hidden states,
  * h~ = [SG(m) ; h], and Sec. 3.3 projects k = h~ W_kE^T, val = h~ W_v^T row by

@@ -229,3 +229,49 @@ def test_rel_attn_bwd_validation(txl):
     assert bwd(s, Rk=288, d_W_kR=304) == 2          # no W_kR gradient with a caller Rk
     assert bwd(s, ws_bytes=wsb - 1) == 4
     assert bwd(s, ws=None) == 1
+
+
+def test_rel_attn_training_pair_validation(txl):
+    """txl_rel_attn_fwd_train / txl_rel_attn_bwd_saved reject bad arguments
+    before anything is enqueued (fake, 16-byte aligned addresses: nothing is
+    dereferenced on these paths)."""
+    s = _shape(txl)
+    wsb = txl.txl_rel_attn_bwd_workspace_bytes(s)
+    fwd = txl.lib.txl_rel_attn_fwd_train
+    bwd = txl.lib.txl_rel_attn_bwd_saved
+
+    def fwd_call(shape, ws_bytes=wsb, **kw):
+        p = dict(h=16, mem=32, mem_start=0, W_q=48, W_kE=64, W_kR=80, W_v=96, u=112, v=128,
+                 R=144, Rk=None, out=160, ws=176)
+        p.update(kw)
+        return fwd(ctypes.byref(shape), p["h"], p["mem"], p["mem_start"], p["W_q"], p["W_kE"],
+                   p["W_kR"], p["W_v"], p["u"], p["v"], p["R"], p["Rk"], p["out"], p["ws"],
+                   ws_bytes, None)
+
+    def bwd_call(shape, ws_bytes=wsb, **kw):
+        p = dict(u=112, v=128, R=144, rk_given=0, out=160, d_out=192, d_q=208, d_k=224,
+                 d_val=240, d_u=256, d_v=272, d_Rk=288, d_W_kR=None, ws=176)
+        p.update(kw)
+        return bwd(ctypes.byref(shape), p["u"], p["v"], p["R"], p["rk_given"], p["out"],
+                   p["d_out"], p["d_q"], p["d_k"], p["d_val"], p["d_u"], p["d_v"], p["d_Rk"],
+                   p["d_W_kR"], p["ws"], ws_bytes, None)
+
+    assert fwd_call(_shape(txl, dtype=txl.TXL_F32)) == 5
+    assert fwd_call(s, out=None) == 1
+    assert fwd_call(s, mem=None) == 1
+    assert fwd_call(s, mem_start=16) == 2
+    assert fwd_call(s, W_kR=None) == 1                 # neither Rk nor W_kR
+    assert fwd_call(s, h=24) == 5                      # misaligned bf16 operand
+    assert fwd_call(s, ws_bytes=wsb - 1) == 4
+    assert fwd_call(s, ws=None) == 1
+    assert bwd_call(_shape(txl, dtype=txl.TXL_F32)) == 5
+    assert bwd_call(s, u=None) == 1
+    assert bwd_call(s, out=None) == 1
+    assert bwd_call(s, d_out=None) == 1
+    assert bwd_call(s, d_q=None) == 1
+    assert bwd_call(s, d_Rk=None) == 1
+    assert bwd_call(s, ws=None) == 1
+    assert bwd_call(s, rk_given=1, d_W_kR=304) == 2    # no W_kR gradient with a caller Rk
+    assert bwd_call(s, R=None, d_W_kR=304) == 2        # d_W_kR needs R
+    assert bwd_call(s, d_out=200) == 5                 # misaligned
+    assert bwd_call(s, ws_bytes=wsb - 1) == 4

@@ -129,3 +129,69 @@ def test_bwd_long_segment(txl):
     cfg = synth.Config("bwd_long_seg", 1, 128, 2, 64, 640, 96, 1, 1, "bf16", 0.05, 91)
     got, want = _run(txl, cfg, np.arange(1))
     _check_summed(got, want, True)
+
+
+@pytest.mark.parametrize("case", ["train_two_rows", "caller_rk_no_memory"])
+def test_bwd_saved_matches_recompute(txl, case):
+    """txl_rel_attn_fwd_train + txl_rel_attn_bwd_saved give txl_rel_attn_fwd's
+    output and txl_rel_attn_bwd's gradients bit for bit (same kernels, no
+    recompute), and the gradients match the oracle."""
+    import torch
+    import oracle
+    if case == "train_two_rows":
+        cfg = synth.get_config("train_l512_m512", batch=2)
+        use_rk = False
+    else:
+        cfg = synth.Config("bwd_saved_nomem", 2, 128, 2, 64, 96, 0, 1, 1, "bf16", 0.05, 57)
+        use_rk = True
+    log(f"[case] backward from saved state {case}")
+    wl = synth.make_workload(cfg, n_segments=1)
+    c = cfg
+    H, dh, L, M, B = c.n_heads, c.d_head, c.seg_len, c.mem_len, c.batch
+    P = M + L
+    rng = np.random.default_rng(11)
+    G = synth.round_to(rng.normal(0.0, 1.0, (B, L, H * dh)), "bf16")
+    dl = DeviceLayers(wl)
+    shp = dl.shape()
+    w = dl.W[0]
+    Rk_host = synth.round_to(rng.normal(0.0, 0.5, (P, H, dh)), "bf16") if use_rk else None
+    Rk = to_dev(Rk_host, "bf16") if use_rk else None
+    h = to_dev(wl.segments[0], "bf16")
+    mem = dl.mem[0] if M else None
+    W_kR = None if use_rk else w["W_kR"]
+    R = None if use_rk else dl.R
+    f32 = dict(dtype=torch.float32, device="cuda")
+
+    def grads():
+        return [torch.empty((B, L, H, dh), **f32), torch.empty((B, P, H, dh), **f32),
+                torch.empty((B, P, H, dh), **f32), torch.empty((H, dh), **f32),
+                torch.empty((H, dh), **f32), torch.empty((P, H, dh), **f32),
+                None if use_rk else torch.empty((H * dh, c.d_pos), **f32)]
+    g_ref, g_sav = grads(), grads()
+    dG = to_dev(G, "bf16")
+    ws_ref = workspace(txl.txl_rel_attn_bwd_workspace_bytes(shp))
+    txl.txl_rel_attn_bwd(shp, h, mem, 0, w["W_q"], w["W_kE"], W_kR, w["W_v"], dl.u, dl.v, R, Rk,
+                         dG, *g_ref, ws_ref)
+    out_ref = torch.empty((B, L, H, dh), dtype=torch.bfloat16, device="cuda")
+    ws_f = workspace(txl.txl_rel_attn_workspace_bytes(shp))
+    txl.txl_rel_attn_fwd(shp, h, mem, 0, w["W_q"], w["W_kE"], W_kR, w["W_v"], dl.u, dl.v, R, Rk,
+                         out_ref, ws_f)
+    out = torch.empty_like(out_ref)
+    ws = workspace(txl.txl_rel_attn_bwd_workspace_bytes(shp))
+    txl.txl_rel_attn_fwd_train(shp, h, mem, 0, w["W_q"], w["W_kE"], W_kR, w["W_v"], dl.u, dl.v,
+                               R, Rk, out, ws)
+    txl.txl_rel_attn_bwd_saved(shp, dl.u, dl.v, R, use_rk, out, dG, *g_sav, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out_ref), "forward output differs from txl_rel_attn_fwd"
+    names = ["d_q", "d_k", "d_val", "d_u", "d_v", "d_Rk", "d_W_kR"]
+    for n, a, b in zip(names, g_sav, g_ref):
+        if a is not None:
+            assert torch.equal(a, b), f"{n} differs from txl_rel_attn_bwd"
+    lay = wl.layers[0]
+    want = oracle.backward.rel_attn_bwd(wl.segments[0][:1], wl.mem[0][:1], lay.W_q, lay.W_kE,
+                                        lay.W_kR, lay.W_v, wl.u, wl.v,
+                                        oracle.sinusoid(P, c.d_pos), H, dh, 1.0 / np.sqrt(dh),
+                                        G[:1], Rk=Rk_host)
+    assert_close(from_dev(g_sav[0])[:1], want["q"], "bf16", "d_q")
+    assert_close(from_dev(g_sav[1])[:1], want["k"], "bf16", "d_k")
+    assert_close(from_dev(g_sav[2])[:1], want["val"], "bf16", "d_val")

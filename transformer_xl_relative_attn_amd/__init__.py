@@ -21,7 +21,8 @@ __all__ = [
     "txl_rel_attn_fwd", "txl_mem_update", "txl_segment_workspace_bytes", "txl_segment_step",
     "txl_kv_ring_slots", "txl_kv_ring_bytes", "txl_kv_ring_workspace_bytes", "txl_kv_ring_init",
     "txl_rel_attn_fwd_kv", "txl_segment_kv_workspace_bytes", "txl_segment_step_kv",
-    "txl_rel_attn_bwd_workspace_bytes", "txl_rel_attn_bwd",
+    "txl_rel_attn_bwd_workspace_bytes", "txl_rel_attn_bwd", "txl_rel_attn_fwd_train",
+    "txl_rel_attn_bwd_saved",
     "txl_timing_enable", "txl_timing_reset", "txl_timing_read",
 ]
 
@@ -96,6 +97,13 @@ _bwd_ws = _sig("txl_rel_attn_bwd_workspace_bytes", _sz, [ctypes.POINTER(AttnShap
 _bwd = _sig("txl_rel_attn_bwd", ctypes.c_int,
             [ctypes.POINTER(AttnShape), _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
              _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp])
+
+_fwd_train = _sig("txl_rel_attn_fwd_train", ctypes.c_int,
+                  [ctypes.POINTER(AttnShape), _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                   _vp, _vp, _vp, _sz, _vp])
+_bwd_saved = _sig("txl_rel_attn_bwd_saved", ctypes.c_int,
+                  [ctypes.POINTER(AttnShape), _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
+                   _vp, _vp, _vp, _vp, _sz, _vp])
 
 _t_enable = _sig("txl_timing_enable", ctypes.c_int, [_i32])
 _t_reset = _sig("txl_timing_reset", None, [])
@@ -262,6 +270,23 @@ def txl_rel_attn_bwd(shape: AttnShape, h, mem, mem_start: int, W_q, W_kE, W_kR, 
                 _ptr(d_q), _ptr(d_k), _ptr(d_val), _ptr(d_u), _ptr(d_v), _ptr(d_Rk),
                 _ptr(d_W_kR), _ptr(workspace), _nbytes(workspace), _stream(stream)),
            "txl_rel_attn_bwd")
+
+
+def txl_rel_attn_fwd_train(shape: AttnShape, h, mem, mem_start: int, W_q, W_kE, W_kR, W_v, u, v,
+                           R, Rk, out, workspace, stream=None):
+    _check(_fwd_train(ctypes.byref(shape), _ptr(h), _ptr(mem), mem_start, _ptr(W_q), _ptr(W_kE),
+                      _ptr(W_kR), _ptr(W_v), _ptr(u), _ptr(v), _ptr(R), _ptr(Rk), _ptr(out),
+                      _ptr(workspace), _nbytes(workspace), _stream(stream)),
+           "txl_rel_attn_fwd_train")
+
+
+def txl_rel_attn_bwd_saved(shape: AttnShape, u, v, R, rk_given: bool, out, d_out, d_q, d_k, d_val,
+                           d_u, d_v, d_Rk, d_W_kR, workspace, stream=None):
+    _check(_bwd_saved(ctypes.byref(shape), _ptr(u), _ptr(v), _ptr(R), 1 if rk_given else 0,
+                      _ptr(out), _ptr(d_out), _ptr(d_q), _ptr(d_k), _ptr(d_val), _ptr(d_u),
+                      _ptr(d_v), _ptr(d_Rk), _ptr(d_W_kR), _ptr(workspace), _nbytes(workspace),
+                      _stream(stream)),
+           "txl_rel_attn_bwd_saved")
 
 
 def txl_timing_enable(on: bool):

@@ -682,8 +682,11 @@ struct BwdOut {
   float *d_q, *d_k, *d_val, *d_u, *d_v, *d_Rk, *d_W_kR;
 };
 
-txl_status_t run_rel_attn_bwd(const BwdPlan& bp, const AttnPtrs& a, const BwdOut& g, char* ws,
-                              void* stream) {
+// Forward of the backward's plan: the projections (q, K, V^T, Rk plus K^T tiles
+// and val rows) and the attention with each row's log-sum-exp, all left in the
+// workspace, the output written to `out`.
+txl_status_t run_bwd_forward(const BwdPlan& bp, const AttnPtrs& a, void* out, char* ws,
+                             void* stream) {
   const AttnPlan& p = bp.p;
   const int dt = p.dtype;
   const int64_t DP = p.DP;
@@ -715,16 +718,26 @@ txl_status_t run_rel_attn_bwd(const BwdPlan& bp, const AttnPtrs& a, const BwdOut
   TXL_TRY(add_rk(gg, p, a, o, ws, stream));
   TXL_TRY(after_launch(timed(K_PROJ_GEMM, stream, [&] { return launch_gemm(gg, dt, stream); }),
                        "backward projection GEMMs", stream));
-  // forward recompute: out (bf16, workspace) and the rows' log-sum-exp
+  // the forward's output and the rows' log-sum-exp
   AttnPtrs fa = a;
-  fa.out = ws + bp.o.off;
+  fa.out = out;
   float* lse = reinterpret_cast<float*>(ws + bp.lse.off);
-  TXL_TRY(run_attention(p, fa, ws, stream, k, v, 0, nullptr, nullptr, lse));
+  return run_attention(p, fa, ws, stream, k, v, 0, nullptr, nullptr, lse);
+}
 
+// Backward from the state run_bwd_forward left in the workspace and its
+// output `out` (a.u, a.v and, for dW_kR, a.R are read again).
+txl_status_t run_bwd_from_state(const BwdPlan& bp, const AttnPtrs& a, const void* out,
+                                const BwdOut& g, char* ws, void* stream) {
+  const AttnPlan& p = bp.p;
+  const int dt = p.dtype;
+  const int64_t DP = p.DP;
+  char* k = ws + p.k.off;
+  float* lse = reinterpret_cast<float*>(ws + bp.lse.off);
   BwdPrepArgs pa{};
   pa.B = p.B; pa.H = p.H; pa.L = p.L; pa.dh = p.dh; pa.Lp = p.Lp;
   pa.dout = g.d_out;
-  pa.out = fa.out;
+  pa.out = out;
   pa.q = reinterpret_cast<const float*>(ws + p.q.off);
   pa.u = a.u;
   pa.v = a.v;
@@ -831,6 +844,14 @@ txl_status_t run_rel_attn_bwd(const BwdPlan& bp, const AttnPtrs& a, const BwdOut
                          "dW_kR GEMM", stream));
   }
   return TXL_OK;
+}
+
+// Forward recompute (output into the workspace) then the backward.
+txl_status_t run_rel_attn_bwd(const BwdPlan& bp, const AttnPtrs& a, const BwdOut& g, char* ws,
+                              void* stream) {
+  char* o = ws + bp.o.off;
+  TXL_TRY(run_bwd_forward(bp, a, o, ws, stream));
+  return run_bwd_from_state(bp, a, o, g, ws, stream);
 }
 
 // --------------------------------------------------------- segment planning
@@ -1148,6 +1169,50 @@ txl_status_t txl_rel_attn_bwd(const txl_attn_shape_t* shape, const void* h, cons
     return fail(TXL_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes, need);
   const BwdOut g{d_out, d_q, d_k, d_val, d_u, d_v, d_Rk, d_W_kR};
   return run_rel_attn_bwd(bp, a, g, static_cast<char*>(workspace), stream);
+}
+
+txl_status_t txl_rel_attn_fwd_train(const txl_attn_shape_t* shape, const void* h, const void* mem,
+                                    int32_t mem_start, const void* W_q, const void* W_kE,
+                                    const void* W_kR, const void* W_v, const void* u,
+                                    const void* v, const void* R, const void* Rk, void* out,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  TXL_TRY(check_shape(shape));
+  if (shape->dtype != TXL_BF16) return fail(TXL_ERR_UNSUPPORTED, "training calls are bf16 only");
+  AttnPtrs a{h, mem, W_q, W_kE, W_kR, W_v, u, v, R, Rk, mem_start, out};
+  TXL_TRY(check_attn_ptrs(shape, a, true, workspace));
+  const size_t need = txl_rel_attn_bwd_workspace_bytes(shape);
+  if (workspace_bytes < need)
+    return fail(TXL_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes, need);
+  const BwdPlan bp = make_bwd_plan(shape, Rk == nullptr, true);
+  return run_bwd_forward(bp, a, out, static_cast<char*>(workspace), stream);
+}
+
+txl_status_t txl_rel_attn_bwd_saved(const txl_attn_shape_t* shape, const void* u, const void* v,
+                                    const void* R, int32_t rk_given, const void* out,
+                                    const void* d_out, float* d_q, float* d_k, float* d_val,
+                                    float* d_u, float* d_v, float* d_Rk, float* d_W_kR,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  TXL_TRY(check_shape(shape));
+  if (shape->dtype != TXL_BF16) return fail(TXL_ERR_UNSUPPORTED, "the backward is bf16 only");
+  if (!u || !v || !out || !d_out || !workspace)
+    return fail(TXL_ERR_NULL_ARG, "u, v, out, d_out and workspace are required");
+  if (!d_q || !d_k || !d_val || !d_u || !d_v || !d_Rk)
+    return fail(TXL_ERR_NULL_ARG, "d_q, d_k, d_val, d_u, d_v and d_Rk are required");
+  if (d_W_kR && (rk_given || !R))
+    return fail(TXL_ERR_BAD_SHAPE, "d_W_kR needs Rk computed from W_kR and R (rk_given 0, R set)");
+  for (const void* q : {out, d_out, static_cast<const void*>(workspace), R})
+    if (q && !aligned16(q))
+      return fail(TXL_ERR_UNSUPPORTED, "bf16 path needs 16-byte aligned tensor pointers");
+  const size_t need = txl_rel_attn_bwd_workspace_bytes(shape);
+  if (workspace_bytes < need)
+    return fail(TXL_ERR_WORKSPACE_TOO_SMALL, "workspace %zu < %zu bytes", workspace_bytes, need);
+  const BwdPlan bp = make_bwd_plan(shape, !rk_given, true);
+  AttnPtrs a{};
+  a.u = u;
+  a.v = v;
+  a.R = R;
+  const BwdOut g{d_out, d_q, d_k, d_val, d_u, d_v, d_Rk, d_W_kR};
+  return run_bwd_from_state(bp, a, out, g, static_cast<char*>(workspace), stream);
 }
 
 int32_t txl_kv_ring_slots(const txl_attn_shape_t* shape) {
