@@ -785,32 +785,31 @@ txl_status_t run_bwd_from_state(const BwdPlan& bp, const AttnPtrs& a, const void
   // dRk = scale dS'^T (q+v) (per head, summed over batch rows)
   const int64_t HD = (int64_t)p.H * p.dh;
   auto bmm = [&](const void* A, int64_t lda, AxisMap ab, const void* Bm, int64_t ldb, AxisMap bb,
-                 int32_t batch, int32_t K, float alpha, float* C, AxisMap cb, float* C2,
-                 AxisMap c2b, int64_t c2m, int64_t c2n, const char* what) -> txl_status_t {
+                 int32_t batch, int32_t K, float alpha, float* C, AxisMap cb) {
     BmmArgs m{};
     m.A = A; m.Bm = Bm; m.lda = lda; m.ldb = ldb; m.a_batch = ab; m.b_batch = bb;
     m.M = p.P; m.K = K; m.batch = batch; m.n_valid = p.dh; m.m_valid = p.P;
     m.moff = p.M; m.klim = p.L; m.alpha = alpha;
     m.C = C; m.ldc = HD; m.c_batch = cb;
-    m.C2 = C2; m.c2_m = c2m; m.c2_n = c2n; m.c2_batch = c2b;
-    return after_launch(timed(K_BWD_BMM, stream, [&] { return launch_bmm64(m, stream); }), what,
-                        stream);
+    m.C2 = nullptr; m.c2_batch = kNoAxis;
+    return m;
   };
   const int32_t BHn = p.B * p.H;
   const AxisMap per_bh_c = make_axis(p.H, (int64_t)p.P * HD, p.dh);   // [B][P][H][dh]
-  TXL_TRY(bmm(ws + bp.dst.off, p.Lp, axis_linear((int64_t)p.Np * p.Lp), ws + bp.qut.off, p.Lp,
-              axis_linear(DP * p.Lp), BHn, p.Lp, p.scale, g.d_k, per_bh_c, nullptr, kNoAxis, 0, 0,
-              "dk product"));
-  TXL_TRY(bmm(ws + bp.pt.off, p.Lp, axis_linear((int64_t)p.Np * p.Lp), ws + bp.dot.off, p.Lp,
-              axis_linear(DP * p.Lp), BHn, p.Lp, 1.0f, g.d_val, per_bh_c, nullptr, kNoAxis, 0, 0,
-              "dval product"));
   // dRk per (head, batch row) into partials [B][P][H][dh], then summed over
   // the batch rows in order (one product per head would leave the chip idle)
   const int64_t BL = (int64_t)p.B * p.Lp;
   float* drk_part = reinterpret_cast<float*>(ws + bp.drkp.off);
-  TXL_TRY(bmm(ws + bp.dspt.off, BL, make_axis(p.B, (int64_t)bp.dsp_rows * BL, p.Lp),
-              ws + bp.qvt.off, BL, make_axis(p.B, DP * BL, p.Lp), BHn, p.Lp, p.scale, drk_part,
-              make_axis(p.B, p.dh, (int64_t)p.P * HD), nullptr, kNoAxis, 0, 0, "dRk product"));
+  const BmmArgs prods[3] = {
+      bmm(ws + bp.dst.off, p.Lp, axis_linear((int64_t)p.Np * p.Lp), ws + bp.qut.off, p.Lp,
+          axis_linear(DP * p.Lp), BHn, p.Lp, p.scale, g.d_k, per_bh_c),
+      bmm(ws + bp.pt.off, p.Lp, axis_linear((int64_t)p.Np * p.Lp), ws + bp.dot.off, p.Lp,
+          axis_linear(DP * p.Lp), BHn, p.Lp, 1.0f, g.d_val, per_bh_c),
+      bmm(ws + bp.dspt.off, BL, make_axis(p.B, (int64_t)bp.dsp_rows * BL, p.Lp), ws + bp.qvt.off,
+          BL, make_axis(p.B, DP * BL, p.Lp), BHn, p.Lp, p.scale, drk_part,
+          make_axis(p.B, p.dh, (int64_t)p.P * HD))};
+  TXL_TRY(after_launch(timed(K_BWD_BMM, stream, [&] { return launch_bmm64(prods, 3, stream); }),
+                       "dk, dval, dRk products", stream));
   TXL_TRY(after_launch(timed(K_BWD_AUX, stream, [&] {
                          return launch_sum_rows(drk_part, p.B, (int64_t)p.P * HD, g.d_Rk, stream);
                        }),

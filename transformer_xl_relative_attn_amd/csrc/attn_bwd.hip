@@ -379,7 +379,16 @@ __device__ __forceinline__ bf16x8 band_mask(bf16x8 f, int32_t lo, int32_t hi, bo
   return __builtin_bit_cast(bf16x8, w);
 }
 
-__global__ __launch_bounds__(256, 2) void bmm64_kernel(BmmArgs a) {
+// Up to three products in one launch (blockIdx.z): their workgroups share the
+// chip instead of each product's last partial round running alone.
+struct BmmBatch {
+  BmmArgs p[3];
+};
+
+__global__ __launch_bounds__(256, 2) void bmm64_kernel(BmmBatch bt) {
+  const int z = blockIdx.z;
+  const BmmArgs a = z == 0 ? bt.p[0] : z == 1 ? bt.p[1] : bt.p[2];
+  if ((int32_t)blockIdx.x * BMM_ROWS >= a.M || (int32_t)blockIdx.y >= a.batch) return;
   // B chunk: row n (1 KB) holds 16-byte chunk c at slot c ^ (n & 15), so the
   // 16 rows a fragment read serves at once sit on distinct bank groups
   __shared__ u32x4 bsm[64 * (BMM_KC / 8)];
@@ -688,10 +697,18 @@ int launch_attn_bwd_q(const BwdArgs& a, void* stream) {
   return static_cast<int>(hipGetLastError());
 }
 
-int launch_bmm64(const BmmArgs& a, void* stream) {
-  if (a.K % 16 != 0) return static_cast<int>(hipErrorInvalidValue);
-  hipLaunchKernelGGL(bmm64_kernel, dim3((a.M + BMM_ROWS - 1) / BMM_ROWS, a.batch), dim3(256), 0,
-                     static_cast<hipStream_t>(stream), a);
+int launch_bmm64(const BmmArgs* a, int n, void* stream) {
+  if (n < 1 || n > 3) return static_cast<int>(hipErrorInvalidValue);
+  BmmBatch bt{};
+  int32_t gx = 1, gy = 1;
+  for (int i = 0; i < n; ++i) {
+    if (a[i].K % 16 != 0) return static_cast<int>(hipErrorInvalidValue);
+    bt.p[i] = a[i];
+    gx = std::max(gx, (a[i].M + BMM_ROWS - 1) / BMM_ROWS);
+    gy = std::max(gy, a[i].batch);
+  }
+  hipLaunchKernelGGL(bmm64_kernel, dim3(gx, gy, n), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), bt);
   return static_cast<int>(hipGetLastError());
 }
 

@@ -261,7 +261,7 @@ int launch_layernorm(const float* resid, const float* parts, int32_t n_parts, in
                      void* stream);
 int launch_cast_f32(const void* src, float* dst, int64_t n, int32_t dtype, void* stream);
 int launch_attn_bwd_q(const BwdArgs& a, void* stream);
-int launch_bmm64(const BmmArgs& a, void* stream);
+int launch_bmm64(const BmmArgs* a, int n, void* stream);   // n <= 3 products, one launch
 int launch_bwd_prep(const BwdPrepArgs& a, void* stream);
 int launch_rk_transpose(const void* rk_ws, void* rkt, int32_t H, int32_t Pp, int32_t pad_ws,
                         int32_t ld, int32_t pad_t, void* stream);
