@@ -120,8 +120,17 @@ def cpu_baseline(cfg, wl, budget_s):
     el = time.perf_counter() - t0
     f = flops(cfg)["total"] * cfg.n_layers
     _ = np
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {"value": f * done / el / 1e12, "unit": "TFLOP/s", "cores": int(cores),
-            "kind": "oracle",
+            "cpu_model": model, "kind": "oracle",
             "sample": f"{done} consecutive segment(s) of the {cfg.name} workload, all "
                       f"{cfg.batch} batch rows, fp64 numpy oracle, {el:.1f} s",
             "tokens_per_s": cfg.batch * cfg.seg_len * done / el}
