@@ -60,8 +60,11 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_q_kernel(BwdArgs a) {
   const int32_t nqg = (a.L + 127) / 128;
   const int32_t wid = blockIdx.x;
   if (wid >= a.B * a.H * nqg) return;
-  const int32_t qg = wid % nqg;
-  const int32_t rest = wid / nqg;
+  // Later query groups see more keys (the causal part grows with i): they are
+  // dealt first, so that the shorter groups fill the last round of the chip.
+  const int32_t nbh = a.B * a.H;
+  const int32_t qg = nqg - 1 - wid / nbh;
+  const int32_t rest = wid % nbh;
   const int32_t b = rest % a.B, head = rest / a.B;
   const int32_t bh = b * a.H + head;
 
