@@ -33,8 +33,9 @@
 //     operand fragments of block t+1 are read from LDS; block t+1's (b)+(d)
 //     and (q+u).K products follow block t's P.V on the matrix cores.
 //   * P (bf16) times V^T on the matrix cores: bf16 pairs of P are exchanged
-//     with the partner lane so that both operands list the keys in order; P
-//     times a ones operand accumulates the softmax denominators.
+//     with the partner lane so that both operands list the keys in order.  The
+//     softmax denominators are per-lane sums of p (half of a column's keys
+//     each), joined with the partner lane at the end.
 //   * With several key-range splits each workgroup writes (max, sum, O) and
 //     attn_combine_kernel merges them in split order (deterministic).  The
 //     segment step's memory-ring update rides on that launch (or on the tail of
@@ -347,10 +348,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a, int32_t p
     S = qk(kf, read_win());
   }
 
-  bf16x8 ones;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) ones[e] = static_cast<bf16>(1.0f);
-  floatx16 lacc = floatx16{0};   // every row: sum_j p_ij of column ii
+  float lpart = 0.0f;             // sum of this lane's p (half of column ii's keys)
   floatx16 o[2] = {floatx16{0}, floatx16{0}};
   float m_ref = 0.0f;            // running reference maximum (lazy)
   bool fresh = true;             // no visible key seen yet
@@ -408,12 +406,18 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a, int32_t p
         for (int e = 0; e < 16; ++e) {
           o[0][e] *= alpha;
           o[1][e] *= alpha;
-          lacc[e] *= alpha;
         }
+        lpart *= alpha;
       }
       float p[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e) p[e] = __builtin_amdgcn_exp2f(S[e] - m_ref);
+      {
+        float s4[4];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) s4[g] = (p[4 * g] + p[4 * g + 1]) + (p[4 * g + 2] + p[4 * g + 3]);
+        lpart += (s4[0] + s4[1]) + (s4[2] + s4[3]);
+      }
       // The lane holds p for keys 16t2 + 4hf + {0..3} and 16t2 + 8 + 4hf +
       // {0..3}; swapping bf16 pairs with the partner lane gives it keys
       // 16t2 + 8hf .. +7 in order, the k-slots of the V^T fragment.
@@ -427,13 +431,12 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a, int32_t p
     }
     if (next_on) cur = bd_chunk(rf);   // chunk t+1-w
     if (cur_on) {
-      // P^T (keys x queries) times V^T; P times ones accumulates the row sums
+      // P^T (keys x queries) times V^T
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2) {
 #pragma unroll
         for (int e = 0; e < 2; ++e)
           o[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[t2][e], pb[t2], o[e], 0, 0, 0);
-        lacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pb[t2], lacc, 0, 0, 0);
       }
     }
     if (next_on) {
@@ -455,7 +458,11 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a, int32_t p
   // the repeated loads past the split's last block must land before exit
   wait_vm<0>();
 
-  const float l_sum = lacc[0];
+  float l_sum;   // both halves of the column's keys
+  {
+    const auto ll = __builtin_amdgcn_permlane32_swap(__float_as_uint(lpart), __float_as_uint(lpart), false, false);
+    l_sum = __uint_as_float(ll[0]) + __uint_as_float(ll[1]);
+  }
   const int32_t i = i0 + ii;
   typedef float floatx2_t __attribute__((ext_vector_type(2)));
   typedef bf16 bf16x2_t __attribute__((ext_vector_type(2)));
