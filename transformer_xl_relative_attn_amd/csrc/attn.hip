@@ -139,14 +139,16 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a, int32_t p
   const int32_t total = a.B * a.H * nqg * a.n_split;
   const int32_t wid = xcd_swizzle(blockIdx.x, padded);
   if (wid >= total) return;
-  // work order: split fastest, then query group, batch, head, so that the
+  // work order: split fastest, then batch, query group, head, so that the
   // work items dealt to one XCD share a head's position keys in its L2
   const int32_t split = wid % a.n_split;
   int32_t rest = wid / a.n_split;
-  const int32_t qg = rest % nqg;
-  rest /= nqg;
   const int32_t b = rest % a.B;
-  const int32_t head = rest / a.B;
+  rest /= a.B;
+  // within a head, later query groups (more visible keys) come first, so the
+  // shorter ones fill the last round of each XCD
+  const int32_t qg = nqg - 1 - rest % nqg;
+  const int32_t head = rest / nqg;
   const int32_t bh = b * a.H + head;
   const int32_t M = a.M, L = a.L;
 
