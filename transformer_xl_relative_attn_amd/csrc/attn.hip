@@ -13,9 +13,9 @@
 // in the lane and its partner (ii, 1-hf).
 //   * LDS-DMA ring: block t's K tile and V^T tile (4 KB each, contiguous in the
 //     workspace) and Rk chunk t (32 rows) are loaded by direct global->LDS
-//     loads NST blocks ahead.  The refill of a slot is issued right after the
-//     block barrier, and every wave issues exactly three loads per block, so
-//     the vmcnt waits are constants.  Wave w uses Rk chunk t+1-w at block t,
+//     loads three to four blocks ahead, two blocks at a time after the barrier
+//     that every second block takes; every wave issues exactly three loads per
+//     block, so the vmcnt waits are constants.  Wave w uses Rk chunk t+1-w at block t,
 //     so a chunk stays resident for four blocks.
 //   * Term (b)+(d): for block t+1 a wave multiplies its 32 queries (q+v) by the
 //     32-row Rk chunk that starts at distance D-31, D = M + i0 - 32(t+1), on the
@@ -255,9 +255,9 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a, int32_t p
   }
   compiler_fence();   // the q loads go out before the later blocks' DMA
 #pragma unroll
-  for (int s = 1; s < NST; ++s) issue_block(t_lo + s);
-  // everything but blocks t_lo+1 .. t_lo+NST-1 has landed
-  wait_vm<LOADS_PER_BLOCK * (NST - 1)>();
+  for (int s = 1; s < NST - 1; ++s) issue_block(t_lo + s);
+  // everything but blocks t_lo+1 .. t_lo+NST-2 has landed
+  wait_vm<LOADS_PER_BLOCK * (NST - 2)>();
   if (tid < 2 * DP) sm.uv[tid] = uvv;
   barrier_lds();
 
@@ -361,10 +361,16 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a, int32_t p
   // static and the two chunk products trade roles instead of being copied.
   auto block = [&](auto U, int32_t t, floatx16& cur, floatx16& prev) {
     constexpr int u = decltype(U)::value, un = (u + 1) % NST;
-    // block t+1 has landed once only blocks t+2 .. t+NST-1 may be in flight
-    wait_vm<LOADS_PER_BLOCK * (NST - 2)>();
-    barrier_lds();   // ... for every wave; block t's stage (read during block t-1) is free
-    issue_block(t + NST);
+    // One barrier per two blocks: at an even block t every block issued so far
+    // (up to t+2) has landed and, after the barrier, is visible to every wave,
+    // and the stages of blocks t-1 and t (read during blocks t-2 and t-1) take
+    // blocks t+3 and t+4.  Block t+1 then runs on data covered by this barrier.
+    if constexpr (u % 2 == 0) {
+      wait_vm<0>();
+      barrier_lds();
+      issue_block(t + NST - 1);
+      issue_block(t + NST);
+    }
 
     const bool cur_on = t < t_end;
     const bool next_on = t + 1 < t_end;
