@@ -138,6 +138,77 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const float* resid, cons
   }
 }
 
+// The same LayerNorm for rows of d <= 4096 floats with d % 4 == 0 and 16-byte
+// aligned operands: each thread owns the float4 chunks tid + 256k of its row
+// and issues the residual load and all NP partial loads of a chunk before it
+// adds them (residual first, then part 0, 1, ..., as layernorm_kernel), so
+// every load of a row is in flight at once instead of one after another.
+template <int NP>
+__global__ __launch_bounds__(256) void layernorm_vec_kernel(const float* resid, const float* parts,
+                                                            int64_t part_stride, float* y,
+                                                            void* y_lo, int32_t d,
+                                                            int32_t lo_dtype, float eps) {
+  __shared__ float red[4];
+  const int64_t row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int n4 = d >> 2;
+  floatx4 x[4];
+  float s = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int c4 = tid + 256 * k;
+    x[k] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    if (c4 < n4) {
+      const int64_t off = row * d + 4 * c4;
+      floatx4 ld[NP + 1];
+      ld[0] = *reinterpret_cast<const floatx4*>(resid + off);
+#pragma unroll
+      for (int p = 0; p < NP; ++p) ld[p + 1] = *reinterpret_cast<const floatx4*>(parts + p * part_stride + off);
+      floatx4 v = ld[0];
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] += ld[p + 1][e];
+      }
+      x[k] = v;
+      s += (v[0] + v[1]) + (v[2] + v[3]);
+    }
+  }
+  const float mean = block_sum256(s, red) / d;
+  float s2 = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    if (tid + 256 * k < n4) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float dv = x[k][e] - mean;
+        s2 += dv * dv;
+      }
+    }
+  }
+  const float rstd = rsqrtf(block_sum256(s2, red) / d + eps);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int c4 = tid + 256 * k;
+    if (c4 < n4) {
+      const int64_t off = row * d + 4 * c4;
+      floatx4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = (x[k][e] - mean) * rstd;
+      *reinterpret_cast<floatx4*>(y + off) = v;
+      if (y_lo) {
+        if (lo_dtype == TXL_F32) {
+          *reinterpret_cast<floatx4*>(static_cast<float*>(y_lo) + off) = v;
+        } else {
+          const uint32_t lo = f32_to_bf16_bits(v[0]) | (uint32_t)f32_to_bf16_bits(v[1]) << 16;
+          const uint32_t hi = f32_to_bf16_bits(v[2]) | (uint32_t)f32_to_bf16_bits(v[3]) << 16;
+          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(y_lo) + off) = make_uint2(lo, hi);
+        }
+      }
+    }
+  }
+}
+
 __global__ void cast_f32_kernel(const void* src, float* dst, int64_t n, int32_t dtype) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx < n) dst[idx] = load_as_f32(src, idx, dtype);
@@ -214,7 +285,22 @@ int launch_layernorm(const float* resid, const float* parts, int32_t n_parts, in
                      float* y_f32, void* y_lo, int32_t rows, int32_t d, int32_t lo_dtype, float eps,
                      void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (d <= 1024)
+  auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; };
+  const bool vec = d % 4 == 0 && d <= 4096 && n_parts >= 0 && n_parts <= 8 && al16(resid) &&
+                   (n_parts == 0 || (al16(parts) && part_stride % 4 == 0)) && al16(y_f32) &&
+                   (y_lo == nullptr || al16(y_lo));
+  if (vec) {
+#define TXL_LN_VEC(NP)                                                                          \
+  case NP:                                                                                     \
+    hipLaunchKernelGGL(layernorm_vec_kernel<NP>, dim3(rows), dim3(256), 0, st, resid, parts,   \
+                       part_stride, y_f32, y_lo, d, lo_dtype, eps);                            \
+    break;
+    switch (n_parts) {
+      TXL_LN_VEC(0) TXL_LN_VEC(1) TXL_LN_VEC(2) TXL_LN_VEC(3) TXL_LN_VEC(4)
+      TXL_LN_VEC(5) TXL_LN_VEC(6) TXL_LN_VEC(7) TXL_LN_VEC(8)
+    }
+#undef TXL_LN_VEC
+  } else if (d <= 1024)
     hipLaunchKernelGGL(layernorm_kernel<4>, dim3(rows), dim3(256), 0, st, resid, parts, n_parts,
                        part_stride, y_f32, y_lo, d, lo_dtype, eps);
   else if (d <= 4096)
