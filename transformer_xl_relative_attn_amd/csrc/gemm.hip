@@ -61,8 +61,12 @@ struct Var {
 //           projections, 118 vs 121 us at 4096^3.
 //   V128:   128x128, 4 waves of 64x64, two workgroups per CU (problems with
 //           few 256-tiles)
+//   V128W8: 128x128, 8 waves of 32x64, one workgroup per CU (problems with no
+//           more 128-tiles than compute units, which would otherwise leave
+//           one wave per SIMD and nothing to cover its waits)
 using V256W8 = Var<4, 2, 2, 4, TXL_GEMM_NSTAGE, 1>;
 using V128 = Var<2, 2, 2, 2, 4, 2>;
+using V128W8 = Var<1, 2, 4, 2, 4, 1>;
 
 // 128 bytes of zeros: the source of every "zero row" chunk (padding rows).
 __device__ __align__(16) uint32_t g_zero_chunk[32];
@@ -399,6 +403,9 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmGroup& g, int32_t padde
       if (x < NF) read_one(st, 1, x, f1a, f1b);
       __builtin_amdgcn_sched_barrier(0);
     }
+    // (a wave tile of fewer 32x32 blocks than fragments reads the rest here)
+#pragma unroll
+    for (int x = WM * WN; x < NF; ++x) read_one(st, 1, x, f1a, f1b);
     wait_vm<(NSTAGE - 2) * 2 * LOADS + EXTRA>();
     barrier_lds();
     u32x4* rs = smem + slot * STAGE_U + wave_s * 64;
@@ -514,6 +521,13 @@ __global__ __launch_bounds__(V128::NTH, 2) void gemm_bf16_t128_kernel(GemmGroup 
   gemm_bf16_body<V128>(g, padded, grid);
 }
 
+// 128x128 blocks of 8 waves (two per SIMD), one workgroup per CU
+__global__ __launch_bounds__(V128W8::NTH, 1) void gemm_bf16_t128w8_kernel(GemmGroup g,
+                                                                          int32_t padded,
+                                                                          int32_t grid) {
+  gemm_bf16_body<V128W8>(g, padded, grid);
+}
+
 // ------------------------------------------------------------------ fp32 GEMM
 constexpr int FT = 64, FK = 16;
 
@@ -591,12 +605,16 @@ int32_t device_cu_count() {
 
 int launch_tiles(const GemmGroup& g, bool small, void* stream) {
   const int32_t padded = (g.total_tiles + 7) & ~7;
-  // persistent workgroups, one (256x256) or two (128x128) per compute unit,
-  // a multiple of 8 (the XCD count)
-  int32_t grid = (device_cu_count() * (small ? 2 : 1) + 7) & ~7;
+  const int cus = device_cu_count();
+  // persistent workgroups, one (256x256, or 128x128 of 8 waves) or two
+  // (128x128 of 4 waves) per compute unit, a multiple of 8 (the XCD count)
+  const bool w8 = small && g.total_tiles <= cus;
+  int32_t grid = (cus * (small && !w8 ? 2 : 1) + 7) & ~7;
   if (grid > padded) grid = padded;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (small)
+  if (w8)
+    hipLaunchKernelGGL(gemm_bf16_t128w8_kernel, dim3(grid), dim3(V128W8::NTH), 0, st, g, padded, grid);
+  else if (small)
     hipLaunchKernelGGL(gemm_bf16_t128_kernel, dim3(grid), dim3(V128::NTH), 0, st, g, padded, grid);
   else
     hipLaunchKernelGGL(gemm_bf16_kernel, dim3(grid), dim3(V256W8::NTH), 0, st, g, padded, grid);
@@ -604,8 +622,9 @@ int launch_tiles(const GemmGroup& g, bool small, void* stream) {
 }
 
 // The group arrives tiled for 256x256 blocks.  A group with no more such
-// tiles than half the compute units is re-tiled for 128x128 blocks (two
-// workgroups per CU).
+// tiles than half the compute units is re-tiled for 128x128 blocks: two
+// workgroups of 4 waves per CU, or, if the 128x128 tiles do not outnumber the
+// compute units, one workgroup of 8 waves per tile.
 int launch_gemm_bf16(const GemmGroup& g, void* stream) {
   if (g.total_tiles <= 0) return 0;
   if (2 * g.total_tiles > device_cu_count()) return launch_tiles(g, false, stream);
