@@ -625,19 +625,60 @@ int launch_tiles(const GemmGroup& g, bool small, void* stream) {
 // tiles than half the compute units is re-tiled for 128x128 blocks: two
 // workgroups of 4 waves per CU, or, if the 128x128 tiles do not outnumber the
 // compute units, one workgroup of 8 waves per tile.
-int launch_gemm_bf16(const GemmGroup& g, void* stream) {
-  if (g.total_tiles <= 0) return 0;
-  if (2 * g.total_tiles > device_cu_count()) return launch_tiles(g, false, stream);
-  GemmGroup s = g;
-  s.total_tiles = 0;
-  for (int i = 0; i < s.count; ++i) {
-    GemmProblem& p = s.p[i];
-    p.tiles_m = (p.M + 127) / 128;
-    p.tiles_n = (p.N + 127) / 128;
+// The problems of g selected by `pick` (all if null), numbered afresh, in
+// tiles of `t` x `t`.
+GemmGroup regroup(const GemmGroup& g, const bool* pick, int t) {
+  GemmGroup s{};
+  for (int i = 0; i < g.count; ++i) {
+    if (pick && !pick[i]) continue;
+    GemmProblem p = g.p[i];
+    p.tiles_m = (p.M + t - 1) / t;
+    p.tiles_n = (p.N + t - 1) / t;
     p.tile_begin = s.total_tiles;
     s.total_tiles += p.tiles_m * p.tiles_n;
+    s.p[s.count++] = p;
   }
-  return launch_tiles(s, true, stream);
+  return s;
+}
+
+int launch_gemm_bf16(const GemmGroup& g, void* stream) {
+  if (g.total_tiles <= 0) return 0;
+  const int cus = device_cu_count();
+  if (2 * g.total_tiles <= cus) return launch_tiles(regroup(g, nullptr, 128), true, stream);
+  // A last round of 256x256 tiles less than a quarter full would take as long
+  // as a full one: the smallest problem that covers it (else the smallest
+  // ones together) moves to a 128x128 launch of its own, and the rest takes
+  // one round less (16-layer stack at memory 3800: the 64-tile Rk product of
+  // 568 tiles).
+  const int32_t excess = g.total_tiles % cus;
+  if (g.count > 1 && g.total_tiles > cus && excess > 0 && 4 * excess <= cus) {
+    bool pick[kMaxGroup] = {};
+    auto tiles = [&](int i) { return g.p[i].tiles_m * g.p[i].tiles_n; };
+    int one = -1;
+    for (int i = 0; i < g.count; ++i)
+      if (tiles(i) >= excess && (one < 0 || tiles(i) < tiles(one))) one = i;
+    int32_t moved = 0;
+    if (one >= 0) {
+      pick[one] = true;
+      moved = tiles(one);
+    } else {
+      while (moved < excess) {
+        int k = -1;
+        for (int i = 0; i < g.count; ++i)
+          if (!pick[i] && (k < 0 || tiles(i) < tiles(k))) k = i;
+        pick[k] = true;
+        moved += tiles(k);
+      }
+    }
+    if (2 * moved <= cus && moved < g.total_tiles) {
+      bool rest[kMaxGroup];
+      for (int i = 0; i < g.count; ++i) rest[i] = !pick[i];
+      const int e = launch_tiles(regroup(g, rest, 256), false, stream);
+      if (e) return e;
+      return launch_tiles(regroup(g, pick, 128), true, stream);
+    }
+  }
+  return launch_tiles(g, false, stream);
 }
 
 int launch_gemm_f32(const GemmGroup& g, void* stream) {
