@@ -145,7 +145,7 @@ __device__ __forceinline__ void epilogue_vec(const OutDst& o, const floatx16 (&a
     }
 }
 
-// bf16 output without residual / activation: the wave's WTM x WTN
+// bf16 output without a residual (ReLU optional): the wave's WTM x WTN
 // sub-tile (rows mw.., columns nw..) passes through the wave's own LDS region
 // in rounds of 32 rows, so that the global stores write whole lines (CPR
 // lanes cover one output row of the sub-tile contiguously) instead of
@@ -155,7 +155,7 @@ __device__ __forceinline__ void epilogue_vec(const OutDst& o, const floatx16 (&a
 // r (0..31) is CPR chunks of 16 bytes, chunk c at slot c ^ (r % CPR); both the
 // 8-byte writes (32 rows x 2 halves) and the 16-byte reads (CPR lanes per row)
 // are then spread over all 64 banks.
-template <class V>
+template <class V, bool RELU>
 __device__ __forceinline__ void epilogue_staged(const OutDst& o,
                                                 const floatx16 (&acc)[V::WM][V::WN], int32_t mw,
                                                 int32_t nw, int lane, u32x4* region) {
@@ -180,6 +180,7 @@ __device__ __forceinline__ void epilogue_staged(const OutDst& o,
   int64_t off = (int64_t)q0 * o.row.s1 + (int64_t)rem * o.row.s2 + coff;
   const int64_t step = RG * o.row.s2, wrap = o.row.s1 - (int64_t)o.row.div * o.row.s2;
   uint16_t* out = static_cast<uint16_t*>(o.p);
+  auto act = [](float x) { return RELU ? fmaxf(x, 0.0f) : x; };
 #pragma unroll
   for (int i = 0; i < WM; ++i) {
 #pragma unroll
@@ -187,10 +188,10 @@ __device__ __forceinline__ void epilogue_staged(const OutDst& o,
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int cc = 4 * j + q;   // columns 32j + 8q + 4*lhalf .. +3
-        const bf16x2_t lo =
-            __builtin_convertvector(floatx2_t{acc[i][j][4 * q], acc[i][j][4 * q + 1]}, bf16x2_t);
-        const bf16x2_t hi =
-            __builtin_convertvector(floatx2_t{acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]}, bf16x2_t);
+        const bf16x2_t lo = __builtin_convertvector(
+            floatx2_t{act(acc[i][j][4 * q]), act(acc[i][j][4 * q + 1])}, bf16x2_t);
+        const bf16x2_t hi = __builtin_convertvector(
+            floatx2_t{act(acc[i][j][4 * q + 2]), act(acc[i][j][4 * q + 3])}, bf16x2_t);
         *reinterpret_cast<u32x2*>(base + lrow * (CPR * 16) + ((cc ^ (lrow % CPR)) << 4) +
                                   8 * lhalf) =
             u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
@@ -231,7 +232,11 @@ __device__ __forceinline__ void epilogue(const GemmProblem& P, const floatx16 (&
   const int32_t mb = m0 + wm * WTM + lrow;
   const int32_t nb = n0 + wn * WTN + 4 * lhalf;
   if (o.vec8_ok && o.flags == 0) {
-    epilogue_staged<V>(o, acc, m0 + wm * WTM, n0 + wn * WTN, lane, smem + wave * EPI_U);
+    epilogue_staged<V, false>(o, acc, m0 + wm * WTM, n0 + wn * WTN, lane, smem + wave * EPI_U);
+    return;
+  }
+  if (o.vec8_ok && o.flags == EPI_RELU) {
+    epilogue_staged<V, true>(o, acc, m0 + wm * WTM, n0 + wn * WTN, lane, smem + wave * EPI_U);
     return;
   }
   if (o.vec_ok) {
@@ -498,7 +503,7 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmGroup& g, int32_t padde
     {
       const OutDst& o = g.p[cpidx].out;
       const int wms = wave_s / V::GN, wns = wave_s % V::GN;   // wave-uniform
-      pend = more && o.vec8_ok && o.flags == 0 && cm0 + wms * WTM + WTM <= o.m_valid &&
+      pend = more && o.vec8_ok && (o.flags & ~EPI_RELU) == 0 && cm0 + wms * WTM + WTM <= o.m_valid &&
              cn0 + wns * WTN + WTN <= o.n_valid;
     }
     epilogue<V>(g.p[cpidx], acc, cm0, cn0, wm, wn, lane, stage_out);
