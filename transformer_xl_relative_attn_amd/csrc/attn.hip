@@ -111,9 +111,13 @@ __device__ __forceinline__ void compiler_fence() { __asm__ volatile("" ::: "memo
 // dealt to `nworkers` workers of 256 threads.
 __device__ __forceinline__ void ring_copy(const AttnArgs& a, int32_t worker, int32_t nworkers,
                                           int tid) {
+  // the (row, 16-byte chunk) pairs of all copied rows, 256 consecutive ones
+  // per workgroup and pass, so that every thread copies one chunk per pass
   const int64_t chunks = a.upd_row_bytes / 16;
-  const int32_t nrow = a.B * a.upd_rows;
-  for (int32_t r = worker; r < nrow; r += nworkers) {
+  const int64_t n = (int64_t)a.B * a.upd_rows * chunks;
+  for (int64_t g = (int64_t)worker * 256 + tid; g < n; g += (int64_t)nworkers * 256) {
+    const int32_t r = (int32_t)(g / chunks);
+    const int64_t c = g - (int64_t)r * chunks;
     const int32_t bb = r / a.upd_rows, t = r - bb * a.upd_rows;
     const int32_t src = a.L < a.M ? t : a.L - a.M + t;
     const int32_t slot = a.L < a.M ? (a.upd_start + t) % a.M : t;
@@ -121,7 +125,7 @@ __device__ __forceinline__ void ring_copy(const AttnArgs& a, int32_t worker, int
         static_cast<const char*>(a.upd_src) + ((int64_t)bb * a.L + src) * a.upd_row_bytes);
     u32x4* dp = reinterpret_cast<u32x4*>(static_cast<char*>(a.upd_mem) +
                                          ((int64_t)bb * a.M + slot) * a.upd_row_bytes);
-    for (int64_t c = tid; c < chunks; c += 256) dp[c] = sp[c];
+    dp[c] = sp[c];
   }
 }
 
@@ -529,17 +533,18 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a, int32_t p
 }
 
 // Merge split partials in split order: with w_s = 2^(m_s-m*) l_s,
-// out = sum_s w_s (O_s / l_s) / sum_s w_s.  16 threads per output row, 4
-// columns each; the partials of all splits are loaded before any is used.  The workgroups past the output
-// rows copy the segment into the memory ring when the step asks for it.
+// out = sum_s w_s (O_s / l_s) / sum_s w_s.  8 threads per output row, 8
+// columns (16 bytes) each; the partials of all splits are loaded before any
+// is used.  The workgroups past the output rows copy the segment into the
+// memory ring when the step asks for it.
 template <int S>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, int32_t out_blocks) {
   if ((int32_t)blockIdx.x >= out_blocks) {
     ring_copy(a, blockIdx.x - out_blocks, gridDim.x - out_blocks, threadIdx.x);
     return;
   }
-  const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);   // (b, h, i), i < L
-  const int c4 = threadIdx.x & 15;
+  const int64_t row = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);   // (b, h, i), i < L
+  const int c8 = threadIdx.x & 7;
   const int64_t rows = (int64_t)a.B * a.H * a.L;
   if (row >= rows) return;
   const int32_t i = row % a.L;
@@ -550,7 +555,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, int32_t o
   const int ns = S > 0 ? S : a.n_split;
   constexpr int CAP = S > 0 ? S : 16;
   float ms[CAP], ls[CAP];
-  u32x2 os[CAP];   // four bf16 of O/sum
+  u32x4 os[CAP];   // eight bf16 of O/sum
 #pragma unroll
   for (int s = 0; s < CAP; ++s) {
     if (s < ns) {
@@ -558,40 +563,44 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a, int32_t o
       const float2 ml = reinterpret_cast<const float2*>(a.part_ml)[pr];
       ms[s] = ml.x;
       ls[s] = ml.y;
-      os[s] = reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(a.part_o) + pr * DP)[c4];
+      os[s] = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.part_o) + pr * DP)[c8];
     }
   }
   float mx = kNegInf;
 #pragma unroll
   for (int s = 0; s < CAP; ++s)
     if (s < ns) mx = fmaxf(mx, ms[s]);
-  floatx4 num = floatx4{0.f, 0.f, 0.f, 0.f};
+  float num[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float den = 0.0f;
 #pragma unroll
   for (int s = 0; s < CAP; ++s) {
     if (s < ns) {
       const float w = (ms[s] == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(ms[s] - mx) * ls[s];
-      const floatx4 x = floatx4{__uint_as_float(os[s][0] << 16), __uint_as_float(os[s][0] & 0xffff0000u),
-                                __uint_as_float(os[s][1] << 16), __uint_as_float(os[s][1] & 0xffff0000u)};
-      num += w * x;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        num[2 * e] += w * __uint_as_float(os[s][e] << 16);
+        num[2 * e + 1] += w * __uint_as_float(os[s][e] & 0xffff0000u);
+      }
       den += w;
     }
   }
   const float inv = 1.0f / den;
-  if (a.lse && c4 == 0) a.lse[prow] = mx + log2f(den);
+  if (a.lse && c8 == 0) a.lse[prow] = mx + log2f(den);
   uint16_t* out = static_cast<uint16_t*>(a.out) + ((int64_t)b * a.L + i) * a.H * a.dh +
                   (int64_t)head * a.dh;
   if (a.dh == DP) {
     typedef float floatx2_t __attribute__((ext_vector_type(2)));
     typedef bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-    const bf16x2_t lo = __builtin_convertvector(floatx2_t{num[0] * inv, num[1] * inv}, bf16x2_t);
-    const bf16x2_t hi = __builtin_convertvector(floatx2_t{num[2] * inv, num[3] * inv}, bf16x2_t);
-    *reinterpret_cast<u32x2*>(out + 4 * c4) =
-        u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+    u32x4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      v[e] = __builtin_bit_cast(
+          uint32_t, __builtin_convertvector(floatx2_t{num[2 * e] * inv, num[2 * e + 1] * inv}, bf16x2_t));
+    *reinterpret_cast<u32x4*>(out + 8 * c8) = v;
   } else {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int d = 4 * c4 + r;
+    for (int r = 0; r < 8; ++r) {
+      const int d = 8 * c8 + r;
       if (d < a.dh) out[d] = f32_to_bf16_bits(num[r] * inv);
     }
   }
@@ -676,9 +685,11 @@ int launch_attn_bf16(const AttnArgs& a, void* stream) {
 
 int launch_attn_combine(const AttnArgs& a, void* stream) {
   const int64_t rows = (int64_t)a.B * a.H * a.L;
-  const int32_t out_blocks = (int32_t)((rows + 15) / 16);
-  // the memory-ring copy (segment step) gets one workgroup per two rows
-  const int32_t copy_blocks = a.upd_mem ? (a.B * a.upd_rows + 1) / 2 : 0;
+  const int32_t out_blocks = (int32_t)((rows + 31) / 32);
+  // the memory-ring copy (segment step) gets one workgroup per 256 chunks of
+  // 16 bytes (two rows of d_model 1024 in bf16)
+  const int32_t copy_blocks =
+      a.upd_mem ? (int32_t)(((int64_t)a.B * a.upd_rows * (a.upd_row_bytes / 16) + 255) / 256) : 0;
   const dim3 grid(out_blocks + copy_blocks);
   hipStream_t st = static_cast<hipStream_t>(stream);
   switch (a.n_split) {
