@@ -383,3 +383,121 @@ def test_pins_catch_planted_mistakes(monkeypatch):
         monkeypatch.setattr(mod, "rel_attn_terms", mut)
         assert not _pins_pass(), f"pins missed planted mistake {mut.__name__}"
         monkeypatch.setattr(mod, "rel_attn_terms", orig)
+
+
+# ------------------------------------------------ N-layer recurrence (CPU)
+def _brute_stack_stream(wl, R, H, dh, scale, n_seg):
+    """Independent route for an N-layer stream (Sec. 3.2 recurrence and the
+    Sec. 3.3 summary equations, for n = 1..N): the attention of each layer is
+    the pure-Python brute force, the rest of the layer is torch's functional
+    linear / relu / layer_norm in float64, and layer n's memory is rebuilt from
+    scratch as the last M rows of everything layer n has been given as input
+    (its own input history), with no ring buffer."""
+    F = torch.nn.functional
+    T = torch.tensor
+    M = wl.cfg.mem_len
+    d = wl.cfg.d_model
+    hist = [wl.mem[n].copy() for n in range(len(wl.layers))]   # logical, oldest first
+    outs, per_layer = [], []
+    for s in range(n_seg):
+        x = wl.segments[s]
+        layer_outs = []
+        for n, lay in enumerate(wl.layers):
+            a, _ = brute.brute_rel_attn(_tolist(x), _tolist(hist[n][:, -M:] if M else hist[n][:, :0]),
+                                        _tolist(lay.W_q), _tolist(lay.W_kE), _tolist(lay.W_kR),
+                                        _tolist(lay.W_v), _tolist(wl.u), _tolist(wl.v),
+                                        _tolist(R), H, dh, scale)
+            a = T(np.array(a))
+            o = F.layer_norm(F.linear(a, T(lay.W_o)) + T(x), (d,), eps=1e-5)
+            y = F.layer_norm(o + F.linear(F.relu(F.linear(o, T(lay.W_ff1))), T(lay.W_ff2)),
+                             (d,), eps=1e-5).numpy()
+            hist[n] = np.concatenate([hist[n], x], axis=1)   # layer n cached its own input
+            layer_outs.append(y)
+            x = y
+        outs.append(x)
+        per_layer.append(layer_outs)
+    return outs, per_layer, [h[:, -M:] for h in hist]
+
+
+def _stack_case():
+    from synth import Config, make_workload
+    cfg = Config("stack3_tiny", batch=2, d_model=8, n_heads=2, d_head=4, seg_len=3, mem_len=4,
+                 n_layers=3, n_segments=3, dtype="f32", w_std=0.4, seed=31, d_inner=12)
+    return cfg, make_workload(cfg)
+
+
+def _stack_pin_passes():
+    cfg, wl = _stack_case()
+    H, dh, M = cfg.n_heads, cfg.d_head, cfg.mem_len
+    R = oracle.sinusoid(M + cfg.seg_len, cfg.d_model)
+    scale = 1.0 / math.sqrt(dh)
+    want, want_layers, want_mem = _brute_stack_stream(wl, R, H, dh, scale, cfg.n_segments)
+    mems = [m.copy() for m in wl.mem]
+    start = 0
+    for s in range(cfg.n_segments):
+        y, mems, start, layer_outs = oracle.segment_step(wl.segments[s], wl.layers, mems, start,
+                                                         wl.u, wl.v, R, H, dh, scale)
+        if np.max(np.abs(y - want[s])) > 1e-11:
+            return False
+        for n in range(cfg.n_layers):
+            if np.max(np.abs(layer_outs[n] - want_layers[s][n])) > 1e-11:
+                return False
+    for n in range(cfg.n_layers):
+        # layer 0 caches the segment inputs themselves (exact); deeper layers
+        # cache outputs of the layer below, formed by the two routes
+        got = oracle.logical_memory(mems[n], start)
+        if got.shape != want_mem[n].shape or np.max(np.abs(got - want_mem[n])) > 1e-11:
+            return False
+    return True
+
+
+def test_stack_recurrence_three_layers():
+    """Three full layers (W_o, LayerNorm, ReLU feed-forward), each with its own
+    memory, over three segments with L < M: every layer output and final ring of
+    oracle.segment_step equals the independent brute-force route."""
+    assert _stack_pin_passes()
+
+
+def _stack_mutants(orig):
+    """Plausible mistakes in the N-layer recurrence, each a variant of
+    segment_step (Sec. 3.3 summary: layer n attends over [SG(m^{n-1}) ; h^{n-1}]
+    and caches h^{n-1})."""
+    from oracle import oracle as mod
+
+    def run(h, layers, mems, start, u, v, R, H, dh, scale=None, Rks=None, *, seg_input=False,
+            shared_mem=False, cache_output=False):
+        outs, new_mems, x, new_start = [], [], h, start
+        for n, lay in enumerate(layers):
+            src = mems[0] if shared_mem else mems[n]
+            inp = h if seg_input else x
+            a = mod.rel_attn_fwd(inp, mod.logical_memory(src, start), lay.W_q, lay.W_kE, lay.W_kR,
+                                 lay.W_v, u, v, R, H, dh, scale)
+            y = mod.stack_layer(a, inp, lay.W_o, lay.W_ff1, lay.W_ff2)
+            m_new, new_start = mod.mem_update(src, start, y if cache_output else inp)
+            new_mems.append(m_new)
+            outs.append(y)
+            x = y
+        return x, new_mems, new_start, outs
+
+    def segment_input_to_every_layer(*a, **k):
+        return run(*a, **k, seg_input=True)
+
+    def one_shared_memory(*a, **k):
+        return run(*a, **k, shared_mem=True)
+
+    def memory_caches_layer_output(*a, **k):
+        return run(*a, **k, cache_output=True)
+
+    return [segment_input_to_every_layer, one_shared_memory, memory_caches_layer_output]
+
+
+def test_stack_pin_catches_planted_mistakes(monkeypatch):
+    from oracle import oracle as mod
+    orig = mod.segment_step
+    assert _stack_pin_passes()
+    for mut in _stack_mutants(orig):
+        monkeypatch.setattr(mod, "segment_step", mut)
+        monkeypatch.setattr(oracle, "segment_step", mut)
+        assert not _stack_pin_passes(), f"stack pin missed planted mistake {mut.__name__}"
+        monkeypatch.setattr(mod, "segment_step", orig)
+        monkeypatch.setattr(oracle, "segment_step", orig)
