@@ -408,8 +408,10 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a, int32_t p
       }
       const bool need = mb > m_ref + 8.0f || (fresh && mb > kNegInf);
       if (__builtin_expect(__ballot(need) != 0, 0)) {
-        // move the reference up to mb and rescale the accumulators
-        const float alpha = need ? __builtin_amdgcn_exp2f(m_ref - mb) : 1.0f;
+        // move the reference up to mb and rescale the accumulators.  Before the
+        // first visible key they are still zero and the old reference means
+        // nothing: alpha = 0 (2^(0 - mb) would overflow for mb < -128).
+        const float alpha = need ? (fresh ? 0.0f : __builtin_amdgcn_exp2f(m_ref - mb)) : 1.0f;
         if (need) {
           m_ref = mb;
           fresh = false;
