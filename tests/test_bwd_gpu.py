@@ -3,8 +3,7 @@ backward (oracle.backward, pinned by finite differences and torch autograd).
 
 Tolerance as for the bf16 path: max|gpu - oracle| <= 2e-2 * max|oracle| per
 gradient tensor.  Gradients that sum over batch rows (d_Rk, d_u, d_v, d_W_kR)
-are compared whole; per-row gradients of the train-shaped workload (22 batch
-rows) are compared on sampled rows (rows never mix)."""
+are compared whole, for the full train-shaped batch (22 rows) too."""
 import numpy as np
 import pytest
 
@@ -22,7 +21,7 @@ def txl():
     return mod
 
 
-def _run(txl, cfg, b_idx, use_rk=False, with_wkr=True, seed=7):
+def _run(txl, cfg, b_idx, use_rk=False, with_wkr=True, seed=7, oracle_rows=False):
     import torch
     import oracle
     log(f"[case] backward {cfg.name} B={cfg.batch} L={cfg.seg_len} M={cfg.mem_len} "
@@ -59,9 +58,15 @@ def _run(txl, cfg, b_idx, use_rk=False, with_wkr=True, seed=7):
     lay = wl.layers[0]
     R = oracle.sinusoid(P, c.d_pos)
     scale = 1.0 / np.sqrt(dh)
-    want = oracle.backward.rel_attn_bwd(wl.segments[0][b_idx], wl.mem[0][b_idx], lay.W_q,
-                                        lay.W_kE, lay.W_kR, lay.W_v, wl.u, wl.v, R, H, dh, scale,
-                                        G[b_idx], Rk=Rk_host)
+    if oracle_rows:
+        from oracle_pool import oracle_bwd_rows
+        assert not use_rk and np.array_equal(b_idx, np.arange(B))
+        log(f"  oracle backward on {B} rows in worker processes")
+        want = oracle_bwd_rows(cfg, seed)
+    else:
+        want = oracle.backward.rel_attn_bwd(wl.segments[0][b_idx], wl.mem[0][b_idx], lay.W_q,
+                                            lay.W_kE, lay.W_kR, lay.W_v, wl.u, wl.v, R, H, dh,
+                                            scale, G[b_idx], Rk=Rk_host)
     assert_close(from_dev(d_q)[b_idx], want["q"], "bf16", "d_q")
     assert_close(from_dev(d_k)[b_idx], want["k"], "bf16", "d_k")
     assert_close(from_dev(d_val)[b_idx], want["val"], "bf16", "d_val")
@@ -116,10 +121,14 @@ def test_bwd_train_shaped_two_rows(txl):
     _check_summed(got, want, True)
 
 
-def test_bwd_train_shaped_full_batch_sampled(txl):
-    """The full train-shaped batch (22 rows): per-row gradients on sampled rows."""
+def test_bwd_train_shaped_full_batch(txl):
+    """The full train-shaped batch (22 rows): every row's d_q, d_k, d_val, and
+    the gradients summed over all 22 rows (d_Rk, d_u, d_v, d_W_kR), which go
+    through the per-row ordered sums.  The oracle runs one row per worker
+    process."""
     cfg = synth.get_config("train_l512_m512")
-    _run(txl, cfg, np.array([0, 21]), with_wkr=False)
+    got, want = _run(txl, cfg, np.arange(cfg.batch), oracle_rows=True)
+    _check_summed(got, want, True)
 
 
 def test_bwd_long_segment(txl):

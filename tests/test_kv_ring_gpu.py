@@ -11,6 +11,7 @@ import pytest
 import synth
 from gpu_helpers import (DeviceLayers, assert_close, from_dev, log, oracle_stream,
                          run_attn_stream, tdtype, to_dev, txl_dtype, workspace)
+from oracle_pool import oracle_stream_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -182,7 +183,8 @@ def test_segment_ring_stack_16_layers(txl):
     log("[case] kv-ring 16-layer stack, 4 segments")
     wl = synth.make_workload(cfg)
     outs = run_segment_ring_stream(wl, 4)
-    b_idx = np.array([0])
-    o_outs, _, _ = oracle_stream(wl, 4, b_idx)
+    b_idx = np.arange(cfg.batch)
+    log(f"  oracle on {cfg.batch} rows in worker processes")
+    o_outs, _, _, _ = oracle_stream_rows(cfg, 4, b_idx, chunk=1)
     for s in range(4):
         assert_close(outs[s][b_idx], o_outs[s], "bf16", f"segment {s}")

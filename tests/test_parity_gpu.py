@@ -3,8 +3,9 @@
 Tolerances: max|gpu - oracle| <= 1e-4 * max|oracle| on the fp32 path and
 <= 2e-2 * max|oracle| on the bf16-in / fp32-accumulate path.  Memory rings
 after an update are compared bit for bit (they are copies of the inputs).
-Large workloads run whole on the GPU and are compared on sampled batch rows
-(rows never mix, see test_oracle.test_batch_independence).
+Every workload is compared on all of its batch rows; the larger ones run the
+oracle's rows in parallel worker processes (rows never mix, see
+test_oracle.test_batch_independence).
 """
 import numpy as np
 import pytest
@@ -13,6 +14,7 @@ import synth
 from gpu_helpers import (DeviceLayers, TOL, assert_close, bf16_bits_of, from_dev, log,
                          oracle_stream, run_attn_stream, run_segment_stream, tdtype, to_dev,
                          txl_dtype, workspace)
+from oracle_pool import oracle_stream_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -85,16 +87,19 @@ def test_rel_proj(txl, dtype, n_pos, d_pos, H, dh):
 
 
 # --------------------------------------------------- single layer workloads
-def _stream_case(txl, cfg, n_seg, b_idx, start=0, use_rk=False, scale=0.0):
+def _stream_case(txl, cfg, n_seg, b_idx, start=0, use_rk=False, scale=0.0, parallel=False):
     log(f"[case] {cfg.name} B={cfg.batch} L={cfg.seg_len} M={cfg.mem_len} H={cfg.n_heads} "
         f"dh={cfg.d_head} d={cfg.d_model} {cfg.dtype} segs={n_seg} start={start} rk={use_rk}")
     wl = synth.make_workload(cfg, n_segments=n_seg)
     outs, dl, start_g = run_attn_stream(wl, n_seg, scale=scale, start=start, use_rk=use_rk)
-    if start and cfg.mem_len:
-        import oracle
-        # the oracle sees the same logical memory; its own ring starts at 0
-        _ = oracle
-    o_outs, o_mems, start_o = oracle_stream(wl, n_seg, b_idx, scale if scale > 0 else None)
+    # the oracle sees the same logical memory (with a rotated GPU ring too); its
+    # own ring starts at 0
+    if parallel:
+        log(f"  oracle on {len(b_idx)} rows in worker processes")
+        o_outs, _, o_mems, start_o = oracle_stream_rows(cfg, n_seg, b_idx,
+                                                        scale if scale > 0 else None)
+    else:
+        o_outs, o_mems, start_o = oracle_stream(wl, n_seg, b_idx, scale if scale > 0 else None)
     for s in range(n_seg):
         assert_close(outs[s][b_idx], o_outs[s], cfg.dtype, f"segment {s}")
     if not start:
@@ -109,17 +114,17 @@ def test_tiny_fp32_two_segments(txl):
 
 def test_odd_head_dim(txl):
     cfg = synth.get_config("odd_head41")
-    _stream_case(txl, cfg, 1, np.array([0, 7, 15]))
+    _stream_case(txl, cfg, 1, np.arange(cfg.batch), parallel=True)
 
 
 def test_train_shaped(txl):
     cfg = synth.get_config("train_l512_m512")
-    _stream_case(txl, cfg, 4, np.array([0, 21]))
+    _stream_case(txl, cfg, 4, np.arange(cfg.batch), parallel=True)
 
 
 def test_eval_shaped(txl):
     cfg = synth.get_config("eval_l128_m1600")
-    _stream_case(txl, cfg, 8, np.array([0, 5]))
+    _stream_case(txl, cfg, 8, np.arange(cfg.batch), parallel=True)
 
 
 def test_eval_with_cached_rk(txl):
@@ -183,8 +188,8 @@ def test_segment_step_single_layer_eval(txl):
     log("[case] segment_step eval layer, 8 segments")
     wl = synth.make_workload(cfg, n_segments=8)
     outs, dl, start = run_segment_stream(wl, 8)
-    b_idx = np.array([0, 7])
-    o_outs, o_mems, start_o = oracle_stream(wl, 8, b_idx)
+    b_idx = np.arange(cfg.batch)
+    o_outs, _, o_mems, start_o = oracle_stream_rows(cfg, 8, b_idx)
     for s in range(8):
         assert_close(outs[s][b_idx], o_outs[s], "bf16", f"segment {s}")
     _check_ring(dl, wl, o_mems, start_o, start, b_idx)
@@ -223,16 +228,51 @@ def test_segment_step_stack_f32(txl, d, H, dh):
 
 
 def test_stack_16_layers(txl):
+    """The 16-layer stack over 4 segments, all batch rows, against the oracle.
+    Per-layer outputs: the same stream is run a second time one layer per
+    txl_segment_step call (fresh memories, the shared ring start passed to each
+    layer's call), and every layer's output of that chain is compared with the
+    oracle's output of the same layer.  (The chain hands bf16 outputs from call
+    to call, while one 16-layer call keeps the LayerNorm output in fp32 for the
+    next residual, so the two agree to rounding, not bit for bit.)"""
+    import torch
+    import transformer_xl_relative_attn_amd as txl_mod
     cfg = synth.get_config("stack16_l128_m3800")
     log("[case] 16-layer stack, 4 segments")
     wl = synth.make_workload(cfg)
     outs, dl, start = run_segment_stream(wl, 4)
-    b_idx = np.array([0])
-    o_outs, o_mems, start_o = oracle_stream(wl, 4, b_idx)
+    log("  one layer per call")
+    dl1 = DeviceLayers(wl)
+    shp = dl1.shape()
+    ws = workspace(txl_mod.txl_segment_workspace_bytes(shp, 1, cfg.d_inner))
+    layers = dl1.layer_structs()
+    st = 0
+    per_layer = []
     for s in range(4):
-        assert_close(outs[s][b_idx], o_outs[s], "bf16", f"segment {s}")
+        x = to_dev(wl.segments[s], "bf16")
+        ys = []
+        new_st = st
+        for n in range(cfg.n_layers):
+            y = torch.empty_like(x)
+            new_st = txl_mod.txl_segment_step(shp, 1, cfg.d_inner, [layers[n]], dl1.R, x, y, st,
+                                              ws)
+            ys.append(y)
+            x = y
+        st = new_st
+        torch.cuda.synchronize()
+        per_layer.append([from_dev(y) for y in ys])
+    assert st == start
+    b_idx = np.arange(cfg.batch)
+    log(f"  oracle on {cfg.batch} rows in worker processes")
+    o_outs, o_layers, o_mems, start_o = oracle_stream_rows(cfg, 4, b_idx, chunk=1)
+    for s in range(4):
+        for n in range(cfg.n_layers):
+            assert_close(per_layer[s][n], o_layers[s][n], "bf16", f"segment {s} layer {n}")
+        assert_close(outs[s], o_outs[s], "bf16", f"segment {s}")
+        assert_close(per_layer[s][-1], outs[s], "bf16", f"segment {s}: chain vs 16-layer call")
     _check_ring(dl, wl, o_mems, start_o, start, b_idx, layer=0, exact=True)
-    _check_ring(dl, wl, o_mems, start_o, start, b_idx, layer=15, exact=False)
+    for n in range(1, cfg.n_layers):
+        _check_ring(dl, wl, o_mems, start_o, start, b_idx, layer=n, exact=False)
 
 
 def test_segment_step_in_place(txl):
