@@ -547,6 +547,17 @@ def main():
     gpu_ms = ev0.elapsed_time(ev1)
     ms_per_step = max(gpu_ms, wall * 1e3) / args.steps
 
+    # ---- median step time over at least 50 steps, one event between steps
+    n_med = max(50, args.steps)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_med + 1)]
+    torch.cuda.synchronize()
+    evs[0].record(stream)
+    for r in range(n_med):
+        step()
+        evs[r + 1].record(stream)
+    torch.cuda.synchronize()
+    med_ms = float(np.median([evs[r].elapsed_time(evs[r + 1]) for r in range(n_med)]))
+
     # ---- per-kernel timing with HIP events on the launch stream
     txl.txl_timing_reset()
     txl.txl_timing_enable(True)
@@ -675,6 +686,9 @@ def main():
                    "parallelism": "single GPU"},
         "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "tokens_per_s": round(tokens, 1),
+        "median_step": {"ms": round(med_ms, 4), "reps": n_med,
+                        "tflops": round(f_step / (med_ms * 1e-3) / 1e12, 2),
+                        "tokens_per_s": round(cfg.batch * cfg.seg_len / (med_ms * 1e-3), 1)},
         "gflop_per_step": round(f_step / 1e9, 3),
         "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv)
                         for kk, vv in d.items()} for k, d in kernels.items()},

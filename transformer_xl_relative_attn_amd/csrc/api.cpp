@@ -75,7 +75,8 @@ txl_status_t after_launch(int err, const char* what, void* stream) {
 
 // ------------------------------------------------------------ kernel timing
 // Optional diagnostics: when enabled, every kernel launch is bracketed by two
-// HIP events recorded on the launch stream; txl_timing_read() waits for them.
+// HIP events (created without the system-scope fence) recorded on the launch
+// stream; txl_timing_read() waits for them.
 enum Kind : int {
   K_PROJ_GEMM, K_ATTN, K_ATTN_COMBINE, K_MEM_UPDATE, K_REL_PROJ, K_WO_GEMM, K_FFN1_GEMM,
   K_FFN2_GEMM, K_LAYERNORM, K_PACK, K_SINUSOID, K_CAST, K_REPACK_RK, K_BWD_Q, K_BWD_BMM,
@@ -106,8 +107,10 @@ hipEvent_t take_event(TimingState& t) {
     t.pool.pop_back();
     return e;
   }
+  // timing-only events: no system-scope fence (cache writeback) when they
+  // are recorded, so the bracket measures the kernel rather than the fence
   hipEvent_t e = nullptr;
-  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
   return e;
 }
 
@@ -228,13 +231,15 @@ AttnPlan make_plan(const txl_attn_shape_t* s, bool compute_rk, int kind = PLAN_S
   p.nqg = (p.L + 127) / 128;
   p.n_split = 1;
   if (bf) {
-    // Key-range splits fill the 512 workgroup slots (256 CUs, two each) in one
-    // round: S = floor(512 / work items), so a split never adds a partial
-    // round (measured: d_head 41, L = M = 150, 320 items: 1 split 23 us, 2
-    // splits 25 us plus the combine).  Every split keeps >= 4 key blocks.
+    // Key-range splits fill the workgroup slots (two per compute unit) in one
+    // round: S = floor(slots / work items), so a split never adds a partial
+    // round (measured on 256 CUs: d_head 41, L = M = 150, 320 items: 1 split
+    // 23 us, 2 splits 25 us plus the combine).  Every split keeps >= 4 key
+    // blocks.
     const int64_t wgs = (int64_t)p.B * p.H * p.nqg;
+    const int64_t slots = 2 * (int64_t)device_cu_count();
     const int nb_min = (p.Mk + std::min(p.L, 128) + 31) / 32;
-    int want = (int)std::min<int64_t>(512 / wgs, 16);
+    int want = (int)std::min<int64_t>(slots / wgs, 16);
     want = std::min(want, std::max(1, nb_min / 4));
     p.n_split = std::max(1, want);
   }
@@ -1051,6 +1056,7 @@ txl_status_t segment_step(const txl_attn_shape_t* shape, int32_t n_layers, int32
 }
 
 }  // namespace
+
 }  // namespace txl
 
 using namespace txl;
