@@ -133,6 +133,25 @@ txl_status_t txl_rel_attn_fwd(const txl_attn_shape_t* shape, const void* h, cons
                               size_t workspace_bytes, void* stream);
 
 /*
+ * txl_rel_attn_fwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments without the workspace, the same result and errors.  The
+ * temporaries live in a static device array of TXL_STATIC_SCRATCH_BYTES that
+ * every GPU the library runs on holds until the process ends.  A shape whose
+ * txl_rel_attn_workspace_bytes() exceeds that returns
+ * TXL_ERR_WORKSPACE_TOO_SMALL before anything is launched.  The call makes no
+ * device allocation (and records no timing events).  All calls on one GPU
+ * share its array and leave their contents in it: calls that overlap on one
+ * GPU (different streams or threads) race, so the caller must order them.
+ */
+#define TXL_STATIC_SCRATCH_BYTES (96u << 20)
+txl_status_t txl_rel_attn_fwd_static(const txl_attn_shape_t* shape, const void* h,
+                                     const void* mem, int32_t mem_start, const void* W_q,
+                                     const void* W_kE, const void* W_kR, const void* W_v,
+                                     const void* u, const void* v, const void* R, const void* Rk,
+                                     void* out, void* stream);
+
+/*
  * Backward of txl_rel_attn_fwd (bf16 inputs; fp32 gradients).  Gradients flow
  * within the segment only: Sec. 3.2 puts a stop-gradient on the cached
  * memory, so nothing is returned for `mem`, while the keys and values computed

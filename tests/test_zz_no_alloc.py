@@ -1,0 +1,67 @@
+"""txl_rel_attn_fwd_static (the entry point for callers that cannot allocate)
+against txl_rel_attn_fwd with a caller workspace: two calls in a row on the
+same static scratch, the second with a smaller input, each bit-identical to the
+workspace entry point (same kernels, same operands); a shape beyond the static
+maximum is rejected before any launch."""
+import numpy as np
+import pytest
+
+import synth
+from gpu_helpers import DeviceLayers, log, to_dev, workspace
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def txl():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import transformer_xl_relative_attn_amd as mod
+    return mod
+
+
+def _pair(txl, cfg):
+    import torch
+    wl = synth.make_workload(cfg, n_segments=1)
+    dl = DeviceLayers(wl)
+    shp = dl.shape()
+    need = txl.txl_rel_attn_workspace_bytes(shp)
+    assert 0 < need <= txl.TXL_STATIC_SCRATCH_BYTES
+    w = dl.W[0]
+    h = to_dev(wl.segments[0], cfg.dtype)
+    mem = dl.mem[0] if cfg.mem_len else None
+    start = 3 if cfg.mem_len > 3 else 0
+    out_ref = torch.empty((cfg.batch, cfg.seg_len, cfg.n_heads * cfg.d_head),
+                          dtype=h.dtype, device="cuda")
+    out = torch.full_like(out_ref, float("nan"))
+    ws = workspace(need)
+    txl.txl_rel_attn_fwd(shp, h, mem, start, w["W_q"], w["W_kE"], w["W_kR"], w["W_v"], dl.u,
+                         dl.v, dl.R, None, out_ref, ws)
+    txl.txl_rel_attn_fwd_static(shp, h, mem, start, w["W_q"], w["W_kE"], w["W_kR"], w["W_v"],
+                                dl.u, dl.v, dl.R, None, out)
+    torch.cuda.synchronize()
+    return out, out_ref
+
+
+def test_static_scratch_two_calls(txl):
+    import torch
+    big = synth.get_config("eval_l128_m1600")
+    small = synth.Config("static_small", 2, 256, 4, 64, 96, 200, 1, 1, "bf16", 0.05, 808)
+    for cfg in (big, small):
+        log(f"[case] static scratch {cfg.name} B={cfg.batch} L={cfg.seg_len} M={cfg.mem_len}")
+        out, ref = _pair(txl, cfg)
+        assert torch.isfinite(out.float()).all()
+        assert torch.equal(out, ref), f"{cfg.name}: differs from txl_rel_attn_fwd"
+
+
+def test_static_scratch_rejects_large_shape(txl):
+    import torch
+    cfg = synth.get_config("eval_l128_m1600", batch=64)
+    shp = txl.AttnShape(cfg.batch, cfg.seg_len, cfg.mem_len, cfg.d_model, cfg.n_heads,
+                        cfg.d_head, cfg.d_pos, txl.TXL_BF16, 0.0)
+    assert txl.txl_rel_attn_workspace_bytes(shp) > txl.TXL_STATIC_SCRATCH_BYTES
+    t = torch.empty(16, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(txl.TxlError) as ei:
+        txl.txl_rel_attn_fwd_static(shp, t, t, 0, t, t, t, t, t, t, t, None, t)
+    assert ei.value.status == 4     # TXL_ERR_WORKSPACE_TOO_SMALL
+    _ = np

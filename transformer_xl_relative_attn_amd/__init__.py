@@ -18,7 +18,8 @@ __all__ = [
     "TXL_F32", "TXL_BF16", "TxlError", "AttnShape", "Layer", "lib", "lib_path",
     "txl_abi_version", "txl_status_str", "txl_last_error", "txl_sinusoid_pos",
     "txl_rel_proj_workspace_bytes", "txl_rel_proj", "txl_rel_attn_workspace_bytes",
-    "txl_rel_attn_fwd", "txl_mem_update", "txl_segment_workspace_bytes", "txl_segment_step",
+    "txl_rel_attn_fwd", "txl_rel_attn_fwd_static", "TXL_STATIC_SCRATCH_BYTES",
+    "txl_mem_update", "txl_segment_workspace_bytes", "txl_segment_step",
     "txl_kv_ring_slots", "txl_kv_ring_bytes", "txl_kv_ring_workspace_bytes", "txl_kv_ring_init",
     "txl_rel_attn_fwd_kv", "txl_segment_kv_workspace_bytes", "txl_segment_step_kv",
     "txl_rel_attn_bwd_workspace_bytes", "txl_rel_attn_bwd", "txl_rel_attn_fwd_train",
@@ -72,6 +73,10 @@ _attn_ws = _sig("txl_rel_attn_workspace_bytes", _sz, [ctypes.POINTER(AttnShape)]
 _attn = _sig("txl_rel_attn_fwd", ctypes.c_int,
              [ctypes.POINTER(AttnShape), _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
               _vp, _vp, _vp, _sz, _vp])
+_attn_static = _sig("txl_rel_attn_fwd_static", ctypes.c_int,
+                    [ctypes.POINTER(AttnShape), _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
+                     _vp, _vp, _vp, _vp])
+TXL_STATIC_SCRATCH_BYTES = 96 << 20
 _memup = _sig("txl_mem_update", ctypes.c_int,
               [_vp, ctypes.POINTER(_i32), _vp, _i32, _i32, _i32, _i32, _i32, _vp])
 _seg_ws = _sig("txl_segment_workspace_bytes", _sz, [ctypes.POINTER(AttnShape), _i32, _i32])
@@ -179,6 +184,13 @@ def txl_rel_attn_fwd(shape: AttnShape, h, mem, mem_start: int, W_q, W_kE, W_kR, 
     _check(_attn(ctypes.byref(shape), _ptr(h), _ptr(mem), mem_start, _ptr(W_q), _ptr(W_kE),
                  _ptr(W_kR), _ptr(W_v), _ptr(u), _ptr(v), _ptr(R), _ptr(Rk), _ptr(out),
                  _ptr(workspace), _nbytes(workspace), _stream(stream)), "txl_rel_attn_fwd")
+
+
+def txl_rel_attn_fwd_static(shape: AttnShape, h, mem, mem_start: int, W_q, W_kE, W_kR, W_v, u, v,
+                            R, Rk, out, stream=None):
+    _check(_attn_static(ctypes.byref(shape), _ptr(h), _ptr(mem), mem_start, _ptr(W_q),
+                        _ptr(W_kE), _ptr(W_kR), _ptr(W_v), _ptr(u), _ptr(v), _ptr(R), _ptr(Rk),
+                        _ptr(out), _stream(stream)), "txl_rel_attn_fwd_static")
 
 
 def txl_mem_update(mem, mem_start: int, h, batch, mem_len, seg_len, d_model, dtype,

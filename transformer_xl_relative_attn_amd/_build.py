@@ -17,7 +17,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtxl.so")
 ARCH = "gfx950"
 
-SOURCES = ["gemm.hip", "attn.hip", "attn_bwd.hip", "misc.hip", "api.cpp"]
+SOURCES = ["gemm.hip", "attn.hip", "attn_bwd.hip", "misc.hip", "static_scratch.hip", "api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

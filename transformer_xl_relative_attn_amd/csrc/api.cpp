@@ -114,13 +114,16 @@ hipEvent_t take_event(TimingState& t) {
   return e;
 }
 
+// Set while a call must not create events (the no-allocation entry point).
+thread_local bool g_timing_suppressed = false;
+
 // Run a launch function, bracketed by timing events when timing is on.
 template <class F>
 int timed(int kind, void* stream, F&& launch) {
   TimingState& t = timing();
   hipEvent_t a = nullptr, b = nullptr;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  {
+  if (!g_timing_suppressed) {
     std::lock_guard<std::mutex> lk(t.mu);
     if (t.on) {
       a = take_event(t);
@@ -1056,6 +1059,10 @@ txl_status_t segment_step(const txl_attn_shape_t* shape, int32_t n_layers, int32
 }
 
 }  // namespace
+
+txl_status_t set_error(txl_status_t st, const char* msg) { return fail(st, "%s", msg); }
+
+void suppress_timing(bool on) { g_timing_suppressed = on; }
 
 }  // namespace txl
 

@@ -181,6 +181,12 @@ struct AttnArgs {
 // Compute units of the current device (cached per device id).
 int32_t device_cu_count();
 
+// Record `msg` as the calling thread's last error and return st.
+txl_status_t set_error(txl_status_t st, const char* msg);
+
+// While set on the calling thread, the timing diagnostics record no events.
+void suppress_timing(bool on);
+
 // Backward of the bf16 attention core (attn_bwd.hip).  Gradients are taken
 // with respect to the score s = scale * A (dS), then scaled by `scale`.
 struct BwdArgs {
