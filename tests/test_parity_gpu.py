@@ -64,8 +64,39 @@ def test_sinusoid(txl, dtype):
     if dtype == "f32":
         assert np.max(np.abs(got - want)) <= 1e-7
     else:
-        # one rounding of the fp64 value: within half a bf16 ulp (2^-9 relative)
-        assert np.all(np.abs(got - want) <= np.abs(want) * 2.0 ** -8 + 1e-30)
+        # One rounding of the fp64 value to the nearest bf16 (ties to even),
+        # computed here exactly in float64: the two bf16 neighbours of x and
+        # their midpoint are exact float64 numbers.  Values within 1e-9 of a
+        # midpoint are exempt (fp64 sin/cos may differ in the last bits).
+        lo = _bf16_toward_zero(want)
+        ulp = _bf16_ulp(lo)
+        hi = lo + np.sign(want) * ulp
+        mid = (lo + hi) / 2
+        away = np.abs(want) > np.abs(mid)
+        tie = want == mid
+        lo_even = (synth.bf16_bits(lo) & 1) == 0
+        rne = np.where(away | (tie & ~lo_even), hi, lo)
+        ambiguous = np.abs(want - mid) <= 1e-9 * np.abs(want)
+        bad = (got != rne) & ~ambiguous
+        assert not np.any(bad), f"{np.sum(bad)} values not correctly rounded"
+        assert np.all(np.abs(got - want) <= ulp / 2 + 1e-300)
+
+
+def _bf16_toward_zero(x):
+    """Largest-magnitude bf16 value not above |x| in magnitude (normal range)."""
+    bits = np.ascontiguousarray(x, dtype=np.float64).view(np.uint64)
+    sign = bits >> np.uint64(63)
+    exp = (bits >> np.uint64(52)) & np.uint64(0x7FF)
+    man = (bits >> np.uint64(45)) & np.uint64(0x7F)          # top 7 fraction bits
+    val = (1.0 + man.astype(np.float64) / 128.0) * np.exp2(exp.astype(np.float64) - 1023.0)
+    val = np.where(exp == 0, 0.0, val)
+    return np.where(sign == 1, -val, val)
+
+
+def _bf16_ulp(v):
+    """Spacing of bf16 numbers at the (normal, nonzero) bf16 value v."""
+    e = np.floor(np.log2(np.where(v == 0, 1.0, np.abs(v))))
+    return np.where(v == 0, 2.0 ** -133, np.exp2(e - 7))
 
 
 @pytest.mark.parametrize("dtype,n_pos,d_pos,H,dh", [
@@ -193,6 +224,38 @@ def test_segment_step_single_layer_eval(txl):
     for s in range(8):
         assert_close(outs[s][b_idx], o_outs[s], "bf16", f"segment {s}")
     _check_ring(dl, wl, o_mems, start_o, start, b_idx)
+
+
+@pytest.mark.parametrize("L,M,n_seg", [(150, 150, 3), (40, 100, 4)], ids=["L_ge_M", "L_lt_M_wrap"])
+def test_segment_step_packed_rows(txl, L, M, n_seg):
+    """d_model 410 (rows repacked to 448 columns, 820-byte rows): the packing
+    launch also applies the memory update, so the ring is checked bit for bit
+    after every segment, with L >= M and with L < M wrapping around the ring."""
+    cfg = synth.Config(f"packed_{L}_{M}", 4 if L >= M else 2, 410, 10, 41, L, M, 1, n_seg, "bf16",
+                       0.02, 5150 + L)
+    log(f"[case] segment step with packed rows L={L} M={M}")
+    wl = synth.make_workload(cfg)
+    import torch
+    import oracle
+    dl = DeviceLayers(wl)
+    shp = dl.shape()
+    ws = workspace(txl.txl_segment_workspace_bytes(shp, 1, 0))
+    layers = dl.layer_structs()
+    R = oracle.sinusoid(cfg.n_pos, cfg.d_pos)
+    mems = [m.copy() for m in wl.mem]
+    start = start_o = 0
+    for s in range(n_seg):
+        h = to_dev(wl.segments[s], "bf16")
+        out = torch.empty((cfg.batch, L, cfg.n_heads * cfg.d_head), dtype=torch.bfloat16,
+                          device="cuda")
+        start = txl.txl_segment_step(shp, 1, 0, layers, dl.R, h, out, start, ws)
+        torch.cuda.synchronize()
+        want, mems, start_o, _ = oracle.segment_step(wl.segments[s], wl.layers, mems, start_o,
+                                                     wl.u, wl.v, R, cfg.n_heads, cfg.d_head)
+        assert_close(from_dev(out), want, "bf16", f"segment {s}")
+        assert start == start_o
+        assert np.array_equal(bf16_bits_of(dl.mem[0]), synth.bf16_bits(mems[0])), \
+            f"segment {s}: memory ring differs"
 
 
 def test_segment_step_stack_small(txl):

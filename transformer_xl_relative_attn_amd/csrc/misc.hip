@@ -8,7 +8,10 @@ namespace {
 
 // R[delta][2k] = sin(delta / 10000^(2k/d)), R[delta][2k+1] = cos(same):
 // Transformer-XL Sec. 3.3 takes R to be Vaswani et al.'s sinusoid matrix.
-// Evaluated in fp64, rounded once to the storage dtype.
+// Evaluated in fp64, rounded once to the storage dtype: fp32 directly; bf16
+// through fp32 rounded to odd (truncate, then set the last bit if inexact),
+// whose 24 bits keep the information the final round-to-nearest-even needs,
+// so the result is the correctly rounded bf16 of the fp64 value.
 __global__ void sinusoid_kernel(void* R, int32_t n_pos, int32_t d, int32_t dtype) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (int64_t)n_pos * d) return;
@@ -17,7 +20,13 @@ __global__ void sinusoid_kernel(void* R, int32_t n_pos, int32_t d, int32_t dtype
   const double inv = pow(10000.0, -(double)k2 / (double)d);
   const double ang = (double)pos * inv;
   const double val = (c & 1) ? cos(ang) : sin(ang);
-  store_from_f32(R, idx, (float)val, dtype);
+  if (dtype == TXL_F32) {
+    static_cast<float*>(R)[idx] = (float)val;
+    return;
+  }
+  float f = __double2float_rz(val);
+  if ((double)f != val) f = __uint_as_float(__float_as_uint(f) | 1u);
+  static_cast<uint16_t*>(R)[idx] = f32_to_bf16_bits(f);
 }
 
 // Ring update (Transformer-XL Sec. 3.2, memory of the M most recent states):
@@ -58,6 +67,50 @@ __global__ void pack_rows_kernel(uint16_t* dst, int64_t ld_dst, const uint16_t* 
   if (idx >= rows * ld_dst) return;
   const int64_t r = idx / ld_dst, c = idx % ld_dst;
   dst[idx] = c < cols ? src[r * ld_src + c] : uint16_t(0);
+}
+
+// Grouped packs: workgroup r copies global row r (of the job whose row range
+// holds it), one word (2 or 4 bytes) per thread and pass.  The job that packs
+// the memory ring may also carry the ring update (Sec. 3.2): each thread
+// overwrites exactly the words of the ring row it has just read.
+template <class T>
+__device__ __forceinline__ void pack_row(const PackGroup& g, int j, int64_t row) {
+  constexpr int E = sizeof(T) / 2;   // bf16 elements per word
+  const PackJob& J = g.job[j];
+  T* src = reinterpret_cast<T*>(const_cast<void*>(J.src)) + row * (J.ld_src / E);
+  T* dst = static_cast<T*>(J.dst) + row * (J.ld_dst / E);
+  const int64_t wd = J.ld_dst / E, ws = J.cols / E;
+  const T* hrow = nullptr;
+  if (j == g.ring_job) {
+    const int32_t M = g.ring_M, L = g.ring_L;
+    const int32_t b = (int32_t)(row / M), slot = (int32_t)(row - (int64_t)b * M);
+    int32_t t;
+    if (L < M) {
+      t = slot - g.ring_start;
+      if (t < 0) t += M;
+    } else {
+      t = L - M + slot;
+    }
+    if (t < L) hrow = static_cast<const T*>(g.ring_h) + ((int64_t)b * L + t) * ws;
+  }
+  for (int64_t c = threadIdx.x; c < wd; c += 256) {
+    const T x = c < ws ? src[c] : T(0);
+    dst[c] = x;
+    if (hrow && c < ws) src[c] = hrow[c];
+  }
+}
+
+__global__ __launch_bounds__(256) void pack_group_kernel(PackGroup g) {
+  const int64_t r = blockIdx.x;
+  int j = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxPackJobs; ++i)
+    if (i < g.n && r >= g.row_begin[i]) j = i;
+  const int64_t row = r - g.row_begin[j];
+  if (g.words4)
+    pack_row<uint32_t>(g, j, row);
+  else
+    pack_row<uint16_t>(g, j, row);
 }
 
 // Sum over the 256 threads of a workgroup (fixed order: deterministic).
@@ -278,6 +331,14 @@ int launch_pack_rows(void* dst, int64_t ld_dst, const void* src, int64_t ld_src,
   hipLaunchKernelGGL(pack_rows_kernel, grid1d(n), dim3(256), 0, static_cast<hipStream_t>(stream),
                      static_cast<uint16_t*>(dst), ld_dst, static_cast<const uint16_t*>(src),
                      ld_src, rows, cols);
+  return static_cast<int>(hipGetLastError());
+}
+
+int launch_pack_group(const PackGroup& g, void* stream) {
+  const int64_t rows = g.row_begin[g.n];
+  if (rows == 0) return 0;
+  hipLaunchKernelGGL(pack_group_kernel, dim3((uint32_t)rows), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), g);
   return static_cast<int>(hipGetLastError());
 }
 
