@@ -411,38 +411,67 @@ struct Operands {
   int64_t ld_d, ld_pos;
 };
 
+// If `ring_upd` is set (and is the memory being packed) the pack of the
+// memory also applies the ring update with h, and *ring_upd is cleared.
 txl_status_t pack_operands(const AttnPlan& p, const AttnPtrs& a, char* ws, void* stream,
-                           Operands& o) {
+                           Operands& o, void** ring_upd = nullptr) {
   const int dt = p.dtype;
   const int32_t Hd = p.H * p.dh;
   o = Operands{a.h, a.mem, a.W_q, a.W_kE, a.W_v, a.W_kR, a.R, p.d, p.dpos};
   const bool seg = p.kind != PLAN_RING_INIT;    // the segment h and W_q are read
   const bool mem = p.kind != PLAN_RING && p.M > 0;
+  // every repack of the call goes into one grouped launch
+  PackGroup pg{};
+  pg.ring_job = -1;
+  auto pack = [&](const Region& r, const void* src, int64_t rows, int64_t ld_dst, int64_t cols,
+                  const void*& dst) {
+    PackJob& J = pg.job[pg.n];
+    J.dst = ws + r.off;
+    J.src = src;
+    J.ld_dst = ld_dst;
+    J.ld_src = cols;
+    J.rows = rows;
+    J.cols = (int32_t)cols;
+    pg.row_begin[pg.n + 1] = pg.row_begin[pg.n] + rows;
+    ++pg.n;
+    dst = ws + r.off;
+  };
+  (void)dt;
   if (p.pack_d) {
-    auto pack = [&](const Region& r, const void* src, int64_t rows, const char* what,
-                    const void*& dst) -> txl_status_t {
-      TXL_HIP(timed(K_PACK, stream, [&] {
-                return launch_pack_rows(ws + r.off, p.Kd, src, p.d, rows, p.d, dt, stream);
-              }),
-              what);
-      dst = ws + r.off;
-      return TXL_OK;
-    };
-    if (seg) TXL_TRY(pack(p.ph, a.h, (int64_t)p.B * p.L, "pack h", o.h));
-    if (mem) TXL_TRY(pack(p.pmem, a.mem, (int64_t)p.B * p.M, "pack mem", o.mem));
-    if (seg) TXL_TRY(pack(p.pwq, a.W_q, Hd, "pack W_q", o.Wq));
-    TXL_TRY(pack(p.pwk, a.W_kE, Hd, "pack W_kE", o.WkE));
-    TXL_TRY(pack(p.pwv, a.W_v, Hd, "pack W_v", o.Wv));
+    if (seg) pack(p.ph, a.h, (int64_t)p.B * p.L, p.Kd, p.d, o.h);
+    if (mem) {
+      if (ring_upd && *ring_upd == a.mem) {
+        // the GEMMs read the packed copy, so the ring itself may take the
+        // segment now (the attention reads only the projections)
+        pg.ring_job = pg.n;
+        pg.ring_h = a.h;
+        pg.ring_L = p.L;
+        pg.ring_M = p.M;
+        pg.ring_start = a.mem_start;
+        *ring_upd = nullptr;
+      }
+      pack(p.pmem, a.mem, (int64_t)p.B * p.M, p.Kd, p.d, o.mem);
+    }
+    if (seg) pack(p.pwq, a.W_q, Hd, p.Kd, p.d, o.Wq);
+    pack(p.pwk, a.W_kE, Hd, p.Kd, p.d, o.WkE);
+    pack(p.pwv, a.W_v, Hd, p.Kd, p.d, o.Wv);
     o.ld_d = p.Kd;
   }
   if (seg && !a.Rk && p.pack_pos) {
-    TXL_HIP(timed(K_PACK, stream, [&] { return launch_pack_rows(ws + p.pwr.off, p.Kpos, a.W_kR, p.dpos, Hd, p.dpos, dt, stream); }),
-            "pack W_kR");
-    TXL_HIP(timed(K_PACK, stream, [&] { return launch_pack_rows(ws + p.pr.off, p.Kpos, a.R, p.dpos, p.P, p.dpos, dt, stream); }),
-            "pack R");
-    o.WkR = ws + p.pwr.off;
-    o.R = ws + p.pr.off;
+    pack(p.pwr, a.W_kR, Hd, p.Kpos, p.dpos, o.WkR);
+    pack(p.pr, a.R, p.P, p.Kpos, p.dpos, o.R);
     o.ld_pos = p.Kpos;
+  }
+  if (pg.n > 0) {
+    bool w4 = true;
+    for (int i = 0; i < pg.n; ++i) {
+      const PackJob& J = pg.job[i];
+      w4 = w4 && J.cols % 2 == 0 && J.ld_src % 2 == 0 && J.ld_dst % 2 == 0 &&
+           (reinterpret_cast<uintptr_t>(J.src) & 3) == 0 && (reinterpret_cast<uintptr_t>(J.dst) & 3) == 0;
+    }
+    if (pg.ring_job >= 0) w4 = w4 && (reinterpret_cast<uintptr_t>(pg.ring_h) & 3) == 0;
+    pg.words4 = w4 ? 1 : 0;
+    TXL_HIP(timed(K_PACK, stream, [&] { return launch_pack_group(pg, stream); }), "operand packs");
   }
   return TXL_OK;
 }
@@ -486,15 +515,17 @@ txl_status_t run_attention(const AttnPlan& p, const AttnPtrs& a, char* ws, void*
   const bool bf = p.dtype == TXL_BF16;
   const int dt = p.dtype;
   // The ring update rides on the bf16 attention launch (the split combine, or
-  // the attention kernel's tail with one split) when rows are 16-byte
-  // multiples; otherwise it is a kernel of its own.  (Not when the output
-  // overlaps h: other workgroups may still be copying it.)
+  // the attention kernel's tail with one split) when rows are multiples of 4
+  // bytes (copied in 16-byte words when they are multiples of 16); otherwise
+  // it is a kernel of its own.  (Not when the output overlaps h: other
+  // workgroups may still be copying it.)
   const char* h_lo = static_cast<const char*>(a.h);
   const char* h_hi = h_lo + (size_t)p.B * p.L * p.d * esize(dt);
   const char* o_lo = static_cast<const char*>(a.out);
   const char* o_hi = o_lo + (size_t)p.B * p.L * p.H * p.dh * esize(dt);
   const bool overlap = o_lo < h_hi && h_lo < o_hi;
-  const bool fuse_upd = mem_upd && bf && p.M > 0 && (p.d * 2) % 16 == 0 && !overlap;
+  const int upd_unit = (p.d * 2) % 16 == 0 ? 16 : (p.d * 2) % 4 == 0 ? 4 : 0;
+  const bool fuse_upd = mem_upd && bf && p.M > 0 && upd_unit > 0 && !overlap;
   if (mem_upd) {
     if (!fuse_upd)
       TXL_TRY(after_launch(timed(K_MEM_UPDATE, stream, [&] { return launch_mem_update(mem_upd, a.mem_start, a.h, p.B, p.M, p.L, p.d, dt,
@@ -533,6 +564,7 @@ txl_status_t run_attention(const AttnPlan& p, const AttnPtrs& a, char* ws, void*
     aa.upd_start = a.mem_start;
     aa.upd_rows = p.L < p.M ? p.L : p.M;
     aa.upd_row_bytes = (int64_t)p.d * 2;
+    aa.upd_unit = upd_unit;
   }
   TXL_TRY(after_launch(timed(K_ATTN, stream,
                              [&] {
@@ -555,7 +587,11 @@ txl_status_t run_rel_attn(const AttnPlan& p, const AttnPtrs& a, char* ws, void* 
   char* k = ws + p.k.off;
   char* v = ws + p.v.off;
   Operands o;
-  TXL_TRY(pack_operands(p, a, ws, stream, o));
+  const int32_t start0 = a.mem_start;
+  void* upd = mem_upd;
+  TXL_TRY(pack_operands(p, a, ws, stream, o, &upd));
+  if (mem_upd && !upd)   // the pack carried the ring update
+    *new_start = (p.M == 0) ? 0 : (p.L < p.M ? (start0 + p.L) % p.M : 0);
 
   const int tile = gemm_tile(dt);
   const int64_t DP = p.DP;
@@ -584,7 +620,7 @@ txl_status_t run_rel_attn(const AttnPlan& p, const AttnPtrs& a, char* ws, void* 
   TXL_TRY(add_rk(g, p, a, o, ws, stream));
   TXL_TRY(after_launch(timed(K_PROJ_GEMM, stream, [&] { return launch_gemm(g, dt, stream); }),
                        "projection GEMMs", stream));
-  return run_attention(p, a, ws, stream, k, v, 0, mem_upd, new_start);
+  return run_attention(p, a, ws, stream, k, v, 0, upd, new_start);
 }
 
 // ------------------------------------------------------------- K/V ring

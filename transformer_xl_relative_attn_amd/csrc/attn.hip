@@ -108,25 +108,34 @@ __device__ __forceinline__ void compiler_fence() { __asm__ volatile("" ::: "memo
 // Copy min(L, M) segment rows into their memory-ring slots (the segment step's
 // update, Sec. 3.2): row r of the flattened [B][rows] range goes to slot
 // (start + t) mod M, or to slot t with the last M rows when L >= M.  Rows are
-// dealt to `nworkers` workers of 256 threads.
-__device__ __forceinline__ void ring_copy(const AttnArgs& a, int32_t worker, int32_t nworkers,
-                                          int tid) {
-  // the (row, 16-byte chunk) pairs of all copied rows, 256 consecutive ones
-  // per workgroup and pass, so that every thread copies one chunk per pass
-  const int64_t chunks = a.upd_row_bytes / 16;
-  const int64_t n = (int64_t)a.B * a.upd_rows * chunks;
+// dealt to `nworkers` workers of 256 threads, in words of W bytes.
+template <class W>
+__device__ __forceinline__ void ring_copy_words(const AttnArgs& a, int32_t worker,
+                                                int32_t nworkers, int tid) {
+  // the (row, word) pairs of all copied rows, 256 consecutive ones per
+  // workgroup and pass, so that every thread copies one word per pass
+  const int64_t words = a.upd_row_bytes / (int64_t)sizeof(W);
+  const int64_t n = (int64_t)a.B * a.upd_rows * words;
   for (int64_t g = (int64_t)worker * 256 + tid; g < n; g += (int64_t)nworkers * 256) {
-    const int32_t r = (int32_t)(g / chunks);
-    const int64_t c = g - (int64_t)r * chunks;
+    const int32_t r = (int32_t)(g / words);
+    const int64_t c = g - (int64_t)r * words;
     const int32_t bb = r / a.upd_rows, t = r - bb * a.upd_rows;
     const int32_t src = a.L < a.M ? t : a.L - a.M + t;
     const int32_t slot = a.L < a.M ? (a.upd_start + t) % a.M : t;
-    const u32x4* sp = reinterpret_cast<const u32x4*>(
-        static_cast<const char*>(a.upd_src) + ((int64_t)bb * a.L + src) * a.upd_row_bytes);
-    u32x4* dp = reinterpret_cast<u32x4*>(static_cast<char*>(a.upd_mem) +
-                                         ((int64_t)bb * a.M + slot) * a.upd_row_bytes);
+    const W* sp = reinterpret_cast<const W*>(static_cast<const char*>(a.upd_src) +
+                                             ((int64_t)bb * a.L + src) * a.upd_row_bytes);
+    W* dp = reinterpret_cast<W*>(static_cast<char*>(a.upd_mem) +
+                                 ((int64_t)bb * a.M + slot) * a.upd_row_bytes);
     dp[c] = sp[c];
   }
+}
+
+__device__ __forceinline__ void ring_copy(const AttnArgs& a, int32_t worker, int32_t nworkers,
+                                          int tid) {
+  if (a.upd_unit == 16)
+    ring_copy_words<u32x4>(a, worker, nworkers, tid);
+  else
+    ring_copy_words<uint32_t>(a, worker, nworkers, tid);
 }
 
 template <int V>
@@ -688,10 +697,11 @@ int launch_attn_bf16(const AttnArgs& a, void* stream) {
 int launch_attn_combine(const AttnArgs& a, void* stream) {
   const int64_t rows = (int64_t)a.B * a.H * a.L;
   const int32_t out_blocks = (int32_t)((rows + 31) / 32);
-  // the memory-ring copy (segment step) gets one workgroup per 256 chunks of
-  // 16 bytes (two rows of d_model 1024 in bf16)
+  // the memory-ring copy (segment step) gets one workgroup per 256 words
+  // (of 16 bytes: two rows of d_model 1024 in bf16)
   const int32_t copy_blocks =
-      a.upd_mem ? (int32_t)(((int64_t)a.B * a.upd_rows * (a.upd_row_bytes / 16) + 255) / 256) : 0;
+      a.upd_mem ? (int32_t)(((int64_t)a.B * a.upd_rows * (a.upd_row_bytes / a.upd_unit) + 255) / 256)
+                : 0;
   const dim3 grid(out_blocks + copy_blocks);
   hipStream_t st = static_cast<hipStream_t>(stream);
   switch (a.n_split) {

@@ -171,11 +171,13 @@ struct AttnArgs {
                            // in the base-2 units of the bf16 kernel (rows i < L)
   int32_t dtype;
   // optional fused ring update (bf16 kernel): copy min(L, M) rows of upd_src
-  // [B][L][*] into upd_mem [B][M][*] (row_bytes % 16 == 0); NULL = none
+  // [B][L][*] into upd_mem [B][M][*] in words of upd_unit bytes (16 or 4; a
+  // divisor of row_bytes and of both base addresses' alignment); NULL = none
   const void* upd_src;
   void* upd_mem;
   int32_t upd_start, upd_rows;
   int64_t upd_row_bytes;
+  int32_t upd_unit;
 };
 
 // Compute units of the current device (cached per device id).
@@ -262,6 +264,31 @@ int launch_mem_update(void* mem, int32_t start, const void* h, int32_t B, int32_
                       int32_t d, int32_t dtype, void* stream);
 int launch_pack_rows(void* dst, int64_t ld_dst, const void* src, int64_t ld_src, int64_t rows,
                      int32_t cols, int32_t dtype, void* stream);
+
+// Several bf16 row packs in one launch: job j copies rows x cols elements from
+// src (row pitch ld_src) into dst (row pitch ld_dst), zero-filling columns
+// cols .. ld_dst-1.
+constexpr int kMaxPackJobs = 8;
+struct PackJob {
+  void* dst;
+  const void* src;
+  int64_t ld_dst, ld_src, rows;
+  int32_t cols;
+};
+struct PackGroup {
+  int32_t n;
+  int64_t row_begin[kMaxPackJobs + 1];   // first global row of each job; [n] = total rows
+  PackJob job[kMaxPackJobs];
+  int32_t words4;        // every row start and length is a multiple of 4 bytes
+  // optional memory-ring update carried by job ring_job (the pack of the
+  // ring [B][M][cols] itself): after a thread has read its columns of ring
+  // row (b, slot) it overwrites them with segment row t of ring_h [B][L][cols],
+  // where slot = (start + t) mod M for t < L (L < M), or t = L - M + slot (L >= M)
+  int32_t ring_job;      // -1 = none
+  const void* ring_h;
+  int32_t ring_L, ring_M, ring_start;
+};
+int launch_pack_group(const PackGroup& g, void* stream);
 int launch_layernorm(const float* resid, const float* parts, int32_t n_parts, int64_t part_stride,
                      float* y_f32, void* y_lo, int32_t rows, int32_t d, int32_t lo_dtype, float eps,
                      void* stream);
