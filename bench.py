@@ -425,6 +425,8 @@ def main():
                     help="pass precomputed position keys (Rk computed once, outside the step)")
     ap.add_argument("--no-ring", action="store_true",
                     help="skip the carried K/V ring leg")
+    ap.add_argument("--no-mall", dest="mall", action="store_false",
+                    help="skip the cold/warm Infinity Cache leg of the attention kernel")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--table9", action="store_true",
@@ -636,7 +638,36 @@ def main():
         wall_r = time.perf_counter() - t0
         ms_r = max(ev0.elapsed_time(ev1), wall_r * 1e3) / args.steps
         fr = flops_kv_ring(cfg, with_rk=not args.cached_rk) * cfg.n_layers
+        # the same kernel with its inputs in the Infinity Cache (the ring's
+        # memory keys and values were written by earlier steps) or flushed
+        # from it: a 512 MiB fill (twice the cache) between steps
+        mall = None
+        if args.mall:
+            flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+
+            def attn_us(flushed):
+                txl.txl_timing_reset()
+                txl.txl_timing_enable(True)
+                for _ in range(args.steps):
+                    if flushed:
+                        flush.zero_()
+                    ring_step()
+                torch.cuda.synchronize()
+                per_k = txl.txl_timing_read()
+                txl.txl_timing_enable(False)
+                c, ms = per_k.get("rel_attn", (0, 0.0))
+                return ms / c * 1e3 if c else None
+
+            warm, cold = attn_us(False), attn_us(True)
+            by = attn_bytes(cfg)
+            mall = {"kernel": "rel_attn (K/V-ring step)", "algorithmic_bytes": by,
+                    "warm_us": round(warm, 2), "cold_us": round(cold, 2),
+                    "warm_gbs": round(by / (warm * 1e-6) / 1e9, 1),
+                    "cold_gbs": round(by / (cold * 1e-6) / 1e9, 1),
+                    "flush": "512 MiB device fill between steps"}
+            del flush
         ring_info = {"ms_per_step": round(ms_r, 4),
+                     "attention_infinity_cache": mall,
                      "tokens_per_s": round(cfg.batch * cfg.seg_len / (ms_r * 1e-3), 1),
                      "speedup_vs_hidden_state_memory": round(ms_per_step / ms_r, 3),
                      "executed_gflop_per_step": round(fr / 1e9, 3),
