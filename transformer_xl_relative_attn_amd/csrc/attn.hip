@@ -12,13 +12,12 @@
 // S^T[j][i], so a lane owns one query column and the softmax statistics stay
 // in the lane and its partner (ii, 1-hf).
 //   * LDS-DMA ring: block t's K tile and V^T tile (4 KB each, contiguous in the
-//     workspace) and Rk chunk t (32 rows) are loaded by direct global->LDS
-//     loads three to four blocks ahead, two blocks at a time after the barrier
-//     that every second block takes; every wave issues exactly three loads per
-//     block, so the vmcnt waits are constants.  Wave w uses Rk chunk t+1-w at block t,
-//     so a chunk stays resident for four blocks.
-//   * Term (b)+(d): for block t+1 a wave multiplies its 32 queries (q+v) by the
-//     32-row Rk chunk that starts at distance D-31, D = M + i0 - 32(t+1), on the
+//     workspace) and Rk chunk t+1 (32 rows, one block ahead) are loaded by
+//     direct buffer->LDS loads three blocks ahead, one block per barrier;
+//     every wave issues exactly three loads per block (a quarter of each), so
+//     the vmcnt waits are constants.  Wave w uses Rk chunk t+2-w at block t.
+//   * Term (b)+(d): for block t+2 a wave multiplies its 32 queries (q+v) by the
+//     32-row Rk chunk that starts at distance D-31, D = M + i0 - 32(t+2), on the
 //     matrix cores.  Pair (i, j) needs distance D + i - j: row 31 + i - j of the
 //     window [this chunk ; previous chunk], and the previous chunk's product is
 //     still in registers, so every chunk is multiplied once.  Each lane writes
@@ -28,14 +27,18 @@
 //     vector instruction.
 //   * Online softmax in base 2: c = scale * log2(e) is folded into q+u and q+v.
 //     The reference maximum moves only when a block's maximum exceeds it by
-//     more than 8 (p <= 2^8); the first block with a visible key sets it.
-//   * Software pipeline: block t's softmax runs on the vector ALUs while the
-//     operand fragments of block t+1 are read from LDS; block t+1's (b)+(d)
-//     and (q+u).K products follow block t's P.V on the matrix cores.
+//     more than 8 (p <= 2^8); it starts at -FLT_MAX, so the first block with a
+//     visible key sets it.
+//   * Software pipeline, two blocks deep: block t issues the (b)+(d) product
+//     for block t+2 and the (q+u).K product of block t+1 on the matrix cores,
+//     passes the block's barrier and runs block t's softmax on the vector ALUs
+//     while they execute, then P.V of block t; block t+2's window is written
+//     and block t+1's operands are read from LDS at the end of block t.
 //   * P (bf16) times V^T on the matrix cores: bf16 pairs of P are exchanged
 //     with the partner lane so that both operands list the keys in order.  The
-//     softmax denominators are per-lane sums of p (half of a column's keys
-//     each), joined with the partner lane at the end.
+//     softmax denominators are per-lane sums of the same bf16 p (half of a
+//     column's keys each, two per dot instruction), joined with the partner
+//     lane at the end.
 //   * With several key-range splits each workgroup writes (max, sum, O) and
 //     attn_combine_kernel merges them in split order (deterministic).  The
 //     segment step's memory-ring update rides on that launch (or on the tail of
@@ -54,14 +57,16 @@ constexpr int DP = 64;        // padded head width of the bf16 path
 constexpr int KB = 32;        // keys per block
 constexpr int NWAVE = 4;      // waves per workgroup, 32 queries each
 constexpr int QG = 32 * NWAVE;
-constexpr int NST = 4;        // K / V^T ring stages (blocks t+1 .. t+NST resident or in flight)
-constexpr int RKS = NST + 3;  // Rk chunk slots: chunks t-2 .. t+NST
+constexpr int NST = 4;        // K / V^T ring stages (blocks t .. t+3 resident or in flight)
+constexpr int RKS = 7;        // Rk chunk slots (the prologue holds chunks t_lo-3 .. t_lo+3)
 constexpr int WP = 36;        // floats per query row of a wave's shifted (b)+(d) window
 constexpr int KT_U = KB * 8;  // 16-byte units of a K tile (32 keys x 128 bytes)
 constexpr int VT_U = DP * 4;  // of a V^T tile (64 rows x 64 bytes)
 constexpr int RK_U = KB * 8;  // of an Rk chunk (32 rows x 128 bytes)
 constexpr int LOADS_PER_BLOCK = 3;   // LDS-DMA instructions per wave per block
 constexpr float kNegInf = -__builtin_inff();
+constexpr float kNoMax = -3.40282347e38f;   // -FLT_MAX
+typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 struct AttnSmem {
   u32x4 kv[NST][KT_U + VT_U];   // per stage: K tile, then V^T tile
@@ -94,6 +99,21 @@ __device__ __forceinline__ bf16x8 pack8(const float* x) {
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Raw buffer resource over `bytes` bytes at `base` (word 3: 32-bit data
+// format, the value gfx9 untyped loads expect).  Offsets at or past `bytes`
+// read zero instead of touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+
+// 16 bytes per lane from buffer offset lane_off + blk_off into LDS at dst +
+// 16 * lane (dst is wave-uniform; it goes to M0).
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t rs, u32x4* dst,
+                                                  uint32_t lane_off, int32_t blk_off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      rs, (__attribute__((address_space(3))) void*)dst, 16, (int)lane_off, blk_off, 0, 0);
 }
 
 __device__ __forceinline__ void barrier_lds() {
@@ -141,12 +161,10 @@ __device__ __forceinline__ void ring_copy(const AttnArgs& a, int32_t worker, int
 template <int V>
 using IC = std::integral_constant<int, V>;
 
-// v_max3_f32 without the NaN-quieting copies the compiler adds to fmaxf chains
 __device__ __forceinline__ float max3(float a, float b, float c) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
+  return __builtin_fmaxf(__builtin_fmaxf(a, b), c);
 }
+__device__ __forceinline__ float max2(float a, float b) { return __builtin_fmaxf(a, b); }
 
 __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a, int32_t padded, int32_t nqg) {
   const int32_t total = a.B * a.H * nqg * a.n_split;
@@ -184,71 +202,65 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a, int32_t p
 
   // ---- LDS-DMA.  Block t brings K tile t, V^T tile t and Rk chunk t (rows
   // M + i_base - 31 - 32 t + r, r = 0..31; the table's padding covers rows
-  // outside [0, Pp)).  Each is 4 KB contiguous: four wave-instructions of 64
-  // lanes x 16 bytes, the 12 of a block dealt three per wave.  A lane fetches
-  // the global chunk that lands in its swizzled slot.  Block t uses K/V stage
-  // (t - t_lo) % NST and chunk c slot (c - t_lo + 4) % RKS.
+  // outside [0, Pp)).  Each is 4 KB contiguous; wave w loads quarter w of all
+  // three (one wave-instruction of 64 lanes x 16 bytes each), so every wave
+  // issues three loads per block.  A lane fetches the global chunk that lands
+  // in its swizzled slot.  Block t uses K/V stage (t - t_lo) % NST and chunk c
+  // slot (c - t_lo + 4) % RKS.  The loads go through buffer resources: the
+  // lane offset is a constant register and the block offset a scalar, so a
+  // block's three loads cost no vector instruction.
   const int32_t nkb = a.Np / KB;
   const char* kbase = static_cast<const char*>(a.k) + (int64_t)bh * a.Np * DP * 2;
   const char* vbase = static_cast<const char*>(a.vt) + ((int64_t)b * nkb * a.H + head) * DP * KB * 2;
-  const int64_t vstep = (int64_t)a.H * DP * KB * 2;
+  const int32_t vstep = a.H * DP * KB * 2;
   const char* rbase = static_cast<const char*>(a.rk) +
                       ((int64_t)head * (a.Pp + 2 * kRkPad) + kRkPad + M + i_base - (KB - 1)) * DP * 2;
-  auto rk_slot = [&](int32_t c) { return (c - t_lo + 4) % RKS; };   // c >= t_lo - 4
   auto row_off = [&](int n) {      // instruction n (0..3) of a K tile or Rk chunk
     const int r = n * 8 + (lane >> 3);
     return (uint32_t)(r * 128 + (((lane & 7) ^ ((r >> 1) & 7)) << 4));
   };
-  // this wave's three loads of a block: a wave-uniform base advanced by tb *
-  // step, plus a 32-bit lane offset; into the stage (K, V^T) or the chunk
-  // slot (Rk) at a fixed unit offset
-  const char* gbase[LOADS_PER_BLOCK];
-  int64_t gstep[LOADS_PER_BLOCK];
-  uint32_t loff[LOADS_PER_BLOCK];
-  int32_t doff[LOADS_PER_BLOCK];
-  bool to_rk[LOADS_PER_BLOCK];
-#pragma unroll
-  for (int j = 0; j < LOADS_PER_BLOCK; ++j) {
-    const int n = 3 * wave + j;
-    if (n < 4 || n >= 8) {
-      loff[j] = row_off(n & 3);
-    } else {
-      const int d = (n - 4) * 16 + (lane >> 2);
-      loff[j] = (uint32_t)(d * 64 + (((lane & 3) ^ ((d >> 2) & 3)) << 4));
-    }
-    gbase[j] = n < 4 ? kbase : n < 8 ? vbase : rbase;
-    gstep[j] = n < 4 ? (int64_t)KB * DP * 2 : n < 8 ? vstep : -(int64_t)KB * DP * 2;
-    doff[j] = n < 4 ? n * 64 : n < 8 ? KT_U + (n - 4) * 64 : (n - 8) * 64;
-    to_rk[j] = n >= 8;
-  }
-  // Block tb's three loads of this wave.  Past the split's last block the
-  // loads repeat that block (valid memory) into the free slots, so every wave
-  // always issues three per block.
-  // K/V tiles are addressed through the ring rotation (block t at tile
+  // buffers: this (b, h)'s K tiles, its V^T tiles (stride vstep), and the Rk
+  // chunks t_lo - 4 .. t_hi addressed from chunk t_hi upwards
+  constexpr int32_t kTileBytes = KB * DP * 2;
+  const __amdgpu_buffer_rsrc_t rs_k = make_rsrc(kbase, a.Np * DP * 2);
+  const __amdgpu_buffer_rsrc_t rs_v = make_rsrc(vbase, (nkb - 1) * vstep + kTileBytes);
+  const __amdgpu_buffer_rsrc_t rs_r =
+      make_rsrc(rbase - (int64_t)t_hi * kTileBytes, (t_hi - t_lo + 5) * kTileBytes);
+  auto rk_off = [&](int32_t c) { return (t_hi - c) * kTileBytes; };   // chunk c, t_lo-4 <= c <= t_hi
+  const uint32_t lo_k = row_off(wave), lo_r = lo_k;
+  const uint32_t lo_v = [&] {
+    const int d = wave * 16 + (lane >> 2);
+    return (uint32_t)(d * 64 + (((lane & 3) ^ ((d >> 2) & 3)) << 4));
+  }();
+  // DMA block tb: this wave's three loads, K tile and V^T tile tb into K/V
+  // stage `kv` and Rk chunk tb+1 (one block ahead of the keys) into slot `rs`.
+  // Past the split's last block the loads repeat that block (valid memory)
+  // into the free slots, so every wave always issues three per block.  K/V
+  // tiles are addressed through the ring rotation (block t at tile
   // (t + kv_tile0) mod nkb; kv_tile0 = 0 outside the ring).
-  auto issue_block = [&](int32_t tb) {
+  auto issue_block = [&](int32_t tb, u32x4* kv, u32x4* rs) {
     const int32_t tl = min(tb, t_hi - 1);
     int32_t tk = tl + a.kv_tile0;
     tk -= tk >= nkb ? nkb : 0;
-    u32x4* kv = sm.kv[(tb - t_lo) % NST];
-    u32x4* rs = sm.rk[rk_slot(tb)];
-#pragma unroll
-    for (int j = 0; j < LOADS_PER_BLOCK; ++j) {
-      const char* g = gbase[j] + (to_rk[j] ? tl : tk) * gstep[j];
-      __builtin_amdgcn_global_load_lds(g + loff[j], (to_rk[j] ? rs : kv) + doff[j], 16, 0, 0);
-    }
+    const int32_t q = wave * 64;
+    buffer_load_lds16(rs_k, kv + q, lo_k, tk * kTileBytes);
+    buffer_load_lds16(rs_v, kv + KT_U + q, lo_v, tk * vstep);
+    buffer_load_lds16(rs_r, rs + q, lo_r, rk_off(tl + 1));
   };
+  auto rk_slot = [&](int32_t c) { return (c - t_lo + 4) % RKS; };   // c >= t_lo - 4
 
-  // ---- prologue.  Chunks t_lo-4 .. t_lo-1 (one per wave; chunk t_lo-4, which
-  // only wave 3 needs, goes to wave 3's window region, still unused), blocks
-  // t_lo .. t_lo+NST-1, and this head's u, v and the wave's q rows.
+  // ---- prologue.  Rk chunks t_lo-4 .. t_lo (wave w loads chunk t_lo-4+w
+  // whole, and quarter w of chunk t_lo; chunk t_lo-4, which only wave 3 needs,
+  // goes to wave 3's window region, still unused), DMA blocks t_lo .. t_lo+2
+  // (Rk chunks t_lo+1 .. t_lo+3), and this head's u, v and the wave's q rows.
   {
     const int32_t c = t_lo - 4 + wave;
     u32x4* dst = wave == 0 ? reinterpret_cast<u32x4*>(sm.win[3]) : sm.rk[rk_slot(c)];
-    const char* g = rbase - (int64_t)c * (KB * DP * 2);
 #pragma unroll
-    for (int n = 0; n < 4; ++n) __builtin_amdgcn_global_load_lds(g + row_off(n), dst + n * 64, 16, 0, 0);
-    issue_block(t_lo);
+    for (int n = 0; n < 4; ++n) buffer_load_lds16(rs_r, dst + n * 64, row_off(n), rk_off(c));
+    buffer_load_lds16(rs_r, sm.rk[rk_slot(t_lo)] + wave * 64, lo_r, rk_off(t_lo));
+    issue_block(t_lo, sm.kv[0], sm.rk[rk_slot(t_lo + 1)]);
+    issue_block(t_lo + 1, sm.kv[1], sm.rk[rk_slot(t_lo + 2)]);
   }
   float uvv = 0.0f;
   if (tid < 2 * DP) {
@@ -266,11 +278,10 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a, int32_t p
       qraw[2 * s + 1] = qrow[(16 * s + 8 * hf) / 4 + 1];
     }
   }
-  compiler_fence();   // the q loads go out before the later blocks' DMA
-#pragma unroll
-  for (int s = 1; s < NST - 1; ++s) issue_block(t_lo + s);
-  // everything but blocks t_lo+1 .. t_lo+NST-2 has landed
-  wait_vm<LOADS_PER_BLOCK * (NST - 2)>();
+  compiler_fence();   // the q loads go out before the third block's DMA
+  issue_block(t_lo + 2, sm.kv[2], sm.rk[rk_slot(t_lo + 3)]);
+  // everything but DMA block t_lo+2 has landed
+  wait_vm<LOADS_PER_BLOCK>();
   if (tid < 2 * DP) sm.uv[tid] = uvv;
   barrier_lds();
 
@@ -344,56 +355,77 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a, int32_t p
     return c;
   };
 
-  // ---- block t_lo: (b)+(d) of chunks t_lo-w-1 and t_lo-w, window, scores
-  floatx16 S = floatx16{0}, bdA = floatx16{0}, bdB = floatx16{0};
-  bf16x8 vf[2][2];
-  if (t_lo < t_end) {
+  // ---- prologue compute: (b)+(d) products of chunks t_lo-1-w, t_lo-w and
+  // t_lo+1-w, the scores of block t_lo on its window, and block t_lo+1's
+  // window left in LDS
+  floatx16 SA, SB = floatx16{0}, bdA = floatx16{0}, bdB;
+  bf16x8 kf[4], rf[4], vf[2][2];
+  floatx16 W;
+  {
     const u32x4* pc = wave == 3 ? reinterpret_cast<const u32x4*>(sm.win[3])
                                 : sm.rk[rk_slot(t_lo - wave - 1)];
-    bf16x8 pf[4], cf[4], kf[4];
+    bf16x8 pf[4], cf[4], nf[4];
     read_rows(pc, pf);
     read_rows(sm.rk[rk_slot(t_lo - wave)], cf);
+    read_rows(sm.rk[rk_slot(t_lo + 1 - wave)], nf);
     read_rows(sm.kv[0], kf);
-    read_vt(sm.kv[0], vf);
     const floatx16 bp = bd_chunk(pf);
-    bdB = bd_chunk(cf);
+    const floatx16 bc = bd_chunk(cf);
+    bdB = bd_chunk(nf);
     compiler_fence();   // (wave 3) the chunk reads precede the window writes in LDS order
-    write_win(bdB, bp);
+    write_win(bc, bp);
     compiler_fence();
-    S = qk(kf, read_win());
+    SA = qk(kf, read_win());
+    write_win(bdB, bc);
+    compiler_fence();
+    // operands of block t_lo's products: window t_lo+1, K tile t_lo+1, Rk
+    // chunk t_lo+2-w
+    W = read_win();
+    read_rows(sm.kv[1], kf);
+    read_rows(sm.rk[rk_slot(t_lo + 2 - wave)], rf);
   }
 
   float lpart = 0.0f;             // sum of this lane's p (half of column ii's keys)
   floatx16 o[2] = {floatx16{0}, floatx16{0}};
-  float m_ref = 0.0f;            // running reference maximum (lazy)
-  bool fresh = true;             // no visible key seen yet
+  // Running reference maximum (lazy) and the threshold m_ref + 8 that moves it.
+  // Before the first visible key it is -FLT_MAX: every finite block maximum
+  // then moves it, the rescale factor 2^(m_ref - mb) is 0 (the accumulators
+  // are still zero), and p = 2^(-inf - m_ref) = 0 for masked keys.
+  float m_ref = kNoMax, m_thr = kNoMax;
 
-  // One block t (K/V stage U = (t - t_lo) % NST): softmax and P.V of block t,
-  // (b)+(d) window and (q+u).K of block t+1.  `cur` receives chunk t+1-w,
-  // `prev` holds chunk t-w.  The loop is unrolled NST times so that stages are
-  // static and the two chunk products trade roles instead of being copied.
-  auto block = [&](auto U, int32_t t, floatx16& cur, floatx16& prev) {
-    constexpr int u = decltype(U)::value, un = (u + 1) % NST;
-    // One barrier per two blocks: at an even block t every block issued so far
-    // (up to t+2) has landed and, after the barrier, is visible to every wave,
-    // and the stages of blocks t-1 and t (read during blocks t-2 and t-1) take
-    // blocks t+3 and t+4.  Block t+1 then runs on data covered by this barrier.
-    if constexpr (u % 2 == 0) {
-      wait_vm<0>();
-      barrier_lds();
-      issue_block(t + NST - 1);
-      issue_block(t + NST);
-    }
+  // Rk slots of chunk t+3-w (read at the end of block t) and of the next
+  // chunk to load, advanced once per block (wave-uniform scalars).
+  int32_t rd_slot = rk_slot(t_lo + 3 - wave);
+  int32_t is_slot = rk_slot(t_lo + 4);
+  auto next_slot = [](int32_t sl) { return sl == RKS - 1 ? 0 : sl + 1; };
 
+  // One block t (K/V stage U = (t - t_lo) % NST).  On entry the registers hold
+  // the scores S of block t, block t+1's window W, K fragments kf of tile t+1,
+  // Rk fragments rf of chunk t+2-w, and `prev`, the (b)+(d) product of chunk
+  // t+1-w.  The block issues the (b)+(d) product of chunk t+2-w and block
+  // t+1's (q+u).K on the matrix cores first, runs block t's softmax on the
+  // vector ALUs while they execute, then P.V of block t, writes block t+2's
+  // window and reads the operands of block t+1's products.  The
+  // loop is unrolled NST times so that stages are static and the register
+  // sets trade roles instead of being copied.
+  auto block = [&](auto U, int32_t t, floatx16& S, floatx16& Snext, floatx16& cur,
+                   floatx16& prev) {
+    constexpr int u = decltype(U)::value;
+    constexpr int u2 = (u + 2) % NST, u3 = (u + 3) % NST;
     const bool cur_on = t < t_end;
-    const bool next_on = t + 1 < t_end;
-    // block t+1's K and Rk chunk t+1-w fragments first: they land during the
-    // softmax (V^T(t) was read during block t-1, before this block's refill)
-    bf16x8 kf[4], rf[4];
-    if (next_on) {
-      read_rows(sm.rk[rk_slot(t + 1 - wave)], rf);
-      read_rows(sm.kv[un], kf);
-    }
+    const bool n1_on = t + 1 < t_end;
+    const bool n2_on = t + 2 < t_end;
+    if (n2_on) cur = bd_chunk(rf);   // chunk t+2-w
+    if (n1_on) Snext = qk(kf, W);    // block t+1
+    // A barrier per block, passed while those products execute: DMA block t+2
+    // (issued one block ago) has landed and is visible to every wave; the
+    // stage of block t-1 (its K tile read in block t-3, its V^T tile in block
+    // t-1) takes DMA block t+3.
+    wait_vm<0>();
+    barrier_lds();
+    issue_block(t + 3, sm.kv[u3], sm.rk[is_slot]);
+    is_slot = next_slot(is_slot);
+    if (cur_on) read_vt(sm.kv[u], vf);   // V^T tile t, used after the softmax
     bf16x8 pb[2];
     if (cur_on) {
       // causal/memory mask: key j = 32t + jj visible iff k_lo <= j <= M + i0 + ii
@@ -410,20 +442,19 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a, int32_t p
       float mb = max3(S[0], S[1], S[2]);
 #pragma unroll
       for (int e = 3; e < 15; e += 2) mb = max3(mb, S[e], S[e + 1]);
-      mb = fmaxf(mb, S[15]);
+      mb = max2(mb, S[15]);
       {  // with the partner lane (ii, 1-hf): both halves of the column
         const auto mm = __builtin_amdgcn_permlane32_swap(__float_as_uint(mb), __float_as_uint(mb), false, false);
-        mb = fmaxf(__uint_as_float(mm[0]), __uint_as_float(mm[1]));
+        mb = max2(__uint_as_float(mm[0]), __uint_as_float(mm[1]));
       }
-      const bool need = mb > m_ref + 8.0f || (fresh && mb > kNegInf);
+      const bool need = mb > m_thr;
       if (__builtin_expect(__ballot(need) != 0, 0)) {
-        // move the reference up to mb and rescale the accumulators.  Before the
-        // first visible key they are still zero and the old reference means
-        // nothing: alpha = 0 (2^(0 - mb) would overflow for mb < -128).
-        const float alpha = need ? (fresh ? 0.0f : __builtin_amdgcn_exp2f(m_ref - mb)) : 1.0f;
+        // move the reference up to mb and rescale the accumulators (by 0 before
+        // the first visible key: 2^(-FLT_MAX - mb) = 0)
+        const float alpha = need ? __builtin_amdgcn_exp2f(m_ref - mb) : 1.0f;
         if (need) {
           m_ref = mb;
-          fresh = false;
+          m_thr = mb + 8.0f;
         }
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
@@ -435,24 +466,26 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a, int32_t p
       float p[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e) p[e] = __builtin_amdgcn_exp2f(S[e] - m_ref);
-      {
-        float s4[4];
-#pragma unroll
-        for (int g = 0; g < 4; ++g) s4[g] = (p[4 * g] + p[4 * g + 1]) + (p[4 * g + 2] + p[4 * g + 3]);
-        lpart += (s4[0] + s4[1]) + (s4[2] + s4[3]);
-      }
       // The lane holds p for keys 16t2 + 4hf + {0..3} and 16t2 + 8 + 4hf +
       // {0..3}; swapping bf16 pairs with the partner lane gives it keys
-      // 16t2 + 8hf .. +7 in order, the k-slots of the V^T fragment.
+      // 16t2 + 8hf .. +7 in order, the k-slots of the V^T fragment.  The
+      // denominator sums the same bf16 values the P.V product uses, two per
+      // dot instruction.
+      const bf16x8 pk[2] = {pack8(&p[0]), pack8(&p[8])};
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          lpart = __builtin_amdgcn_fdot2_f32_bf16(
+              bf16x2{pk[t2][2 * e], pk[t2][2 * e + 1]}, bf16x2{(bf16)1.0f, (bf16)1.0f}, lpart, false);
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2) {
-        const u32x4 pw = __builtin_bit_cast(u32x4, pack8(&p[8 * t2]));
+        const u32x4 pw = __builtin_bit_cast(u32x4, pk[t2]);
         const auto s02 = __builtin_amdgcn_permlane32_swap(pw[0], pw[2], false, false);
         const auto s13 = __builtin_amdgcn_permlane32_swap(pw[1], pw[3], false, false);
         pb[t2] = __builtin_bit_cast(bf16x8, u32x4{s02[0], s13[0], s02[1], s13[1]});
       }
     }
-    if (next_on) cur = bd_chunk(rf);   // chunk t+1-w
     if (cur_on) {
       // P^T (keys x queries) times V^T
 #pragma unroll
@@ -462,20 +495,21 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a, int32_t p
           o[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[t2][e], pb[t2], o[e], 0, 0, 0);
       }
     }
-    if (next_on) {
-      // block t+1: V^T fragments, shifted (b)+(d) window, then its (q+u).K on
-      // top of it
-      read_vt(sm.kv[un], vf);
-      write_win(cur, prev);
-      compiler_fence();
-      S = qk(kf, read_win());
+    if (n2_on) write_win(cur, prev);   // window of block t+2
+    compiler_fence();
+    // operands of block t+1's products (landed before this block's barrier)
+    if (n2_on) {
+      W = read_win();
+      read_rows(sm.kv[u2], kf);
+      read_rows(sm.rk[rd_slot], rf);   // chunk t+3-w
     }
+    rd_slot = next_slot(rd_slot);
   };
   for (int32_t t = t_lo; t < t_hi; t += NST) {
-    block(IC<0>{}, t, bdA, bdB);
-    if (t + 1 < t_hi) block(IC<1>{}, t + 1, bdB, bdA);
-    if (t + 2 < t_hi) block(IC<2>{}, t + 2, bdA, bdB);
-    if (t + 3 < t_hi) block(IC<3>{}, t + 3, bdB, bdA);
+    block(IC<0>{}, t, SA, SB, bdA, bdB);
+    if (t + 1 < t_hi) block(IC<1>{}, t + 1, SB, SA, bdB, bdA);
+    if (t + 2 < t_hi) block(IC<2>{}, t + 2, SA, SB, bdA, bdB);
+    if (t + 3 < t_hi) block(IC<3>{}, t + 3, SB, SA, bdB, bdA);
   }
   static_assert(NST == 4, "the block loop is unrolled NST times");
   // the repeated loads past the split's last block must land before exit
@@ -538,7 +572,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a, int32_t p
     }
   if (hf == 0) {
     // a range with no visible key for this query reports max -inf, sum 0
-    a.part_ml[row * 2 + 0] = fresh ? kNegInf : m_ref;
+    a.part_ml[row * 2 + 0] = m_ref == kNoMax ? kNegInf : m_ref;
     a.part_ml[row * 2 + 1] = l_sum;
   }
 }
