@@ -69,12 +69,13 @@ __global__ void pack_rows_kernel(uint16_t* dst, int64_t ld_dst, const uint16_t* 
   dst[idx] = c < cols ? src[r * ld_src + c] : uint16_t(0);
 }
 
-// Grouped packs: workgroup r copies global row r (of the job whose row range
-// holds it), one word (2 or 4 bytes) per thread and pass.  The job that packs
-// the memory ring may also carry the ring update (Sec. 3.2): each thread
-// overwrites exactly the words of the ring row it has just read.
+// Grouped packs: wave w of workgroup b copies global row 4b + w (of the job
+// whose row range holds it), one word (2 or 4 bytes) per lane and pass.  The
+// job that packs the memory ring may also carry the ring update (Sec. 3.2):
+// each lane overwrites exactly the words of the ring row it has just read.
+constexpr int kPackRowsPerBlock = 4;
 template <class T>
-__device__ __forceinline__ void pack_row(const PackGroup& g, int j, int64_t row) {
+__device__ __forceinline__ void pack_row(const PackGroup& g, int j, int64_t row, int lane) {
   constexpr int E = sizeof(T) / 2;   // bf16 elements per word
   const PackJob& J = g.job[j];
   T* src = reinterpret_cast<T*>(const_cast<void*>(J.src)) + row * (J.ld_src / E);
@@ -93,24 +94,36 @@ __device__ __forceinline__ void pack_row(const PackGroup& g, int j, int64_t row)
     }
     if (t < L) hrow = static_cast<const T*>(g.ring_h) + ((int64_t)b * L + t) * ws;
   }
-  for (int64_t c = threadIdx.x; c < wd; c += 256) {
-    const T x = c < ws ? src[c] : T(0);
-    dst[c] = x;
-    if (hrow && c < ws) src[c] = hrow[c];
+  // four words per lane and pass, all loads of a pass issued before its stores
+  for (int64_t c0 = lane; c0 < wd; c0 += 256) {
+    T x[4], y[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t c = c0 + 64 * u;
+      x[u] = c < ws ? src[c] : T(0);
+      y[u] = (hrow && c < ws) ? hrow[c] : T(0);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t c = c0 + 64 * u;
+      if (c < wd) dst[c] = x[u];
+      if (hrow && c < ws) src[c] = y[u];
+    }
   }
 }
 
 __global__ __launch_bounds__(256) void pack_group_kernel(PackGroup g) {
-  const int64_t r = blockIdx.x;
+  const int64_t r = (int64_t)blockIdx.x * kPackRowsPerBlock + (threadIdx.x >> 6);
+  if (r >= g.row_begin[g.n]) return;
   int j = 0;
 #pragma unroll
   for (int i = 1; i < kMaxPackJobs; ++i)
     if (i < g.n && r >= g.row_begin[i]) j = i;
   const int64_t row = r - g.row_begin[j];
   if (g.words4)
-    pack_row<uint32_t>(g, j, row);
+    pack_row<uint32_t>(g, j, row, threadIdx.x & 63);
   else
-    pack_row<uint16_t>(g, j, row);
+    pack_row<uint16_t>(g, j, row, threadIdx.x & 63);
 }
 
 // Sum over the 256 threads of a workgroup (fixed order: deterministic).
@@ -337,7 +350,8 @@ int launch_pack_rows(void* dst, int64_t ld_dst, const void* src, int64_t ld_src,
 int launch_pack_group(const PackGroup& g, void* stream) {
   const int64_t rows = g.row_begin[g.n];
   if (rows == 0) return 0;
-  hipLaunchKernelGGL(pack_group_kernel, dim3((uint32_t)rows), dim3(256), 0,
+  const int64_t blocks = (rows + kPackRowsPerBlock - 1) / kPackRowsPerBlock;
+  hipLaunchKernelGGL(pack_group_kernel, dim3((uint32_t)blocks), dim3(256), 0,
                      static_cast<hipStream_t>(stream), g);
   return static_cast<int>(hipGetLastError());
 }
