@@ -599,6 +599,7 @@ txl_status_t run_rel_attn(const AttnPlan& p, const AttnPtrs& a, char* ws, void* 
   add_q_problem(g, p, o, ws);
   // k = h~ W_kE^T -> [B][H][Np][DP]
   const RowSrc ht = src_htilde(o.mem, o.h, o.ld_d, p.Np, p.M, p.L, a.mem_start);
+  const int k_idx = g.count;
   add_problem(g, p.B * p.Np, p.H * p.DP, p.Kd, ht, src_headpad(o.WkE, o.ld_d, p.dh, p.DP),
               out_map(k, dt, p.B * p.Np, p.H * p.DP, axis(p.Np, (int64_t)p.H * p.Np * DP, DP),
                       axis(p.DP, (int64_t)p.Np * DP, 1)),
@@ -611,6 +612,8 @@ txl_status_t run_rel_attn(const AttnPlan& p, const AttnPtrs& a, char* ws, void* 
                 out_map(v, dt, p.H * p.DP, p.B * p.Np, axis_linear(32),
                         axis(32, (int64_t)p.H * DP * 32, 1)),
                 tile);
+    // K and V^T read the same rows of h~: their tiles are dealt panel by panel
+    g.pair1 = k_idx + 1;
   } else {
     add_problem(g, p.B * p.Np, p.H * p.DP, p.Kd, ht, src_headpad(o.Wv, o.ld_d, p.dh, p.DP),
                 out_map(v, dt, p.B * p.Np, p.H * p.DP, axis(p.Np, (int64_t)p.H * p.Np * DP, DP),

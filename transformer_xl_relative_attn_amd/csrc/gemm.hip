@@ -80,6 +80,33 @@ __device__ __forceinline__ int find_problem(const GemmGroup& g, int32_t tile, in
   return idx;
 }
 
+// Problem and (row, column) tile of a tile id: n fastest within a problem,
+// except for an interleaved pair (GemmGroup::pair1).
+__device__ __forceinline__ int tile_coords(const GemmGroup& g, int32_t tile, int32_t* tm,
+                                           int32_t* tn) {
+  int32_t local;
+  int idx = find_problem(g, tile, &local);
+  const int pr = g.pair1 - 1;
+  if (pr >= 0 && (idx == pr || idx == pr + 1)) {
+    const GemmProblem& P = g.p[pr];
+    const int32_t loc = tile - P.tile_begin;
+    const int32_t per = 2 * P.tiles_n;
+    const int32_t panel = loc / per, r = loc - panel * per;
+    if (r < P.tiles_n) {
+      *tm = panel;
+      *tn = r;
+      return pr;
+    }
+    *tm = r - P.tiles_n;
+    *tn = panel;
+    return pr + 1;
+  }
+  const GemmProblem& P = g.p[idx];
+  *tm = local / P.tiles_n;
+  *tn = local - *tm * P.tiles_n;
+  return idx;
+}
+
 // Wait until at most N LDS-DMA loads of this wave are still in flight.  The
 // loads are not fenced by the compiler (a __syncthreads would wait for all of
 // them), so the waits are explicit.
@@ -323,11 +350,9 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmGroup& g, int32_t padde
   const char* pb[LOADS];
   int64_t sa[LOADS], sb[LOADS];   // per-K-step advance: BK*2 bytes, or 0 for zero rows
   auto setup = [&](int32_t tile) {
-    int32_t local;
-    pidx = find_problem(g, tile, &local);
+    int32_t tm, tn;
+    pidx = tile_coords(g, tile, &tm, &tn);
     const GemmProblem& P = g.p[pidx];
-    // consecutive tiles share the A rows (tm), sweeping n fastest
-    const int32_t tm = local / P.tiles_n, tn = local - tm * P.tiles_n;
     m0 = tm * BM;
     n0 = tn * BN;
     nk = P.K / BK;
@@ -539,9 +564,8 @@ constexpr int FT = 64, FK = 16;
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmGroup g, int32_t padded) {
   const int32_t tile = xcd_swizzle(blockIdx.x, padded);
   if (tile >= g.total_tiles) return;
-  int32_t local;
-  const GemmProblem& P = g.p[find_problem(g, tile, &local)];
-  const int32_t tm = local / P.tiles_n, tn = local - tm * P.tiles_n;
+  int32_t tm, tn;
+  const GemmProblem& P = g.p[tile_coords(g, tile, &tm, &tn)];
   const int32_t m0 = tm * FT, n0 = tn * FT;
 
   __shared__ float sA[FK][FT + 1];
@@ -626,6 +650,16 @@ int launch_tiles(const GemmGroup& g, bool small, void* stream) {
   return static_cast<int>(hipGetLastError());
 }
 
+// An interleaved pair needs matching panel counts (see GemmGroup::pair1).
+static bool pair_ok(const GemmGroup& g) {
+  const int pr = g.pair1 - 1;
+  if (pr < 0) return true;
+  if (pr + 1 >= g.count) return false;
+  const GemmProblem &x = g.p[pr], &y = g.p[pr + 1];
+  return x.tiles_n == y.tiles_m && x.tiles_m == y.tiles_n &&
+         y.tile_begin == x.tile_begin + x.tiles_m * x.tiles_n;
+}
+
 // The group arrives tiled for 256x256 blocks.  A group with no more such
 // tiles than half the compute units is re-tiled for 128x128 blocks: two
 // workgroups of 4 waves per CU, or, if the 128x128 tiles do not outnumber the
@@ -634,20 +668,29 @@ int launch_tiles(const GemmGroup& g, bool small, void* stream) {
 // tiles of `t` x `t`.
 GemmGroup regroup(const GemmGroup& g, const bool* pick, int t) {
   GemmGroup s{};
+  int newidx[kMaxGroup];
   for (int i = 0; i < g.count; ++i) {
+    newidx[i] = -1;
     if (pick && !pick[i]) continue;
     GemmProblem p = g.p[i];
     p.tiles_m = (p.M + t - 1) / t;
     p.tiles_n = (p.N + t - 1) / t;
     p.tile_begin = s.total_tiles;
     s.total_tiles += p.tiles_m * p.tiles_n;
+    newidx[i] = s.count;
     s.p[s.count++] = p;
+  }
+  const int pr = g.pair1 - 1;
+  if (pr >= 0 && newidx[pr] >= 0 && newidx[pr + 1] == newidx[pr] + 1) {
+    s.pair1 = newidx[pr] + 1;
+    if (!pair_ok(s)) s.pair1 = 0;
   }
   return s;
 }
 
 int launch_gemm_bf16(const GemmGroup& g, void* stream) {
   if (g.total_tiles <= 0) return 0;
+  if (!pair_ok(g)) return static_cast<int>(hipErrorInvalidValue);
   const int cus = device_cu_count();
   if (2 * g.total_tiles <= cus) return launch_tiles(regroup(g, nullptr, 128), true, stream);
   // A last round of 256x256 tiles less than a quarter full would take as long

@@ -140,6 +140,14 @@ constexpr int kMaxGroup = 8;
 struct GemmGroup {
   int32_t count;
   int32_t total_tiles;
+  // 1 + index i of an interleaved pair (0 = none): problems i and i+1 share
+  // an operand, as A of i and B of i+1 (the keys and the values^T both read
+  // the rows of h~), with p[i].tiles_n == p[i+1].tiles_m and p[i].tiles_m ==
+  // p[i+1].tiles_n.  Their tiles are dealt panel by panel: the tiles_n tiles
+  // of row panel x of problem i, then the tiles_m tiles of column panel x of
+  // problem i+1, so that tiles reading the same rows are consecutive and run
+  // on one XCD.
+  int32_t pair1;
   GemmProblem p[kMaxGroup];
 };
 
