@@ -12,11 +12,13 @@
 //   du     = scale * sum_ij dS_ij k_j,  dv = scale * sum_ij dS_ij Rk[M+i-j]
 //   dRk[delta] = scale * sum over pairs with M+i-j = delta of dS_ij (q_i + v)
 //
-// attn_bwd_q_kernel (one wave per 32 queries of one (b, h); no barriers): for
-//   every visible 32-key block it recomputes the scores exactly as the forward
-//   kernel does (the (b)+(d) window written shifted to LDS and read back as the
-//   accumulator of (q+u).K), P from the forward's log-sum-exp, dP^T = val
-//   G^T on the matrix cores, and dS.  It accumulates dq's k-part (K^T tile
+// attn_bwd_q_kernel (a workgroup of 4 waves x 32 queries of one (b, h)): the
+//   K, val and K^T tiles and the Rk and Rk^T chunks of every 32-key block are
+//   staged in LDS by direct loads two blocks ahead, one barrier per block, and
+//   shared by the four waves.  For every visible block a wave recomputes the
+//   scores exactly as the forward kernel does (the (b)+(d) window written
+//   shifted to LDS and read back as the accumulator of (q+u).K), P from the
+//   forward's log-sum-exp, dP^T = val G^T on the matrix cores, and dS.  It accumulates dq's k-part (K^T tile
 //   times dS^T) and its Rk-part (Rk^T window times dS written shifted, row
 //   31 + i - j of the window holds pair (i, j), the App. B shift in reverse),
 //   and writes P^T, dS^T and the shifted dS'^T (row delta) for the key-side
@@ -33,13 +35,44 @@ constexpr int DP = 64;
 constexpr int KB = 32;
 constexpr int WP = 36;     // floats per query row of the score window
 constexpr int DSW = 72;    // bf16 per query row of the dS' window (64 + pad)
+constexpr int NST = 3;     // K / val / K^T ring stages (blocks t .. t+2)
+constexpr int RKS = 8;     // Rk and Rk^T chunk slots: chunk c in slot (c + 8) & 7
+constexpr int TU = 256;    // 16-byte units of a 4 KB tile
 constexpr float kNegInf = -__builtin_inff();
 
 struct BwdSmem {
+  u32x4 kv[NST][3 * TU];            // per stage: K tile, val tile (32 keys x 128 B), K^T tile (64 d x 64 B)
+  u32x4 rk[RKS][TU];                // Rk chunk: 32 rows x 128 B
+  u32x4 rkt[RKS][TU];               // Rk^T chunk: 64 d x 32 distances (64 B)
   float win[4][32 * WP];            // per wave: shifted (b)+(d) window of the scores
   uint16_t dsw[4][32 * DSW];        // per wave: query row i, position 31 + i - j -> dS_ij
   uint16_t half[4][2][32 * 32];     // per wave: two 32-row halves of dS'^T [row][query]
 };
+static_assert(sizeof(BwdSmem) <= 160 * 1024, "one workgroup per CU");
+
+// 16-byte slots: chunk c of a 128-byte row r at r*8 + (c ^ ((r >> 1) & 7)),
+// of a 64-byte row d at d*4 + (c ^ ((d >> 2) & 3)); a fragment read (16 rows
+// at one chunk per 16 lanes) then covers all 64 banks.
+__device__ __forceinline__ int sw128(int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); }
+__device__ __forceinline__ int sw64(int d, int c) { return d * 4 + (c ^ ((d >> 2) & 3)); }
+
+__device__ __forceinline__ int rk_slot(int32_t c) { return (c + 8) & (RKS - 1); }
+
+// 16 bytes per lane from global address p + blk_off into LDS at dst + 16 *
+// lane (dst is wave-uniform; it goes to M0).
+__device__ __forceinline__ void dma16(const char* p, u32x4* dst, int64_t blk_off) {
+  __builtin_amdgcn_global_load_lds(p + blk_off, dst, 16, 0, 0);
+}
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void barrier_lds() {
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
 
 __device__ __forceinline__ bf16x8 load8(const void* base, int64_t elem) {
   return *reinterpret_cast<const bf16x8*>(static_cast<const uint16_t*>(base) + elem);
@@ -59,7 +92,7 @@ __device__ __forceinline__ uint16_t bf16_bits(float x) {
 __global__ __launch_bounds__(256, 1) void attn_bwd_q_kernel(BwdArgs a) {
   const int32_t nqg = (a.L + 127) / 128;
   const int32_t wid = blockIdx.x;
-  if (wid >= a.B * a.H * nqg) return;
+  if (wid >= a.B * a.H * nqg) return;   // the whole workgroup
   // Later query groups see more keys (the causal part grows with i): they are
   // dealt first, so that the shorter groups fill the last round of the chip.
   const int32_t nbh = a.B * a.H;
@@ -72,21 +105,74 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_q_kernel(BwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ii = lane & 31, hf = lane >> 5;
-  const int32_t i0 = qg * 128 + 32 * wave;
-  if (i0 >= a.L) return;   // no workgroup barrier below: idle waves leave
   const int32_t M = a.M, L = a.L, Np = a.Np, Lp = a.Lp;
+  const int32_t i_base = qg * 128;
+  const int32_t i_last = min(i_base + 127, L - 1);
+  const int32_t nb = (M + i_last + 1 + KB - 1) / KB;   // key blocks of the workgroup
+  const int32_t i0 = i_base + 32 * wave;
+  const bool wave_on = i0 < L;   // waves past L only take part in the loads and barriers
   const int32_t i = i0 + ii;
   const bool qok = i < L;
-  const int32_t t_end = (M + min(i0 + 31, L - 1) + 1 + KB - 1) / KB;
+  const int32_t t_end = wave_on ? (M + min(i0 + 31, L - 1) + 1 + KB - 1) / KB : 0;
   const int32_t nkb = Np / KB;
 
-  const float lse = qok ? a.lse[(int64_t)bh * Lp + i] : 0.0f;
+  // ---- LDS-DMA.  Block t brings K tile t, val tile t (rows 32t.., 128 B
+  // each), the K^T tile t ([64 d][32 keys]) into stage t % NST, and Rk chunk t
+  // (rows base0 - 32t + r of the head's table) and the Rk^T chunk of the same
+  // distances ([64 d][32 distances]) into slot (t + 8) & 7.  Wave w uses Rk
+  // chunk t-w for block t's scores and Rk^T chunks t-w, t-w-1 for its dq; each
+  // chunk is loaded once per workgroup.  Every wave loads a quarter of each of
+  // the five tiles per block; past the last block the loads repeat it.
+  const int32_t base0 = M + i_base - (KB - 1);   // distance of chunk 0's first row
+  const int32_t rk_rows = a.Pp + 2 * kRkPad;
+  const int32_t ktstep = a.H * DP * KB * 2;
+  // first row / column of chunk c, clamped into the tables (chunks outside
+  // them are never used)
+  auto rk_row0 = [&](int32_t c) { return min(max(kRkPad + base0 - KB * c, 0), rk_rows - KB); };
+  auto rkt_col0 = [&](int32_t c) { return min(max(a.rkt_pad + base0 - KB * c, 0), a.rkt_ld - KB); };
+  // per-lane sources: 128-byte rows r = 8w + lane/8, 64-byte rows d = 16w +
+  // lane/4; a lane fetches the global chunk that lands in its swizzled slot
+  const char *pk, *pv, *pkt, *prk, *prkt;
+  {
+    const int r = wave * 8 + (lane >> 3);
+    const int64_t lo128 = r * 128 + (((lane & 7) ^ ((r >> 1) & 7)) << 4);
+    const int d = wave * 16 + (lane >> 2);
+    const int gc = (lane & 3) ^ ((d >> 2) & 3);
+    pk = static_cast<const char*>(a.k) + (int64_t)bh * Np * DP * 2 + lo128;
+    pv = static_cast<const char*>(a.vn) + (int64_t)bh * Np * DP * 2 + lo128;
+    pkt = static_cast<const char*>(a.kt) + ((int64_t)b * nkb * a.H + head) * DP * KB * 2 + d * 64 +
+          gc * 16;
+    prk = static_cast<const char*>(a.rk) + (int64_t)head * rk_rows * DP * 2 + lo128;
+    prkt = static_cast<const char*>(a.rkt) + ((int64_t)head * DP + d) * a.rkt_ld * 2 + gc * 16;
+  }
+  auto issue_block = [&](int32_t tb, int st) {
+    const int32_t tt = min(tb, nb - 1);
+    u32x4* kvs = sm.kv[st] + wave * 64;
+    dma16(pk, kvs, (int64_t)tt * (KB * DP * 2));
+    dma16(pv, kvs + TU, (int64_t)tt * (KB * DP * 2));
+    dma16(pkt, kvs + 2 * TU, (int64_t)tt * ktstep);
+    const int sl = rk_slot(tb);
+    dma16(prk, sm.rk[sl] + wave * 64, (int64_t)rk_row0(tt) * (DP * 2));
+    dma16(prkt, sm.rkt[sl] + wave * 64, (int64_t)rkt_col0(tt) * 2);
+  };
+  // prologue loads: chunks -4 .. -1, blocks 0 and 1
+#pragma unroll
+  for (int32_t c = -4; c < 0; ++c) {
+    dma16(prk, sm.rk[rk_slot(c)] + wave * 64, (int64_t)rk_row0(c) * (DP * 2));
+    dma16(prkt, sm.rkt[rk_slot(c)] + wave * 64, (int64_t)rkt_col0(c) * 2);
+  }
+  issue_block(0, 0);
+  issue_block(1, 1);
+
+  // lanes past L take lse = +inf: their p = 2^(S - inf) = 0
+  const float lse = qok ? a.lse[(int64_t)bh * Lp + i] : __builtin_inff();
   const float dsum = qok ? a.dsum[(int64_t)bh * Lp + i] : 0.0f;
 
   // query operands (q+u)c, (q+v)c, d = 16s + 8hf + e, and G_i for dP^T
   bf16x8 qu[4], qv[4], go[4];
   {
-    const float* qrow = a.q + ((int64_t)bh * Lp + i) * DP;
+    const int32_t ic = wave_on ? i : 0;   // rows past Lp are never read
+    const float* qrow = a.q + ((int64_t)bh * Lp + ic) * DP;
     const uint16_t* up = static_cast<const uint16_t*>(a.u) + (int64_t)head * a.dh;
     const uint16_t* vp = static_cast<const uint16_t*>(a.v) + (int64_t)head * a.dh;
 #pragma unroll
@@ -107,14 +193,24 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_q_kernel(BwdArgs a) {
       }
       qu[s] = pack8(xu);
       qv[s] = pack8(xv);
-      go[s] = load8(a.dop, ((int64_t)bh * Lp + i) * DP + 16 * s + 8 * hf);
+      go[s] = load8(a.dop, ((int64_t)bh * Lp + ic) * DP + 16 * s + 8 * hf);
     }
   }
+  wait_vm<0>();
+  barrier_lds();
 
-  const int64_t rk_head = (int64_t)head * (a.Pp + 2 * kRkPad) + kRkPad;
-  auto rk_rows = [&](int32_t base, bf16x8 (&f)[4]) {   // Rk rows base + ii
+  // fragment offsets: rows ii of a 128-byte-row tile at chunk 2s+hf (dims
+  // 16s + 8hf ..), rows d = 32e + ii of a 64-byte-row tile at chunk 2t2+hf
+  int ofs128[4], ofs64[2][2];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) f[s] = load8(a.rk, (rk_head + base + ii) * DP + 16 * s + 8 * hf);
+  for (int s = 0; s < 4; ++s) ofs128[s] = sw128(ii, 2 * s + hf);
+#pragma unroll
+  for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+    for (int e = 0; e < 2; ++e) ofs64[t2][e] = sw64(32 * e + ii, 2 * t2 + hf);
+  auto read_rows = [&](const u32x4* base, bf16x8 (&f)[4]) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) f[s] = __builtin_bit_cast(bf16x8, base[ofs128[s]]);
   };
   auto bd_chunk = [&](const bf16x8 (&rf)[4]) {
     floatx16 acc = floatx16{0};
@@ -167,58 +263,31 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_q_kernel(BwdArgs a) {
   };
 
   floatx16 dqk[2] = {floatx16{0}, floatx16{0}}, dqr[2] = {floatx16{0}, floatx16{0}};
-  // upper chunk of block 0: rows base_0 + 32 .. +63, base_t = M + i0 - 32t - 31
-  floatx16 upper;
-  {
+  // upper chunk of block 0: chunk -w-1 (distances base_0 + 32 .. +63,
+  // base_t = M + i0 - 32t - 31)
+  floatx16 upper = floatx16{0};
+  if (wave_on) {
     bf16x8 rf[4];
-    rk_rows(M + i0 - 31 + 32, rf);
+    read_rows(sm.rk[rk_slot(-wave - 1)], rf);
     upper = bd_chunk(rf);
   }
-  // P^T, dS^T rows are written as bf16 pairs of queries (2i', 2i'+1): the even
-  // lane of a pair stores one key, the odd lane the next
-  uint32_t* ptp = reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.pt) +
-                                              (int64_t)bh * Np * Lp + (i & ~1));
-  uint32_t* dstp = reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(a.dst) +
-                                               (int64_t)bh * Np * Lp + (i & ~1));
-  const bool odd = ii & 1;
-  const int64_t rkt_row0 = (int64_t)head * DP * a.rkt_ld + a.rkt_pad;
+  // P^T, dS^T [key][query]: lane (ii, hf) writes query i of key rows
+  // j0 + 8g + 4hf + r, 2 bytes each (a row of 32 queries is 64 contiguous
+  // bytes); the row base is a scalar, the lane's part a constant offset
+  char* const pt_bh = static_cast<char*>(a.pt) + (int64_t)bh * Np * Lp * 2;
+  char* const dst_bh = static_cast<char*>(a.dst) + (int64_t)bh * Np * Lp * 2;
+  const uint32_t st_lane = (uint32_t)(((4 * hf) * Lp + i) * 2);
 
-  // operand fragments of a block, each group reloaded for the next block as
-  // soon as this block has consumed it: K, val and Rk rows (scores, dP^T),
-  // K^T tile (rows d = 32e + ii, keys 16t2 + 8hf ..) and the Rk^T window
-  // (rows d, window positions 16s + 8hf ..)
-  bf16x8 kf[4], vf[4], rf[4], ktf[2][2], rtf[2][4];
-  auto load_rows = [&](int32_t t) {
-    const int32_t j0 = t * KB;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      kf[s] = load8(a.k, ((int64_t)bh * Np + j0 + ii) * DP + 16 * s + 8 * hf);
-      vf[s] = load8(a.vn, ((int64_t)bh * Np + j0 + ii) * DP + 16 * s + 8 * hf);
-    }
-    rk_rows(M + i0 - 32 * t - 31, rf);
-  };
-  auto load_kt = [&](int32_t t) {
-#pragma unroll
-    for (int e = 0; e < 2; ++e)
-#pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2)
-        ktf[t2][e] = load8(a.kt, ((((int64_t)b * nkb + t) * a.H + head) * DP + 32 * e + ii) * KB +
-                                     16 * t2 + 8 * hf);
-  };
-  auto load_rt = [&](int32_t t) {
-    const int32_t base = M + i0 - 32 * t - 31;
-#pragma unroll
-    for (int e = 0; e < 2; ++e)
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-        rtf[e][s] = load8(a.rkt, rkt_row0 + (int64_t)(32 * e + ii) * a.rkt_ld + base + 16 * s + 8 * hf);
-  };
-
-  // scores and dP^T of block t from the row fragments (which are then free
-  // for the next block's load); `upper` holds the chunk product of rows
-  // base_t + 32 .. +63 and receives that of base_t .. +31
-  floatx16 S, dpt;
+  // scores and dP^T of block t (its tiles and Rk chunk t-w in LDS); `upper`
+  // holds the chunk product of distances base_t + 32 .. +63 and receives that
+  // of base_t .. +31
+  floatx16 S = floatx16{0}, dpt = floatx16{0};
   auto scores = [&](int32_t t, floatx16& So, floatx16& dpo) {
+    const u32x4* kvs = sm.kv[t % NST];
+    bf16x8 kf[4], vf[4], rf[4];
+    read_rows(sm.rk[rk_slot(t - wave)], rf);
+    read_rows(kvs + TU, vf);
+    read_rows(kvs, kf);
     const floatx16 lower = bd_chunk(rf);
     dpo = floatx16{0};
 #pragma unroll
@@ -229,55 +298,67 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_q_kernel(BwdArgs a) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) So = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qu[s], So, 0, 0, 0);
     upper = lower;
-    if (t + 1 < t_end) load_rows(t + 1);
   };
 
   // Block t with its scores and dP^T already in S, dpt.  The next block's
   // products are issued once this block's dS exists, so that they run on the
   // matrix cores while this block's shifted-dS phase runs on LDS and VALU.
+  // The previous block's completed dS'^T half is written out first, so that
+  // its stores have landed by the next barrier.
+  bool pend = false;   // halves[(t) & 1] holds rows pend_row .. +31, complete
+  int32_t pend_row = 0;
   auto block = [&](int32_t t) {
     const int32_t j0 = t * KB;
     const int32_t base = M + i0 - 32 * t - 31;
     const bool more = t + 1 < t_end;
     // P and dS; key jj = 8g + 4hf + r (element 4g + r) visible iff j0 + jj <= M + i
-    const int32_t lim = M + i - j0 - 4 * hf;
-    float ds[16];
-    uint32_t pb[16], db[16];
+    // (only blocks that reach past the wave's first query need the mask)
+    float p[16], ds[16];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int kk = 8 * (e >> 2) + (e & 3);
-      const float p = (qok && kk <= lim) ? __builtin_amdgcn_exp2f(S[e] - lse) : 0.0f;
-      ds[e] = p * (dpt[e] - dsum);
-      pb[e] = bf16_bits(p);
-      db[e] = bf16_bits(ds[e]);
+    for (int e = 0; e < 16; ++e) p[e] = __builtin_amdgcn_exp2f(S[e] - lse);
+    if (j0 + KB - 1 > M + i0) {
+      const int32_t lim = M + i - j0 - 4 * hf;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int kk = 8 * (e >> 2) + (e & 3);
+        if (kk > lim) p[e] = 0.0f;
+      }
     }
-    // keys (e, e+1) of the query pair: the partner lane's two values arrive
-    // in one 32-bit exchange; the even lane stores key e, the odd key e+1
+#pragma unroll
+    for (int e = 0; e < 16; ++e) ds[e] = p[e] * (dpt[e] - dsum);
+    // bf16 pairs (keys 8g + 4hf + r, r and r+1) stored as two 2-byte halves
 #pragma unroll
     for (int e = 0; e < 16; e += 2) {
-      const uint32_t pmine = pb[e] | (pb[e + 1] << 16), dmine = db[e] | (db[e + 1] << 16);
-      const uint32_t pnb = __builtin_amdgcn_update_dpp(0u, pmine, 0xB1, 0xF, 0xF, false);
-      const uint32_t dnb = __builtin_amdgcn_update_dpp(0u, dmine, 0xB1, 0xF, 0xF, false);
-      const int jj = 8 * (e >> 2) + (e & 3) + 4 * hf + (odd ? 1 : 0);
-      const uint32_t pw = odd ? (pnb >> 16) | (pmine & 0xffff0000u) : (pmine & 0xffffu) | (pnb << 16);
-      const uint32_t dw2 = odd ? (dnb >> 16) | (dmine & 0xffff0000u) : (dmine & 0xffffu) | (dnb << 16);
-      ptp[((int64_t)(j0 + jj) * Lp) >> 1] = pw;
-      dstp[((int64_t)(j0 + jj) * Lp) >> 1] = dw2;
+      const int jj = 8 * (e >> 2) + (e & 3);   // key of element e, less 4hf
+      typedef float floatx2_t __attribute__((ext_vector_type(2)));
+      typedef bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+      const uint32_t pw = __builtin_bit_cast(uint32_t, __builtin_convertvector(floatx2_t{p[e], p[e + 1]}, bf16x2_t));
+      const uint32_t dw2 = __builtin_bit_cast(uint32_t, __builtin_convertvector(floatx2_t{ds[e], ds[e + 1]}, bf16x2_t));
+      char* pr = pt_bh + (int64_t)(j0 + jj) * Lp * 2;
+      char* dr = dst_bh + (int64_t)(j0 + jj) * Lp * 2;
+      *reinterpret_cast<uint16_t*>(pr + st_lane) = (uint16_t)pw;
+      *reinterpret_cast<uint16_t*>(pr + Lp * 2 + st_lane) = (uint16_t)(pw >> 16);
+      *reinterpret_cast<uint16_t*>(dr + st_lane) = (uint16_t)dw2;
+      *reinterpret_cast<uint16_t*>(dr + Lp * 2 + st_lane) = (uint16_t)(dw2 >> 16);
     }
+    if (pend) flush_half(halves + (t & 1) * (32 * 32), pend_row);
     // dq, k-part: K^T tile times dS^T (bf16 pairs exchanged with the partner
     // lane so that the operand lists keys 16t2 + 8hf .. +7 in order)
+    {
+      const u32x4* kts = sm.kv[t % NST] + 2 * TU;
 #pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2) {
-      const u32x4 pw = __builtin_bit_cast(u32x4, pack8(&ds[8 * t2]));
-      const auto s02 = __builtin_amdgcn_permlane32_swap(pw[0], pw[2], false, false);
-      const auto s13 = __builtin_amdgcn_permlane32_swap(pw[1], pw[3], false, false);
-      const bf16x8 dsb = __builtin_bit_cast(bf16x8, u32x4{s02[0], s13[0], s02[1], s13[1]});
+      for (int t2 = 0; t2 < 2; ++t2) {
+        const u32x4 pw = __builtin_bit_cast(u32x4, pack8(&ds[8 * t2]));
+        const auto s02 = __builtin_amdgcn_permlane32_swap(pw[0], pw[2], false, false);
+        const auto s13 = __builtin_amdgcn_permlane32_swap(pw[1], pw[3], false, false);
+        const bf16x8 dsb = __builtin_bit_cast(bf16x8, u32x4{s02[0], s13[0], s02[1], s13[1]});
 #pragma unroll
-      for (int e = 0; e < 2; ++e)
-        dqk[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ktf[t2][e], dsb, dqk[e], 0, 0, 0);
+        for (int e = 0; e < 2; ++e)
+          dqk[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8, kts[ofs64[t2][e]]), dsb, dqk[e], 0, 0, 0);
+      }
     }
-    if (more) load_kt(t + 1);
-    floatx16 Sn, dptn;
+    floatx16 Sn = floatx16{0}, dptn = floatx16{0};
     if (more) scores(t + 1, Sn, dptn);
     // dS shifted by distance: window position r = 31 + ii - jj, rows base + r
     uint16_t* lo = halves + (t & 1) * (32 * 32);
@@ -303,29 +384,48 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_q_kernel(BwdArgs a) {
         lo[r * 32 + ii] = x;
     }
     wave_lds_fence();
-    bf16x8 dw[4];
+    // dq, Rk-part: the Rk^T window (rows d, positions 0..31 from chunk t-w,
+    // 32..63 from chunk t-w-1) times the shifted dS
+    {
+      bf16x8 dw[4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) dw[s] = *reinterpret_cast<const bf16x8*>(drow + 16 * s + 8 * hf);
+      for (int s = 0; s < 4; ++s) dw[s] = *reinterpret_cast<const bf16x8*>(drow + 16 * s + 8 * hf);
+      const u32x4* rl = sm.rkt[rk_slot(t - wave)];
+      const u32x4* ru = sm.rkt[rk_slot(t - wave - 1)];
 #pragma unroll
-    for (int e = 0; e < 2; ++e)
+      for (int e = 0; e < 2; ++e)
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
-        dqr[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rtf[e][s], dw[s], dqr[e], 0, 0, 0);
-    if (more) load_rt(t + 1);
-    // rows base + 32 .. +63 are complete (keys of blocks t-1 and t)
-    flush_half(up, base + 32);
-    wave_lds_fence();
-    if (more) {
-      S = Sn;
-      dpt = dptn;
+        for (int s = 0; s < 4; ++s) {
+          const u32x4* src = s < 2 ? rl : ru;
+          dqr[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8, src[ofs64[s & 1][e]]), dw[s], dqr[e], 0, 0, 0);
+        }
     }
+    // rows base + 32 .. +63 are complete (keys of blocks t-1 and t): written
+    // out at the start of the next block
+    pend = true;
+    pend_row = base + 32;
+    S = Sn;
+    dpt = dptn;
   };
-  load_rows(0);
-  load_kt(0);
-  load_rt(0);
-  scores(0, S, dpt);
-  for (int32_t t = 0; t < t_end; ++t) block(t);
-  flush_half(halves + ((t_end - 1) & 1) * (32 * 32), M + i0 - 32 * (t_end - 1) - 31);
+
+  if (wave_on) scores(0, S, dpt);
+  for (int32_t t = 0; t < nb; ++t) {
+    // DMA block t+1 (issued one block ago) and this wave's stores of the
+    // previous block have landed; the stage of block t-1 takes DMA block t+2
+    if (t > 0) {
+      wait_vm<0>();
+      barrier_lds();
+    }
+    issue_block(t + 2, (t + 2) % NST);
+    if (t < t_end) block(t);
+  }
+  wait_vm<0>();   // the repeated loads past the last block
+  if (wave_on) {
+    if (pend) flush_half(halves + (t_end & 1) * (32 * 32), pend_row);
+    flush_half(halves + ((t_end - 1) & 1) * (32 * 32), M + i0 - 32 * (t_end - 1) - 31);
+  }
+  if (!wave_on) return;
 
   // dq = scale (k-part + Rk-part); lane holds d = 32e + 8g + 4hf + r of query i
   if (qok) {
