@@ -241,11 +241,16 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_q_kernel(BwdArgs a) {
 
   uint16_t* drow = sm.dsw[wave] + ii * DSW;
   uint16_t* halves = sm.half[wave][0];
-  // the first block's upper half starts empty
+  // the first block's upper half starts empty; a lane's row of the dS window
+  // is written at positions ii .. ii+31 by every block, so its other
+  // positions stay zero from here on
   {
     u32x4* h1 = reinterpret_cast<u32x4*>(sm.half[wave][1]);
     h1[lane] = u32x4{0u, 0u, 0u, 0u};
     h1[lane + 64] = u32x4{0u, 0u, 0u, 0u};
+    u32x4* z = reinterpret_cast<u32x4*>(drow + 32 * hf);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) z[c] = u32x4{0u, 0u, 0u, 0u};
   }
   const int64_t dsp_col = (int64_t)b * Lp + i0;
   const int64_t dsp_ld = (int64_t)a.B * Lp;
@@ -313,6 +318,22 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_q_kernel(BwdArgs a) {
     const bool more = t + 1 < t_end;
     // P and dS; key jj = 8g + 4hf + r (element 4g + r) visible iff j0 + jj <= M + i
     // (only blocks that reach past the wave's first query need the mask)
+    // operands of this block's dq products (K^T tile; Rk^T chunks t-w for
+    // window positions 0..31 and t-w-1 for 32..63), read now so that their
+    // LDS latency hides behind the softmax arithmetic and the stores
+    bf16x8 ktf[2][2], rtf[2][4];
+    {
+      const u32x4* kts = sm.kv[t % NST] + 2 * TU;
+      const u32x4* rl = sm.rkt[rk_slot(t - wave)];
+      const u32x4* ru = sm.rkt[rk_slot(t - wave - 1)];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2) ktf[t2][e] = __builtin_bit_cast(bf16x8, kts[ofs64[t2][e]]);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) rtf[e][s] = __builtin_bit_cast(bf16x8, (s < 2 ? rl : ru)[ofs64[s & 1][e]]);
+      }
+    }
     float p[16], ds[16];
 #pragma unroll
     for (int e = 0; e < 16; ++e) p[e] = __builtin_amdgcn_exp2f(S[e] - lse);
@@ -345,7 +366,6 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_q_kernel(BwdArgs a) {
     // dq, k-part: K^T tile times dS^T (bf16 pairs exchanged with the partner
     // lane so that the operand lists keys 16t2 + 8hf .. +7 in order)
     {
-      const u32x4* kts = sm.kv[t % NST] + 2 * TU;
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2) {
         const u32x4 pw = __builtin_bit_cast(u32x4, pack8(&ds[8 * t2]));
@@ -354,24 +374,18 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_q_kernel(BwdArgs a) {
         const bf16x8 dsb = __builtin_bit_cast(bf16x8, u32x4{s02[0], s13[0], s02[1], s13[1]});
 #pragma unroll
         for (int e = 0; e < 2; ++e)
-          dqk[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8, kts[ofs64[t2][e]]), dsb, dqk[e], 0, 0, 0);
+          dqk[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ktf[t2][e], dsb, dqk[e], 0, 0, 0);
       }
     }
     floatx16 Sn = floatx16{0}, dptn = floatx16{0};
     if (more) scores(t + 1, Sn, dptn);
     // dS shifted by distance: window position r = 31 + ii - jj, rows base + r
+    // Block t writes entries r >= ii of its lower half and r < ii of its
+    // upper half (block t-1's lower half), so the two halves it touches are
+    // whole once it is done; only the last block's lower half keeps stale
+    // entries (r < ii), cleared after the loop.
     uint16_t* lo = halves + (t & 1) * (32 * 32);
     uint16_t* up = halves + ((t + 1) & 1) * (32 * 32);
-    {
-      u32x4* z = reinterpret_cast<u32x4*>(drow + 32 * hf);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) z[c] = u32x4{0u, 0u, 0u, 0u};
-      u32x4* zl = reinterpret_cast<u32x4*>(lo);
-      zl[lane] = u32x4{0u, 0u, 0u, 0u};
-      zl[lane + 64] = u32x4{0u, 0u, 0u, 0u};
-    }
-    wave_lds_fence();
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int jj = 8 * (e >> 2) + 4 * hf + (e & 3);
@@ -390,16 +404,10 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_q_kernel(BwdArgs a) {
       bf16x8 dw[4];
 #pragma unroll
       for (int s = 0; s < 4; ++s) dw[s] = *reinterpret_cast<const bf16x8*>(drow + 16 * s + 8 * hf);
-      const u32x4* rl = sm.rkt[rk_slot(t - wave)];
-      const u32x4* ru = sm.rkt[rk_slot(t - wave - 1)];
 #pragma unroll
       for (int e = 0; e < 2; ++e)
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const u32x4* src = s < 2 ? rl : ru;
-          dqr[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8, src[ofs64[s & 1][e]]), dw[s], dqr[e], 0, 0, 0);
-        }
+        for (int s = 0; s < 4; ++s) dqr[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rtf[e][s], dw[s], dqr[e], 0, 0, 0);
     }
     // rows base + 32 .. +63 are complete (keys of blocks t-1 and t): written
     // out at the start of the next block
@@ -423,7 +431,12 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_q_kernel(BwdArgs a) {
   wait_vm<0>();   // the repeated loads past the last block
   if (wave_on) {
     if (pend) flush_half(halves + (t_end & 1) * (32 * 32), pend_row);
-    flush_half(halves + ((t_end - 1) & 1) * (32 * 32), M + i0 - 32 * (t_end - 1) - 31);
+    // entries r < ii of the last lower half belong to keys past the last
+    // block (not visible): zero
+    uint16_t* lo = halves + ((t_end - 1) & 1) * (32 * 32);
+    for (int r = 0; r < ii; ++r) lo[r * 32 + ii] = 0;
+    wave_lds_fence();
+    flush_half(lo, M + i0 - 32 * (t_end - 1) - 31);
   }
   if (!wave_on) return;
 
