@@ -25,11 +25,16 @@
 //   products, which need sums over queries.
 // bmm64_kernel: batched A B^T with 64 output columns (dk, dval, dRk), the
 //   masked entries of A selected away by index.
+#include <type_traits>
+
 #include "dev_common.h"
 
 namespace txl {
 
 namespace {
+
+template <int X>
+using IC = std::integral_constant<int, X>;
 
 constexpr int DP = 64;
 constexpr int KB = 32;
@@ -221,11 +226,26 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_q_kernel(BwdArgs a) {
   // score window: value for (query ii, key jj) is window row 31 + ii - jj of
   // [lower chunk ; upper chunk], stored at position jj of row ii
   float* win = sm.win[wave] + ii * WP;
+  // bit e of sel_bits: element e comes from the lower chunk (w >= ii).  The
+  // per-element choice is a bit select on a mask extracted from it inside
+  // the loop: sixteen lane masks kept live across the loop would not fit in
+  // the scalar registers.
+  uint32_t sel_bits = 0;
+#pragma unroll
+  for (int e = 0; e < 16; ++e)
+    if (8 * (e >> 2) + 4 * hf + (e & 3) >= ii) sel_bits |= 1u << e;
   auto write_win = [&](const floatx16& lower, const floatx16& upper) {
+    uint32_t sb = sel_bits;
+    asm volatile("" : "+v"(sb));
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int w = 8 * (e >> 2) + 4 * hf + (e & 3);
-      win[(31 + ii - w) & 31] = w >= ii ? lower[e] : upper[e];
+      const uint32_t m = (uint32_t)((int32_t)(sb << (31 - e)) >> 31);
+      // (elements copied out first: a bit cast of a vector element itself
+      // reads element 0)
+      const float le = lower[e], ue = upper[e];
+      const uint32_t x = (__builtin_bit_cast(uint32_t, le) & m) | (__builtin_bit_cast(uint32_t, ue) & ~m);
+      win[(31 + ii - w) & 31] = __builtin_bit_cast(float, x);
     }
   };
   auto read_win = [&]() {
@@ -268,14 +288,6 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_q_kernel(BwdArgs a) {
   };
 
   floatx16 dqk[2] = {floatx16{0}, floatx16{0}}, dqr[2] = {floatx16{0}, floatx16{0}};
-  // upper chunk of block 0: chunk -w-1 (distances base_0 + 32 .. +63,
-  // base_t = M + i0 - 32t - 31)
-  floatx16 upper = floatx16{0};
-  if (wave_on) {
-    bf16x8 rf[4];
-    read_rows(sm.rk[rk_slot(-wave - 1)], rf);
-    upper = bd_chunk(rf);
-  }
   // P^T, dS^T [key][query]: lane (ii, hf) writes query i of key rows
   // j0 + 8g + 4hf + r, 2 bytes each (a row of 32 queries is 64 contiguous
   // bytes); the row base is a scalar, the lane's part a constant offset
@@ -283,60 +295,78 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_q_kernel(BwdArgs a) {
   char* const dst_bh = static_cast<char*>(a.dst) + (int64_t)bh * Np * Lp * 2;
   const uint32_t st_lane = (uint32_t)(((4 * hf) * Lp + i) * 2);
 
-  // scores and dP^T of block t (its tiles and Rk chunk t-w in LDS); `upper`
-  // holds the chunk product of distances base_t + 32 .. +63 and receives that
-  // of base_t .. +31
-  floatx16 S = floatx16{0}, dpt = floatx16{0};
-  auto scores = [&](int32_t t, floatx16& So, floatx16& dpo) {
-    const u32x4* kvs = sm.kv[t % NST];
-    bf16x8 kf[4], vf[4], rf[4];
-    read_rows(sm.rk[rk_slot(t - wave)], rf);
-    read_rows(kvs + TU, vf);
-    read_rows(kvs, kf);
-    const floatx16 lower = bd_chunk(rf);
-    dpo = floatx16{0};
+  // Chunk products of the score window: block t uses [chunk t-w ; chunk
+  // t-w-1] (distances base_t .. +31, base_t + 32 .. +63, base_t = M + i0 -
+  // 32t - 31).  Two registers sets alternate: block t reads chunk t-w from
+  // one and writes chunk t+1-w into the other.
+  floatx16 C0 = floatx16{0}, C1 = floatx16{0};
+  // scores and dP^T of the current and the next block (alternating sets)
+  floatx16 SA = floatx16{0}, DA = floatx16{0}, SB = floatx16{0}, DB = floatx16{0};
+  if (wave_on) {
+    bf16x8 rf[4], vf[4], kf[4];
+    read_rows(sm.rk[rk_slot(-wave - 1)], rf);
+    C0 = bd_chunk(rf);
+    read_rows(sm.rk[rk_slot(-wave)], rf);
+    read_rows(sm.kv[0] + TU, vf);
+    read_rows(sm.kv[0], kf);
+    C1 = bd_chunk(rf);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) dpo = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[s], go[s], dpo, 0, 0, 0);
-    write_win(lower, upper);
+    for (int s = 0; s < 4; ++s) DA = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[s], go[s], DA, 0, 0, 0);
+    write_win(C1, C0);
     wave_lds_fence();
-    So = read_win();
+    SA = read_win();
 #pragma unroll
-    for (int s = 0; s < 4; ++s) So = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qu[s], So, 0, 0, 0);
-    upper = lower;
-  };
+    for (int s = 0; s < 4; ++s) SA = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qu[s], SA, 0, 0, 0);
+  }
 
-  // Block t with its scores and dP^T already in S, dpt.  The next block's
-  // products are issued once this block's dS exists, so that they run on the
-  // matrix cores while this block's shifted-dS phase runs on LDS and VALU.
-  // The previous block's completed dS'^T half is written out first, so that
-  // its stores have landed by the next barrier.
+  // Block t, with its scores and dP^T in Sc, dpc and chunk t-w in up_in.
+  // Order: the LDS reads of every operand this block needs (its dq products,
+  // the next block's scores), the next block's chunk and dP^T products, P
+  // and dS on the vector ALUs while those run, dq's k-part; then the LDS
+  // writes (the next block's score window, the shifted dS) and the P^T /
+  // dS^T stores, one fence, and the products that read what was written.
+  // The previous block's completed dS'^T half is written out before this
+  // block's shifted dS overwrites it.
   bool pend = false;   // halves[(t) & 1] holds rows pend_row .. +31, complete
   int32_t pend_row = 0;
-  auto block = [&](int32_t t) {
+  auto block = [&](auto PAR, int32_t t, const floatx16& Sc, const floatx16& dpc, floatx16& Sn,
+                   floatx16& dpn, const floatx16& up_in, floatx16& low_out) {
+    constexpr int par = decltype(PAR)::value;   // t & 1
     const int32_t j0 = t * KB;
     const int32_t base = M + i0 - 32 * t - 31;
     const bool more = t + 1 < t_end;
-    // P and dS; key jj = 8g + 4hf + r (element 4g + r) visible iff j0 + jj <= M + i
-    // (only blocks that reach past the wave's first query need the mask)
-    // operands of this block's dq products (K^T tile; Rk^T chunks t-w for
-    // window positions 0..31 and t-w-1 for 32..63), read now so that their
-    // LDS latency hides behind the softmax arithmetic and the stores
-    bf16x8 ktf[2][2], rtf[2][4];
+    // operands: K^T tile t and Rk^T chunks t-w (window positions 0..31),
+    // t-w-1 (32..63) for dq; Rk chunk t+1-w, val and K tiles t+1 for the
+    // next block (read whether or not it exists: every slot holds valid data)
+    bf16x8 ktf[2][2], rtf[2][4], rf[4], vf[4], kf[4];
     {
       const u32x4* kts = sm.kv[t % NST] + 2 * TU;
       const u32x4* rl = sm.rkt[rk_slot(t - wave)];
       const u32x4* ru = sm.rkt[rk_slot(t - wave - 1)];
+      const u32x4* kvn = sm.kv[(t + 1) % NST];
+      read_rows(sm.rk[rk_slot(t + 1 - wave)], rf);
+      read_rows(kvn + TU, vf);
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
+      for (int e = 0; e < 2; ++e)
 #pragma unroll
         for (int t2 = 0; t2 < 2; ++t2) ktf[t2][e] = __builtin_bit_cast(bf16x8, kts[ofs64[t2][e]]);
 #pragma unroll
+      for (int e = 0; e < 2; ++e)
+#pragma unroll
         for (int s = 0; s < 4; ++s) rtf[e][s] = __builtin_bit_cast(bf16x8, (s < 2 ? rl : ru)[ofs64[s & 1][e]]);
-      }
+      read_rows(kvn, kf);
     }
+    if (more) {
+      low_out = bd_chunk(rf);
+      dpn = floatx16{0};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) dpn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[s], go[s], dpn, 0, 0, 0);
+    }
+    // P and dS; key jj = 8g + 4hf + r (element 4g + r) visible iff j0 + jj <= M + i
+    // (only blocks that reach past the wave's first query need the mask)
     float p[16], ds[16];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) p[e] = __builtin_amdgcn_exp2f(S[e] - lse);
+    for (int e = 0; e < 16; ++e) p[e] = __builtin_amdgcn_exp2f(Sc[e] - lse);
     if (j0 + KB - 1 > M + i0) {
       const int32_t lim = M + i - j0 - 4 * hf;
 #pragma unroll
@@ -346,58 +376,68 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_q_kernel(BwdArgs a) {
       }
     }
 #pragma unroll
-    for (int e = 0; e < 16; ++e) ds[e] = p[e] * (dpt[e] - dsum);
-    // bf16 pairs (keys 8g + 4hf + r, r and r+1) stored as two 2-byte halves
+    for (int e = 0; e < 16; ++e) ds[e] = p[e] * (dpc[e] - dsum);
+    // bf16 pairs: keys (8g + 4hf + r, r+1) for e = 4g + r, r even
+    typedef float floatx2_t __attribute__((ext_vector_type(2)));
+    typedef bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    uint32_t pw[8], dw2[8];
 #pragma unroll
-    for (int e = 0; e < 16; e += 2) {
-      const int jj = 8 * (e >> 2) + (e & 3);   // key of element e, less 4hf
-      typedef float floatx2_t __attribute__((ext_vector_type(2)));
-      typedef bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-      const uint32_t pw = __builtin_bit_cast(uint32_t, __builtin_convertvector(floatx2_t{p[e], p[e + 1]}, bf16x2_t));
-      const uint32_t dw2 = __builtin_bit_cast(uint32_t, __builtin_convertvector(floatx2_t{ds[e], ds[e + 1]}, bf16x2_t));
-      char* pr = pt_bh + (int64_t)(j0 + jj) * Lp * 2;
-      char* dr = dst_bh + (int64_t)(j0 + jj) * Lp * 2;
-      *reinterpret_cast<uint16_t*>(pr + st_lane) = (uint16_t)pw;
-      *reinterpret_cast<uint16_t*>(pr + Lp * 2 + st_lane) = (uint16_t)(pw >> 16);
-      *reinterpret_cast<uint16_t*>(dr + st_lane) = (uint16_t)dw2;
-      *reinterpret_cast<uint16_t*>(dr + Lp * 2 + st_lane) = (uint16_t)(dw2 >> 16);
+    for (int m = 0; m < 8; ++m) {
+      pw[m] = __builtin_bit_cast(uint32_t, __builtin_convertvector(floatx2_t{p[2 * m], p[2 * m + 1]}, bf16x2_t));
+      dw2[m] = __builtin_bit_cast(uint32_t, __builtin_convertvector(floatx2_t{ds[2 * m], ds[2 * m + 1]}, bf16x2_t));
     }
-    if (pend) flush_half(halves + (t & 1) * (32 * 32), pend_row);
     // dq, k-part: K^T tile times dS^T (bf16 pairs exchanged with the partner
     // lane so that the operand lists keys 16t2 + 8hf .. +7 in order)
-    {
 #pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2) {
-        const u32x4 pw = __builtin_bit_cast(u32x4, pack8(&ds[8 * t2]));
-        const auto s02 = __builtin_amdgcn_permlane32_swap(pw[0], pw[2], false, false);
-        const auto s13 = __builtin_amdgcn_permlane32_swap(pw[1], pw[3], false, false);
-        const bf16x8 dsb = __builtin_bit_cast(bf16x8, u32x4{s02[0], s13[0], s02[1], s13[1]});
+    for (int t2 = 0; t2 < 2; ++t2) {
+      const auto s02 = __builtin_amdgcn_permlane32_swap(dw2[4 * t2 + 0], dw2[4 * t2 + 2], false, false);
+      const auto s13 = __builtin_amdgcn_permlane32_swap(dw2[4 * t2 + 1], dw2[4 * t2 + 3], false, false);
+      const bf16x8 dsb = __builtin_bit_cast(bf16x8, u32x4{s02[0], s13[0], s02[1], s13[1]});
 #pragma unroll
-        for (int e = 0; e < 2; ++e)
-          dqk[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ktf[t2][e], dsb, dqk[e], 0, 0, 0);
-      }
+      for (int e = 0; e < 2; ++e)
+        dqk[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ktf[t2][e], dsb, dqk[e], 0, 0, 0);
     }
-    floatx16 Sn = floatx16{0}, dptn = floatx16{0};
-    if (more) scores(t + 1, Sn, dptn);
-    // dS shifted by distance: window position r = 31 + ii - jj, rows base + r
-    // Block t writes entries r >= ii of its lower half and r < ii of its
-    // upper half (block t-1's lower half), so the two halves it touches are
-    // whole once it is done; only the last block's lower half keeps stale
-    // entries (r < ii), cleared after the loop.
-    uint16_t* lo = halves + (t & 1) * (32 * 32);
-    uint16_t* up = halves + ((t + 1) & 1) * (32 * 32);
+    if (more) write_win(low_out, up_in);
+    if (pend) flush_half(halves + par * (32 * 32), pend_row);
+    // dS shifted by distance: window position r = 31 + ii - jj, rows base + r.
+    // The two halves form a ring of 64 rows: block t's lower half (r < 32)
+    // is half t & 1 and its upper half the other, i.e. ring row r for even
+    // t and r ^ 32 for odd t.  Block t writes entries r >= ii of its lower
+    // half and r < ii of its upper half (block t-1's lower half), so the two
+    // halves it touches are whole once it is done; only the last block's
+    // lower half keeps stale entries (r < ii), cleared after the loop.
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int jj = 8 * (e >> 2) + 4 * hf + (e & 3);
       const int r = 31 + ii - jj;
-      const uint16_t x = bf16_bits(ds[e]);
+      const uint16_t x = (uint16_t)(dw2[e >> 1] >> (16 * (e & 1)));
       drow[r] = x;
-      if (r >= 32)
-        up[(r - 32) * 32 + ii] = x;
-      else
-        lo[r * 32 + ii] = x;
+      halves[(par ? r ^ 32 : r) * 32 + ii] = x;
+    }
+    // P^T and dS^T of block t, two bytes per lane and row: one scalar base per
+    // block (the first key made opaque, so that the compiler keeps no
+    // per-row pointers across the loop) and a 32-bit offset per store
+    {
+      int32_t j0s = j0;
+      asm volatile("" : "+s"(j0s));
+      const char* pb = pt_bh + (int64_t)j0s * Lp * 2;
+      const char* db = dst_bh + (int64_t)j0s * Lp * 2;
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const int jj = 8 * (m >> 1) + 2 * (m & 1);   // key of element 2m, less 4hf
+        const uint32_t o0 = st_lane + (uint32_t)(jj * Lp * 2), o1 = o0 + (uint32_t)(Lp * 2);
+        *reinterpret_cast<uint16_t*>(const_cast<char*>(pb) + o0) = (uint16_t)pw[m];
+        *reinterpret_cast<uint16_t*>(const_cast<char*>(pb) + o1) = (uint16_t)(pw[m] >> 16);
+        *reinterpret_cast<uint16_t*>(const_cast<char*>(db) + o0) = (uint16_t)dw2[m];
+        *reinterpret_cast<uint16_t*>(const_cast<char*>(db) + o1) = (uint16_t)(dw2[m] >> 16);
+      }
     }
     wave_lds_fence();
+    if (more) {
+      Sn = read_win();
+#pragma unroll
+      for (int s = 0; s < 4; ++s) Sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qu[s], Sn, 0, 0, 0);
+    }
     // dq, Rk-part: the Rk^T window (rows d, positions 0..31 from chunk t-w,
     // 32..63 from chunk t-w-1) times the shifted dS
     {
@@ -413,20 +453,25 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_q_kernel(BwdArgs a) {
     // out at the start of the next block
     pend = true;
     pend_row = base + 32;
-    S = Sn;
-    dpt = dptn;
   };
 
-  if (wave_on) scores(0, S, dpt);
-  for (int32_t t = 0; t < nb; ++t) {
-    // DMA block t+1 (issued one block ago) and this wave's stores of the
-    // previous block have landed; the stage of block t-1 takes DMA block t+2
+  // one loop step: DMA block t+1 (issued one block ago) and this wave's
+  // stores of the previous block have landed; the stage of block t-1 takes
+  // DMA block t+2
+  auto step = [&](auto PAR, int32_t t, const floatx16& Sc, const floatx16& dpc, floatx16& Sn,
+                  floatx16& dpn, const floatx16& up_in, floatx16& low_out) {
     if (t > 0) {
       wait_vm<0>();
       barrier_lds();
     }
     issue_block(t + 2, (t + 2) % NST);
-    if (t < t_end) block(t);
+    if (t < t_end) block(PAR, t, Sc, dpc, Sn, dpn, up_in, low_out);
+  };
+  // unrolled twice so that the two register sets trade roles without copies
+  // and the ring parity of the dS halves is a constant
+  for (int32_t t = 0; t < nb; t += 2) {
+    step(IC<0>{}, t, SA, DA, SB, DB, C1, C0);
+    if (t + 1 < nb) step(IC<1>{}, t + 1, SB, DB, SA, DA, C0, C1);
   }
   wait_vm<0>();   // the repeated loads past the last block
   if (wave_on) {
