@@ -39,7 +39,6 @@ using IC = std::integral_constant<int, X>;
 constexpr int DP = 64;
 constexpr int KB = 32;
 constexpr int WP = 36;     // floats per query row of the score window
-constexpr int DSW = 72;    // bf16 per query row of the dS' window (64 + pad)
 constexpr int NST = 3;     // K / val / K^T ring stages (blocks t .. t+2)
 constexpr int RKS = 8;     // Rk and Rk^T chunk slots: chunk c in slot (c + 8) & 7
 constexpr int TU = 256;    // 16-byte units of a 4 KB tile
@@ -50,7 +49,6 @@ struct BwdSmem {
   u32x4 rk[RKS][TU];                // Rk chunk: 32 rows x 128 B
   u32x4 rkt[RKS][TU];               // Rk^T chunk: 64 d x 32 distances (64 B)
   float win[4][32 * WP];            // per wave: shifted (b)+(d) window of the scores
-  uint16_t dsw[4][32 * DSW];        // per wave: query row i, position 31 + i - j -> dS_ij
   uint16_t half[4][2][32 * 32];     // per wave: two 32-row halves of dS'^T [row][query]
 };
 static_assert(sizeof(BwdSmem) <= 160 * 1024, "one workgroup per CU");
@@ -259,18 +257,12 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_q_kernel(BwdArgs a) {
     return c;
   };
 
-  uint16_t* drow = sm.dsw[wave] + ii * DSW;
   uint16_t* halves = sm.half[wave][0];
-  // the first block's upper half starts empty; a lane's row of the dS window
-  // is written at positions ii .. ii+31 by every block, so its other
-  // positions stay zero from here on
+  // the first block's upper half starts empty
   {
     u32x4* h1 = reinterpret_cast<u32x4*>(sm.half[wave][1]);
     h1[lane] = u32x4{0u, 0u, 0u, 0u};
     h1[lane + 64] = u32x4{0u, 0u, 0u, 0u};
-    u32x4* z = reinterpret_cast<u32x4*>(drow + 32 * hf);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) z[c] = u32x4{0u, 0u, 0u, 0u};
   }
   const int64_t dsp_col = (int64_t)b * Lp + i0;
   const int64_t dsp_ld = (int64_t)a.B * Lp;
@@ -288,6 +280,39 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_q_kernel(BwdArgs a) {
   };
 
   floatx16 dqk[2] = {floatx16{0}, floatx16{0}}, dqr[2] = {floatx16{0}, floatx16{0}};
+  // dq, Rk-part, one complete half at a time: dq_i += sum over its 32
+  // distances of dS'[delta][i] Rk[delta], the Rk^T chunk of those distances
+  // (rows d, k = distance) times the half ([distance][query], row-major).
+  // The half feeds the matrix cores through transposing LDS reads: in each
+  // group of 16 lanes, lane a + 4q points at row k0 + q, queries 4a .. 4a+3,
+  // and lane j receives query j of rows k0 .. k0+3; two reads give the eight
+  // distances 16t2 + 8(lane / 32) .. +7 of query lane % 32.
+  typedef short short4_t __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) short4_t lds_short4;
+  const int tr_base = (8 * (lane >> 5) + ((lane >> 2) & 3)) * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  auto half_frags = [&](const uint16_t* hsrc, bf16x8 (&bq)[2]) {
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) {
+      const short4_t r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_short4*)(hsrc + tr_base + (16 * t2) * 32));
+      const short4_t r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_short4*)(hsrc + tr_base + (16 * t2 + 4) * 32));
+      bq[t2] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+  };
+  auto chunk_frags = [&](int32_t c, bf16x8 (&af)[2][2]) {   // [t2][e]
+    const u32x4* rt = sm.rkt[rk_slot(c)];
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) af[t2][e] = __builtin_bit_cast(bf16x8, rt[ofs64[t2][e]]);
+  };
+  auto half_dqr = [&](const bf16x8 (&af)[2][2], const bf16x8 (&bq)[2]) {
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) dqr[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[t2][e], bq[t2], dqr[e], 0, 0, 0);
+  };
   // P^T, dS^T [key][query]: lane (ii, hf) writes query i of key rows
   // j0 + 8g + 4hf + r, 2 bytes each (a row of 32 queries is 64 contiguous
   // bytes); the row base is a scalar, the lane's part a constant offset
@@ -335,14 +360,12 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_q_kernel(BwdArgs a) {
     const int32_t j0 = t * KB;
     const int32_t base = M + i0 - 32 * t - 31;
     const bool more = t + 1 < t_end;
-    // operands: K^T tile t and Rk^T chunks t-w (window positions 0..31),
-    // t-w-1 (32..63) for dq; Rk chunk t+1-w, val and K tiles t+1 for the
-    // next block (read whether or not it exists: every slot holds valid data)
-    bf16x8 ktf[2][2], rtf[2][4], rf[4], vf[4], kf[4];
+    // operands: K^T tile t and the Rk^T chunk t-w-2 of the half completed by
+    // block t-1 for dq; Rk chunk t+1-w, val and K tiles t+1 for the next
+    // block (read whether or not it exists: every slot holds valid data)
+    bf16x8 ktf[2][2], rtf[2][2], rf[4], vf[4], kf[4];
     {
       const u32x4* kts = sm.kv[t % NST] + 2 * TU;
-      const u32x4* rl = sm.rkt[rk_slot(t - wave)];
-      const u32x4* ru = sm.rkt[rk_slot(t - wave - 1)];
       const u32x4* kvn = sm.kv[(t + 1) % NST];
       read_rows(sm.rk[rk_slot(t + 1 - wave)], rf);
       read_rows(kvn + TU, vf);
@@ -350,10 +373,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_q_kernel(BwdArgs a) {
       for (int e = 0; e < 2; ++e)
 #pragma unroll
         for (int t2 = 0; t2 < 2; ++t2) ktf[t2][e] = __builtin_bit_cast(bf16x8, kts[ofs64[t2][e]]);
-#pragma unroll
-      for (int e = 0; e < 2; ++e)
-#pragma unroll
-        for (int s = 0; s < 4; ++s) rtf[e][s] = __builtin_bit_cast(bf16x8, (s < 2 ? rl : ru)[ofs64[s & 1][e]]);
+      chunk_frags(t - wave - 2, rtf);
       read_rows(kvn, kf);
     }
     if (more) {
@@ -398,7 +418,14 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_q_kernel(BwdArgs a) {
         dqk[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ktf[t2][e], dsb, dqk[e], 0, 0, 0);
     }
     if (more) write_win(low_out, up_in);
-    if (pend) flush_half(halves + par * (32 * 32), pend_row);
+    // the half completed by block t-1 (distances base + 64 .. +95): dq's
+    // Rk-part and the write-out, before this block's lower half reuses it
+    if (pend) {
+      bf16x8 bq[2];
+      half_frags(halves + par * (32 * 32), bq);
+      flush_half(halves + par * (32 * 32), pend_row);
+      half_dqr(rtf, bq);
+    }
     // dS shifted by distance: window position r = 31 + ii - jj, rows base + r.
     // The two halves form a ring of 64 rows: block t's lower half (r < 32)
     // is half t & 1 and its upper half the other, i.e. ring row r for even
@@ -411,7 +438,6 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_q_kernel(BwdArgs a) {
       const int jj = 8 * (e >> 2) + 4 * hf + (e & 3);
       const int r = 31 + ii - jj;
       const uint16_t x = (uint16_t)(dw2[e >> 1] >> (16 * (e & 1)));
-      drow[r] = x;
       halves[(par ? r ^ 32 : r) * 32 + ii] = x;
     }
     // P^T and dS^T of block t, two bytes per lane and row: one scalar base per
@@ -437,17 +463,6 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_q_kernel(BwdArgs a) {
       Sn = read_win();
 #pragma unroll
       for (int s = 0; s < 4; ++s) Sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qu[s], Sn, 0, 0, 0);
-    }
-    // dq, Rk-part: the Rk^T window (rows d, positions 0..31 from chunk t-w,
-    // 32..63 from chunk t-w-1) times the shifted dS
-    {
-      bf16x8 dw[4];
-#pragma unroll
-      for (int s = 0; s < 4; ++s) dw[s] = *reinterpret_cast<const bf16x8*>(drow + 16 * s + 8 * hf);
-#pragma unroll
-      for (int e = 0; e < 2; ++e)
-#pragma unroll
-        for (int s = 0; s < 4; ++s) dqr[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rtf[e][s], dw[s], dqr[e], 0, 0, 0);
     }
     // rows base + 32 .. +63 are complete (keys of blocks t-1 and t): written
     // out at the start of the next block
@@ -475,13 +490,23 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_q_kernel(BwdArgs a) {
   }
   wait_vm<0>();   // the repeated loads past the last block
   if (wave_on) {
-    if (pend) flush_half(halves + (t_end & 1) * (32 * 32), pend_row);
+    bf16x8 af[2][2], bq[2];
+    if (pend) {   // block t_end-1's upper half: distances base + 32 .. +63 of that block
+      const uint16_t* hp = halves + (t_end & 1) * (32 * 32);
+      chunk_frags(t_end - wave - 2, af);
+      half_frags(hp, bq);
+      flush_half(hp, pend_row);
+      half_dqr(af, bq);
+    }
     // entries r < ii of the last lower half belong to keys past the last
     // block (not visible): zero
     uint16_t* lo = halves + ((t_end - 1) & 1) * (32 * 32);
     for (int r = 0; r < ii; ++r) lo[r * 32 + ii] = 0;
     wave_lds_fence();
+    chunk_frags(t_end - 1 - wave, af);
+    half_frags(lo, bq);
     flush_half(lo, M + i0 - 32 * (t_end - 1) - 31);
+    half_dqr(af, bq);
   }
   if (!wave_on) return;
 
