@@ -885,13 +885,31 @@ txl_status_t run_bwd_from_state(const BwdPlan& bp, const AttnPtrs& a, const void
                                                         stream);
                          }),
                          "dRk transpose", stream));
+    // Split K (the distances) S ways into fp32 partials, summed in order by
+    // a second launch: the product alone has too few 128x128 tiles to fill
+    // the chip (d_model 512: 16).  The partials reuse the dRk partial buffer,
+    // whose sum has already been taken.
+    const int64_t tiles = (int64_t)((HD + 127) / 128) * ((p.dpos + 127) / 128);
+    int S = 1;
+    while (2 * S <= 8 && Pk % (64 * 2 * S) == 0 && Pk / (2 * S) >= 128 &&
+           tiles * 2 * S <= device_cu_count() && (int64_t)2 * S * p.dpos <= (int64_t)p.B * p.P)
+      S *= 2;
+    const int32_t Ks = Pk / S;
+    float* wparts = S > 1 ? drk_part : g.d_W_kR;
     GemmGroup gw{};
-    add_problem(gw, (int32_t)HD, p.dpos, Pk, src_plain(drkt, Pk, (int32_t)HD),
-                src_plain(rt, Pk, p.dpos),
-                out_map(g.d_W_kR, TXL_F32, (int32_t)HD, p.dpos, axis_linear(p.dpos), axis_linear(1)),
-                gemm_tile(TXL_BF16));
+    for (int sk = 0; sk < S; ++sk)
+      add_problem(gw, (int32_t)HD, p.dpos, Ks, src_plain(drkt + (size_t)sk * Ks * 2, Pk, (int32_t)HD),
+                  src_plain(rt + (size_t)sk * Ks * 2, Pk, p.dpos),
+                  out_map(wparts + (int64_t)sk * HD * p.dpos, TXL_F32, (int32_t)HD, p.dpos,
+                          axis_linear(p.dpos), axis_linear(1)),
+                  gemm_tile(TXL_BF16));
     TXL_TRY(after_launch(timed(K_BWD_AUX, stream, [&] { return launch_gemm_bf16(gw, stream); }),
                          "dW_kR GEMM", stream));
+    if (S > 1)
+      TXL_TRY(after_launch(timed(K_BWD_AUX, stream, [&] {
+                             return launch_sum_rows(wparts, S, HD * p.dpos, g.d_W_kR, stream);
+                           }),
+                           "dW_kR split sum", stream));
   }
   return TXL_OK;
 }
