@@ -859,7 +859,8 @@ txl_status_t run_bwd_from_state(const BwdPlan& bp, const AttnPtrs& a, const void
       bmm(ws + bp.dspt.off, BL, make_axis(p.B, (int64_t)bp.dsp_rows * BL, p.Lp), ws + bp.qvt.off,
           BL, make_axis(p.B, DP * BL, p.Lp), BHn, p.Lp, p.scale, drk_part,
           make_axis(p.B, p.dh, (int64_t)p.P * HD))};
-  TXL_TRY(after_launch(timed(K_BWD_BMM, stream, [&] { return launch_bmm64(prods, 3, stream); }),
+  // products 0 and 1 read P^T, dS^T from the query kernel's fragment tiles
+  TXL_TRY(after_launch(timed(K_BWD_BMM, stream, [&] { return launch_bmm64(prods, 3, 0x3, stream); }),
                        "dk, dval, dRk products", stream));
   TXL_TRY(after_launch(timed(K_BWD_AUX, stream, [&] {
                          return launch_sum_rows(drk_part, p.B, (int64_t)p.P * HD, g.d_Rk, stream);

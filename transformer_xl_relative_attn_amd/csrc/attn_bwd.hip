@@ -42,6 +42,7 @@ constexpr int WP = 36;     // floats per query row of the score window
 constexpr int NST = 3;     // K / val / K^T ring stages (blocks t .. t+2)
 constexpr int RKS = 8;     // Rk and Rk^T chunk slots: chunk c in slot (c + 8) & 7
 constexpr int TU = 256;    // 16-byte units of a 4 KB tile
+constexpr int TPW = 36;    // bf16 per query row of the P / dS transpose tiles (32 + pad)
 constexpr float kNegInf = -__builtin_inff();
 
 struct BwdSmem {
@@ -50,6 +51,7 @@ struct BwdSmem {
   u32x4 rkt[RKS][TU];               // Rk^T chunk: 64 d x 32 distances (64 B)
   float win[4][32 * WP];            // per wave: shifted (b)+(d) window of the scores
   uint16_t half[4][2][32 * 32];     // per wave: two 32-row halves of dS'^T [row][query]
+  uint16_t tp[4][2][32 * TPW];      // per wave: P and dS of a block, [query][key]
 };
 static_assert(sizeof(BwdSmem) <= 160 * 1024, "one workgroup per CU");
 
@@ -313,12 +315,26 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_q_kernel(BwdArgs a) {
 #pragma unroll
       for (int e = 0; e < 2; ++e) dqr[e] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[t2][e], bq[t2], dqr[e], 0, 0, 0);
   };
-  // P^T, dS^T [key][query]: lane (ii, hf) writes query i of key rows
-  // j0 + 8g + 4hf + r, 2 bytes each (a row of 32 queries is 64 contiguous
-  // bytes); the row base is a scalar, the lane's part a constant offset
+  // P^T, dS^T in fragment tiles: tile (jb, kb) holds keys 32jb .. +31 and
+  // queries 16kb .. +15 as 64 lanes x 16 bytes, lane key % 32 + 32 ((query %
+  // 16) / 8) with queries 8 apart in order, i.e. the matrix-core operand of
+  // the key-side products, read there as one contiguous kilobyte.  A block's
+  // two tiles are assembled by a [query][key] transpose tile in LDS (lane
+  // (ii, hf) writes four keys at a time) read back with transposing reads.
   char* const pt_bh = static_cast<char*>(a.pt) + (int64_t)bh * Np * Lp * 2;
   char* const dst_bh = static_cast<char*>(a.dst) + (int64_t)bh * Np * Lp * 2;
-  const uint32_t st_lane = (uint32_t)(((4 * hf) * Lp + i) * 2);
+  uint16_t* const tpp = sm.tp[wave][0];
+  uint16_t* const tpd = sm.tp[wave][1];
+  const int tp_w = ii * TPW + 4 * hf;   // + 8g: keys 8g + 4hf .. +3 of query ii
+  const int tp_r = (8 * (lane >> 5) + ((lane >> 2) & 3)) * TPW + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  auto tile_frags = [&](const uint16_t* src, bf16x8 (&fq)[2]) {
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const short4_t r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(src + tp_r + (16 * s2) * TPW));
+      const short4_t r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(src + tp_r + (16 * s2 + 4) * TPW));
+      fq[s2] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+  };
 
   // Chunk products of the score window: block t uses [chunk t-w ; chunk
   // t-w-1] (distances base_t .. +31, base_t + 32 .. +63, base_t = M + i0 -
@@ -440,29 +456,31 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_q_kernel(BwdArgs a) {
       const uint16_t x = (uint16_t)(dw2[e >> 1] >> (16 * (e & 1)));
       halves[(par ? r ^ 32 : r) * 32 + ii] = x;
     }
-    // P^T and dS^T of block t, two bytes per lane and row: one scalar base per
-    // block (the first key made opaque, so that the compiler keeps no
-    // per-row pointers across the loop) and a 32-bit offset per store
-    {
-      int32_t j0s = j0;
-      asm volatile("" : "+s"(j0s));
-      const char* pb = pt_bh + (int64_t)j0s * Lp * 2;
-      const char* db = dst_bh + (int64_t)j0s * Lp * 2;
+    // P and dS of block t into the transpose tiles (keys 8g + 4hf .. +3 of
+    // query ii: the bf16 pairs 2g, 2g+1)
 #pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        const int jj = 8 * (m >> 1) + 2 * (m & 1);   // key of element 2m, less 4hf
-        const uint32_t o0 = st_lane + (uint32_t)(jj * Lp * 2), o1 = o0 + (uint32_t)(Lp * 2);
-        *reinterpret_cast<uint16_t*>(const_cast<char*>(pb) + o0) = (uint16_t)pw[m];
-        *reinterpret_cast<uint16_t*>(const_cast<char*>(pb) + o1) = (uint16_t)(pw[m] >> 16);
-        *reinterpret_cast<uint16_t*>(const_cast<char*>(db) + o0) = (uint16_t)dw2[m];
-        *reinterpret_cast<uint16_t*>(const_cast<char*>(db) + o1) = (uint16_t)(dw2[m] >> 16);
-      }
+    for (int g = 0; g < 4; ++g) {
+      *reinterpret_cast<uint2*>(tpp + tp_w + 8 * g) = uint2{pw[2 * g], pw[2 * g + 1]};
+      *reinterpret_cast<uint2*>(tpd + tp_w + 8 * g) = uint2{dw2[2 * g], dw2[2 * g + 1]};
     }
     wave_lds_fence();
     if (more) {
       Sn = read_win();
 #pragma unroll
       for (int s = 0; s < 4; ++s) Sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qu[s], Sn, 0, 0, 0);
+    }
+    // P^T and dS^T tiles (t, i0/16 + s2): one contiguous kilobyte each
+    {
+      bf16x8 fp[2], fd[2];
+      tile_frags(tpp, fp);
+      tile_frags(tpd, fd);
+      const int64_t tile0 = (int64_t)t * (Lp / 16) + i0 / 16;
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const int64_t off = ((tile0 + s2) * 64 + lane) * 16;
+        *reinterpret_cast<bf16x8*>(pt_bh + off) = fp[s2];
+        *reinterpret_cast<bf16x8*>(dst_bh + off) = fd[s2];
+      }
     }
     // rows base + 32 .. +63 are complete (keys of blocks t-1 and t): written
     // out at the start of the next block
@@ -569,6 +587,7 @@ __device__ __forceinline__ bf16x8 band_mask(bf16x8 f, int32_t lo, int32_t hi, bo
 // chip instead of each product's last partial round running alone.
 struct BmmBatch {
   BmmArgs p[3];
+  int32_t frag_bits;   // bit z: product z reads A from the query kernel's fragment tiles
 };
 
 __global__ __launch_bounds__(256, 2) void bmm64_kernel(BmmBatch bt) {
@@ -601,6 +620,24 @@ __global__ __launch_bounds__(256, 2) void bmm64_kernel(BmmBatch bt) {
   floatx16 acc[BMM_RM][2];
 #pragma unroll
   for (int r = 0; r < BMM_RM; ++r) acc[r][0] = acc[r][1] = floatx16{0};
+  // Fragment tiles (a_frag): the lane's 16 bytes of k-step 0 in each of its
+  // row tiles (clamped into the rows that hold data; rows past M are not
+  // stored).  A tile (jb, k-step) was written by the query kernel's wave of
+  // queries 32w .. +31 (w = k-step / 2) iff that wave visited key block jb,
+  // i.e. jb < t_end(w); other tiles hold no data and are skipped.
+  const bool frag = (bt.frag_bits >> z) & 1;
+  if (frag) {
+#pragma unroll
+    for (int r = 0; r < BMM_RM; ++r) {
+      const int32_t jb = min(m0 / 32 + r, (a.M + 31) / 32 - 1);
+      arow[r] = A + ((int64_t)jb * (a.K / 16) * 64 + lane) * 8;
+    }
+  }
+  auto tile_written = [&](int r, int32_t kk) {
+    const int32_t w = kk >> 5;   // query tile of 32
+    const int32_t t_end = (a.moff + min(32 * w + 31, a.klim - 1) + 32) / 32;
+    return m0 / 32 + r < t_end;
+  };
   // rows need k >= m - moff and none at or past kend
   const int32_t kend = min(a.K, a.klim);
   const int32_t kfirst_wg = max(0, mwg - a.moff) & ~(BMM_KC - 1);
@@ -614,6 +651,10 @@ __global__ __launch_bounds__(256, 2) void bmm64_kernel(BmmBatch bt) {
     bf16x8 a[BMM_RM];
     int32_t kk;   // first k of the step (wave-uniform)
   };
+  // the K loop, instantiated once per layout of A (registers are allocated
+  // per instantiation)
+  auto run = [&](auto FR) {
+  constexpr bool fr = decltype(FR)::value;
   for (int32_t kc = kfirst_wg; kc < kend; kc += BMM_KC) {
     const int32_t kc_end = min(kend, kc + BMM_KC);
     // stage B[:, kc .. kc + 512): wave w fills rows 16w .. 16w+15, one 1 KB
@@ -634,8 +675,9 @@ __global__ __launch_bounds__(256, 2) void bmm64_kernel(BmmBatch bt) {
     auto load = [&](int32_t st, Frag& f) {
       f.kk = k_lo + 16 * st;
       const int32_t k = f.kk + 8 * hf;
+      const int32_t off = fr ? (f.kk >> 4) * 512 : k;
 #pragma unroll
-      for (int r = 0; r < BMM_RM; ++r) f.a[r] = *reinterpret_cast<const bf16x8*>(arow[r] + k);
+      for (int r = 0; r < BMM_RM; ++r) f.a[r] = *reinterpret_cast<const bf16x8*>(arow[r] + off);
     };
     auto use = [&](Frag& f) {
       const int c = (f.kk - kc) / 8 + hf;
@@ -644,11 +686,15 @@ __global__ __launch_bounds__(256, 2) void bmm64_kernel(BmmBatch bt) {
       for (int e = 0; e < 2; ++e) b[e] = __builtin_bit_cast(bf16x8, bsm[bofs[e] + (c ^ bsw)]);
 #pragma unroll
       for (int r = 0; r < BMM_RM; ++r) {
-        const int32_t mlast = m0 + 32 * r + 31;
-        const bool inside = mlast < a.M && mlast - a.moff <= f.kk && f.kk + 16 <= kend;
-        if (!inside) {
-          const int32_t k8 = f.kk + 8 * hf;
-          f.a[r] = band_mask(f.a[r], lo_row[r] - k8, kend - k8, mok[r]);
+        if (fr) {
+          if (!tile_written(r, f.kk)) continue;
+        } else {
+          const int32_t mlast = m0 + 32 * r + 31;
+          const bool inside = mlast < a.M && mlast - a.moff <= f.kk && f.kk + 16 <= kend;
+          if (!inside) {
+            const int32_t k8 = f.kk + 8 * hf;
+            f.a[r] = band_mask(f.a[r], lo_row[r] - k8, kend - k8, mok[r]);
+          }
         }
 #pragma unroll
         for (int e = 0; e < 2; ++e)
@@ -675,6 +721,11 @@ __global__ __launch_bounds__(256, 2) void bmm64_kernel(BmmBatch bt) {
       use_group(g0 + G, fb);
     }
   }
+  };
+  if (frag)
+    run(IC<1>{});
+  else
+    run(IC<0>{});
   if (!wave_on) return;
   // lane holds column n = 32e + ii, rows m0 + 32r + 8g + 4hf + q (element 4g + q)
   float* C = a.C + axis_offset(a.c_batch, bi);
@@ -883,9 +934,10 @@ int launch_attn_bwd_q(const BwdArgs& a, void* stream) {
   return static_cast<int>(hipGetLastError());
 }
 
-int launch_bmm64(const BmmArgs* a, int n, void* stream) {
+int launch_bmm64(const BmmArgs* a, int n, int32_t frag_bits, void* stream) {
   if (n < 1 || n > 3) return static_cast<int>(hipErrorInvalidValue);
   BmmBatch bt{};
+  bt.frag_bits = frag_bits;
   int32_t gx = 1, gy = 1;
   for (int i = 0; i < n; ++i) {
     if (a[i].K % 16 != 0) return static_cast<int>(hipErrorInvalidValue);

@@ -215,8 +215,10 @@ struct BwdArgs {
   const void* dop;         // bf16 dLoss/dout [B][H][Lp][DP] (zero padded)
   const float* lse;        // [B*H*Lp] log2 softmax denominators (base-2 score units)
   const float* dsum;       // [B*H*Lp] D_i = dout_i . out_i
-  void* pt;                // bf16 P^T  [B][H][Np][Lp]
-  void* dst;               // bf16 dS^T [B][H][Np][Lp]
+  void* pt;                // bf16 P^T  [B][H], fragment tiles: keys 32jb.., queries 16kb..
+                           //   at ((jb * Lp/16 + kb) * 64 + lane) * 8, lane = key % 32 +
+                           //   32 ((query % 16) / 8), eight consecutive queries per lane
+  void* dst;               // bf16 dS^T [B][H], the same tiles
   void* dspt;              // bf16 dS'^T [H][dsp_rows][B*Lp]: row delta, column b*Lp + i holds
   int32_t dsp_rows;        //   dS[i][M+i-delta] (rows and columns outside the band unwritten)
   float* dq;               // fp32 [B][L][H][dh]
@@ -302,7 +304,9 @@ int launch_layernorm(const float* resid, const float* parts, int32_t n_parts, in
                      void* stream);
 int launch_cast_f32(const void* src, float* dst, int64_t n, int32_t dtype, void* stream);
 int launch_attn_bwd_q(const BwdArgs& a, void* stream);
-int launch_bmm64(const BmmArgs* a, int n, void* stream);   // n <= 3 products, one launch
+int launch_bmm64(const BmmArgs* a, int n, int32_t frag_bits,
+                 void* stream);   // n <= 3 products, one launch; bit z of frag_bits:
+                                  // product z reads A as the query kernel's fragment tiles
 int launch_bwd_prep(const BwdPrepArgs& a, void* stream);
 int launch_rk_transpose(const void* rk_ws, void* rkt, int32_t H, int32_t Pp, int32_t pad_ws,
                         int32_t ld, int32_t pad_t, void* stream);
