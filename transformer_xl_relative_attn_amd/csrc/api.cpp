@@ -683,7 +683,7 @@ txl_status_t run_rel_attn_ring(const AttnPlan& p, const AttnPtrs& a, void* ring,
 struct BwdPlan {
   AttnPlan p;
   Region kt, vn, o, lse, dop, dot, qut, qvt, dsum, pt, dst, dspt, duv, rkt, rt, drkt, drkp;
-  int32_t rkt_ld, rkt_pad, dsp_rows;
+  int32_t rkt_ld, rkt_pad, dsp_lo, dsp_tiles;
   size_t total;
 };
 
@@ -709,8 +709,15 @@ BwdPlan make_bwd_plan(const txl_attn_shape_t* s, bool compute_rk, bool want_wkr)
   take(bp.dsum, BH * p.Lp * 4);
   take(bp.pt, BH * p.Np * p.Lp * 2);
   take(bp.dst, BH * p.Np * p.Lp * 2);
-  bp.dsp_rows = p.Pp + 32;
-  take(bp.dspt, (size_t)p.H * bp.dsp_rows * p.B * p.Lp * 2);
+  // dS'^T tiles of 32 distances from the lowest half the query kernel
+  // flushes (its halves start at distances = M + 1 mod 32) to the highest
+  // (queries 32w.. of the last wave: M + 32w + 1 .. +31)
+  {
+    const int32_t mu = (p.M + 1) % 32;
+    bp.dsp_lo = mu <= 1 ? mu - 32 : mu - 64;
+    bp.dsp_tiles = (p.M + p.Lp + 1 - bp.dsp_lo) / 32;
+  }
+  take(bp.dspt, (size_t)p.H * bp.dsp_tiles * 32 * p.B * p.Lp * 2);
   take(bp.duv, 2 * BH * (p.Lp / 32) * p.DP * 4);
   take(bp.drkp, (size_t)p.B * p.P * p.H * p.dh * 4);
   // Rk^T columns: distance delta at rkt_pad + delta; rkt_pad = 31 - M (mod 8)
@@ -826,7 +833,8 @@ txl_status_t run_bwd_from_state(const BwdPlan& bp, const AttnPtrs& a, const void
   ba.pt = ws + bp.pt.off;
   ba.dst = ws + bp.dst.off;
   ba.dspt = ws + bp.dspt.off;
-  ba.dsp_rows = bp.dsp_rows;
+  ba.dsp_lo = bp.dsp_lo;
+  ba.dsp_tiles = bp.dsp_tiles;
   ba.dq = g.d_q;
   ba.duv_part = reinterpret_cast<float*>(ws + bp.duv.off);
   TXL_TRY(after_launch(timed(K_BWD_Q, stream, [&] { return launch_attn_bwd_q(ba, stream); }),
@@ -851,16 +859,19 @@ txl_status_t run_bwd_from_state(const BwdPlan& bp, const AttnPtrs& a, const void
   // the batch rows in order (one product per head would leave the chip idle)
   const int64_t BL = (int64_t)p.B * p.Lp;
   float* drk_part = reinterpret_cast<float*>(ws + bp.drkp.off);
-  const BmmArgs prods[3] = {
+  BmmArgs prods[3] = {
       bmm(ws + bp.dst.off, p.Lp, axis_linear((int64_t)p.Np * p.Lp), ws + bp.qut.off, p.Lp,
           axis_linear(DP * p.Lp), BHn, p.Lp, p.scale, g.d_k, per_bh_c),
       bmm(ws + bp.pt.off, p.Lp, axis_linear((int64_t)p.Np * p.Lp), ws + bp.dot.off, p.Lp,
           axis_linear(DP * p.Lp), BHn, p.Lp, 1.0f, g.d_val, per_bh_c),
-      bmm(ws + bp.dspt.off, BL, make_axis(p.B, (int64_t)bp.dsp_rows * BL, p.Lp), ws + bp.qvt.off,
+      bmm(ws + bp.dspt.off, BL, make_axis(p.B, (int64_t)bp.dsp_tiles * 32 * BL, 32 * (int64_t)p.Lp), ws + bp.qvt.off,
           BL, make_axis(p.B, DP * BL, p.Lp), BHn, p.Lp, p.scale, drk_part,
           make_axis(p.B, p.dh, (int64_t)p.P * HD))};
-  // products 0 and 1 read P^T, dS^T from the query kernel's fragment tiles
-  TXL_TRY(after_launch(timed(K_BWD_BMM, stream, [&] { return launch_bmm64(prods, 3, 0x3, stream); }),
+  // all three read A from the query kernel's fragment tiles; dS'^T rows are
+  // distances from dsp_lo
+  prods[2].M = bp.dsp_tiles * 32;
+  const int32_t kinds[3] = {1, 1, 2}, row_offs[3] = {0, 0, bp.dsp_lo};
+  TXL_TRY(after_launch(timed(K_BWD_BMM, stream, [&] { return launch_bmm64(prods, 3, kinds, row_offs, stream); }),
                        "dk, dval, dRk products", stream));
   TXL_TRY(after_launch(timed(K_BWD_AUX, stream, [&] {
                          return launch_sum_rows(drk_part, p.B, (int64_t)p.P * HD, g.d_Rk, stream);

@@ -266,18 +266,18 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_q_kernel(BwdArgs a) {
     h1[lane] = u32x4{0u, 0u, 0u, 0u};
     h1[lane + 64] = u32x4{0u, 0u, 0u, 0u};
   }
-  const int64_t dsp_col = (int64_t)b * Lp + i0;
-  const int64_t dsp_ld = (int64_t)a.B * Lp;
-  auto flush_half = [&](const uint16_t* hsrc, int32_t row0) {   // rows row0 + rr of dS'^T
+  // A complete half (distances row0 .. +31, row0 = dsp_lo mod 32) goes out as
+  // the two fragment tiles of its queries: lane l holds distance row l % 32,
+  // queries 16s + 8 (l / 32) .. +7, one contiguous kilobyte per tile.
+  const int64_t dsp_kt = (int64_t)a.B * Lp / 16;   // 16-query tiles per tile row
+  uint16_t* const dsp_h = static_cast<uint16_t*>(a.dspt) + (int64_t)head * a.dsp_tiles * 32 * a.B * Lp;
+  const int64_t dsp_k0 = ((int64_t)b * Lp + i0) / 16;
+  auto flush_half = [&](const uint16_t* hsrc, int32_t row0) {
+    const int64_t tb = (row0 - a.dsp_lo) / 32;
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int c = lane + 64 * q, rr = c >> 2, part = c & 3;
-      const u32x4 val = *reinterpret_cast<const u32x4*>(hsrc + rr * 32 + 8 * part);
-      const int32_t row = row0 + rr;
-      if (row >= 0 && row < a.dsp_rows)
-        *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.dspt) +
-                                  ((int64_t)head * a.dsp_rows + row) * dsp_ld + dsp_col +
-                                  8 * part) = val;
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const u32x4 val = *reinterpret_cast<const u32x4*>(hsrc + (lane & 31) * 32 + 16 * s2 + 8 * (lane >> 5));
+      *reinterpret_cast<u32x4*>(dsp_h + ((tb * dsp_kt + dsp_k0 + s2) * 64 + lane) * 8) = val;
     }
   };
 
@@ -587,7 +587,8 @@ __device__ __forceinline__ bf16x8 band_mask(bf16x8 f, int32_t lo, int32_t hi, bo
 // chip instead of each product's last partial round running alone.
 struct BmmBatch {
   BmmArgs p[3];
-  int32_t frag_bits;   // bit z: product z reads A from the query kernel's fragment tiles
+  int32_t kind[3];      // layout of A (see launch_bmm64)
+  int32_t row_off[3];   // output row of A row m: m + row_off
 };
 
 __global__ __launch_bounds__(256, 2) void bmm64_kernel(BmmBatch bt) {
@@ -620,28 +621,37 @@ __global__ __launch_bounds__(256, 2) void bmm64_kernel(BmmBatch bt) {
   floatx16 acc[BMM_RM][2];
 #pragma unroll
   for (int r = 0; r < BMM_RM; ++r) acc[r][0] = acc[r][1] = floatx16{0};
-  // Fragment tiles (a_frag): the lane's 16 bytes of k-step 0 in each of its
-  // row tiles (clamped into the rows that hold data; rows past M are not
-  // stored).  A tile (jb, k-step) was written by the query kernel's wave of
-  // queries 32w .. +31 (w = k-step / 2) iff that wave visited key block jb,
-  // i.e. jb < t_end(w); other tiles hold no data and are skipped.
-  const bool frag = (bt.frag_bits >> z) & 1;
-  if (frag) {
+  // Fragment tiles (kind 1, 2): the lane's 16 bytes of k-step 0 in each of
+  // its row tiles (clamped into the rows that hold data; rows past M are not
+  // stored).  Tiles no wave of the query kernel wrote hold no data and are
+  // skipped; a tile (row tile, k-step) belongs to the wave of queries 32w ..
+  // +31, w = k-step / 2.  Key-row tiles (kind 1, P^T and dS^T): written iff
+  // that wave visited the key block, i.e. row tile < t_end(w).
+  //   Distance-row tiles (kind 2, dS'^T): that wave flushed the halves of
+  // distances M + 32w + 1 - 32u, u = 0 .. t_end(w), i.e. tile rows
+  // top(w) - t_end(w) .. top(w) counted from row_off.
+  const int kind = z == 0 ? bt.kind[0] : z == 1 ? bt.kind[1] : bt.kind[2];
+  const int32_t row_off = z == 0 ? bt.row_off[0] : z == 1 ? bt.row_off[1] : bt.row_off[2];
+  const bool frag = kind != 0;
+  if (frag) {   // lda: the tile row's length in elements (16 per tile)
 #pragma unroll
     for (int r = 0; r < BMM_RM; ++r) {
       const int32_t jb = min(m0 / 32 + r, (a.M + 31) / 32 - 1);
-      arow[r] = A + ((int64_t)jb * (a.K / 16) * 64 + lane) * 8;
+      arow[r] = A + ((int64_t)jb * (a.lda / 16) * 64 + lane) * 8;
     }
   }
   auto tile_written = [&](int r, int32_t kk) {
     const int32_t w = kk >> 5;   // query tile of 32
     const int32_t t_end = (a.moff + min(32 * w + 31, a.klim - 1) + 32) / 32;
-    return m0 / 32 + r < t_end;
+    const int32_t tr = m0 / 32 + r;
+    if (kind == 1) return tr < t_end;
+    const int32_t top = (a.moff + 32 * w + 1 - row_off) / 32;
+    return tr <= top && tr >= top - t_end;
   };
   // rows need k >= m - moff and none at or past kend
   const int32_t kend = min(a.K, a.klim);
-  const int32_t kfirst_wg = max(0, mwg - a.moff) & ~(BMM_KC - 1);
-  const int32_t kfirst = max(0, m0 - a.moff) & ~15;
+  const int32_t kfirst_wg = kind == 2 ? 0 : max(0, mwg - a.moff) & ~(BMM_KC - 1);
+  const int32_t kfirst = kind == 2 ? 0 : max(0, m0 - a.moff) & ~15;
   int bofs[2];   // this lane's B row base (16-byte units) and swizzle
 #pragma unroll
   for (int e = 0; e < 2; ++e) bofs[e] = (32 * e + ii) * (BMM_KC / 8);
@@ -738,8 +748,8 @@ __global__ __launch_bounds__(256, 2) void bmm64_kernel(BmmBatch bt) {
       if (n >= a.n_valid) continue;
 #pragma unroll
       for (int x = 0; x < 16; ++x) {
-        const int32_t row = m0 + 32 * r + 8 * (x >> 2) + 4 * hf + (x & 3);
-        if (row >= a.m_valid) continue;
+        const int32_t row = m0 + 32 * r + 8 * (x >> 2) + 4 * hf + (x & 3) + row_off;
+        if (row < 0 || row >= a.m_valid) continue;
         const float val = a.alpha * acc[r][e][x];
         C[(int64_t)row * a.ldc + n] = val;
         if (C2) C2[(int64_t)row * a.c2_m + (int64_t)n * a.c2_n] = val;
@@ -934,10 +944,14 @@ int launch_attn_bwd_q(const BwdArgs& a, void* stream) {
   return static_cast<int>(hipGetLastError());
 }
 
-int launch_bmm64(const BmmArgs* a, int n, int32_t frag_bits, void* stream) {
+int launch_bmm64(const BmmArgs* a, int n, const int32_t* kind, const int32_t* row_off,
+                 void* stream) {
   if (n < 1 || n > 3) return static_cast<int>(hipErrorInvalidValue);
   BmmBatch bt{};
-  bt.frag_bits = frag_bits;
+  for (int i = 0; i < n; ++i) {
+    bt.kind[i] = kind[i];
+    bt.row_off[i] = row_off[i];
+  }
   int32_t gx = 1, gy = 1;
   for (int i = 0; i < n; ++i) {
     if (a[i].K % 16 != 0) return static_cast<int>(hipErrorInvalidValue);

@@ -219,8 +219,10 @@ struct BwdArgs {
                            //   at ((jb * Lp/16 + kb) * 64 + lane) * 8, lane = key % 32 +
                            //   32 ((query % 16) / 8), eight consecutive queries per lane
   void* dst;               // bf16 dS^T [B][H], the same tiles
-  void* dspt;              // bf16 dS'^T [H][dsp_rows][B*Lp]: row delta, column b*Lp + i holds
-  int32_t dsp_rows;        //   dS[i][M+i-delta] (rows and columns outside the band unwritten)
+  void* dspt;              // bf16 dS'^T per head: row delta, column b*Lp + i holds dS[i][M+i-delta],
+                           //   in fragment tiles of 32 rows from delta dsp_lo and 16 columns
+                           //   ([dsp_tiles][B*Lp/16] tiles per head, tiles no wave flushed unwritten)
+  int32_t dsp_lo, dsp_tiles;
   float* dq;               // fp32 [B][L][H][dh]
   float* duv_part;         // fp32 [2][B][H][Lp/32][DP]: per 32 queries, the sums of the
                            //   k-part and the Rk-part of dq (-> du, dv)
@@ -304,9 +306,11 @@ int launch_layernorm(const float* resid, const float* parts, int32_t n_parts, in
                      void* stream);
 int launch_cast_f32(const void* src, float* dst, int64_t n, int32_t dtype, void* stream);
 int launch_attn_bwd_q(const BwdArgs& a, void* stream);
-int launch_bmm64(const BmmArgs* a, int n, int32_t frag_bits,
-                 void* stream);   // n <= 3 products, one launch; bit z of frag_bits:
-                                  // product z reads A as the query kernel's fragment tiles
+// n <= 3 products in one launch.  kind[z]: 0 = A in rows; 1 = A in the query
+// kernel's key-row fragment tiles (P^T, dS^T); 2 = A in its distance-row
+// fragment tiles (dS'^T).  Output row of A row m: m + row_off[z].
+int launch_bmm64(const BmmArgs* a, int n, const int32_t* kind, const int32_t* row_off,
+                 void* stream);
 int launch_bwd_prep(const BwdPrepArgs& a, void* stream);
 int launch_rk_transpose(const void* rk_ws, void* rkt, int32_t H, int32_t Pp, int32_t pad_ws,
                         int32_t ld, int32_t pad_t, void* stream);
