@@ -682,7 +682,7 @@ txl_status_t run_rel_attn_ring(const AttnPlan& p, const AttnPtrs& a, void* ring,
 // P^T, dS^T, dS'^T of the key-side products.
 struct BwdPlan {
   AttnPlan p;
-  Region kt, vn, o, lse, dop, dot, qut, qvt, dsum, pt, dst, dspt, duv, rkt, rt, drkt, drkp;
+  Region o, lse, dop, dot, qut, qvt, dsum, pt, dst, dspt, duv, rkt, rt, drkt, drkp;
   int32_t rkt_ld, rkt_pad, dsp_lo, dsp_tiles;
   size_t total;
 };
@@ -698,8 +698,6 @@ BwdPlan make_bwd_plan(const txl_attn_shape_t* s, bool compute_rk, bool want_wkr)
     off = align256(off + bytes);
   };
   const size_t BH = (size_t)p.B * p.H;
-  take(bp.kt, BH * p.Np * p.DP * 2);
-  take(bp.vn, BH * p.Np * p.DP * 2);
   take(bp.o, (size_t)p.B * p.L * p.H * p.dh * 2);
   take(bp.lse, BH * p.Lp * 4);
   take(bp.dop, BH * p.Lp * p.DP * 2);
@@ -740,9 +738,9 @@ struct BwdOut {
   float *d_q, *d_k, *d_val, *d_u, *d_v, *d_Rk, *d_W_kR;
 };
 
-// Forward of the backward's plan: the projections (q, K, V^T, Rk plus K^T tiles
-// and val rows) and the attention with each row's log-sum-exp, all left in the
-// workspace, the output written to `out`.
+// Forward of the backward's plan: the projections (q, K, V^T, Rk) and the
+// attention with each row's log-sum-exp, all left in the workspace, the output
+// written to `out`.
 txl_status_t run_bwd_forward(const BwdPlan& bp, const AttnPtrs& a, void* out, char* ws,
                              void* stream) {
   const AttnPlan& p = bp.p;
@@ -752,11 +750,13 @@ txl_status_t run_bwd_forward(const BwdPlan& bp, const AttnPtrs& a, void* out, ch
   char* v = ws + p.v.off;
   Operands o;
   TXL_TRY(pack_operands(p, a, ws, stream, o));
-  // projections: the forward's q, K, V^T, Rk, plus K^T tiles and V rows
+  // projections: the forward's q, K, V^T, Rk (the backward reads K^T and the
+  // val rows out of the K and V^T tiles)
   const int tile = gemm_tile(dt);
   GemmGroup gg{};
   add_q_problem(gg, p, o, ws);
   const RowSrc ht = src_htilde(o.mem, o.h, o.ld_d, p.Np, p.M, p.L, a.mem_start);
+  const int k_idx = gg.count;
   add_problem(gg, p.B * p.Np, p.H * p.DP, p.Kd, ht, src_headpad(o.WkE, o.ld_d, p.dh, p.DP),
               out_map(k, dt, p.B * p.Np, p.H * p.DP, axis(p.Np, (int64_t)p.H * p.Np * DP, DP),
                       axis(p.DP, (int64_t)p.Np * DP, 1)),
@@ -765,14 +765,7 @@ txl_status_t run_bwd_forward(const BwdPlan& bp, const AttnPtrs& a, void* out, ch
               out_map(v, dt, p.H * p.DP, p.B * p.Np, axis_linear(32),
                       axis(32, (int64_t)p.H * DP * 32, 1)),
               tile);
-  add_problem(gg, p.H * p.DP, p.B * p.Np, p.Kd, src_headpad(o.WkE, o.ld_d, p.dh, p.DP), ht,
-              out_map(ws + bp.kt.off, dt, p.H * p.DP, p.B * p.Np, axis_linear(32),
-                      axis(32, (int64_t)p.H * DP * 32, 1)),
-              tile);
-  add_problem(gg, p.B * p.Np, p.H * p.DP, p.Kd, ht, src_headpad(o.Wv, o.ld_d, p.dh, p.DP),
-              out_map(ws + bp.vn.off, dt, p.B * p.Np, p.H * p.DP,
-                      axis(p.Np, (int64_t)p.H * p.Np * DP, DP), axis(p.DP, (int64_t)p.Np * DP, 1)),
-              tile);
+  gg.pair1 = k_idx + 1;   // K and V^T read the same rows of h~
   TXL_TRY(add_rk(gg, p, a, o, ws, stream));
   TXL_TRY(after_launch(timed(K_PROJ_GEMM, stream, [&] { return launch_gemm(gg, dt, stream); }),
                        "backward projection GEMMs", stream));
@@ -819,8 +812,7 @@ txl_status_t run_bwd_from_state(const BwdPlan& bp, const AttnPtrs& a, const void
   ba.scale = p.scale;
   ba.q = pa.q;
   ba.k = k;
-  ba.kt = ws + bp.kt.off;
-  ba.vn = ws + bp.vn.off;
+  ba.vt = ws + p.v.off;
   ba.rk = ws + p.rk.off;
   ba.rkt = ws + bp.rkt.off;
   ba.rkt_ld = bp.rkt_ld;

@@ -46,7 +46,7 @@ constexpr int TPW = 36;    // bf16 per query row of the P / dS transpose tiles (
 constexpr float kNegInf = -__builtin_inff();
 
 struct BwdSmem {
-  u32x4 kv[NST][3 * TU];            // per stage: K tile, val tile (32 keys x 128 B), K^T tile (64 d x 64 B)
+  u32x4 kv[NST][2 * TU];            // per stage: K tile (32 keys x 128 B), V^T tile (64 d x 64 B)
   u32x4 rk[RKS][TU];                // Rk chunk: 32 rows x 128 B
   u32x4 rkt[RKS][TU];               // Rk^T chunk: 64 d x 32 distances (64 B)
   float win[4][32 * WP];            // per wave: shifted (b)+(d) window of the scores
@@ -121,13 +121,14 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_q_kernel(BwdArgs a) {
   const int32_t t_end = wave_on ? (M + min(i0 + 31, L - 1) + 1 + KB - 1) / KB : 0;
   const int32_t nkb = Np / KB;
 
-  // ---- LDS-DMA.  Block t brings K tile t, val tile t (rows 32t.., 128 B
-  // each), the K^T tile t ([64 d][32 keys]) into stage t % NST, and Rk chunk t
+  // ---- LDS-DMA.  Block t brings K tile t (rows 32t.., 128 B each) and the
+  // forward's V^T tile t ([64 d][32 keys]) into stage t % NST, and Rk chunk t
   // (rows base0 - 32t + r of the head's table) and the Rk^T chunk of the same
-  // distances ([64 d][32 distances]) into slot (t + 8) & 7.  Wave w uses Rk
-  // chunk t-w for block t's scores and Rk^T chunks t-w, t-w-1 for its dq; each
-  // chunk is loaded once per workgroup.  Every wave loads a quarter of each of
-  // the five tiles per block; past the last block the loads repeat it.
+  // distances ([64 d][32 distances]) into slot (t + 8) & 7.  The K^T and val
+  // operands come out of the K and V^T tiles through transposing reads.  Wave
+  // w uses Rk chunk t-w for block t's scores and Rk^T chunk t-w-2 for its dq;
+  // each chunk is loaded once per workgroup.  Every wave loads a quarter of
+  // each of the four tiles per block; past the last block the loads repeat it.
   const int32_t base0 = M + i_base - (KB - 1);   // distance of chunk 0's first row
   const int32_t rk_rows = a.Pp + 2 * kRkPad;
   const int32_t ktstep = a.H * DP * KB * 2;
@@ -137,15 +138,14 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_q_kernel(BwdArgs a) {
   auto rkt_col0 = [&](int32_t c) { return min(max(a.rkt_pad + base0 - KB * c, 0), a.rkt_ld - KB); };
   // per-lane sources: 128-byte rows r = 8w + lane/8, 64-byte rows d = 16w +
   // lane/4; a lane fetches the global chunk that lands in its swizzled slot
-  const char *pk, *pv, *pkt, *prk, *prkt;
+  const char *pk, *pvt, *prk, *prkt;
   {
     const int r = wave * 8 + (lane >> 3);
     const int64_t lo128 = r * 128 + (((lane & 7) ^ ((r >> 1) & 7)) << 4);
     const int d = wave * 16 + (lane >> 2);
     const int gc = (lane & 3) ^ ((d >> 2) & 3);
     pk = static_cast<const char*>(a.k) + (int64_t)bh * Np * DP * 2 + lo128;
-    pv = static_cast<const char*>(a.vn) + (int64_t)bh * Np * DP * 2 + lo128;
-    pkt = static_cast<const char*>(a.kt) + ((int64_t)b * nkb * a.H + head) * DP * KB * 2 + d * 64 +
+    pvt = static_cast<const char*>(a.vt) + ((int64_t)b * nkb * a.H + head) * DP * KB * 2 + d * 64 +
           gc * 16;
     prk = static_cast<const char*>(a.rk) + (int64_t)head * rk_rows * DP * 2 + lo128;
     prkt = static_cast<const char*>(a.rkt) + ((int64_t)head * DP + d) * a.rkt_ld * 2 + gc * 16;
@@ -154,8 +154,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_q_kernel(BwdArgs a) {
     const int32_t tt = min(tb, nb - 1);
     u32x4* kvs = sm.kv[st] + wave * 64;
     dma16(pk, kvs, (int64_t)tt * (KB * DP * 2));
-    dma16(pv, kvs + TU, (int64_t)tt * (KB * DP * 2));
-    dma16(pkt, kvs + 2 * TU, (int64_t)tt * ktstep);
+    dma16(pvt, kvs + TU, (int64_t)tt * ktstep);
     const int sl = rk_slot(tb);
     dma16(prk, sm.rk[sl] + wave * 64, (int64_t)rk_row0(tt) * (DP * 2));
     dma16(prkt, sm.rkt[sl] + wave * 64, (int64_t)rkt_col0(tt) * 2);
@@ -309,6 +308,48 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_q_kernel(BwdArgs a) {
 #pragma unroll
       for (int e = 0; e < 2; ++e) af[t2][e] = __builtin_bit_cast(bf16x8, rt[ofs64[t2][e]]);
   };
+  // val and K^T operands through the same transposing reads (lane a + 4q of
+  // each 16-lane group: q = (lane >> 2) & 3, a = lane & 3):
+  //   val fragment s (A of dP^T: row = key lane % 32, d = 16s + 8 (lane / 32)
+  //   .. +7) from the V^T tile [64 d][32 keys], 64-byte rows with chunk c of
+  //   row d at c ^ ((d >> 2) & 3): lane points at d row 16s + 8 (lane / 32) +
+  //   4rd + q, keys 16 ((lane / 16) % 2) + 4a .. +3;
+  //   K^T fragment (t2, e) (A of dq's k-part: row = d 32e + lane % 32, keys
+  //   16t2 + 8 (lane / 32) .. +7) from the K tile [32 keys][64 d], 128-byte
+  //   rows with chunk c of row r at c ^ ((r >> 1) & 7): lane points at key
+  //   row 16t2 + 8 (lane / 32) + 4rd + q, d 32e + 16 ((lane / 16) % 2) + 4a .. +3.
+  // The swizzle terms do not depend on s or t2, so each lane keeps one byte
+  // offset per (rd) and (e, rd); s and t2 add 1 KB and 2 KB.
+  int vt_off[2], kt_off[2][2];
+  {
+    const int q4 = (lane >> 2) & 3, a4 = lane & 3, g2 = (lane >> 4) & 1, kh = lane >> 5;
+#pragma unroll
+    for (int rd = 0; rd < 2; ++rd) {
+      const int dr = 8 * kh + 4 * rd + q4;
+      vt_off[rd] = dr * 64 + (((2 * g2 + (a4 >> 1)) ^ ((2 * kh + rd) & 3)) << 4) + 8 * (a4 & 1);
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+        kt_off[e][rd] = dr * 128 + (((4 * e + 2 * g2 + (a4 >> 1)) ^ ((4 * kh + 2 * rd + (q4 >> 1)) & 7)) << 4) +
+                        8 * (a4 & 1);
+    }
+  }
+  auto tr8 = [&](const char* p0, const char* p1) {
+    const short4_t r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)p0);
+    const short4_t r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)p1);
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  auto val_frags = [&](const u32x4* vtile, bf16x8 (&f)[4]) {
+    const char* base = reinterpret_cast<const char*>(vtile);
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) f[s4] = tr8(base + vt_off[0] + 1024 * s4, base + vt_off[1] + 1024 * s4);
+  };
+  auto kt_frags = [&](const u32x4* ktile, bf16x8 (&f)[2][2]) {   // [t2][e]
+    const char* base = reinterpret_cast<const char*>(ktile);
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) f[t2][e] = tr8(base + kt_off[e][0] + 2048 * t2, base + kt_off[e][1] + 2048 * t2);
+  };
   auto half_dqr = [&](const bf16x8 (&af)[2][2], const bf16x8 (&bq)[2]) {
 #pragma unroll
     for (int t2 = 0; t2 < 2; ++t2)
@@ -348,7 +389,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_q_kernel(BwdArgs a) {
     read_rows(sm.rk[rk_slot(-wave - 1)], rf);
     C0 = bd_chunk(rf);
     read_rows(sm.rk[rk_slot(-wave)], rf);
-    read_rows(sm.kv[0] + TU, vf);
+    val_frags(sm.kv[0] + TU, vf);
     read_rows(sm.kv[0], kf);
     C1 = bd_chunk(rf);
 #pragma unroll
@@ -379,21 +420,19 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_q_kernel(BwdArgs a) {
     // operands: K^T tile t and the Rk^T chunk t-w-2 of the half completed by
     // block t-1 for dq; Rk chunk t+1-w, val and K tiles t+1 for the next
     // block (read whether or not it exists: every slot holds valid data)
+    // (the Rk chunk first and its product issued at once: with the other
+    // reads ahead of it the compiler fetched it one fragment at a time)
     bf16x8 ktf[2][2], rtf[2][2], rf[4], vf[4], kf[4];
-    {
-      const u32x4* kts = sm.kv[t % NST] + 2 * TU;
-      const u32x4* kvn = sm.kv[(t + 1) % NST];
-      read_rows(sm.rk[rk_slot(t + 1 - wave)], rf);
-      read_rows(kvn + TU, vf);
-#pragma unroll
-      for (int e = 0; e < 2; ++e)
-#pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2) ktf[t2][e] = __builtin_bit_cast(bf16x8, kts[ofs64[t2][e]]);
-      chunk_frags(t - wave - 2, rtf);
-      read_rows(kvn, kf);
-    }
+    const u32x4* kvn = sm.kv[(t + 1) % NST];
+    read_rows(sm.rk[rk_slot(t + 1 - wave)], rf);
+    __builtin_amdgcn_sched_barrier(0);
+    if (more) low_out = bd_chunk(rf);
+    __builtin_amdgcn_sched_barrier(0);
+    val_frags(kvn + TU, vf);
+    kt_frags(sm.kv[t % NST], ktf);
+    chunk_frags(t - wave - 2, rtf);
+    read_rows(kvn, kf);
     if (more) {
-      low_out = bd_chunk(rf);
       dpn = floatx16{0};
 #pragma unroll
       for (int s = 0; s < 4; ++s) dpn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[s], go[s], dpn, 0, 0, 0);

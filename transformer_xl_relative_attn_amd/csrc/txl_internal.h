@@ -205,8 +205,7 @@ struct BwdArgs {
   float scale;
   const float* q;          // fp32 [B][H][Lp][DP]
   const void* k;           // bf16 K [B][H][Np][DP]
-  const void* kt;          // bf16 K^T in 32-key tiles [B][Np/32][H][DP][32]
-  const void* vn;          // bf16 val [B][H][Np][DP]
+  const void* vt;          // bf16 val^T in 32-key tiles [B][Np/32][H][DP][32] (the forward's V^T)
   const void* rk;          // bf16 [H][kRkPad + Pp + kRkPad][DP]
   const void* rkt;         // bf16 Rk^T [H][DP][rkt_ld], distance delta at column rkt_pad + delta
   int32_t rkt_ld, rkt_pad;
