@@ -38,7 +38,7 @@ using IC = std::integral_constant<int, X>;
 
 constexpr int DP = 64;
 constexpr int KB = 32;
-constexpr int WP = 36;     // floats per query row of the score window
+constexpr int WP = 68;     // floats per query row of the score window (64 + pad)
 constexpr int NST = 3;     // K / val / K^T ring stages (blocks t .. t+2)
 constexpr int RKS = 8;     // Rk and Rk^T chunk slots: chunk c in slot (c + 8) & 7
 constexpr int TU = 256;    // 16-byte units of a 4 KB tile
@@ -49,7 +49,7 @@ struct BwdSmem {
   u32x4 kv[NST][2 * TU];            // per stage: K tile (32 keys x 128 B), V^T tile (64 d x 64 B)
   u32x4 rk[RKS][TU];                // Rk chunk: 32 rows x 128 B
   u32x4 rkt[RKS][TU];               // Rk^T chunk: 64 d x 32 distances (64 B)
-  float win[4][32 * WP];            // per wave: shifted (b)+(d) window of the scores
+  float win[4][33 * WP];            // per wave: shifted (b)+(d) window of the scores (+ a spill row)
   uint16_t half[4][2][32 * 32];     // per wave: two 32-row halves of dS'^T [row][query]
   uint16_t tp[4][2][32 * TPW];      // per wave: P and dS of a block, [query][key]
 };
@@ -222,36 +222,28 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_q_kernel(BwdArgs a) {
     for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rf[s], qv[s], acc, 0, 0, 0);
     return acc;
   };
-  // score window: value for (query ii, key jj) is window row 31 + ii - jj of
-  // [lower chunk ; upper chunk], stored at position jj of row ii
-  float* win = sm.win[wave] + ii * WP;
-  // bit e of sel_bits: element e comes from the lower chunk (w >= ii).  The
-  // per-element choice is a bit select on a mask extracted from it inside
-  // the loop: sixteen lane masks kept live across the loop would not fit in
-  // the scalar registers.
-  uint32_t sel_bits = 0;
-#pragma unroll
-  for (int e = 0; e < 16; ++e)
-    if (8 * (e >> 2) + 4 * hf + (e & 3) >= ii) sel_bits |= 1u << e;
+  // Score window: the value for (query ii, key jj) is row R = 31 + ii - jj of
+  // [lower chunk ; upper chunk].  Each query has a 64-wide row read at
+  // positions 32 .. 63 (key jj at 32 + jj); the lane writes its lower chunk
+  // row w at 63 + ii - w and its upper chunk row w at 31 + ii - w, every one
+  // of them, with no choice: the rows the key range needs (lower w >= ii,
+  // upper w < ii) land in 32 .. 63, the others in this row's 0 .. 31 or, past
+  // 63, in the next row's 0 .. 31, which no one reads (one spare row per
+  // wave).  Row pitch 68: the 16-byte reads of 16 queries hit distinct banks.
+  float* win = sm.win[wave] + ii * WP + ii + 31 - 4 * hf - 27;
   auto write_win = [&](const floatx16& lower, const floatx16& upper) {
-    uint32_t sb = sel_bits;
-    asm volatile("" : "+v"(sb));
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const int w = 8 * (e >> 2) + 4 * hf + (e & 3);
-      const uint32_t m = (uint32_t)((int32_t)(sb << (31 - e)) >> 31);
-      // (elements copied out first: a bit cast of a vector element itself
-      // reads element 0)
-      const float le = lower[e], ue = upper[e];
-      const uint32_t x = (__builtin_bit_cast(uint32_t, le) & m) | (__builtin_bit_cast(uint32_t, ue) & ~m);
-      win[(31 + ii - w) & 31] = __builtin_bit_cast(float, x);
+      const int w = 8 * (e >> 2) + (e & 3);   // chunk row less 4hf
+      win[59 - w] = lower[e];
+      win[27 - w] = upper[e];
     }
   };
   auto read_win = [&]() {
     floatx16 c;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const floatx4 x = *reinterpret_cast<const floatx4*>(win + 8 * g + 4 * hf);
+      const floatx4 x = *reinterpret_cast<const floatx4*>(sm.win[wave] + ii * WP + 32 + 8 * g + 4 * hf);
 #pragma unroll
       for (int r = 0; r < 4; ++r) c[4 * g + r] = x[r];
     }
