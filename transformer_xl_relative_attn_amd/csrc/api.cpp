@@ -797,13 +797,27 @@ txl_status_t run_bwd_from_state(const BwdPlan& bp, const AttnPtrs& a, const void
   pa.qut = ws + bp.qut.off;
   pa.qvt = ws + bp.qvt.off;
   pa.dsum = reinterpret_cast<float*>(ws + bp.dsum.off);
-  TXL_TRY(after_launch(timed(K_BWD_AUX, stream, [&] { return launch_bwd_prep(pa, stream); }),
-                       "backward prep", stream));
-  TXL_TRY(after_launch(timed(K_BWD_AUX, stream, [&] {
-                         return launch_rk_transpose(ws + p.rk.off, ws + bp.rkt.off, p.H, p.Pp,
-                                                    p.rk_pad, bp.rkt_ld, bp.rkt_pad, stream);
-                       }),
-                       "Rk transpose", stream));
+  // one launch: the prep, the Rk^T table and (for dW_kR) R^T in bf16 with the
+  // distances padded to a multiple of 64
+  const int32_t Pk = (int32_t)round_up(p.P, 64);
+  BwdPreArgs pre{};
+  pre.prep = pa;
+  pre.rk_ws = ws + p.rk.off;
+  pre.rkt = ws + bp.rkt.off;
+  pre.Pp = p.Pp;
+  pre.pad_ws = p.rk_pad;
+  pre.rkt_ld = bp.rkt_ld;
+  pre.pad_t = bp.rkt_pad;
+  if (g.d_W_kR) {
+    pre.r = a.R;
+    pre.rt = ws + bp.rt.off;
+    pre.P = p.P;
+    pre.d_pos = p.dpos;
+    pre.r_dtype = dt;
+    pre.r_ld = Pk;
+  }
+  TXL_TRY(after_launch(timed(K_BWD_AUX, stream, [&] { return launch_bwd_pre(pre, stream); }),
+                       "backward prep, Rk^T and R^T", stream));
 
   BwdArgs ba{};
   ba.B = p.B; ba.H = p.H; ba.L = p.L; ba.M = p.M; ba.dh = p.dh;
@@ -865,30 +879,30 @@ txl_status_t run_bwd_from_state(const BwdPlan& bp, const AttnPtrs& a, const void
   const int32_t kinds[3] = {1, 1, 2}, row_offs[3] = {0, 0, bp.dsp_lo};
   TXL_TRY(after_launch(timed(K_BWD_BMM, stream, [&] { return launch_bmm64(prods, 3, kinds, row_offs, stream); }),
                        "dk, dval, dRk products", stream));
-  TXL_TRY(after_launch(timed(K_BWD_AUX, stream, [&] {
-                         return launch_sum_rows(drk_part, p.B, (int64_t)p.P * HD, g.d_Rk, stream);
-                       }),
-                       "dRk batch sum", stream));
-  TXL_TRY(after_launch(timed(K_BWD_AUX, stream, [&] {
-                         return launch_duv_reduce(ba.duv_part, p.B, p.H, p.Lp / 32, p.dh, g.d_u,
-                                                  g.d_v, stream);
-                       }),
-                       "du, dv reduction", stream));
+  // one launch: dRk (the batch rows' partials summed in order) with its bf16
+  // transpose for dW_kR, and du, dv
+  BwdPostArgs post{};
+  post.drk_part = drk_part;
+  post.d_rk = g.d_Rk;
+  post.drkt = g.d_W_kR ? ws + bp.drkt.off : nullptr;
+  post.B = p.B;
+  post.P = p.P;
+  post.HD = (int32_t)HD;
+  post.r_ld = Pk;
+  post.duv_part = ba.duv_part;
+  post.d_u = g.d_u;
+  post.d_v = g.d_v;
+  post.H = p.H;
+  post.nchunk = p.Lp / 32;
+  post.dh = p.dh;
+  TXL_TRY(after_launch(timed(K_BWD_AUX, stream, [&] { return launch_bwd_post(post, stream); }),
+                       "dRk batch sum, du, dv", stream));
   if (g.d_W_kR) {
     // dW_kR = sum_delta dRk[delta] (x) R_delta on the matrix cores: rows
-    // h*dh + c, K = distances (bf16 transposes padded with zero distances)
-    const int32_t Pk = (int32_t)round_up(p.P, 64);
+    // h*dh + c, K = distances (the bf16 transposes, padded with zero
+    // distances, written by the pre and post launches)
     char* rt = ws + bp.rt.off;
     char* drkt = ws + bp.drkt.off;
-    TXL_TRY(after_launch(timed(K_BWD_AUX, stream, [&] {
-                           return launch_transpose_bf16(a.R, p.P, p.dpos, dt, Pk, rt, stream);
-                         }),
-                         "R transpose", stream));
-    TXL_TRY(after_launch(timed(K_BWD_AUX, stream, [&] {
-                           return launch_transpose_bf16(g.d_Rk, p.P, (int32_t)HD, TXL_F32, Pk, drkt,
-                                                        stream);
-                         }),
-                         "dRk transpose", stream));
     // Split K (the distances) S ways into fp32 partials, summed in order by
     // a second launch: the product alone has too few 128x128 tiles to fill
     // the chip (d_model 512: 16).  The partials reuse the dRk partial buffer,

@@ -793,13 +793,13 @@ __global__ __launch_bounds__(256, 2) void bmm64_kernel(BmmBatch bt) {
 // [bh][i][64] and, through an LDS tile, transposed [bh][64][i]; (q+u)^T
 // [bh][64][i] and (q+v)^T [h][64][b*Lp + i].  Rows i >= L and columns d >= dh
 // are zeros.
-__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdPrepArgs a) {
+__device__ __forceinline__ void bwd_prep_block(const BwdPrepArgs& a, int32_t blk) {
   __shared__ __align__(16) uint16_t tg[64][72];   // [i][d], 144-byte rows
   __shared__ __align__(16) uint16_t tu[64][72];
   __shared__ __align__(16) uint16_t tv[64][72];
   __shared__ float red[64][4];
   const int32_t nch = a.Lp / 64 + (a.Lp % 64 ? 1 : 0);
-  const int32_t bh = blockIdx.x / nch, i_base = (blockIdx.x % nch) * 64;
+  const int32_t bh = blk / nch, i_base = (blk % nch) * 64;
   const int32_t b = bh / a.H, head = bh % a.H;
   const int tid = threadIdx.x;
   {
@@ -903,48 +903,104 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdPrepArgs a) {
   }
 }
 
-// Rk^T [h][d][c] = Rk[h][pad_ws + c - pad_t][d] for 0 <= c - pad_t < Pp, else 0.
-__global__ void rk_transpose_kernel(const uint16_t* rk, uint16_t* rkt, int32_t H, int32_t Pp,
-                                    int32_t pad_ws, int32_t ld, int32_t pad_t) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (int64_t)H * DP * ld) return;
-  const int32_t c = idx % ld;
-  const int64_t hd = idx / ld;
-  const int32_t d = hd % DP, h = hd / DP;
-  const int32_t delta = c - pad_t;
-  rkt[idx] = (delta >= 0 && delta < Pp)
-                 ? rk[(((int64_t)h * (Pp + 2 * pad_ws)) + pad_ws + delta) * DP + d]
-                 : uint16_t(0);
+// Rk^T [h][d][c] = Rk[h][pad_ws + c - pad_t][d] for 0 <= c - pad_t < Pp, else 0
+// (ld a multiple of 8).  One workgroup per (64 columns c, head): the 64 Rk
+// rows (128 bytes each) are read whole into an LDS tile, and each output row
+// segment is written as 16-byte chunks.
+__device__ __forceinline__ void rk_transpose_block(const uint16_t* rk, uint16_t* rkt, int32_t Pp,
+                                                   int32_t pad_ws, int32_t ld, int32_t pad_t,
+                                                   int32_t bx, int32_t h) {
+  __shared__ uint16_t tile[64][DP + 2];   // [c][d]
+  const int32_t c0 = bx * 64;
+  const int tid = threadIdx.x;
+  const uint16_t* src = rk + ((int64_t)h * (Pp + 2 * pad_ws) + pad_ws) * DP;
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    const int cl = 32 * pass + (tid >> 3), d0 = 8 * (tid & 7);
+    const int32_t delta = c0 + cl - pad_t;
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (delta >= 0 && delta < Pp) x = *reinterpret_cast<const u32x4*>(src + (int64_t)delta * DP + d0);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      tile[cl][d0 + 2 * w] = x[w] & 0xffff;
+      tile[cl][d0 + 2 * w + 1] = x[w] >> 16;
+    }
+  }
+  __syncthreads();
+  const int d = tid >> 2;
+  uint16_t* dst = rkt + ((int64_t)h * DP + d) * ld;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int cl = 16 * (tid & 3) + 8 * q;
+    if (c0 + cl >= ld) continue;
+    u32x4 v;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      v[w] = (uint32_t)tile[cl + 2 * w][d] | ((uint32_t)tile[cl + 2 * w + 1][d] << 16);
+    *reinterpret_cast<u32x4*>(dst + c0 + cl) = v;
+  }
 }
 
 // dst[c][r] = bf16(src[r][c]) for r < rows, zero for rows <= r < ld (src in
-// `dtype`, [rows][cols]; dst [cols][ld]).
-__global__ void transpose_bf16_kernel(const void* src, int32_t rows, int32_t cols, int32_t dtype,
-                                      int32_t ld, uint16_t* dst) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (int64_t)cols * ld) return;
-  const int32_t r = idx % ld;
-  const int32_t c = idx / ld;
-  dst[idx] = r < rows ? bf16_bits(load_as_f32(src, (int64_t)r * cols + c, dtype)) : uint16_t(0);
+// `dtype`, [rows][cols]; dst [cols][ld], ld a multiple of 16).  One workgroup
+// per 16 rows x 64 columns: each thread reads four elements of src along c
+// (consecutive threads, consecutive columns; all four in flight) into LDS, and
+// each row of dst gets two 16-byte chunks.
+__device__ __forceinline__ void transpose_block(const void* src, int32_t rows, int32_t cols,
+                                                int32_t dtype, int32_t ld, uint16_t* dst,
+                                                int32_t bx, int32_t by) {
+  __shared__ uint16_t tile[16][66];   // [r][c]
+  const int32_t r0 = bx * 16, c0 = by * 64;
+  const int tid = threadIdx.x;
+  {
+    const int cl = tid & 63;
+    const int32_t c = c0 + cl;
+    float x[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int32_t r = r0 + (tid >> 6) + 4 * k;
+      x[k] = (r < rows && c < cols) ? load_as_f32(src, (int64_t)r * cols + c, dtype) : 0.0f;
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) tile[(tid >> 6) + 4 * k][cl] = bf16_bits(x[k]);
+  }
+  __syncthreads();
+  if (tid >= 128) return;
+  const int cl = tid >> 1, rl = 8 * (tid & 1);
+  if (c0 + cl >= cols) return;
+  u32x4 v;
+#pragma unroll
+  for (int w = 0; w < 4; ++w)
+    v[w] = (uint32_t)tile[rl + 2 * w][cl] | ((uint32_t)tile[rl + 2 * w + 1][cl] << 16);
+  *reinterpret_cast<u32x4*>(dst + (int64_t)(c0 + cl) * ld + r0 + rl) = v;
 }
 
 // du[h][d], dv[h][d] = sums over batch rows and 32-query chunks.  One
 // workgroup per (which, h, 8 columns): 32 strided partial sums per column,
 // then a fixed-order tree.
-__global__ __launch_bounds__(256) void duv_reduce_kernel(const float* part, int32_t B, int32_t H,
-                                                         int32_t nchunk, int32_t dh, float* du,
-                                                         float* dv) {
+__device__ __forceinline__ void duv_reduce_block(const float* part, int32_t B, int32_t H,
+                                                 int32_t nchunk, int32_t dh, float* du, float* dv,
+                                                 int32_t blk) {
   __shared__ float red[32][8];
   const int32_t nblk = (dh + 7) / 8;
-  const int32_t which = blockIdx.x / (H * nblk);
-  const int32_t rest = blockIdx.x % (H * nblk);
+  const int32_t which = blk / (H * nblk);
+  const int32_t rest = blk % (H * nblk);
   const int32_t h = rest / nblk, d0 = 8 * (rest % nblk);
   const int tid = threadIdx.x, dd = tid & 7, grp = tid >> 3;
   const int32_t n = B * nchunk;
   float s = 0.0f;
-  for (int32_t p = grp; p < n; p += 32) {
-    const int32_t bb = p / nchunk, c = p % nchunk;
-    s += part[((((int64_t)which * B + bb) * H + h) * nchunk + c) * DP + d0 + dd];
+  // partial p = grp, grp + 32, ... added in that order; eight loads in flight
+  for (int32_t p0 = grp; p0 < n; p0 += 8 * 32) {
+    float x[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int32_t p = p0 + 32 * k;
+      const int32_t bb = p / nchunk, c = p % nchunk;
+      x[k] = p < n ? part[((((int64_t)which * B + bb) * H + h) * nchunk + c) * DP + d0 + dd] : 0.0f;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (p0 + 32 * k < n) s += x[k];
   }
   red[grp][dd] = s;
   __syncthreads();
@@ -955,13 +1011,119 @@ __global__ __launch_bounds__(256) void duv_reduce_kernel(const float* part, int3
   if (tid < 8 && d0 + tid < dh) (which == 0 ? du : dv)[(int64_t)h * dh + d0 + tid] = red[0][tid];
 }
 
-// dst[x] = sum_r src[r][x] over n_rows rows of length row_len, in row order.
+// dst[x] = sum_r src[r][x] over n_rows rows of length row_len, in row order
+// (eight rows' loads in flight at a time).
 __global__ void sum_rows_kernel(const float* src, int32_t n_rows, int64_t row_len, float* dst) {
   const int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (x >= row_len) return;
   float s = 0.0f;
-  for (int32_t r = 0; r < n_rows; ++r) s += src[(int64_t)r * row_len + x];
+  for (int32_t r0 = 0; r0 < n_rows; r0 += 8) {
+    float v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = r0 + k < n_rows ? src[(int64_t)(r0 + k) * row_len + x] : 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (r0 + k < n_rows) s += v[k];
+  }
   dst[x] = s;
+}
+
+// dRk[delta][x] = sum_b part[b][delta][x] in row order for a tile of 16
+// distances x 64 columns (four elements per thread, eight rows' loads in
+// flight), and, when drkt is set, the tile's bf16 transpose into
+// drkt[x][delta] (distances P .. r_ld-1 zero) as 16-byte chunks.
+__device__ __forceinline__ void drk_sum_block(const BwdPostArgs& a, int32_t bx, int32_t by) {
+  __shared__ uint16_t tile[16][66];   // [delta][x]
+  const int32_t d0 = bx * 16, x0 = by * 64;
+  const int tid = threadIdx.x;
+  const int xl = tid & 63;
+  const int32_t x = x0 + xl;
+  const int64_t plane = (int64_t)a.P * a.HD;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int dl = (tid >> 6) + 4 * k;
+    const int32_t delta = d0 + dl;
+    const bool ok = delta < a.P && x < a.HD;
+    float s = 0.0f;
+    if (ok) {
+      const float* src = a.drk_part + (int64_t)delta * a.HD + x;
+      for (int32_t b0 = 0; b0 < a.B; b0 += 8) {
+        float v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = b0 + j < a.B ? src[(b0 + j) * plane] : 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (b0 + j < a.B) s += v[j];
+      }
+      a.d_rk[(int64_t)delta * a.HD + x] = s;
+    }
+    tile[dl][xl] = bf16_bits(s);   // zero past P
+  }
+  if (!a.drkt) return;
+  __syncthreads();
+  if (tid >= 128) return;
+  const int cl = tid >> 1, rl = 8 * (tid & 1);
+  if (x0 + cl >= a.HD) return;
+  u32x4 v;
+#pragma unroll
+  for (int w = 0; w < 4; ++w)
+    v[w] = (uint32_t)tile[rl + 2 * w][cl] | ((uint32_t)tile[rl + 2 * w + 1][cl] << 16);
+  *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(a.drkt) + (int64_t)(x0 + cl) * a.r_ld + d0 + rl) = v;
+}
+
+// Grid of the pre step: prep blocks, then Rk^T tiles (64 columns x head),
+// then R^T tiles (16 rows x 64 columns).
+struct PreGrid {
+  int32_t n_prep, rk_nx, n_rk, r_nx, n_r;
+};
+__host__ __device__ inline PreGrid pre_grid(const BwdPreArgs& a) {
+  PreGrid g;
+  g.n_prep = a.prep.B * a.prep.H * ((a.prep.Lp + 63) / 64);
+  g.rk_nx = (a.rkt_ld + 63) / 64;
+  g.n_rk = g.rk_nx * a.prep.H;
+  g.r_nx = a.r ? a.r_ld / 16 : 0;
+  g.n_r = a.r ? g.r_nx * ((a.d_pos + 63) / 64) : 0;
+  return g;
+}
+
+__global__ __launch_bounds__(256) void bwd_pre_kernel(BwdPreArgs a) {
+  const PreGrid g = pre_grid(a);
+  int32_t blk = blockIdx.x;
+  if (blk < g.n_prep) {
+    bwd_prep_block(a.prep, blk);
+    return;
+  }
+  blk -= g.n_prep;
+  if (blk < g.n_rk) {
+    rk_transpose_block(static_cast<const uint16_t*>(a.rk_ws), static_cast<uint16_t*>(a.rkt), a.Pp,
+                       a.pad_ws, a.rkt_ld, a.pad_t, blk % g.rk_nx, blk / g.rk_nx);
+    return;
+  }
+  blk -= g.n_rk;
+  transpose_block(a.r, a.P, a.d_pos, a.r_dtype, a.r_ld, static_cast<uint16_t*>(a.rt), blk % g.r_nx,
+                  blk / g.r_nx);
+}
+
+// Grid of the post step: dRk tiles (16 distances x 64 columns, over r_ld
+// distances when the transpose is written), then du/dv blocks.
+struct PostGrid {
+  int32_t sum_nx, n_sum;
+};
+__host__ __device__ inline PostGrid post_grid(const BwdPostArgs& a) {
+  PostGrid g;
+  g.sum_nx = ((a.drkt ? a.r_ld : a.P) + 15) / 16;
+  g.n_sum = g.sum_nx * ((a.HD + 63) / 64);
+  return g;
+}
+
+__global__ __launch_bounds__(256) void bwd_post_kernel(BwdPostArgs a) {
+  const PostGrid g = post_grid(a);
+  const int32_t blk = blockIdx.x;
+  if (blk < g.n_sum) {
+    drk_sum_block(a, blk % g.sum_nx, blk / g.sum_nx);
+    return;
+  }
+  duv_reduce_block(a.duv_part, a.B, a.H, a.nchunk, a.dh, a.d_u, a.d_v, blk - g.n_sum);
 }
 
 dim3 grid_for(int64_t n) { return dim3((unsigned)((n + 255) / 256)); }
@@ -995,39 +1157,27 @@ int launch_bmm64(const BmmArgs* a, int n, const int32_t* kind, const int32_t* ro
   return static_cast<int>(hipGetLastError());
 }
 
-int launch_bwd_prep(const BwdPrepArgs& a, void* stream) {
-  const int32_t nch = (a.Lp + 63) / 64;
-  hipLaunchKernelGGL(bwd_prep_kernel, dim3(a.B * a.H * nch), dim3(256), 0,
+int launch_bwd_pre(const BwdPreArgs& a, void* stream) {
+  if (a.rkt_ld % 8 != 0 || (a.r && (a.r_ld % 16 != 0 || a.P > a.r_ld)))
+    return static_cast<int>(hipErrorInvalidValue);
+  const PreGrid g = pre_grid(a);
+  hipLaunchKernelGGL(bwd_pre_kernel, dim3(g.n_prep + g.n_rk + g.n_r), dim3(256), 0,
                      static_cast<hipStream_t>(stream), a);
   return static_cast<int>(hipGetLastError());
 }
 
-int launch_rk_transpose(const void* rk_ws, void* rkt, int32_t H, int32_t Pp, int32_t pad_ws,
-                        int32_t ld, int32_t pad_t, void* stream) {
-  hipLaunchKernelGGL(rk_transpose_kernel, grid_for((int64_t)H * DP * ld), dim3(256), 0,
-                     static_cast<hipStream_t>(stream), static_cast<const uint16_t*>(rk_ws),
-                     static_cast<uint16_t*>(rkt), H, Pp, pad_ws, ld, pad_t);
-  return static_cast<int>(hipGetLastError());
-}
-
-int launch_transpose_bf16(const void* src, int32_t rows, int32_t cols, int32_t dtype, int32_t ld,
-                          void* dst, void* stream) {
-  hipLaunchKernelGGL(transpose_bf16_kernel, grid_for((int64_t)cols * ld), dim3(256), 0,
-                     static_cast<hipStream_t>(stream), src, rows, cols, dtype, ld,
-                     static_cast<uint16_t*>(dst));
+int launch_bwd_post(const BwdPostArgs& a, void* stream) {
+  if (a.drkt && (a.r_ld % 16 != 0 || a.P > a.r_ld)) return static_cast<int>(hipErrorInvalidValue);
+  const PostGrid g = post_grid(a);
+  const int32_t n_duv = 2 * a.H * ((a.dh + 7) / 8);
+  hipLaunchKernelGGL(bwd_post_kernel, dim3(g.n_sum + n_duv), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), a);
   return static_cast<int>(hipGetLastError());
 }
 
 int launch_sum_rows(const float* src, int32_t n_rows, int64_t row_len, float* dst, void* stream) {
   hipLaunchKernelGGL(sum_rows_kernel, grid_for(row_len), dim3(256), 0,
                      static_cast<hipStream_t>(stream), src, n_rows, row_len, dst);
-  return static_cast<int>(hipGetLastError());
-}
-
-int launch_duv_reduce(const float* part, int32_t B, int32_t H, int32_t nchunk, int32_t dh,
-                      float* du, float* dv, void* stream) {
-  hipLaunchKernelGGL(duv_reduce_kernel, dim3(2 * H * ((dh + 7) / 8)), dim3(256), 0,
-                     static_cast<hipStream_t>(stream), part, B, H, nchunk, dh, du, dv);
   return static_cast<int>(hipGetLastError());
 }
 

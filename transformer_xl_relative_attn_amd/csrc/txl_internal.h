@@ -310,14 +310,33 @@ int launch_attn_bwd_q(const BwdArgs& a, void* stream);
 // fragment tiles (dS'^T).  Output row of A row m: m + row_off[z].
 int launch_bmm64(const BmmArgs* a, int n, const int32_t* kind, const int32_t* row_off,
                  void* stream);
-int launch_bwd_prep(const BwdPrepArgs& a, void* stream);
-int launch_rk_transpose(const void* rk_ws, void* rkt, int32_t H, int32_t Pp, int32_t pad_ws,
-                        int32_t ld, int32_t pad_t, void* stream);
-int launch_transpose_bf16(const void* src, int32_t rows, int32_t cols, int32_t dtype, int32_t ld,
-                          void* dst, void* stream);
+// The backward's small steps before the query kernel, one grid: the prep
+// (BwdPrepArgs), the Rk^T table and, for dW_kR, the bf16 transpose of R.
+struct BwdPreArgs {
+  BwdPrepArgs prep;
+  const void* rk_ws;       // bf16 [H][pad_ws + Pp + pad_ws][64] (the attention's table)
+  void* rkt;               // bf16 [H][64][rkt_ld]: distance delta at column pad_t + delta,
+                           // zeros elsewhere (rkt_ld a multiple of 8)
+  int32_t Pp, pad_ws, rkt_ld, pad_t;
+  const void* r;           // optional [P][d_pos] in r_dtype -> rt bf16 [d_pos][r_ld],
+  void* rt;                // zero columns P .. r_ld-1 (r_ld a multiple of 16)
+  int32_t P, d_pos, r_dtype, r_ld;
+};
+// ... and after the key-side products, one grid: dRk = the batch rows' partials
+// summed in row order (with, for dW_kR, its bf16 transpose), and du, dv.
+struct BwdPostArgs {
+  const float* drk_part;   // [B][P][HD]
+  float* d_rk;             // [P][HD]
+  void* drkt;              // optional bf16 [HD][r_ld], zero columns P .. r_ld-1
+  int32_t B, P, HD, r_ld;
+  const float* duv_part;   // [2][B][H][nchunk][64] (per 32-query chunk)
+  float* d_u;              // [H][dh]
+  float* d_v;
+  int32_t H, nchunk, dh;
+};
+int launch_bwd_pre(const BwdPreArgs& a, void* stream);
+int launch_bwd_post(const BwdPostArgs& a, void* stream);
 int launch_sum_rows(const float* src, int32_t n_rows, int64_t row_len, float* dst, void* stream);
-int launch_duv_reduce(const float* part, int32_t B, int32_t H, int32_t nchunk, int32_t dh,
-                      float* du, float* dv, void* stream);
 int launch_repack_rk(const void* rk_pub, void* rk_ws, int32_t P, int32_t Pp, int32_t pad, int32_t H,
                      int32_t dh, int32_t dp, int32_t dtype, void* stream);
 
