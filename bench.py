@@ -558,7 +558,8 @@ def main():
         step()
         evs[r + 1].record(stream)
     torch.cuda.synchronize()
-    med_ms = float(np.median([evs[r].elapsed_time(evs[r + 1]) for r in range(n_med)]))
+    step_ms = [evs[r].elapsed_time(evs[r + 1]) for r in range(n_med)]
+    med_ms = float(np.median(step_ms))
 
     # ---- per-kernel timing with HIP events on the launch stream
     txl.txl_timing_reset()
@@ -719,7 +720,11 @@ def main():
         "tokens_per_s": round(tokens, 1),
         "median_step": {"ms": round(med_ms, 4), "reps": n_med,
                         "tflops": round(f_step / (med_ms * 1e-3) / 1e12, 2),
-                        "tokens_per_s": round(cfg.batch * cfg.seg_len / (med_ms * 1e-3), 1)},
+                        "tokens_per_s": round(cfg.batch * cfg.seg_len / (med_ms * 1e-3), 1),
+                        "p10_p90_max_ms": [round(float(np.percentile(step_ms, 10)), 4),
+                                           round(float(np.percentile(step_ms, 90)), 4),
+                                           round(float(max(step_ms)), 4)]},
+        "headline_clocks_ms": {"gpu_events": round(gpu_ms, 3), "host_wall": round(wall * 1e3, 3)},
         "gflop_per_step": round(f_step / 1e9, 3),
         "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv)
                         for kk, vv in d.items()} for k, d in kernels.items()},
