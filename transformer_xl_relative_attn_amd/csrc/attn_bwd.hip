@@ -13,18 +13,23 @@
 //   dRk[delta] = scale * sum over pairs with M+i-j = delta of dS_ij (q_i + v)
 //
 // attn_bwd_q_kernel (a workgroup of 4 waves x 32 queries of one (b, h)): the
-//   K, val and K^T tiles and the Rk and Rk^T chunks of every 32-key block are
-//   staged in LDS by direct loads two blocks ahead, one barrier per block, and
-//   shared by the four waves.  For every visible block a wave recomputes the
-//   scores exactly as the forward kernel does (the (b)+(d) window written
+//   forward's K and V^T tiles and the Rk and Rk^T chunks of every 32-key block
+//   are staged in LDS by direct loads two blocks ahead, one barrier per block,
+//   and shared by the four waves (K^T and the val rows are the same tiles read
+//   through transposing LDS reads).  For every visible block a wave recomputes
+//   the scores exactly as the forward kernel does (the (b)+(d) window written
 //   shifted to LDS and read back as the accumulator of (q+u).K), P from the
-//   forward's log-sum-exp, dP^T = val G^T on the matrix cores, and dS.  It accumulates dq's k-part (K^T tile
-//   times dS^T) and its Rk-part (Rk^T window times dS written shifted, row
-//   31 + i - j of the window holds pair (i, j), the App. B shift in reverse),
-//   and writes P^T, dS^T and the shifted dS'^T (row delta) for the key-side
-//   products, which need sums over queries.
+//   forward's log-sum-exp, dP^T = val G^T on the matrix cores, and dS.  It
+//   accumulates dq's k-part (K^T times dS^T) and its Rk-part (Rk^T chunks
+//   times dS written shifted, row 31 + i - j of the window holds pair (i, j),
+//   the App. B shift in reverse), and writes P^T, dS^T and the shifted dS'^T
+//   (row delta) as fragment tiles for the key-side products, which need sums
+//   over queries.
 // bmm64_kernel: batched A B^T with 64 output columns (dk, dval, dRk), the
 //   masked entries of A selected away by index.
+// bwd_pre_kernel / bwd_post_kernel: the small steps before the query kernel
+//   (D, operand layouts, Rk^T, R^T) and after the key-side products (dRk's
+//   ordered batch sum and its transpose, du, dv), one launch each.
 #include <type_traits>
 
 #include "dev_common.h"
@@ -39,11 +44,10 @@ using IC = std::integral_constant<int, X>;
 constexpr int DP = 64;
 constexpr int KB = 32;
 constexpr int WP = 68;     // floats per query row of the score window (64 + pad)
-constexpr int NST = 3;     // K / val / K^T ring stages (blocks t .. t+2)
+constexpr int NST = 3;     // K / V^T ring stages (blocks t .. t+2)
 constexpr int RKS = 8;     // Rk and Rk^T chunk slots: chunk c in slot (c + 8) & 7
 constexpr int TU = 256;    // 16-byte units of a 4 KB tile
 constexpr int TPW = 36;    // bf16 per query row of the P / dS transpose tiles (32 + pad)
-constexpr float kNegInf = -__builtin_inff();
 
 struct BwdSmem {
   u32x4 kv[NST][2 * TU];            // per stage: K tile (32 keys x 128 B), V^T tile (64 d x 64 B)
