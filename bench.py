@@ -74,6 +74,10 @@ def source_sha(names):
     return h.hexdigest()[:16]
 
 
+# where roofline.achieved's launch duration comes from
+TIMING_SOURCE = ("mean launch duration from HIP events recorded on the launch stream around "
+                 "each launch (no system-scope fence), over --steps steps after the timed region")
+
 KERNEL_SOURCES = {
     "proj_gemm": ["gemm.hip", "dev_common.h", "txl_internal.h"],
     "rel_attn": ["attn.hip", "dev_common.h", "txl_internal.h"],
@@ -590,13 +594,14 @@ def main():
         roof = {"kernel": "proj_gemm", "bound": "mfma", "achieved": round(ach, 1),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
                 "traffic": load_traffic("proj_gemm", wl_name),
-                "algorithmic_per_launch": fl}
+                "algorithmic_per_launch": fl, "timing": TIMING_SOURCE}
     elif dominant == "rel_attn":
         by = attn_bytes(cfg)
         ach = by / (kernels[dominant]["avg_us"] * 1e-6) / 1e9
         roof = {"kernel": "rel_attn", "bound": "hbm", "achieved": round(ach, 1),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
-                "traffic": load_traffic("rel_attn", wl_name), "algorithmic_per_launch": by}
+                "traffic": load_traffic("rel_attn", wl_name), "algorithmic_per_launch": by,
+                "timing": TIMING_SOURCE}
     else:
         roof = {"kernel": dominant, "bound": "hbm", "achieved": None, "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": None, "traffic": None}
