@@ -476,13 +476,14 @@ txl_status_t pack_operands(const AttnPlan& p, const AttnPtrs& a, char* ws, void*
   return TXL_OK;
 }
 
-// q = h W_q^T -> fp32 [B][H][Lp][DP]
+// q = h W_q^T -> fp32 [B][H][Lp][DP], rows i < L only (the attention kernels
+// read the padding rows L .. Lp-1 as zeros without loading them)
 void add_q_problem(GemmGroup& g, const AttnPlan& p, const Operands& o, char* ws) {
   const int64_t DP = p.DP;
-  add_problem(g, p.B * p.Lp, p.H * p.DP, p.Kd,
-              src_htilde(nullptr, o.h, o.ld_d, p.Lp, 0, p.L, 0), src_headpad(o.Wq, o.ld_d, p.dh, p.DP),
-              out_map(ws + p.q.off, TXL_F32, p.B * p.Lp, p.H * p.DP,
-                      axis(p.Lp, (int64_t)p.H * p.Lp * DP, DP), axis(p.DP, (int64_t)p.Lp * DP, 1)),
+  add_problem(g, p.B * p.L, p.H * p.DP, p.Kd,
+              src_htilde(nullptr, o.h, o.ld_d, p.L, 0, p.L, 0), src_headpad(o.Wq, o.ld_d, p.dh, p.DP),
+              out_map(ws + p.q.off, TXL_F32, p.B * p.L, p.H * p.DP,
+                      axis(p.L, (int64_t)p.H * p.Lp * DP, DP), axis(p.DP, (int64_t)p.Lp * DP, 1)),
               gemm_tile(p.dtype));
 }
 

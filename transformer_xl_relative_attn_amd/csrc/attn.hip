@@ -270,13 +270,19 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a, int32_t p
   }
   floatx4 qraw[8];
   {
+    // rows L .. Lp-1 of q are not computed: those lanes take q = 0 (their
+    // outputs are never stored)
+    const bool q_ok = i0 + ii < L;
     const floatx4* qrow =
-        reinterpret_cast<const floatx4*>(a.q + ((int64_t)bh * a.Lp + (wave_on ? i0 + ii : 0)) * DP);
+        reinterpret_cast<const floatx4*>(a.q + ((int64_t)bh * a.Lp + (q_ok ? i0 + ii : 0)) * DP);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       qraw[2 * s] = qrow[(16 * s + 8 * hf) / 4];
       qraw[2 * s + 1] = qrow[(16 * s + 8 * hf) / 4 + 1];
     }
+#pragma unroll
+    for (int x = 0; x < 8; ++x)
+      if (!q_ok) qraw[x] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
   }
   compiler_fence();   // the q loads go out before the third block's DMA
   issue_block(t_lo + 2, sm.kv[2], sm.rk[rk_slot(t_lo + 3)]);

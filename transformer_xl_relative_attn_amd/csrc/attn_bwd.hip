@@ -179,7 +179,8 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_q_kernel(BwdArgs a) {
   // query operands (q+u)c, (q+v)c, d = 16s + 8hf + e, and G_i for dP^T
   bf16x8 qu[4], qv[4], go[4];
   {
-    const int32_t ic = wave_on ? i : 0;   // rows past Lp are never read
+    // q rows L .. Lp-1 are not computed: those lanes take q = 0
+    const int32_t ic = qok ? i : 0;
     const float* qrow = a.q + ((int64_t)bh * Lp + ic) * DP;
     const uint16_t* up = static_cast<const uint16_t*>(a.u) + (int64_t)head * a.dh;
     const uint16_t* vp = static_cast<const uint16_t*>(a.v) + (int64_t)head * a.dh;
@@ -189,7 +190,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_q_kernel(BwdArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int d = 16 * s + 8 * hf + e;
-        const float qd = qrow[d];
+        const float qd = qok ? qrow[d] : 0.0f;
         // clamped in-bounds element, selected after the load, so the loads
         // issue together instead of one branch-and-wait each
         const int dc = min(d, a.dh - 1);

@@ -692,7 +692,14 @@ int launch_gemm_bf16(const GemmGroup& g, void* stream) {
   if (g.total_tiles <= 0) return 0;
   if (!pair_ok(g)) return static_cast<int>(hipErrorInvalidValue);
   const int cus = device_cu_count();
-  if (2 * g.total_tiles <= cus) return launch_tiles(regroup(g, nullptr, 128), true, stream);
+  // 128x128 tiles when the 256x256 ones fill at most half the chip, or when
+  // both tilings take one round (two 128x128 workgroups per CU then share the
+  // work that one 256x256 workgroup per CU would do alone)
+  int64_t t128 = 0;
+  for (int i = 0; i < g.count; ++i)
+    t128 += (int64_t)((g.p[i].M + 127) / 128) * ((g.p[i].N + 127) / 128);
+  if (2 * g.total_tiles <= cus || (g.total_tiles <= cus && t128 <= 2 * (int64_t)cus))
+    return launch_tiles(regroup(g, nullptr, 128), true, stream);
   // A last round of 256x256 tiles less than a quarter full would take as long
   // as a full one: the smallest problem that covers it (else the smallest
   // ones together) moves to a 128x128 launch of its own, and the rest takes
