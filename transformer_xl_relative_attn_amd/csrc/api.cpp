@@ -862,30 +862,38 @@ txl_status_t run_bwd_from_state(const BwdPlan& bp, const AttnPtrs& a, const void
   };
   const int32_t BHn = p.B * p.H;
   const AxisMap per_bh_c = make_axis(p.H, (int64_t)p.P * HD, p.dh);   // [B][P][H][dh]
-  // dRk per (head, batch row) into partials [B][P][H][dh], then summed over
-  // the batch rows in order (one product per head would leave the chip idle)
+  // dRk per (head, pair of batch rows) into partials [B/2][P][H][dh] (one
+  // batch row per partial when B is odd), then summed over the partials in
+  // order (one product per head would leave the chip idle)
   const int64_t BL = (int64_t)p.B * p.Lp;
+  const int32_t rc = p.B % 2 == 0 ? 2 : 1;   // batch rows per dRk partial
+  const int32_t nrc = p.B / rc;
   float* drk_part = reinterpret_cast<float*>(ws + bp.drkp.off);
   BmmArgs prods[3] = {
+      bmm(ws + bp.dspt.off, BL,
+          make_axis(nrc, (int64_t)bp.dsp_tiles * 32 * BL, 32 * (int64_t)rc * p.Lp), ws + bp.qvt.off,
+          BL, make_axis(nrc, DP * BL, (int64_t)rc * p.Lp), p.H * nrc, rc * p.Lp, p.scale, drk_part,
+          make_axis(nrc, p.dh, (int64_t)p.P * HD)),
       bmm(ws + bp.dst.off, p.Lp, axis_linear((int64_t)p.Np * p.Lp), ws + bp.qut.off, p.Lp,
           axis_linear(DP * p.Lp), BHn, p.Lp, p.scale, g.d_k, per_bh_c),
       bmm(ws + bp.pt.off, p.Lp, axis_linear((int64_t)p.Np * p.Lp), ws + bp.dot.off, p.Lp,
-          axis_linear(DP * p.Lp), BHn, p.Lp, 1.0f, g.d_val, per_bh_c),
-      bmm(ws + bp.dspt.off, BL, make_axis(p.B, (int64_t)bp.dsp_tiles * 32 * BL, 32 * (int64_t)p.Lp), ws + bp.qvt.off,
-          BL, make_axis(p.B, DP * BL, p.Lp), BHn, p.Lp, p.scale, drk_part,
-          make_axis(p.B, p.dh, (int64_t)p.P * HD))};
+          axis_linear(DP * p.Lp), BHn, p.Lp, 1.0f, g.d_val, per_bh_c)};
   // all three read A from the query kernel's fragment tiles; dS'^T rows are
-  // distances from dsp_lo
-  prods[2].M = bp.dsp_tiles * 32;
-  const int32_t kinds[3] = {1, 1, 2}, row_offs[3] = {0, 0, bp.dsp_lo};
-  TXL_TRY(after_launch(timed(K_BWD_BMM, stream, [&] { return launch_bmm64(prods, 3, kinds, row_offs, stream); }),
+  // distances from dsp_lo.  The dRk product's workgroups (the longest, with
+  // K over rc batch rows) are dealt first.
+  prods[0].M = bp.dsp_tiles * 32;
+  const int32_t kinds[3] = {2, 1, 1}, row_offs[3] = {bp.dsp_lo, 0, 0}, kpers[3] = {p.Lp, 0, 0};
+  TXL_TRY(after_launch(timed(K_BWD_BMM, stream, [&] {
+                         return launch_bmm64(prods, 3, kinds, row_offs, kpers, stream);
+                       }),
                        "dk, dval, dRk products", stream));
-  // one launch: dRk (the batch rows' partials summed in order) with its bf16
+  // one launch: dRk (the partials summed in order) with its bf16
   // transpose for dW_kR, and du, dv
   BwdPostArgs post{};
   post.drk_part = drk_part;
   post.d_rk = g.d_Rk;
   post.drkt = g.d_W_kR ? ws + bp.drkt.off : nullptr;
+  post.drk_rows = nrc;
   post.B = p.B;
   post.P = p.P;
   post.HD = (int32_t)HD;

@@ -625,6 +625,8 @@ struct BmmBatch {
   BmmArgs p[3];
   int32_t kind[3];      // layout of A (see launch_bmm64)
   int32_t row_off[3];   // output row of A row m: m + row_off
+  int32_t kper[3];      // kind 2: K spans K / kper batch rows of kper queries each
+                        // (klim applies within each), 0 = one
 };
 
 __global__ __launch_bounds__(256, 2) void bmm64_kernel(BmmBatch bt) {
@@ -668,6 +670,7 @@ __global__ __launch_bounds__(256, 2) void bmm64_kernel(BmmBatch bt) {
   // top(w) - t_end(w) .. top(w) counted from row_off.
   const int kind = z == 0 ? bt.kind[0] : z == 1 ? bt.kind[1] : bt.kind[2];
   const int32_t row_off = z == 0 ? bt.row_off[0] : z == 1 ? bt.row_off[1] : bt.row_off[2];
+  const int32_t kper = z == 0 ? bt.kper[0] : z == 1 ? bt.kper[1] : bt.kper[2];
   const bool frag = kind != 0;
   if (frag) {   // lda: the tile row's length in elements (16 per tile)
 #pragma unroll
@@ -677,7 +680,10 @@ __global__ __launch_bounds__(256, 2) void bmm64_kernel(BmmBatch bt) {
     }
   }
   auto tile_written = [&](int r, int32_t kk) {
-    const int32_t w = kk >> 5;   // query tile of 32
+    // query of the step within its batch row (kind 2 may span several)
+    const int32_t kq = kper > 0 ? kk % kper : kk;
+    if (kq >= a.klim) return false;
+    const int32_t w = kq >> 5;   // query tile of 32
     const int32_t t_end = (a.moff + min(32 * w + 31, a.klim - 1) + 32) / 32;
     const int32_t tr = m0 / 32 + r;
     if (kind == 1) return tr < t_end;
@@ -685,7 +691,7 @@ __global__ __launch_bounds__(256, 2) void bmm64_kernel(BmmBatch bt) {
     return tr <= top && tr >= top - t_end;
   };
   // rows need k >= m - moff and none at or past kend
-  const int32_t kend = min(a.K, a.klim);
+  const int32_t kend = kper > 0 ? a.K : min(a.K, a.klim);
   const int32_t kfirst_wg = kind == 2 ? 0 : max(0, mwg - a.moff) & ~(BMM_KC - 1);
   const int32_t kfirst = kind == 2 ? 0 : max(0, m0 - a.moff) & ~15;
   int bofs[2];   // this lane's B row base (16-byte units) and swizzle
@@ -1033,7 +1039,7 @@ __global__ void sum_rows_kernel(const float* src, int32_t n_rows, int64_t row_le
   dst[x] = s;
 }
 
-// dRk[delta][x] = sum_b part[b][delta][x] in row order for a tile of 16
+// dRk[delta][x] = sum_r part[r][delta][x] in row order for a tile of 16
 // distances x 64 columns (four elements per thread, eight rows' loads in
 // flight), and, when drkt is set, the tile's bf16 transpose into
 // drkt[x][delta] (distances P .. r_ld-1 zero) as 16-byte chunks.
@@ -1052,13 +1058,13 @@ __device__ __forceinline__ void drk_sum_block(const BwdPostArgs& a, int32_t bx, 
     float s = 0.0f;
     if (ok) {
       const float* src = a.drk_part + (int64_t)delta * a.HD + x;
-      for (int32_t b0 = 0; b0 < a.B; b0 += 8) {
+      for (int32_t b0 = 0; b0 < a.drk_rows; b0 += 8) {
         float v[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = b0 + j < a.B ? src[(b0 + j) * plane] : 0.0f;
+        for (int j = 0; j < 8; ++j) v[j] = b0 + j < a.drk_rows ? src[(b0 + j) * plane] : 0.0f;
 #pragma unroll
         for (int j = 0; j < 8; ++j)
-          if (b0 + j < a.B) s += v[j];
+          if (b0 + j < a.drk_rows) s += v[j];
       }
       a.d_rk[(int64_t)delta * a.HD + x] = s;
     }
@@ -1143,12 +1149,15 @@ int launch_attn_bwd_q(const BwdArgs& a, void* stream) {
 }
 
 int launch_bmm64(const BmmArgs* a, int n, const int32_t* kind, const int32_t* row_off,
-                 void* stream) {
+                 const int32_t* kper, void* stream) {
   if (n < 1 || n > 3) return static_cast<int>(hipErrorInvalidValue);
   BmmBatch bt{};
   for (int i = 0; i < n; ++i) {
     bt.kind[i] = kind[i];
     bt.row_off[i] = row_off[i];
+    bt.kper[i] = kper ? kper[i] : 0;
+    if (bt.kper[i] != 0 && (kind[i] != 2 || bt.kper[i] % 32 != 0 || a[i].K % bt.kper[i] != 0))
+      return static_cast<int>(hipErrorInvalidValue);
   }
   int32_t gx = 1, gy = 1;
   for (int i = 0; i < n; ++i) {

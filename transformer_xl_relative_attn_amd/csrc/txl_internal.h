@@ -307,9 +307,11 @@ int launch_cast_f32(const void* src, float* dst, int64_t n, int32_t dtype, void*
 int launch_attn_bwd_q(const BwdArgs& a, void* stream);
 // n <= 3 products in one launch.  kind[z]: 0 = A in rows; 1 = A in the query
 // kernel's key-row fragment tiles (P^T, dS^T); 2 = A in its distance-row
-// fragment tiles (dS'^T).  Output row of A row m: m + row_off[z].
+// fragment tiles (dS'^T).  Output row of A row m: m + row_off[z].  kper[z]
+// (kind 2 only; NULL = all 0): K covers K / kper consecutive batch rows of
+// kper (a multiple of 32) padded queries each, klim applying within each.
 int launch_bmm64(const BmmArgs* a, int n, const int32_t* kind, const int32_t* row_off,
-                 void* stream);
+                 const int32_t* kper, void* stream);
 // The backward's small steps before the query kernel, one grid: the prep
 // (BwdPrepArgs), the Rk^T table and, for dW_kR, the bf16 transpose of R.
 struct BwdPreArgs {
@@ -325,10 +327,10 @@ struct BwdPreArgs {
 // ... and after the key-side products, one grid: dRk = the batch rows' partials
 // summed in row order (with, for dW_kR, its bf16 transpose), and du, dv.
 struct BwdPostArgs {
-  const float* drk_part;   // [B][P][HD]
+  const float* drk_part;   // [drk_rows][P][HD]
   float* d_rk;             // [P][HD]
   void* drkt;              // optional bf16 [HD][r_ld], zero columns P .. r_ld-1
-  int32_t B, P, HD, r_ld;
+  int32_t drk_rows, B, P, HD, r_ld;
   const float* duv_part;   // [2][B][H][nchunk][64] (per 32-query chunk)
   float* d_u;              // [H][dh]
   float* d_v;
