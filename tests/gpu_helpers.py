@@ -103,8 +103,18 @@ class DeviceLayers:
 
 
 def workspace(nbytes: int):
+    """A device workspace filled with 0xFF bytes (NaN in bf16 and fp32), so that
+    a kernel reading workspace memory that no kernel of the call wrote shows up
+    as NaN in the compared outputs."""
     torch = torch_mod()
-    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device="cuda")
+    return torch.full((max(int(nbytes), 1),), 0xFF, dtype=torch.uint8, device="cuda")
+
+
+def poisoned(shape, dtype):
+    """An output buffer filled with NaN: elements the library leaves unwritten fail
+    the comparison."""
+    torch = torch_mod()
+    return torch.full(shape, float("nan"), dtype=dtype, device="cuda")
 
 
 def run_attn_stream(wl: synth.Workload, n_seg: int, scale: float = 0.0, start: int = 0,

@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 
 import synth
-from gpu_helpers import DeviceLayers, assert_close, from_dev, log, to_dev, workspace
+from gpu_helpers import DeviceLayers, assert_close, from_dev, log, poisoned, to_dev, workspace
 
 pytestmark = pytest.mark.gpu
 
@@ -41,13 +41,13 @@ def _run(txl, cfg, b_idx, use_rk=False, with_wkr=True, seed=7, oracle_rows=False
         Rk_host = synth.round_to(rng.normal(0.0, 0.5, (P, H, dh)), "bf16")
         Rk = to_dev(Rk_host, "bf16")
     f32 = dict(dtype=torch.float32, device="cuda")
-    d_q = torch.empty((B, L, H, dh), **f32)
-    d_k = torch.empty((B, P, H, dh), **f32)
-    d_val = torch.empty((B, P, H, dh), **f32)
-    d_u = torch.empty((H, dh), **f32)
-    d_v = torch.empty((H, dh), **f32)
-    d_Rk = torch.empty((P, H, dh), **f32)
-    d_W = torch.empty((H * dh, c.d_pos), **f32) if with_wkr else None
+    d_q = poisoned((B, L, H, dh), torch.float32)
+    d_k = poisoned((B, P, H, dh), torch.float32)
+    d_val = poisoned((B, P, H, dh), torch.float32)
+    d_u = poisoned((H, dh), torch.float32)
+    d_v = poisoned((H, dh), torch.float32)
+    d_Rk = poisoned((P, H, dh), torch.float32)
+    d_W = poisoned((H * dh, c.d_pos), torch.float32) if with_wkr else None
     ws = workspace(txl.txl_rel_attn_bwd_workspace_bytes(shp))
     h = to_dev(wl.segments[0], "bf16")
     txl.txl_rel_attn_bwd(shp, h, dl.mem[0] if M else None, 0, w["W_q"], w["W_kE"],

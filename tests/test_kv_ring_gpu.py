@@ -35,7 +35,7 @@ def run_ring_stream(wl, n_seg, mem_start=0, use_rk=False):
     if mem_start and c.mem_len:
         mem = torch.roll(mem, shifts=mem_start, dims=1).contiguous()
     shp = dl.shape()
-    ring = torch.empty(txl.txl_kv_ring_bytes(shp), dtype=torch.uint8, device="cuda")
+    ring = workspace(txl.txl_kv_ring_bytes(shp))
     ws = workspace(txl.txl_kv_ring_workspace_bytes(shp))
     w = dl.W[0]
     Rk = None
@@ -134,7 +134,7 @@ def run_segment_ring_stream(wl, n_seg):
     ws = workspace(txl.txl_segment_kv_workspace_bytes(shp, c.n_layers, c.d_inner))
     rings = []
     for n, w in enumerate(dl.W):
-        ring = torch.empty(txl.txl_kv_ring_bytes(shp), dtype=torch.uint8, device="cuda")
+        ring = workspace(txl.txl_kv_ring_bytes(shp))
         assert txl.txl_kv_ring_init(shp, dl.mem[n] if c.mem_len else None, 0, w["W_kE"],
                                     w["W_v"], ring, ws) == 0
         rings.append(ring)

@@ -400,7 +400,7 @@ def test_shaw_variant(txl, path):
             outs.append(from_dev(out))
     else:
         ws = workspace(txl.txl_kv_ring_workspace_bytes(shp))
-        ring = torch.empty(txl.txl_kv_ring_bytes(shp), dtype=torch.uint8, device="cuda")
+        ring = workspace(txl.txl_kv_ring_bytes(shp))
         start = txl.txl_kv_ring_init(shp, dl.mem[0], 0, w["W_kE"], w["W_v"], ring, ws)
         for s in range(3):
             h = to_dev(wl.segments[s], "bf16")

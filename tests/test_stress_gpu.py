@@ -33,7 +33,7 @@ import pytest
 
 import synth
 from gpu_helpers import (TOL, DeviceLayers, assert_close, from_dev, log, rel_err,
-                         run_attn_stream, to_dev)
+                         run_attn_stream, to_dev, workspace)
 
 pytestmark = pytest.mark.gpu
 
@@ -191,8 +191,7 @@ def test_vanilla_window_stack(txl, L, n_layers):
     wl = synth.make_workload(cfg)
     dl = DeviceLayers(wl)
     shp = dl.shape()
-    ws = torch.empty(txl.txl_segment_workspace_bytes(shp, n_layers, cfg.d_inner),
-                     dtype=torch.uint8, device="cuda")
+    ws = workspace(txl.txl_segment_workspace_bytes(shp, n_layers, cfg.d_inner))
     h = to_dev(wl.segments[0], "bf16")
     out = torch.empty_like(h)
     start = txl.txl_segment_step(shp, n_layers, cfg.d_inner, dl.layer_structs(), dl.R, h, out, 0,
