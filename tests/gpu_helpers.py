@@ -81,7 +81,7 @@ class DeviceLayers:
                          W_ff2=to_dev(lay.W_ff2, dt))
             self.W.append(d)
         self.mem = [to_dev(m, dt) for m in wl.mem]
-        self.R = torch.empty((c.n_pos, c.d_pos), dtype=tdtype(dt), device="cuda")
+        self.R = nan_empty((c.n_pos, c.d_pos), dtype=tdtype(dt), device="cuda")
         import transformer_xl_relative_attn_amd as txl
         txl.txl_sinusoid_pos(self.R, c.n_pos, c.d_pos, txl_dtype(dt))
 
@@ -110,6 +110,14 @@ def workspace(nbytes: int):
     return torch.full((max(int(nbytes), 1),), 0xFF, dtype=torch.uint8, device="cuda")
 
 
+def nan_empty(shape, dtype, device="cuda"):
+    """torch.empty for output buffers, filled with NaN instead."""
+    torch = torch_mod()
+    if isinstance(shape, int):
+        shape = (shape,)
+    return torch.full(shape, float("nan"), dtype=dtype, device=device)
+
+
 def poisoned(shape, dtype):
     """An output buffer filled with NaN: elements the library leaves unwritten fail
     the comparison."""
@@ -133,7 +141,7 @@ def run_attn_stream(wl: synth.Workload, n_seg: int, scale: float = 0.0, start: i
     w = dl.W[0]
     Rk = None
     if use_rk:
-        Rk = torch.empty((c.n_pos, c.n_heads, c.d_head), dtype=tdtype(c.dtype), device="cuda")
+        Rk = nan_empty((c.n_pos, c.n_heads, c.d_head), dtype=tdtype(c.dtype), device="cuda")
         pws = workspace(txl.txl_rel_proj_workspace_bytes(c.n_pos, c.d_pos, c.n_heads, c.d_head,
                                                          txl_dtype(c.dtype)))
         txl.txl_rel_proj(dl.R, w["W_kR"], Rk, c.n_pos, c.d_pos, c.n_heads, c.d_head,
@@ -141,7 +149,7 @@ def run_attn_stream(wl: synth.Workload, n_seg: int, scale: float = 0.0, start: i
     outs = []
     for s in range(n_seg):
         h = to_dev(wl.segments[s], c.dtype)
-        out = torch.empty((c.batch, c.seg_len, c.n_heads * c.d_head), dtype=tdtype(c.dtype),
+        out = nan_empty((c.batch, c.seg_len, c.n_heads * c.d_head), dtype=tdtype(c.dtype),
                           device="cuda")
         txl.txl_rel_attn_fwd(shp, h, dl.mem[0] if c.mem_len else None, start, w["W_q"],
                              w["W_kE"], w["W_kR"], w["W_v"], dl.u, dl.v, dl.R, Rk, out, ws)
@@ -167,7 +175,7 @@ def run_segment_stream(wl: synth.Workload, n_seg: int, scale: float = 0.0):
     outs = []
     for s in range(n_seg):
         h = to_dev(wl.segments[s], c.dtype)
-        out = torch.empty((c.batch, c.seg_len, d_out), dtype=tdtype(c.dtype), device="cuda")
+        out = nan_empty((c.batch, c.seg_len, d_out), dtype=tdtype(c.dtype), device="cuda")
         start = txl.txl_segment_step(shp, c.n_layers, c.d_inner, layers, dl.R, h, out, start, ws)
         torch.cuda.synchronize()
         outs.append(from_dev(out))

@@ -8,7 +8,8 @@ import numpy as np
 import pytest
 
 import synth
-from gpu_helpers import DeviceLayers, assert_close, from_dev, log, poisoned, to_dev, workspace
+from gpu_helpers import (DeviceLayers, assert_close, from_dev, log, nan_empty, poisoned, to_dev,
+                         workspace)
 
 pytestmark = pytest.mark.gpu
 
@@ -172,20 +173,20 @@ def test_bwd_saved_matches_recompute(txl, case):
     f32 = dict(dtype=torch.float32, device="cuda")
 
     def grads():
-        return [torch.empty((B, L, H, dh), **f32), torch.empty((B, P, H, dh), **f32),
-                torch.empty((B, P, H, dh), **f32), torch.empty((H, dh), **f32),
-                torch.empty((H, dh), **f32), torch.empty((P, H, dh), **f32),
-                None if use_rk else torch.empty((H * dh, c.d_pos), **f32)]
+        return [nan_empty((B, L, H, dh), **f32), nan_empty((B, P, H, dh), **f32),
+                nan_empty((B, P, H, dh), **f32), nan_empty((H, dh), **f32),
+                nan_empty((H, dh), **f32), nan_empty((P, H, dh), **f32),
+                None if use_rk else nan_empty((H * dh, c.d_pos), **f32)]
     g_ref, g_sav = grads(), grads()
     dG = to_dev(G, "bf16")
     ws_ref = workspace(txl.txl_rel_attn_bwd_workspace_bytes(shp))
     txl.txl_rel_attn_bwd(shp, h, mem, 0, w["W_q"], w["W_kE"], W_kR, w["W_v"], dl.u, dl.v, R, Rk,
                          dG, *g_ref, ws_ref)
-    out_ref = torch.empty((B, L, H, dh), dtype=torch.bfloat16, device="cuda")
+    out_ref = nan_empty((B, L, H, dh), dtype=torch.bfloat16, device="cuda")
     ws_f = workspace(txl.txl_rel_attn_workspace_bytes(shp))
     txl.txl_rel_attn_fwd(shp, h, mem, 0, w["W_q"], w["W_kE"], W_kR, w["W_v"], dl.u, dl.v, R, Rk,
                          out_ref, ws_f)
-    out = torch.empty_like(out_ref)
+    out = torch.full_like(out_ref, float("nan"))
     ws = workspace(txl.txl_rel_attn_bwd_workspace_bytes(shp))
     txl.txl_rel_attn_fwd_train(shp, h, mem, 0, w["W_q"], w["W_kE"], W_kR, w["W_v"], dl.u, dl.v,
                                R, Rk, out, ws)

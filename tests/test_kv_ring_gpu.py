@@ -10,7 +10,7 @@ import pytest
 
 import synth
 from gpu_helpers import (DeviceLayers, assert_close, from_dev, log, oracle_stream,
-                         run_attn_stream, tdtype, to_dev, txl_dtype, workspace)
+                         nan_empty, run_attn_stream, tdtype, to_dev, txl_dtype, workspace)
 from oracle_pool import oracle_stream_rows
 
 pytestmark = pytest.mark.gpu
@@ -40,7 +40,7 @@ def run_ring_stream(wl, n_seg, mem_start=0, use_rk=False):
     w = dl.W[0]
     Rk = None
     if use_rk:
-        Rk = torch.empty((c.n_pos, c.n_heads, c.d_head), dtype=tdtype(c.dtype), device="cuda")
+        Rk = nan_empty((c.n_pos, c.n_heads, c.d_head), dtype=tdtype(c.dtype), device="cuda")
         pws = workspace(txl.txl_rel_proj_workspace_bytes(c.n_pos, c.d_pos, c.n_heads, c.d_head,
                                                          txl_dtype(c.dtype)))
         txl.txl_rel_proj(dl.R, w["W_kR"], Rk, c.n_pos, c.d_pos, c.n_heads, c.d_head,
@@ -51,7 +51,7 @@ def run_ring_stream(wl, n_seg, mem_start=0, use_rk=False):
     outs, starts = [], []
     for s in range(n_seg):
         h = to_dev(wl.segments[s], c.dtype)
-        out = torch.empty((c.batch, c.seg_len, c.n_heads * c.d_head), dtype=tdtype(c.dtype),
+        out = nan_empty((c.batch, c.seg_len, c.n_heads * c.d_head), dtype=tdtype(c.dtype),
                           device="cuda")
         starts.append(start)
         new = txl.txl_rel_attn_fwd_kv(shp, h, w["W_q"], w["W_kE"], w["W_kR"], w["W_v"], dl.u,
@@ -143,7 +143,7 @@ def run_segment_ring_stream(wl, n_seg):
     start, outs = 0, []
     for s in range(n_seg):
         h = to_dev(wl.segments[s], c.dtype)
-        out = torch.empty((c.batch, c.seg_len, d_out), dtype=tdtype(c.dtype), device="cuda")
+        out = nan_empty((c.batch, c.seg_len, d_out), dtype=tdtype(c.dtype), device="cuda")
         start = txl.txl_segment_step_kv(shp, c.n_layers, c.d_inner, layers, rings, dl.R, h, out,
                                         start, ws)
         torch.cuda.synchronize()

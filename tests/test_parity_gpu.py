@@ -13,7 +13,7 @@ import pytest
 import synth
 from gpu_helpers import (DeviceLayers, TOL, assert_close, bf16_bits_of, from_dev, log,
                          oracle_stream, run_attn_stream, run_segment_stream, tdtype, to_dev,
-                         txl_dtype, workspace)
+                         txl_dtype, nan_empty, workspace)
 from oracle_pool import oracle_stream_rows
 
 pytestmark = pytest.mark.gpu
@@ -56,7 +56,7 @@ def test_sinusoid(txl, dtype):
     import torch
     import oracle
     n, d = 3928, 1024
-    R = torch.empty((n, d), dtype=tdtype(dtype), device="cuda")
+    R = nan_empty((n, d), dtype=tdtype(dtype), device="cuda")
     txl.txl_sinusoid_pos(R, n, d, txl_dtype(dtype))
     torch.cuda.synchronize()
     want = oracle.sinusoid(n, d)
@@ -109,7 +109,7 @@ def test_rel_proj(txl, dtype, n_pos, d_pos, H, dh):
     W = synth.round_to(rng.normal(0, 0.02, (H * dh, d_pos)), dtype)
     Rw = oracle.sinusoid(n_pos, d_pos)
     R = to_dev(synth.round_to(Rw, dtype), dtype)
-    Rk = torch.empty((n_pos, H, dh), dtype=tdtype(dtype), device="cuda")
+    Rk = nan_empty((n_pos, H, dh), dtype=tdtype(dtype), device="cuda")
     ws = workspace(txl.txl_rel_proj_workspace_bytes(n_pos, d_pos, H, dh, txl_dtype(dtype)))
     txl.txl_rel_proj(R, to_dev(W, dtype), Rk, n_pos, d_pos, H, dh, txl_dtype(dtype), ws)
     torch.cuda.synchronize()
@@ -246,7 +246,7 @@ def test_segment_step_packed_rows(txl, L, M, n_seg):
     start = start_o = 0
     for s in range(n_seg):
         h = to_dev(wl.segments[s], "bf16")
-        out = torch.empty((cfg.batch, L, cfg.n_heads * cfg.d_head), dtype=torch.bfloat16,
+        out = nan_empty((cfg.batch, L, cfg.n_heads * cfg.d_head), dtype=torch.bfloat16,
                           device="cuda")
         start = txl.txl_segment_step(shp, 1, 0, layers, dl.R, h, out, start, ws)
         torch.cuda.synchronize()
@@ -316,7 +316,7 @@ def test_stack_16_layers(txl):
         ys = []
         new_st = st
         for n in range(cfg.n_layers):
-            y = torch.empty_like(x)
+            y = torch.full_like(x, float("nan"))
             new_st = txl_mod.txl_segment_step(shp, 1, cfg.d_inner, [layers[n]], dl1.R, x, y, st,
                                               ws)
             ys.append(y)
@@ -390,7 +390,7 @@ def test_shaw_variant(txl, path):
         start = 0
         for s in range(3):
             h = to_dev(wl.segments[s], "bf16")
-            out = torch.empty((cfg.batch, cfg.seg_len, cfg.n_heads * cfg.d_head),
+            out = nan_empty((cfg.batch, cfg.seg_len, cfg.n_heads * cfg.d_head),
                               dtype=torch.bfloat16, device="cuda")
             txl.txl_rel_attn_fwd(shp, h, dl.mem[0], start, w["W_q"], w["W_kE"], None, w["W_v"],
                                  zu, zu, None, Rk, out, ws)
@@ -404,7 +404,7 @@ def test_shaw_variant(txl, path):
         start = txl.txl_kv_ring_init(shp, dl.mem[0], 0, w["W_kE"], w["W_v"], ring, ws)
         for s in range(3):
             h = to_dev(wl.segments[s], "bf16")
-            out = torch.empty((cfg.batch, cfg.seg_len, cfg.n_heads * cfg.d_head),
+            out = nan_empty((cfg.batch, cfg.seg_len, cfg.n_heads * cfg.d_head),
                               dtype=torch.bfloat16, device="cuda")
             start = txl.txl_rel_attn_fwd_kv(shp, h, w["W_q"], w["W_kE"], None, w["W_v"], zu, zu,
                                             None, Rk, ring, start, out, ws)

@@ -193,7 +193,7 @@ def test_vanilla_window_stack(txl, L, n_layers):
     shp = dl.shape()
     ws = workspace(txl.txl_segment_workspace_bytes(shp, n_layers, cfg.d_inner))
     h = to_dev(wl.segments[0], "bf16")
-    out = torch.empty_like(h)
+    out = torch.full_like(h, float("nan"))
     start = txl.txl_segment_step(shp, n_layers, cfg.d_inner, dl.layer_structs(), dl.R, h, out, 0,
                                  ws)
     torch.cuda.synchronize()

@@ -7,7 +7,7 @@ import numpy as np
 import pytest
 
 import synth
-from gpu_helpers import DeviceLayers, log, to_dev, workspace
+from gpu_helpers import DeviceLayers, log, nan_empty, to_dev, workspace
 
 pytestmark = pytest.mark.gpu
 
@@ -31,7 +31,7 @@ def _pair(txl, cfg):
     h = to_dev(wl.segments[0], cfg.dtype)
     mem = dl.mem[0] if cfg.mem_len else None
     start = 3 if cfg.mem_len > 3 else 0
-    out_ref = torch.empty((cfg.batch, cfg.seg_len, cfg.n_heads * cfg.d_head),
+    out_ref = nan_empty((cfg.batch, cfg.seg_len, cfg.n_heads * cfg.d_head),
                           dtype=h.dtype, device="cuda")
     out = torch.full_like(out_ref, float("nan"))
     ws = workspace(need)
@@ -60,7 +60,7 @@ def test_static_scratch_rejects_large_shape(txl):
     shp = txl.AttnShape(cfg.batch, cfg.seg_len, cfg.mem_len, cfg.d_model, cfg.n_heads,
                         cfg.d_head, cfg.d_pos, txl.TXL_BF16, 0.0)
     assert txl.txl_rel_attn_workspace_bytes(shp) > txl.TXL_STATIC_SCRATCH_BYTES
-    t = torch.empty(16, dtype=torch.bfloat16, device="cuda")
+    t = nan_empty(16, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(txl.TxlError) as ei:
         txl.txl_rel_attn_fwd_static(shp, t, t, 0, t, t, t, t, t, t, t, None, t)
     assert ei.value.status == 4     # TXL_ERR_WORKSPACE_TOO_SMALL
