@@ -132,6 +132,14 @@ def test_bwd_train_shaped_full_batch(txl):
     _check_summed(got, want, True)
 
 
+def test_bwd_odd_batch(txl):
+    """Three batch rows: the dRk product takes one batch row per partial (pairs
+    when the count is even), and the partials are summed in order."""
+    cfg = synth.Config("bwd_odd_batch", 3, 128, 2, 64, 96, 64, 1, 1, "bf16", 0.05, 303)
+    got, want = _run(txl, cfg, np.arange(3))
+    _check_summed(got, want, True)
+
+
 def test_bwd_long_segment(txl):
     """Segment 640 > 512: the key-side products stage their shared operand in
     two K chunks, and workgroups whose band starts in the second chunk skip the
