@@ -303,6 +303,7 @@ RowSrc src_headpad(const void* w, int64_t ld, int32_t dh, int32_t dp) {
   r.ld = ld;
   r.dh = dh;
   r.dp = dp;
+  div_magic(dp, &r.qmul, &r.qshift);
   return r;
 }
 RowSrc src_htilde(const void* mem, const void* h, int64_t ld, int32_t np, int32_t M, int32_t L,
@@ -317,6 +318,7 @@ RowSrc src_htilde(const void* mem, const void* h, int64_t ld, int32_t np, int32_
   r.M = M;
   r.L = L;
   r.start = start;
+  div_magic(np, &r.qmul, &r.qshift);
   return r;
 }
 

@@ -50,12 +50,12 @@ __device__ __forceinline__ const char* row_address(const RowSrc& s, int32_t v, i
       if (v < s.rows) p = static_cast<const char*>(s.p0) + (int64_t)v * s.ld * esize;
       break;
     case ROW_HEADPAD: {
-      int32_t head = v / s.dp, c = v - head * s.dp;
+      const int32_t head = magic_quot(v, s.qmul, s.qshift), c = v - head * s.dp;
       if (c < s.dh) p = static_cast<const char*>(s.p0) + (int64_t)(head * s.dh + c) * s.ld * esize;
       break;
     }
     default: {  // ROW_HTILDE
-      int32_t b = v / s.np, r = v - b * s.np - s.lead;
+      const int32_t b = magic_quot(v, s.qmul, s.qshift), r = v - b * s.np - s.lead;
       if (r < 0) {
       } else if (r < s.M) {
         int32_t slot = r + s.start;

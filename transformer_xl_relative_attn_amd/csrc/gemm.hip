@@ -470,6 +470,7 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmGroup& g, int32_t padde
 
   setup(xcd_swizzle(seq, padded));
   prologue();
+  int slot0 = 0;   // ring slot of the current tile's K step 0
 
   // A staged epilogue of a sub-tile that lies wholly inside the output issues
   // exactly EPI_STORES global stores, after the next tile's first NSTAGE
@@ -496,34 +497,71 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmGroup& g, int32_t padde
       wait_vm<(NSTAGE - 1) * 2 * LOADS>();
     barrier_lds();
     {
-      const u32x4* st = stage_ptr(0);
+      const u32x4* st = stage_ptr(slot0);
 #pragma unroll
       for (int f = 0; f < NF; ++f) read_one(st, 0, f, f0a, f0b);
     }
-    int slot = 0, kt = 0;
+    // This tile's problem and position (the epilogue's), and the next tile of
+    // this workgroup.  Once the refills run past this tile's last K step they
+    // load the next tile's first NSTAGE K steps instead of zero chunks: its
+    // operands then land while this tile finishes and writes its epilogue.
+    // The next tile's step j goes to the slot of this tile's step nk + j, so
+    // its K loop starts at slot (slot0 + nk) % NSTAGE.  Tiles shorter than the
+    // ring (nk < NSTAGE) keep the plain prologue after the loop.
+    const int cpidx = pidx;
+    const int32_t cm0 = m0, cn0 = n0, nkc = nk;
+    const int32_t nseq = next_tile(seq + grid);
+    const bool more = nseq < padded;
+    const bool ahead = more && nkc >= NSTAGE;
+    int32_t nkn = 0;   // the next tile's K steps (known once its pointers are set up)
+    auto refill = [&](int32_t tgt) {   // refill for step tgt of this tile: real load?
+      if (tgt < nkc) return true;
+      if (!ahead) return false;
+      if (tgt == nkc) {
+        setup(xcd_swizzle(nseq, padded));
+        nkn = nk;
+      }
+      return tgt - nkc < nkn;
+    };
+    int slot = slot0, kt = 0;
     if (peel) {
 #pragma unroll
-      for (int p = 0; p < NSTAGE - 1; ++p) kstep(IC<EPI_STORES>{}, p, p + 1, p + NSTAGE < nk);
-      slot = kt = NSTAGE - 1;
+      for (int p = 0; p < NSTAGE - 1; ++p) {
+        const int cs = slot + 1 == NSTAGE ? 0 : slot + 1;
+        const bool real = refill(p + NSTAGE);
+        kstep(IC<EPI_STORES>{}, slot, cs, real);
+        slot = cs;
+      }
+      kt = NSTAGE - 1;
     }
 #pragma unroll 1
-    for (; kt < nk; ++kt) {
+    for (; kt < nkc - 1; ++kt) {
       const int nslot = slot + 1 == NSTAGE ? 0 : slot + 1;
-      kstep(IC<0>{}, slot, nslot, kt + NSTAGE < nk);
+      const bool real = refill(kt + NSTAGE);
+      kstep(IC<0>{}, slot, nslot, real);
       slot = nslot;
     }
-    // Every wave is done reading the ring: the next tile's first K steps are
-    // issued now and land while this tile's epilogue runs (this tile's
-    // trailing zero-chunk loads into the same slots were issued earlier by
-    // the same lanes and land first).
+    if (kt == nkc - 1) {
+      // the last K step: the stage after it (the next tile's first, or zero
+      // chunks) is not read by this tile, so its loads may stay in flight
+      const int nslot = slot + 1 == NSTAGE ? 0 : slot + 1;
+      const bool real = refill(kt + NSTAGE);
+      kstep(IC<2 * LOADS>{}, slot, nslot, real);
+      slot = nslot;
+    }
+    // Every wave is done reading the ring.  Without the look-ahead the next
+    // tile's first K steps are issued now (into slots 0 .. NSTAGE-1; this
+    // tile's trailing zero-chunk loads into the same slots were issued earlier
+    // by the same lanes and land first); either way they land while this
+    // tile's epilogue runs.
     barrier_lds();
-    const int cpidx = pidx;
-    const int32_t cm0 = m0, cn0 = n0;
-    seq = next_tile(seq + grid);
-    const bool more = seq < padded;
-    if (more) {
+    seq = nseq;
+    if (ahead) {
+      slot0 = (slot0 + nkc) % NSTAGE;
+    } else if (more) {
       setup(xcd_swizzle(seq, padded));
       prologue();
+      slot0 = 0;
     }
     {
       const OutDst& o = g.p[cpidx].out;

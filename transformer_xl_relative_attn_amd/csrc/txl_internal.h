@@ -29,6 +29,8 @@ struct RowSrc {
   int32_t dh, dp;  // HEADPAD
   int32_t np, M, L, start;  // HTILDE
   int32_t lead;             // HTILDE: zero rows before the memory rows
+  uint32_t qmul;   // floor(v / dp) (HEADPAD) or floor(v / np) (HTILDE) as
+  int32_t qshift;  //   (v * qmul) >> qshift, set up by the host
   int64_t ld;      // elements between consecutive source rows
   const void* p0;  // PLAIN/HEADPAD base, HTILDE memory base
   const void* p1;  // HTILDE segment base
@@ -57,20 +59,27 @@ struct AxisMap {
 constexpr int32_t kLinearDiv = 0x7fffffff;
 
 // Multiplier and shift with floor(x / d) == (x * mul) >> shift for all
-// 0 <= x < 2^31 (round-up reciprocal with l = ceil(log2 d) extra bits).
+// 0 <= x < 2^31 and 1 <= d < 2^31 (round-up reciprocal with
+// l = ceil(log2 d) extra bits).
+inline void div_magic(int32_t d, uint32_t* mul, int32_t* shift) {
+  int l = 0;
+  while ((1ull << l) < (uint64_t)d) ++l;
+  *mul = (uint32_t)(((1ull << (31 + l)) / (uint64_t)d) + 1);
+  *shift = 31 + l;
+}
+
+TXL_HD inline int32_t magic_quot(int32_t x, uint32_t mul, int32_t shift) {
+  return (int32_t)(((uint64_t)(uint32_t)x * mul) >> shift);
+}
+
 inline AxisMap make_axis(int32_t div, int64_t s1, int64_t s2) {
   AxisMap a{div, 0u, 0, s1, s2};
   if (div == kLinearDiv) return a;
-  int l = 0;
-  while ((1ull << l) < (uint64_t)div) ++l;
-  a.mul = (uint32_t)(((1ull << (31 + l)) / (uint64_t)div) + 1);
-  a.shift = 31 + l;
+  div_magic(div, &a.mul, &a.shift);
   return a;
 }
 
-TXL_HD inline int32_t axis_quot(const AxisMap& a, int32_t x) {
-  return (int32_t)(((uint64_t)(uint32_t)x * a.mul) >> a.shift);
-}
+TXL_HD inline int32_t axis_quot(const AxisMap& a, int32_t x) { return magic_quot(x, a.mul, a.shift); }
 
 TXL_HD inline int64_t axis_offset(const AxisMap& a, int32_t x) {
   const int32_t q = axis_quot(a, x);
