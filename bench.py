@@ -99,6 +99,44 @@ def load_traffic(kernel, workload):
     return rec.get("bytes_per_launch")
 
 
+def mfma_probe_leg():
+    """Sustained bf16 matrix-core rate on zero and on random N(0,1) operands
+    (txl_probe_mfma: 8 waves per compute unit, independent 32x32x16 products),
+    with the shader clock the products ran at."""
+    import numpy as np
+    import torch
+    import transformer_xl_relative_attn_amd as txl
+    n_wg = torch.cuda.get_device_properties(0).multi_processor_count
+    units = n_wg * 512 * 24
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(20261202)
+    data = {"zeros": torch.zeros(units * 8, dtype=torch.bfloat16, device="cuda"),
+            "random": torch.randn(units * 8, generator=gen, device="cuda").to(torch.bfloat16)}
+    clocks = torch.zeros(2 * n_wg + 1, dtype=torch.int64, device="cuda")
+    stream = torch.cuda.current_stream()
+    out = {"kernel": "txl_probe_mfma", "workgroups": n_wg}
+    for name, buf in data.items():
+        for label, iters, reps in (("burst", 256, 1), ("sustained", 4096, 3)):
+            txl.txl_probe_mfma(buf, n_wg, 64, clocks, stream)
+            torch.cuda.synchronize()
+            for _ in range(reps):   # the last repetition is reported
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                txl.txl_probe_mfma(buf, n_wg, iters, clocks, stream)
+                e1.record(stream)
+                torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+            c = clocks[:2 * n_wg].view(n_wg, 2).cpu().numpy().astype(np.float64)
+            ghz = float(np.median(c[:, 0] / c[:, 1])) * 0.1
+            fl = 2.0 * 32 * 32 * 16 * 16 * iters * 8 * n_wg
+            out[f"{name}_{label}"] = {"us": round(ms * 1e3, 1),
+                                      "tflops": round(fl / (ms * 1e-3) / 1e12, 1),
+                                      "clock_ghz": round(ghz, 3)}
+    del data, clocks
+    return out
+
+
 def cpu_baseline(cfg, wl, budget_s):
     """Time the fp64 oracle on the host for consecutive segments of the same
     workload until the budget is spent (at least one segment)."""
@@ -431,6 +469,8 @@ def main():
                     help="skip the carried K/V ring leg")
     ap.add_argument("--no-mall", dest="mall", action="store_false",
                     help="skip the cold/warm Infinity Cache leg of the attention kernel")
+    ap.add_argument("--no-probe", dest="probe", action="store_false",
+                    help="skip the matrix-core probe (sustained bf16 rate on zero/random operands)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--table9", action="store_true",
@@ -680,6 +720,13 @@ def main():
                      "executed_tflops": round(fr / (ms_r * 1e-3) / 1e12, 1)}
         del rings, ws_r
 
+    probe = None
+    if args.probe and cfg.dtype == "bf16" and not args.shaw:
+        probe = mfma_probe_leg()
+        rs = probe["random_sustained"]["tflops"]
+        probe["proj_gemm_vs_random_sustained"] = round(roof["achieved"] / rs, 3) \
+            if roof and roof.get("kernel") == "proj_gemm" and roof.get("achieved") and rs else None
+
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(cfg, wl, args.cpu_budget)
@@ -736,6 +783,7 @@ def main():
         "attention_kernel": attn_info,
         "kv_ring": ring_info,
         "roofline": roof,
+        "mfma_probe": probe,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -346,6 +346,27 @@ txl_status_t txl_timing_enable(int32_t on);
 void txl_timing_reset(void);
 int32_t txl_timing_read(int32_t capacity, const char** names, int64_t* counts, double* total_ms);
 
+/*
+ * Matrix-core probe (diagnostics; no part of the attention path).  Measures the
+ * bf16 matrix-core rate the chip sustains on given operand data, against which
+ * the projection GEMM's throughput can be read.  Launches n_wg workgroups of
+ * eight waves on `stream`; every wave issues `iters` rounds of 16 independent
+ * 32x32x16 bf16 products (2 * 32 * 32 * 16 * 16 * iters * 8 * n_wg FLOP in
+ * all), with operands taken from `operands`:
+ *   operands  device, 16-byte aligned, n_wg * 512 * 24 units of 16 bytes (eight
+ *             bf16 values each); thread t of workgroup w reads units
+ *             (w * 512 + t) * 24 .. +23.  Caller-owned, read only.
+ *   clocks    device, 2 * n_wg + 1 uint64 entries, caller-owned: entry 2w gets
+ *             the shader-clock cycles and entry 2w + 1 the 100 MHz reference
+ *             ticks of workgroup w's product loop (their ratio times 100 MHz is
+ *             the clock the matrix cores ran at); the last entry is scratch.
+ * n_wg in [1, 65536], iters even and >= 2; TXL_ERR_NULL_ARG / TXL_ERR_BAD_SHAPE /
+ * TXL_ERR_UNSUPPORTED (misaligned operands) before any launch.  Asynchronous:
+ * time it with events on `stream`.
+ */
+txl_status_t txl_probe_mfma(const void* operands, int32_t n_wg, int32_t iters, uint64_t* clocks,
+                            void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -24,7 +24,7 @@ __all__ = [
     "txl_rel_attn_fwd_kv", "txl_segment_kv_workspace_bytes", "txl_segment_step_kv",
     "txl_rel_attn_bwd_workspace_bytes", "txl_rel_attn_bwd", "txl_rel_attn_fwd_train",
     "txl_rel_attn_bwd_saved",
-    "txl_timing_enable", "txl_timing_reset", "txl_timing_read",
+    "txl_timing_enable", "txl_timing_reset", "txl_timing_read", "txl_probe_mfma",
 ]
 
 TXL_F32 = 0
@@ -66,6 +66,7 @@ _abi = _sig("txl_abi_version", ctypes.c_int, [])
 _status_str = _sig("txl_status_str", ctypes.c_char_p, [ctypes.c_int])
 _last_error = _sig("txl_last_error", ctypes.c_char_p, [])
 _sinusoid = _sig("txl_sinusoid_pos", ctypes.c_int, [_vp, _i32, _i32, _i32, _vp])
+_probe = _sig("txl_probe_mfma", ctypes.c_int, [_vp, _i32, _i32, _vp, _vp])
 _proj_ws = _sig("txl_rel_proj_workspace_bytes", _sz, [_i32, _i32, _i32, _i32, _i32])
 _proj = _sig("txl_rel_proj", ctypes.c_int,
              [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _sz, _vp])
@@ -307,6 +308,12 @@ def txl_timing_enable(on: bool):
 
 def txl_timing_reset():
     _t_reset()
+
+
+def txl_probe_mfma(operands, n_wg: int, iters: int, clocks, stream=None):
+    """Matrix-core probe: operands (n_wg * 512 * 24 * 8 bf16 values), clocks
+    (2 * n_wg + 1 uint64 entries: per workgroup, shader cycles and 100 MHz ticks)."""
+    _check(_probe(_ptr(operands), n_wg, iters, _ptr(clocks), _stream(stream)), "txl_probe_mfma")
 
 
 def txl_timing_read() -> dict:

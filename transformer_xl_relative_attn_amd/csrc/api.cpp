@@ -328,8 +328,7 @@ void add_problem(GemmGroup& g, int32_t M, int32_t N, int32_t K, const RowSrc& a,
   p.M = M;
   p.N = N;
   p.K = K;
-  p.tiles_m = (M + tile - 1) / tile;
-  p.tiles_n = (N + tile - 1) / tile;
+  set_tiling(p, tile);
   p.tile_begin = g.total_tiles;
   p.a = a;
   p.b = b;
@@ -1172,6 +1171,16 @@ const char* txl_status_str(txl_status_t st) {
 }
 
 const char* txl_last_error(void) { return g_last_error.c_str(); }
+
+txl_status_t txl_probe_mfma(const void* operands, int32_t n_wg, int32_t iters, uint64_t* clocks,
+                            void* stream) {
+  if (!operands || !clocks) return fail(TXL_ERR_NULL_ARG, "operands and clocks are required");
+  if (n_wg < 1 || n_wg > 65536 || iters < 2 || iters % 2 != 0)
+    return fail(TXL_ERR_BAD_SHAPE, "n_wg=%d iters=%d (need 1 <= n_wg <= 65536, even iters >= 2)", n_wg,
+                iters);
+  if (!aligned16(operands)) return fail(TXL_ERR_UNSUPPORTED, "operands must be 16-byte aligned");
+  return after_launch(launch_mfma_probe(operands, n_wg, iters, clocks, stream), "mfma probe", stream);
+}
 
 txl_status_t txl_sinusoid_pos(void* R, int32_t n_pos, int32_t d_pos, int32_t dtype, void* stream) {
   if (!R) return fail(TXL_ERR_NULL_ARG, "R is NULL");

@@ -711,8 +711,7 @@ GemmGroup regroup(const GemmGroup& g, const bool* pick, int t) {
     newidx[i] = -1;
     if (pick && !pick[i]) continue;
     GemmProblem p = g.p[i];
-    p.tiles_m = (p.M + t - 1) / t;
-    p.tiles_n = (p.N + t - 1) / t;
+    set_tiling(p, t);
     p.tile_begin = s.total_tiles;
     s.total_tiles += p.tiles_m * p.tiles_n;
     newidx[i] = s.count;

@@ -144,6 +144,12 @@ struct GemmProblem {
   OutDst out;
 };
 
+// Tile counts of a problem for square tiles of `tile` rows.
+inline void set_tiling(GemmProblem& p, int32_t tile) {
+  p.tiles_m = (p.M + tile - 1) / tile;
+  p.tiles_n = (p.N + tile - 1) / tile;
+}
+
 constexpr int kMaxGroup = 8;
 
 struct GemmGroup {
@@ -280,6 +286,8 @@ int launch_attn_bf16(const AttnArgs& a, void* stream);
 int launch_attn_combine(const AttnArgs& a, void* stream);
 int launch_attn_f32(const AttnArgs& a, void* stream);
 int launch_sinusoid(void* R, int32_t n_pos, int32_t d_pos, int32_t dtype, void* stream);
+int launch_mfma_probe(const void* operands, int32_t n_wg, int32_t iters, uint64_t* clocks,
+                      void* stream);
 int launch_mem_update(void* mem, int32_t start, const void* h, int32_t B, int32_t M, int32_t L,
                       int32_t d, int32_t dtype, void* stream);
 int launch_pack_rows(void* dst, int64_t ld_dst, const void* src, int64_t ld_src, int64_t rows,
