@@ -512,7 +512,10 @@ __device__ __forceinline__ void gemm_bf16_body(const GemmGroup& g, int32_t padde
     const int32_t cm0 = m0, cn0 = n0, nkc = nk;
     const int32_t nseq = next_tile(seq + grid);
     const bool more = nseq < padded;
-    const bool ahead = more && nkc >= NSTAGE;
+    // (the 128x128 variants, which mostly run one tile per workgroup, keep the
+    // plain prologue: the set-up inside their K loop made the compiler copy
+    // the kernel-argument block to scratch)
+    const bool ahead = V::BM == 256 && more && nkc >= NSTAGE;
     int32_t nkn = 0;   // the next tile's K steps (known once its pointers are set up)
     auto refill = [&](int32_t tgt) {   // refill for step tgt of this tile: real load?
       if (tgt < nkc) return true;
