@@ -358,8 +358,9 @@ int32_t txl_timing_read(int32_t capacity, const char** names, int64_t* counts, d
  *             (w * 512 + t) * 24 .. +23.  Caller-owned, read only.
  *   clocks    device, 2 * n_wg + 1 uint64 entries, caller-owned: entry 2w gets
  *             the shader-clock cycles and entry 2w + 1 the 100 MHz reference
- *             ticks of workgroup w's product loop (their ratio times 100 MHz is
- *             the clock the matrix cores ran at); the last entry is scratch.
+ *             ticks of the product loop of workgroup w's first wave (their ratio
+ *             times 100 MHz is the clock the matrix cores ran at); the last entry
+ *             is scratch.
  * n_wg in [1, 65536], iters even and >= 2; TXL_ERR_NULL_ARG / TXL_ERR_BAD_SHAPE /
  * TXL_ERR_UNSUPPORTED (misaligned operands) before any launch.  Asynchronous:
  * time it with events on `stream`.

@@ -147,6 +147,17 @@ def test_rel_proj_and_sinusoid_validation(txl):
     assert g(16, 4, 4, 5, None) == 3
 
 
+def test_probe_mfma_validation(txl):
+    f = txl.lib.txl_probe_mfma
+    assert f(None, 4, 2, 16, None) == 1          # operands
+    assert f(16, 4, 2, None, None) == 1          # clocks
+    assert f(16, 0, 2, 16, None) == 2            # n_wg
+    assert f(16, 65537, 2, 16, None) == 2
+    assert f(16, 4, 3, 16, None) == 2            # iters odd
+    assert f(16, 4, 0, 16, None) == 2
+    assert f(24, 4, 2, 16, None) == 5            # operands not 16-byte aligned
+
+
 def test_kv_ring_queries_and_validation(txl):
     # eval-shaped layer: C = round_up(1600, 32) + 128 slots, K and V^T in bf16
     s = _shape(txl, batch=8, seg_len=128, mem_len=1600, d_model=1024, n_heads=16, d_head=64,

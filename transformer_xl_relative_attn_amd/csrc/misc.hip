@@ -316,7 +316,8 @@ inline dim3 grid1d(int64_t n) { return dim3((unsigned)((n + 255) / 256)); }
 // lane each) and issues `iters` rounds of 16 independent 32x32x16 products
 // on them (operands rotate between rounds; iters is even).  Wave 0 of each
 // workgroup records the shader-clock cycles and 100 MHz reference ticks its
-// loop took, so the caller can read the clock the matrix cores ran at.
+// loop took (it may finish before the other wave of its SIMD), so the caller
+// can read the clock the matrix cores ran at.
 __global__ __launch_bounds__(512, 1) void mfma_probe_kernel(const u32x4* operands, int32_t iters,
                                                             uint64_t* clocks) {
   const int tid = threadIdx.x;
