@@ -12,10 +12,12 @@
 //   K steps filled by direct global->LDS loads (no register staging), issued
 //   NSTAGE-1 K steps ahead of their use; MFMA operand reads and refill loads
 //   are spread evenly between the MFMAs.  Persistent: one workgroup per CU
-//   walks the tiles; the next tile's first K steps are issued before the
-//   current tile's epilogue, which stages its bf16 output through a separate
-//   32 KB LDS region.  Requirements (checked by the host): K % 64 == 0, every
-//   row 16-byte aligned.
+//   walks the tiles; in the 256x256 variant the ring refills past a tile's
+//   last K step load the next tile's first K steps (elsewhere they are issued
+//   before the epilogue), so they land while the current tile's epilogue
+//   stages its bf16 output through a separate 32 KB LDS region.
+//   Requirements (checked by the host): K % 64 == 0, every row 16-byte
+//   aligned.
 //
 // gemm_f32: fp32 operands and arithmetic on the vector ALUs (64x64 tile),
 //   used by the fp32 path.
