@@ -60,8 +60,13 @@ constexpr int32_t kLinearDiv = 0x7fffffff;
 
 // Multiplier and shift with floor(x / d) == (x * mul) >> shift for all
 // 0 <= x < 2^31 and 1 <= d < 2^31 (round-up reciprocal with
-// l = ceil(log2 d) extra bits).
+// l = ceil(log2 d) extra bits).  A divisor below 1 (no rows) gives quotient 0.
 inline void div_magic(int32_t d, uint32_t* mul, int32_t* shift) {
+  if (d < 1) {
+    *mul = 0u;
+    *shift = 0;
+    return;
+  }
   int l = 0;
   while ((1ull << l) < (uint64_t)d) ++l;
   *mul = (uint32_t)(((1ull << (31 + l)) / (uint64_t)d) + 1);
